@@ -1,0 +1,132 @@
+/*
+ * lisa.h -- C ABI of the MI355X (gfx950) LiSA forward-pass library, liblisa.so.
+ *
+ * LiSA (Linear Stochastic Attention) is described by the reading note
+ * "LiSA:面向长程视觉建模的线性随机注意力" of arXiv:2611.04216v2; sections below
+ * are that note's.  Per (batch, head) slice with n = grid_h * grid_w tokens in
+ * row-major grid order (token i = row * grid_w + col):
+ *
+ *   global branch  [note §2.1-§2.3]
+ *     phi = ReLU;  s = sum_j phi(K_j);  r_i = 1 / (phi(Q_i) . s + eps)
+ *     Qt = diag(r) phi(Q);  S = Qt phi(K)^T   (row-stochastic up to eps)
+ *     G  = sum_{k=0}^{T-1} diag(w_k) S^k V,  S^0 = I,
+ *     computed as S^k V = Qt M^(k-1) (phi(K)^T V) with M = phi(K)^T Qt
+ *     (Eq. 8), never forming an n x n matrix.
+ *   step weights  [note §2.2 Eq. 4; §2.4 Eq. 10]
+ *     geometric: w_k = (1-beta) beta^k / (1-beta^T), the same for every token;
+ *     adaptive : w_k(i) given per token and head, used as given.
+ *   local branch  [note §2.4, Fig. 2]
+ *     L_i = sum_{j in N(i)} e_ij V_j / sum_{j in N(i)} e_ij,
+ *     e_ij = exp(Q_i . K_j / sqrt(d_h)), N(i) = token i and its spatial
+ *     neighbours in the 3x3 window, clipped at the grid border.  Q and K are
+ *     used as given (no feature map) in this branch.
+ *   mix  [note §2.4; §4.4 Table 6]
+ *     Y = alpha_h G + (1 - alpha_h) L, one alpha per head.
+ *
+ * Conventions for every entry point:
+ *   - Array pointers are DEVICE pointers unless stated; the caller owns every
+ *     buffer.  The library never allocates, frees or synchronises; work is
+ *     enqueued on `stream` (a hipStream_t, NULL = the null stream) and the
+ *     call returns at once.
+ *   - Q, K: [batch, heads, n, d_h]; V: [batch, heads, n, d_v]; Y: like V.
+ *     Contiguous, element type `dtype`, 16-byte aligned.  Y must not overlap
+ *     Q, K, V or the workspace.
+ *   - Arguments are checked on the host before anything is enqueued; an
+ *     error status means nothing was enqueued and nothing was written.  A
+ *     failed launch is reported as LISA_ERR_HIP.  No C++ exception crosses
+ *     the ABI.  NaN/Inf inputs are not checked; they propagate.
+ *   - Workspace: `lisa_workspace_size` bytes of device memory, 256-byte
+ *     aligned, ZERO-FILLED before its first use.  Every completed call leaves
+ *     its counter words at zero again, so a workspace can be reused by later
+ *     calls of any problem that fits it.  Calls that share a workspace must
+ *     be ordered on one stream; concurrent calls on one workspace race.
+ *   - Arithmetic: fp32 accumulation throughout.  With LISA_BF16 inputs the
+ *     matrix products run on bf16 MFMA with fp32 accumulation, and the
+ *     operands the library derives itself (r_i phi(Q_i), powers of M applied
+ *     to phi(Q_i), and the d_h x d_h statistics) are rounded to bf16 before
+ *     entering a product; with LISA_FP32 inputs every product is fp32.
+ *     Y is written in the input dtype (bf16: round to nearest even).
+ */
+#ifndef LISA_H
+#define LISA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lisa_status {
+  LISA_OK = 0,
+  LISA_ERR_NULL = 1,        /* a required pointer is NULL */
+  LISA_ERR_SHAPE = 2,       /* a dimension is <= 0 or too large */
+  LISA_ERR_PARAM = 3,       /* T outside 1..8, beta outside [0,1), eps <= 0 or not finite */
+  LISA_ERR_DTYPE = 4,       /* dtype is not LISA_FP32 / LISA_BF16 */
+  LISA_ERR_UNSUPPORTED = 5, /* d_h or d_v other than 64, or batch*heads > 65535 */
+  LISA_ERR_WORKSPACE = 6,   /* workspace NULL, too small or not 256-byte aligned */
+  LISA_ERR_ALIGN = 7,       /* Q, K, V, Y not 16-byte or weights/alpha/outputs not 4-byte aligned */
+  LISA_ERR_HIP = 8          /* a HIP launch or copy failed */
+} lisa_status;
+
+typedef enum lisa_dtype { LISA_FP32 = 0, LISA_BF16 = 1 } lisa_dtype;
+
+/* Problem description.  n = grid_h * grid_w tokens per (batch, head). */
+typedef struct lisa_problem {
+  int32_t batch;  /* B >= 1 */
+  int32_t heads;  /* >= 1; batch * heads <= 65535 */
+  int32_t grid_h; /* H >= 1 */
+  int32_t grid_w; /* W >= 1; H * W <= 2^24 */
+  int32_t d_h;    /* query/key width: 64 */
+  int32_t d_v;    /* value width: 64 */
+  int32_t T;      /* walk terms k = 0..T-1, 1 <= T <= 8 */
+  int32_t dtype;  /* lisa_dtype of Q, K, V, Y */
+  float eps;      /* row-normaliser stabiliser, finite and > 0 */
+} lisa_problem;
+
+/* Bytes of device workspace the calls below need for problem *p; 0 if *p is
+ * invalid (or p is NULL).  Host only; enqueues nothing. */
+size_t lisa_workspace_size(const lisa_problem* p);
+
+/* The whole LiSA forward pass: Y = alpha G + (1 - alpha) L (see top).
+ *   weights : [batch, heads, n, T] fp32 adaptive step weights w_k(i)
+ *             [note §2.4 Eq. 10], or NULL for geometric weights of `beta`
+ *             [note §2.2 Eq. 4].
+ *   beta    : continuation probability in [0, 1); read only when weights is
+ *             NULL.
+ *   alpha   : [heads] fp32 mixing coefficients (device); not range-checked,
+ *             values outside [0, 1] extrapolate.
+ *   Y       : [batch, heads, n, d_v] output, dtype of the problem. */
+lisa_status lisa_forward(const lisa_problem* p, const void* Q, const void* K, const void* V,
+                         const float* weights, float beta, const float* alpha, void* Y,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* First stage alone: the d_h-space statistics of every (batch, head)
+ * [note §2.3 Eq. 8]:
+ *   s_out  [batch, heads, d_h]      s = sum_j phi(K_j)
+ *   kv_out [batch, heads, d_h, d_v] phi(K)^T V
+ *   m_out  [batch, heads, d_h, d_h] M = phi(K)^T Qt, Qt_i = phi(Q_i) / (phi(Q_i) . s + eps)
+ * All three fp32, row-major; each may be NULL to skip that copy.  The
+ * statistics are also left in the workspace, where lisa_apply reads them.
+ * p->T is checked like everywhere else but all three are always formed. */
+lisa_status lisa_reduce(const lisa_problem* p, const void* Q, const void* K, const void* V,
+                        float* s_out, float* kv_out, float* m_out,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Second stage alone: the output pass of lisa_forward, using the statistics
+ * that the last lisa_reduce on the same problem, inputs and workspace left
+ * there.  lisa_reduce followed by lisa_apply computes the same Y as
+ * lisa_forward, with the same kernels when T >= 3 (for T < 3 lisa_forward
+ * skips the statistics it does not need).  Arguments as for lisa_forward. */
+lisa_status lisa_apply(const lisa_problem* p, const void* Q, const void* K, const void* V,
+                       const float* weights, float beta, const float* alpha, void* Y,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* lisa_status_str(lisa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LISA_H */

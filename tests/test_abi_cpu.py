@@ -1,0 +1,129 @@
+"""The C-ABI library loads, exports what include/lisa.h declares, and rejects
+bad arguments on the host before touching the GPU (CPU only: every call here
+fails validation, so nothing is enqueued)."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lisa.h")
+
+lisa = pytest.importorskip("vision_transformer_token_amd.lisa", reason="liblisa.so not built")
+lib = lisa.raw
+
+OK, NULL, SHAPE, PARAM, DTYPE, UNSUP, WS, ALIGN, HIP = range(9)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(lisa_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == [
+        "lisa_apply", "lisa_forward", "lisa_reduce", "lisa_status_str", "lisa_workspace_size"]
+
+
+def test_library_exports_every_declared_symbol():
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_problem_struct_matches_header():
+    assert ctypes.sizeof(lisa.Problem) == 9 * 4
+
+
+def prob(**kw):
+    base = dict(batch=2, heads=3, grid_h=5, grid_w=7, d_h=64, d_v=64, T=3, dtype=lisa.LISA_BF16,
+                eps=1e-6)
+    base.update(kw)
+    return lisa.Problem(**base)
+
+
+# Fake, aligned device addresses: never dereferenced, since validation fails first.
+A = 0x10000000
+Q, K, V, Y, W_, AL, WS_ = (A + i * 0x1000000 for i in range(7))
+
+
+def forward(p, q=Q, k=K, v=V, w=W_, beta=0.5, alpha=AL, y=Y, ws=WS_, ws_bytes=None, fn=None):
+    if ws_bytes is None:
+        ws_bytes = lisa.lisa_workspace_size(p) if p is not None else 0
+    f = fn or lib.lisa_forward
+    return f(None if p is None else ctypes.byref(p), q, k, v, w, ctypes.c_float(beta), alpha, y, ws,
+             ctypes.c_size_t(ws_bytes), None)
+
+
+def test_workspace_size():
+    assert lib.lisa_workspace_size(None) == 0
+    assert lisa.lisa_workspace_size(prob(batch=0)) == 0
+    assert lisa.lisa_workspace_size(prob(d_h=32)) == 0
+    a = lisa.lisa_workspace_size(prob())
+    b = lisa.lisa_workspace_size(prob(batch=4))
+    assert 0 < a < b and a % 256 == 0
+    # long sequences: partial count is capped, so the size stays linear in batch*heads
+    big = lisa.lisa_workspace_size(prob(batch=1, heads=1, grid_h=400, grid_w=400))
+    assert 0 < big < 64 << 20
+
+
+@pytest.mark.parametrize("fn", ["lisa_forward", "lisa_apply"])
+def test_forward_argument_errors(fn):
+    f = getattr(lib, fn)
+    assert forward(None, fn=f) == NULL
+    assert forward(prob(dtype=7), fn=f) == DTYPE
+    for bad in (dict(batch=0), dict(heads=-1), dict(grid_h=0), dict(grid_w=0), dict(d_h=0),
+                dict(grid_h=5000, grid_w=5000)):
+        assert forward(prob(**bad), fn=f) == SHAPE, bad
+    for bad in (dict(d_h=32), dict(d_v=128), dict(batch=300, heads=300)):
+        assert forward(prob(**bad), fn=f) == UNSUP, bad
+    for bad in (dict(T=0), dict(T=9), dict(eps=0.0), dict(eps=-1e-6), dict(eps=math.nan),
+                dict(eps=math.inf)):
+        assert forward(prob(**bad), fn=f) == PARAM, bad
+    for beta in (1.0, -0.1, math.nan):
+        assert forward(prob(), w=None, beta=beta, fn=f) == PARAM
+    for name in ("q", "k", "v", "alpha", "y"):
+        assert forward(prob(), fn=f, **{name: None}) == NULL, name
+    for name in ("q", "k", "v", "y"):
+        assert forward(prob(), fn=f, **{name: A + 8}) == ALIGN, name
+    assert forward(prob(), w=A + 2, fn=f) == ALIGN
+    assert forward(prob(), alpha=A + 2, fn=f) == ALIGN
+    p = prob()
+    need = lisa.lisa_workspace_size(p)
+    assert forward(p, ws=None, fn=f) == WS
+    assert forward(p, ws_bytes=need - 1, fn=f) == WS
+    assert forward(p, ws=WS_ + 128, fn=f) == WS
+    # Y overlapping an input or the workspace
+    assert forward(p, y=Q + 64, fn=f) == PARAM
+    assert forward(p, y=WS_, fn=f) == PARAM
+
+
+def test_reduce_argument_errors():
+    def reduce(p, q=Q, k=K, v=V, s=A, kv=A + 0x100000, m=A + 0x200000, ws=WS_, ws_bytes=None):
+        if ws_bytes is None:
+            ws_bytes = lisa.lisa_workspace_size(p) if p is not None else 0
+        return lib.lisa_reduce(None if p is None else ctypes.byref(p), q, k, v, s, kv, m, ws,
+                               ctypes.c_size_t(ws_bytes), None)
+
+    assert reduce(None) == NULL
+    assert reduce(prob(dtype=3)) == DTYPE
+    assert reduce(prob(grid_h=0)) == SHAPE
+    assert reduce(prob(d_v=16)) == UNSUP
+    assert reduce(prob(T=0)) == PARAM
+    assert reduce(prob(), q=None) == NULL
+    assert reduce(prob(), k=A + 4) == ALIGN
+    assert reduce(prob(), s=A + 2) == ALIGN
+    assert reduce(prob(), ws=None) == WS
+    p = prob()
+    assert reduce(p, ws_bytes=lisa.lisa_workspace_size(p) - 256) == WS
+
+
+def test_status_strings():
+    seen = set()
+    for code in range(9):
+        s = lisa.lisa_status_str(code)
+        assert s and s not in seen
+        seen.add(s)
+    assert lisa.lisa_status_str(42) == "unknown status"

@@ -1,0 +1,209 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on the GPU.
+
+Tolerances (relative L2 over the whole output, and per element against
+|ref| + rms(ref)): 1e-5 for fp32 inputs, 2e-2 for bf16 inputs with fp32
+accumulation.  Every workload preset runs at full size; the oracle computes
+the whole output in fp64 on the host.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import lisa as olisa
+from vision_transformer_token_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-5, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def lisa():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from vision_transformer_token_amd import lisa as mod
+
+    return mod
+
+
+def f64(t):
+    return None if t is None else t.double().cpu().numpy()
+
+
+def to_dev(x):
+    out = dict(x)
+    for key in ("q", "k", "v", "weights", "alpha"):
+        if x[key] is not None:
+            out[key] = x[key].cuda()
+    return out
+
+
+def oracle_y(x):
+    return oracle.lisa_forward(f64(x["q"]), f64(x["k"]), f64(x["v"]), H=x["H"], W=x["W"], T=x["T"],
+                               alpha=f64(x["alpha"]), weights=f64(x["weights"]), beta=x["beta"],
+                               eps=x["eps"])
+
+
+def gpu_y(lisa, d, **kw):
+    y = lisa.lisa_forward(d["q"], d["k"], d["v"], grid=(d["H"], d["W"]), T=d["T"], alpha=d["alpha"],
+                          weights=d["weights"], beta=d["beta"], eps=d["eps"], **kw)
+    torch.cuda.synchronize()
+    return y
+
+
+def check(y_gpu, y_ref, dtype, label):
+    y = f64(y_gpu)
+    diff = y - y_ref
+    rel = np.linalg.norm(diff) / np.linalg.norm(y_ref)
+    rms = np.sqrt(np.mean(y_ref**2))
+    el = np.max(np.abs(diff) / (np.abs(y_ref) + rms))
+    B, h = y_ref.shape[:2]
+    per = [np.linalg.norm(diff[b, i]) / np.linalg.norm(y_ref[b, i]) for b in range(B) for i in range(h)]
+    print(f"[parity] {label}: rel_l2={rel:.3e} worst_slice={max(per):.3e} max_el={el:.3e}", flush=True)
+    assert np.all(np.isfinite(y))
+    assert rel <= TOL[dtype], (label, rel)
+    assert el <= TOL[dtype], (label, el)
+    return rel
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_workload_parity(lisa, name):
+    w = workloads.get(name)
+    x = workloads.make_inputs(w)
+    check(gpu_y(lisa, to_dev(x)), oracle_y(x), w.dtype, w.describe())
+
+
+RAGGED = [
+    # (B, heads, H, W, T, dtype, mode)
+    (1, 1, 1, 1, 3, "bf16", "adaptive"),
+    (1, 1, 1, 1, 1, "fp32", "geometric"),
+    (2, 1, 1, 7, 3, "fp32", "adaptive"),
+    (1, 2, 7, 1, 4, "bf16", "geometric"),
+    (2, 3, 5, 7, 2, "bf16", "adaptive"),
+    (1, 1, 13, 17, 5, "fp32", "adaptive"),
+    (3, 1, 13, 17, 8, "bf16", "adaptive"),
+    (1, 1, 3, 100, 3, "bf16", "adaptive"),
+    (1, 2, 2, 65, 6, "fp32", "geometric"),
+    (2, 1, 9, 33, 3, "bf16", "geometric"),
+    (1, 1, 70, 70, 3, "bf16", "adaptive"),   # 4900 tokens: two-level combine
+    (1, 1, 41, 45, 7, "fp32", "adaptive"),
+    (1, 1, 260, 260, 3, "bf16", "adaptive"),  # > 65536 tokens: enlarged chunks
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=[f"{c[0]}x{c[1]}_{c[2]}x{c[3]}_T{c[4]}_{c[5]}_{c[6]}" for c in RAGGED])
+def test_ragged_and_edge_shapes(lisa, case):
+    B, heads, H, W, T, dtype, mode = case
+    w = workloads.small("ragged", B, heads, H, W, T, dtype=dtype, mode=mode, beta=0.6,
+                        seed=7 + H * 131 + W)
+    x = workloads.make_inputs(w)
+    check(gpu_y(lisa, to_dev(x)), oracle_y(x), dtype, str(case))
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_each_walk_term_alone(lisa, dtype):
+    """One-hot weights e_k isolate S^k V; alpha = 1 isolates the global branch."""
+    T = 6
+    w = workloads.small("onehot", 2, 1, 9, 11, T, dtype=dtype, alpha=1.0, seed=31)
+    x = workloads.make_inputs(w)
+    for k in range(T):
+        wt = torch.zeros_like(x["weights"])
+        wt[..., k] = 1.0
+        xk = dict(x, weights=wt)
+        check(gpu_y(lisa, to_dev(xk)), oracle_y(xk), dtype, f"S^{k} V {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_alpha_isolates_branches(lisa, dtype):
+    for a in (0.0, 1.0):
+        w = workloads.small("alpha", 1, 2, 12, 10, 3, dtype=dtype, alpha=a, seed=41)
+        x = workloads.make_inputs(w)
+        check(gpu_y(lisa, to_dev(x)), oracle_y(x), dtype, f"alpha={a} {dtype}")
+
+
+@pytest.mark.parametrize("name", ["tiny_oracle_14x14", "deit_t_224", "pvt_t_stage1", "long_range_200x320"])
+def test_statistics_stage(lisa, name):
+    """lisa_reduce: s, phi(K)^T V and M against the oracle's statistics."""
+    w = workloads.get(name)
+    x = workloads.make_inputs(w)
+    d = to_dev(x)
+    s, kv, m = lisa.lisa_reduce(d["q"], d["k"], d["v"], grid=(w.H, w.W), eps=w.eps, T=w.T)
+    torch.cuda.synchronize()
+    q, k, v = f64(x["q"]), f64(x["k"]), f64(x["v"])
+    tol_s = 1e-5
+    tol_m = 1e-5 if w.dtype == "fp32" else 1e-2  # bf16: r_i phi(Q_i) is rounded to bf16
+    worst = [0.0, 0.0, 0.0]
+    for b in range(w.B):
+        for h in range(w.heads):
+            rs, rkv, rm = olisa.stats(q[b, h], k[b, h], v[b, h], w.eps)
+            for j, (g, r) in enumerate(((s[b, h], rs), (kv[b, h], rkv), (m[b, h], rm))):
+                e = np.linalg.norm(f64(g) - r) / np.linalg.norm(r)
+                worst[j] = max(worst[j], e)
+    print(f"[parity] stats {name}: s={worst[0]:.2e} kv={worst[1]:.2e} m={worst[2]:.2e}", flush=True)
+    assert worst[0] <= tol_s and worst[1] <= tol_s and worst[2] <= tol_m
+
+
+def test_reduce_then_apply_equals_forward(lisa):
+    w = workloads.get("pvt_t_stage1")
+    d = to_dev(workloads.make_inputs(w))
+    y1 = gpu_y(lisa, d)
+    prob = lisa.make_problem(d["q"], d["v"], grid=(w.H, w.W), T=w.T, eps=w.eps)
+    ws = lisa.new_workspace(prob, d["q"].device)
+    lisa.lisa_reduce(d["q"], d["k"], d["v"], grid=(w.H, w.W), eps=w.eps, T=w.T, workspace=ws,
+                     outputs=False)
+    y2 = lisa.lisa_apply(d["q"], d["k"], d["v"], grid=(w.H, w.W), T=w.T, alpha=d["alpha"],
+                         weights=d["weights"], eps=w.eps, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+def test_deterministic_and_workspace_reuse(lisa):
+    """Bitwise repeatable; one workspace serves problems of different shapes in turn."""
+    wa = workloads.get("deit_t_384")
+    wb = workloads.small("reuse", 1, 1, 70, 70, 5, seed=5)
+    xa, xb = workloads.make_inputs(wa), workloads.make_inputs(wb)
+    da, db = to_dev(xa), to_dev(xb)
+    pa = lisa.make_problem(da["q"], da["v"], grid=(wa.H, wa.W), T=wa.T)
+    pb = lisa.make_problem(db["q"], db["v"], grid=(wb.H, wb.W), T=wb.T)
+    size = max(lisa.lisa_workspace_size(pa), lisa.lisa_workspace_size(pb))
+    ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+    ya1 = gpu_y(lisa, da, workspace=ws)
+    yb1 = gpu_y(lisa, db, workspace=ws)
+    ya2 = gpu_y(lisa, da, workspace=ws)
+    yb2 = gpu_y(lisa, db, workspace=ws)
+    assert torch.equal(ya1, ya2) and torch.equal(yb1, yb2)
+    check(yb2, oracle_y(xb), "bf16", "reuse 70x70")
+
+
+def test_side_stream(lisa):
+    w = workloads.get("deit_t_224")
+    x = workloads.make_inputs(w)
+    d = to_dev(x)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y = lisa.lisa_forward(d["q"], d["k"], d["v"], grid=(w.H, w.W), T=w.T, alpha=d["alpha"],
+                              weights=d["weights"], eps=w.eps)
+    s.synchronize()
+    check(y, oracle_y(x), "bf16", "side stream")
+
+
+@pytest.mark.parametrize("name", ["pvt_t_stage1", "long_range_200x320"])
+def test_constant_values_give_constant_output(lisa, name):
+    """V = 1 gives Y = 1 up to eps r_i (row sums of S) and bf16 rounding."""
+    w = workloads.get(name)
+    x = workloads.make_inputs(w)
+    x["v"] = torch.ones_like(x["v"])
+    y = f64(gpu_y(lisa, to_dev(x)))
+    assert np.max(np.abs(y - 1.0)) <= 2.0**-8
+
+
+def test_output_invariant_to_scaling_of_q_and_k_in_global_branch(lisa):
+    """alpha = 1: the global branch ignores the scale of Q and of K (up to eps)."""
+    w = workloads.small("scale", 2, 2, 8, 9, 4, dtype="fp32", alpha=1.0, seed=3)
+    x = workloads.make_inputs(w)
+    y1 = f64(gpu_y(lisa, to_dev(x)))
+    xs = dict(x, q=x["q"] * 4.0, k=x["k"] * 0.25)
+    y2 = f64(gpu_y(lisa, to_dev(xs)))
+    assert np.linalg.norm(y1 - y2) / np.linalg.norm(y1) < 1e-5
