@@ -1,0 +1,348 @@
+"""LiSA forward throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one lisa_forward call (statistics sweeps + fused output pass) over
+one batch of synthetic inputs already resident in HBM.  Input sets rotate over
+more than twice the 256 MB Infinity Cache so every call starts cold.  Prints
+one JSON line: token-heads/s (B*heads*n per second), the roofline of the
+dominant kernel (measured with HIP events on the stream it runs on), and the
+CPU oracle timed on a bounded sample on the host cores.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LiSA fwd tokens/s (B·heads·n) at T=3, % of HBM roofline, 1 MI355X"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+DEFAULT_WORKLOAD = "pvt_t_stage1"
+ROTATE_BYTES = 600 << 20
+COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+KERNEL_SOURCES = [
+    os.path.join(ROOT, "vision_transformer_token_amd", "csrc", f)
+    for f in ("lisa_kernels.hip", "lisa_kernels.hpp", "lisa_api.hip")
+]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def compulsory_bytes_per_token_head(w):
+    """Q, K, V read once, Y written once, adaptive weights read once."""
+    esize = 2 if w.dtype == "bf16" else 4
+    b = (2 * w.d_h + w.d_v) * esize + w.d_v * esize
+    if w.mode == "adaptive":
+        b += 4 * w.T
+    return b
+
+
+def cpu_baseline(w, x, budget_s=10.0):
+    """The fp64 NumPy oracle, as it stands, on a bounded sample of the workload."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    f64 = lambda t: None if t is None else t.double().numpy()  # noqa: E731
+    q, k, v, wt, al = f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["weights"]), f64(x["alpha"])
+    # Sample: whole batch entries in turn (cycling), until the time budget is spent.
+    nslice = 0
+    th = 0
+    t0 = time.perf_counter()
+    b = 0
+    while time.perf_counter() - t0 < budget_s:
+        oracle.lisa_forward(q[b:b + 1], k[b:b + 1], v[b:b + 1], H=w.H, W=w.W, T=w.T, alpha=al,
+                            weights=None if wt is None else wt[b:b + 1], beta=x["beta"], eps=w.eps)
+        nslice += w.heads
+        th += w.heads * w.n
+        b = (b + 1) % w.B
+    dt = time.perf_counter() - t0
+    return {
+        "value": th / dt,
+        "unit": "token-heads/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{nslice} (batch, head) slices of {w.name} ({w.B * w.heads} per step), "
+                  f"fp64 NumPy, {dt:.1f} s",
+    }
+
+
+def load_counters(w, kernel):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if current."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = c.get("kernels", {}).get(f"{kernel}@{w.name}")
+    if not entry or c.get("source_hash") != kernel_source_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def _csv_rows(path):
+    import csv
+
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _short(name):
+    for key in ("stats_kernel", "output_kernel", "copyBuffer"):
+        if key in name:
+            if key == "stats_kernel":
+                return "stats_kernel<M>" if "true>" in name else "stats_kernel<KV>"
+            return key
+    return name[:60]
+
+
+def summarize_profiles(outdir, workload, commands):
+    """Turn rocprofv3 CSV output (kernel trace + FETCH_SIZE/WRITE_SIZE passes of
+    bench.py and of the plain-copy calibration) into profiles/ summaries."""
+    w = None
+    from vision_transformer_token_amd import workloads
+
+    w = workloads.get(workload)
+    stats = _csv_rows(os.path.join(outdir, "prof_trace", "trace_kernel_stats.csv"))
+    lines = [f"# rocprofv3 kernel trace, workload {w.describe()}", "",
+             f"command: {commands['trace']}", "",
+             "| kernel | calls | average ns | min ns | max ns | share |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                     f"{r['MinNs']} | {r['MaxNs']} | {float(r['Percentage']):.1f}% |")
+
+    def per_kernel(sub, stem, counter):
+        rows = _csv_rows(os.path.join(outdir, sub, f"{stem}_counter_collection.csv"))
+        acc = {}
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    fetch = per_kernel("pmc_fetch", "fetch", "FETCH_SIZE")
+    write = per_kernel("pmc_write", "write", "WRITE_SIZE")
+    cfetch = per_kernel("pmc_copy_fetch", "cfetch", "FETCH_SIZE")["copyBuffer"]
+    cwrite = per_kernel("pmc_copy_write", "cwrite", "WRITE_SIZE")["copyBuffer"]
+    copy_kib = commands["copy_mib"] * 1024
+    f_scale, w_scale = copy_kib / cfetch, copy_kib / cwrite
+    lines += ["", "# HBM traffic per launch (rocprofv3 --pmc, one counter per pass)", "",
+              f"fetch pass: {commands['fetch']}", f"write pass: {commands['write']}",
+              f"copy calibration: {commands['copy']} (FETCH_SIZE then WRITE_SIZE)", "",
+              f"A plain device copy of {commands['copy_mib']} MiB reads FETCH_SIZE = {cfetch:.0f} KiB "
+              f"and WRITE_SIZE = {cwrite:.0f} KiB per dispatch, so FETCH_SIZE is scaled by "
+              f"{f_scale:.3f} and WRITE_SIZE by {w_scale:.3f}.", "",
+              "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) |", "|---|---|---|---|"]
+    entries = {}
+    for k in sorted(set(fetch) & set(write)):
+        if k == "copyBuffer":
+            continue
+        hbm = fetch[k] * 1024 * f_scale + write[k] * 1024 * w_scale
+        entries[f"{k}@{w.name}"] = {"fetch_kib": fetch[k], "write_kib": write[k],
+                                    "hbm_bytes_per_launch": hbm}
+        lines.append(f"| {k} | {fetch[k]:.0f} | {write[k]:.0f} | {hbm / 1e6:.2f} MB |")
+    lines += ["", f"algorithmic bytes per forward: {w.token_heads * compulsory_bytes_per_token_head(w) / 1e6:.2f} MB",
+              f"kernel source hash: {kernel_source_hash()}"]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"lisa_forward_{w.name}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        c = {}
+    if c.get("source_hash") != kernel_source_hash():
+        c = {"source_hash": kernel_source_hash(), "kernels": {}}
+    c["kernels"].update(entries)
+    c["copy_calibration"] = {"fetch_scale": f_scale, "write_scale": w_scale}
+    with open(COUNTERS, "w") as f:
+        json.dump(c, f, indent=1)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="instead of LiSA, run 20 plain device copies of this many MiB "
+                         "(the known-size kernel that scales the FETCH_SIZE/WRITE_SIZE counters)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write profiles/ summaries from rocprofv3 output under DIR and exit")
+    args = ap.parse_args()
+
+    if args.summarize_profiles:
+        fixed = "python3 bench.py --steps {s} --warmup {w} --no-cpu-baseline --workload " + args.workload
+        summarize_profiles(args.summarize_profiles, args.workload, {
+            "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace "
+                     "-o trace -- " + fixed.format(s=200, w=20),
+            "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o fetch -- "
+                     + fixed.format(s=10, w=2),
+            "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o write -- "
+                     + fixed.format(s=10, w=2),
+            "copy": "rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE --output-format csv -d gpurun_out/pmc_copy_{fetch|write} "
+                    "-o c{fetch|write} -- python3 bench.py --calibrate-copy-mib 256",
+            "copy_mib": 256,
+        })
+        return
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the LiSA path "
+              "shards by (batch, head) or by grid-row bands without collectives in this build.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from vision_transformer_token_amd import lisa, workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    if args.calibrate_copy_mib:
+        nbytes = args.calibrate_copy_mib << 20
+        src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(20):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": 20}))
+        return
+    w = workloads.get(args.workload)
+    x = workloads.make_inputs(w)
+    stream = torch.cuda.Stream(dev)
+
+    # Q, K, V, Y and the adaptive weights of one input set.
+    per_set = sum(t.numel() * t.element_size() for t in (x["q"], x["k"], x["v"], x["v"])
+                  ) + (0 if x["weights"] is None else x["weights"].numel() * 4)
+    nsets = max(2, -(-ROTATE_BYTES // per_set))
+    sets = []
+    with torch.cuda.stream(stream):
+        for _ in range(nsets):
+            d = {key: (x[key].to(dev) if x[key] is not None else None)
+                 for key in ("q", "k", "v", "weights", "alpha")}
+            d["y"] = torch.empty_like(d["v"])
+            sets.append(d)
+        prob = lisa.make_problem(sets[0]["q"], sets[0]["v"], grid=(w.H, w.W), T=w.T, eps=w.eps)
+        ws = lisa.new_workspace(prob, dev)
+    torch.cuda.synchronize()
+
+    def forward(d):
+        lisa.lisa_forward(d["q"], d["k"], d["v"], grid=(w.H, w.W), T=w.T, alpha=d["alpha"],
+                          weights=d["weights"], beta=x["beta"], eps=w.eps, out=d["y"], workspace=ws,
+                          stream=stream)
+
+    def reduce(d):
+        lisa.lisa_reduce(d["q"], d["k"], d["v"], grid=(w.H, w.W), eps=w.eps, T=w.T, workspace=ws,
+                         outputs=False, stream=stream)
+
+    def apply(d):
+        lisa.lisa_apply(d["q"], d["k"], d["v"], grid=(w.H, w.W), T=w.T, alpha=d["alpha"],
+                        weights=d["weights"], beta=x["beta"], eps=w.eps, out=d["y"], workspace=ws,
+                        stream=stream)
+
+    for i in range(args.warmup):
+        forward(sets[i % nsets])
+    torch.cuda.synchronize()
+
+    # Timed region: K whole forward passes.
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        forward(sets[i % nsets])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / args.steps
+
+    # Same K steps as two stages, with events around each on the same stream:
+    # the dominant (output) kernel's average launch duration.
+    split = w.T >= 3
+    kernel_ms = stats_ms = None
+    if split:
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            d = sets[i % nsets]
+            ev[i][0].record(stream)
+            reduce(d)
+            ev[i][1].record(stream)
+            apply(d)
+            ev[i][2].record(stream)
+        torch.cuda.synchronize()
+        stats_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
+        kernel_ms = sum(b.elapsed_time(c) for _, b, c in ev) / args.steps
+
+    th = w.token_heads
+    bpt = compulsory_bytes_per_token_head(w)
+    value = th / (step_ms * 1e-3)
+    path_gbs = th * bpt / (step_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "token-heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "B": w.B,
+            "heads": w.heads,
+            "grid": f"{w.H}x{w.W}",
+            "n": w.n,
+            "d_h": w.d_h,
+            "d_v": w.d_v,
+            "T": w.T,
+            "weights": w.mode,
+            "token_heads": th,
+            "rotating_input_sets": nsets,
+        },
+        "path_roofline_frac": path_gbs / HBM_PEAK_GBS,
+    }
+    if kernel_ms is not None:
+        achieved = th * bpt / (kernel_ms * 1e-3) / 1e9
+        traffic = load_counters(w, "output_kernel")
+        out["roofline"] = {
+            "bound": "hbm",
+            "kernel": "output_kernel",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "kernel_ms": kernel_ms,
+            "algorithmic_bytes_per_launch": th * bpt,
+        }
+        out["stages_ms"] = {"statistics": stats_ms, "output": kernel_ms}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
