@@ -27,7 +27,7 @@ ROTATE_BYTES = 600 << 20
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 KERNEL_SOURCES = [
     os.path.join(ROOT, "vision_transformer_token_amd", "csrc", f)
-    for f in ("lisa_kernels.hip", "lisa_kernels.hpp", "lisa_api.hip")
+    for f in ("lisa_flow.hip", "lisa_device.hpp", "lisa_kernels.hpp", "lisa_api.hip")
 ]
 
 

@@ -12,29 +12,23 @@
 
 namespace {
 
-using lisa::kCellStride;
-using lisa::kCntWords;
 using lisa::kD;
-using lisa::kGroup;
-using lisa::kMaxChunks;
-using lisa::kStatTile;
+using lisa::kThreads;
 
 constexpr size_t kAlign = 256;
-constexpr size_t kMaxOutLds = 64 * 1024;
+constexpr size_t kMaxSlices = 65535;  // batch * heads limit
 
 size_t up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Plan {
   int BH = 0, n = 0, H = 0, W = 0, T = 0, dtype = 0, heads = 0;
   size_t esize = 0;
-  // statistics sweeps
-  int chunk = 0, P = 0, ngroups = 0;
-  // output tiles
-  int TR = 0, TC = 0, tiles_x = 0, ntiles = 0;
-  size_t lds = 0;
+  int chunk = 0, P = 0;                          // statistics items per slice
+  int TR = 0, TC = 0, tiles_x = 0, ntiles = 0;   // output tiles per slice
+  int nq = 1;                                    // work queues
   // workspace layout (byte offsets)
-  size_t cnt_kv = 0, cnt_m = 0, part_s = 0, part_kv = 0, part_m = 0, gpart_s = 0, gpart_kv = 0,
-         gpart_m = 0, fin_s = 0, fin_kv = 0, fin_m = 0, frag_kv = 0, frag_m = 0, total = 0;
+  size_t slice_cnt = 0, queue_cnt = 0, part_s = 0, part_kv = 0, part_m = 0, fin_s = 0, fin_kv = 0,
+         fin_m = 0, frag_kv = 0, frag_m = 0, total = 0;
 };
 
 lisa_status check_problem(const lisa_problem* p) {
@@ -45,29 +39,26 @@ lisa_status check_problem(const lisa_problem* p) {
     return LISA_ERR_SHAPE;
   if ((int64_t)p->grid_h * p->grid_w > (int64_t(1) << 24)) return LISA_ERR_SHAPE;
   if (p->d_h != kD || p->d_v != kD) return LISA_ERR_UNSUPPORTED;
-  if ((int64_t)p->batch * p->heads > 65535) return LISA_ERR_UNSUPPORTED;
+  if ((int64_t)p->batch * p->heads > (int64_t)kMaxSlices) return LISA_ERR_UNSUPPORTED;
   if (p->T < 1 || p->T > lisa::kMaxT) return LISA_ERR_PARAM;
   if (!std::isfinite(p->eps) || !(p->eps > 0.f)) return LISA_ERR_PARAM;
   return LISA_OK;
 }
 
 // Output tile: whole grid rows when the grid is at most 64 wide, else
-// 32-column strips; as many rows as fit the LDS budget (tile plus one-cell
-// halo of K and V), at most 256 tokens.
+// 32-column strips; as many rows as one LDS staging buffer holds with a
+// one-cell halo of K and V, at most kMaxTileTokens tokens.
 void plan_tiles(Plan& pl) {
-  const size_t cell_bytes = 2 * kCellStride * pl.esize;  // K and V
-  const int max_cells = (int)(kMaxOutLds / cell_bytes);
+  const int max_cells = lisa::kBufBytes / 2 / (int)(kD * pl.esize);
   pl.TC = pl.W <= 64 ? pl.W : 32;
-  if (pl.TC > max_cells / 3 - 2) pl.TC = max_cells / 3 - 2;  // at least one row with halo
+  if (pl.TC > max_cells / 3 - 2) pl.TC = max_cells / 3 - 2;
   int tr = max_cells / (pl.TC + 2) - 2;
   if (tr < 1) tr = 1;
-  while (tr > 1 && tr * pl.TC > 256) --tr;
+  while (tr > 1 && tr * pl.TC > lisa::kMaxTileTokens) --tr;
   if (tr > pl.H) tr = pl.H;
   pl.TR = tr;
   pl.tiles_x = (pl.W + pl.TC - 1) / pl.TC;
-  const int tiles_y = (pl.H + pl.TR - 1) / pl.TR;
-  pl.ntiles = pl.tiles_x * tiles_y;
-  pl.lds = (size_t)(pl.TR + 2) * (pl.TC + 2) * cell_bytes;
+  pl.ntiles = pl.tiles_x * ((pl.H + pl.TR - 1) / pl.TR);
 }
 
 lisa_status make_plan(const lisa_problem* p, Plan& pl) {
@@ -81,20 +72,14 @@ lisa_status make_plan(const lisa_problem* p, Plan& pl) {
   pl.T = p->T;
   pl.dtype = p->dtype;
   pl.esize = p->dtype == LISA_BF16 ? 2 : 4;
-
-  // Statistics chunks: 256 tokens per workgroup, larger when a slice would
-  // need more than kMaxChunks chunks.
-  int chunk = 256;
-  if ((pl.n + chunk - 1) / chunk > kMaxChunks) {
-    chunk = (pl.n + kMaxChunks - 1) / kMaxChunks;
-    chunk = (chunk + kStatTile - 1) / kStatTile * kStatTile;
-  }
-  pl.chunk = chunk;
-  pl.P = (pl.n + chunk - 1) / chunk;
-  pl.ngroups = (pl.P + kGroup - 1) / kGroup;
+  // Statistics items: one LDS buffer holds the chunk's K rows and V (or Q) rows.
+  // (a multiple of 16 tokens: the MFMA sweep reads whole 16-row steps).
+  pl.chunk = pl.esize == 2 ? 256 : 128;
+  pl.P = (pl.n + pl.chunk - 1) / pl.chunk;
   plan_tiles(pl);
+  pl.nq = (pl.BH % lisa::kMaxQueues == 0) ? lisa::kMaxQueues : 1;
 
-  const size_t BH = pl.BH, P = pl.P, NG = pl.ngroups > 1 ? pl.ngroups : 0;
+  const size_t BH = pl.BH, P = pl.P;
   const size_t mat = kD * kD * sizeof(float), vec = kD * sizeof(float);
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -102,14 +87,14 @@ lisa_status make_plan(const lisa_problem* p, Plan& pl) {
     o = up(o + bytes, kAlign);
     return at;
   };
-  pl.cnt_kv = take(BH * kCntWords * sizeof(unsigned));
-  pl.cnt_m = take(BH * kCntWords * sizeof(unsigned));
+  // Counters first, at offsets and sizes that do not depend on the problem:
+  // a workspace reused by problems of other shapes never has another
+  // problem's data written over a counter (each call leaves them at zero).
+  pl.queue_cnt = take(32 * sizeof(unsigned));
+  pl.slice_cnt = take((size_t)kMaxSlices * 4 * sizeof(unsigned));
   pl.part_s = take(BH * P * vec);
   pl.part_kv = take(BH * P * mat);
   pl.part_m = take(BH * P * mat);
-  pl.gpart_s = take(BH * NG * vec);
-  pl.gpart_kv = take(BH * NG * mat);
-  pl.gpart_m = take(BH * NG * mat);
   pl.fin_s = take(BH * vec);
   pl.fin_kv = take(BH * mat);
   pl.fin_m = take(BH * mat);
@@ -151,51 +136,19 @@ lisa_status check_forward(const lisa_problem* p, const void* Q, const void* K, c
   return LISA_OK;
 }
 
-lisa::StatsArgs stats_args(const Plan& pl, char* ws, const void* K, const void* X, float eps,
-                           bool m_stage) {
-  lisa::StatsArgs a{};
-  a.K = K;
-  a.X = X;
-  a.n = pl.n;
-  a.chunk = pl.chunk;
-  a.P = pl.P;
-  a.ngroups = pl.ngroups;
-  a.eps = eps;
-  a.part = reinterpret_cast<float*>(ws + (m_stage ? pl.part_m : pl.part_kv));
-  a.part_s = reinterpret_cast<float*>(ws + pl.part_s);
-  a.gpart = reinterpret_cast<float*>(ws + (m_stage ? pl.gpart_m : pl.gpart_kv));
-  a.gpart_s = reinterpret_cast<float*>(ws + pl.gpart_s);
-  a.s_in = reinterpret_cast<const float*>(ws + pl.fin_s);
-  a.fin = reinterpret_cast<float*>(ws + (m_stage ? pl.fin_m : pl.fin_kv));
-  a.fin_s = reinterpret_cast<float*>(ws + pl.fin_s);
-  a.frag = ws + (m_stage ? pl.frag_m : pl.frag_kv);
-  a.cnt = reinterpret_cast<unsigned*>(ws + (m_stage ? pl.cnt_m : pl.cnt_kv));
-  return a;
-}
+enum class Mode { kForward, kReduce, kApply };
 
-lisa_status run_stats(const Plan& pl, const void* Q, const void* K, const void* V, char* ws,
-                      float eps, bool need_m, hipStream_t s) {
-  if (lisa::launch_stats_kv(pl.dtype, stats_args(pl, ws, K, V, eps, false), pl.BH, s) != hipSuccess)
-    return LISA_ERR_HIP;
-  if (need_m &&
-      lisa::launch_stats_m(pl.dtype, stats_args(pl, ws, K, Q, eps, true), pl.BH, s) != hipSuccess)
-    return LISA_ERR_HIP;
-  return LISA_OK;
-}
-
-lisa_status run_output(const Plan& pl, const void* Q, const void* K, const void* V,
-                       const float* weights, float beta, const float* alpha, void* Y, char* ws,
-                       float eps, hipStream_t s) {
-  lisa::OutArgs a{};
+// One launch of the persistent kernel, one workgroup per compute unit.
+lisa_status run(const Plan& pl, Mode mode, const void* Q, const void* K, const void* V,
+                const float* weights, float beta, const float* alpha, void* Y, char* ws, float eps,
+                hipStream_t s) {
+  lisa::FlowArgs a{};
   a.Q = Q;
   a.K = K;
   a.V = V;
   a.weights = weights;
   a.alpha = alpha;
   a.Y = Y;
-  a.s = reinterpret_cast<const float*>(ws + pl.fin_s);
-  a.frag_kv = ws + pl.frag_kv;
-  a.frag_m = ws + pl.frag_m;
   // Geometric weights w_k = (1-beta) beta^k / (1-beta^T) in double, rounded once.
   const double b = weights ? 0.0 : (double)beta;
   const double norm = (1.0 - b) / (1.0 - std::pow(b, pl.T));
@@ -205,12 +158,41 @@ lisa_status run_output(const Plan& pl, const void* Q, const void* K, const void*
   a.n = pl.n;
   a.T = pl.T;
   a.heads = pl.heads;
+  a.BH = pl.BH;
+  a.eps = eps;
+  a.logit_scale = (float)(1.4426950408889634 / std::sqrt((double)kD));
+  a.chunk = pl.chunk;
+  a.P = pl.P;
   a.TR = pl.TR;
   a.TC = pl.TC;
   a.tiles_x = pl.tiles_x;
-  a.eps = eps;
-  a.logit_scale = (float)(1.4426950408889634 / std::sqrt((double)kD));
-  if (lisa::launch_output(pl.dtype, a, pl.BH, pl.ntiles, pl.lds, s) != hipSuccess) return LISA_ERR_HIP;
+  const bool stats = mode == Mode::kReduce || (mode == Mode::kForward && pl.T >= 2);
+  const bool need_m = mode == Mode::kReduce || (mode == Mode::kForward && pl.T >= 3);
+  a.nKV = stats ? pl.P : 0;
+  a.nM = need_m ? pl.P : 0;
+  a.nC = stats ? (need_m ? 2 : 1) * lisa::kCombineBlocks : 0;
+  a.nOUT = mode == Mode::kReduce ? 0 : pl.ntiles;
+  a.wait_out = (mode == Mode::kForward && stats) ? 1 : 0;
+  a.nq = pl.nq;
+  a.part_s = reinterpret_cast<float*>(ws + pl.part_s);
+  a.part_kv = reinterpret_cast<float*>(ws + pl.part_kv);
+  a.part_m = reinterpret_cast<float*>(ws + pl.part_m);
+  a.fin_s = reinterpret_cast<float*>(ws + pl.fin_s);
+  a.fin_kv = reinterpret_cast<float*>(ws + pl.fin_kv);
+  a.fin_m = reinterpret_cast<float*>(ws + pl.fin_m);
+  a.frag_kv = ws + pl.frag_kv;
+  a.frag_m = ws + pl.frag_m;
+  a.slice_cnt = reinterpret_cast<unsigned*>(ws + pl.slice_cnt);
+  a.queue_cnt = reinterpret_cast<unsigned*>(ws + pl.queue_cnt);
+  a.err = a.queue_cnt + 17;
+
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return LISA_ERR_HIP;
+  int grid = cus / lisa::kMaxQueues * lisa::kMaxQueues;
+  if (grid < lisa::kMaxQueues) grid = lisa::kMaxQueues;
+  if (lisa::launch_flow(pl.dtype, a, grid, s) != hipSuccess) return LISA_ERR_HIP;
   return LISA_OK;
 }
 
@@ -227,16 +209,11 @@ lisa_status lisa_forward(const lisa_problem* p, const void* Q, const void* K, co
                          const float* weights, float beta, const float* alpha, void* Y,
                          void* workspace, size_t workspace_bytes, void* stream) {
   Plan pl;
-  lisa_status st = check_forward(p, Q, K, V, weights, beta, alpha, Y, workspace, workspace_bytes, pl);
+  const lisa_status st = check_forward(p, Q, K, V, weights, beta, alpha, Y, workspace, workspace_bytes, pl);
   if (st != LISA_OK) return st;
   (void)hipGetLastError();  // clear a stale error so that ours are reported alone
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  if (pl.T >= 2) {
-    st = run_stats(pl, Q, K, V, ws, p->eps, pl.T >= 3, s);
-    if (st != LISA_OK) return st;
-  }
-  return run_output(pl, Q, K, V, weights, beta, alpha, Y, ws, p->eps, s);
+  return run(pl, Mode::kForward, Q, K, V, weights, beta, alpha, Y, static_cast<char*>(workspace),
+             p->eps, static_cast<hipStream_t>(stream));
 }
 
 lisa_status lisa_reduce(const lisa_problem* p, const void* Q, const void* K, const void* V,
@@ -254,7 +231,7 @@ lisa_status lisa_reduce(const lisa_problem* p, const void* Q, const void* K, con
   (void)hipGetLastError();
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  st = run_stats(pl, Q, K, V, ws, p->eps, true, s);
+  st = run(pl, Mode::kReduce, Q, K, V, nullptr, 0.f, nullptr, nullptr, ws, p->eps, s);
   if (st != LISA_OK) return st;
   const size_t mat = (size_t)pl.BH * kD * kD * sizeof(float), vec = (size_t)pl.BH * kD * sizeof(float);
   if (s_out && hipMemcpyAsync(s_out, ws + pl.fin_s, vec, hipMemcpyDeviceToDevice, s) != hipSuccess)
@@ -270,11 +247,11 @@ lisa_status lisa_apply(const lisa_problem* p, const void* Q, const void* K, cons
                        const float* weights, float beta, const float* alpha, void* Y,
                        void* workspace, size_t workspace_bytes, void* stream) {
   Plan pl;
-  lisa_status st = check_forward(p, Q, K, V, weights, beta, alpha, Y, workspace, workspace_bytes, pl);
+  const lisa_status st = check_forward(p, Q, K, V, weights, beta, alpha, Y, workspace, workspace_bytes, pl);
   if (st != LISA_OK) return st;
   (void)hipGetLastError();
-  return run_output(pl, Q, K, V, weights, beta, alpha, Y, static_cast<char*>(workspace), p->eps,
-                    static_cast<hipStream_t>(stream));
+  return run(pl, Mode::kApply, Q, K, V, weights, beta, alpha, Y, static_cast<char*>(workspace), p->eps,
+             static_cast<hipStream_t>(stream));
 }
 
 const char* lisa_status_str(lisa_status s) {

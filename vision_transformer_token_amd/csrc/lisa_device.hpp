@@ -1,0 +1,170 @@
+// Device helpers shared by the gfx950 kernels: element traits, MFMA wrappers,
+// the accumulator-layout feature map (dimof), conversions, swizzled LDS
+// addressing for DMA-staged rows, and the fence-free cross-workgroup hand-off.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lisa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Element traits.  EPL: contraction slots per lane in one MFMA; NQ: MFMAs to
+// contract over 64; EPP: elements per 16-byte piece; PPR: pieces per 64-wide
+// row; RB: bytes per row.
+struct BF16 {
+  using S = uint16_t;
+  using Frag = bf16x8;
+  static constexpr int EPL = 8, NQ = 4, EPP = 8, PPR = 8, RB = 128;
+};
+struct F32 {
+  using S = float;
+  using Frag = float;
+  static constexpr int EPL = 1, NQ = 32, EPP = 4, PPR = 16, RB = 256;
+};
+
+__device__ __forceinline__ uint16_t f2bf(float x) {
+  __bf16 h = (__bf16)x;  // round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mma(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// MFMA 32x32 layouts (lane l, m = l % 32, h = l / 32): operand A[m][k-slot],
+// B[k-slot][m] with k-slots 8h + e (bf16, e < 8) or h (fp32); accumulator
+// element i holds C[8 (i / 4) + 4 h + i % 4][m].  A 64-vector is kept "in
+// accumulator layout" as 32 slots per lane: slot v of a lane of half h holds
+// feature dimof(v, h); slots 0..15 are the first 32x32 block's accumulators.
+__device__ __forceinline__ int dimof(int v, int h) {
+  return 32 * (v >> 4) + 8 * ((v >> 2) & 3) + 4 * h + (v & 3);
+}
+
+// MFMA B operand from slots q*EPL .. q*EPL+EPL-1 of a 32-slot fp32 vector.
+__device__ __forceinline__ bf16x8 operand(const float (&u)[32], int q, BF16) {
+  bf16x8 b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) b[e] = (__bf16)u[8 * q + e];
+  return b;
+}
+__device__ __forceinline__ float operand(const float (&u)[32], int q, F32) { return u[q]; }
+
+// y = x X for x in accumulator layout and X given as A-operand fragments:
+// fragment (mb, q, lane, e) = X[dimof(q*EPL + e, lane/32)][32 mb + lane%32].
+// Because a contraction index may be permuted as long as A and B agree, the
+// accumulator slots of x feed the B operand directly.
+template <class Tr>
+__device__ __forceinline__ void apply(const typename Tr::Frag (&fr)[2][Tr::NQ], const float (&x)[32],
+                                      float (&y)[32]) {
+  f32x16 c0 = {}, c1 = {};
+#pragma unroll
+  for (int q = 0; q < Tr::NQ; ++q) {
+    auto b = operand(x, q, Tr{});
+    c0 = mma(fr[0][q], b, c0);
+    c1 = mma(fr[1][q], b, c1);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    y[i] = c0[i];
+    y[16 + i] = c1[i];
+  }
+}
+
+// Four consecutive elements (8 B bf16 / 16 B fp32) -> floats, and back.
+__device__ __forceinline__ void load4(const uint16_t* p, float* x) {
+  uint2 w = *reinterpret_cast<const uint2*>(p);
+  x[0] = __uint_as_float(w.x << 16);
+  x[1] = __uint_as_float(w.x & 0xffff0000u);
+  x[2] = __uint_as_float(w.y << 16);
+  x[3] = __uint_as_float(w.y & 0xffff0000u);
+}
+__device__ __forceinline__ void load4(const float* p, float* x) {
+  float4 w = *reinterpret_cast<const float4*>(p);
+  x[0] = w.x;
+  x[1] = w.y;
+  x[2] = w.z;
+  x[3] = w.w;
+}
+__device__ __forceinline__ void store4(uint16_t* p, const float* x) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(f2bf(x[0]) | ((uint32_t)f2bf(x[1]) << 16),
+                                            f2bf(x[2]) | ((uint32_t)f2bf(x[3]) << 16));
+}
+__device__ __forceinline__ void store4(float* p, const float* x) {
+  *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+}
+
+// ---------------------------------------------------------------------------
+// Swizzled LDS rows.  A staged 64-wide row (a token's features, or a grid
+// cell) occupies RB bytes split into PPR 16-byte pieces; piece g of row r
+// sits in slot g ^ swz(r), which spreads the lanes of the gathers below over
+// the LDS banks.  Rows are written by global_load_lds DMA, one 1 KB run of
+// 64 pieces per wave instruction, each lane fetching the piece that belongs
+// in its slot.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ (((r >> 3) & 1) << 2); }
+
+template <class Tr>
+__device__ __forceinline__ int row_off(int r, int d) {  // byte offset of element d of row r
+  constexpr int SH = Tr::EPP == 8 ? 3 : 2;             // log2(elements per piece)
+  constexpr int ES = (int)sizeof(typename Tr::S);
+  return r * Tr::RB + ((((d >> SH) ^ swz(r)) & (Tr::PPR - 1)) << 4) + (d & (Tr::EPP - 1)) * ES;
+}
+
+// DMA `nrow` rows into `lds` (a multiple of 1 KB is written: the last run is
+// padded with copies of row nrow-1).  src(r) returns the global address of
+// row r (16-byte aligned).  Every wave takes every 4th run; no wait here.
+template <class Tr, class SrcFn>
+__device__ __forceinline__ void dma_rows(unsigned char* lds, int nrow, SrcFn src) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int npieces = nrow * Tr::PPR;
+  for (int base = wave * 64; base < npieces; base += 64 * 4) {
+    const int P = base + lane;
+    const int r = min(P / Tr::PPR, nrow - 1);
+    const int slot = P % Tr::PPR;
+    const int g = (slot ^ swz(P / Tr::PPR)) & (Tr::PPR - 1);
+    const unsigned char* gp = static_cast<const unsigned char*>(src(r)) + g * 16;
+    __builtin_amdgcn_global_load_lds(gp, (lds_ptr_t)(lds + base * 16), 16, 0, 0);
+  }
+}
+// Bytes that dma_rows writes for nrow rows.
+__host__ __device__ constexpr int dma_bytes(int nrow, int row_bytes) {
+  return (nrow * row_bytes + 1023) / 1024 * 1024;
+}
+
+// ---------------------------------------------------------------------------
+// Cross-workgroup hand-off without cache-wide fences: data shared between
+// workgroups of one launch is written and read with relaxed agent-scope
+// atomics (coherent accesses that bypass the non-coherent per-XCD L2), the
+// writer waits for its stores to complete before bumping an arrival counter,
+// and the reader reads the data only after it has observed the count.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void put(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void put(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float get(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t get(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t get64(const void* p) {
+  return __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+__device__ __forceinline__ unsigned bump(unsigned* cnt) {
+  return __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace lisa
