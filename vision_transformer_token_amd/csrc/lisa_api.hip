@@ -45,17 +45,19 @@ lisa_status check_problem(const lisa_problem* p) {
   return LISA_OK;
 }
 
-// Output tile: whole grid rows when the grid is at most 64 wide, else
-// 32-column strips; as many rows as one LDS staging buffer holds with a
-// one-cell halo of K and V, at most kMaxTileTokens tokens.
+// Output tile: TR x TC cells made of whole 4 x 8 token blocks (the MFMA local
+// branch works on such blocks), 8..32 columns (at most 16 for fp32), as many
+// rows as one LDS staging buffer holds with a one-cell halo of K and V, at
+// most kMaxTileTokens tokens.
 void plan_tiles(Plan& pl) {
   const int max_cells = lisa::kBufBytes / 2 / (int)(kD * pl.esize);
-  pl.TC = pl.W <= 64 ? pl.W : 32;
-  if (pl.TC > max_cells / 3 - 2) pl.TC = max_cells / 3 - 2;
-  int tr = max_cells / (pl.TC + 2) - 2;
-  if (tr < 1) tr = 1;
-  while (tr > 1 && tr * pl.TC > lisa::kMaxTileTokens) --tr;
-  if (tr > pl.H) tr = pl.H;
+  const int tc_max = pl.esize == 2 ? 32 : 16;
+  pl.TC = (pl.W + 7) / 8 * 8;
+  if (pl.TC > tc_max) pl.TC = tc_max;
+  int tr = (max_cells / (pl.TC + 2) - 2) / 4 * 4;
+  while (tr > 4 && tr * pl.TC > lisa::kMaxTileTokens) tr -= 4;
+  const int h4 = (pl.H + 3) / 4 * 4;
+  if (tr > h4) tr = h4;
   pl.TR = tr;
   pl.tiles_x = (pl.W + pl.TC - 1) / pl.TC;
   pl.ntiles = pl.tiles_x * ((pl.H + pl.TR - 1) / pl.TR);

@@ -140,6 +140,45 @@ __host__ __device__ constexpr int dma_bytes(int nrow, int row_bytes) {
 }
 
 // ---------------------------------------------------------------------------
+// Operands whose contraction index runs over staged rows.  gfx950's
+// ds_read_b64_tr_b16 works on groups of 16 lanes: lane i of a group receives
+// element (i & 3) of the 8-byte chunks addressed by lanes (i >> 2) + 4k,
+// k = 0..3.  With each source lane pointing at 4 columns of one row, two such
+// reads give lane (m, h) the MFMA operand X[row0 + 8h + e][col0 + m],
+// e = 0..7, of a bf16 32x32x16 product whose k runs over rows.
+// ---------------------------------------------------------------------------
+// Operand bits are kept in integer vectors and reinterpreted as bf16 only at
+// the MFMA: element-wise work on bf16 vectors rebuilt from such reads was
+// folded wrongly by the compiler in testing.
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ v4s tr_read(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p);
+}
+__device__ __forceinline__ v4s relu4(v4s x) { return __builtin_elementwise_max(x, (v4s)0); }
+__device__ __forceinline__ v8s join(v4s lo, v4s hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ bf16x8 as_bf16(v8s x) { return __builtin_bit_cast(bf16x8, x); }
+
+// Bits of X[row0 + 8h + e][col0 + m] (bf16 rows of a staged region), e = 0..7;
+// with kRelu the values are clamped at zero (a negative bf16 is a negative int16).
+template <bool kRelu>
+__device__ __forceinline__ v8s rows_bits(const unsigned char* base, int row0, int col0) {
+  const int L = threadIdx.x & 63, i = L & 15, g = L >> 4;
+  const int col = col0 + 16 * (g & 1) + 4 * (i & 3);
+  const int r = row0 + 8 * (g >> 1) + (i >> 2);
+  v4s lo = tr_read(base + row_off<BF16>(r, col));
+  v4s hi = tr_read(base + row_off<BF16>(r + 4, col));
+  if (kRelu) {
+    lo = relu4(lo);
+    hi = relu4(hi);
+  }
+  return join(lo, hi);
+}
+
+// ---------------------------------------------------------------------------
 // Cross-workgroup hand-off without cache-wide fences: data shared between
 // workgroups of one launch is written and read with relaxed agent-scope
 // atomics (coherent accesses that bypass the non-coherent per-XCD L2), the

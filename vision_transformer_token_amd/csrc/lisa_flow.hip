@@ -101,33 +101,29 @@ __device__ void stage(const FlowArgs& a, Item it, unsigned char* buf) {
   }
 }
 
-// Element d of staged row r as float (bf16 bits widened).
-__device__ __forceinline__ float lds_elem(const unsigned char* base, int r, int d, BF16) {
-  return bf2f(*reinterpret_cast<const uint16_t*>(base + row_off<BF16>(r, d)));
-}
+// Element d of staged fp32 row r.
 __device__ __forceinline__ float lds_elem(const unsigned char* base, int r, int d, F32) {
   return *reinterpret_cast<const float*>(base + row_off<F32>(r, d));
-}
-__device__ __forceinline__ uint16_t lds_bits(const unsigned char* base, int r, int d) {
-  return *reinterpret_cast<const uint16_t*>(base + row_off<BF16>(r, d));
 }
 
 // ---------------------------------------------------------------------------
 // KV / M items: contraction over the chunk's tokens.  Wave w owns block
 // (w / 2, w % 2) of the 64x64 result; A = phi(K) rows, B = V rows (KV) or
-// r_j phi(Q_j) rounded to the input dtype (M).  KV items also form s with a
-// second MFMA against a ones operand.
+// r_j phi(Q_j) rows rounded to the input dtype (M, rescaled in LDS first).
+// KV items also form s with a second MFMA against a ones operand.  Rows past
+// the chunk's last token are zeroed in LDS, so the sweep needs no masks.
 // ---------------------------------------------------------------------------
 template <class Tr, bool kIsM, class Prefetch>
-__device__ void stats_item(const FlowArgs& a, Item it, const unsigned char* buf, float* s_sh,
-                           float* r_sh, Prefetch prefetch) {
+__device__ void stats_item(const FlowArgs& a, Item it, unsigned char* buf, float* s_sh,
+                           Prefetch prefetch) {
+  using S = typename Tr::S;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 31, h = lane >> 5, mb = wave >> 1, nb = wave & 1;
   const int tok0 = it.idx * a.chunk;
   const int nv = min(a.chunk, a.n - tok0);
   const int nvr = (nv + 15) & ~15;
-  const unsigned char* bK = buf;
-  const unsigned char* bX = buf + kBufBytes / 2;
+  unsigned char* bK = buf;
+  unsigned char* bX = buf + kBufBytes / 2;
 
   if (kIsM && tid < kD) {  // s = sum of the KV items' partials, fixed order
     float t = 0.f;
@@ -135,61 +131,51 @@ __device__ void stats_item(const FlowArgs& a, Item it, const unsigned char* buf,
     s_sh[tid] = t;
   }
   prefetch();
-  if (kIsM) {
-    __syncthreads();
+  if (kIsM || nv < nvr) {
+    if (kIsM) __syncthreads();
     for (int t = tid; t < nvr; t += kThreads) {
-      float r = 0.f;
-      if (t < nv) {
+      if (t >= nv) {
+#pragma unroll
+        for (int g = 0; g < Tr::PPR; ++g) {
+          *reinterpret_cast<uint4*>(bK + t * Tr::RB + g * 16) = make_uint4(0, 0, 0, 0);
+          *reinterpret_cast<uint4*>(bX + t * Tr::RB + g * 16) = make_uint4(0, 0, 0, 0);
+        }
+      } else if (kIsM) {
+        // r_t = 1 / (phi(Q_t) . s + eps); the row becomes r_t phi(Q_t).
+        float x[kD];
+#pragma unroll
+        for (int c = 0; c < kD / 4; ++c) load4(reinterpret_cast<const S*>(bX + row_off<Tr>(t, 4 * c)), &x[4 * c]);
         float dot = 0.f;
-#pragma unroll 8
-        for (int d = 0; d < kD; ++d) dot += fmaxf(lds_elem(bX, t, d, Tr{}), 0.f) * s_sh[d];
-        r = 1.f / (dot + a.eps);
+#pragma unroll
+        for (int d = 0; d < kD; ++d) {
+          x[d] = fmaxf(x[d], 0.f);
+          dot += x[d] * s_sh[d];
+        }
+        const float r = 1.f / (dot + a.eps);
+#pragma unroll
+        for (int d = 0; d < kD; ++d) x[d] *= r;
+#pragma unroll
+        for (int c = 0; c < kD / 4; ++c) store4(reinterpret_cast<S*>(bX + row_off<Tr>(t, 4 * c)), &x[4 * c]);
       }
-      r_sh[t] = r;
     }
     __syncthreads();
   }
 
   f32x16 acc = {}, acc_s = {};
   for (int kk = 0; kk < nvr; kk += 16) {
-#pragma unroll
-    for (int q = 0; q < 8 / Tr::EPL; ++q) {
-      const int row0 = kk + 8 * h + q * Tr::EPL;
-      typename Tr::Frag A, B;
-      if constexpr (Tr::EPL == 8) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = row0 + e;
-          const uint16_t kb = lds_bits(bK, r, 32 * mb + m);
-          const bool in = r < nv;
-          A[e] = __builtin_bit_cast(__bf16, (uint16_t)((in && !(kb & 0x8000u)) ? kb : 0));
-          if (kIsM) {
-            const float xq = fmaxf(bf2f(lds_bits(bX, r, 32 * nb + m)), 0.f) * r_sh[r];
-            B[e] = (__bf16)(in ? xq : 0.f);
-          } else {
-            const uint16_t vb = lds_bits(bX, r, 32 * nb + m);
-            B[e] = __builtin_bit_cast(__bf16, (uint16_t)(in ? vb : 0));
-          }
-        }
-      } else {
-        const int r = row0;
-        const bool in = r < nv;
-        A = in ? fmaxf(lds_elem(bK, r, 32 * mb + m, Tr{}), 0.f) : 0.f;
-        if (kIsM)
-          B = in ? fmaxf(lds_elem(bX, r, 32 * nb + m, Tr{}), 0.f) * r_sh[r] : 0.f;
-        else
-          B = in ? lds_elem(bX, r, 32 * nb + m, Tr{}) : 0.f;
-      }
+    if constexpr (Tr::EPL == 8) {
+      const bf16x8 A = as_bf16(rows_bits<true>(bK, kk, 32 * mb));
+      const bf16x8 B = as_bf16(rows_bits<false>(bX, kk, 32 * nb));
       acc = mma(A, B, acc);
-      if (!kIsM && nb == 0) {
-        typename Tr::Frag one;
-        if constexpr (Tr::EPL == 8) {
+      if (!kIsM && nb == 0) acc_s = mma(A, as_bf16((v8s)(short)0x3f80), acc_s);  // ones: bf16 1.0
+    } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) one[e] = (__bf16)1.0f;
-        } else {
-          one = 1.f;
-        }
-        acc_s = mma(A, one, acc_s);
+      for (int q = 0; q < 8; ++q) {
+        const int r = kk + 8 * h + q;
+        const float A = fmaxf(lds_elem(bK, r, 32 * mb + m, Tr{}), 0.f);
+        const float B = lds_elem(bX, r, 32 * nb + m, Tr{});
+        acc = mma(A, B, acc);
+        if (!kIsM && nb == 0) acc_s = mma(A, 1.f, acc_s);
       }
     }
   }
@@ -313,25 +299,172 @@ __device__ __forceinline__ void load_frags(const void* frag, int b, typename Tr:
     }
 }
 
+// Local branch of one 4x8 token block on MFMA (bf16).  The block's 3x3
+// windows lie in a 6x10 window of staged cells (60, padded to 64).  Logits
+// C[cell][token] = K_win Q_blk^T come out with one token per lane pair and the
+// cells in accumulator order; after the masked softmax, those probabilities
+// are already the B operand of L^T = V_win^T P^T (the contraction index
+// permuted to match), whose A operand comes from transposed LDS reads, and L
+// lands in the same accumulator layout as the global branch.
+__device__ __forceinline__ void local_block_mfma(const FlowArgs& a, const unsigned char* cK,
+                                                 const unsigned char* cV, int CW, int r0, int c0,
+                                                 int br, int bc, const bf16x8 (&qB)[4], float (&L)[32]) {
+  const int lane = threadIdx.x & 63, n = lane & 31, h = lane >> 5;
+  const int i16 = lane & 15, g = lane >> 4;
+  auto wcell = [&](int c) {
+    c = min(c, 59);
+    return (4 * br + c / 10) * CW + 8 * bc + c % 10;
+  };
+  // Logits: A = K rows of window cells (16-byte pieces), B = this token's queries.
+  f32x16 lg[2] = {};
+  const int sc0 = wcell(n), sc1 = wcell(32 + n);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const bf16x8 A0 = *reinterpret_cast<const bf16x8*>(cK + row_off<BF16>(sc0, 16 * kb + 8 * h));
+    const bf16x8 A1 = *reinterpret_cast<const bf16x8*>(cK + row_off<BF16>(sc1, 16 * kb + 8 * h));
+    lg[0] = mma(A0, qB[kb], lg[0]);
+    lg[1] = mma(A1, qB[kb], lg[1]);
+  }
+  // Mask: window cell (wr, wc) is a neighbour of token (ta, tb) iff
+  // wr - ta and wc - tb lie in {0, 1, 2}; and it must lie on the grid.
+  const int ta = n >> 3, tb = n & 7;
+  unsigned rowbits = 0, colbits = 0;
+#pragma unroll
+  for (int wr = 0; wr < 6; ++wr) {
+    const int gr = r0 + 4 * br + wr - 1;
+    rowbits |= (unsigned)(gr >= 0 && gr < a.H) << wr;
+  }
+#pragma unroll
+  for (int wc = 0; wc < 10; ++wc) {
+    const int gc = c0 + 8 * bc + wc - 1;
+    colbits |= (unsigned)(gc >= 0 && gc < a.W) << wc;
+  }
+  float p[32];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int cl = 32 * cb + 8 * (i >> 2) + (i & 3);  // cell of lane half 0; half 1 adds 4
+      const int c = cl + 4 * h;
+      const int wr = h ? (cl + 4) / 10 : cl / 10;
+      const int wc = h ? (cl + 4) % 10 : cl % 10;
+      const bool ok = c < 60 && (unsigned)(wr - ta) <= 2u && (unsigned)(wc - tb) <= 2u &&
+                      ((rowbits >> wr) & (colbits >> wc) & 1u);
+      const float l = ok ? lg[cb][i] * a.logit_scale : -INFINITY;
+      p[16 * cb + i] = l;
+      mx = fmaxf(mx, l);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  float den = 0.f;
+  bf16x8 Bp[4];
+#pragma unroll
+  for (int v = 0; v < 32; ++v) {
+    const float e = (p[v] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(p[v] - mx);
+    const __bf16 eb = (__bf16)e;
+    Bp[v >> 3][v & 7] = eb;
+    den += (float)eb;  // normalise by the rounded weights actually applied
+  }
+  den += __shfl_xor(den, 32);
+  // L^T = V_win^T P^T: k-slot (h, e) of step kb is cell 16 kb + 8 (e >> 2) + 4 h + (e & 3).
+  f32x16 la[2] = {};
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const int cA = wcell(16 * kb + 4 * (g >> 1) + (i16 >> 2));
+    const int cB = wcell(16 * kb + 8 + 4 * (g >> 1) + (i16 >> 2));
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int d = 32 * db + 16 * (g & 1) + 4 * (i16 & 3);
+      const bf16x8 A = as_bf16(join(tr_read(cV + row_off<BF16>(cA, d)), tr_read(cV + row_off<BF16>(cB, d))));
+      la[db] = mma(A, Bp[kb], la[db]);
+    }
+  }
+  const float inv = 1.f / den;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    L[v] = la[0][v] * inv;
+    L[16 + v] = la[1][v] * inv;
+  }
+}
+
+// The same local branch on VALU (fp32 inputs): each lane pair reduces the
+// nine dot products of its token and accumulates the weighted values.
+template <class Tr>
+__device__ __forceinline__ void local_token_valu(const FlowArgs& a, const unsigned char* cK,
+                                                 const unsigned char* cV, int CW, int ccell, int row,
+                                                 int col, const float (&q)[32], float (&L)[32]) {
+  using S = typename Tr::S;
+  const int h = (threadIdx.x & 63) >> 5;
+  float lg[9];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 9; ++j) {
+    const int dr = j / 3 - 1, dc = j % 3 - 1;
+    const int cell = ccell + dr * CW + dc;
+    float part = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float kx[4];
+      load4(reinterpret_cast<const S*>(cK + row_off<Tr>(cell, dimof(4 * c, h))), kx);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) part += q[4 * c + e] * kx[e];
+    }
+    part += __shfl_xor(part, 32);
+    const bool in = (row + dr >= 0) && (row + dr < a.H) && (col + dc >= 0) && (col + dc < a.W);
+    lg[j] = in ? part * a.logit_scale : -INFINITY;
+    mx = fmaxf(mx, lg[j]);
+  }
+#pragma unroll
+  for (int v = 0; v < 32; ++v) L[v] = 0.f;
+  float den = 0.f;
+#pragma unroll
+  for (int j = 0; j < 9; ++j) {
+    const int dr = j / 3 - 1, dc = j % 3 - 1;
+    const int cell = ccell + dr * CW + dc;
+    const bool in = lg[j] != -INFINITY;
+    const float pj = in ? __builtin_amdgcn_exp2f(lg[j] - mx) : 0.f;
+    den += pj;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float vx[4];
+      load4(reinterpret_cast<const S*>(cV + row_off<Tr>(cell, dimof(4 * c, h))), vx);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) L[4 * c + e] = in ? L[4 * c + e] + pj * vx[e] : L[4 * c + e];
+    }
+  }
+  const float inv = 1.f / den;
+#pragma unroll
+  for (int v = 0; v < 32; ++v) L[v] *= inv;
+}
+
+// ---------------------------------------------------------------------------
+// OUT items: one TR x TC tile (whole 4x8 token blocks) of one slice.  Each
+// wave takes a block at a time, one token per lane pair: lanes m and m + 32
+// hold 32 features each in accumulator layout, so the chain
+// u_1 = phi(Q_i), u_k = u_(k-1) M and the projection z (phi(K)^T V),
+// z = sum_k w_k(i) u_k, run on MFMA with no data movement.  K and V cells of
+// the tile plus a one-cell halo are in the staged LDS buffer.
+// ---------------------------------------------------------------------------
 template <class Tr, class Prefetch>
 __device__ void out_item(const FlowArgs& a, Item it, const unsigned char* buf, Prefetch prefetch) {
   using S = typename Tr::S;
   using Frag = typename Tr::Frag;
+  constexpr bool kMfmaLocal = Tr::EPL == 8;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int m = lane & 31, h = lane >> 5;
+  const int n = lane & 31, h = lane >> 5;
   const int b = it.b;
   int r0, c0;
   tile_origin(a, it.idx, r0, c0);
   const int CW = a.TC + 2;
+  const int CB = a.TC / 8, nblk = (a.TR / 4) * CB;
   const unsigned char* cK = buf;
   const unsigned char* cV = buf + kBufBytes / 2;
   const size_t base = (size_t)b * a.n * kD;
   const S* Qb = static_cast<const S*>(a.Q) + base;
   S* Yb = static_cast<S*>(a.Y) + base;
   const bool global = a.T >= 2;
-  const int ntok = a.TR * a.TC;
 
-  // Statistics (coherent loads), then this wave's first group of queries.
+  // Statistics (coherent loads), then this wave's first block of queries.
   float s_l[32];
   Frag fkv[2][Tr::NQ], fm[2][Tr::NQ];
   if (global) {
@@ -350,18 +483,24 @@ __device__ void out_item(const FlowArgs& a, Item it, const unsigned char* buf, P
   const float alpha = a.alpha[b % a.heads];
 
   float q[32];
+  bf16x8 qB[4];
   float w[kMaxT];
-  auto load_group = [&](int t0, int& row, int& col, int& i, bool& valid, int& ccell) {
-    const int t = t0 + m;
-    int tr = t / a.TC, tc = t % a.TC;
+  int row, col, i, ccell;
+  bool valid;
+  auto load_block = [&](int blk) {
+    const int tr = 4 * (blk / CB) + (n >> 3), tc = 8 * (blk % CB) + (n & 7);
     row = r0 + tr;
     col = c0 + tc;
-    valid = (t < ntok) && (row < a.H) && (col < a.W);
-    if (!valid) tr = tc = 0;  // any staged cell; results are discarded
+    valid = row < a.H && col < a.W;
     i = valid ? row * a.W + col : 0;
     ccell = (tr + 1) * CW + (tc + 1);
+    const S* qi = Qb + (size_t)i * kD;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) load4(Qb + (size_t)i * kD + dimof(4 * c, h), &q[4 * c]);
+    for (int c = 0; c < 8; ++c) load4(qi + dimof(4 * c, h), &q[4 * c]);
+    if constexpr (kMfmaLocal) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) qB[kb] = *reinterpret_cast<const bf16x8*>(qi + 16 * kb + 8 * h);
+    }
     if (a.weights) {
       const float* wp = a.weights + ((size_t)b * a.n + i) * a.T;
 #pragma unroll
@@ -372,14 +511,19 @@ __device__ void out_item(const FlowArgs& a, Item it, const unsigned char* buf, P
     }
   };
 
-  int row, col, i, ccell;
-  bool valid;
-  int t0 = 32 * wave;
-  if (t0 < ntok) load_group(t0, row, col, i, valid, ccell);
+  int blk = wave;
+  if (blk < nblk) load_block(blk);
   prefetch();
 
-  for (; t0 < ntok; t0 += 32 * (kThreads / 64)) {
-    if (t0 != 32 * wave) load_group(t0, row, col, i, valid, ccell);
+  for (; blk < nblk; blk += kThreads / 64) {
+    if (blk != wave) load_block(blk);
+
+    // Local branch.
+    float L[32];
+    if constexpr (kMfmaLocal)
+      local_block_mfma(a, cK, cV, CW, r0, c0, blk / CB, blk % CB, qB, L);
+    else
+      local_token_valu<Tr>(a, cK, cV, CW, ccell, row, col, q, L);
 
     // Global branch.
     float G[32];
@@ -415,53 +559,12 @@ __device__ void out_item(const FlowArgs& a, Item it, const unsigned char* buf, P
       for (int v = 0; v < 32; ++v) G[v] += r * y[v];
     }
 
-    // Local branch: 3x3 window clipped to the grid, row max subtracted.
-    float lg[9];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 9; ++j) {
-      const int dr = j / 3 - 1, dc = j % 3 - 1;
-      const int cell = ccell + dr * CW + dc;
-      float part = 0.f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        float kx[4];
-        load4(reinterpret_cast<const S*>(cK + row_off<Tr>(cell, dimof(4 * c, h))), kx);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) part += q[4 * c + e] * kx[e];
-      }
-      part += __shfl_xor(part, 32);
-      const bool in = (row + dr >= 0) && (row + dr < a.H) && (col + dc >= 0) && (col + dc < a.W);
-      lg[j] = in ? part * a.logit_scale : -INFINITY;
-      mx = fmaxf(mx, lg[j]);
-    }
-    float L[32];
-#pragma unroll
-    for (int v = 0; v < 32; ++v) L[v] = 0.f;
-    float den = 0.f;
-#pragma unroll
-    for (int j = 0; j < 9; ++j) {
-      const int dr = j / 3 - 1, dc = j % 3 - 1;
-      const int cell = ccell + dr * CW + dc;
-      const bool in = lg[j] != -INFINITY;
-      const float pj = in ? __builtin_amdgcn_exp2f(lg[j] - mx) : 0.f;
-      den += pj;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        float vx[4];
-        load4(reinterpret_cast<const S*>(cV + row_off<Tr>(cell, dimof(4 * c, h))), vx);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) L[4 * c + e] = in ? L[4 * c + e] + pj * vx[e] : L[4 * c + e];
-      }
-    }
-    const float inv = 1.f / den;
-
     if (valid) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         float o[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = alpha * G[4 * c + e] + (1.f - alpha) * (L[4 * c + e] * inv);
+        for (int e = 0; e < 4; ++e) o[e] = alpha * G[4 * c + e] + (1.f - alpha) * L[4 * c + e];
         store4(Yb + (size_t)i * kD + dimof(4 * c, h), o);
       }
     }
@@ -484,7 +587,6 @@ template <class Tr>
 __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
   extern __shared__ __align__(1024) unsigned char smem[];
   __shared__ float s_sh[kD];
-  __shared__ float r_sh[kMaxTileTokens];
   __shared__ int sh_t[3];
   const int tid = threadIdx.x;
   const int x = blockIdx.x % a.nq;
@@ -526,9 +628,9 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
       if (nxt < total) stage<Tr>(a, decode(a, x, nxt), nb);
     };
     if (it.kind == kKV)
-      stats_item<Tr, false>(a, it, cb, s_sh, r_sh, prefetch);
+      stats_item<Tr, false>(a, it, cb, s_sh, prefetch);
     else if (it.kind == kM)
-      stats_item<Tr, true>(a, it, cb, s_sh, r_sh, prefetch);
+      stats_item<Tr, true>(a, it, cb, s_sh, prefetch);
     else if (it.kind == kC)
       combine_item<Tr>(a, it, prefetch);
     else
