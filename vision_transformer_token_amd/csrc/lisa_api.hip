@@ -3,6 +3,7 @@
 // touches the GPU before every argument has been checked.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -46,21 +47,47 @@ lisa_status check_problem(const lisa_problem* p) {
 }
 
 // Output tile: TR x TC cells made of whole 4 x 8 token blocks (the MFMA local
-// branch works on such blocks), 8..32 columns (at most 16 for fp32), as many
-// rows as one LDS staging buffer holds with a one-cell halo of K and V, at
-// most kMaxTileTokens tokens.
-void plan_tiles(Plan& pl) {
-  const int max_cells = lisa::kBufBytes / 2 / (int)(kD * pl.esize);
-  const int tc_max = pl.esize == 2 ? 32 : 16;
-  pl.TC = (pl.W + 7) / 8 * 8;
-  if (pl.TC > tc_max) pl.TC = tc_max;
-  int tr = (max_cells / (pl.TC + 2) - 2) / 4 * 4;
-  while (tr > 4 && tr * pl.TC > lisa::kMaxTileTokens) tr -= 4;
+// branch works on such blocks), 8..32 columns (at most 16 for fp32), the most
+// rows (at most kMaxTileTokens tokens) whose staged inputs (TileLayout: K and
+// V cells with a one-cell halo, Q rows, per-token weights) fit one staging
+// buffer; narrower tiles when even 4 rows do not fit.
+bool plan_tiles(Plan& pl, bool per_token_weights) {
+  const int es = (int)pl.esize;
+  const int stage = es == 2 ? lisa::Lds<2>::kStage : lisa::Lds<4>::kStage;
+  const int wT = per_token_weights ? pl.T : 0;
   const int h4 = (pl.H + 3) / 4 * 4;
-  if (tr > h4) tr = h4;
-  pl.TR = tr;
+  int tc = std::min((pl.W + 7) / 8 * 8, es == 2 ? 32 : 16);
+  for (;; tc -= 8) {
+    int tr = 0;
+    for (int r = 4; r <= h4 && r * tc <= lisa::kMaxTileTokens; r += 4)
+      if (lisa::tile_layout(r, tc, wT, es).total <= stage) tr = r;
+    if (tr > 0) {
+      pl.TR = tr;
+      pl.TC = tc;
+      break;
+    }
+    if (tc == 8) return false;
+  }
   pl.tiles_x = (pl.W + pl.TC - 1) / pl.TC;
   pl.ntiles = pl.tiles_x * ((pl.H + pl.TR - 1) / pl.TR);
+  return true;
+}
+
+// Tiles per OUT item (at most 64): the run length that finishes a queue's
+// output tiles in the fewest tile-rounds over the queue's workgroups (ties:
+// longer runs, which read the slice statistics fewer times).
+int plan_runs(int ntiles, int slices_per_queue, int wgs_per_queue) {
+  int best = 1;
+  long best_span = -1;
+  for (int r = 1; r <= ntiles && r <= 64; ++r) {
+    const long runs = (long)slices_per_queue * ((ntiles + r - 1) / r);
+    const long span = (long)r * ((runs + wgs_per_queue - 1) / wgs_per_queue);
+    if (best_span < 0 || span <= best_span) {
+      best_span = span;
+      best = r;
+    }
+  }
+  return best;
 }
 
 lisa_status make_plan(const lisa_problem* p, Plan& pl) {
@@ -74,11 +101,10 @@ lisa_status make_plan(const lisa_problem* p, Plan& pl) {
   pl.T = p->T;
   pl.dtype = p->dtype;
   pl.esize = p->dtype == LISA_BF16 ? 2 : 4;
-  // Statistics items: one LDS buffer holds the chunk's K rows and V (or Q) rows.
-  // (a multiple of 16 tokens: the MFMA sweep reads whole 16-row steps).
-  pl.chunk = pl.esize == 2 ? 256 : 128;
+  // Statistics items: one staging buffer holds the chunk's K rows and V (or
+  // Q) rows (a multiple of 16 tokens: the MFMA sweep reads whole 16-row steps).
+  pl.chunk = pl.esize == 2 ? lisa::Lds<2>::kChunk : lisa::Lds<4>::kChunk;
   pl.P = (pl.n + pl.chunk - 1) / pl.chunk;
-  plan_tiles(pl);
   pl.nq = (pl.BH % lisa::kMaxQueues == 0) ? lisa::kMaxQueues : 1;
 
   const size_t BH = pl.BH, P = pl.P;
@@ -93,7 +119,7 @@ lisa_status make_plan(const lisa_problem* p, Plan& pl) {
   // a workspace reused by problems of other shapes never has another
   // problem's data written over a counter (each call leaves them at zero).
   pl.queue_cnt = take(32 * sizeof(unsigned));
-  pl.slice_cnt = take((size_t)kMaxSlices * 4 * sizeof(unsigned));
+  pl.slice_cnt = take((size_t)kMaxSlices * lisa::kCntWords * sizeof(unsigned));
   pl.part_s = take(BH * P * vec);
   pl.part_kv = take(BH * P * mat);
   pl.part_m = take(BH * P * mat);
@@ -141,7 +167,7 @@ lisa_status check_forward(const lisa_problem* p, const void* Q, const void* K, c
 enum class Mode { kForward, kReduce, kApply };
 
 // One launch of the persistent kernel, one workgroup per compute unit.
-lisa_status run(const Plan& pl, Mode mode, const void* Q, const void* K, const void* V,
+lisa_status run(Plan pl, Mode mode, const void* Q, const void* K, const void* V,
                 const float* weights, float beta, const float* alpha, void* Y, char* ws, float eps,
                 hipStream_t s) {
   lisa::FlowArgs a{};
@@ -163,17 +189,27 @@ lisa_status run(const Plan& pl, Mode mode, const void* Q, const void* K, const v
   a.BH = pl.BH;
   a.eps = eps;
   a.logit_scale = (float)(1.4426950408889634 / std::sqrt((double)kD));
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return LISA_ERR_HIP;
+  int grid = cus / lisa::kMaxQueues * lisa::kMaxQueues;
+  if (grid < lisa::kMaxQueues) grid = lisa::kMaxQueues;
+
+  if (!plan_tiles(pl, weights != nullptr)) return LISA_ERR_UNSUPPORTED;
   a.chunk = pl.chunk;
   a.P = pl.P;
   a.TR = pl.TR;
   a.TC = pl.TC;
   a.tiles_x = pl.tiles_x;
+  a.ntiles = pl.ntiles;
+  a.R = plan_runs(pl.ntiles, pl.nq == 1 ? pl.BH : pl.BH / pl.nq, grid / pl.nq);
   const bool stats = mode == Mode::kReduce || (mode == Mode::kForward && pl.T >= 2);
   const bool need_m = mode == Mode::kReduce || (mode == Mode::kForward && pl.T >= 3);
   a.nKV = stats ? pl.P : 0;
   a.nM = need_m ? pl.P : 0;
   a.nC = stats ? (need_m ? 2 : 1) * lisa::kCombineBlocks : 0;
-  a.nOUT = mode == Mode::kReduce ? 0 : pl.ntiles;
+  a.nOUT = mode == Mode::kReduce ? 0 : (pl.ntiles + a.R - 1) / a.R;
   a.wait_out = (mode == Mode::kForward && stats) ? 1 : 0;
   a.nq = pl.nq;
   a.part_s = reinterpret_cast<float*>(ws + pl.part_s);
@@ -187,13 +223,6 @@ lisa_status run(const Plan& pl, Mode mode, const void* Q, const void* K, const v
   a.slice_cnt = reinterpret_cast<unsigned*>(ws + pl.slice_cnt);
   a.queue_cnt = reinterpret_cast<unsigned*>(ws + pl.queue_cnt);
   a.err = a.queue_cnt + 17;
-
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return LISA_ERR_HIP;
-  int grid = cus / lisa::kMaxQueues * lisa::kMaxQueues;
-  if (grid < lisa::kMaxQueues) grid = lisa::kMaxQueues;
   if (lisa::launch_flow(pl.dtype, a, grid, s) != hipSuccess) return LISA_ERR_HIP;
   return LISA_OK;
 }

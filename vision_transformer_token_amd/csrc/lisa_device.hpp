@@ -101,6 +101,14 @@ __device__ __forceinline__ void store4(float* p, const float* x) {
   *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
 }
 
+// Index of this thread's wave in the workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+// q = floor(x / d) for 0 <= x < 2^20, 0 < d < 2^10, via a float reciprocal
+// (inv_d = 1.0f / d): (x + 0.5) / d lies at least 0.5 / d from an integer, far
+// more than the rounding error of the product.
+__device__ __forceinline__ int div_small(int x, float inv_d) { return (int)(((float)x + 0.5f) * inv_d); }
+
 // ---------------------------------------------------------------------------
 // Swizzled LDS rows.  A staged 64-wide row (a token's features, or a grid
 // cell) occupies RB bytes split into PPR 16-byte pieces; piece g of row r
@@ -118,12 +126,33 @@ __device__ __forceinline__ int row_off(int r, int d) {  // byte offset of elemen
   return r * Tr::RB + ((((d >> SH) ^ swz(r)) & (Tr::PPR - 1)) << 4) + (d & (Tr::EPP - 1)) * ES;
 }
 
+// LDS DMA (global_load_lds) issued through inline assembly.  The compiler
+// then neither sees the LDS writes nor inserts waits for them; if it did, it
+// would wait for the whole DMA of the next stage before the first LDS access
+// of the current one.  Every read of DMA-staged data therefore follows an
+// explicit wait_all() and a barrier.  Lane i writes bytes [16 i, 16 i + 16)
+// (dwordx4) or [4 i, 4 i + 4) (dword) after the wave-uniform LDS address
+// held in M0.
+__device__ __forceinline__ unsigned lds_addr(const unsigned char* p) {
+  return __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_ptr_t)p);
+}
+__device__ __forceinline__ void dma16(const void* g, unsigned m0) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0) : "memory");
+}
+// Coherent at agent scope (sc1): for data other workgroups of the launch wrote.
+__device__ __forceinline__ void dma16_coherent(const void* g, unsigned m0) {
+  asm volatile("global_load_lds_dwordx4 %0, off sc1" ::"v"(g), "{m0}"(m0) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* g, unsigned m0) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(m0) : "memory");
+}
+
 // DMA `nrow` rows into `lds` (a multiple of 1 KB is written: the last run is
 // padded with copies of row nrow-1).  src(r) returns the global address of
 // row r (16-byte aligned).  Every wave takes every 4th run; no wait here.
 template <class Tr, class SrcFn>
 __device__ __forceinline__ void dma_rows(unsigned char* lds, int nrow, SrcFn src) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int npieces = nrow * Tr::PPR;
   for (int base = wave * 64; base < npieces; base += 64 * 4) {
     const int P = base + lane;
@@ -131,9 +160,20 @@ __device__ __forceinline__ void dma_rows(unsigned char* lds, int nrow, SrcFn src
     const int slot = P % Tr::PPR;
     const int g = (slot ^ swz(P / Tr::PPR)) & (Tr::PPR - 1);
     const unsigned char* gp = static_cast<const unsigned char*>(src(r)) + g * 16;
-    __builtin_amdgcn_global_load_lds(gp, (lds_ptr_t)(lds + base * 16), 16, 0, 0);
+    dma16(gp, lds_addr(lds + base * 16));
   }
 }
+
+// Coherent DMA of `bytes` (a multiple of 16) from src to lds unchanged, 1 KB
+// per wave instruction.
+__device__ __forceinline__ void dma_linear_coherent(unsigned char* lds, const void* src, int bytes) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  for (int base = wave * 1024; base < bytes; base += 4096) {
+    const int off = min(base + lane * 16, bytes - 16);  // spare lanes repeat the last piece
+    if (base + lane * 16 < bytes) dma16_coherent(static_cast<const unsigned char*>(src) + off, lds_addr(lds + base));
+  }
+}
+
 // Bytes that dma_rows writes for nrow rows.
 __host__ __device__ constexpr int dma_bytes(int nrow, int row_bytes) {
   return (nrow * row_bytes + 1023) / 1024 * 1024;
@@ -201,7 +241,24 @@ __device__ __forceinline__ uint64_t get64(const void* p) {
   return __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+// Wait for every outstanding memory access of this wave (the compiler may
+// not move memory accesses across it).
+__device__ __forceinline__ void wait_all() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// waits for every global load in flight, which includes the LDS DMA of the
+// next stage; this one lets that DMA continue.  Each wave first waits for
+// its own LDS accesses (lgkmcnt(0)).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 __device__ __forceinline__ unsigned bump(unsigned* cnt) {
   return __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
