@@ -22,6 +22,9 @@ HIPCC_FLAGS = [
     "-Wall",
     # Packed fp32 VALU ops stay off: plain float code only.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the kernels feed them straight into
+    # VALU work, which would otherwise copy them out of accumulation registers.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

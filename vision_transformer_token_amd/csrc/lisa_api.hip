@@ -24,11 +24,13 @@ size_t up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 struct Plan {
   int BH = 0, n = 0, H = 0, W = 0, T = 0, dtype = 0, heads = 0;
   size_t esize = 0;
-  int chunk = 0, P = 0;                          // statistics items per slice
+  int gmax = 1;                                  // ranks per slice the partials are sized for
+  int grid = 0;                                  // workgroups (one per compute unit)
+  int G = 1, S = 1, Z = 1, xcd_groups = 0;       // ranks per slice, groups, slices per round
+  int chunk = 0;                                 // tokens per KV / M stage
   int TR = 0, TC = 0, tiles_x = 0, ntiles = 0;   // output tiles per slice
-  int nq = 1;                                    // work queues
   // workspace layout (byte offsets)
-  size_t slice_cnt = 0, queue_cnt = 0, part_s = 0, part_kv = 0, part_m = 0, fin_s = 0, fin_kv = 0,
+  size_t slice_cnt = 0, done_cnt = 0, part_s = 0, part_kv = 0, part_m = 0, fin_s = 0, fin_kv = 0,
          fin_m = 0, frag_kv = 0, frag_m = 0, total = 0;
 };
 
@@ -73,21 +75,19 @@ bool plan_tiles(Plan& pl, bool per_token_weights) {
   return true;
 }
 
-// Tiles per OUT item (at most 64): the run length that finishes a queue's
-// output tiles in the fewest tile-rounds over the queue's workgroups (ties:
-// longer runs, which read the slice statistics fewer times).
-int plan_runs(int ntiles, int slices_per_queue, int wgs_per_queue) {
-  int best = 1;
-  long best_span = -1;
-  for (int r = 1; r <= ntiles && r <= 64; ++r) {
-    const long runs = (long)slices_per_queue * ((ntiles + r - 1) / r);
-    const long span = (long)r * ((runs + wgs_per_queue - 1) / wgs_per_queue);
-    if (best_span < 0 || span <= best_span) {
-      best_span = span;
-      best = r;
-    }
-  }
-  return best;
+// Workgroups per slice: twice as many as there are workgroups per slice of
+// the grid (so that a group has two slices to interleave), at most one per
+// 128 tokens and kMaxRanks, rounded down to a power of two (the combine
+// splits the 8192 statistics evenly).
+int plan_ranks(int grid, int BH, int n) {
+  long per = 2L * grid / BH;
+  const long tok = (n + 127) / 128;
+  if (per > grid) per = grid;
+  if (per > tok) per = tok;
+  if (per > lisa::kMaxRanks) per = lisa::kMaxRanks;
+  int G = 1;
+  while (2L * G <= per) G *= 2;
+  return G;
 }
 
 lisa_status make_plan(const lisa_problem* p, Plan& pl) {
@@ -101,13 +101,14 @@ lisa_status make_plan(const lisa_problem* p, Plan& pl) {
   pl.T = p->T;
   pl.dtype = p->dtype;
   pl.esize = p->dtype == LISA_BF16 ? 2 : 4;
-  // Statistics items: one staging buffer holds the chunk's K rows and V (or
-  // Q) rows (a multiple of 16 tokens: the MFMA sweep reads whole 16-row steps).
+  // The partials are sized for the most ranks any grid can give a slice
+  // (the launch picks G <= gmax from the device's compute units).
+  pl.gmax = plan_ranks(lisa::kMaxRanks, 2, pl.n);
+  // KV / M stages: one staging buffer holds a chunk's K rows and V (or Q)
+  // rows (a multiple of 16 tokens: the MFMA sweep reads whole 16-row steps).
   pl.chunk = pl.esize == 2 ? lisa::Lds<2>::kChunk : lisa::Lds<4>::kChunk;
-  pl.P = (pl.n + pl.chunk - 1) / pl.chunk;
-  pl.nq = (pl.BH % lisa::kMaxQueues == 0) ? lisa::kMaxQueues : 1;
 
-  const size_t BH = pl.BH, P = pl.P;
+  const size_t BH = pl.BH, G = pl.gmax;
   const size_t mat = kD * kD * sizeof(float), vec = kD * sizeof(float);
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -118,11 +119,11 @@ lisa_status make_plan(const lisa_problem* p, Plan& pl) {
   // Counters first, at offsets and sizes that do not depend on the problem:
   // a workspace reused by problems of other shapes never has another
   // problem's data written over a counter (each call leaves them at zero).
-  pl.queue_cnt = take(32 * sizeof(unsigned));
+  pl.done_cnt = take(32 * sizeof(unsigned));
   pl.slice_cnt = take((size_t)kMaxSlices * lisa::kCntWords * sizeof(unsigned));
-  pl.part_s = take(BH * P * vec);
-  pl.part_kv = take(BH * P * mat);
-  pl.part_m = take(BH * P * mat);
+  pl.part_s = take(BH * G * vec);
+  pl.part_kv = take(BH * G * mat);
+  pl.part_m = take(BH * G * mat);
   pl.fin_s = take(BH * vec);
   pl.fin_kv = take(BH * mat);
   pl.fin_m = take(BH * mat);
@@ -189,29 +190,32 @@ lisa_status run(Plan pl, Mode mode, const void* Q, const void* K, const void* V,
   a.BH = pl.BH;
   a.eps = eps;
   a.logit_scale = (float)(1.4426950408889634 / std::sqrt((double)kD));
+  if (!plan_tiles(pl, weights != nullptr)) return LISA_ERR_UNSUPPORTED;
+  // One persistent workgroup per compute unit.
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     return LISA_ERR_HIP;
-  int grid = cus / lisa::kMaxQueues * lisa::kMaxQueues;
-  if (grid < lisa::kMaxQueues) grid = lisa::kMaxQueues;
-
-  if (!plan_tiles(pl, weights != nullptr)) return LISA_ERR_UNSUPPORTED;
+  pl.grid = cus;
+  pl.G = plan_ranks(pl.grid, pl.BH, pl.n);
+  if (pl.G > pl.gmax) pl.G = pl.gmax;
+  pl.S = pl.grid / pl.G;
+  // Slices per round: all of the group's slices, at most 4.
+  pl.Z = std::min(4, (pl.BH + pl.S - 1) / pl.S);
+  // Keep a group's workgroups on one XCD (shared L2) when the grid allows it.
+  pl.xcd_groups = (pl.grid % lisa::kXcds == 0 && (pl.grid / lisa::kXcds) % pl.G == 0) ? 1 : 0;
   a.chunk = pl.chunk;
-  a.P = pl.P;
+  a.G = pl.G;
+  a.S = pl.S;
+  a.Z = pl.Z;
+  a.xcd_groups = pl.xcd_groups;
   a.TR = pl.TR;
   a.TC = pl.TC;
   a.tiles_x = pl.tiles_x;
   a.ntiles = pl.ntiles;
-  a.R = plan_runs(pl.ntiles, pl.nq == 1 ? pl.BH : pl.BH / pl.nq, grid / pl.nq);
-  const bool stats = mode == Mode::kReduce || (mode == Mode::kForward && pl.T >= 2);
-  const bool need_m = mode == Mode::kReduce || (mode == Mode::kForward && pl.T >= 3);
-  a.nKV = stats ? pl.P : 0;
-  a.nM = need_m ? pl.P : 0;
-  a.nC = stats ? (need_m ? 2 : 1) * lisa::kCombineBlocks : 0;
-  a.nOUT = mode == Mode::kReduce ? 0 : (pl.ntiles + a.R - 1) / a.R;
-  a.wait_out = (mode == Mode::kForward && stats) ? 1 : 0;
-  a.nq = pl.nq;
+  a.do_kv = (mode == Mode::kReduce || (mode == Mode::kForward && pl.T >= 2)) ? 1 : 0;
+  a.do_m = (mode == Mode::kReduce || (mode == Mode::kForward && pl.T >= 3)) ? 1 : 0;
+  a.do_out = mode == Mode::kReduce ? 0 : 1;
   a.part_s = reinterpret_cast<float*>(ws + pl.part_s);
   a.part_kv = reinterpret_cast<float*>(ws + pl.part_kv);
   a.part_m = reinterpret_cast<float*>(ws + pl.part_m);
@@ -221,9 +225,10 @@ lisa_status run(Plan pl, Mode mode, const void* Q, const void* K, const void* V,
   a.frag_kv = ws + pl.frag_kv;
   a.frag_m = ws + pl.frag_m;
   a.slice_cnt = reinterpret_cast<unsigned*>(ws + pl.slice_cnt);
-  a.queue_cnt = reinterpret_cast<unsigned*>(ws + pl.queue_cnt);
-  a.err = a.queue_cnt + 17;
-  if (lisa::launch_flow(pl.dtype, a, grid, s) != hipSuccess) return LISA_ERR_HIP;
+  a.done_cnt = reinterpret_cast<unsigned*>(ws + pl.done_cnt);
+  a.err = a.done_cnt + 1;
+  a.tickets = a.done_cnt + 8;
+  if (lisa::launch_flow(pl.dtype, a, pl.grid, s) != hipSuccess) return LISA_ERR_HIP;
   return LISA_OK;
 }
 

@@ -149,10 +149,11 @@ __device__ __forceinline__ void dma4(const void* g, unsigned m0) {
 
 // DMA `nrow` rows into `lds` (a multiple of 1 KB is written: the last run is
 // padded with copies of row nrow-1).  src(r) returns the global address of
-// row r (16-byte aligned).  Every wave takes every 4th run; no wait here.
+// row r (16-byte aligned).  Run j (1 KB) is issued by wave j % 4 of the
+// calling role's four waves (`wave` in 0..3); no wait here.
 template <class Tr, class SrcFn>
-__device__ __forceinline__ void dma_rows(unsigned char* lds, int nrow, SrcFn src) {
-  const int lane = threadIdx.x & 63, wave = wave_id();
+__device__ __forceinline__ void dma_rows(unsigned char* lds, int nrow, SrcFn src, int wave) {
+  const int lane = threadIdx.x & 63;
   const int npieces = nrow * Tr::PPR;
   for (int base = wave * 64; base < npieces; base += 64 * 4) {
     const int P = base + lane;
@@ -165,9 +166,9 @@ __device__ __forceinline__ void dma_rows(unsigned char* lds, int nrow, SrcFn src
 }
 
 // Coherent DMA of `bytes` (a multiple of 16) from src to lds unchanged, 1 KB
-// per wave instruction.
-__device__ __forceinline__ void dma_linear_coherent(unsigned char* lds, const void* src, int bytes) {
-  const int lane = threadIdx.x & 63, wave = wave_id();
+// per wave instruction, spread over four waves (`wave` in 0..3).
+__device__ __forceinline__ void dma_linear_coherent(unsigned char* lds, const void* src, int bytes, int wave) {
+  const int lane = threadIdx.x & 63;
   for (int base = wave * 1024; base < bytes; base += 4096) {
     const int off = min(base + lane * 16, bytes - 16);  // spare lanes repeat the last piece
     if (base + lane * 16 < bytes) dma16_coherent(static_cast<const unsigned char*>(src) + off, lds_addr(lds + base));

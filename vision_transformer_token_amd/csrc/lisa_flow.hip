@@ -1,4 +1,4 @@
-// The LiSA forward pass on gfx950 as one persistent, dependency-driven kernel.
+// The LiSA forward pass on gfx950 as one persistent kernel.
 //
 // Method: reading note "LiSA:面向长程视觉建模的线性随机注意力" (arXiv:2611.04216v2),
 // §2.1-§2.4.  Per (batch, head) slice with n tokens of width 64:
@@ -9,20 +9,20 @@
 //   local branch: L_i = softmax over the clipped 3x3 window of q_i . k_j / sqrt(d_h), times V;
 //   Y_i = alpha G_i + (1 - alpha) L_i.
 //
-// Work is split into items (see FlowArgs): KV and M items sweep token chunks
-// and contract over tokens on MFMA; C items sum the chunk partials in a fixed
-// order and write the statistics as MFMA fragments; OUT items produce a run
-// of spatial tiles of Y.  Each workgroup takes items from its XCD's queue (an
-// atomic ticket) and waits for the items an item depends on through
-// per-slice arrival counters.
+// Schedule (FlowArgs): the G ranks of a group split each slice's tokens for
+// the KV and M sweeps (contractions over tokens on MFMA), its 64x64
+// statistics for the combine, and its output tiles; a rank waits for the
+// group's previous phase through per-slice arrival counters.
 //
-// Every input an item reads from Q, K, V and the weights reaches LDS by
-// global_load_lds DMA, one stage (a chunk, or a tile) ahead, into the other of
-// two staging buffers.  Data written by other workgroups of the launch
-// (partials, fragments) is read with coherent loads right after the
-// dependency wait and before the next stage's DMA is issued, and barriers
-// after that issue order LDS only, so the DMA of the next stage overlaps the
-// whole compute of the current one.
+// A workgroup has two roles of four waves each, one wave of each per SIMD.
+// Producer waves prepare the next stage (a chunk, an output tile, or the
+// partials a combine sums) in the other of two LDS staging buffers: they
+// issue its global_load_lds DMA (issuing stalls a wave for about as long as
+// the transfer takes), wait for its dependencies, load what other
+// workgroups wrote, and finish the staged data in place (the rescaled Q rows
+// of an M chunk).  Consumer waves only compute on the current stage and
+// publish results; they never wait for a DMA.  One workgroup barrier per
+// stage hands the buffers over.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -32,41 +32,95 @@
 namespace lisa {
 namespace {
 
-enum Kind { kKV = 0, kM = 1, kC = 2, kOut = 3, kNone = 4 };
-struct Item {
-  int kind, b, idx;
-};
-
 template <class Tr>
 using LdsOf = Lds<(int)sizeof(typename Tr::S)>;
 
-__device__ __forceinline__ int queue_slices(const FlowArgs& a, int x) {
-  return a.nq == 1 ? a.BH : (a.BH - x + a.nq - 1) / a.nq;
-}
-__device__ __forceinline__ int queue_items(const FlowArgs& a, int x) {
-  return queue_slices(a, x) * (a.nKV + a.nM + a.nC + a.nOUT);
-}
-// Queue order: all KV items of the queue's slices (slice-major), then all M,
-// then all C, then all OUT items.  An item only waits for items earlier in
-// this order, which the workgroups have already taken.
-__device__ __forceinline__ Item decode(const FlowArgs& a, int x, int t) {
-  const int ns = queue_slices(a, x);
-  const int per[4] = {a.nKV, a.nM, a.nC, a.nOUT};
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int cnt = ns * per[k];
-    if (t < cnt) {
-      const int j = t / per[k];
-      return Item{k, a.nq == 1 ? j : x + a.nq * j, t % per[k]};
-    }
-    t -= cnt;
+enum Phase { kPKV = 0, kPM = 1, kPC = 2, kPOut = 3, kPEnd = 4 };
+enum Counter { kCntKV = 0, kCntM = 1, kCntC = 2 };
+
+// This workgroup's place in the schedule.
+struct Rank {
+  int group, g;       // group (-1: idle workgroup), rank within the group
+  int tok0, ntok;     // token range of each slice
+  int nch;            // chunks of that range
+  int t0, nt;         // output tiles
+  int e0, E;          // combine elements of the flattened [phi(K)^T V | M]
+};
+
+// Ranks are handed out in the order workgroups start (a ticket per XCD when
+// groups stay within an XCD): a group then only ever waits for workgroups
+// that are already running, so the launch makes progress as long as G
+// workgroups fit on the device at once.  `ticket` comes from take_ticket.
+__device__ __forceinline__ Rank make_rank(const FlowArgs& a, int ticket) {
+  Rank r;
+  if (a.xcd_groups) {
+    r.group = (blockIdx.x % kXcds) * (a.S / kXcds) + ticket / a.G;
+    if (ticket / a.G >= a.S / kXcds) r.group = -1;
+  } else {
+    r.group = ticket / a.G;
+    if (r.group >= a.S) r.group = -1;
   }
-  return Item{kNone, 0, 0};
+  r.g = ticket % a.G;
+  r.tok0 = (int)((long long)r.g * a.n / a.G);
+  r.ntok = (int)((long long)(r.g + 1) * a.n / a.G) - r.tok0;
+  r.nch = (r.ntok + a.chunk - 1) / a.chunk;
+  r.t0 = (int)((long long)r.g * a.ntiles / a.G);
+  r.nt = (int)((long long)(r.g + 1) * a.ntiles / a.G) - r.t0;
+  r.E = 2 * kD * kD / a.G;
+  r.e0 = r.g * r.E;
+  return r;
 }
 
-// Thread 0 only: spin until *c >= target.  The wait is bounded (about a
-// second); on giving up it raises the error word, after which every later
-// wait of the launch returns at once, so the launch always finishes.
+// A stage: round r of the group's slices, phase `ph`, slice z of the round
+// (slice b = group + (r Z + z) S), step j (chunk or tile index in the rank's
+// range).  A round runs each phase for all its slices before the next phase,
+// so a slice's dependency wait overlaps the other slices' stages.
+struct Pos {
+  int r, ph, z, j;
+};
+__device__ __forceinline__ int slice_of(const FlowArgs& a, const Rank& rk, int r, int z) {
+  return rk.group + (r * a.Z + z) * a.S;
+}
+// Slices in round r (0: past the group's last slice).
+__device__ __forceinline__ int round_slices(const FlowArgs& a, const Rank& rk, int r) {
+  const int b0 = slice_of(a, rk, r, 0);
+  if (rk.group < 0 || b0 >= a.BH) return 0;
+  return min(a.Z, (a.BH - b0 + a.S - 1) / a.S);
+}
+__device__ __forceinline__ int phase_len(const FlowArgs& a, const Rank& r, int ph) {
+  switch (ph) {
+    case kPKV: return a.do_kv ? r.nch : 0;
+    case kPM: return a.do_m ? r.nch : 0;
+    case kPC: return a.do_kv ? 1 : 0;
+    case kPOut: return a.do_out ? r.nt : 0;
+  }
+  return 0;
+}
+// The stage after `p` (ph == kPEnd: none); empty phases are skipped.
+__device__ Pos advance(const FlowArgs& a, const Rank& rk, Pos p) {
+  if (p.ph != kPEnd) {
+    if (p.j + 1 < phase_len(a, rk, p.ph)) return Pos{p.r, p.ph, p.z, p.j + 1};
+    if (p.z + 1 < round_slices(a, rk, p.r)) return Pos{p.r, p.ph, p.z + 1, 0};
+  }
+  int r = p.r, ph = p.ph + 1;
+  for (;;) {
+    if (ph >= kPEnd) {
+      ++r;
+      ph = kPKV;
+      if (round_slices(a, rk, r) == 0) return Pos{r, kPEnd, 0, 0};
+    }
+    if (phase_len(a, rk, ph) > 0) return Pos{r, ph, 0, 0};
+    ++ph;
+  }
+}
+__device__ __forceinline__ Pos first_pos(const FlowArgs& a, const Rank& rk) {
+  if (round_slices(a, rk, 0) == 0) return Pos{0, kPEnd, 0, 0};
+  return advance(a, rk, Pos{-1, kPEnd, 0, 0});
+}
+
+// Spin (one lane) until *c >= target.  The wait is bounded (about a second);
+// on giving up it raises the error word, after which every later wait of the
+// launch returns at once, so the launch always finishes.
 __device__ void wait_for(const unsigned* c, unsigned target, unsigned* err) {
   unsigned spins = 0;
   while (get(c) < target) {
@@ -79,6 +133,13 @@ __device__ void wait_for(const unsigned* c, unsigned target, unsigned* err) {
   }
 }
 
+// Arrival of one consumer wave (lane 0, after its stores completed): a rank
+// counts kRoleWaves arrivals per phase.  Nothing waits for the atomic itself;
+// counters only grow during a launch and the last workgroup clears them.
+__device__ __forceinline__ void arrive(unsigned* c) {
+  (void)__hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ void tile_origin(const FlowArgs& a, int t, int& r0, int& c0) {
   r0 = (t / a.tiles_x) * a.TR;
   c0 = (t % a.tiles_x) * a.TC;
@@ -89,25 +150,29 @@ __device__ __forceinline__ TileLayout layout_of(const FlowArgs& a) {
   return tile_layout(a.TR, a.TC, a.weights ? a.T : 0, (int)sizeof(typename Tr::S));
 }
 
-// ---------------------------------------------------------------------------
-// Staging DMA (no wait here).
-// ---------------------------------------------------------------------------
-// A KV / M item's K rows, and its V (KV) or Q (M) rows.
-template <class Tr>
-__device__ void stage_chunk(const FlowArgs& a, Item it, unsigned char* buf) {
-  using S = typename Tr::S;
-  const int tok0 = it.idx * a.chunk;
-  const int nv = min(a.chunk, a.n - tok0);
-  const S* Kb = static_cast<const S*>(a.K) + ((size_t)it.b * a.n + tok0) * kD;
-  const S* Xb = static_cast<const S*>(it.kind == kKV ? a.V : a.Q) + ((size_t)it.b * a.n + tok0) * kD;
-  dma_rows<Tr>(buf, nv, [&](int r) { return static_cast<const void*>(Kb + (size_t)r * kD); });
-  dma_rows<Tr>(buf + LdsOf<Tr>::kXOff, nv, [&](int r) { return static_cast<const void*>(Xb + (size_t)r * kD); });
+// Chunk j of the rank's range: first token and length.
+__device__ __forceinline__ void chunk_of(const FlowArgs& a, const Rank& r, int j, int& tok0, int& nv) {
+  tok0 = r.tok0 + j * a.chunk;
+  nv = min(a.chunk, r.tok0 + r.ntok - tok0);
 }
 
-// Output tile t of slice b (see TileLayout).  Cells and token slots off the
-// grid fetch token 0 of the slice; they are never used.
+// ---------------------------------------------------------------------------
+// Producer side (pw = producer wave, 0..3).
+// ---------------------------------------------------------------------------
+// DMA of a KV / M chunk: its K rows, and its V (KV) or Q (M) rows.
 template <class Tr>
-__device__ void stage_tile(const FlowArgs& a, int b, int t, unsigned char* buf) {
+__device__ void stage_chunk(const FlowArgs& a, int b, bool is_m, int tok0, int nv, unsigned char* buf, int pw) {
+  using S = typename Tr::S;
+  const S* Kb = static_cast<const S*>(a.K) + ((size_t)b * a.n + tok0) * kD;
+  const S* Xb = static_cast<const S*>(is_m ? a.Q : a.V) + ((size_t)b * a.n + tok0) * kD;
+  dma_rows<Tr>(buf, nv, [&](int r) { return static_cast<const void*>(Kb + (size_t)r * kD); }, pw);
+  dma_rows<Tr>(buf + LdsOf<Tr>::kXOff, nv, [&](int r) { return static_cast<const void*>(Xb + (size_t)r * kD); }, pw);
+}
+
+// DMA of output tile t of slice b (see TileLayout).  Cells and token slots
+// off the grid fetch token 0 of the slice; they are never used.
+template <class Tr>
+__device__ void stage_tile(const FlowArgs& a, int b, int t, unsigned char* buf, int pw) {
   using S = typename Tr::S;
   const TileLayout L = layout_of<Tr>(a);
   int r0, c0;
@@ -130,17 +195,17 @@ __device__ void stage_tile(const FlowArgs& a, int b, int t, unsigned char* buf) 
     const bool on = (row < a.H) & (col < a.W);
     return (size_t)(on ? row * a.W + col : 0);
   };
-  dma_rows<Tr>(buf + L.k, L.cells, [&](int r) { return static_cast<const void*>(Kb + cell_tok(r) * kD); });
-  dma_rows<Tr>(buf + L.v, L.cells, [&](int r) { return static_cast<const void*>(Vb + cell_tok(r) * kD); });
-  dma_rows<Tr>(buf + L.q, L.tokens, [&](int r) { return static_cast<const void*>(Qb + slot_tok(r) * kD); });
+  dma_rows<Tr>(buf + L.k, L.cells, [&](int r) { return static_cast<const void*>(Kb + cell_tok(r) * kD); }, pw);
+  dma_rows<Tr>(buf + L.v, L.cells, [&](int r) { return static_cast<const void*>(Vb + cell_tok(r) * kD); }, pw);
+  dma_rows<Tr>(buf + L.q, L.tokens, [&](int r) { return static_cast<const void*>(Qb + slot_tok(r) * kD); }, pw);
   if (a.weights) {
-    // T floats per slot, 4 bytes per lane; the last instruction's spare lanes
-    // repeat the last element into the region's padding.
-    const int lane = threadIdx.x & 63, wave = wave_id();
+    // T floats per slot, 4 bytes per lane, 64 per wave instruction; the last
+    // instruction's spare lanes repeat the last element into the padding.
+    const int lane = threadIdx.x & 63;
     const int cnt = L.tokens * a.T;
     const float* wb = a.weights + base * a.T;
     const float inv_t = 1.f / (float)a.T;
-    for (int e0 = wave * 64; e0 < cnt; e0 += 256) {
+    for (int e0 = pw * 64; e0 < cnt; e0 += 256) {
       const int e = min(e0 + lane, cnt - 1);
       const int sl = div_small(e, inv_t);
       dma4(wb + slot_tok(sl) * a.T + (e - sl * a.T), lds_addr(buf + L.w + e0 * 4));
@@ -148,13 +213,144 @@ __device__ void stage_tile(const FlowArgs& a, int b, int t, unsigned char* buf) 
   }
 }
 
-// The first stage of an item (C items stage nothing).
+// After the wave's own DMA has landed: zero the chunk's rows [nv, nvr) (the
+// sweeps read whole 16-row steps) and, for M chunks, rewrite each Q row as
+// r_j phi(Q_j) with r_j = 1 / (phi(Q_j) . s + eps).  A wave only touches the
+// 1 KB runs it issued itself (run j belongs to wave j % 4): each lane holds
+// one 16-byte piece, and the lanes of a row reduce the dot product together.
+template <class Tr, bool kIsM>
+__device__ void finish_chunk(const FlowArgs& a, int nv, unsigned char* buf, const float* s, int pw) {
+  constexpr int RPR = 1024 / Tr::RB;  // rows per run
+  const int lane = threadIdx.x & 63;
+  const int nvr = (nv + 15) & ~15;
+  unsigned char* bK = buf;
+  unsigned char* bX = buf + LdsOf<Tr>::kXOff;
+  const int slot = lane % Tr::PPR;
+  for (int j = pw; j * RPR < nvr; j += 4) {
+    if (!kIsM && (j + 1) * RPR <= nv) continue;  // nothing to zero in this run
+    const int r = j * RPR + lane / Tr::PPR;
+    const int g = (slot ^ swz(r)) & (Tr::PPR - 1);  // the piece in this slot
+    uint4* pK = reinterpret_cast<uint4*>(bK + r * Tr::RB + slot * 16);
+    uint4* pX = reinterpret_cast<uint4*>(bX + r * Tr::RB + slot * 16);
+    if (kIsM) {
+      float x[Tr::EPP];
+      if constexpr (Tr::EPP == 8) {
+        load4(reinterpret_cast<const uint16_t*>(pX), x);
+        load4(reinterpret_cast<const uint16_t*>(pX) + 4, x + 4);
+      } else {
+        load4(reinterpret_cast<const float*>(pX), x);
+      }
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < Tr::EPP; ++e) {
+        x[e] = fmaxf(x[e], 0.f);
+        dot += x[e] * s[g * Tr::EPP + e];
+      }
+#pragma unroll
+      for (int o = 1; o < Tr::PPR; o <<= 1) dot += __shfl_xor(dot, o);
+      const float rr = 1.f / (dot + a.eps);
+#pragma unroll
+      for (int e = 0; e < Tr::EPP; ++e) x[e] *= rr;
+      if (r < nv) {
+        if constexpr (Tr::EPP == 8) {
+          store4(reinterpret_cast<uint16_t*>(pX), x);
+          store4(reinterpret_cast<uint16_t*>(pX) + 4, x + 4);
+        } else {
+          store4(reinterpret_cast<float*>(pX), x);
+        }
+      }
+    }
+    if (r >= nv) {
+      *pK = make_uint4(0, 0, 0, 0);
+      *pX = make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+// Lane l of a wave: s[l] = fixed-order sum over the G ranks' partials.
+__device__ __forceinline__ float sum_s_partials(const FlowArgs& a, int b) {
+  const int lane = threadIdx.x & 63;
+  const float* ps = a.part_s + (size_t)b * a.G * kD + lane;
+  float t = 0.f;
+  for (int p0 = 0; p0 < a.G; p0 += 16) {
+    float x[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) x[q] = get(ps + (size_t)min(p0 + q, a.G - 1) * kD);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) t += (p0 + q < a.G) ? x[q] : 0.f;
+  }
+  return t;
+}
+
+// Producer waves: make stage `p` ready for the consumers in `buf` and, at the
+// start of an OUT phase, in the statistics area `st`: issue the DMA, wait for
+// the dependency, load what other workgroups wrote, wait, finish.  Only
+// producer wave 0 polls the arrival counter; it then posts `tag` in `dep_ok`,
+// which the other producer waves watch in LDS.  `s_w` is this wave's 64-float
+// scratch in LDS (s of the slice whose M chunks it prepares).
 template <class Tr>
-__device__ void stage_first(const FlowArgs& a, Item it, unsigned char* buf) {
-  if (it.kind == kKV || it.kind == kM)
-    stage_chunk<Tr>(a, it, buf);
-  else if (it.kind == kOut)
-    stage_tile<Tr>(a, it.b, it.idx * a.R, buf);
+__device__ void prepare(const FlowArgs& a, const Rank& rk, Pos p, unsigned char* buf, unsigned char* st,
+                        float* s_w, volatile int* dep_ok, int pw) {
+  using S = typename Tr::S;
+  using L = LdsOf<Tr>;
+  const int lane = threadIdx.x & 63;
+  const int b = slice_of(a, rk, p.r, p.z);
+  const unsigned* cnt = a.slice_cnt + (size_t)b * kCntWords;
+  const unsigned full = kRoleWaves * a.G;
+  auto dependency = [&](int counter) {
+    const int tag = b * 4 + p.ph;
+    if (pw == 0) {
+      if (lane == 0) {
+        wait_for(&cnt[counter], full, a.err);
+        *dep_ok = tag;
+      }
+    } else if (lane == 0) {
+      while (*dep_ok != tag) __builtin_amdgcn_s_sleep(1);  // wave 0 always posts
+    }
+  };
+  if (p.ph == kPKV || p.ph == kPM) {
+    const bool is_m = p.ph == kPM;
+    int tok0, nv;
+    chunk_of(a, rk, p.j, tok0, nv);
+    stage_chunk<Tr>(a, b, is_m, tok0, nv, buf, pw);
+    if (is_m && p.j == 0) {
+      dependency(kCntKV);
+      const float sv = sum_s_partials(a, b);
+      s_w[lane] = sv;
+      if (rk.g == 0 && pw == 0) put(a.fin_s + (size_t)b * kD + lane, sv);
+    }
+    wait_all();
+    if (is_m)
+      finish_chunk<Tr, true>(a, nv, buf, s_w, pw);
+    else
+      finish_chunk<Tr, false>(a, nv, buf, s_w, pw);
+  } else if (p.ph == kPC) {
+    dependency(a.do_m ? kCntM : kCntKV);
+    if (!a.do_m && rk.g == 0 && pw == 0) put(a.fin_s + (size_t)b * kD + lane, sum_s_partials(a, b));
+    // The G partials' elements [e0, e0 + E), coherent (other workgroups wrote
+    // them), as [G][E] floats: 16 bytes per lane, 1 KB per wave instruction.
+    const int total = a.G * rk.E;
+    for (int q0 = pw * 256; q0 < total; q0 += 1024) {
+      const int q = q0 + lane * 4;
+      const int part = q / rk.E, f = rk.e0 + q % rk.E;
+      const float* src = (f < kD * kD ? a.part_kv : a.part_m) + ((size_t)b * a.G + part) * (kD * kD) + (f % (kD * kD));
+      dma16_coherent(src, lds_addr(buf + q0 * 4));
+    }
+    wait_all();
+  } else if (p.ph == kPOut) {
+    stage_tile<Tr>(a, b, rk.t0 + p.j, buf, pw);
+    if (p.j == 0) {
+      if (a.do_kv) dependency(kCntC);
+      if (a.T >= 2) {
+        dma_linear_coherent(st, static_cast<const S*>(a.frag_kv) + (size_t)b * (kD * kD), L::kFragBytes, pw);
+        if (a.T >= 3)
+          dma_linear_coherent(st + L::kFragBytes, static_cast<const S*>(a.frag_m) + (size_t)b * (kD * kD),
+                              L::kFragBytes, pw);
+        dma_linear_coherent(st + 2 * L::kFragBytes, a.fin_s + (size_t)b * kD, kD * 4, pw);
+      }
+    }
+    wait_all();
+  }
 }
 
 // Element d of staged fp32 row r.
@@ -163,62 +359,18 @@ __device__ __forceinline__ float lds_elem(const unsigned char* base, int r, int 
 }
 
 // ---------------------------------------------------------------------------
-// KV / M items: contraction over the chunk's tokens.  Wave w owns block
-// (w / 2, w % 2) of the 64x64 result; A = phi(K) rows, B = V rows (KV) or
-// r_j phi(Q_j) rows rounded to the input dtype (M, rescaled in LDS first).
-// KV items also form s with a second MFMA against a ones operand.  Rows past
-// the chunk's last token are zeroed in LDS, so the sweep needs no masks.
+// Consumer side (cw = consumer wave, 0..3; ct = thread index in the role).
 // ---------------------------------------------------------------------------
-template <class Tr, bool kIsM, class Prefetch>
-__device__ void stats_item(const FlowArgs& a, Item it, unsigned char* buf, float* s_sh,
-                           Prefetch prefetch) {
-  using S = typename Tr::S;
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int m = lane & 31, h = lane >> 5, mb = wave >> 1, nb = wave & 1;
-  const int tok0 = it.idx * a.chunk;
-  const int nv = min(a.chunk, a.n - tok0);
+// One chunk of a KV / M sweep, accumulated into acc (and acc_s: s, KV only).
+// Wave cw owns block (cw / 2, cw % 2) of the 64x64 result; A = phi(K) rows,
+// B = V rows (KV) or the rescaled Q rows (M); rows past the chunk are zero.
+template <class Tr, bool kIsM>
+__device__ __forceinline__ void sweep_chunk(const unsigned char* buf, int nv, int cw, f32x16& acc, f32x16& acc_s) {
+  const int lane = threadIdx.x & 63;
+  const int m = lane & 31, h = lane >> 5, mb = cw >> 1, nb = cw & 1;
   const int nvr = (nv + 15) & ~15;
-  unsigned char* bK = buf;
-  unsigned char* bX = buf + LdsOf<Tr>::kXOff;
-
-  if (kIsM && tid < kD) {  // s = sum of the KV items' partials, fixed order
-    float t = 0.f;
-    for (int p = 0; p < a.nKV; ++p) t += get(a.part_s + ((size_t)it.b * a.P + p) * kD + tid);
-    s_sh[tid] = t;
-  }
-  wait_all();  // nothing of this item is loaded after the next stage's DMA goes out
-  prefetch();
-  if (kIsM || nv < nvr) {
-    if (kIsM) lds_barrier();
-    for (int t = tid; t < nvr; t += kThreads) {
-      if (t >= nv) {
-#pragma unroll
-        for (int g = 0; g < Tr::PPR; ++g) {
-          *reinterpret_cast<uint4*>(bK + t * Tr::RB + g * 16) = make_uint4(0, 0, 0, 0);
-          *reinterpret_cast<uint4*>(bX + t * Tr::RB + g * 16) = make_uint4(0, 0, 0, 0);
-        }
-      } else if (kIsM) {
-        // r_t = 1 / (phi(Q_t) . s + eps); the row becomes r_t phi(Q_t).
-        float x[kD];
-#pragma unroll
-        for (int c = 0; c < kD / 4; ++c) load4(reinterpret_cast<const S*>(bX + row_off<Tr>(t, 4 * c)), &x[4 * c]);
-        float dot = 0.f;
-#pragma unroll
-        for (int d = 0; d < kD; ++d) {
-          x[d] = fmaxf(x[d], 0.f);
-          dot += x[d] * s_sh[d];
-        }
-        const float r = 1.f / (dot + a.eps);
-#pragma unroll
-        for (int d = 0; d < kD; ++d) x[d] *= r;
-#pragma unroll
-        for (int c = 0; c < kD / 4; ++c) store4(reinterpret_cast<S*>(bX + row_off<Tr>(t, 4 * c)), &x[4 * c]);
-      }
-    }
-    lds_barrier();
-  }
-
-  f32x16 acc = {}, acc_s = {};
+  const unsigned char* bK = buf;
+  const unsigned char* bX = buf + LdsOf<Tr>::kXOff;
   for (int kk = 0; kk < nvr; kk += 16) {
     if constexpr (Tr::EPL == 8) {
       const bf16x8 A = as_bf16(rows_bits<true>(bK, kk, 32 * mb));
@@ -236,96 +388,81 @@ __device__ void stats_item(const FlowArgs& a, Item it, unsigned char* buf, float
       }
     }
   }
+}
 
-  // Partials, shared through coherent stores.
-  float* part = (kIsM ? a.part_m : a.part_kv) + ((size_t)it.b * a.P + it.idx) * (kD * kD);
+// The KV or M phase of slice b: the rank's chunks, one stage each, then its
+// partial (coherent stores) and the wave's arrival.
+template <class Tr, bool kIsM>
+__device__ int consume_sweep(const FlowArgs& a, const Rank& rk, int b, unsigned char* smem, int bsel, int cw) {
+  using L = LdsOf<Tr>;
+  const int lane = threadIdx.x & 63;
+  const int m = lane & 31, h = lane >> 5, mb = cw >> 1, nb = cw & 1;
+  f32x16 acc = {}, acc_s = {};
+  for (int j = 0; j < rk.nch; ++j) {
+    int tok0, nv;
+    chunk_of(a, rk, j, tok0, nv);
+    sweep_chunk<Tr, kIsM>(smem + bsel * L::kStage, nv, cw, acc, acc_s);
+    if (j + 1 < rk.nch) {
+      lds_barrier();
+      bsel ^= 1;
+    }
+  }
+  float* part = (kIsM ? a.part_m : a.part_kv) + ((size_t)b * a.G + rk.g) * (kD * kD);
 #pragma unroll
   for (int i = 0; i < 16; ++i) put(part + (32 * mb + 8 * (i >> 2) + 4 * h + (i & 3)) * kD + 32 * nb + m, acc[i]);
   if (!kIsM && nb == 0 && m == 0) {
-    float* ps = a.part_s + ((size_t)it.b * a.P + it.idx) * kD;
+    float* ps = a.part_s + ((size_t)b * a.G + rk.g) * kD;
 #pragma unroll
     for (int i = 0; i < 16; ++i) put(ps + 32 * mb + 8 * (i >> 2) + 4 * h + (i & 3), acc_s[i]);
   }
   wait_all();
+  if (lane == 0) arrive(a.slice_cnt + (size_t)b * kCntWords + (kIsM ? kCntM : kCntKV));
   lds_barrier();
-  if (tid == 0) {
-    unsigned* cnt = a.slice_cnt + (size_t)it.b * kCntWords;
-    const unsigned old = bump(&cnt[kIsM ? kM : kKV]);
-    // The last M item of a slice: every M item has passed its wait on the
-    // KV count, which can now be cleared for the next launch.
-    if (kIsM && old == (unsigned)(a.nM - 1)) put(&cnt[kKV], 0u);
+  return bsel ^ 1;
+}
+
+// Store element f of the flattened [phi(K)^T V | M] (value v) as fp32 and in
+// its MFMA fragment slot: fragment (mb, q', lane, e) holds
+// X[dimof(q' EPL + e, lane / 32)][32 mb + lane % 32].
+template <class Tr>
+__device__ __forceinline__ void store_stat(const FlowArgs& a, int b, int f, float v) {
+  const int mat = f >> 12, r = (f >> 6) & 63, c = f & 63;
+  (mat == 0 ? a.fin_kv : a.fin_m)[(size_t)b * (kD * kD) + r * kD + c] = v;
+  const int vs = 16 * (r >> 5) + 4 * ((r >> 3) & 3) + (r & 3);
+  const int ln = (c & 31) + 32 * ((r >> 2) & 1);
+  const int idx = (((c >> 5) * Tr::NQ + vs / Tr::EPL) * 64 + ln) * Tr::EPL + vs % Tr::EPL;
+  if constexpr (Tr::EPL == 8) {
+    uint16_t* fr = static_cast<uint16_t*>(mat == 0 ? a.frag_kv : a.frag_m) + (size_t)b * (kD * kD);
+    __hip_atomic_store(fr + idx, f2bf(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    float* fr = static_cast<float*>(mat == 0 ? a.frag_kv : a.frag_m) + (size_t)b * (kD * kD);
+    put(fr + idx, v);
   }
 }
 
-// ---------------------------------------------------------------------------
-// C items: fixed-order sum of the P partials of rows [16 rb, 16 rb + 16) of
-// phi(K)^T V (q < 4) or M (q >= 4); fp32 result plus MFMA fragments, where
-// fragment (mb, q', lane, e) holds X[dimof(q' EPL + e, lane / 32)][32 mb + lane % 32].
-// ---------------------------------------------------------------------------
+// The C phase of slice b: elements [e0, e0 + E) summed over the G staged
+// partials in a fixed order.  With E < 256, TPE = 256 / E threads share an
+// element (partials p = q, q + TPE, ...) and combine by a fixed xor tree.
 template <class Tr>
-__device__ void combine_item(const FlowArgs& a, Item it) {
-  constexpr int kBatch = 16;
-  const int tid = threadIdx.x;
-  const int mat = it.idx / kCombineBlocks, rb = it.idx % kCombineBlocks;
-  const float* part = (mat == 0 ? a.part_kv : a.part_m) + (size_t)it.b * a.P * (kD * kD);
-  const int col = tid & 63, rp = tid >> 6;
-  int rows[4];
-  rows[0] = 16 * rb + 2 * rp;
-  rows[1] = rows[0] + 1;
-  rows[2] = 16 * rb + 2 * (rp + 4);
-  rows[3] = rows[2] + 1;
-  float v[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int p0 = 0; p0 < a.P; p0 += kBatch) {
-    float x[kBatch][4];
-#pragma unroll
-    for (int bb = 0; bb < kBatch; ++bb) {
-      const int p = min(p0 + bb, a.P - 1);  // loads stay unconditional; extra ones are masked below
-#pragma unroll
-      for (int j = 0; j < 4; ++j) x[bb][j] = get(part + (size_t)p * (kD * kD) + rows[j] * kD + col);
+__device__ void consume_combine(const FlowArgs& a, const Rank& rk, int b, const unsigned char* buf, int ct) {
+  const float* stg = reinterpret_cast<const float*>(buf);  // [G][E]
+  if (rk.E >= kRoleWaves * 64) {
+    for (int e = ct; e < rk.E; e += kRoleWaves * 64) {
+      float v = 0.f;
+      for (int p = 0; p < a.G; ++p) v += stg[p * rk.E + e];
+      store_stat<Tr>(a, b, rk.e0 + e, v);
     }
-#pragma unroll
-    for (int bb = 0; bb < kBatch; ++bb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] += (p0 + bb < a.P) ? x[bb][j] : 0.f;
-  }
-  const bool do_s = (it.idx == 0) && tid < kD;
-  float sv = 0.f;
-  if (do_s)
-    for (int p = 0; p < a.P; ++p) sv += get(a.part_s + ((size_t)it.b * a.P + p) * kD + tid);
-
-  float* fin = (mat == 0 ? a.fin_kv : a.fin_m) + (size_t)it.b * (kD * kD);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) fin[rows[j] * kD + col] = v[j];
-  if (do_s) put(a.fin_s + (size_t)it.b * kD + tid, sv);
-  void* fragv = mat == 0 ? a.frag_kv : a.frag_m;
-  const int mbo = col >> 5, mm = col & 31;
-#pragma unroll
-  for (int j = 0; j < 4; j += 2) {
-    const int r = rows[j];  // even: r and r + 1 sit in adjacent fragment slots
-    const int vs = 16 * (r >> 5) + 4 * ((r & 31) >> 3) + (r & 3);
-    const int hh = (r & 7) >> 2;
-    const int ln = mm + 32 * hh;
-    if constexpr (Tr::EPL == 8) {
-      const int f = ((mbo * Tr::NQ + (vs >> 3)) * 64 + ln) * 8 + (vs & 7);
-      uint32_t* w = static_cast<uint32_t*>(fragv) + (size_t)it.b * (kD * kD / 2) + (f >> 1);
-      put(w, (uint32_t)f2bf(v[j]) | ((uint32_t)f2bf(v[j + 1]) << 16));
-    } else {
-      float* fv = static_cast<float*>(fragv) + (size_t)it.b * (kD * kD);
-      put(fv + (mbo * Tr::NQ + vs) * 64 + ln, v[j]);
-      put(fv + (mbo * Tr::NQ + vs + 1) * 64 + ln, v[j + 1]);
-    }
+  } else {
+    const int tpe = kRoleWaves * 64 / rk.E;  // 2..8, consecutive lanes
+    const int e = ct / tpe, q = ct % tpe;
+    float v = 0.f;
+    for (int p = q; p < a.G; p += tpe) v += stg[p * rk.E + e];
+    for (int o = 1; o < tpe; o <<= 1) v += __shfl_xor(v, o);
+    if (q == 0) store_stat<Tr>(a, b, rk.e0 + e, v);
   }
   wait_all();
+  if ((threadIdx.x & 63) == 0) arrive(a.slice_cnt + (size_t)b * kCntWords + kCntC);
   lds_barrier();
-  if (tid == 0) {
-    unsigned* cnt = a.slice_cnt + (size_t)it.b * kCntWords;
-    const unsigned old = bump(&cnt[kC]);
-    if (old == (unsigned)(a.nC - 1)) {
-      // Every C item of the slice has passed its wait: clear that count.
-      put(&cnt[a.nM ? kM : kKV], 0u);
-      if (!(a.nOUT && a.wait_out)) put(&cnt[kC], 0u);
-    }
-  }
 }
 
 // Window slots of the MFMA local branch: logit slot v (0..31) of lane half h
@@ -517,19 +654,19 @@ __device__ __forceinline__ void local_token_valu(const FlowArgs& a, const unsign
 
 // ---------------------------------------------------------------------------
 // One output tile (whole 4x8 token blocks) of slice b, all inputs in LDS.
-// Each wave takes a block at a time, one token per lane pair: lanes m and
-// m + 32 hold 32 features each in accumulator layout, so the chain
-// u_1 = phi(Q_i), u_k = u_(k-1) M and the projection z (phi(K)^T V),
-// z = sum_k w_k(i) u_k, run on MFMA with no data movement.
+// Consumer wave cw takes blocks cw, cw + 4, ..., one token per lane pair:
+// lanes m and m + 32 hold 32 features each in accumulator layout, so the
+// chain u_1 = phi(Q_i), u_k = u_(k-1) M and the projection z (phi(K)^T V),
+// z = sum_k w_k(i) u_k, run on MFMA with no data movement.  `sl` is s in LDS.
 // ---------------------------------------------------------------------------
 template <class Tr>
 __device__ __forceinline__ void out_tile(const FlowArgs& a, int b, int t, const unsigned char* buf,
                                          const typename Tr::Frag (&fkv)[2][Tr::NQ],
                                          const typename Tr::Frag (&fm)[2][Tr::NQ], const float* sl,
-                                         float alpha, unsigned nbr) {
+                                         float alpha, unsigned nbr, int cw) {
   using S = typename Tr::S;
   constexpr bool kMfmaLocal = Tr::EPL == 8;
-  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int lane = threadIdx.x & 63;
   const int n = lane & 31, h = lane >> 5;
   const TileLayout Lt = layout_of<Tr>(a);
   int r0, c0;
@@ -543,7 +680,7 @@ __device__ __forceinline__ void out_tile(const FlowArgs& a, int b, int t, const 
   S* Yb = static_cast<S*>(a.Y) + (size_t)b * a.n * kD;
   const bool global = a.T >= 2;
 
-  for (int blk = wave; blk < nblk; blk += kThreads / 64) {
+  for (int blk = cw; blk < nblk; blk += kRoleWaves) {
     const int br = blk / CB, bc = blk % CB;
     if (r0 + 4 * br >= a.H || c0 + 8 * bc >= a.W) continue;  // no token of the block is on the grid
     const int tr = 4 * br + (n >> 3), tc = 8 * bc + (n & 7);
@@ -627,64 +764,33 @@ __device__ __forceinline__ void out_tile(const FlowArgs& a, int b, int t, const 
   }
 }
 
-// OUT item: tiles [idx R, idx R + R) of slice b.  The slice's statistics are
-// read once per item: fragments and s by coherent DMA into the statistics
-// area, then into registers.  Tile k + 1's DMA is issued before tile k is
-// computed; the last tile issues the next item's first stage.  Returns the
-// staging buffer that the next item's first stage went to.
-template <class Tr, class Prefetch>
-__device__ int out_item(const FlowArgs& a, Item it, unsigned char* smem, int bsel, Prefetch prefetch_next) {
-  using S = typename Tr::S;
+// The OUT phase of slice b: take the slice statistics out of the statistics
+// area (fragments into registers, s into `s_own`), free the area (barrier),
+// then compute the rank's tiles, one stage each.  Returns the buffer index.
+template <class Tr>
+__device__ int consume_out(const FlowArgs& a, const Rank& rk, int b, unsigned char* smem, int bsel, float* s_own,
+                           int cw) {
   using Frag = typename Tr::Frag;
   using L = LdsOf<Tr>;
-  const int lane = threadIdx.x & 63, h = lane >> 5;
-  const int b = it.b;
-  const int t0 = it.idx * a.R, nt = min(a.R, a.ntiles - t0);
-  unsigned char* st = smem + 2 * L::kStage;
-
+  const int lane = threadIdx.x & 63;
+  const unsigned char* st = smem + 2 * L::kStage;
   Frag fkv[2][Tr::NQ], fm[2][Tr::NQ];
-  const float* sl = reinterpret_cast<const float*>(st + 2 * L::kFragBytes);  // s, in LDS
-  if (a.T >= 2) {
-    dma_linear_coherent(st, static_cast<const S*>(a.frag_kv) + (size_t)b * (kD * kD), L::kFragBytes);
-    if (a.T >= 3)
-      dma_linear_coherent(st + L::kFragBytes, static_cast<const S*>(a.frag_m) + (size_t)b * (kD * kD), L::kFragBytes);
-    dma_linear_coherent(st + 2 * L::kFragBytes, a.fin_s + (size_t)b * kD, kD * 4);
-    wait_all();
-    lds_barrier();
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int q = 0; q < Tr::NQ; ++q) {
-        const int off = ((mb * Tr::NQ + q) * 64 + lane) * (int)sizeof(Frag);
-        fkv[mb][q] = *reinterpret_cast<const Frag*>(st + off);
-        fm[mb][q] = *reinterpret_cast<const Frag*>(st + L::kFragBytes + off);
-      }
-  } else {
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int q = 0; q < Tr::NQ; ++q) {
-        fkv[mb][q] = Frag{};
-        fm[mb][q] = Frag{};
-      }
-  }
-  const float alpha = a.alpha[b % a.heads];
-  wait_all();
-  const int tok = lane & 31;
-  const unsigned nbr = neighbour_slots(tok >> 3, tok & 7, h);
-
-  for (int k = 0; k < nt; ++k) {
-    unsigned char* cb = smem + bsel * L::kStage;
-    unsigned char* nb = smem + (bsel ^ 1) * L::kStage;
-    if (k > 0) {
-      wait_all();
-      lds_barrier();
+    for (int q = 0; q < Tr::NQ; ++q) {
+      const int off = ((mb * Tr::NQ + q) * 64 + lane) * (int)sizeof(Frag);
+      fkv[mb][q] = *reinterpret_cast<const Frag*>(st + off);
+      fm[mb][q] = *reinterpret_cast<const Frag*>(st + L::kFragBytes + off);  // unused unless T >= 3
     }
-    if (k + 1 < nt)
-      stage_tile<Tr>(a, b, t0 + k + 1, nb);
-    else
-      prefetch_next(nb);
-    out_tile<Tr>(a, b, t0 + k, cb, fkv, fm, sl, alpha, nbr);
+  if (cw == 0) s_own[lane] = reinterpret_cast<const float*>(st + 2 * L::kFragBytes)[lane];
+  const float alpha = a.alpha[b % a.heads];
+  const int tok = lane & 31;
+  const unsigned nbr = neighbour_slots(tok >> 3, tok & 7, lane >> 5);
+  lds_barrier();  // the statistics area may now be refilled; s_own is complete
+  for (int k = 0; k < rk.nt; ++k) {
+    out_tile<Tr>(a, b, rk.t0 + k, smem + bsel * L::kStage, fkv, fm, s_own, alpha, nbr, cw);
+    lds_barrier();
     bsel ^= 1;
   }
   return bsel;
@@ -694,81 +800,72 @@ template <class Tr>
 __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
   using L = LdsOf<Tr>;
   extern __shared__ __align__(1024) unsigned char smem[];
-  __shared__ float s_sh[kD];
-  __shared__ int sh_t[3];
+  __shared__ float s_w[kRoleWaves][kD];  // producers: s of the slice whose M chunks they prepare
+  __shared__ float s_own[kD];            // consumers: s of the slice of the current OUT phase
+  __shared__ int dep_ok;                 // tag of the stage whose dependency producer wave 0 has seen met
+  __shared__ int last;                   // this workgroup's ticket, later: it finished last
   const int tid = threadIdx.x;
-  const int x = blockIdx.x % a.nq;
-  unsigned* qc = a.queue_cnt + x;
-  const int total = queue_items(a, x);
+  const int wave = wave_id();
+  const bool producer = wave < kRoleWaves;
+  const int rw = producer ? wave : wave - kRoleWaves;  // wave index within the role
+  unsigned char* st = smem + 2 * L::kStage;
 
   if (tid == 0) {
-    sh_t[0] = (int)bump(qc);
-    sh_t[1] = (int)bump(qc);
+    dep_ok = -1;
+    last = (int)bump(a.tickets + (a.xcd_groups ? blockIdx.x % kXcds : 0));
   }
   __syncthreads();
-  int cur = sh_t[0], nxt = sh_t[1];
-  int bsel = 0;
-  if (cur < total) stage_first<Tr>(a, decode(a, x, cur), smem);
-
-  while (cur < total) {
-    const Item it = decode(a, x, cur);
-    const Item nit = nxt < total ? decode(a, x, nxt) : Item{kNone, 0, 0};
-    wait_all();  // this item's first stage (and everything before it)
+  const Rank rk = make_rank(a, last);
+  // The roles run separate loops over the same stage sequence, with the same
+  // barriers: one per stage, plus one at the start of each OUT phase.
+  if (producer) {
+    Pos p = first_pos(a, rk);
+    if (p.ph != kPEnd) prepare<Tr>(a, rk, p, smem, st, s_w[rw], &dep_ok, rw);
     lds_barrier();
-    unsigned char* nb = smem + (bsel ^ 1) * L::kStage;
-    auto prefetch_into = [&](unsigned char* dst) {
-      if (nit.kind != kNone) stage_first<Tr>(a, nit, dst);
-    };
-    // C items stage nothing, so the next item's inputs can go out before the wait.
-    if (it.kind == kC) prefetch_into(nb);
-    if (tid == 0) {
-      const int t2 = (int)bump(qc);
-      unsigned* cnt = a.slice_cnt + (size_t)it.b * kCntWords;
-      if (it.kind == kM) {
-        wait_for(&cnt[kKV], a.nKV, a.err);
-      } else if (it.kind == kC) {
-        if (a.nM)
-          wait_for(&cnt[kM], a.nM, a.err);
-        else
-          wait_for(&cnt[kKV], a.nKV, a.err);
-      } else if (it.kind == kOut && a.wait_out) {
-        wait_for(&cnt[kC], a.nC, a.err);
-        // Count the OUT items past their wait; the last clears both counts.
-        const unsigned old = bump(&cnt[kOut]);
-        if (old == (unsigned)(a.nOUT - 1)) {
-          put(&cnt[kC], 0u);
-          put(&cnt[kOut], 0u);
-        }
+    int bsel = 0;
+    while (p.ph != kPEnd) {
+      const Pos np = advance(a, rk, p);
+      if (p.ph == kPOut && p.j == 0) lds_barrier();  // the consumers have taken the statistics
+      if (np.ph != kPEnd) prepare<Tr>(a, rk, np, smem + (bsel ^ 1) * L::kStage, st, s_w[rw], &dep_ok, rw);
+      lds_barrier();
+      bsel ^= 1;
+      p = np;
+    }
+  } else {
+    lds_barrier();
+    int bsel = 0;
+    if (rk.group >= 0) {
+      // Phases are entered exactly when the producers' sequence has them.
+      for (int r = 0; round_slices(a, rk, r) > 0; ++r) {
+        const int nz = round_slices(a, rk, r);
+        if (phase_len(a, rk, kPKV) > 0)
+          for (int z = 0; z < nz; ++z) bsel = consume_sweep<Tr, false>(a, rk, slice_of(a, rk, r, z), smem, bsel, rw);
+        if (phase_len(a, rk, kPM) > 0)
+          for (int z = 0; z < nz; ++z) bsel = consume_sweep<Tr, true>(a, rk, slice_of(a, rk, r, z), smem, bsel, rw);
+        if (phase_len(a, rk, kPC) > 0)
+          for (int z = 0; z < nz; ++z) {
+            consume_combine<Tr>(a, rk, slice_of(a, rk, r, z), smem + bsel * L::kStage, tid - kRoleWaves * 64);
+            bsel ^= 1;
+          }
+        if (phase_len(a, rk, kPOut) > 0)
+          for (int z = 0; z < nz; ++z) bsel = consume_out<Tr>(a, rk, slice_of(a, rk, r, z), smem, bsel, s_own, rw);
       }
-      sh_t[2] = t2;
     }
-    lds_barrier();
-    const int after = sh_t[2];
-    unsigned char* cb = smem + bsel * L::kStage;
-    auto prefetch = [&]() { prefetch_into(nb); };
-    if (it.kind == kKV) {
-      stats_item<Tr, false>(a, it, cb, s_sh, prefetch);
-      bsel ^= 1;
-    } else if (it.kind == kM) {
-      stats_item<Tr, true>(a, it, cb, s_sh, prefetch);
-      bsel ^= 1;
-    } else if (it.kind == kC) {
-      combine_item<Tr>(a, it);
-      bsel ^= 1;
-    } else {
-      bsel = out_item<Tr>(a, it, smem, bsel, prefetch_into);
-    }
-    cur = nxt;
-    nxt = after;
   }
 
-  // The last workgroup to finish clears the queue tickets for the next launch.
-  if (tid == 0) {
-    const unsigned done = bump(a.queue_cnt + 16);
-    if (done == gridDim.x - 1) {
-      for (int q = 0; q < kMaxQueues; ++q) put(a.queue_cnt + q, 0u);
-      put(a.queue_cnt + 16, 0u);
-    }
+  // The last workgroup to finish clears the arrival counters for the next
+  // launch (every other workgroup's atomics have completed: each waited for
+  // them before counting itself done).
+  wait_all();
+  __syncthreads();
+  if (tid == 0) last = bump(a.done_cnt) == gridDim.x - 1;
+  __syncthreads();
+  if (last) {
+    for (int i = tid; i < a.BH * kCntWords; i += kThreads) put(a.slice_cnt + i, 0u);
+    if (tid < kXcds) put(a.tickets + tid, 0u);
+    wait_all();
+    __syncthreads();
+    if (tid == 0) put(a.done_cnt, 0u);
   }
 }
 

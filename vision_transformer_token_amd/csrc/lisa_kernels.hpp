@@ -9,11 +9,12 @@ namespace lisa {
 
 constexpr int kD = 64;          // d_h = d_v supported by the kernel
 constexpr int kMaxT = 8;        // walk terms k = 0..T-1
-constexpr int kThreads = 256;   // 4 waves of 64 per workgroup
-constexpr int kMaxQueues = 8;   // one work queue per XCD
-constexpr int kCombineBlocks = 4;   // combine items per 64x64 matrix (16 rows each)
+constexpr int kThreads = 512;   // 8 waves of 64 per workgroup: 4 producers, 4 consumers
+constexpr int kRoleWaves = 4;   // waves per role
+constexpr int kXcds = 8;        // workgroup w runs on XCD w % 8
+constexpr int kMaxRanks = 256;  // G <= 256: each rank combines >= 32 elements
 constexpr int kMaxTileTokens = 256;
-constexpr int kCntWords = 4;    // arrival counters per (batch, head) slice: KV, M, C, OUT
+constexpr int kCntWords = 4;    // arrival counters per (batch, head) slice: KV, M, C (+ pad)
 
 // LDS of one workgroup, per element size ES: two staging buffers of kStage
 // bytes that the DMA of the next stage and the compute of the current one
@@ -50,18 +51,20 @@ __host__ __device__ inline TileLayout tile_layout(int TR, int TC, int T, int es)
   return L;
 }
 
-// One launch of the persistent kernel processes, for every (batch, head)
-// slice b, work items of four kinds in queue order:
-//   KV(b, p): tokens [p*chunk, ...) -> partial s and phi(K)^T V;
-//   M(b, p):  after all KV(b, *): s = fixed-order sum of the partial s, then
-//             partial M = phi(K)^T Qt over the chunk;
-//   C(b, q):  after all M(b, *) (all KV(b, *) when M is absent): the
-//             fixed-order sum of the partials of one 16-row block of
-//             phi(K)^T V (q < 4) or M (q >= 4), written as fp32 and as MFMA
-//             fragments (C item 0 also writes s);
-//   OUT(b, j): after all C(b, *): the run of output tiles [j R, j R + R).
-// Slice b's items sit in queue b % 8 (served by the workgroups of XCD b % 8)
-// when the slice count is a multiple of 8, else in a single queue.
+// Static schedule of one launch.  G workgroups (ranks) share each (batch,
+// head) slice; S = grid / G groups take slices b = group, group + S, ...,
+// Z at a time (each phase runs for the round's Z slices before the next).
+// For each slice, rank g of its group:
+//   KV: sweeps its token range [g n / G, (g + 1) n / G) in chunks of at most
+//       `chunk` tokens -> partial g of s and phi(K)^T V;
+//   M:  after all G KV partials: s = their fixed-order sum, then partial g of
+//       M = phi(K)^T Qt over the same range;
+//   C:  after all G M partials (all KV partials when M is absent): elements
+//       [g E, g E + E) of the flattened [phi(K)^T V | M] (E = 8192 / G), the
+//       fixed-order sum of the G partials, written as fp32 and as MFMA
+//       fragments (rank 0 also writes s);
+//   OUT: after all G ranks' C parts: output tiles [g T / G, (g + 1) T / G).
+// Each phase's completion is counted per slice (kRoleWaves arrivals per rank).
 struct FlowArgs {
   const void* Q;
   const void* K;
@@ -73,22 +76,23 @@ struct FlowArgs {
   int H, W, n, T, heads, BH;
   float eps;
   float logit_scale;      // log2(e) / sqrt(d_h)
-  int chunk, P;           // statistics items: tokens per item, items per slice
-  int TR, TC, tiles_x, ntiles, R;  // output tiles, tiles per grid row / slice, tiles per run
-  int nKV, nM, nC, nOUT;  // items per slice of each kind (0 = kind absent)
-  int wait_out;           // output items wait for their slice's statistics
-  int nq;                 // work queues (8 or 1)
-  float* part_s;          // [BH][P][64]
-  float* part_kv;         // [BH][P][64*64]
-  float* part_m;          // [BH][P][64*64]
+  int chunk;              // tokens per KV / M stage (<= Lds::kChunk, multiple of 16)
+  int G, S, Z;            // ranks per slice (a power of two), groups, slices per round
+  int xcd_groups;         // groups sit within one XCD (workgroup w on XCD w % 8)
+  int TR, TC, tiles_x, ntiles;  // output tiles, tiles per grid row / slice
+  int do_kv, do_m, do_out;      // phases present (C runs whenever KV does)
+  float* part_s;          // [BH][G][64]
+  float* part_kv;         // [BH][G][64*64]
+  float* part_m;          // [BH][G][64*64]
   float* fin_s;           // [BH][64]
   float* fin_kv;          // [BH][64*64]
   float* fin_m;           // [BH][64*64]
   void* frag_kv;          // [BH][64*64] elements of the input dtype
   void* frag_m;           // [BH][64*64]
   unsigned* slice_cnt;    // [BH][kCntWords]
-  unsigned* queue_cnt;    // [8] tickets, [16] finished workgroups, [17] error word
-  unsigned* err;
+  unsigned* done_cnt;     // finished workgroups
+  unsigned* tickets;      // [kXcds] rank tickets
+  unsigned* err;          // error word (a dependency wait timed out)
 };
 
 // dtype: 0 = fp32, 1 = bf16 (lisa_dtype).  grid = workgroups to launch.
