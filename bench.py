@@ -102,12 +102,14 @@ def _csv_rows(path):
         return list(csv.DictReader(f))
 
 
+KERNEL = "flow_kernel<bf16>"  # the one kernel of the path (one launch per forward)
+
+
 def _short(name):
-    for key in ("stats_kernel", "output_kernel", "copyBuffer"):
-        if key in name:
-            if key == "stats_kernel":
-                return "stats_kernel<M>" if "true>" in name else "stats_kernel<KV>"
-            return key
+    if "flow_kernel" in name:
+        return "flow_kernel<bf16>" if "BF16" in name else "flow_kernel<fp32>"
+    if "copyBuffer" in name:
+        return "copyBuffer"
     return name[:60]
 
 
@@ -181,6 +183,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--forward-only", action="store_true",
+                    help="skip the reduce/apply reference timing (profiling runs: every "
+                         "launch of the kernel is then a forward)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="instead of LiSA, run 20 plain device copies of this many MiB "
@@ -190,7 +195,8 @@ def main():
     args = ap.parse_args()
 
     if args.summarize_profiles:
-        fixed = "python3 bench.py --steps {s} --warmup {w} --no-cpu-baseline --workload " + args.workload
+        fixed = ("python3 bench.py --steps {s} --warmup {w} --no-cpu-baseline --forward-only --workload "
+                 + args.workload)
         summarize_profiles(args.summarize_profiles, args.workload, {
             "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace "
                      "-o trace -- " + fixed.format(s=200, w=20),
@@ -274,11 +280,21 @@ def main():
     torch.cuda.synchronize()
     step_ms = e0.elapsed_time(e1) / args.steps
 
-    # Same K steps as two stages, with events around each on the same stream:
-    # the dominant (output) kernel's average launch duration.
-    split = w.T >= 3
-    kernel_ms = stats_ms = None
-    if split:
+    # The same K forwards with events around each launch on the stream it runs
+    # on: the kernel's average launch duration, for the roofline.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        forward(sets[i % nsets])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    kernel_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+
+    # The two halves the C ABI also offers (statistics only; output from
+    # stored statistics), timed the same way, for reference.
+    stats_ms = apply_ms = None
+    if w.T >= 2 and not args.forward_only:
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
         torch.cuda.synchronize()
         for i in range(args.steps):
@@ -290,7 +306,7 @@ def main():
             ev[i][2].record(stream)
         torch.cuda.synchronize()
         stats_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
-        kernel_ms = sum(b.elapsed_time(c) for _, b, c in ev) / args.steps
+        apply_ms = sum(b.elapsed_time(c) for _, b, c in ev) / args.steps
 
     th = w.token_heads
     bpt = compulsory_bytes_per_token_head(w)
@@ -326,10 +342,10 @@ def main():
     }
     if kernel_ms is not None:
         achieved = th * bpt / (kernel_ms * 1e-3) / 1e9
-        traffic = load_counters(w, "output_kernel")
+        traffic = load_counters(w, KERNEL)
         out["roofline"] = {
             "bound": "hbm",
-            "kernel": "output_kernel",
+            "kernel": KERNEL,
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -338,7 +354,7 @@ def main():
             "kernel_ms": kernel_ms,
             "algorithmic_bytes_per_launch": th * bpt,
         }
-        out["stages_ms"] = {"statistics": stats_ms, "output": kernel_ms}
+        out["stages_ms"] = {"forward_kernel": kernel_ms, "reduce_only": stats_ms, "apply_only": apply_ms}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
     print(json.dumps(out), flush=True)

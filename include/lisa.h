@@ -40,6 +40,14 @@
  *     its counter words at zero again, so a workspace can be reused by later
  *     calls of any problem that fits it.  Calls that share a workspace must
  *     be ordered on one stream; concurrent calls on one workspace race.
+ *   - Scheduling: a call launches one workgroup per compute unit, and groups
+ *     of its workgroups (up to 256, as many as the problem splits a
+ *     (batch, head) slice into) wait for each other.  Ranks are handed out in
+ *     the order workgroups start, so a call always completes when it can
+ *     eventually run one group at a time; work on other streams only delays
+ *     it.  A wait that lasts about 0.1 s is abandoned (the call then finishes
+ *     with undefined Y); that only happens if other work keeps a group's
+ *     workgroups from starting for that long.
  *   - Arithmetic: fp32 accumulation throughout.  With LISA_BF16 inputs the
  *     matrix products run on bf16 MFMA with fp32 accumulation, and the
  *     operands the library derives itself (r_i phi(Q_i), powers of M applied
