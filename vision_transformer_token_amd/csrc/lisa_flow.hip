@@ -421,44 +421,57 @@ __device__ int consume_sweep(const FlowArgs& a, const Rank& rk, int b, unsigned 
   return bsel ^ 1;
 }
 
-// Store element f of the flattened [phi(K)^T V | M] (value v) as fp32 and in
-// its MFMA fragment slot: fragment (mb, q', lane, e) holds
-// X[dimof(q' EPL + e, lane / 32)][32 mb + lane % 32].
+// Store element e = 64 r + c of one statistics matrix (value v) as fp32 at
+// fin[e] and in its MFMA fragment slot of frag: fragment (mb, q', lane, j)
+// holds X[dimof(q' EPL + j, lane / 32)][32 mb + lane % 32].
 template <class Tr>
-__device__ __forceinline__ void store_stat(const FlowArgs& a, int b, int f, float v) {
-  const int mat = f >> 12, r = (f >> 6) & 63, c = f & 63;
-  (mat == 0 ? a.fin_kv : a.fin_m)[(size_t)b * (kD * kD) + r * kD + c] = v;
+__device__ __forceinline__ void store_stat(float* fin, void* frag, int e, float v) {
+  const int r = e >> 6, c = e & 63;
+  fin[e] = v;
   const int vs = 16 * (r >> 5) + 4 * ((r >> 3) & 3) + (r & 3);
   const int ln = (c & 31) + 32 * ((r >> 2) & 1);
   const int idx = (((c >> 5) * Tr::NQ + vs / Tr::EPL) * 64 + ln) * Tr::EPL + vs % Tr::EPL;
-  if constexpr (Tr::EPL == 8) {
-    uint16_t* fr = static_cast<uint16_t*>(mat == 0 ? a.frag_kv : a.frag_m) + (size_t)b * (kD * kD);
-    __hip_atomic_store(fr + idx, f2bf(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  } else {
-    float* fr = static_cast<float*>(mat == 0 ? a.frag_kv : a.frag_m) + (size_t)b * (kD * kD);
-    put(fr + idx, v);
-  }
+  if constexpr (Tr::EPL == 8)
+    __hip_atomic_store(static_cast<uint16_t*>(frag) + idx, f2bf(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    put(static_cast<float*>(frag) + idx, v);
 }
 
-// The C phase of slice b: elements [e0, e0 + E) summed over the G staged
-// partials in a fixed order.  With E < 256, TPE = 256 / E threads share an
-// element (partials p = q, q + TPE, ...) and combine by a fixed xor tree.
+// The C phase of slice b: elements [e0, e0 + E) of the flattened
+// [phi(K)^T V | M], summed over the G staged partials in a fixed order.
+// Elements go 256 at a time (one per consumer thread), which never straddle
+// the two matrices, so the matrix choice stays wave-uniform.  With E < 256,
+// TPE = 256 / E threads share an element (partials p = q, q + TPE, ...) and
+// combine by a fixed xor tree.
 template <class Tr>
 __device__ void consume_combine(const FlowArgs& a, const Rank& rk, int b, const unsigned char* buf, int ct) {
+  using S = typename Tr::S;
   const float* stg = reinterpret_cast<const float*>(buf);  // [G][E]
+  auto mat_base = [&](int f0, float*& fin, void*& frag) {
+    const bool m = f0 >= kD * kD;
+    fin = (m ? a.fin_m : a.fin_kv) + (size_t)b * (kD * kD);
+    frag = static_cast<S*>(m ? a.frag_m : a.frag_kv) + (size_t)b * (kD * kD);
+  };
   if (rk.E >= kRoleWaves * 64) {
-    for (int e = ct; e < rk.E; e += kRoleWaves * 64) {
+    for (int e0 = 0; e0 < rk.E; e0 += kRoleWaves * 64) {
+      float* fin;
+      void* frag;
+      mat_base(rk.e0 + e0, fin, frag);
+      const int e = e0 + ct;
       float v = 0.f;
       for (int p = 0; p < a.G; ++p) v += stg[p * rk.E + e];
-      store_stat<Tr>(a, b, rk.e0 + e, v);
+      store_stat<Tr>(fin, frag, (rk.e0 + e) & (kD * kD - 1), v);
     }
   } else {
+    float* fin;
+    void* frag;
+    mat_base(rk.e0, fin, frag);
     const int tpe = kRoleWaves * 64 / rk.E;  // 2..8, consecutive lanes
     const int e = ct / tpe, q = ct % tpe;
     float v = 0.f;
     for (int p = q; p < a.G; p += tpe) v += stg[p * rk.E + e];
     for (int o = 1; o < tpe; o <<= 1) v += __shfl_xor(v, o);
-    if (q == 0) store_stat<Tr>(a, b, rk.e0 + e, v);
+    if (q == 0) store_stat<Tr>(fin, frag, (rk.e0 + e) & (kD * kD - 1), v);
   }
   wait_all();
   if ((threadIdx.x & 63) == 0) arrive(a.slice_cnt + (size_t)b * kCntWords + kCntC);
@@ -552,24 +565,26 @@ __device__ __forceinline__ void local_block_mfma(const FlowArgs& a, const unsign
     lg[0] = mma(A0, qB[kb], lg[0]);
     lg[1] = mma(A1, qB[kb], lg[1]);
   }
-  // Valid slots: the token's neighbourhood, on the grid.
-  unsigned rowbits = 0, colbits = 0;
+  // Valid slots: the token's neighbourhood, on the grid (window rows
+  // gr0 .. gr0 + 5, columns gc0 .. gc0 + 9; wave-uniform).
+  const int gr0 = r0 + 4 * br - 1, gc0 = c0 + 8 * bc - 1;
+  unsigned valid = nbr;
+  if (gr0 < 0 || gr0 + 6 > a.H || gc0 < 0 || gc0 + 10 > a.W) {
+    unsigned rowbits = 0, colbits = 0;
 #pragma unroll
-  for (int wr = 0; wr < 6; ++wr) {
-    const int gr = r0 + 4 * br + wr - 1;
-    rowbits |= (unsigned)(gr >= 0 && gr < a.H) << wr;
-  }
+    for (int wr = 0; wr < 6; ++wr) rowbits |= (unsigned)(gr0 + wr >= 0 && gr0 + wr < a.H) << wr;
 #pragma unroll
-  for (int wc = 0; wc < 10; ++wc) {
-    const int gc = c0 + 8 * bc + wc - 1;
-    colbits |= (unsigned)(gc >= 0 && gc < a.W) << wc;
+    for (int wc = 0; wc < 10; ++wc) colbits |= (unsigned)(gc0 + wc >= 0 && gc0 + wc < a.W) << wc;
+    valid &= grid_slots(rowbits, colbits, h);
   }
-  const unsigned valid = nbr & grid_slots(rowbits, colbits, h);
+  // Invalid slots become -inf: bit v of `valid`, sign-extended, selects
+  // between the logit's bits and those of -inf.
   float p[32];
   float mx = -1e30f;  // finite: a token off the grid may have no valid slot
 #pragma unroll
   for (int v = 0; v < 32; ++v) {
-    p[v] = (valid & (1u << v)) ? lg[v >> 4][v & 15] : -INFINITY;
+    const unsigned keep = (unsigned)__builtin_amdgcn_sbfe((int)valid, v, 1);
+    p[v] = __uint_as_float((__float_as_uint(lg[v >> 4][v & 15]) & keep) | (0xff800000u & ~keep));
     mx = fmaxf(mx, p[v]);
   }
   mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -594,7 +609,7 @@ __device__ __forceinline__ void local_block_mfma(const FlowArgs& a, const unsign
       la[db] = mma(A, Bp[kb], la[db]);
     }
   }
-  const float inv = scale / lden[0];
+  const float inv = scale * __builtin_amdgcn_rcpf(lden[0]);
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     L[v] = la[0][v] * inv;
@@ -657,13 +672,14 @@ __device__ __forceinline__ void local_token_valu(const FlowArgs& a, const unsign
 // Consumer wave cw takes blocks cw, cw + 4, ..., one token per lane pair:
 // lanes m and m + 32 hold 32 features each in accumulator layout, so the
 // chain u_1 = phi(Q_i), u_k = u_(k-1) M and the projection z (phi(K)^T V),
-// z = sum_k w_k(i) u_k, run on MFMA with no data movement.  `sl` is s in LDS.
+// z = sum_k w_k(i) u_k, run on MFMA with no data movement.  `sl` is s and
+// `geo` the geometric walk weights, in LDS.
 // ---------------------------------------------------------------------------
 template <class Tr>
 __device__ __forceinline__ void out_tile(const FlowArgs& a, int b, int t, const unsigned char* buf,
                                          const typename Tr::Frag (&fkv)[2][Tr::NQ],
                                          const typename Tr::Frag (&fm)[2][Tr::NQ], const float* sl,
-                                         float alpha, unsigned nbr, int cw) {
+                                         const float* geo, float alpha, unsigned nbr, int cw) {
   using S = typename Tr::S;
   constexpr bool kMfmaLocal = Tr::EPL == 8;
   const int lane = threadIdx.x & 63;
@@ -690,14 +706,9 @@ __device__ __forceinline__ void out_tile(const FlowArgs& a, int b, int t, const 
     const int i = valid ? row * a.W + col : 0;
     const int ccell = (tr + 1) * CW + (tc + 1);
 
-    float w[kMaxT];
-    if (a.weights) {
-#pragma unroll
-      for (int k = 0; k < kMaxT; ++k) w[k] = cW[slot * a.T + min(k, a.T - 1)];  // terms k >= T are never used
-    } else {
-#pragma unroll
-      for (int k = 0; k < kMaxT; ++k) w[k] = a.geo[k];
-    }
+    // This token's walk weights in LDS: its staged row, or the geometric table.
+    const float* wrow = a.weights ? cW + slot * a.T : geo;
+    const float w0 = wrow[0], w1 = a.T >= 2 ? wrow[1] : 0.f;
 
     // acc = (1 - alpha) L_i: the local branch.
     float acc[32];
@@ -715,7 +726,7 @@ __device__ __forceinline__ void out_tile(const FlowArgs& a, int b, int t, const 
 
     // + alpha w_0(i) V_i: the k = 0 term of the walk.
     {
-      const float f = alpha * w[0];
+      const float f = alpha * w0;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         float vc[4];
@@ -739,20 +750,22 @@ __device__ __forceinline__ void out_tile(const FlowArgs& a, int b, int t, const 
           const int v = 4 * c + e;
           u[v] = fmaxf(qx[e], 0.f);
           part += u[v] * sx[e];
-          z[v] = w[1] * u[v];
+          z[v] = w1 * u[v];
         }
       }
       part += __shfl_xor(part, 32);
+      // u_k = u_(k-1) M, z += w_k u_k for k = 2 .. T-1.
       for (int k = 2; k < a.T; ++k) {
         apply<Tr>(fm, u, y);
+        const float wk = wrow[k];
 #pragma unroll
         for (int v = 0; v < 32; ++v) {
           u[v] = y[v];
-          z[v] += w[k] * y[v];
+          z[v] += wk * y[v];
         }
       }
       apply<Tr>(fkv, z, y);
-      const float f = alpha / (part + a.eps);
+      const float f = alpha * __builtin_amdgcn_rcpf(part + a.eps);
 #pragma unroll
       for (int v = 0; v < 32; ++v) acc[v] += f * y[v];
     }
@@ -769,7 +782,7 @@ __device__ __forceinline__ void out_tile(const FlowArgs& a, int b, int t, const 
 // then compute the rank's tiles, one stage each.  Returns the buffer index.
 template <class Tr>
 __device__ int consume_out(const FlowArgs& a, const Rank& rk, int b, unsigned char* smem, int bsel, float* s_own,
-                           int cw) {
+                           const float* geo, int cw) {
   using Frag = typename Tr::Frag;
   using L = LdsOf<Tr>;
   const int lane = threadIdx.x & 63;
@@ -789,7 +802,7 @@ __device__ int consume_out(const FlowArgs& a, const Rank& rk, int b, unsigned ch
   const unsigned nbr = neighbour_slots(tok >> 3, tok & 7, lane >> 5);
   lds_barrier();  // the statistics area may now be refilled; s_own is complete
   for (int k = 0; k < rk.nt; ++k) {
-    out_tile<Tr>(a, b, rk.t0 + k, smem + bsel * L::kStage, fkv, fm, s_own, alpha, nbr, cw);
+    out_tile<Tr>(a, b, rk.t0 + k, smem + bsel * L::kStage, fkv, fm, s_own, geo, alpha, nbr, cw);
     lds_barrier();
     bsel ^= 1;
   }
@@ -802,6 +815,7 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
   extern __shared__ __align__(1024) unsigned char smem[];
   __shared__ float s_w[kRoleWaves][kD];  // producers: s of the slice whose M chunks they prepare
   __shared__ float s_own[kD];            // consumers: s of the slice of the current OUT phase
+  __shared__ float geo_sh[kMaxT];        // geometric walk weights
   __shared__ int dep_ok;                 // tag of the stage whose dependency producer wave 0 has seen met
   __shared__ int last;                   // this workgroup's ticket, later: it finished last
   const int tid = threadIdx.x;
@@ -810,6 +824,7 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
   const int rw = producer ? wave : wave - kRoleWaves;  // wave index within the role
   unsigned char* st = smem + 2 * L::kStage;
 
+  if (tid < kMaxT) geo_sh[tid] = a.geo[tid];
   if (tid == 0) {
     dep_ok = -1;
     last = (int)bump(a.tickets + (a.xcd_groups ? blockIdx.x % kXcds : 0));
@@ -848,7 +863,8 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
             bsel ^= 1;
           }
         if (phase_len(a, rk, kPOut) > 0)
-          for (int z = 0; z < nz; ++z) bsel = consume_out<Tr>(a, rk, slice_of(a, rk, r, z), smem, bsel, s_own, rw);
+          for (int z = 0; z < nz; ++z)
+            bsel = consume_out<Tr>(a, rk, slice_of(a, rk, r, z), smem, bsel, s_own, geo_sh, rw);
       }
     }
   }
