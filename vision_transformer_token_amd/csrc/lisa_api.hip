@@ -75,12 +75,17 @@ bool plan_tiles(Plan& pl, bool per_token_weights) {
   return true;
 }
 
-// Workgroups per slice: twice as many as there are workgroups per slice of
-// the grid (so that a group has two slices to interleave), at most one per
-// 128 tokens and kMaxRanks, rounded down to a power of two (the combine
-// splits the 8192 statistics evenly).
+// Workgroups per slice: kRoundSlices times as many as there are workgroups
+// per slice of the grid (so that a group has that many slices to
+// interleave), at most one per 128 tokens and kMaxRanks, rounded down to a
+// power of two (the combine splits the 8192 statistics evenly).
+#ifndef LISA_ROUND_SLICES
+#define LISA_ROUND_SLICES 2
+#endif
+constexpr int kRoundSlices = LISA_ROUND_SLICES;
+
 int plan_ranks(int grid, int BH, int n) {
-  long per = 2L * grid / BH;
+  long per = (long)kRoundSlices * grid / BH;
   const long tok = (n + 127) / 128;
   if (per > grid) per = grid;
   if (per > tok) per = tok;
@@ -103,7 +108,7 @@ lisa_status make_plan(const lisa_problem* p, Plan& pl) {
   pl.esize = p->dtype == LISA_BF16 ? 2 : 4;
   // The partials are sized for the most ranks any grid can give a slice
   // (the launch picks G <= gmax from the device's compute units).
-  pl.gmax = plan_ranks(lisa::kMaxRanks, 2, pl.n);
+  pl.gmax = plan_ranks(lisa::kMaxRanks, kRoundSlices, pl.n);
   // KV / M stages: one staging buffer holds a chunk's K rows and V (or Q)
   // rows (a multiple of 16 tokens: the MFMA sweep reads whole 16-row steps).
   pl.chunk = pl.esize == 2 ? lisa::Lds<2>::kChunk : lisa::Lds<4>::kChunk;

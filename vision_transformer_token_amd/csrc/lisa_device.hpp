@@ -101,6 +101,26 @@ __device__ __forceinline__ void store4(float* p, const float* x) {
   *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
 }
 
+// Sums over aligned groups of 8 (16) consecutive lanes, by DPP lane moves
+// within rows of 16 lanes: xor 1 and xor 2 (quad permutes), then the mirror
+// within each half row (lane i <-> 7 - i), then within the row (i <-> 15 - i).
+__device__ __forceinline__ float dpp_add(float x, int ctrl) {
+  int y;
+  switch (ctrl) {  // the control must be a constant
+    case 0xB1: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, true); break;
+    case 0x4E: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, true); break;
+    case 0x141: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, true); break;
+    default: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, true); break;
+  }
+  return x + __int_as_float(y);
+}
+__device__ __forceinline__ float group_sum8(float x) {
+  x = dpp_add(x, 0xB1);   // quad_perm [1, 0, 3, 2]
+  x = dpp_add(x, 0x4E);   // quad_perm [2, 3, 0, 1]
+  return dpp_add(x, 0x141);  // row_half_mirror
+}
+__device__ __forceinline__ float group_sum16(float x) { return dpp_add(group_sum8(x), 0x140); }  // row_mirror
+
 // Index of this thread's wave in the workgroup, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 

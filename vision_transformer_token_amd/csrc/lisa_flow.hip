@@ -226,6 +226,7 @@ __device__ void finish_chunk(const FlowArgs& a, int nv, unsigned char* buf, cons
   unsigned char* bK = buf;
   unsigned char* bX = buf + LdsOf<Tr>::kXOff;
   const int slot = lane % Tr::PPR;
+#pragma unroll 2
   for (int j = pw; j * RPR < nvr; j += 4) {
     if (!kIsM && (j + 1) * RPR <= nv) continue;  // nothing to zero in this run
     const int r = j * RPR + lane / Tr::PPR;
@@ -246,8 +247,7 @@ __device__ void finish_chunk(const FlowArgs& a, int nv, unsigned char* buf, cons
         x[e] = fmaxf(x[e], 0.f);
         dot += x[e] * s[g * Tr::EPP + e];
       }
-#pragma unroll
-      for (int o = 1; o < Tr::PPR; o <<= 1) dot += __shfl_xor(dot, o);
+      dot = Tr::PPR == 8 ? group_sum8(dot) : group_sum16(dot);
       const float rr = 1.f / (dot + a.eps);
 #pragma unroll
       for (int e = 0; e < Tr::EPP; ++e) x[e] *= rr;
@@ -371,6 +371,7 @@ __device__ __forceinline__ void sweep_chunk(const unsigned char* buf, int nv, in
   const int nvr = (nv + 15) & ~15;
   const unsigned char* bK = buf;
   const unsigned char* bX = buf + LdsOf<Tr>::kXOff;
+#pragma unroll 2
   for (int kk = 0; kk < nvr; kk += 16) {
     if constexpr (Tr::EPL == 8) {
       const bf16x8 A = as_bf16(rows_bits<true>(bK, kk, 32 * mb));
