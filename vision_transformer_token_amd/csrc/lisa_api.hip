@@ -48,28 +48,33 @@ lisa_status check_problem(const lisa_problem* p) {
   return LISA_OK;
 }
 
-// Output tile: TR x TC cells made of whole 4 x 8 token blocks (the MFMA local
-// branch works on such blocks), 8..32 columns (at most 16 for fp32), the most
-// rows (at most kMaxTileTokens tokens) whose staged inputs (TileLayout: K and
-// V cells with a one-cell halo, Q rows, per-token weights) fit one staging
-// buffer; narrower tiles when even 4 rows do not fit.
+// Output tile: TR x TC cells made of whole 4 x 8 token blocks (the MFMA
+// local branch works on such blocks), at most kMaxTileTokens tokens, whose
+// staged inputs (TileLayout: K and V cells with a one-cell halo, Q rows,
+// per-token weights) fit one staging buffer.  Among those, the shape that
+// stages the fewest bytes per slice, counting each tile as kTileOverhead
+// bytes more (a stage has fixed costs), ties to the wider tile.
+constexpr long kTileOverhead = 8192;
+
 bool plan_tiles(Plan& pl, bool per_token_weights) {
   const int es = (int)pl.esize;
   const int stage = es == 2 ? lisa::Lds<2>::kStage : lisa::Lds<4>::kStage;
   const int wT = per_token_weights ? pl.T : 0;
-  const int h4 = (pl.H + 3) / 4 * 4;
-  int tc = std::min((pl.W + 7) / 8 * 8, es == 2 ? 32 : 16);
-  for (;; tc -= 8) {
-    int tr = 0;
-    for (int r = 4; r <= h4 && r * tc <= lisa::kMaxTileTokens; r += 4)
-      if (lisa::tile_layout(r, tc, wT, es).total <= stage) tr = r;
-    if (tr > 0) {
-      pl.TR = tr;
-      pl.TC = tc;
-      break;
+  const int h4 = (pl.H + 3) / 4 * 4, w8 = (pl.W + 7) / 8 * 8;
+  long best = -1;
+  for (int tc = std::min(w8, 64); tc >= 8; tc -= 8)
+    for (int tr = 4; tr <= h4 && tr * tc <= lisa::kMaxTileTokens; tr += 4) {
+      const lisa::TileLayout L = lisa::tile_layout(tr, tc, wT, es);
+      if (L.total > stage) break;
+      const long ntiles = (long)((pl.W + tc - 1) / tc) * ((pl.H + tr - 1) / tr);
+      const long cost = ntiles * (L.total + kTileOverhead);
+      if (best < 0 || cost < best) {
+        best = cost;
+        pl.TR = tr;
+        pl.TC = tc;
+      }
     }
-    if (tc == 8) return false;
-  }
+  if (best < 0) return false;
   pl.tiles_x = (pl.W + pl.TC - 1) / pl.TC;
   pl.ntiles = pl.tiles_x * ((pl.H + pl.TR - 1) / pl.TR);
   return true;

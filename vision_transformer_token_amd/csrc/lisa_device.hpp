@@ -223,6 +223,40 @@ __device__ __forceinline__ v8s join(v4s lo, v4s hi) {
 }
 __device__ __forceinline__ bf16x8 as_bf16(v8s x) { return __builtin_bit_cast(bf16x8, x); }
 
+// phi of a 64-vector held as B operands in feature order (lane (m, h) holds
+// features 16 q + 8 h + e of piece q, e = 0..7), returned as B operands in
+// accumulator slot order (piece q holds slots 8 q .. 8 q + 7, i.e. features
+// dimof(8 q + e, h)).  Within a piece, the lower half keeps features 0..3 and
+// takes 8..11 from the upper half, which takes 4..7 in exchange: the upper
+// half of dwords 0, 1 trades places with the lower half of dwords 2, 3.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v8s relu_to_slots(v8s x) {
+  u32x4 w = __builtin_bit_cast(u32x4, x);
+  const auto p = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+  const auto q = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+  w[0] = p[0];
+  w[2] = p[1];
+  w[1] = q[0];
+  w[3] = q[1];
+  return __builtin_elementwise_max(__builtin_bit_cast(v8s, w), (v8s)0);
+}
+
+// apply() for a bf16 x given as the bits of its B operands (slot order).
+__device__ __forceinline__ void apply_bits(const bf16x8 (&fr)[2][4], const v8s (&x)[4], float (&y)[32]) {
+  f32x16 c0 = {}, c1 = {};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const bf16x8 b = as_bf16(x[q]);
+    c0 = mma(fr[0][q], b, c0);
+    c1 = mma(fr[1][q], b, c1);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    y[i] = c0[i];
+    y[16 + i] = c1[i];
+  }
+}
+
 // Bits of X[row0 + 8h + e][col0 + m] (bf16 rows of a staged region), e = 0..7;
 // with kRelu the values are clamped at zero (a negative bf16 is a negative int16).
 template <bool kRelu>

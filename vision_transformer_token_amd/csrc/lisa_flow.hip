@@ -26,6 +26,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "lisa_device.hpp"
 #include "lisa_kernels.hpp"
 
@@ -267,6 +269,37 @@ __device__ void finish_chunk(const FlowArgs& a, int nv, unsigned char* buf, cons
   }
 }
 
+// After the wave's own DMA of an output tile has landed: r_j = 1 / (phi(Q_j)
+// . s + eps) for the Q rows of the 1 KB runs it issued (run j belongs to
+// wave j % 4), written to the tile's r region.  The lanes of a row each take
+// one 16-byte piece and reduce the dot product together.
+template <class Tr>
+__device__ void finish_tile(const FlowArgs& a, const TileLayout& L, unsigned char* buf, const float* s, int pw) {
+  constexpr int RPR = 1024 / Tr::RB;  // rows per run
+  const int lane = threadIdx.x & 63;
+  const int slot = lane % Tr::PPR;
+  const unsigned char* bQ = buf + L.q;
+  float* rr = reinterpret_cast<float*>(buf + L.r);
+#pragma unroll 2
+  for (int j = pw; j * RPR < L.tokens; j += 4) {
+    const int r = j * RPR + lane / Tr::PPR;
+    const int g = (slot ^ swz(r)) & (Tr::PPR - 1);  // the piece in this slot
+    const unsigned char* pX = bQ + r * Tr::RB + slot * 16;
+    float x[Tr::EPP];
+    if constexpr (Tr::EPP == 8) {
+      load4(reinterpret_cast<const uint16_t*>(pX), x);
+      load4(reinterpret_cast<const uint16_t*>(pX) + 4, x + 4);
+    } else {
+      load4(reinterpret_cast<const float*>(pX), x);
+    }
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < Tr::EPP; ++e) dot += fmaxf(x[e], 0.f) * s[g * Tr::EPP + e];
+    dot = Tr::PPR == 8 ? group_sum8(dot) : group_sum16(dot);
+    if (slot == 0) rr[r] = 1.f / (dot + a.eps);
+  }
+}
+
 // Lane l of a wave: s[l] = fixed-order sum over the G ranks' partials.
 __device__ __forceinline__ float sum_s_partials(const FlowArgs& a, int b) {
   const int lane = threadIdx.x & 63;
@@ -346,10 +379,11 @@ __device__ void prepare(const FlowArgs& a, const Rank& rk, Pos p, unsigned char*
         if (a.T >= 3)
           dma_linear_coherent(st + L::kFragBytes, static_cast<const S*>(a.frag_m) + (size_t)b * (kD * kD),
                               L::kFragBytes, pw);
-        dma_linear_coherent(st + 2 * L::kFragBytes, a.fin_s + (size_t)b * kD, kD * 4, pw);
+        s_w[lane] = get(a.fin_s + (size_t)b * kD + lane);  // kept for the slice's later tiles
       }
     }
     wait_all();
+    if (a.T >= 2) finish_tile<Tr>(a, layout_of<Tr>(a), buf, s_w, pw);
   }
 }
 
@@ -673,14 +707,16 @@ __device__ __forceinline__ void local_token_valu(const FlowArgs& a, const unsign
 // Consumer wave cw takes blocks cw, cw + 4, ..., one token per lane pair:
 // lanes m and m + 32 hold 32 features each in accumulator layout, so the
 // chain u_1 = phi(Q_i), u_k = u_(k-1) M and the projection z (phi(K)^T V),
-// z = sum_k w_k(i) u_k, run on MFMA with no data movement.  `sl` is s and
-// `geo` the geometric walk weights, in LDS.
+// z = sum_k w_k(i) u_k, run on MFMA with no data movement.  u_1 comes from
+// the token's Q operands of the local branch (re-paired across the lane
+// pair), r_i from the tile's r region and `geo` holds the geometric walk
+// weights, all in LDS.
 // ---------------------------------------------------------------------------
 template <class Tr>
 __device__ __forceinline__ void out_tile(const FlowArgs& a, int b, int t, const unsigned char* buf,
                                          const typename Tr::Frag (&fkv)[2][Tr::NQ],
-                                         const typename Tr::Frag (&fm)[2][Tr::NQ], const float* sl,
-                                         const float* geo, float alpha, unsigned nbr, int cw) {
+                                         const typename Tr::Frag (&fm)[2][Tr::NQ], const float* geo,
+                                         float alpha, unsigned nbr, int cw) {
   using S = typename Tr::S;
   constexpr bool kMfmaLocal = Tr::EPL == 8;
   const int lane = threadIdx.x & 63;
@@ -694,6 +730,7 @@ __device__ __forceinline__ void out_tile(const FlowArgs& a, int b, int t, const 
   const unsigned char* cV = buf + Lt.v;
   const unsigned char* cQ = buf + Lt.q;
   const float* cW = reinterpret_cast<const float*>(buf + Lt.w);
+  const float* cR = reinterpret_cast<const float*>(buf + Lt.r);
   S* Yb = static_cast<S*>(a.Y) + (size_t)b * a.n * kD;
   const bool global = a.T >= 2;
 
@@ -711,18 +748,25 @@ __device__ __forceinline__ void out_tile(const FlowArgs& a, int b, int t, const 
     const float* wrow = a.weights ? cW + slot * a.T : geo;
     const float w0 = wrow[0], w1 = a.T >= 2 ? wrow[1] : 0.f;
 
-    // acc = (1 - alpha) L_i: the local branch.
+    // acc = (1 - alpha) L_i: the local branch; u1 = u_1 = phi(Q_i) in
+    // accumulator slot order (bf16: as the bits of its B operands).
     float acc[32];
+    using U1 = std::conditional_t<kMfmaLocal, v8s[4], float[32]>;
+    U1 u1;
     if constexpr (kMfmaLocal) {
       bf16x8 qB[4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) qB[kb] = *reinterpret_cast<const bf16x8*>(cQ + row_off<BF16>(slot, 16 * kb + 8 * h));
       local_block_mfma(a, cK, cV, CW, r0, c0, br, bc, nbr, qB, 1.f - alpha, acc);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) u1[kb] = relu_to_slots(__builtin_bit_cast(v8s, qB[kb]));
     } else {
       float q[32];
 #pragma unroll
       for (int c = 0; c < 8; ++c) load4(reinterpret_cast<const S*>(cQ + row_off<Tr>(slot, dimof(4 * c, h))), &q[4 * c]);
       local_token_valu<Tr>(a, cK, cV, CW, ccell, row, col, q, 1.f - alpha, acc);
+#pragma unroll
+      for (int v = 0; v < 32; ++v) u1[v] = fmaxf(q[v], 0.f);
     }
 
     // + alpha w_0(i) V_i: the k = 0 term of the walk.
@@ -738,35 +782,36 @@ __device__ __forceinline__ void out_tile(const FlowArgs& a, int b, int t, const 
     }
     // + alpha r_i sum_{k>=1} w_k(i) phi(Q_i) M^(k-1) (phi(K)^T V).
     if (global) {
-      float u[32], z[32], y[32];
-      float part = 0.f;
+      float z[32], y[32];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        float qx[4];
-        load4(reinterpret_cast<const S*>(cQ + row_off<Tr>(slot, dimof(4 * c, h))), qx);
-        const float4 sv = *reinterpret_cast<const float4*>(sl + dimof(4 * c, h));
-        const float sx[4] = {sv.x, sv.y, sv.z, sv.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int v = 4 * c + e;
-          u[v] = fmaxf(qx[e], 0.f);
-          part += u[v] * sx[e];
-          z[v] = w1 * u[v];
-        }
+      for (int v = 0; v < 32; ++v) {
+        if constexpr (kMfmaLocal)
+          z[v] = w1 * __uint_as_float((uint32_t)(uint16_t)u1[v >> 3][v & 7] << 16);
+        else
+          z[v] = w1 * u1[v];
       }
-      part += __shfl_xor(part, 32);
       // u_k = u_(k-1) M, z += w_k u_k for k = 2 .. T-1.
-      for (int k = 2; k < a.T; ++k) {
-        apply<Tr>(fm, u, y);
-        const float wk = wrow[k];
+      if (a.T >= 3) {
+        float u[32];
+        if constexpr (kMfmaLocal)
+          apply_bits(fm, u1, u);
+        else
+          apply<Tr>(fm, u1, u);
+        const float w2 = wrow[2];
 #pragma unroll
-        for (int v = 0; v < 32; ++v) {
-          u[v] = y[v];
-          z[v] += wk * y[v];
+        for (int v = 0; v < 32; ++v) z[v] += w2 * u[v];
+        for (int k = 3; k < a.T; ++k) {
+          apply<Tr>(fm, u, y);
+          const float wk = wrow[k];
+#pragma unroll
+          for (int v = 0; v < 32; ++v) {
+            u[v] = y[v];
+            z[v] += wk * y[v];
+          }
         }
       }
       apply<Tr>(fkv, z, y);
-      const float f = alpha * __builtin_amdgcn_rcpf(part + a.eps);
+      const float f = alpha * cR[slot];
 #pragma unroll
       for (int v = 0; v < 32; ++v) acc[v] += f * y[v];
     }
@@ -779,10 +824,10 @@ __device__ __forceinline__ void out_tile(const FlowArgs& a, int b, int t, const 
 }
 
 // The OUT phase of slice b: take the slice statistics out of the statistics
-// area (fragments into registers, s into `s_own`), free the area (barrier),
+// area (fragments into registers), free the area (barrier),
 // then compute the rank's tiles, one stage each.  Returns the buffer index.
 template <class Tr>
-__device__ int consume_out(const FlowArgs& a, const Rank& rk, int b, unsigned char* smem, int bsel, float* s_own,
+__device__ int consume_out(const FlowArgs& a, const Rank& rk, int b, unsigned char* smem, int bsel,
                            const float* geo, int cw) {
   using Frag = typename Tr::Frag;
   using L = LdsOf<Tr>;
@@ -797,13 +842,12 @@ __device__ int consume_out(const FlowArgs& a, const Rank& rk, int b, unsigned ch
       fkv[mb][q] = *reinterpret_cast<const Frag*>(st + off);
       fm[mb][q] = *reinterpret_cast<const Frag*>(st + L::kFragBytes + off);  // unused unless T >= 3
     }
-  if (cw == 0) s_own[lane] = reinterpret_cast<const float*>(st + 2 * L::kFragBytes)[lane];
   const float alpha = a.alpha[b % a.heads];
   const int tok = lane & 31;
   const unsigned nbr = neighbour_slots(tok >> 3, tok & 7, lane >> 5);
-  lds_barrier();  // the statistics area may now be refilled; s_own is complete
+  lds_barrier();  // the statistics area may now be refilled
   for (int k = 0; k < rk.nt; ++k) {
-    out_tile<Tr>(a, b, rk.t0 + k, smem + bsel * L::kStage, fkv, fm, s_own, geo, alpha, nbr, cw);
+    out_tile<Tr>(a, b, rk.t0 + k, smem + bsel * L::kStage, fkv, fm, geo, alpha, nbr, cw);
     lds_barrier();
     bsel ^= 1;
   }
@@ -815,7 +859,6 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
   using L = LdsOf<Tr>;
   extern __shared__ __align__(1024) unsigned char smem[];
   __shared__ float s_w[kRoleWaves][kD];  // producers: s of the slice whose M chunks they prepare
-  __shared__ float s_own[kD];            // consumers: s of the slice of the current OUT phase
   __shared__ float geo_sh[kMaxT];        // geometric walk weights
   __shared__ int dep_ok;                 // tag of the stage whose dependency producer wave 0 has seen met
   __shared__ int last;                   // this workgroup's ticket, later: it finished last
@@ -865,7 +908,7 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
           }
         if (phase_len(a, rk, kPOut) > 0)
           for (int z = 0; z < nz; ++z)
-            bsel = consume_out<Tr>(a, rk, slice_of(a, rk, r, z), smem, bsel, s_own, geo_sh, rw);
+            bsel = consume_out<Tr>(a, rk, slice_of(a, rk, r, z), smem, bsel, geo_sh, rw);
       }
     }
   }

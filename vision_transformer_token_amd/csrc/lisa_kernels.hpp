@@ -19,12 +19,12 @@ constexpr int kCntWords = 4;    // arrival counters per (batch, head) slice: KV,
 // LDS of one workgroup, per element size ES: two staging buffers of kStage
 // bytes that the DMA of the next stage and the compute of the current one
 // alternate between, then the statistics area (the two 64x64 MFMA fragment
-// sets and s) of the slice the output items work on.
+// sets) of the slice the output items work on.
 template <int ES>
 struct Lds {
   static constexpr int kStage = ES == 2 ? 71680 : 61440;
   static constexpr int kFragBytes = kD * kD * ES;          // one fragment set
-  static constexpr int kStats = 2 * kFragBytes + 1024;    // + s (256 B, padded)
+  static constexpr int kStats = 2 * kFragBytes;
   static constexpr int kTotal = 2 * kStage + kStats;
   static constexpr int kChunk = ES == 2 ? 256 : 112;      // max tokens per KV / M item
   static constexpr int kXOff = kStage / 2 / 1024 * 1024;  // V / Q rows of a KV / M stage
@@ -32,10 +32,12 @@ struct Lds {
 
 // Byte offsets of an output tile's regions inside a staging buffer: K cells
 // and V cells of the tile plus a one-cell halo, the Q rows of its token
-// slots, and their walk weights (fp32, T per slot) when they are per token.
+// slots, their walk weights (fp32, T per slot) when they are per token, and
+// r_i = 1 / (phi(Q_i) . s + eps) per slot (fp32), which the producer waves
+// fill in once the Q rows have landed.
 struct TileLayout {
   int cells, tokens;
-  int k, v, q, w, total;
+  int k, v, q, w, r, total;
 };
 __host__ __device__ inline int round_kb(int x) { return (x + 1023) / 1024 * 1024; }
 __host__ __device__ inline TileLayout tile_layout(int TR, int TC, int T, int es) {
@@ -47,7 +49,8 @@ __host__ __device__ inline TileLayout tile_layout(int TR, int TC, int T, int es)
   L.v = round_kb(L.cells * rb);
   L.q = 2 * L.v;
   L.w = L.q + round_kb(L.tokens * rb);
-  L.total = L.w + round_kb(L.tokens * T * 4);
+  L.r = L.w + round_kb(L.tokens * T * 4);
+  L.total = L.r + round_kb(L.tokens * 4);
   return L;
 }
 
