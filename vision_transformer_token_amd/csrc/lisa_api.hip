@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -17,6 +18,38 @@ using lisa::kD;
 using lisa::kThreads;
 
 constexpr size_t kAlign = 256;
+
+// Compute units and XCDs of a device, queried once per device (attribute
+// queries cost far more than a launch).  Entries are filled at most once per
+// device by whichever call gets there first; a racing second fill stores the
+// same values.
+struct DeviceInfo {
+  int cus, xccs;
+};
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_cus[kMaxDevices];
+std::atomic<int> g_dev_xccs[kMaxDevices];
+
+bool device_info(DeviceInfo& info) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return false;
+  if (dev < kMaxDevices) {
+    info.cus = g_dev_cus[dev].load(std::memory_order_relaxed);
+    info.xccs = g_dev_xccs[dev].load(std::memory_order_relaxed);
+    if (info.cus > 0) return true;
+  }
+  int cus = 0, xccs = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return false;
+  if (hipDeviceGetAttribute(&xccs, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess) xccs = 0;
+  info.cus = cus;
+  info.xccs = xccs;
+  if (dev < kMaxDevices) {
+    g_dev_xccs[dev].store(xccs, std::memory_order_relaxed);
+    g_dev_cus[dev].store(cus, std::memory_order_relaxed);
+  }
+  return true;
+}
 constexpr size_t kMaxSlices = 65535;  // batch * heads limit
 
 size_t up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -202,18 +235,25 @@ lisa_status run(Plan pl, Mode mode, const void* Q, const void* K, const void* V,
   a.logit_scale = (float)(1.4426950408889634 / std::sqrt((double)kD));
   if (!plan_tiles(pl, weights != nullptr)) return LISA_ERR_UNSUPPORTED;
   // One persistent workgroup per compute unit.
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    return LISA_ERR_HIP;
-  pl.grid = cus;
+  DeviceInfo dinfo;
+  if (!device_info(dinfo)) return LISA_ERR_HIP;
+  pl.grid = dinfo.cus;
   pl.G = plan_ranks(pl.grid, pl.BH, pl.n);
   if (pl.G > pl.gmax) pl.G = pl.gmax;
   pl.S = pl.grid / pl.G;
   // Slices per round: all of the group's slices, at most 4.
   pl.Z = std::min(4, (pl.BH + pl.S - 1) / pl.S);
-  // Keep a group's workgroups on one XCD (shared L2) when the grid allows it.
-  pl.xcd_groups = (pl.grid % lisa::kXcds == 0 && (pl.grid / lisa::kXcds) % pl.G == 0) ? 1 : 0;
+  // Where a group's workgroups run.  Pairs (G <= 2) stay on one XCD (the
+  // device hands workgroup w to XCD w % kXcds, so rank tickets are drawn per
+  // XCD): their many small hand-offs then start and finish together.  Larger
+  // groups take tickets from one counter in start order and so spread over
+  // all XCDs: when they were kept on one XCD, an XCD that fell behind in the
+  // HBM-bound KV and M phases held back every group on it (a PVT stage-1
+  // forward, G = 16: 61 us on one XCD, 58 us spread; G = 4 and 8 about even).
+  pl.xcd_groups = (dinfo.xccs == lisa::kXcds && pl.G <= 2 && pl.grid % lisa::kXcds == 0 &&
+                   (pl.grid / lisa::kXcds) % pl.G == 0)
+                      ? 1
+                      : 0;
   a.chunk = pl.chunk;
   a.G = pl.G;
   a.S = pl.S;
