@@ -270,15 +270,59 @@ def main():
         forward(sets[i % nsets])
     torch.cuda.synchronize()
 
-    # Timed region: K whole forward passes.
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Timed region: K whole forward passes, with events at the boundaries of
+    # five equal segments (median of the five reported beside the total).
+    seg = [i * args.steps // 5 for i in range(6)]
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     torch.cuda.synchronize()
-    e0.record(stream)
+    marks[0].record(stream)
     for i in range(args.steps):
         forward(sets[i % nsets])
-    e1.record(stream)
+        if i + 1 in seg[1:]:
+            marks[seg.index(i + 1)].record(stream)
     torch.cuda.synchronize()
-    step_ms = e0.elapsed_time(e1) / args.steps
+    step_ms = marks[0].elapsed_time(marks[5]) / args.steps
+    seg_ms = sorted(marks[j].elapsed_time(marks[j + 1]) / max(1, seg[j + 1] - seg[j]) for j in range(5))
+
+    # The same calls captured once into a HIP graph (one forward per input
+    # set) and replayed: launch overhead off the host's critical path.
+    graph_ms = None
+    if not args.forward_only:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for d in sets:
+                forward(d)
+        reps = max(1, args.steps // nsets)
+        g.replay()
+        torch.cuda.synchronize()
+        ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        cur = torch.cuda.current_stream(dev)
+        ga.record(cur)
+        for _ in range(reps):
+            g.replay()
+        gb.record(cur)
+        torch.cuda.synchronize()
+        graph_ms = ga.elapsed_time(gb) / (reps * nsets)
+        del g
+
+    # A plain device copy on the same box: the bandwidth a streaming kernel
+    # actually gets, for the path's fraction of it.
+    copy_gbs = None
+    if not args.forward_only:
+        cb = 256 << 20
+        src = torch.ones(cb // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        ca, cz = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ca.record()
+        for _ in range(20):
+            dst.copy_(src)
+        cz.record()
+        torch.cuda.synchronize()
+        copy_gbs = 2 * cb * 20 / (ca.elapsed_time(cz) * 1e-3) / 1e9
+        del src, dst
 
     # The same K forwards with events around each launch on the stream it runs
     # on: the kernel's average launch duration, for the roofline.
@@ -339,7 +383,13 @@ def main():
             "rotating_input_sets": nsets,
         },
         "path_roofline_frac": path_gbs / HBM_PEAK_GBS,
+        "ms_per_step_median5": seg_ms[2],
     }
+    if graph_ms is not None:
+        out["graph"] = {"ms_per_step": graph_ms, "value": th / (graph_ms * 1e-3)}
+    if copy_gbs is not None:
+        out["copy_gbs"] = copy_gbs
+        out["path_copy_frac"] = path_gbs / copy_gbs
     if kernel_ms is not None:
         achieved = th * bpt / (kernel_ms * 1e-3) / 1e9
         traffic = load_counters(w, KERNEL)

@@ -207,3 +207,29 @@ def test_output_invariant_to_scaling_of_q_and_k_in_global_branch(lisa):
     xs = dict(x, q=x["q"] * 4.0, k=x["k"] * 0.25)
     y2 = f64(gpu_y(lisa, to_dev(xs)))
     assert np.linalg.norm(y1 - y2) / np.linalg.norm(y1) < 1e-5
+
+
+def test_graph_replay_matches_eager(lisa):
+    """lisa_forward captured in a HIP graph: every replay, with eager calls on
+    the same workspace in between, equals the eager result bit for bit."""
+    wa = workloads.get("deit_t_224")
+    wb = workloads.small("graph-other", 2, 1, 20, 24, 3, seed=23)
+    da, db = to_dev(workloads.make_inputs(wa)), to_dev(workloads.make_inputs(wb))
+    pa = lisa.make_problem(da["q"], da["v"], grid=(wa.H, wa.W), T=wa.T)
+    pb = lisa.make_problem(db["q"], db["v"], grid=(wb.H, wb.W), T=wb.T)
+    ws = torch.zeros(max(lisa.lisa_workspace_size(pa), lisa.lisa_workspace_size(pb)), dtype=torch.uint8,
+                     device="cuda")
+    ya = gpu_y(lisa, da, workspace=ws)
+    yb = gpu_y(lisa, db, workspace=ws)
+    out = torch.empty_like(da["v"])
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        lisa.lisa_forward(da["q"], da["k"], da["v"], grid=(wa.H, wa.W), T=wa.T, alpha=da["alpha"],
+                          weights=da["weights"], eps=wa.eps, out=out, workspace=ws, stream=s)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ya), f"replay {rep}"
+        assert torch.equal(gpu_y(lisa, db, workspace=ws), yb), f"eager call after replay {rep}"
