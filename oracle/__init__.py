@@ -1,4 +1,4 @@
-"""CPU oracle for the LiSA forward pass -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for the LiSA forward and backward passes -- TEST INFRASTRUCTURE ONLY.
 
 This package is a plain, slow, float64 NumPy statement of what the LiSA
 (Linear Stochastic Attention) forward pass computes, written from the paper
@@ -11,6 +11,11 @@ shares no code with the GPU library: no kernels, helpers, tables or constants.
 The only thing both sides consume is the seeded synthetic input generator,
 which holds none of the method's arithmetic and which this package does not
 import.
+
+``oracle.lisa_backward`` holds the exact derivative of that forward pass
+(gradients for Q, K, V, the adaptive weights and alpha), pinned by
+``tests/test_oracle_backward_pins.py`` (finite differences, explicit n x n
+powers of S, branch isolation, planted mistakes).
 
 Every function of ``oracle.lisa`` is pinned by ``tests/test_oracle_pins.py``
 to facts other than itself (brute force on tiny grids, closed forms,
@@ -31,4 +36,9 @@ from .lisa import (  # noqa: F401
     lisa_forward,
     lisa_bruteforce,
     neighbour_offsets,
+)
+from .lisa_backward import (  # noqa: F401
+    global_branch_backward,
+    local_branch_backward,
+    lisa_backward,
 )
