@@ -12,7 +12,7 @@ The only thing both sides consume is the seeded synthetic input generator,
 which holds none of the method's arithmetic and which this package does not
 import.
 
-``oracle.lisa_backward`` holds the exact derivative of that forward pass
+``oracle.backward`` holds the exact derivative of that forward pass
 (gradients for Q, K, V, the adaptive weights and alpha), pinned by
 ``tests/test_oracle_backward_pins.py`` (finite differences, explicit n x n
 powers of S, branch isolation, planted mistakes).
@@ -37,7 +37,7 @@ from .lisa import (  # noqa: F401
     lisa_bruteforce,
     neighbour_offsets,
 )
-from .lisa_backward import (  # noqa: F401
+from .backward import (  # noqa: F401
     global_branch_backward,
     local_branch_backward,
     lisa_backward,

@@ -1,4 +1,4 @@
-"""Pins of the backward oracle (oracle/lisa_backward.py) to facts other than itself (CPU only).
+"""Pins of the backward oracle (oracle/backward.py) to facts other than itself (CPU only).
 
 - Central finite differences of the forward oracle, along random directions
   for every input and element by element on a tiny grid.
@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 from oracle import lisa as olisa
-from oracle import lisa_backward as oback
+from oracle import backward as oback
 
 
 def _problem(rng, B, heads, H, W, dh, dv, T, adaptive, eps=1e-3):
@@ -162,7 +162,7 @@ def _patched_module(old, new):
 
     src = inspect.getsource(oback)
     assert src.count(old) == 1, old
-    mod = types.ModuleType("oracle.lisa_backward_mutant")
+    mod = types.ModuleType("oracle.backward_mutant")
     mod.__package__ = "oracle"
     exec(compile(src.replace(old, new), "<mutant>", "exec"), mod.__dict__)
     return mod
