@@ -130,6 +130,30 @@ lisa_status lisa_apply(const lisa_problem* p, const void* Q, const void* K, cons
                        const float* weights, float beta, const float* alpha, void* Y,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* Backward pass: the gradients of lisa_forward's Y, contracted with the
+ * output gradient dY, for every input.  The note trains every model it
+ * reports [note §3] and gives no backward formulas; these are the exact
+ * derivatives of the forward pass [note §2.1-§2.4] (the ReLU's derivative at
+ * 0 is taken as 0).  The call recomputes the slice statistics (as
+ * lisa_reduce) and then runs the token passes; all arithmetic is fp32.
+ *   Q, K, V, weights, beta, alpha : as for lisa_forward (device)
+ *   dY       : [batch, heads, n, d_v] output gradient, dtype of the problem
+ *   dQ, dK, dV : [batch, heads, n, d] gradients, dtype of the problem
+ *                (bf16: rounded once, to nearest even)
+ *   dweights : [batch, heads, n, T] fp32 gradient of the adaptive weights;
+ *              may be NULL to skip it; ignored with geometric weights (no
+ *              gradient for beta is formed)
+ *   dalpha   : [heads] fp32 gradient of alpha (summed over the batch)
+ * Outputs must not overlap any input, each other or the workspace
+ * (LISA_ERR_PARAM).  Workspace: lisa_backward_workspace_size bytes, 256-byte
+ * aligned, zero-filled before its first use like lisa_forward's; it also
+ * serves lisa_forward, lisa_reduce and lisa_apply of the same problem. */
+size_t lisa_backward_workspace_size(const lisa_problem* p);
+lisa_status lisa_backward(const lisa_problem* p, const void* Q, const void* K, const void* V,
+                          const float* weights, float beta, const float* alpha, const void* dY,
+                          void* dQ, void* dK, void* dV, float* dweights, float* dalpha,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* lisa_status_str(lisa_status s);
 

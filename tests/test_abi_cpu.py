@@ -25,7 +25,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == [
-        "lisa_apply", "lisa_forward", "lisa_reduce", "lisa_status_str", "lisa_workspace_size"]
+        "lisa_apply", "lisa_backward", "lisa_backward_workspace_size", "lisa_forward", "lisa_reduce",
+        "lisa_status_str", "lisa_workspace_size"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -118,6 +119,48 @@ def test_reduce_argument_errors():
     assert reduce(prob(), ws=None) == WS
     p = prob()
     assert reduce(p, ws_bytes=lisa.lisa_workspace_size(p) - 256) == WS
+
+
+DY, DQ, DK, DV, DW, DA = (A + (8 + i) * 0x1000000 for i in range(6))
+
+
+def backward(p, q=Q, k=K, v=V, w=W_, beta=0.5, alpha=AL, dy=DY, dq=DQ, dk=DK, dv=DV, dw=DW, da=DA, ws=WS_,
+             ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lisa.lisa_backward_workspace_size(p) if p is not None else 0
+    return lib.lisa_backward(None if p is None else ctypes.byref(p), q, k, v, w, ctypes.c_float(beta), alpha,
+                             dy, dq, dk, dv, dw, da, ws, ctypes.c_size_t(ws_bytes), None)
+
+
+def test_backward_workspace_covers_the_forward():
+    for T in (1, 3, 8):
+        p = prob(T=T, grid_h=40, grid_w=33)
+        assert lisa.lisa_backward_workspace_size(p) >= lisa.lisa_workspace_size(p) > 0
+    assert lisa.lisa_backward_workspace_size(prob(T=9)) == 0
+
+
+def test_backward_argument_errors():
+    assert backward(None) == NULL
+    assert backward(prob(dtype=3)) == DTYPE
+    assert backward(prob(grid_w=-1)) == SHAPE
+    assert backward(prob(d_h=32)) == UNSUP
+    assert backward(prob(T=9)) == PARAM
+    assert backward(prob(), w=None, beta=1.0) == PARAM
+    for name in ("q", "k", "v", "alpha", "dy", "dq", "dk", "dv", "da"):
+        assert backward(prob(), **{name: None}) == NULL, name
+    assert backward(prob(), dy=DY + 8) == ALIGN
+    assert backward(prob(), dq=DQ + 4) == ALIGN
+    assert backward(prob(), dw=DW + 2) == ALIGN
+    p = prob()
+    assert backward(p, ws=None) == WS
+    assert backward(p, ws_bytes=lisa.lisa_workspace_size(p)) == WS  # the forward's size is not enough
+    assert backward(p, ws=WS_ + 128) == WS
+    # outputs overlapping an input, each other or the workspace
+    assert backward(p, dq=Q + 256) == PARAM
+    assert backward(p, dk=DQ) == PARAM
+    assert backward(p, dv=WS_ + 1024) == PARAM
+    assert backward(p, da=AL) == PARAM
+    assert backward(p, dw=DY) == PARAM
 
 
 def test_status_strings():

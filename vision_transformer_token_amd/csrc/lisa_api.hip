@@ -65,6 +65,9 @@ struct Plan {
   // workspace layout (byte offsets)
   size_t slice_cnt = 0, done_cnt = 0, part_s = 0, part_kv = 0, part_m = 0, fin_s = 0, fin_kv = 0,
          fin_m = 0, frag_kv = 0, frag_m = 0, total = 0;
+  // backward regions, after the forward's (lisa_backward_workspace_size)
+  int nblk = 0;
+  size_t b_pk = 0, b_tok = 0, b_dp = 0, b_da = 0, b_das = 0, b_dmkv = 0, b_ds = 0, btotal = 0;
 };
 
 lisa_status check_problem(const lisa_problem* p) {
@@ -173,6 +176,19 @@ lisa_status make_plan(const lisa_problem* p, Plan& pl) {
   pl.frag_kv = take(BH * kD * kD * pl.esize);
   pl.frag_m = take(BH * kD * kD * pl.esize);
   pl.total = o;
+  // Backward: P_1..P_(T-1); per-token scalars; per-workgroup partials of dP_k,
+  // dalpha and ds; each slice's dalpha, dM and dKV.
+  const size_t T1 = pl.T > 1 ? (size_t)pl.T - 1 : 1;
+  pl.nblk = (pl.n + lisa::kBwdTokens - 1) / lisa::kBwdTokens;
+  const size_t nb = pl.nblk;
+  pl.b_pk = take(BH * T1 * mat);
+  pl.b_tok = take(BH * pl.n * 4 * sizeof(float));
+  pl.b_dp = take(BH * nb * T1 * mat);
+  pl.b_da = take(BH * nb * sizeof(float));
+  pl.b_das = take(BH * sizeof(float));
+  pl.b_dmkv = take(BH * 2 * mat);
+  pl.b_ds = take(BH * nb * vec);
+  pl.btotal = o;
   return LISA_OK;
 }
 
@@ -338,6 +354,84 @@ lisa_status lisa_apply(const lisa_problem* p, const void* Q, const void* K, cons
   (void)hipGetLastError();
   return run(pl, Mode::kApply, Q, K, V, weights, beta, alpha, Y, static_cast<char*>(workspace), p->eps,
              static_cast<hipStream_t>(stream));
+}
+
+size_t lisa_backward_workspace_size(const lisa_problem* p) {
+  Plan pl;
+  return make_plan(p, pl) == LISA_OK ? pl.btotal : 0;
+}
+
+lisa_status lisa_backward(const lisa_problem* p, const void* Q, const void* K, const void* V,
+                          const float* weights, float beta, const float* alpha, const void* dY, void* dQ,
+                          void* dK, void* dV, float* dweights, float* dalpha, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  Plan pl;
+  lisa_status st = make_plan(p, pl);
+  if (st != LISA_OK) return st;
+  if (!weights && !(beta >= 0.f && beta < 1.f)) return LISA_ERR_PARAM;
+  if (!Q || !K || !V || !alpha || !dY || !dQ || !dK || !dV || !dalpha) return LISA_ERR_NULL;
+  if (misaligned(Q, 16) || misaligned(K, 16) || misaligned(V, 16) || misaligned(dY, 16) ||
+      misaligned(dQ, 16) || misaligned(dK, 16) || misaligned(dV, 16) || misaligned(weights, 4) ||
+      misaligned(alpha, 4) || misaligned(dweights, 4) || misaligned(dalpha, 4))
+    return LISA_ERR_ALIGN;
+  if (!workspace || workspace_bytes < pl.btotal || misaligned(workspace, kAlign)) return LISA_ERR_WORKSPACE;
+  // Outputs overlap no input, no other output and not the workspace.
+  const size_t tensor = (size_t)pl.BH * pl.n * kD * pl.esize;
+  const size_t wbytes = (size_t)pl.BH * pl.n * pl.T * sizeof(float);
+  const struct {
+    const void* p;
+    size_t n;
+  } ins[] = {{Q, tensor}, {K, tensor}, {V, tensor}, {dY, tensor}, {weights, weights ? wbytes : 0},
+             {alpha, (size_t)pl.heads * sizeof(float)}, {workspace, pl.btotal}},
+    outs[] = {{dQ, tensor}, {dK, tensor}, {dV, tensor}, {dweights, dweights ? wbytes : 0},
+              {dalpha, (size_t)pl.heads * sizeof(float)}};
+  for (size_t o = 0; o < sizeof(outs) / sizeof(outs[0]); ++o) {
+    for (const auto& in : ins)
+      if (in.n && outs[o].n && overlaps(outs[o].p, outs[o].n, in.p, in.n)) return LISA_ERR_PARAM;
+    for (size_t q = o + 1; q < sizeof(outs) / sizeof(outs[0]); ++q)
+      if (outs[o].n && outs[q].n && overlaps(outs[o].p, outs[o].n, outs[q].p, outs[q].n)) return LISA_ERR_PARAM;
+  }
+  (void)hipGetLastError();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  // The slice statistics s, phi(K)^T V and M, as lisa_reduce forms them.
+  st = run(pl, Mode::kReduce, Q, K, V, nullptr, 0.f, nullptr, nullptr, ws, p->eps, s);
+  if (st != LISA_OK) return st;
+  lisa::BwdArgs a{};
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.dY = dY;
+  a.weights = weights;
+  a.alpha = alpha;
+  a.dQ = dQ;
+  a.dK = dK;
+  a.dV = dV;
+  a.dweights = weights ? dweights : nullptr;
+  a.dalpha = dalpha;
+  const double b = weights ? 0.0 : (double)beta;
+  const double norm = (1.0 - b) / (1.0 - std::pow(b, pl.T));
+  for (int k = 0; k < lisa::kMaxT; ++k) a.geo[k] = k < pl.T ? (float)(norm * std::pow(b, k)) : 0.f;
+  a.H = pl.H;
+  a.W = pl.W;
+  a.n = pl.n;
+  a.T = pl.T;
+  a.heads = pl.heads;
+  a.BH = pl.BH;
+  a.nblk = pl.nblk;
+  a.eps = p->eps;
+  a.fin_s = reinterpret_cast<const float*>(ws + pl.fin_s);
+  a.fin_kv = reinterpret_cast<const float*>(ws + pl.fin_kv);
+  a.fin_m = reinterpret_cast<const float*>(ws + pl.fin_m);
+  a.pk = reinterpret_cast<float*>(ws + pl.b_pk);
+  a.tok = reinterpret_cast<float4*>(ws + pl.b_tok);
+  a.dp_part = reinterpret_cast<float*>(ws + pl.b_dp);
+  a.da_part = reinterpret_cast<float*>(ws + pl.b_da);
+  a.da_slice = reinterpret_cast<float*>(ws + pl.b_das);
+  a.dmkv = reinterpret_cast<float*>(ws + pl.b_dmkv);
+  a.ds_part = reinterpret_cast<float*>(ws + pl.b_ds);
+  if (lisa::launch_backward(pl.dtype, a, s) != hipSuccess) return LISA_ERR_HIP;
+  return LISA_OK;
 }
 
 const char* lisa_status_str(lisa_status s) {

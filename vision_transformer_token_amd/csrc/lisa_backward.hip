@@ -1,0 +1,633 @@
+// LiSA backward pass on gfx950: gradients of Y = alpha G + (1 - alpha) L
+// with respect to Q, K, V, the adaptive walk weights and alpha.
+//
+// Source: the reading note of "LiSA: Linear Stochastic Attention for
+// Long-Range Visual Modeling" trains every model it reports (§3) and picks
+// the truncation T with the cost of backpropagation in mind (§2.3); it gives
+// no backward formulas.  The gradients here are the exact adjoint of the
+// forward pass (§2.1-§2.4), step by step:
+//   G_i = w_0(i) V_i + sum_{k>=1} w_k(i) Qt_i P_k,  P_k = M^(k-1) phi(K)^T V,
+//   Qt_i = r_i phi(Q_i), r_i = 1 / (phi(Q_i) . s + eps), s = sum_j phi(K_j),
+//   M = phi(K)^T Qt;  L_i = softmax over the 3x3 window of q_i . k_j / 8.
+// With dG = alpha dY and dL = (1 - alpha) dY:
+//   dP_k = sum_i w_k(i) Qt_i^T dG_i              (token reduction, pass A)
+//   dM, dKV by the power chain in d_h space      (adjoint kernel)
+//   dQt_i = sum_k w_k(i) P_k dG_i + dM^T phi(K_i)
+//   dz_i = -r_i^2 dQt_i . phi(Q_i),  ds = sum_i dz_i phi(Q_i)   (pass B)
+//   dQ_i = (r_i dQt_i + dz_i s) [Q_i > 0] + local
+//   dK_j = (dM Qt_j + dKV V_j + ds) [K_j > 0] + local
+//   dV_j = w_0(j) dG_j + dKV^T phi(K_j) + local
+//   dw_k(i) = dG_i . (Qt_i P_k), dw_0(i) = dG_i . V_i, dalpha = sum dY.(G - L)
+// The local branch's softmax adjoint uses, per centre token i, the window's
+// logit maximum m_i and sum Z_i and c_i = dL_i . L_i, which pass A keeps.
+//
+// Layout: one lane per token (kBwdTokens per workgroup) for the token
+// passes; the slice's 64 x 64 matrices sit in LDS and every lane reads the
+// same element at once (broadcast).  Vectors that are indexed at run time
+// live in a per-lane LDS row; the rest stay in registers.  Everything is
+// fp32; outputs dQ, dK, dV are written once in the input dtype.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lisa_device.hpp"
+#include "lisa_kernels.hpp"
+
+namespace lisa {
+namespace {
+
+constexpr int kBT = kBwdTokens;
+constexpr int kR = kD + 1;           // padded LDS row (floats)
+constexpr float kRs = 0.125f;        // 1 / sqrt(d_h), d_h = 64
+constexpr int kAdjThreads = 256;
+
+template <class S>
+__device__ __forceinline__ void load_row(const S* p, float (&x)[kD]) {
+#pragma unroll
+  for (int e = 0; e < kD; e += 4) load4(p + e, &x[e]);
+}
+template <class S>
+__device__ __forceinline__ void store_row(S* p, const float (&x)[kD]) {
+#pragma unroll
+  for (int e = 0; e < kD; e += 4) store4(p + e, &x[e]);
+}
+template <class S>
+__device__ __forceinline__ float dot_row(const S* p, const float (&x)[kD]) {
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < kD; e += 4) {
+    float y[4];
+    load4(p + e, y);
+    acc += x[e] * y[0] + x[e + 1] * y[1] + x[e + 2] * y[2] + x[e + 3] * y[3];
+  }
+  return acc;
+}
+template <class S>
+__device__ __forceinline__ void axpy_row(float f, const S* p, float (&x)[kD]) {
+#pragma unroll
+  for (int e = 0; e < kD; e += 4) {
+    float y[4];
+    load4(p + e, y);
+    x[e] += f * y[0];
+    x[e + 1] += f * y[1];
+    x[e + 2] += f * y[2];
+    x[e + 3] += f * y[3];
+  }
+}
+
+// y[c] += sum_a xs[a] mat[a][c]  (xs: the lane's LDS row; mat: 64 x 64 in LDS)
+__device__ __forceinline__ void row_times_mat(const float* xs, const float* mat, float (&y)[kD]) {
+#pragma unroll 1
+  for (int a = 0; a < kD; ++a) {
+    const float xa = xs[a];
+    const float4* m = reinterpret_cast<const float4*>(mat + a * kD);
+#pragma unroll
+    for (int c = 0; c < kD / 4; ++c) {
+      const float4 v = m[c];
+      y[4 * c] += xa * v.x;
+      y[4 * c + 1] += xa * v.y;
+      y[4 * c + 2] += xa * v.z;
+      y[4 * c + 3] += xa * v.w;
+    }
+  }
+}
+// ys[a] = f * sum_c mat[a][c] x[c]  (+= when accumulate)
+__device__ __forceinline__ void mat_times_vec(const float* mat, const float (&x)[kD], float f, float* ys,
+                                              bool accumulate) {
+#pragma unroll 1
+  for (int a = 0; a < kD; ++a) {
+    const float4* m = reinterpret_cast<const float4*>(mat + a * kD);
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < kD / 4; ++c) {
+      const float4 v = m[c];
+      acc += v.x * x[4 * c] + v.y * x[4 * c + 1] + v.z * x[4 * c + 2] + v.w * x[4 * c + 3];
+    }
+    ys[a] = accumulate ? ys[a] + f * acc : f * acc;
+  }
+}
+// sum_a xs[a] sum_c mat[a][c] x[c]
+__device__ __forceinline__ float bilinear(const float* xs, const float* mat, const float (&x)[kD]) {
+  float tot = 0.f;
+#pragma unroll 1
+  for (int a = 0; a < kD; ++a) {
+    const float4* m = reinterpret_cast<const float4*>(mat + a * kD);
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < kD / 4; ++c) {
+      const float4 v = m[c];
+      acc += v.x * x[4 * c] + v.y * x[4 * c + 1] + v.z * x[4 * c + 2] + v.w * x[4 * c + 3];
+    }
+    tot += xs[a] * acc;
+  }
+  return tot;
+}
+
+// Whole workgroup: copy a 64 x 64 fp32 matrix into LDS.
+__device__ __forceinline__ void load_mat(float* dst, const float* src) {
+  for (int e = threadIdx.x * 4; e < kD * kD; e += blockDim.x * 4)
+    *reinterpret_cast<float4*>(dst + e) = *reinterpret_cast<const float4*>(src + e);
+}
+
+__device__ __forceinline__ float wgt(const BwdArgs& a, size_t tok, int k) {
+  return a.weights ? a.weights[tok * a.T + k] : a.geo[k];
+}
+
+// The valid 3x3 window of token i: slot j (0..8) is the cell (row + j/3 - 1,
+// col + j%3 - 1); returns its token index or -1 off the grid.
+__device__ __forceinline__ int window_cell(const BwdArgs& a, int row, int col, int j) {
+  const int rr = row + j / 3 - 1, cc = col + j % 3 - 1;
+  return (rr >= 0 && rr < a.H && cc >= 0 && cc < a.W) ? rr * a.W + cc : -1;
+}
+
+// P_1 = phi(K)^T V, P_k = M P_(k-1) for k = 2 .. T-1: one workgroup per slice.
+__global__ __launch_bounds__(kAdjThreads) void bwd_powers(BwdArgs a) {
+  __shared__ float Ms[kD * kD];
+  __shared__ float Ps[kD * kR];
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int T1 = a.T - 1;
+  if (T1 < 1) return;
+  const float* M = a.fin_m + (size_t)b * kD * kD;
+  const float* P1 = a.fin_kv + (size_t)b * kD * kD;
+  float* out = a.pk + (size_t)b * T1 * kD * kD;
+  load_mat(Ms, M);
+  for (int e = t; e < kD * kD; e += kAdjThreads) {
+    Ps[(e >> 6) * kR + (e & 63)] = P1[e];
+    out[e] = P1[e];
+  }
+  for (int k = 2; k <= T1; ++k) {
+    __syncthreads();
+    float acc[kD * kD / kAdjThreads];
+#pragma unroll
+    for (int x = 0; x < kD * kD / kAdjThreads; ++x) {
+      const int e = t + kAdjThreads * x, r = e >> 6, c = e & 63;
+      float v = 0.f;
+      for (int j = 0; j < kD; ++j) v += Ms[r * kD + j] * Ps[j * kR + c];
+      acc[x] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < kD * kD / kAdjThreads; ++x) {
+      const int e = t + kAdjThreads * x;
+      Ps[(e >> 6) * kR + (e & 63)] = acc[x];
+      out[(size_t)(k - 1) * kD * kD + e] = acc[x];
+    }
+  }
+}
+
+// Pass A: per token the local window statistics, dY . V_i, dY . (Qt_i P_k),
+// the weight gradients and dalpha's share; per workgroup the partial sums of
+// dP_k = sum_i w_k(i) alpha Qt_i^T dY_i.
+template <class S>
+__global__ __launch_bounds__(kBT) void bwd_token_a(BwdArgs a) {
+  extern __shared__ __align__(16) float sm[];
+  float* Ps = sm;                        // kD * kD: P_k
+  float* s_sh = Ps + kD * kD;            // kD
+  float* qt_sh = s_sh + kD;              // kBT rows of Qt (padded)
+  float* dy_sh = qt_sh + kBT * kR;       // kBT rows of dY (padded)
+  float* w_sh = dy_sh + kBT * kR;        // kBT x kMaxT weights
+  float* red = w_sh + kBT * kMaxT;       // kBT
+  const int b = blockIdx.y, t = threadIdx.x, blk = blockIdx.x;
+  const int i = blk * kBT + t;
+  const bool on = i < a.n;
+  const float alpha = a.alpha[b % a.heads];
+  const size_t base = (size_t)b * a.n;
+  const S* Qb = static_cast<const S*>(a.Q) + base * kD;
+  const S* Kb = static_cast<const S*>(a.K) + base * kD;
+  const S* Vb = static_cast<const S*>(a.V) + base * kD;
+  const S* dYb = static_cast<const S*>(a.dY) + base * kD;
+  if (t < kD) s_sh[t] = a.fin_s[(size_t)b * kD + t];
+  for (int k = 0; k < kMaxT; ++k) w_sh[t * kMaxT + k] = (on && k < a.T) ? wgt(a, base + i, k) : 0.f;
+
+  float q[kD], dy[kD];
+  float m = 0.f, Z = 1.f, dyL = 0.f, dyv = 0.f;
+  if (on) {
+    load_row(Qb + (size_t)i * kD, q);
+    load_row(dYb + (size_t)i * kD, dy);
+    // Local branch at token i: window logits, their max and sum, dY . L_i.
+    const int row = i / a.W, col = i % a.W;
+    float z[9];
+    m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 9; ++j) {
+      const int c = window_cell(a, row, col, j);
+      z[j] = c >= 0 ? dot_row(Kb + (size_t)c * kD, q) * kRs : -INFINITY;
+      m = fmaxf(m, z[j]);
+    }
+    Z = 0.f;
+#pragma unroll
+    for (int j = 0; j < 9; ++j) {
+      const int c = window_cell(a, row, col, j);
+      if (c >= 0) {
+        const float e = __expf(z[j] - m);
+        Z += e;
+        dyL += e * dot_row(Vb + (size_t)c * kD, dy);
+      }
+    }
+    dyL /= Z;
+    dyv = dot_row(Vb + (size_t)i * kD, dy);
+  } else {
+#pragma unroll
+    for (int e = 0; e < kD; ++e) q[e] = dy[e] = 0.f;
+  }
+  __syncthreads();  // s_sh, w_sh
+  // Qt_i = r_i phi(Q_i).
+  float den = 0.f;
+#pragma unroll
+  for (int e = 0; e < kD; ++e) {
+    q[e] = fmaxf(q[e], 0.f);
+    den += q[e] * s_sh[e];
+  }
+  const float r = 1.f / (den + a.eps);
+#pragma unroll
+  for (int e = 0; e < kD; ++e) {
+    q[e] *= r;
+    qt_sh[t * kR + e] = q[e];
+    dy_sh[t * kR + e] = dy[e];
+  }
+  float dyy[kMaxT];
+#pragma unroll
+  for (int k = 0; k < kMaxT; ++k) dyy[k] = 0.f;
+  const int T1 = a.T - 1;
+  const int a0 = (t >> 3) * 4, c0 = (t & 7) * 8;  // this lane's 4 x 8 tile of dP_k
+#pragma unroll
+  for (int k = 1; k < kMaxT; ++k) {
+    if (k > T1) break;
+    __syncthreads();
+    load_mat(Ps, a.pk + ((size_t)b * T1 + (k - 1)) * kD * kD);
+    __syncthreads();
+    // dY_i . (Qt_i P_k) = Qt_i^T P_k dY_i.
+    dyy[k] = bilinear(qt_sh + t * kR, Ps, dy);
+    // This workgroup's share of dP_k.
+    float acc[4][8] = {};
+#pragma unroll 2
+    for (int tt = 0; tt < kBT; ++tt) {
+      const float f = alpha * w_sh[tt * kMaxT + k];
+      float qa[4], dc[8];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) qa[x] = f * qt_sh[tt * kR + a0 + x];
+#pragma unroll
+      for (int y = 0; y < 8; ++y) dc[y] = dy_sh[tt * kR + c0 + y];
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 8; ++y) acc[x][y] += qa[x] * dc[y];
+    }
+    float* dst = a.dp_part + (((size_t)b * a.nblk + blk) * T1 + (k - 1)) * kD * kD;
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 8; y += 4)
+        *reinterpret_cast<float4*>(dst + (a0 + x) * kD + c0 + y) =
+            make_float4(acc[x][y], acc[x][y + 1], acc[x][y + 2], acc[x][y + 3]);
+  }
+  // Scalars of the token.
+  float wy = 0.f;
+#pragma unroll
+  for (int k = 1; k < kMaxT; ++k)
+    if (k <= T1) wy += w_sh[t * kMaxT + k] * dyy[k];
+  const float dyG = w_sh[t * kMaxT] * dyv + wy;
+  if (on) {
+    // a_i = (sum_k w_k P_k dG_i) . phi(Q_i) = alpha / r_i * sum_k w_k dY_i . (Qt_i P_k)
+    a.tok[base + i] = make_float4(m, Z, (1.f - alpha) * dyL, alpha / r * wy);
+    if (a.dweights) {
+      float* dw = a.dweights + (base + i) * a.T;
+      dw[0] = alpha * dyv;
+#pragma unroll
+      for (int k = 1; k < kMaxT; ++k)
+        if (k <= T1) dw[k] = alpha * dyy[k];
+    }
+  }
+  // dalpha's share: sum_i dY_i . (G_i - L_i), fixed-order tree.
+  red[t] = on ? dyG - dyL : 0.f;
+  __syncthreads();
+  for (int o = kBT / 2; o > 0; o >>= 1) {
+    if (t < o) red[t] += red[t + o];
+    __syncthreads();
+  }
+  if (t == 0) a.da_part[(size_t)b * a.nblk + blk] = red[0];
+}
+
+// dP_k summed over the workgroups in order; then, from the last term down,
+// dM += dP_k P_(k-1)^T and dP_(k-1) += M^T dP_k; dKV = dP_1.  One workgroup
+// per slice; also the slice's dalpha.
+__global__ __launch_bounds__(kAdjThreads) void bwd_adjoint(BwdArgs a) {
+  extern __shared__ __align__(16) float sm[];
+  const int b = blockIdx.x, t = threadIdx.x, T1 = a.T - 1;
+  constexpr int kX = kD * kD / kAdjThreads;  // outputs per thread
+  float* dP = sm;                            // T1 x 64 x 64
+  float* Ms = dP + (size_t)(T1 > 0 ? T1 : 1) * kD * kD;
+  float* Pp = Ms + kD * kD;                  // P_(k-1), padded rows
+  float* dMo = a.dmkv + (size_t)b * 2 * kD * kD;
+  float* dKVo = dMo + kD * kD;
+  if (t == 0) {
+    float v = 0.f;
+    for (int p = 0; p < a.nblk; ++p) v += a.da_part[(size_t)b * a.nblk + p];
+    a.da_slice[b] = v;
+  }
+  if (T1 < 1) {
+    for (int e = t; e < kD * kD; e += kAdjThreads) dMo[e] = dKVo[e] = 0.f;
+    return;
+  }
+  const size_t per = (size_t)T1 * kD * kD;
+  for (size_t e = t; e < per; e += kAdjThreads) {
+    float v = 0.f;
+    for (int p = 0; p < a.nblk; ++p) v += a.dp_part[((size_t)b * a.nblk + p) * per + e];
+    dP[e] = v;
+  }
+  load_mat(Ms, a.fin_m + (size_t)b * kD * kD);
+  float dM[kX] = {};
+  for (int k = T1; k >= 2; --k) {
+    __syncthreads();
+    const float* Pk1 = a.pk + ((size_t)b * T1 + (k - 2)) * kD * kD;
+    for (int e = t; e < kD * kD; e += kAdjThreads) Pp[(e >> 6) * kR + (e & 63)] = Pk1[e];
+    __syncthreads();
+    const float* dPk = dP + (size_t)(k - 1) * kD * kD;
+    float up[kX];
+#pragma unroll
+    for (int x = 0; x < kX; ++x) {
+      const int e = t + kAdjThreads * x, r = e >> 6, c = e & 63;
+      float v = 0.f, u = 0.f;
+      for (int j = 0; j < kD; ++j) {
+        v += dPk[r * kD + j] * Pp[c * kR + j];   // (dP_k P_(k-1)^T)[r][c]
+        u += Ms[j * kD + r] * dPk[j * kD + c];    // (M^T dP_k)[r][c]
+      }
+      dM[x] += v;
+      up[x] = u;
+    }
+    __syncthreads();
+    float* dPm = dP + (size_t)(k - 2) * kD * kD;
+#pragma unroll
+    for (int x = 0; x < kX; ++x) dPm[t + kAdjThreads * x] += up[x];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < kX; ++x) {
+    const int e = t + kAdjThreads * x;
+    dMo[e] = dM[x];
+    dKVo[e] = dP[e];
+  }
+}
+
+// Pass B: dz_i = -r_i^2 (a_i + phi(K_i)^T dM phi(Q_i)) (kept in tok[i].w) and
+// the workgroup's share of ds = sum_i dz_i phi(Q_i).
+template <class S>
+__global__ __launch_bounds__(kBT) void bwd_token_b(BwdArgs a) {
+  __shared__ __align__(16) float dMs[kD * kD];
+  __shared__ float s_sh[kD];
+  __shared__ float rows[kBT * kR];
+  const int b = blockIdx.y, t = threadIdx.x, blk = blockIdx.x;
+  const int i = blk * kBT + t;
+  const bool on = i < a.n;
+  const size_t base = (size_t)b * a.n;
+  load_mat(dMs, a.dmkv + (size_t)b * 2 * kD * kD);
+  if (t < kD) s_sh[t] = a.fin_s[(size_t)b * kD + t];
+  float u[kD], kp[kD];
+  if (on) {
+    load_row(static_cast<const S*>(a.Q) + (base + i) * kD, u);
+    load_row(static_cast<const S*>(a.K) + (base + i) * kD, kp);
+  } else {
+#pragma unroll
+    for (int e = 0; e < kD; ++e) u[e] = kp[e] = 0.f;
+  }
+  __syncthreads();
+  float den = 0.f;
+#pragma unroll
+  for (int e = 0; e < kD; ++e) {
+    u[e] = fmaxf(u[e], 0.f);
+    den += u[e] * s_sh[e];
+    rows[t * kR + e] = fmaxf(kp[e], 0.f);
+  }
+  const float r = 1.f / (den + a.eps);
+  float dz = 0.f;
+  if (on) {
+    float4* tk = a.tok + base + i;
+    const float4 v = *tk;
+    dz = -r * r * (v.w + bilinear(rows + t * kR, dMs, u));
+    *tk = make_float4(v.x, v.y, v.z, dz);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < kD; ++e) rows[t * kR + e] = dz * u[e];
+  __syncthreads();
+  if (t < kD) {
+    float v = 0.f;
+    for (int tt = 0; tt < kBT; ++tt) v += rows[tt * kR + t];
+    a.ds_part[((size_t)b * a.nblk + blk) * kD + t] = v;
+  }
+}
+
+// dQ_i = (r_i dQt_i + dz_i s) [Q_i > 0] + sum_j dz_ij k_j / 8, with
+// dQt_i = dM^T phi(K_i) + sum_k w_k P_k dG_i and dz_ij the softmax adjoint
+// of window slot j.
+template <class S>
+__global__ __launch_bounds__(kBT) void bwd_token_q(BwdArgs a) {
+  __shared__ __align__(16) float Ps[kD * kD];
+  __shared__ __align__(16) float dMs[kD * kD];
+  __shared__ float s_sh[kD];
+  __shared__ float rows[kBT * kR];
+  const int b = blockIdx.y, t = threadIdx.x, blk = blockIdx.x;
+  const int i = blk * kBT + t;
+  const bool on = i < a.n;
+  const size_t base = (size_t)b * a.n;
+  const float alpha = a.alpha[b % a.heads];
+  const S* Qb = static_cast<const S*>(a.Q) + base * kD;
+  const S* Kb = static_cast<const S*>(a.K) + base * kD;
+  const S* Vb = static_cast<const S*>(a.V) + base * kD;
+  const S* dYb = static_cast<const S*>(a.dY) + base * kD;
+  load_mat(dMs, a.dmkv + (size_t)b * 2 * kD * kD);
+  if (t < kD) s_sh[t] = a.fin_s[(size_t)b * kD + t];
+  // dQt = dM^T phi(K_i): row phi(K_i) times dM.
+  float x[kD];
+  if (on) load_row(Kb + (size_t)i * kD, x);
+  else
+#pragma unroll
+    for (int e = 0; e < kD; ++e) x[e] = 0.f;
+#pragma unroll
+  for (int e = 0; e < kD; ++e) rows[t * kR + e] = fmaxf(x[e], 0.f);
+  float dqt[kD] = {};
+  __syncthreads();
+  row_times_mat(rows + t * kR, dMs, dqt);
+  // + sum_k w_k P_k dG_i, dG_i = alpha dY_i.
+  if (on) load_row(dYb + (size_t)i * kD, x);
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < kD; ++e) rows[t * kR + e] = dqt[e];
+  const int T1 = a.T - 1;
+  for (int k = 1; k <= T1; ++k) {
+    __syncthreads();
+    load_mat(Ps, a.pk + ((size_t)b * T1 + (k - 1)) * kD * kD);
+    __syncthreads();
+    mat_times_vec(Ps, x, on ? alpha * wgt(a, base + i, k) : 0.f, rows + t * kR, true);
+  }
+  if (!on) return;  // no barrier follows
+  const float4 tk = a.tok[base + i];  // m_i, Z_i, c_i, dz_i
+  float q[kD];
+  load_row(Qb + (size_t)i * kD, q);
+  float den = 0.f;
+#pragma unroll
+  for (int e = 0; e < kD; ++e) den += fmaxf(q[e], 0.f) * s_sh[e];
+  const float r = 1.f / (den + a.eps);
+#pragma unroll
+  for (int e = 0; e < kD; ++e) dqt[e] = q[e] > 0.f ? r * rows[t * kR + e] + tk.w * s_sh[e] : 0.f;
+  // Local: dz_ij = p_ij ((1 - alpha) dY_i . V_j - c_i).
+  const int row = i / a.W, col = i % a.W;
+#pragma unroll 1
+  for (int j = 0; j < 9; ++j) {
+    const int c = window_cell(a, row, col, j);
+    if (c < 0) continue;
+    const S* kj = Kb + (size_t)c * kD;
+    const float p = __expf(dot_row(kj, q) * kRs - tk.x) / tk.y;
+    const float g = p * ((1.f - alpha) * dot_row(Vb + (size_t)c * kD, x) - tk.z);
+    axpy_row(g * kRs, kj, dqt);
+  }
+  store_row(static_cast<S*>(a.dQ) + (base + i) * kD, dqt);
+}
+
+// dK_j = (dM Qt_j + dKV V_j + ds) [K_j > 0] + sum_i dz_ij q_i / 8 over the
+// centres i whose window holds j (the window relation is symmetric).
+template <class S>
+__global__ __launch_bounds__(kBT) void bwd_token_k(BwdArgs a) {
+  __shared__ __align__(16) float dMs[kD * kD];
+  __shared__ __align__(16) float dKVs[kD * kD];
+  __shared__ float s_sh[kD];
+  __shared__ float ds_sh[kD];
+  __shared__ float rows[kBT * kR];
+  const int b = blockIdx.y, t = threadIdx.x, blk = blockIdx.x;
+  const int i = blk * kBT + t;
+  const bool on = i < a.n;
+  const size_t base = (size_t)b * a.n;
+  const float alpha = a.alpha[b % a.heads];
+  const S* Qb = static_cast<const S*>(a.Q) + base * kD;
+  const S* Kb = static_cast<const S*>(a.K) + base * kD;
+  const S* Vb = static_cast<const S*>(a.V) + base * kD;
+  const S* dYb = static_cast<const S*>(a.dY) + base * kD;
+  load_mat(dMs, a.dmkv + (size_t)b * 2 * kD * kD);
+  load_mat(dKVs, a.dmkv + (size_t)b * 2 * kD * kD + kD * kD);
+  if (t < kD) {
+    s_sh[t] = a.fin_s[(size_t)b * kD + t];
+    float v = 0.f;
+    for (int p = 0; p < a.nblk; ++p) v += a.ds_part[((size_t)b * a.nblk + p) * kD + t];
+    ds_sh[t] = v;
+  }
+  __syncthreads();
+  if (!on) return;  // no barrier follows
+  // dM Qt_j + dKV V_j + ds.
+  float x[kD];
+  load_row(Qb + (size_t)i * kD, x);
+  float den = 0.f;
+#pragma unroll
+  for (int e = 0; e < kD; ++e) {
+    x[e] = fmaxf(x[e], 0.f);
+    den += x[e] * s_sh[e];
+  }
+  const float r = 1.f / (den + a.eps);
+#pragma unroll
+  for (int e = 0; e < kD; ++e) x[e] *= r;
+  float* acc = rows + t * kR;
+  mat_times_vec(dMs, x, 1.f, acc, false);
+  load_row(Vb + (size_t)i * kD, x);
+  mat_times_vec(dKVs, x, 1.f, acc, true);
+  float kr[kD], dk[kD];
+  load_row(Kb + (size_t)i * kD, kr);
+#pragma unroll
+  for (int e = 0; e < kD; ++e) dk[e] = kr[e] > 0.f ? acc[e] + ds_sh[e] : 0.f;
+  // Local: token i as the neighbour of centre c.
+  const int row = i / a.W, col = i % a.W;
+#pragma unroll 1
+  for (int j = 0; j < 9; ++j) {
+    const int c = window_cell(a, row, col, j);
+    if (c < 0) continue;
+    const float4 tc = a.tok[base + c];
+    const S* qc = Qb + (size_t)c * kD;
+    const float p = __expf(dot_row(qc, kr) * kRs - tc.x) / tc.y;
+    const float g = p * ((1.f - alpha) * dot_row(dYb + (size_t)c * kD, x) - tc.z);
+    axpy_row(g * kRs, qc, dk);
+  }
+  store_row(static_cast<S*>(a.dK) + (base + i) * kD, dk);
+}
+
+// dV_j = w_0(j) alpha dY_j + dKV^T phi(K_j) + sum_i p_ij (1 - alpha) dY_i.
+template <class S>
+__global__ __launch_bounds__(kBT) void bwd_token_v(BwdArgs a) {
+  __shared__ __align__(16) float dKVs[kD * kD];
+  __shared__ float rows[kBT * kR];
+  const int b = blockIdx.y, t = threadIdx.x, blk = blockIdx.x;
+  const int i = blk * kBT + t;
+  const bool on = i < a.n;
+  const size_t base = (size_t)b * a.n;
+  const float alpha = a.alpha[b % a.heads];
+  const S* Qb = static_cast<const S*>(a.Q) + base * kD;
+  const S* Kb = static_cast<const S*>(a.K) + base * kD;
+  const S* dYb = static_cast<const S*>(a.dY) + base * kD;
+  load_mat(dKVs, a.dmkv + (size_t)b * 2 * kD * kD + kD * kD);
+  float kr[kD];
+  if (on) load_row(Kb + (size_t)i * kD, kr);
+  else
+#pragma unroll
+    for (int e = 0; e < kD; ++e) kr[e] = 0.f;
+#pragma unroll
+  for (int e = 0; e < kD; ++e) rows[t * kR + e] = fmaxf(kr[e], 0.f);
+  __syncthreads();
+  if (!on) return;  // no barrier follows
+  float dv[kD];
+  load_row(dYb + (size_t)i * kD, dv);
+  const float f0 = alpha * wgt(a, base + i, 0);
+#pragma unroll
+  for (int e = 0; e < kD; ++e) dv[e] *= f0;
+  row_times_mat(rows + t * kR, dKVs, dv);
+  const int row = i / a.W, col = i % a.W;
+#pragma unroll 1
+  for (int j = 0; j < 9; ++j) {
+    const int c = window_cell(a, row, col, j);
+    if (c < 0) continue;
+    const float4 tc = a.tok[base + c];
+    const float p = __expf(dot_row(Qb + (size_t)c * kD, kr) * kRs - tc.x) / tc.y;
+    axpy_row(p * (1.f - alpha), dYb + (size_t)c * kD, dv);
+  }
+  store_row(static_cast<S*>(a.dV) + (base + i) * kD, dv);
+}
+
+// dalpha[h] = sum over the batch of the slices' shares, in batch order.
+__global__ __launch_bounds__(256) void bwd_dalpha(BwdArgs a) {
+  for (int h = threadIdx.x; h < a.heads; h += blockDim.x) {
+    float v = 0.f;
+    for (int b = h; b < a.BH; b += a.heads) v += a.da_slice[b];
+    a.dalpha[h] = v;
+  }
+}
+
+template <class S>
+hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
+  const size_t lds_a = (size_t)(kD * kD + kD + 2 * kBT * kR + kBT * kMaxT + kBT) * sizeof(float);
+  const int T1 = a.T - 1 > 0 ? a.T - 1 : 1;
+  const size_t lds_adj = ((size_t)T1 * kD * kD + kD * kD + kD * kR) * sizeof(float);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_token_a<S>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_a);
+    if (e != hipSuccess) return e;
+    const size_t lds_adj_max = ((size_t)(kMaxT - 1) * kD * kD + kD * kD + kD * kR) * sizeof(float);
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_adjoint),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_adj_max);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const dim3 tok(a.nblk, a.BH);
+  if (a.T >= 2) hipLaunchKernelGGL(bwd_powers, dim3(a.BH), dim3(kAdjThreads), 0, s, a);
+  hipLaunchKernelGGL(bwd_token_a<S>, tok, dim3(kBT), lds_a, s, a);
+  hipLaunchKernelGGL(bwd_adjoint, dim3(a.BH), dim3(kAdjThreads), lds_adj, s, a);
+  hipLaunchKernelGGL(bwd_token_b<S>, tok, dim3(kBT), 0, s, a);
+  hipLaunchKernelGGL(bwd_token_q<S>, tok, dim3(kBT), 0, s, a);
+  hipLaunchKernelGGL(bwd_token_k<S>, tok, dim3(kBT), 0, s, a);
+  hipLaunchKernelGGL(bwd_token_v<S>, tok, dim3(kBT), 0, s, a);
+  hipLaunchKernelGGL(bwd_dalpha, dim3(1), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward(int dtype, const BwdArgs& a, hipStream_t s) {
+  return dtype == 1 ? launch_typed<uint16_t>(a, s) : launch_typed<float>(a, s);
+}
+
+}  // namespace lisa

@@ -101,4 +101,38 @@ struct FlowArgs {
 // dtype: 0 = fp32, 1 = bf16 (lisa_dtype).  grid = workgroups to launch.
 hipError_t launch_flow(int dtype, const FlowArgs& a, int grid, hipStream_t s);
 
+// Backward pass (lisa_backward): token passes take kBwdTokens tokens per
+// workgroup, one per lane; the slice statistics come from a statistics launch
+// (fin_s, fin_kv, fin_m of FlowArgs) that ran before on the same stream.
+constexpr int kBwdTokens = 128;
+
+struct BwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* dY;
+  const float* weights;   // [BH][n][T] or nullptr (geometric: geo)
+  const float* alpha;     // [heads]
+  void* dQ;
+  void* dK;
+  void* dV;
+  float* dweights;        // [BH][n][T] or nullptr
+  float* dalpha;          // [heads]
+  float geo[kMaxT];
+  int H, W, n, T, heads, BH, nblk;  // nblk = ceil(n / kBwdTokens)
+  float eps;
+  const float* fin_s;     // [BH][64]
+  const float* fin_kv;    // [BH][64*64]
+  const float* fin_m;     // [BH][64*64]
+  float* pk;              // [BH][T-1][64*64]  P_k = M^(k-1) phi(K)^T V, k = 1..T-1
+  float4* tok;            // [BH][n]  per token: local max, local sum, dL_i . L_i, then (a_i -> dz_i)
+  float* dp_part;         // [BH][nblk][T-1][64*64]  per-workgroup partials of dP_k
+  float* da_part;         // [BH][nblk]  partials of dalpha
+  float* da_slice;        // [BH]
+  float* dmkv;            // [BH][2][64*64]  dM, dKV
+  float* ds_part;         // [BH][nblk][64]  partials of ds
+};
+
+hipError_t launch_backward(int dtype, const BwdArgs& a, hipStream_t s);
+
 }  // namespace lisa

@@ -72,6 +72,11 @@ _lib.lisa_apply.argtypes = _lib.lisa_forward.argtypes
 _lib.lisa_apply.restype = ctypes.c_int
 _lib.lisa_reduce.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.lisa_reduce.restype = ctypes.c_int
+_lib.lisa_backward_workspace_size.argtypes = [_P]
+_lib.lisa_backward_workspace_size.restype = ctypes.c_size_t
+_lib.lisa_backward.argtypes = [_P, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                               _vp, ctypes.c_size_t, _vp]
+_lib.lisa_backward.restype = ctypes.c_int
 _lib.lisa_status_str.argtypes = [ctypes.c_int]
 _lib.lisa_status_str.restype = ctypes.c_char_p
 
@@ -199,6 +204,50 @@ def lisa_reduce(q, k, v, *, grid, eps=1e-6, T=3, workspace=None, outputs=True, s
     if st != LISA_OK:
         raise LisaError(st, "lisa_reduce")
     return (s, kv, m) if outputs else None
+
+
+def lisa_backward_workspace_size(problem):
+    return int(_lib.lisa_backward_workspace_size(ctypes.byref(problem)))
+
+
+def lisa_backward(q, k, v, dy, *, grid, T, alpha, weights=None, beta=None, eps=1e-6, workspace=None,
+                  stream=None):
+    """Gradients of lisa_forward for the output gradient ``dy``; see include/lisa.h.
+
+    Returns a dict with "dq", "dk", "dv" (dtype of q), "dweights" (fp32
+    [B, heads, n, T], None with geometric weights) and "dalpha" (fp32
+    [heads]).  ``workspace`` (zero-filled, lisa_backward_workspace_size
+    bytes) is allocated when not given.
+    """
+    _check_tensors(q=q, k=k, v=v, dy=dy, alpha=alpha, weights=weights, workspace=workspace)
+    if weights is not None and weights.dtype != torch.float32:
+        raise TypeError("weights must be float32")
+    if alpha.dtype != torch.float32:
+        raise TypeError("alpha must be float32")
+    if weights is None and beta is None:
+        raise ValueError("give adaptive weights or beta")
+    prob = make_problem(q, v, grid=grid, T=T, eps=eps)
+    if workspace is None:
+        nbytes = lisa_backward_workspace_size(prob)
+        if nbytes == 0:
+            raise LisaError(2, "lisa_backward_workspace_size")
+        workspace = torch.zeros(nbytes, dtype=torch.uint8, device=q.device)
+    out = {
+        "dq": torch.empty_like(q),
+        "dk": torch.empty_like(k),
+        "dv": torch.empty_like(v),
+        "dweights": None if weights is None else torch.empty_like(weights),
+        "dalpha": torch.empty_like(alpha),
+    }
+    st = _lib.lisa_backward(
+        ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(weights),
+        ctypes.c_float(0.0 if beta is None else beta), _ptr(alpha), _ptr(dy), _ptr(out["dq"]),
+        _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dweights"]), _ptr(out["dalpha"]), _ptr(workspace),
+        ctypes.c_size_t(workspace.numel()), _stream(stream, q.device),
+    )
+    if st != LISA_OK:
+        raise LisaError(st, "lisa_backward")
+    return out
 
 
 # Raw entry points for callers that marshal their own pointers (tests, bench).
