@@ -14,6 +14,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -27,7 +28,7 @@ ROTATE_BYTES = 600 << 20
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 KERNEL_SOURCES = [
     os.path.join(ROOT, "vision_transformer_token_amd", "csrc", f)
-    for f in ("lisa_flow.hip", "lisa_device.hpp", "lisa_kernels.hpp", "lisa_api.hip")
+    for f in ("lisa_flow.hip", "lisa_device.hpp", "lisa_kernels.hpp", "lisa_api.hip", "lisa_backward.hip")
 ]
 
 
@@ -110,7 +111,20 @@ def _short(name):
         return "flow_kernel<bf16>" if "BF16" in name else "flow_kernel<fp32>"
     if "copyBuffer" in name:
         return "copyBuffer"
+    m = re.search(r"(bwd_\w+)(<(unsigned short|float)>)?", name)
+    if m:
+        return m.group(1) + ({"unsigned short": "<bf16>", "float": "<fp32>"}.get(m.group(3), ""))
     return name[:60]
+
+
+def compulsory_bytes_backward(w):
+    """Q, K, V and dY read once, dQ, dK, dV written once, adaptive weights read
+    and their gradient written once."""
+    esize = 2 if w.dtype == "bf16" else 4
+    b = (2 * w.d_h + 2 * w.d_v) * esize + (2 * w.d_h + w.d_v) * esize
+    if w.mode == "adaptive":
+        b += 8 * w.T
+    return b
 
 
 def summarize_profiles(outdir, workload, commands):
@@ -176,6 +190,35 @@ def summarize_profiles(outdir, workload, commands):
         json.dump(c, f, indent=1)
 
 
+def summarize_backward(outdir, workload, command):
+    """profiles/ summary of a rocprofv3 kernel trace of bench.py --backward-only."""
+    from vision_transformer_token_amd import workloads
+
+    w = workloads.get(workload)
+    stats = _csv_rows(os.path.join(outdir, "prof_bwd", "bwd_kernel_stats.csv"))
+    calls = None
+    lines = [f"# rocprofv3 kernel trace of lisa_backward, workload {w.describe()}", "",
+             f"command: {command}", "",
+             "| kernel | calls | average ns | min ns | max ns | share |", "|---|---|---|---|---|---|"]
+    total_ns = 0.0
+    for r in stats:
+        name = _short(r["Name"])
+        if not (name.startswith("bwd_") or name.startswith("flow_kernel")):
+            continue
+        calls = calls or int(r["Calls"])
+        total_ns += float(r["AverageNs"])
+        lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} | "
+                     f"{float(r['Percentage']):.1f}% |")
+    bb = compulsory_bytes_backward(w)
+    lines += ["", f"sum of the kernels' averages per call: {total_ns / 1e3:.1f} us "
+                  f"(flow_kernel is the statistics launch the backward starts with)",
+              f"algorithmic bytes per call: {w.token_heads * bb / 1e6:.2f} MB ({bb} B per token-head); "
+              f"at 8 TB/s: {w.token_heads * bb / 8e12 * 1e6:.1f} us",
+              f"kernel source hash: {kernel_source_hash()}"]
+    with open(os.path.join(ROOT, "profiles", f"lisa_backward_{w.name}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,10 +229,14 @@ def main():
     ap.add_argument("--forward-only", action="store_true",
                     help="skip the reduce/apply reference timing (profiling runs: every "
                          "launch of the kernel is then a forward)")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only lisa_backward (for a profiler run) and print its line")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="instead of LiSA, run 20 plain device copies of this many MiB "
                          "(the known-size kernel that scales the FETCH_SIZE/WRITE_SIZE counters)")
+    ap.add_argument("--summarize-backward", metavar="DIR",
+                    help="write the profiles/ summary of a backward kernel trace under DIR and exit")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write profiles/ summaries from rocprofv3 output under DIR and exit")
     args = ap.parse_args()
@@ -208,6 +255,13 @@ def main():
                     "-o c{fetch|write} -- python3 bench.py --calibrate-copy-mib 256",
             "copy_mib": 256,
         })
+        return
+
+    if args.summarize_backward:
+        summarize_backward(args.summarize_backward, args.workload,
+                           "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_bwd -o bwd -- "
+                           "python3 bench.py --backward-only --steps 100 --warmup 10 --no-cpu-baseline --workload "
+                           + args.workload)
         return
 
     if args.gpus != 1:
@@ -265,6 +319,41 @@ def main():
         lisa.lisa_apply(d["q"], d["k"], d["v"], grid=(w.H, w.W), T=w.T, alpha=d["alpha"],
                         weights=d["weights"], beta=x["beta"], eps=w.eps, out=d["y"], workspace=ws,
                         stream=stream)
+
+    def backward_timing(steps, warmup):
+        """lisa_backward over the same input sets (dY drawn once per set)."""
+        bws = torch.zeros(lisa.lisa_backward_workspace_size(prob), dtype=torch.uint8, device=dev)
+        with torch.cuda.stream(stream):
+            dys = [torch.randn(d["v"].shape, device=dev, dtype=torch.float32).to(d["v"].dtype) for d in sets]
+            outs = [{"dq": torch.empty_like(d["q"]), "dk": torch.empty_like(d["k"]), "dv": torch.empty_like(d["v"]),
+                     "dweights": None if d["weights"] is None else torch.empty_like(d["weights"]),
+                     "dalpha": torch.empty_like(d["alpha"])} for d in sets]
+        torch.cuda.synchronize()
+
+        def bwd(j):
+            d = sets[j]
+            lisa.lisa_backward(d["q"], d["k"], d["v"], dys[j], grid=(w.H, w.W), T=w.T, alpha=d["alpha"],
+                               weights=d["weights"], beta=x["beta"], eps=w.eps, workspace=bws, out=outs[j],
+                               stream=stream)
+
+        for i in range(warmup):
+            bwd(i % nsets)
+        ba, bz = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ba.record(stream)
+        for i in range(steps):
+            bwd(i % nsets)
+        bz.record(stream)
+        torch.cuda.synchronize()
+        ms = ba.elapsed_time(bz) / steps
+        bb = compulsory_bytes_backward(w)
+        return {"ms_per_step": ms, "value": w.token_heads / (ms * 1e-3), "unit": "token-heads/s",
+                "steps": steps, "algorithmic_bytes_per_call": w.token_heads * bb,
+                "roofline_frac": w.token_heads * bb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+    if args.backward_only:
+        print(json.dumps({"workload": w.name, "backward": backward_timing(args.steps, args.warmup)}), flush=True)
+        return
 
     for i in range(args.warmup):
         forward(sets[i % nsets])
@@ -405,6 +494,8 @@ def main():
             "algorithmic_bytes_per_launch": th * bpt,
         }
         out["stages_ms"] = {"forward_kernel": kernel_ms, "reduce_only": stats_ms, "apply_only": apply_ms}
+    if not args.forward_only:
+        out["backward"] = backward_timing(min(args.steps, 500), min(args.warmup, 50))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kBT) void bwd_token_a(BwdArgs a) {
 #pragma unroll
   for (int k = 0; k < kMaxT; ++k) dyy[k] = 0.f;
   const int T1 = a.T - 1;
-  const int a0 = (t >> 3) * 4, c0 = (t & 7) * 8;  // this lane's 4 x 8 tile of dP_k
+  const int a0 = (t >> 4) * 4, c0 = (t & 15) * 4;  // this lane's 4 x 4 tile of dP_k
 #pragma unroll
   for (int k = 1; k < kMaxT; ++k) {
     if (k > T1) break;
@@ -258,27 +258,24 @@ __global__ __launch_bounds__(kBT) void bwd_token_a(BwdArgs a) {
     // dY_i . (Qt_i P_k) = Qt_i^T P_k dY_i.
     dyy[k] = bilinear(qt_sh + t * kR, Ps, dy);
     // This workgroup's share of dP_k.
-    float acc[4][8] = {};
-#pragma unroll 2
+    float acc[4][4] = {};
+#pragma unroll 4
     for (int tt = 0; tt < kBT; ++tt) {
       const float f = alpha * w_sh[tt * kMaxT + k];
-      float qa[4], dc[8];
+      float qa[4], dc[4];
 #pragma unroll
       for (int x = 0; x < 4; ++x) qa[x] = f * qt_sh[tt * kR + a0 + x];
 #pragma unroll
-      for (int y = 0; y < 8; ++y) dc[y] = dy_sh[tt * kR + c0 + y];
+      for (int y = 0; y < 4; ++y) dc[y] = dy_sh[tt * kR + c0 + y];
 #pragma unroll
       for (int x = 0; x < 4; ++x)
 #pragma unroll
-        for (int y = 0; y < 8; ++y) acc[x][y] += qa[x] * dc[y];
+        for (int y = 0; y < 4; ++y) acc[x][y] += qa[x] * dc[y];
     }
     float* dst = a.dp_part + (((size_t)b * a.nblk + blk) * T1 + (k - 1)) * kD * kD;
 #pragma unroll
     for (int x = 0; x < 4; ++x)
-#pragma unroll
-      for (int y = 0; y < 8; y += 4)
-        *reinterpret_cast<float4*>(dst + (a0 + x) * kD + c0 + y) =
-            make_float4(acc[x][y], acc[x][y + 1], acc[x][y + 2], acc[x][y + 3]);
+      *reinterpret_cast<float4*>(dst + (a0 + x) * kD + c0) = make_float4(acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
   }
   // Scalars of the token.
   float wy = 0.f;
@@ -307,7 +304,20 @@ __global__ __launch_bounds__(kBT) void bwd_token_a(BwdArgs a) {
   if (t == 0) a.da_part[(size_t)b * a.nblk + blk] = red[0];
 }
 
-// dP_k summed over the workgroups in order; then, from the last term down,
+// dP_k: the workgroups' partials summed in order, element by element, into
+// the first workgroup's slot.
+__global__ __launch_bounds__(kAdjThreads) void bwd_reduce_dp(BwdArgs a) {
+  const int b = blockIdx.y, T1 = a.T - 1;
+  const size_t per = (size_t)T1 * kD * kD;
+  const size_t e = (size_t)blockIdx.x * kAdjThreads + threadIdx.x;
+  if (T1 < 1 || e >= per) return;
+  float* base = a.dp_part + (size_t)b * a.nblk * per + e;
+  float v = 0.f;
+  for (int p = 0; p < a.nblk; ++p) v += base[(size_t)p * per];
+  base[0] = v;
+}
+
+// dP_k (summed by bwd_reduce_dp); then, from the last term down,
 // dM += dP_k P_(k-1)^T and dP_(k-1) += M^T dP_k; dKV = dP_1.  One workgroup
 // per slice; also the slice's dalpha.
 __global__ __launch_bounds__(kAdjThreads) void bwd_adjoint(BwdArgs a) {
@@ -329,11 +339,7 @@ __global__ __launch_bounds__(kAdjThreads) void bwd_adjoint(BwdArgs a) {
     return;
   }
   const size_t per = (size_t)T1 * kD * kD;
-  for (size_t e = t; e < per; e += kAdjThreads) {
-    float v = 0.f;
-    for (int p = 0; p < a.nblk; ++p) v += a.dp_part[((size_t)b * a.nblk + p) * per + e];
-    dP[e] = v;
-  }
+  for (size_t e = t; e < per; e += kAdjThreads) dP[e] = a.dp_part[(size_t)b * a.nblk * per + e];
   load_mat(Ms, a.fin_m + (size_t)b * kD * kD);
   float dM[kX] = {};
   for (int k = T1; k >= 2; --k) {
@@ -615,6 +621,9 @@ hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
   const dim3 tok(a.nblk, a.BH);
   if (a.T >= 2) hipLaunchKernelGGL(bwd_powers, dim3(a.BH), dim3(kAdjThreads), 0, s, a);
   hipLaunchKernelGGL(bwd_token_a<S>, tok, dim3(kBT), lds_a, s, a);
+  if (a.T >= 2)
+    hipLaunchKernelGGL(bwd_reduce_dp, dim3((T1 * kD * kD + kAdjThreads - 1) / kAdjThreads, a.BH),
+                       dim3(kAdjThreads), 0, s, a);
   hipLaunchKernelGGL(bwd_adjoint, dim3(a.BH), dim3(kAdjThreads), lds_adj, s, a);
   hipLaunchKernelGGL(bwd_token_b<S>, tok, dim3(kBT), 0, s, a);
   hipLaunchKernelGGL(bwd_token_q<S>, tok, dim3(kBT), 0, s, a);

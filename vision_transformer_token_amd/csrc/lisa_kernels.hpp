@@ -104,7 +104,7 @@ hipError_t launch_flow(int dtype, const FlowArgs& a, int grid, hipStream_t s);
 // Backward pass (lisa_backward): token passes take kBwdTokens tokens per
 // workgroup, one per lane; the slice statistics come from a statistics launch
 // (fin_s, fin_kv, fin_m of FlowArgs) that ran before on the same stream.
-constexpr int kBwdTokens = 128;
+constexpr int kBwdTokens = 256;
 
 struct BwdArgs {
   const void* Q;
@@ -126,7 +126,7 @@ struct BwdArgs {
   const float* fin_m;     // [BH][64*64]
   float* pk;              // [BH][T-1][64*64]  P_k = M^(k-1) phi(K)^T V, k = 1..T-1
   float4* tok;            // [BH][n]  per token: local max, local sum, dL_i . L_i, then (a_i -> dz_i)
-  float* dp_part;         // [BH][nblk][T-1][64*64]  per-workgroup partials of dP_k
+  float* dp_part;         // [BH][nblk][T-1][64*64]  per-workgroup partials of dP_k (block 0: their sum)
   float* da_part;         // [BH][nblk]  partials of dalpha
   float* da_slice;        // [BH]
   float* dmkv;            // [BH][2][64*64]  dM, dKV

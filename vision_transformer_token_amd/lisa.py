@@ -211,13 +211,14 @@ def lisa_backward_workspace_size(problem):
 
 
 def lisa_backward(q, k, v, dy, *, grid, T, alpha, weights=None, beta=None, eps=1e-6, workspace=None,
-                  stream=None):
+                  out=None, stream=None):
     """Gradients of lisa_forward for the output gradient ``dy``; see include/lisa.h.
 
     Returns a dict with "dq", "dk", "dv" (dtype of q), "dweights" (fp32
     [B, heads, n, T], None with geometric weights) and "dalpha" (fp32
     [heads]).  ``workspace`` (zero-filled, lisa_backward_workspace_size
-    bytes) is allocated when not given.
+    bytes) is allocated when not given; ``out`` (a dict like the result)
+    supplies the output tensors.
     """
     _check_tensors(q=q, k=k, v=v, dy=dy, alpha=alpha, weights=weights, workspace=workspace)
     if weights is not None and weights.dtype != torch.float32:
@@ -232,13 +233,15 @@ def lisa_backward(q, k, v, dy, *, grid, T, alpha, weights=None, beta=None, eps=1
         if nbytes == 0:
             raise LisaError(2, "lisa_backward_workspace_size")
         workspace = torch.zeros(nbytes, dtype=torch.uint8, device=q.device)
-    out = {
-        "dq": torch.empty_like(q),
-        "dk": torch.empty_like(k),
-        "dv": torch.empty_like(v),
-        "dweights": None if weights is None else torch.empty_like(weights),
-        "dalpha": torch.empty_like(alpha),
-    }
+    if out is None:
+        out = {
+            "dq": torch.empty_like(q),
+            "dk": torch.empty_like(k),
+            "dv": torch.empty_like(v),
+            "dweights": None if weights is None else torch.empty_like(weights),
+            "dalpha": torch.empty_like(alpha),
+        }
+    _check_tensors(**{k_: t for k_, t in out.items()})
     st = _lib.lisa_backward(
         ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(weights),
         ctypes.c_float(0.0 if beta is None else beta), _ptr(alpha), _ptr(dy), _ptr(out["dq"]),
