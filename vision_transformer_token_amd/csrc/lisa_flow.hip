@@ -125,8 +125,11 @@ __device__ __forceinline__ Pos first_pos(const FlowArgs& a, const Rank& rk) {
 // launch returns at once, so the launch always finishes.
 __device__ void wait_for(const unsigned* c, unsigned target, unsigned* err) {
   unsigned spins = 0;
+  // About 0.27 us between polls: every poll is a device-wide load of the
+  // line the arrivals update, and with hundreds of workgroups polling one
+  // slice (one long sequence) denser polling slows the arrivals themselves.
   while (get(c) < target) {
-    __builtin_amdgcn_s_sleep(2);
+    __builtin_amdgcn_s_sleep(10);
     if ((++spins & 255u) == 0 && get(err)) break;
     if (spins > (1u << 21)) {
       put(err, 1u);
