@@ -138,11 +138,22 @@ __device__ void wait_for(const unsigned* c, unsigned target, unsigned* err) {
   }
 }
 
-// Arrival of one consumer wave (lane 0, after its stores completed): a rank
-// counts kRoleWaves arrivals per phase.  Nothing waits for the atomic itself;
-// counters only grow during a launch and the last workgroup clears them.
+// A rank's arrival for one phase.  Each consumer wave, after its own stores
+// have completed, counts itself in LDS (`waves`); the last of the kRoleWaves
+// waves bumps the slice counter once, so a slice's counter reaches G.  That
+// wave's atomic follows every other wave's completed stores (their LDS
+// increments came first).  Stage barriers separate the phases, so the last
+// wave's reset precedes the next phase's increments.  Nothing waits for the
+// global atomic; counters only grow during a launch and the last workgroup
+// clears them.
 __device__ __forceinline__ void arrive(unsigned* c) {
   (void)__hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void arrive_rank(unsigned* c, int* waves) {
+  if ((threadIdx.x & 63) == 0 && atomicAdd(waves, 1) == kRoleWaves - 1) {
+    *waves = 0;
+    arrive(c);
+  }
 }
 
 __device__ __forceinline__ void tile_origin(const FlowArgs& a, int t, int& r0, int& c0) {
@@ -332,7 +343,7 @@ __device__ void prepare(const FlowArgs& a, const Rank& rk, Pos p, unsigned char*
   const int lane = threadIdx.x & 63;
   const int b = slice_of(a, rk, p.r, p.z);
   const unsigned* cnt = a.slice_cnt + (size_t)b * kCntWords;
-  const unsigned full = kRoleWaves * a.G;
+  const unsigned full = a.G;
   auto dependency = [&](int counter) {
     const int tag = b * 4 + p.ph;
     if (pw == 0) {
@@ -431,7 +442,8 @@ __device__ __forceinline__ void sweep_chunk(const unsigned char* buf, int nv, in
 // The KV or M phase of slice b: the rank's chunks, one stage each, then its
 // partial (coherent stores) and the wave's arrival.
 template <class Tr, bool kIsM>
-__device__ int consume_sweep(const FlowArgs& a, const Rank& rk, int b, unsigned char* smem, int bsel, int cw) {
+__device__ int consume_sweep(const FlowArgs& a, const Rank& rk, int b, unsigned char* smem, int bsel, int cw,
+                             int* waves) {
   using L = LdsOf<Tr>;
   const int lane = threadIdx.x & 63;
   const int m = lane & 31, h = lane >> 5, mb = cw >> 1, nb = cw & 1;
@@ -454,7 +466,7 @@ __device__ int consume_sweep(const FlowArgs& a, const Rank& rk, int b, unsigned 
     for (int i = 0; i < 16; ++i) put(ps + 32 * mb + 8 * (i >> 2) + 4 * h + (i & 3), acc_s[i]);
   }
   wait_all();
-  if (lane == 0) arrive(a.slice_cnt + (size_t)b * kCntWords + (kIsM ? kCntM : kCntKV));
+  arrive_rank(a.slice_cnt + (size_t)b * kCntWords + (kIsM ? kCntM : kCntKV), waves);
   lds_barrier();
   return bsel ^ 1;
 }
@@ -482,7 +494,8 @@ __device__ __forceinline__ void store_stat(float* fin, void* frag, int e, float 
 // TPE = 256 / E threads share an element (partials p = q, q + TPE, ...) and
 // combine by a fixed xor tree.
 template <class Tr>
-__device__ void consume_combine(const FlowArgs& a, const Rank& rk, int b, const unsigned char* buf, int ct) {
+__device__ void consume_combine(const FlowArgs& a, const Rank& rk, int b, const unsigned char* buf, int ct,
+                                int* waves) {
   using S = typename Tr::S;
   const float* stg = reinterpret_cast<const float*>(buf);  // [G][E]
   auto mat_base = [&](int f0, float*& fin, void*& frag) {
@@ -512,7 +525,7 @@ __device__ void consume_combine(const FlowArgs& a, const Rank& rk, int b, const 
     if (q == 0) store_stat<Tr>(fin, frag, (rk.e0 + e) & (kD * kD - 1), v);
   }
   wait_all();
-  if ((threadIdx.x & 63) == 0) arrive(a.slice_cnt + (size_t)b * kCntWords + kCntC);
+  arrive_rank(a.slice_cnt + (size_t)b * kCntWords + kCntC, waves);
   lds_barrier();
 }
 
@@ -865,6 +878,7 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
   __shared__ float geo_sh[kMaxT];        // geometric walk weights
   __shared__ int dep_ok;                 // tag of the stage whose dependency producer wave 0 has seen met
   __shared__ int last;                   // this workgroup's ticket, later: it finished last
+  __shared__ int arrivals;               // consumer waves that have arrived in the current phase
   const int tid = threadIdx.x;
   const int wave = wave_id();
   const bool producer = wave < kRoleWaves;
@@ -874,6 +888,7 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
   if (tid < kMaxT) geo_sh[tid] = a.geo[tid];
   if (tid == 0) {
     dep_ok = -1;
+    arrivals = 0;
     last = (int)bump(a.tickets + (a.xcd_groups ? blockIdx.x % kXcds : 0));
   }
   __syncthreads();
@@ -901,12 +916,15 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
       for (int r = 0; round_slices(a, rk, r) > 0; ++r) {
         const int nz = round_slices(a, rk, r);
         if (phase_len(a, rk, kPKV) > 0)
-          for (int z = 0; z < nz; ++z) bsel = consume_sweep<Tr, false>(a, rk, slice_of(a, rk, r, z), smem, bsel, rw);
+          for (int z = 0; z < nz; ++z)
+            bsel = consume_sweep<Tr, false>(a, rk, slice_of(a, rk, r, z), smem, bsel, rw, &arrivals);
         if (phase_len(a, rk, kPM) > 0)
-          for (int z = 0; z < nz; ++z) bsel = consume_sweep<Tr, true>(a, rk, slice_of(a, rk, r, z), smem, bsel, rw);
+          for (int z = 0; z < nz; ++z)
+            bsel = consume_sweep<Tr, true>(a, rk, slice_of(a, rk, r, z), smem, bsel, rw, &arrivals);
         if (phase_len(a, rk, kPC) > 0)
           for (int z = 0; z < nz; ++z) {
-            consume_combine<Tr>(a, rk, slice_of(a, rk, r, z), smem + bsel * L::kStage, tid - kRoleWaves * 64);
+            consume_combine<Tr>(a, rk, slice_of(a, rk, r, z), smem + bsel * L::kStage, tid - kRoleWaves * 64,
+                                &arrivals);
             bsel ^= 1;
           }
         if (phase_len(a, rk, kPOut) > 0)

@@ -67,7 +67,7 @@ __host__ __device__ inline TileLayout tile_layout(int TR, int TC, int T, int es)
 //       fixed-order sum of the G partials, written as fp32 and as MFMA
 //       fragments (rank 0 also writes s);
 //   OUT: after all G ranks' C parts: output tiles [g T / G, (g + 1) T / G).
-// Each phase's completion is counted per slice (kRoleWaves arrivals per rank).
+// Each phase's completion is counted per slice (one arrival per rank).
 struct FlowArgs {
   const void* Q;
   const void* K;
