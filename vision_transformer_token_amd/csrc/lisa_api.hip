@@ -166,7 +166,7 @@ lisa_status make_plan(const lisa_problem* p, Plan& pl) {
   // a workspace reused by problems of other shapes never has another
   // problem's data written over a counter (each call leaves them at zero).
   pl.done_cnt = take(32 * sizeof(unsigned));
-  pl.slice_cnt = take((size_t)kMaxSlices * lisa::kCntWords * sizeof(unsigned));
+  pl.slice_cnt = take((size_t)kMaxSlices * lisa::kCntStride * sizeof(unsigned));
   pl.part_s = take(BH * G * vec);
   pl.part_kv = take(BH * G * mat);
   pl.part_m = take(BH * G * mat);

@@ -342,7 +342,7 @@ __device__ void prepare(const FlowArgs& a, const Rank& rk, Pos p, unsigned char*
   using L = LdsOf<Tr>;
   const int lane = threadIdx.x & 63;
   const int b = slice_of(a, rk, p.r, p.z);
-  const unsigned* cnt = a.slice_cnt + (size_t)b * kCntWords;
+  const unsigned* cnt = a.slice_cnt + (size_t)b * kCntStride;
   const unsigned full = a.G;
   auto dependency = [&](int counter) {
     const int tag = b * 4 + p.ph;
@@ -466,7 +466,7 @@ __device__ int consume_sweep(const FlowArgs& a, const Rank& rk, int b, unsigned 
     for (int i = 0; i < 16; ++i) put(ps + 32 * mb + 8 * (i >> 2) + 4 * h + (i & 3), acc_s[i]);
   }
   wait_all();
-  arrive_rank(a.slice_cnt + (size_t)b * kCntWords + (kIsM ? kCntM : kCntKV), waves);
+  arrive_rank(a.slice_cnt + (size_t)b * kCntStride + (kIsM ? kCntM : kCntKV), waves);
   lds_barrier();
   return bsel ^ 1;
 }
@@ -525,7 +525,7 @@ __device__ void consume_combine(const FlowArgs& a, const Rank& rk, int b, const 
     if (q == 0) store_stat<Tr>(fin, frag, (rk.e0 + e) & (kD * kD - 1), v);
   }
   wait_all();
-  arrive_rank(a.slice_cnt + (size_t)b * kCntWords + kCntC, waves);
+  arrive_rank(a.slice_cnt + (size_t)b * kCntStride + kCntC, waves);
   lds_barrier();
 }
 
@@ -942,7 +942,8 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
   if (tid == 0) last = bump(a.done_cnt) == gridDim.x - 1;
   __syncthreads();
   if (last) {
-    for (int i = tid; i < a.BH * kCntWords; i += kThreads) put(a.slice_cnt + i, 0u);
+    for (int i = tid; i < a.BH * kCntWords; i += kThreads)
+      put(a.slice_cnt + (size_t)(i / kCntWords) * kCntStride + i % kCntWords, 0u);
     if (tid < kXcds) put(a.tickets + tid, 0u);
     wait_all();
     __syncthreads();

@@ -15,6 +15,7 @@ constexpr int kXcds = 8;        // workgroup w runs on XCD w % 8
 constexpr int kMaxRanks = 256;  // G <= 256: each rank combines >= 32 elements
 constexpr int kMaxTileTokens = 256;
 constexpr int kCntWords = 4;    // arrival counters per (batch, head) slice: KV, M, C (+ pad)
+constexpr int kCntStride = 32;  // words between slices: each slice's counters on their own 128-byte line
 
 // LDS of one workgroup, per element size ES: two staging buffers of kStage
 // bytes that the DMA of the next stage and the compute of the current one
@@ -92,7 +93,7 @@ struct FlowArgs {
   float* fin_m;           // [BH][64*64]
   void* frag_kv;          // [BH][64*64] elements of the input dtype
   void* frag_m;           // [BH][64*64]
-  unsigned* slice_cnt;    // [BH][kCntWords]
+  unsigned* slice_cnt;    // [BH][kCntStride], words 0..kCntWords-1 used
   unsigned* done_cnt;     // finished workgroups
   unsigned* tickets;      // [kXcds] rank tickets
   unsigned* err;          // error word (a dependency wait timed out)
