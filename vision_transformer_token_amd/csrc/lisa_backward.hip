@@ -21,11 +21,12 @@
 // The local branch's softmax adjoint uses, per centre token i, the window's
 // logit maximum m_i and sum Z_i and c_i = dL_i . L_i, which pass A keeps.
 //
-// Layout: one lane per token (kBwdTokens per workgroup) for the token
-// passes; the slice's 64 x 64 matrices sit in LDS and every lane reads the
-// same element at once (broadcast).  Vectors that are indexed at run time
-// live in a per-lane LDS row; the rest stay in registers.  Everything is
-// fp32; outputs dQ, dK, dV are written once in the input dtype.
+// Layout: the token passes take kBwdTokens tokens per workgroup, four lanes
+// per token (lane quarter qd owns features 16 qd .. 16 qd + 15); dot products
+// are reduced over the lane quad with DPP.  The slice's 64 x 64 matrices sit
+// in LDS, read as broadcasts.  Vectors that are indexed at run time live in a
+// per-token LDS row shared by the quad; the rest stay in registers.
+// Everything is fp32; outputs dQ, dK, dV are written once in the input dtype.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -40,48 +41,56 @@ constexpr int kR = kD + 1;           // padded LDS row (floats)
 constexpr float kRs = 0.125f;        // 1 / sqrt(d_h), d_h = 64
 constexpr int kAdjThreads = 256;
 
+constexpr int kQ = 4;                // lanes per token
+constexpr int kF = kD / kQ;          // features per lane
+constexpr int kTT = kBT * kQ;        // threads of a token-pass workgroup
+
+// This lane's 16 features of a row.
 template <class S>
-__device__ __forceinline__ void load_row(const S* p, float (&x)[kD]) {
+__device__ __forceinline__ void load16(const S* row, int f0, float (&x)[kF]) {
 #pragma unroll
-  for (int e = 0; e < kD; e += 4) load4(p + e, &x[e]);
+  for (int e = 0; e < kF; e += 4) load4(row + f0 + e, &x[e]);
 }
 template <class S>
-__device__ __forceinline__ void store_row(S* p, const float (&x)[kD]) {
+__device__ __forceinline__ void store16(S* row, int f0, const float (&x)[kF]) {
 #pragma unroll
-  for (int e = 0; e < kD; e += 4) store4(p + e, &x[e]);
+  for (int e = 0; e < kF; e += 4) store4(row + f0 + e, &x[e]);
 }
+// Sum over the lane quad of a token (every lane of the quad gets it).
+__device__ __forceinline__ float quad_sum(float x) { return dpp_add(dpp_add(x, 0xB1), 0x4E); }
+// x . row over all 64 features (quad-reduced).
 template <class S>
-__device__ __forceinline__ float dot_row(const S* p, const float (&x)[kD]) {
+__device__ __forceinline__ float dot64(const S* row, int f0, const float (&x)[kF]) {
+  float y[kF];
+  load16(row, f0, y);
   float acc = 0.f;
 #pragma unroll
-  for (int e = 0; e < kD; e += 4) {
-    float y[4];
-    load4(p + e, y);
-    acc += x[e] * y[0] + x[e + 1] * y[1] + x[e + 2] * y[2] + x[e + 3] * y[3];
-  }
-  return acc;
+  for (int e = 0; e < kF; ++e) acc += x[e] * y[e];
+  return quad_sum(acc);
 }
 template <class S>
-__device__ __forceinline__ void axpy_row(float f, const S* p, float (&x)[kD]) {
+__device__ __forceinline__ void axpy16(float f, const S* row, int f0, float (&x)[kF]) {
+  float y[kF];
+  load16(row, f0, y);
 #pragma unroll
-  for (int e = 0; e < kD; e += 4) {
-    float y[4];
-    load4(p + e, y);
-    x[e] += f * y[0];
-    x[e + 1] += f * y[1];
-    x[e + 2] += f * y[2];
-    x[e + 3] += f * y[3];
-  }
+  for (int e = 0; e < kF; ++e) x[e] += f * y[e];
+}
+// The quad's rows in LDS are written and read by lanes of one wave: order
+// the LDS accesses (the compiler may not move them across this either).
+__device__ __forceinline__ void quad_lds_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  asm volatile("" ::: "memory");
 }
 
-// y[c] += sum_a xs[a] mat[a][c]  (xs: the lane's LDS row; mat: 64 x 64 in LDS)
-__device__ __forceinline__ void row_times_mat(const float* xs, const float* mat, float (&y)[kD]) {
-#pragma unroll 1
+// y (this lane's 16 columns) += sum_a xs[a] mat[a][f0 + c]; xs: the token's LDS row.
+__device__ __forceinline__ void row_times_mat(const float* xs, const float* mat, int f0, float (&y)[kF]) {
+#pragma unroll 2
   for (int a = 0; a < kD; ++a) {
     const float xa = xs[a];
-    const float4* m = reinterpret_cast<const float4*>(mat + a * kD);
+    const float4* m = reinterpret_cast<const float4*>(mat + a * kD + f0);
 #pragma unroll
-    for (int c = 0; c < kD / 4; ++c) {
+    for (int c = 0; c < kF / 4; ++c) {
       const float4 v = m[c];
       y[4 * c] += xa * v.x;
       y[4 * c + 1] += xa * v.y;
@@ -90,36 +99,42 @@ __device__ __forceinline__ void row_times_mat(const float* xs, const float* mat,
     }
   }
 }
-// ys[a] = f * sum_c mat[a][c] x[c]  (+= when accumulate)
-__device__ __forceinline__ void mat_times_vec(const float* mat, const float (&x)[kD], float f, float* ys,
-                                              bool accumulate) {
+// y (this lane's 16 rows a = f0 + i) += f * sum_c mat[a][c] x[c], x spread
+// over the quad (16 columns per lane).
+__device__ __forceinline__ void mat_times_vec(const float* mat, const float (&x)[kF], float f, int qd, int f0,
+                                              float (&y)[kF]) {
 #pragma unroll 1
-  for (int a = 0; a < kD; ++a) {
-    const float4* m = reinterpret_cast<const float4*>(mat + a * kD);
-    float acc = 0.f;
+  for (int ab = 0; ab < kQ; ++ab) {
 #pragma unroll
-    for (int c = 0; c < kD / 4; ++c) {
-      const float4 v = m[c];
-      acc += v.x * x[4 * c] + v.y * x[4 * c + 1] + v.z * x[4 * c + 2] + v.w * x[4 * c + 3];
+    for (int ai = 0; ai < kF; ++ai) {
+      const float4* m = reinterpret_cast<const float4*>(mat + (ab * kF + ai) * kD + f0);
+      float acc = 0.f;
+#pragma unroll
+      for (int c = 0; c < kF / 4; ++c) {
+        const float4 v = m[c];
+        acc += v.x * x[4 * c] + v.y * x[4 * c + 1] + v.z * x[4 * c + 2] + v.w * x[4 * c + 3];
+      }
+      acc = quad_sum(acc);
+      if (ab == qd) y[ai] += f * acc;
     }
-    ys[a] = accumulate ? ys[a] + f * acc : f * acc;
   }
 }
-// sum_a xs[a] sum_c mat[a][c] x[c]
-__device__ __forceinline__ float bilinear(const float* xs, const float* mat, const float (&x)[kD]) {
+// sum_a xs[a] sum_c mat[a][c] x[c] (quad-reduced); xs: the token's LDS row,
+// x spread over the quad.
+__device__ __forceinline__ float bilinear(const float* xs, const float* mat, int f0, const float (&x)[kF]) {
   float tot = 0.f;
-#pragma unroll 1
+#pragma unroll 2
   for (int a = 0; a < kD; ++a) {
-    const float4* m = reinterpret_cast<const float4*>(mat + a * kD);
+    const float4* m = reinterpret_cast<const float4*>(mat + a * kD + f0);
     float acc = 0.f;
 #pragma unroll
-    for (int c = 0; c < kD / 4; ++c) {
+    for (int c = 0; c < kF / 4; ++c) {
       const float4 v = m[c];
       acc += v.x * x[4 * c] + v.y * x[4 * c + 1] + v.z * x[4 * c + 2] + v.w * x[4 * c + 3];
     }
     tot += xs[a] * acc;
   }
-  return tot;
+  return quad_sum(tot);
 }
 
 // Whole workgroup: copy a 64 x 64 fp32 matrix into LDS.
@@ -178,7 +193,7 @@ __global__ __launch_bounds__(kAdjThreads) void bwd_powers(BwdArgs a) {
 // the weight gradients and dalpha's share; per workgroup the partial sums of
 // dP_k = sum_i w_k(i) alpha Qt_i^T dY_i.
 template <class S>
-__global__ __launch_bounds__(kBT) void bwd_token_a(BwdArgs a) {
+__global__ __launch_bounds__(kTT) void bwd_token_a(BwdArgs a) {
   extern __shared__ __align__(16) float sm[];
   float* Ps = sm;                        // kD * kD: P_k
   float* s_sh = Ps + kD * kD;            // kD
@@ -187,7 +202,8 @@ __global__ __launch_bounds__(kBT) void bwd_token_a(BwdArgs a) {
   float* w_sh = dy_sh + kBT * kR;        // kBT x kMaxT weights
   float* red = w_sh + kBT * kMaxT;       // kBT
   const int b = blockIdx.y, t = threadIdx.x, blk = blockIdx.x;
-  const int i = blk * kBT + t;
+  const int tk = t / kQ, qd = t % kQ, f0 = qd * kF;
+  const int i = blk * kBT + tk;
   const bool on = i < a.n;
   const float alpha = a.alpha[b % a.heads];
   const size_t base = (size_t)b * a.n;
@@ -196,13 +212,14 @@ __global__ __launch_bounds__(kBT) void bwd_token_a(BwdArgs a) {
   const S* Vb = static_cast<const S*>(a.V) + base * kD;
   const S* dYb = static_cast<const S*>(a.dY) + base * kD;
   if (t < kD) s_sh[t] = a.fin_s[(size_t)b * kD + t];
-  for (int k = 0; k < kMaxT; ++k) w_sh[t * kMaxT + k] = (on && k < a.T) ? wgt(a, base + i, k) : 0.f;
+  if (qd == 0)
+    for (int k = 0; k < kMaxT; ++k) w_sh[tk * kMaxT + k] = (on && k < a.T) ? wgt(a, base + i, k) : 0.f;
 
-  float q[kD], dy[kD];
+  float q[kF], dy[kF];
   float m = 0.f, Z = 1.f, dyL = 0.f, dyv = 0.f;
   if (on) {
-    load_row(Qb + (size_t)i * kD, q);
-    load_row(dYb + (size_t)i * kD, dy);
+    load16(Qb + (size_t)i * kD, f0, q);
+    load16(dYb + (size_t)i * kD, f0, dy);
     // Local branch at token i: window logits, their max and sum, dY . L_i.
     const int row = i / a.W, col = i % a.W;
     float z[9];
@@ -210,7 +227,7 @@ __global__ __launch_bounds__(kBT) void bwd_token_a(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < 9; ++j) {
       const int c = window_cell(a, row, col, j);
-      z[j] = c >= 0 ? dot_row(Kb + (size_t)c * kD, q) * kRs : -INFINITY;
+      z[j] = c >= 0 ? dot64(Kb + (size_t)c * kD, f0, q) * kRs : -INFINITY;
       m = fmaxf(m, z[j]);
     }
     Z = 0.f;
@@ -220,35 +237,35 @@ __global__ __launch_bounds__(kBT) void bwd_token_a(BwdArgs a) {
       if (c >= 0) {
         const float e = __expf(z[j] - m);
         Z += e;
-        dyL += e * dot_row(Vb + (size_t)c * kD, dy);
+        dyL += e * dot64(Vb + (size_t)c * kD, f0, dy);
       }
     }
     dyL /= Z;
-    dyv = dot_row(Vb + (size_t)i * kD, dy);
+    dyv = dot64(Vb + (size_t)i * kD, f0, dy);
   } else {
 #pragma unroll
-    for (int e = 0; e < kD; ++e) q[e] = dy[e] = 0.f;
+    for (int e = 0; e < kF; ++e) q[e] = dy[e] = 0.f;
   }
   __syncthreads();  // s_sh, w_sh
   // Qt_i = r_i phi(Q_i).
   float den = 0.f;
 #pragma unroll
-  for (int e = 0; e < kD; ++e) {
+  for (int e = 0; e < kF; ++e) {
     q[e] = fmaxf(q[e], 0.f);
-    den += q[e] * s_sh[e];
+    den += q[e] * s_sh[f0 + e];
   }
-  const float r = 1.f / (den + a.eps);
+  const float r = 1.f / (quad_sum(den) + a.eps);
 #pragma unroll
-  for (int e = 0; e < kD; ++e) {
+  for (int e = 0; e < kF; ++e) {
     q[e] *= r;
-    qt_sh[t * kR + e] = q[e];
-    dy_sh[t * kR + e] = dy[e];
+    qt_sh[tk * kR + f0 + e] = q[e];
+    dy_sh[tk * kR + f0 + e] = dy[e];
   }
   float dyy[kMaxT];
 #pragma unroll
   for (int k = 0; k < kMaxT; ++k) dyy[k] = 0.f;
   const int T1 = a.T - 1;
-  const int a0 = (t >> 4) * 4, c0 = (t & 15) * 4;  // this lane's 4 x 4 tile of dP_k
+  const int ra = t >> 4, c0 = (t & 15) * 4;  // this lane's 1 x 4 piece of dP_k (wave: 4 rows)
 #pragma unroll
   for (int k = 1; k < kMaxT; ++k) {
     if (k > T1) break;
@@ -256,34 +273,25 @@ __global__ __launch_bounds__(kBT) void bwd_token_a(BwdArgs a) {
     load_mat(Ps, a.pk + ((size_t)b * T1 + (k - 1)) * kD * kD);
     __syncthreads();
     // dY_i . (Qt_i P_k) = Qt_i^T P_k dY_i.
-    dyy[k] = bilinear(qt_sh + t * kR, Ps, dy);
+    dyy[k] = bilinear(qt_sh + tk * kR, Ps, f0, dy);
     // This workgroup's share of dP_k.
-    float acc[4][4] = {};
+    float acc[4] = {};
 #pragma unroll 4
     for (int tt = 0; tt < kBT; ++tt) {
-      const float f = alpha * w_sh[tt * kMaxT + k];
-      float qa[4], dc[4];
+      const float fq = alpha * w_sh[tt * kMaxT + k] * qt_sh[tt * kR + ra];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) qa[x] = f * qt_sh[tt * kR + a0 + x];
-#pragma unroll
-      for (int y = 0; y < 4; ++y) dc[y] = dy_sh[tt * kR + c0 + y];
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] += qa[x] * dc[y];
+      for (int y = 0; y < 4; ++y) acc[y] += fq * dy_sh[tt * kR + c0 + y];
     }
     float* dst = a.dp_part + (((size_t)b * a.nblk + blk) * T1 + (k - 1)) * kD * kD;
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-      *reinterpret_cast<float4*>(dst + (a0 + x) * kD + c0) = make_float4(acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
+    *reinterpret_cast<float4*>(dst + ra * kD + c0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
   }
-  // Scalars of the token.
+  // Scalars of the token (every lane of the quad holds them).
   float wy = 0.f;
 #pragma unroll
   for (int k = 1; k < kMaxT; ++k)
-    if (k <= T1) wy += w_sh[t * kMaxT + k] * dyy[k];
-  const float dyG = w_sh[t * kMaxT] * dyv + wy;
-  if (on) {
+    if (k <= T1) wy += w_sh[tk * kMaxT + k] * dyy[k];
+  const float dyG = w_sh[tk * kMaxT] * dyv + wy;
+  if (on && qd == 0) {
     // a_i = (sum_k w_k P_k dG_i) . phi(Q_i) = alpha / r_i * sum_k w_k dY_i . (Qt_i P_k)
     a.tok[base + i] = make_float4(m, Z, (1.f - alpha) * dyL, alpha / r * wy);
     if (a.dweights) {
@@ -295,7 +303,7 @@ __global__ __launch_bounds__(kBT) void bwd_token_a(BwdArgs a) {
     }
   }
   // dalpha's share: sum_i dY_i . (G_i - L_i), fixed-order tree.
-  red[t] = on ? dyG - dyL : 0.f;
+  if (qd == 0) red[tk] = on ? dyG - dyL : 0.f;
   __syncthreads();
   for (int o = kBT / 2; o > 0; o >>= 1) {
     if (t < o) red[t] += red[t + o];
@@ -377,47 +385,61 @@ __global__ __launch_bounds__(kAdjThreads) void bwd_adjoint(BwdArgs a) {
 // Pass B: dz_i = -r_i^2 (a_i + phi(K_i)^T dM phi(Q_i)) (kept in tok[i].w) and
 // the workgroup's share of ds = sum_i dz_i phi(Q_i).
 template <class S>
-__global__ __launch_bounds__(kBT) void bwd_token_b(BwdArgs a) {
+__global__ __launch_bounds__(kTT) void bwd_token_b(BwdArgs a) {
+  constexpr int kG = kTT / kD;  // partial sums per feature in the ds reduction
   __shared__ __align__(16) float dMs[kD * kD];
   __shared__ float s_sh[kD];
   __shared__ float rows[kBT * kR];
+  __shared__ float red[kG * kD];
   const int b = blockIdx.y, t = threadIdx.x, blk = blockIdx.x;
-  const int i = blk * kBT + t;
+  const int tk = t / kQ, qd = t % kQ, f0 = qd * kF;
+  const int i = blk * kBT + tk;
   const bool on = i < a.n;
   const size_t base = (size_t)b * a.n;
   load_mat(dMs, a.dmkv + (size_t)b * 2 * kD * kD);
   if (t < kD) s_sh[t] = a.fin_s[(size_t)b * kD + t];
-  float u[kD], kp[kD];
+  float u[kF], kp[kF];
   if (on) {
-    load_row(static_cast<const S*>(a.Q) + (base + i) * kD, u);
-    load_row(static_cast<const S*>(a.K) + (base + i) * kD, kp);
+    load16(static_cast<const S*>(a.Q) + (base + i) * kD, f0, u);
+    load16(static_cast<const S*>(a.K) + (base + i) * kD, f0, kp);
   } else {
 #pragma unroll
-    for (int e = 0; e < kD; ++e) u[e] = kp[e] = 0.f;
+    for (int e = 0; e < kF; ++e) u[e] = kp[e] = 0.f;
   }
   __syncthreads();
   float den = 0.f;
 #pragma unroll
-  for (int e = 0; e < kD; ++e) {
+  for (int e = 0; e < kF; ++e) {
     u[e] = fmaxf(u[e], 0.f);
-    den += u[e] * s_sh[e];
-    rows[t * kR + e] = fmaxf(kp[e], 0.f);
+    den += u[e] * s_sh[f0 + e];
+    rows[tk * kR + f0 + e] = fmaxf(kp[e], 0.f);
   }
-  const float r = 1.f / (den + a.eps);
+  const float r = 1.f / (quad_sum(den) + a.eps);
+  quad_lds_sync();
+  const float bil = bilinear(rows + tk * kR, dMs, f0, u);
   float dz = 0.f;
   if (on) {
-    float4* tk = a.tok + base + i;
-    const float4 v = *tk;
-    dz = -r * r * (v.w + bilinear(rows + t * kR, dMs, u));
-    *tk = make_float4(v.x, v.y, v.z, dz);
+    float4* tp = a.tok + base + i;
+    const float4 v = *tp;
+    dz = -r * r * (v.w + bil);
+    if (qd == 0) *tp = make_float4(v.x, v.y, v.z, dz);
   }
   __syncthreads();
 #pragma unroll
-  for (int e = 0; e < kD; ++e) rows[t * kR + e] = dz * u[e];
+  for (int e = 0; e < kF; ++e) rows[tk * kR + f0 + e] = dz * u[e];
+  __syncthreads();
+  // Fixed-order sums: kG groups of kBT / kG tokens, then the groups in order.
+  {
+    const int f = t % kD, g = t / kD;
+    float v = 0.f;
+    for (int tt = g * (kBT / kG); tt < (g + 1) * (kBT / kG); ++tt) v += rows[tt * kR + f];
+    red[g * kD + f] = v;
+  }
   __syncthreads();
   if (t < kD) {
     float v = 0.f;
-    for (int tt = 0; tt < kBT; ++tt) v += rows[tt * kR + t];
+#pragma unroll
+    for (int g = 0; g < kG; ++g) v += red[g * kD + t];
     a.ds_part[((size_t)b * a.nblk + blk) * kD + t] = v;
   }
 }
@@ -426,13 +448,14 @@ __global__ __launch_bounds__(kBT) void bwd_token_b(BwdArgs a) {
 // dQt_i = dM^T phi(K_i) + sum_k w_k P_k dG_i and dz_ij the softmax adjoint
 // of window slot j.
 template <class S>
-__global__ __launch_bounds__(kBT) void bwd_token_q(BwdArgs a) {
+__global__ __launch_bounds__(kTT) void bwd_token_q(BwdArgs a) {
   __shared__ __align__(16) float Ps[kD * kD];
   __shared__ __align__(16) float dMs[kD * kD];
   __shared__ float s_sh[kD];
   __shared__ float rows[kBT * kR];
   const int b = blockIdx.y, t = threadIdx.x, blk = blockIdx.x;
-  const int i = blk * kBT + t;
+  const int tk = t / kQ, qd = t % kQ, f0 = qd * kF;
+  const int i = blk * kBT + tk;
   const bool on = i < a.n;
   const size_t base = (size_t)b * a.n;
   const float alpha = a.alpha[b % a.heads];
@@ -443,38 +466,37 @@ __global__ __launch_bounds__(kBT) void bwd_token_q(BwdArgs a) {
   load_mat(dMs, a.dmkv + (size_t)b * 2 * kD * kD);
   if (t < kD) s_sh[t] = a.fin_s[(size_t)b * kD + t];
   // dQt = dM^T phi(K_i): row phi(K_i) times dM.
-  float x[kD];
-  if (on) load_row(Kb + (size_t)i * kD, x);
+  float x[kF], dqt[kF];
+  if (on) load16(Kb + (size_t)i * kD, f0, x);
   else
 #pragma unroll
-    for (int e = 0; e < kD; ++e) x[e] = 0.f;
+    for (int e = 0; e < kF; ++e) x[e] = 0.f;
 #pragma unroll
-  for (int e = 0; e < kD; ++e) rows[t * kR + e] = fmaxf(x[e], 0.f);
-  float dqt[kD] = {};
+  for (int e = 0; e < kF; ++e) {
+    rows[tk * kR + f0 + e] = fmaxf(x[e], 0.f);
+    dqt[e] = 0.f;
+  }
   __syncthreads();
-  row_times_mat(rows + t * kR, dMs, dqt);
+  row_times_mat(rows + tk * kR, dMs, f0, dqt);
   // + sum_k w_k P_k dG_i, dG_i = alpha dY_i.
-  if (on) load_row(dYb + (size_t)i * kD, x);
-  __syncthreads();
-#pragma unroll
-  for (int e = 0; e < kD; ++e) rows[t * kR + e] = dqt[e];
+  if (on) load16(dYb + (size_t)i * kD, f0, x);
   const int T1 = a.T - 1;
   for (int k = 1; k <= T1; ++k) {
     __syncthreads();
     load_mat(Ps, a.pk + ((size_t)b * T1 + (k - 1)) * kD * kD);
     __syncthreads();
-    mat_times_vec(Ps, x, on ? alpha * wgt(a, base + i, k) : 0.f, rows + t * kR, true);
+    mat_times_vec(Ps, x, on ? alpha * wgt(a, base + i, k) : 0.f, qd, f0, dqt);
   }
   if (!on) return;  // no barrier follows
-  const float4 tk = a.tok[base + i];  // m_i, Z_i, c_i, dz_i
-  float q[kD];
-  load_row(Qb + (size_t)i * kD, q);
+  const float4 tp = a.tok[base + i];  // m_i, Z_i, c_i, dz_i
+  float q[kF];
+  load16(Qb + (size_t)i * kD, f0, q);
   float den = 0.f;
 #pragma unroll
-  for (int e = 0; e < kD; ++e) den += fmaxf(q[e], 0.f) * s_sh[e];
-  const float r = 1.f / (den + a.eps);
+  for (int e = 0; e < kF; ++e) den += fmaxf(q[e], 0.f) * s_sh[f0 + e];
+  const float r = 1.f / (quad_sum(den) + a.eps);
 #pragma unroll
-  for (int e = 0; e < kD; ++e) dqt[e] = q[e] > 0.f ? r * rows[t * kR + e] + tk.w * s_sh[e] : 0.f;
+  for (int e = 0; e < kF; ++e) dqt[e] = q[e] > 0.f ? r * dqt[e] + tp.w * s_sh[f0 + e] : 0.f;
   // Local: dz_ij = p_ij ((1 - alpha) dY_i . V_j - c_i).
   const int row = i / a.W, col = i % a.W;
 #pragma unroll 1
@@ -482,24 +504,24 @@ __global__ __launch_bounds__(kBT) void bwd_token_q(BwdArgs a) {
     const int c = window_cell(a, row, col, j);
     if (c < 0) continue;
     const S* kj = Kb + (size_t)c * kD;
-    const float p = __expf(dot_row(kj, q) * kRs - tk.x) / tk.y;
-    const float g = p * ((1.f - alpha) * dot_row(Vb + (size_t)c * kD, x) - tk.z);
-    axpy_row(g * kRs, kj, dqt);
+    const float p = __expf(dot64(kj, f0, q) * kRs - tp.x) / tp.y;
+    const float g = p * ((1.f - alpha) * dot64(Vb + (size_t)c * kD, f0, x) - tp.z);
+    axpy16(g * kRs, kj, f0, dqt);
   }
-  store_row(static_cast<S*>(a.dQ) + (base + i) * kD, dqt);
+  store16(static_cast<S*>(a.dQ) + (base + i) * kD, f0, dqt);
 }
 
 // dK_j = (dM Qt_j + dKV V_j + ds) [K_j > 0] + sum_i dz_ij q_i / 8 over the
 // centres i whose window holds j (the window relation is symmetric).
 template <class S>
-__global__ __launch_bounds__(kBT) void bwd_token_k(BwdArgs a) {
+__global__ __launch_bounds__(kTT) void bwd_token_k(BwdArgs a) {
   __shared__ __align__(16) float dMs[kD * kD];
   __shared__ __align__(16) float dKVs[kD * kD];
   __shared__ float s_sh[kD];
   __shared__ float ds_sh[kD];
-  __shared__ float rows[kBT * kR];
   const int b = blockIdx.y, t = threadIdx.x, blk = blockIdx.x;
-  const int i = blk * kBT + t;
+  const int tk = t / kQ, qd = t % kQ, f0 = qd * kF;
+  const int i = blk * kBT + tk;
   const bool on = i < a.n;
   const size_t base = (size_t)b * a.n;
   const float alpha = a.alpha[b % a.heads];
@@ -518,25 +540,25 @@ __global__ __launch_bounds__(kBT) void bwd_token_k(BwdArgs a) {
   __syncthreads();
   if (!on) return;  // no barrier follows
   // dM Qt_j + dKV V_j + ds.
-  float x[kD];
-  load_row(Qb + (size_t)i * kD, x);
+  float x[kF], acc[kF];
+  load16(Qb + (size_t)i * kD, f0, x);
   float den = 0.f;
 #pragma unroll
-  for (int e = 0; e < kD; ++e) {
+  for (int e = 0; e < kF; ++e) {
     x[e] = fmaxf(x[e], 0.f);
-    den += x[e] * s_sh[e];
+    den += x[e] * s_sh[f0 + e];
+    acc[e] = 0.f;
   }
-  const float r = 1.f / (den + a.eps);
+  const float r = 1.f / (quad_sum(den) + a.eps);
 #pragma unroll
-  for (int e = 0; e < kD; ++e) x[e] *= r;
-  float* acc = rows + t * kR;
-  mat_times_vec(dMs, x, 1.f, acc, false);
-  load_row(Vb + (size_t)i * kD, x);
-  mat_times_vec(dKVs, x, 1.f, acc, true);
-  float kr[kD], dk[kD];
-  load_row(Kb + (size_t)i * kD, kr);
+  for (int e = 0; e < kF; ++e) x[e] *= r;
+  mat_times_vec(dMs, x, 1.f, qd, f0, acc);
+  load16(Vb + (size_t)i * kD, f0, x);
+  mat_times_vec(dKVs, x, 1.f, qd, f0, acc);
+  float kr[kF], dk[kF];
+  load16(Kb + (size_t)i * kD, f0, kr);
 #pragma unroll
-  for (int e = 0; e < kD; ++e) dk[e] = kr[e] > 0.f ? acc[e] + ds_sh[e] : 0.f;
+  for (int e = 0; e < kF; ++e) dk[e] = kr[e] > 0.f ? acc[e] + ds_sh[f0 + e] : 0.f;
   // Local: token i as the neighbour of centre c.
   const int row = i / a.W, col = i % a.W;
 #pragma unroll 1
@@ -545,20 +567,21 @@ __global__ __launch_bounds__(kBT) void bwd_token_k(BwdArgs a) {
     if (c < 0) continue;
     const float4 tc = a.tok[base + c];
     const S* qc = Qb + (size_t)c * kD;
-    const float p = __expf(dot_row(qc, kr) * kRs - tc.x) / tc.y;
-    const float g = p * ((1.f - alpha) * dot_row(dYb + (size_t)c * kD, x) - tc.z);
-    axpy_row(g * kRs, qc, dk);
+    const float p = __expf(dot64(qc, f0, kr) * kRs - tc.x) / tc.y;
+    const float g = p * ((1.f - alpha) * dot64(dYb + (size_t)c * kD, f0, x) - tc.z);
+    axpy16(g * kRs, qc, f0, dk);
   }
-  store_row(static_cast<S*>(a.dK) + (base + i) * kD, dk);
+  store16(static_cast<S*>(a.dK) + (base + i) * kD, f0, dk);
 }
 
 // dV_j = w_0(j) alpha dY_j + dKV^T phi(K_j) + sum_i p_ij (1 - alpha) dY_i.
 template <class S>
-__global__ __launch_bounds__(kBT) void bwd_token_v(BwdArgs a) {
+__global__ __launch_bounds__(kTT) void bwd_token_v(BwdArgs a) {
   __shared__ __align__(16) float dKVs[kD * kD];
   __shared__ float rows[kBT * kR];
   const int b = blockIdx.y, t = threadIdx.x, blk = blockIdx.x;
-  const int i = blk * kBT + t;
+  const int tk = t / kQ, qd = t % kQ, f0 = qd * kF;
+  const int i = blk * kBT + tk;
   const bool on = i < a.n;
   const size_t base = (size_t)b * a.n;
   const float alpha = a.alpha[b % a.heads];
@@ -566,31 +589,31 @@ __global__ __launch_bounds__(kBT) void bwd_token_v(BwdArgs a) {
   const S* Kb = static_cast<const S*>(a.K) + base * kD;
   const S* dYb = static_cast<const S*>(a.dY) + base * kD;
   load_mat(dKVs, a.dmkv + (size_t)b * 2 * kD * kD + kD * kD);
-  float kr[kD];
-  if (on) load_row(Kb + (size_t)i * kD, kr);
+  float kr[kF];
+  if (on) load16(Kb + (size_t)i * kD, f0, kr);
   else
 #pragma unroll
-    for (int e = 0; e < kD; ++e) kr[e] = 0.f;
+    for (int e = 0; e < kF; ++e) kr[e] = 0.f;
 #pragma unroll
-  for (int e = 0; e < kD; ++e) rows[t * kR + e] = fmaxf(kr[e], 0.f);
+  for (int e = 0; e < kF; ++e) rows[tk * kR + f0 + e] = fmaxf(kr[e], 0.f);
   __syncthreads();
   if (!on) return;  // no barrier follows
-  float dv[kD];
-  load_row(dYb + (size_t)i * kD, dv);
-  const float f0 = alpha * wgt(a, base + i, 0);
+  float dv[kF];
+  load16(dYb + (size_t)i * kD, f0, dv);
+  const float w0 = alpha * wgt(a, base + i, 0);
 #pragma unroll
-  for (int e = 0; e < kD; ++e) dv[e] *= f0;
-  row_times_mat(rows + t * kR, dKVs, dv);
+  for (int e = 0; e < kF; ++e) dv[e] *= w0;
+  row_times_mat(rows + tk * kR, dKVs, f0, dv);
   const int row = i / a.W, col = i % a.W;
 #pragma unroll 1
   for (int j = 0; j < 9; ++j) {
     const int c = window_cell(a, row, col, j);
     if (c < 0) continue;
     const float4 tc = a.tok[base + c];
-    const float p = __expf(dot_row(Qb + (size_t)c * kD, kr) * kRs - tc.x) / tc.y;
-    axpy_row(p * (1.f - alpha), dYb + (size_t)c * kD, dv);
+    const float p = __expf(dot64(Qb + (size_t)c * kD, f0, kr) * kRs - tc.x) / tc.y;
+    axpy16(p * (1.f - alpha), dYb + (size_t)c * kD, f0, dv);
   }
-  store_row(static_cast<S*>(a.dV) + (base + i) * kD, dv);
+  store16(static_cast<S*>(a.dV) + (base + i) * kD, f0, dv);
 }
 
 // dalpha[h] = sum over the batch of the slices' shares, in batch order.
@@ -620,15 +643,15 @@ hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
   }
   const dim3 tok(a.nblk, a.BH);
   if (a.T >= 2) hipLaunchKernelGGL(bwd_powers, dim3(a.BH), dim3(kAdjThreads), 0, s, a);
-  hipLaunchKernelGGL(bwd_token_a<S>, tok, dim3(kBT), lds_a, s, a);
+  hipLaunchKernelGGL(bwd_token_a<S>, tok, dim3(kTT), lds_a, s, a);
   if (a.T >= 2)
     hipLaunchKernelGGL(bwd_reduce_dp, dim3((T1 * kD * kD + kAdjThreads - 1) / kAdjThreads, a.BH),
                        dim3(kAdjThreads), 0, s, a);
   hipLaunchKernelGGL(bwd_adjoint, dim3(a.BH), dim3(kAdjThreads), lds_adj, s, a);
-  hipLaunchKernelGGL(bwd_token_b<S>, tok, dim3(kBT), 0, s, a);
-  hipLaunchKernelGGL(bwd_token_q<S>, tok, dim3(kBT), 0, s, a);
-  hipLaunchKernelGGL(bwd_token_k<S>, tok, dim3(kBT), 0, s, a);
-  hipLaunchKernelGGL(bwd_token_v<S>, tok, dim3(kBT), 0, s, a);
+  hipLaunchKernelGGL(bwd_token_b<S>, tok, dim3(kTT), 0, s, a);
+  hipLaunchKernelGGL(bwd_token_q<S>, tok, dim3(kTT), 0, s, a);
+  hipLaunchKernelGGL(bwd_token_k<S>, tok, dim3(kTT), 0, s, a);
+  hipLaunchKernelGGL(bwd_token_v<S>, tok, dim3(kTT), 0, s, a);
   hipLaunchKernelGGL(bwd_dalpha, dim3(1), dim3(256), 0, s, a);
   return hipGetLastError();
 }
