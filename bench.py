@@ -26,15 +26,17 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 DEFAULT_WORKLOAD = "pvt_t_stage1"
 ROTATE_BYTES = 600 << 20
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+# The sources the forward kernel is built from (its counters go stale when they change).
 KERNEL_SOURCES = [
     os.path.join(ROOT, "vision_transformer_token_amd", "csrc", f)
-    for f in ("lisa_flow.hip", "lisa_device.hpp", "lisa_kernels.hpp", "lisa_api.hip", "lisa_backward.hip")
+    for f in ("lisa_flow.hip", "lisa_device.hpp", "lisa_kernels.hpp", "lisa_api.hip")
 ]
+BACKWARD_SOURCES = KERNEL_SOURCES + [os.path.join(ROOT, "vision_transformer_token_amd", "csrc", "lisa_backward.hip")]
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=None):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources or KERNEL_SOURCES:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -214,7 +216,7 @@ def summarize_backward(outdir, workload, command):
                   f"(flow_kernel is the statistics launch the backward starts with)",
               f"algorithmic bytes per call: {w.token_heads * bb / 1e6:.2f} MB ({bb} B per token-head); "
               f"at 8 TB/s: {w.token_heads * bb / 8e12 * 1e6:.1f} us",
-              f"kernel source hash: {kernel_source_hash()}"]
+              f"kernel source hash (forward and backward sources): {kernel_source_hash(BACKWARD_SOURCES)}"]
     with open(os.path.join(ROOT, "profiles", f"lisa_backward_{w.name}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 

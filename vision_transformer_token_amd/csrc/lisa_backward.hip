@@ -44,6 +44,7 @@ constexpr int kAdjThreads = 256;
 constexpr int kQ = 4;                // lanes per token
 constexpr int kF = kD / kQ;          // features per lane
 constexpr int kTT = kBT * kQ;        // threads of a token-pass workgroup
+constexpr int kW = kMaxT + 1;        // padded LDS row of a token's walk weights
 
 // This lane's 16 features of a row.
 template <class S>
@@ -137,10 +138,28 @@ __device__ __forceinline__ float bilinear(const float* xs, const float* mat, int
   return quad_sum(tot);
 }
 
+// MFMA 16x16x4 fp32 (exact fp32 products, fp32 sums).  Lane l = 16 h + m
+// holds A[m][h] and B[h][m]; accumulator element e holds C[4 h + e][m].
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 // Whole workgroup: copy a 64 x 64 fp32 matrix into LDS.
 __device__ __forceinline__ void load_mat(float* dst, const float* src) {
   for (int e = threadIdx.x * 4; e < kD * kD; e += blockDim.x * 4)
     *reinterpret_cast<float4*>(dst + e) = *reinterpret_cast<const float4*>(src + e);
+}
+
+// The same into rows of kR floats.
+__device__ __forceinline__ void load_mat_padded(float* dst, const float* src) {
+  for (int e = threadIdx.x * 4; e < kD * kD; e += blockDim.x * 4) {
+    const float4 v = *reinterpret_cast<const float4*>(src + e);
+    float* d = dst + (e / kD) * kR + e % kD;
+    d[0] = v.x;
+    d[1] = v.y;
+    d[2] = v.z;
+    d[3] = v.w;
+  }
 }
 
 __device__ __forceinline__ float wgt(const BwdArgs& a, size_t tok, int k) {
@@ -195,12 +214,12 @@ __global__ __launch_bounds__(kAdjThreads) void bwd_powers(BwdArgs a) {
 template <class S>
 __global__ __launch_bounds__(kTT) void bwd_token_a(BwdArgs a) {
   extern __shared__ __align__(16) float sm[];
-  float* Ps = sm;                        // kD * kD: P_k
-  float* s_sh = Ps + kD * kD;            // kD
+  float* Ps = sm;                        // kD rows of kR: P_k
+  float* s_sh = Ps + kD * kR;            // kD
   float* qt_sh = s_sh + kD;              // kBT rows of Qt (padded)
   float* dy_sh = qt_sh + kBT * kR;       // kBT rows of dY (padded)
-  float* w_sh = dy_sh + kBT * kR;        // kBT x kMaxT weights
-  float* red = w_sh + kBT * kMaxT;       // kBT
+  float* w_sh = dy_sh + kBT * kR;        // kBT rows of kW weights
+  float* red = w_sh + kBT * kW;          // kBT
   const int b = blockIdx.y, t = threadIdx.x, blk = blockIdx.x;
   const int tk = t / kQ, qd = t % kQ, f0 = qd * kF;
   const int i = blk * kBT + tk;
@@ -213,7 +232,7 @@ __global__ __launch_bounds__(kTT) void bwd_token_a(BwdArgs a) {
   const S* dYb = static_cast<const S*>(a.dY) + base * kD;
   if (t < kD) s_sh[t] = a.fin_s[(size_t)b * kD + t];
   if (qd == 0)
-    for (int k = 0; k < kMaxT; ++k) w_sh[tk * kMaxT + k] = (on && k < a.T) ? wgt(a, base + i, k) : 0.f;
+    for (int k = 0; k < kMaxT; ++k) w_sh[tk * kW + k] = (on && k < a.T) ? wgt(a, base + i, k) : 0.f;
 
   float q[kF], dy[kF];
   float m = 0.f, Z = 1.f, dyL = 0.f, dyv = 0.f;
@@ -265,32 +284,62 @@ __global__ __launch_bounds__(kTT) void bwd_token_a(BwdArgs a) {
 #pragma unroll
   for (int k = 0; k < kMaxT; ++k) dyy[k] = 0.f;
   const int T1 = a.T - 1;
-  const int ra = t >> 4, c0 = (t & 15) * 4;  // this lane's 1 x 4 piece of dP_k (wave: 4 rows)
+  // MFMA roles: wave wv holds tokens 16 wv .. 16 wv + 15 (its quads) and the
+  // 16 x 16 block (ga, gc) of dP_k; lane ln = 16 lk + li.  The contractions
+  // take their terms in an order (features 16 lk + kk, tokens
+  // 64 (kk / 16) + 16 lk + kk % 16) under which every LDS operand read of a
+  // wave hits 64 distinct banks (row stride kR = 1 mod 64).
+  const int wv = t / 64, ln = t % 64, li = ln % 16, lk = ln / 16;
+  const int ga = 16 * (wv / 4), gc = 16 * (wv % 4);
 #pragma unroll
   for (int k = 1; k < kMaxT; ++k) {
     if (k > T1) break;
     __syncthreads();
-    load_mat(Ps, a.pk + ((size_t)b * T1 + (k - 1)) * kD * kD);
+    load_mat_padded(Ps, a.pk + ((size_t)b * T1 + (k - 1)) * kD * kD);
     __syncthreads();
-    // dY_i . (Qt_i P_k) = Qt_i^T P_k dY_i.
-    dyy[k] = bilinear(qt_sh + tk * kR, Ps, f0, dy);
-    // This workgroup's share of dP_k.
-    float acc[4] = {};
+    // dY_i . (Qt_i P_k): X = Qt P_k for the wave's 16 tokens (4 column
+    // blocks), then each row dotted with dY_i.
+    {
+      f32x4 x[4] = {};
 #pragma unroll 4
-    for (int tt = 0; tt < kBT; ++tt) {
-      const float fq = alpha * w_sh[tt * kMaxT + k] * qt_sh[tt * kR + ra];
+      for (int kk = 0; kk < kD / 4; ++kk) {
+        const int f = 16 * lk + kk;
+        const float av = qt_sh[(16 * wv + li) * kR + f];
 #pragma unroll
-      for (int y = 0; y < 4; ++y) acc[y] += fq * dy_sh[tt * kR + c0 + y];
+        for (int ct = 0; ct < 4; ++ct) x[ct] = mfma16(av, Ps[f * kR + 16 * ct + li], x[ct]);
+      }
+      float part[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float* dyr = dy_sh + (16 * wv + 4 * lk + e) * kR + li;
+        float v = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) v += x[ct][e] * dyr[16 * ct];
+        part[e] = group_sum16(v);
+      }
+      // This lane's token 16 wv + ln / 4 is row 4 lk + li / 4 of the block.
+      const int e = li / 4;
+      dyy[k] = e == 0 ? part[0] : e == 1 ? part[1] : e == 2 ? part[2] : part[3];
     }
-    float* dst = a.dp_part + (((size_t)b * a.nblk + blk) * T1 + (k - 1)) * kD * kD;
-    *reinterpret_cast<float4*>(dst + ra * kD + c0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    // This workgroup's share of dP_k = sum_i alpha w_k(i) Qt_i^T dY_i.
+    {
+      f32x4 acc = {};
+#pragma unroll 8
+      for (int kk = 0; kk < kBT / 4; ++kk) {
+        const int tt = 64 * (kk / 16) + 16 * lk + kk % 16;
+        acc = mfma16(w_sh[tt * kW + k] * qt_sh[tt * kR + ga + li], dy_sh[tt * kR + gc + li], acc);
+      }
+      float* dst = a.dp_part + (((size_t)b * a.nblk + blk) * T1 + (k - 1)) * kD * kD;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[(ga + 4 * lk + e) * kD + gc + li] = alpha * acc[e];
+    }
   }
   // Scalars of the token (every lane of the quad holds them).
   float wy = 0.f;
 #pragma unroll
   for (int k = 1; k < kMaxT; ++k)
-    if (k <= T1) wy += w_sh[tk * kMaxT + k] * dyy[k];
-  const float dyG = w_sh[tk * kMaxT] * dyv + wy;
+    if (k <= T1) wy += w_sh[tk * kW + k] * dyy[k];
+  const float dyG = w_sh[tk * kW] * dyv + wy;
   if (on && qd == 0) {
     // a_i = (sum_k w_k P_k dG_i) . phi(Q_i) = alpha / r_i * sum_k w_k dY_i . (Qt_i P_k)
     a.tok[base + i] = make_float4(m, Z, (1.f - alpha) * dyL, alpha / r * wy);
@@ -627,7 +676,7 @@ __global__ __launch_bounds__(256) void bwd_dalpha(BwdArgs a) {
 
 template <class S>
 hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
-  const size_t lds_a = (size_t)(kD * kD + kD + 2 * kBT * kR + kBT * kMaxT + kBT) * sizeof(float);
+  const size_t lds_a = (size_t)(kD * kR + kD + 2 * kBT * kR + kBT * kW + kBT) * sizeof(float);
   const int T1 = a.T - 1 > 0 ? a.T - 1 : 1;
   const size_t lds_adj = ((size_t)T1 * kD * kD + kD * kD + kD * kR) * sizeof(float);
   static bool attr_set = false;
