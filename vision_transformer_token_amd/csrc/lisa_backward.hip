@@ -23,9 +23,10 @@
 //
 // Layout: the token passes take kBwdTokens tokens per workgroup, four lanes
 // per token (lane quarter qd owns features 16 qd .. 16 qd + 15); dot products
-// are reduced over the lane quad with DPP.  The slice's 64 x 64 matrices sit
-// in LDS, read as broadcasts.  Vectors that are indexed at run time live in a
-// per-token LDS row shared by the quad; the rest stay in registers.
+// are reduced over the lane quad with DPP.  Products of token rows with the
+// slice's 64 x 64 matrices (and the token reduction dP_k) run on fp32 MFMA
+// (16x16x4): each wave multiplies the LDS rows of its 16 tokens by a matrix
+// held in LDS, and the result returns to the quad layout through those rows.
 // Everything is fp32; outputs dQ, dK, dV are written once in the input dtype.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -84,66 +85,45 @@ __device__ __forceinline__ void quad_lds_sync() {
   asm volatile("" ::: "memory");
 }
 
-// y (this lane's 16 columns) += sum_a xs[a] mat[a][f0 + c]; xs: the token's LDS row.
-__device__ __forceinline__ void row_times_mat(const float* xs, const float* mat, int f0, float (&y)[kF]) {
-#pragma unroll 2
-  for (int a = 0; a < kD; ++a) {
-    const float xa = xs[a];
-    const float4* m = reinterpret_cast<const float4*>(mat + a * kD + f0);
-#pragma unroll
-    for (int c = 0; c < kF / 4; ++c) {
-      const float4 v = m[c];
-      y[4 * c] += xa * v.x;
-      y[4 * c + 1] += xa * v.y;
-      y[4 * c + 2] += xa * v.z;
-      y[4 * c + 3] += xa * v.w;
-    }
-  }
-}
-// y (this lane's 16 rows a = f0 + i) += f * sum_c mat[a][c] x[c], x spread
-// over the quad (16 columns per lane).
-__device__ __forceinline__ void mat_times_vec(const float* mat, const float (&x)[kF], float f, int qd, int f0,
-                                              float (&y)[kF]) {
-#pragma unroll 1
-  for (int ab = 0; ab < kQ; ++ab) {
-#pragma unroll
-    for (int ai = 0; ai < kF; ++ai) {
-      const float4* m = reinterpret_cast<const float4*>(mat + (ab * kF + ai) * kD + f0);
-      float acc = 0.f;
-#pragma unroll
-      for (int c = 0; c < kF / 4; ++c) {
-        const float4 v = m[c];
-        acc += v.x * x[4 * c] + v.y * x[4 * c + 1] + v.z * x[4 * c + 2] + v.w * x[4 * c + 3];
-      }
-      acc = quad_sum(acc);
-      if (ab == qd) y[ai] += f * acc;
-    }
-  }
-}
-// sum_a xs[a] sum_c mat[a][c] x[c] (quad-reduced); xs: the token's LDS row,
-// x spread over the quad.
-__device__ __forceinline__ float bilinear(const float* xs, const float* mat, int f0, const float (&x)[kF]) {
-  float tot = 0.f;
-#pragma unroll 2
-  for (int a = 0; a < kD; ++a) {
-    const float4* m = reinterpret_cast<const float4*>(mat + a * kD + f0);
-    float acc = 0.f;
-#pragma unroll
-    for (int c = 0; c < kF / 4; ++c) {
-      const float4 v = m[c];
-      acc += v.x * x[4 * c] + v.y * x[4 * c + 1] + v.z * x[4 * c + 2] + v.w * x[4 * c + 3];
-    }
-    tot += xs[a] * acc;
-  }
-  return quad_sum(tot);
-}
-
 // MFMA 16x16x4 fp32 (exact fp32 products, fp32 sums).  Lane l = 16 h + m
 // holds A[m][h] and B[h][m]; accumulator element e holds C[4 h + e][m].
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+// Y += diag(sx) X M (kTr = false) or diag(sx) X M^T (kTr = true) for the
+// wave's 16 tokens: X their LDS rows (stride kR), M a 64 x 64 matrix in LDS
+// rows of kR floats, sx this lane's row scale (row li).  Y in accumulator
+// layout: acc[ct][e] = Y[4 lk + e][16 ct + li].  Features are taken in the
+// order 16 lk + kk, which keeps every operand read of the wave on 64
+// distinct banks (kR = 1 mod 64).
+template <bool kTr>
+__device__ __forceinline__ void wave_mm(const float* X, const float* M, float sx, f32x4 (&acc)[4]) {
+  const int ln = threadIdx.x % 64, li = ln % 16, lk = ln / 16;
+#pragma unroll 4
+  for (int kk = 0; kk < kD / 4; ++kk) {
+    const int f = 16 * lk + kk;
+    const float av = sx * X[li * kR + f];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+      acc[ct] = mfma16(av, kTr ? M[(16 * ct + li) * kR + f] : M[f * kR + 16 * ct + li], acc[ct]);
+  }
+}
+// Y from accumulator layout into the lane-quad layout through the wave's LDS
+// rows X (overwritten): lane (token tw of the wave, quarter f0) gets
+// Y[tw][f0 .. f0 + 15].
+__device__ __forceinline__ void acc_to_quad(const f32x4 (&acc)[4], float* X, int tw, int f0, float (&y)[kF]) {
+  const int ln = threadIdx.x % 64, li = ln % 16, lk = ln / 16;
+  quad_lds_sync();
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) X[(4 * lk + e) * kR + 16 * ct + li] = acc[ct][e];
+  quad_lds_sync();
+#pragma unroll
+  for (int e = 0; e < kF; ++e) y[e] = X[tw * kR + f0 + e];
+}
+
 // Whole workgroup: copy a 64 x 64 fp32 matrix into LDS.
 __device__ __forceinline__ void load_mat(float* dst, const float* src) {
   for (int e = threadIdx.x * 4; e < kD * kD; e += blockDim.x * 4)
@@ -436,16 +416,17 @@ __global__ __launch_bounds__(kAdjThreads) void bwd_adjoint(BwdArgs a) {
 template <class S>
 __global__ __launch_bounds__(kTT) void bwd_token_b(BwdArgs a) {
   constexpr int kG = kTT / kD;  // partial sums per feature in the ds reduction
-  __shared__ __align__(16) float dMs[kD * kD];
+  __shared__ float dMs[kD * kR];
   __shared__ float s_sh[kD];
   __shared__ float rows[kBT * kR];
   __shared__ float red[kG * kD];
   const int b = blockIdx.y, t = threadIdx.x, blk = blockIdx.x;
-  const int tk = t / kQ, qd = t % kQ, f0 = qd * kF;
+  const int tk = t / kQ, qd = t % kQ, f0 = qd * kF, tw = tk % 16;
+  float* wrows = rows + (t / 64) * 16 * kR;  // this wave's 16 token rows
   const int i = blk * kBT + tk;
   const bool on = i < a.n;
   const size_t base = (size_t)b * a.n;
-  load_mat(dMs, a.dmkv + (size_t)b * 2 * kD * kD);
+  load_mat_padded(dMs, a.dmkv + (size_t)b * 2 * kD * kD);
   if (t < kD) s_sh[t] = a.fin_s[(size_t)b * kD + t];
   float u[kF], kp[kF];
   if (on) {
@@ -455,17 +436,25 @@ __global__ __launch_bounds__(kTT) void bwd_token_b(BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < kF; ++e) u[e] = kp[e] = 0.f;
   }
+#pragma unroll
+  for (int e = 0; e < kF; ++e) rows[tk * kR + f0 + e] = fmaxf(kp[e], 0.f);
   __syncthreads();
   float den = 0.f;
 #pragma unroll
   for (int e = 0; e < kF; ++e) {
     u[e] = fmaxf(u[e], 0.f);
     den += u[e] * s_sh[f0 + e];
-    rows[tk * kR + f0 + e] = fmaxf(kp[e], 0.f);
   }
   const float r = 1.f / (quad_sum(den) + a.eps);
-  quad_lds_sync();
-  const float bil = bilinear(rows + tk * kR, dMs, f0, u);
+  // phi(K_i)^T dM phi(Q_i): the row phi(K_i) dM, dotted with phi(Q_i).
+  f32x4 acc[4] = {};
+  wave_mm<false>(wrows, dMs, 1.f, acc);
+  float y[kF];
+  acc_to_quad(acc, wrows, tw, f0, y);
+  float bil = 0.f;
+#pragma unroll
+  for (int e = 0; e < kF; ++e) bil += y[e] * u[e];
+  bil = quad_sum(bil);
   float dz = 0.f;
   if (on) {
     float4* tp = a.tok + base + i;
@@ -498,12 +487,13 @@ __global__ __launch_bounds__(kTT) void bwd_token_b(BwdArgs a) {
 // of window slot j.
 template <class S>
 __global__ __launch_bounds__(kTT) void bwd_token_q(BwdArgs a) {
-  __shared__ __align__(16) float Ps[kD * kD];
-  __shared__ __align__(16) float dMs[kD * kD];
+  __shared__ float Ps[kD * kR];
+  __shared__ float dMs[kD * kR];
   __shared__ float s_sh[kD];
   __shared__ float rows[kBT * kR];
   const int b = blockIdx.y, t = threadIdx.x, blk = blockIdx.x;
-  const int tk = t / kQ, qd = t % kQ, f0 = qd * kF;
+  const int tk = t / kQ, qd = t % kQ, f0 = qd * kF, tw = tk % 16;
+  float* wrows = rows + (t / 64) * 16 * kR;
   const int i = blk * kBT + tk;
   const bool on = i < a.n;
   const size_t base = (size_t)b * a.n;
@@ -512,30 +502,34 @@ __global__ __launch_bounds__(kTT) void bwd_token_q(BwdArgs a) {
   const S* Kb = static_cast<const S*>(a.K) + base * kD;
   const S* Vb = static_cast<const S*>(a.V) + base * kD;
   const S* dYb = static_cast<const S*>(a.dY) + base * kD;
-  load_mat(dMs, a.dmkv + (size_t)b * 2 * kD * kD);
+  load_mat_padded(dMs, a.dmkv + (size_t)b * 2 * kD * kD);
   if (t < kD) s_sh[t] = a.fin_s[(size_t)b * kD + t];
-  // dQt = dM^T phi(K_i): row phi(K_i) times dM.
-  float x[kF], dqt[kF];
+  float x[kF];
   if (on) load16(Kb + (size_t)i * kD, f0, x);
   else
 #pragma unroll
     for (int e = 0; e < kF; ++e) x[e] = 0.f;
 #pragma unroll
-  for (int e = 0; e < kF; ++e) {
-    rows[tk * kR + f0 + e] = fmaxf(x[e], 0.f);
-    dqt[e] = 0.f;
-  }
+  for (int e = 0; e < kF; ++e) rows[tk * kR + f0 + e] = fmaxf(x[e], 0.f);
   __syncthreads();
-  row_times_mat(rows + tk * kR, dMs, f0, dqt);
-  // + sum_k w_k P_k dG_i, dG_i = alpha dY_i.
+  // dQt rows: phi(K) dM, then + sum_k diag(alpha w_k) dY P_k^T.
+  f32x4 acc[4] = {};
+  wave_mm<false>(wrows, dMs, 1.f, acc);
   if (on) load16(dYb + (size_t)i * kD, f0, x);
+  quad_lds_sync();
+#pragma unroll
+  for (int e = 0; e < kF; ++e) rows[tk * kR + f0 + e] = x[e];
   const int T1 = a.T - 1;
+  // The MFMA A operand row of this lane: token 16 (t / 64) + li.
+  const int ia = blk * kBT + (t / 64) * 16 + (t % 16);
   for (int k = 1; k <= T1; ++k) {
     __syncthreads();
-    load_mat(Ps, a.pk + ((size_t)b * T1 + (k - 1)) * kD * kD);
+    load_mat_padded(Ps, a.pk + ((size_t)b * T1 + (k - 1)) * kD * kD);
     __syncthreads();
-    mat_times_vec(Ps, x, on ? alpha * wgt(a, base + i, k) : 0.f, qd, f0, dqt);
+    wave_mm<true>(wrows, Ps, ia < a.n ? alpha * wgt(a, base + ia, k) : 0.f, acc);
   }
+  float dqt[kF];
+  acc_to_quad(acc, wrows, tw, f0, dqt);
   if (!on) return;  // no barrier follows
   const float4 tp = a.tok[base + i];  // m_i, Z_i, c_i, dz_i
   float q[kF];
@@ -564,12 +558,14 @@ __global__ __launch_bounds__(kTT) void bwd_token_q(BwdArgs a) {
 // centres i whose window holds j (the window relation is symmetric).
 template <class S>
 __global__ __launch_bounds__(kTT) void bwd_token_k(BwdArgs a) {
-  __shared__ __align__(16) float dMs[kD * kD];
-  __shared__ __align__(16) float dKVs[kD * kD];
+  __shared__ float dMs[kD * kR];
+  __shared__ float dKVs[kD * kR];
   __shared__ float s_sh[kD];
   __shared__ float ds_sh[kD];
+  __shared__ float rows[kBT * kR];
   const int b = blockIdx.y, t = threadIdx.x, blk = blockIdx.x;
-  const int tk = t / kQ, qd = t % kQ, f0 = qd * kF;
+  const int tk = t / kQ, qd = t % kQ, f0 = qd * kF, tw = tk % 16;
+  float* wrows = rows + (t / 64) * 16 * kR;
   const int i = blk * kBT + tk;
   const bool on = i < a.n;
   const size_t base = (size_t)b * a.n;
@@ -578,8 +574,8 @@ __global__ __launch_bounds__(kTT) void bwd_token_k(BwdArgs a) {
   const S* Kb = static_cast<const S*>(a.K) + base * kD;
   const S* Vb = static_cast<const S*>(a.V) + base * kD;
   const S* dYb = static_cast<const S*>(a.dY) + base * kD;
-  load_mat(dMs, a.dmkv + (size_t)b * 2 * kD * kD);
-  load_mat(dKVs, a.dmkv + (size_t)b * 2 * kD * kD + kD * kD);
+  load_mat_padded(dMs, a.dmkv + (size_t)b * 2 * kD * kD);
+  load_mat_padded(dKVs, a.dmkv + (size_t)b * 2 * kD * kD + kD * kD);
   if (t < kD) {
     s_sh[t] = a.fin_s[(size_t)b * kD + t];
     float v = 0.f;
@@ -587,27 +583,37 @@ __global__ __launch_bounds__(kTT) void bwd_token_k(BwdArgs a) {
     ds_sh[t] = v;
   }
   __syncthreads();
-  if (!on) return;  // no barrier follows
-  // dM Qt_j + dKV V_j + ds.
-  float x[kF], acc[kF];
-  load16(Qb + (size_t)i * kD, f0, x);
+  // Rows Qt_j dM^T + V_j dKV^T.
+  float x[kF];
+  if (on) load16(Qb + (size_t)i * kD, f0, x);
+  else
+#pragma unroll
+    for (int e = 0; e < kF; ++e) x[e] = 0.f;
   float den = 0.f;
 #pragma unroll
   for (int e = 0; e < kF; ++e) {
     x[e] = fmaxf(x[e], 0.f);
     den += x[e] * s_sh[f0 + e];
-    acc[e] = 0.f;
   }
   const float r = 1.f / (quad_sum(den) + a.eps);
 #pragma unroll
-  for (int e = 0; e < kF; ++e) x[e] *= r;
-  mat_times_vec(dMs, x, 1.f, qd, f0, acc);
-  load16(Vb + (size_t)i * kD, f0, x);
-  mat_times_vec(dKVs, x, 1.f, qd, f0, acc);
+  for (int e = 0; e < kF; ++e) rows[tk * kR + f0 + e] = x[e] * r;
+  quad_lds_sync();
+  f32x4 acc[4] = {};
+  wave_mm<true>(wrows, dMs, 1.f, acc);
+  if (on) load16(Vb + (size_t)i * kD, f0, x);
+  quad_lds_sync();
+#pragma unroll
+  for (int e = 0; e < kF; ++e) rows[tk * kR + f0 + e] = x[e];
+  quad_lds_sync();
+  wave_mm<true>(wrows, dKVs, 1.f, acc);
+  float g16[kF];
+  acc_to_quad(acc, wrows, tw, f0, g16);
+  if (!on) return;  // no barrier follows
   float kr[kF], dk[kF];
   load16(Kb + (size_t)i * kD, f0, kr);
 #pragma unroll
-  for (int e = 0; e < kF; ++e) dk[e] = kr[e] > 0.f ? acc[e] + ds_sh[f0 + e] : 0.f;
+  for (int e = 0; e < kF; ++e) dk[e] = kr[e] > 0.f ? g16[e] + ds_sh[f0 + e] : 0.f;
   // Local: token i as the neighbour of centre c.
   const int row = i / a.W, col = i % a.W;
 #pragma unroll 1
@@ -626,10 +632,11 @@ __global__ __launch_bounds__(kTT) void bwd_token_k(BwdArgs a) {
 // dV_j = w_0(j) alpha dY_j + dKV^T phi(K_j) + sum_i p_ij (1 - alpha) dY_i.
 template <class S>
 __global__ __launch_bounds__(kTT) void bwd_token_v(BwdArgs a) {
-  __shared__ __align__(16) float dKVs[kD * kD];
+  __shared__ float dKVs[kD * kR];
   __shared__ float rows[kBT * kR];
   const int b = blockIdx.y, t = threadIdx.x, blk = blockIdx.x;
-  const int tk = t / kQ, qd = t % kQ, f0 = qd * kF;
+  const int tk = t / kQ, qd = t % kQ, f0 = qd * kF, tw = tk % 16;
+  float* wrows = rows + (t / 64) * 16 * kR;
   const int i = blk * kBT + tk;
   const bool on = i < a.n;
   const size_t base = (size_t)b * a.n;
@@ -637,7 +644,7 @@ __global__ __launch_bounds__(kTT) void bwd_token_v(BwdArgs a) {
   const S* Qb = static_cast<const S*>(a.Q) + base * kD;
   const S* Kb = static_cast<const S*>(a.K) + base * kD;
   const S* dYb = static_cast<const S*>(a.dY) + base * kD;
-  load_mat(dKVs, a.dmkv + (size_t)b * 2 * kD * kD + kD * kD);
+  load_mat_padded(dKVs, a.dmkv + (size_t)b * 2 * kD * kD + kD * kD);
   float kr[kF];
   if (on) load16(Kb + (size_t)i * kD, f0, kr);
   else
@@ -646,13 +653,17 @@ __global__ __launch_bounds__(kTT) void bwd_token_v(BwdArgs a) {
 #pragma unroll
   for (int e = 0; e < kF; ++e) rows[tk * kR + f0 + e] = fmaxf(kr[e], 0.f);
   __syncthreads();
-  if (!on) return;  // no barrier follows
+  // Rows phi(K_j) dKV.
+  f32x4 acc[4] = {};
+  wave_mm<false>(wrows, dKVs, 1.f, acc);
   float dv[kF];
-  load16(dYb + (size_t)i * kD, f0, dv);
+  acc_to_quad(acc, wrows, tw, f0, dv);
+  if (!on) return;  // no barrier follows
+  float dy[kF];
+  load16(dYb + (size_t)i * kD, f0, dy);
   const float w0 = alpha * wgt(a, base + i, 0);
 #pragma unroll
-  for (int e = 0; e < kF; ++e) dv[e] *= w0;
-  row_times_mat(rows + tk * kR, dKVs, f0, dv);
+  for (int e = 0; e < kF; ++e) dv[e] += w0 * dy[e];
   const int row = i / a.W, col = i % a.W;
 #pragma unroll 1
   for (int j = 0; j < 9; ++j) {
