@@ -40,7 +40,7 @@ namespace {
 constexpr int kBT = kBwdTokens;
 constexpr int kR = kD + 1;           // padded LDS row (floats)
 constexpr float kRs = 0.125f;        // 1 / sqrt(d_h), d_h = 64
-constexpr int kAdjThreads = 256;
+constexpr int kAdjThreads = 1024;  // per-slice kernels: wave w owns rows 16 (w % 4) .., column block w / 4
 
 constexpr int kQ = 4;                // lanes per token
 constexpr int kF = kD / kQ;          // features per lane
@@ -69,13 +69,6 @@ __device__ __forceinline__ float dot64(const S* row, int f0, const float (&x)[kF
 #pragma unroll
   for (int e = 0; e < kF; ++e) acc += x[e] * y[e];
   return quad_sum(acc);
-}
-template <class S>
-__device__ __forceinline__ void axpy16(float f, const S* row, int f0, float (&x)[kF]) {
-  float y[kF];
-  load16(row, f0, y);
-#pragma unroll
-  for (int e = 0; e < kF; ++e) x[e] += f * y[e];
 }
 // The quad's rows in LDS are written and read by lanes of one wave: order
 // the LDS accesses (the compiler may not move them across this either).
@@ -109,6 +102,18 @@ __device__ __forceinline__ void wave_mm(const float* X, const float* M, float sx
       acc[ct] = mfma16(av, kTr ? M[(16 * ct + li) * kR + f] : M[f * kR + 16 * ct + li], acc[ct]);
   }
 }
+// One 16 x 16 block of X M (kTr = false) or X M^T (kTr = true): X the 16
+// rows (stride kR), column block ct; same operand order as wave_mm.
+template <bool kTr>
+__device__ __forceinline__ f32x4 tile_mm(const float* X, const float* M, int ct, f32x4 acc) {
+  const int ln = threadIdx.x % 64, li = ln % 16, lk = ln / 16;
+#pragma unroll 4
+  for (int kk = 0; kk < kD / 4; ++kk) {
+    const int f = 16 * lk + kk;
+    acc = mfma16(X[li * kR + f], kTr ? M[(16 * ct + li) * kR + f] : M[f * kR + 16 * ct + li], acc);
+  }
+  return acc;
+}
 // Y from accumulator layout into the lane-quad layout through the wave's LDS
 // rows X (overwritten): lane (token tw of the wave, quarter f0) gets
 // Y[tw][f0 .. f0 + 15].
@@ -122,6 +127,26 @@ __device__ __forceinline__ void acc_to_quad(const f32x4 (&acc)[4], float* X, int
   quad_lds_sync();
 #pragma unroll
   for (int e = 0; e < kF; ++e) y[e] = X[tw * kR + f0 + e];
+}
+
+// Sum over the wave (butterfly of fixed shape: the same order every run).
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// sum_{p < n} x[p * stride] in order of p, with 8 loads in flight.
+__device__ __forceinline__ float sum_in_order(const float* x, size_t stride, int n) {
+  float v = 0.f;
+  for (int p0 = 0; p0 < n; p0 += 8) {
+    float y[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) y[u] = p0 + u < n ? x[(size_t)(p0 + u) * stride] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v += y[u];
+  }
+  return v;
 }
 
 // Whole workgroup: copy a 64 x 64 fp32 matrix into LDS.
@@ -155,35 +180,26 @@ __device__ __forceinline__ int window_cell(const BwdArgs& a, int row, int col, i
 
 // P_1 = phi(K)^T V, P_k = M P_(k-1) for k = 2 .. T-1: one workgroup per slice.
 __global__ __launch_bounds__(kAdjThreads) void bwd_powers(BwdArgs a) {
-  __shared__ float Ms[kD * kD];
-  __shared__ float Ps[kD * kR];
-  const int b = blockIdx.x, t = threadIdx.x;
-  const int T1 = a.T - 1;
+  __shared__ float Ms[kD * kR];
+  __shared__ float Ps[2][kD * kR];
+  const int b = blockIdx.x, t = threadIdx.x, T1 = a.T - 1;
   if (T1 < 1) return;
-  const float* M = a.fin_m + (size_t)b * kD * kD;
+  const int w = t / 64, li = t % 16, lk = (t % 64) / 16, r0 = 16 * (w % 4), ct = w / 4;
   const float* P1 = a.fin_kv + (size_t)b * kD * kD;
   float* out = a.pk + (size_t)b * T1 * kD * kD;
-  load_mat(Ms, M);
-  for (int e = t; e < kD * kD; e += kAdjThreads) {
-    Ps[(e >> 6) * kR + (e & 63)] = P1[e];
-    out[e] = P1[e];
-  }
+  load_mat_padded(Ms, a.fin_m + (size_t)b * kD * kD);
+  load_mat_padded(Ps[0], P1);
+  for (int e = t * 4; e < kD * kD; e += kAdjThreads * 4)
+    *reinterpret_cast<float4*>(out + e) = *reinterpret_cast<const float4*>(P1 + e);
   for (int k = 2; k <= T1; ++k) {
     __syncthreads();
-    float acc[kD * kD / kAdjThreads];
+    const f32x4 y = tile_mm<false>(Ms + r0 * kR, Ps[k % 2], ct, f32x4{});
+    float* Po = Ps[(k + 1) % 2];
+    float* o = out + (size_t)(k - 1) * kD * kD;
 #pragma unroll
-    for (int x = 0; x < kD * kD / kAdjThreads; ++x) {
-      const int e = t + kAdjThreads * x, r = e >> 6, c = e & 63;
-      float v = 0.f;
-      for (int j = 0; j < kD; ++j) v += Ms[r * kD + j] * Ps[j * kR + c];
-      acc[x] = v;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int x = 0; x < kD * kD / kAdjThreads; ++x) {
-      const int e = t + kAdjThreads * x;
-      Ps[(e >> 6) * kR + (e & 63)] = acc[x];
-      out[(size_t)(k - 1) * kD * kD + e] = acc[x];
+    for (int e = 0; e < 4; ++e) {
+      Po[(r0 + 4 * lk + e) * kR + 16 * ct + li] = y[e];
+      o[(r0 + 4 * lk + e) * kD + 16 * ct + li] = y[e];
     }
   }
 }
@@ -341,74 +357,70 @@ __global__ __launch_bounds__(kTT) void bwd_token_a(BwdArgs a) {
   if (t == 0) a.da_part[(size_t)b * a.nblk + blk] = red[0];
 }
 
-// dP_k: the workgroups' partials summed in order, element by element, into
-// the first workgroup's slot.
-__global__ __launch_bounds__(kAdjThreads) void bwd_reduce_dp(BwdArgs a) {
-  const int b = blockIdx.y, T1 = a.T - 1;
-  const size_t per = (size_t)T1 * kD * kD;
-  const size_t e = (size_t)blockIdx.x * kAdjThreads + threadIdx.x;
-  if (T1 < 1 || e >= per) return;
-  float* base = a.dp_part + (size_t)b * a.nblk * per + e;
-  float v = 0.f;
-  for (int p = 0; p < a.nblk; ++p) v += base[(size_t)p * per];
-  base[0] = v;
-}
-
-// dP_k (summed by bwd_reduce_dp); then, from the last term down,
-// dM += dP_k P_(k-1)^T and dP_(k-1) += M^T dP_k; dKV = dP_1.  One workgroup
-// per slice; also the slice's dalpha.
+// dP_k (the token workgroups' partials, summed in order); then, from the
+// last term down, dM += dP_k P_(k-1)^T and dP_(k-1) += M^T dP_k; dKV = dP_1.
+// One workgroup per slice.
 __global__ __launch_bounds__(kAdjThreads) void bwd_adjoint(BwdArgs a) {
   extern __shared__ __align__(16) float sm[];
   const int b = blockIdx.x, t = threadIdx.x, T1 = a.T - 1;
-  constexpr int kX = kD * kD / kAdjThreads;  // outputs per thread
-  float* dP = sm;                            // T1 x 64 x 64
-  float* Ms = dP + (size_t)(T1 > 0 ? T1 : 1) * kD * kD;
-  float* Pp = Ms + kD * kD;                  // P_(k-1), padded rows
   float* dMo = a.dmkv + (size_t)b * 2 * kD * kD;
   float* dKVo = dMo + kD * kD;
-  if (t == 0) {
+  // The slice's share of dalpha: lane-strided sums, then the wave's butterfly.
+  if (t < 64) {
     float v = 0.f;
-    for (int p = 0; p < a.nblk; ++p) v += a.da_part[(size_t)b * a.nblk + p];
-    a.da_slice[b] = v;
+    for (int p = t; p < a.nblk; p += 64) v += a.da_part[(size_t)b * a.nblk + p];
+    v = wave_sum(v);
+    if (t == 0) a.da_slice[b] = v;
   }
   if (T1 < 1) {
     for (int e = t; e < kD * kD; e += kAdjThreads) dMo[e] = dKVo[e] = 0.f;
     return;
   }
-  const size_t per = (size_t)T1 * kD * kD;
-  for (size_t e = t; e < per; e += kAdjThreads) dP[e] = a.dp_part[(size_t)b * a.nblk * per + e];
-  load_mat(Ms, a.fin_m + (size_t)b * kD * kD);
-  float dM[kX] = {};
+  const int w = t / 64, li = t % 16, lk = (t % 64) / 16, r0 = 16 * (w % 4), ct = w / 4;
+  float* dP = sm;                          // T1 blocks of kD rows of kR
+  float* MT = dP + (size_t)T1 * kD * kR;   // M^T
+  float* Pp = MT + kD * kR;                // P_(k-1)
+  const int per = T1 * kD * kD;
+  const float* part = a.dp_part + (size_t)b * a.nblk * per;
+  // Each sum in workgroup order; 4 elements x 8 partials of loads in flight.
+  for (int j0 = 0; j0 < per / kAdjThreads; j0 += 4) {
+    float v[4] = {};
+    for (int p0 = 0; p0 < a.nblk; p0 += 8) {
+      float x[4][8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          x[jj][u] = p0 + u < a.nblk ? part[(size_t)(p0 + u) * per + (j0 + jj) * kAdjThreads + t] : 0.f;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[jj] += x[jj][u];
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int e = (j0 + jj) * kAdjThreads + t;
+      dP[(e / (kD * kD)) * kD * kR + ((e / kD) % kD) * kR + e % kD] = v[jj];
+    }
+  }
+  const float* M = a.fin_m + (size_t)b * kD * kD;
+  for (int e = t; e < kD * kD; e += kAdjThreads) MT[(e % kD) * kR + e / kD] = M[e];
+  f32x4 dm = {};
   for (int k = T1; k >= 2; --k) {
     __syncthreads();
-    const float* Pk1 = a.pk + ((size_t)b * T1 + (k - 2)) * kD * kD;
-    for (int e = t; e < kD * kD; e += kAdjThreads) Pp[(e >> 6) * kR + (e & 63)] = Pk1[e];
+    load_mat_padded(Pp, a.pk + ((size_t)b * T1 + (k - 2)) * kD * kD);
     __syncthreads();
-    const float* dPk = dP + (size_t)(k - 1) * kD * kD;
-    float up[kX];
+    const float* dPk = dP + (size_t)(k - 1) * kD * kR;
+    dm = tile_mm<true>(dPk + r0 * kR, Pp, ct, dm);                   // dP_k P_(k-1)^T
+    const f32x4 up = tile_mm<false>(MT + r0 * kR, dPk, ct, f32x4{});  // M^T dP_k
+    float* dPm = dP + (size_t)(k - 2) * kD * kR;
 #pragma unroll
-    for (int x = 0; x < kX; ++x) {
-      const int e = t + kAdjThreads * x, r = e >> 6, c = e & 63;
-      float v = 0.f, u = 0.f;
-      for (int j = 0; j < kD; ++j) {
-        v += dPk[r * kD + j] * Pp[c * kR + j];   // (dP_k P_(k-1)^T)[r][c]
-        u += Ms[j * kD + r] * dPk[j * kD + c];    // (M^T dP_k)[r][c]
-      }
-      dM[x] += v;
-      up[x] = u;
-    }
-    __syncthreads();
-    float* dPm = dP + (size_t)(k - 2) * kD * kD;
-#pragma unroll
-    for (int x = 0; x < kX; ++x) dPm[t + kAdjThreads * x] += up[x];
+    for (int e = 0; e < 4; ++e) dPm[(r0 + 4 * lk + e) * kR + 16 * ct + li] += up[e];
   }
   __syncthreads();
 #pragma unroll
-  for (int x = 0; x < kX; ++x) {
-    const int e = t + kAdjThreads * x;
-    dMo[e] = dM[x];
-    dKVo[e] = dP[e];
-  }
+  for (int e = 0; e < 4; ++e) dMo[(r0 + 4 * lk + e) * kD + 16 * ct + li] = dm[e];
+  for (int e = t; e < kD * kD; e += kAdjThreads) dKVo[e] = dP[(e / kD) * kR + e % kD];
 }
 
 // Pass B: dz_i = -r_i^2 (a_i + phi(K_i)^T dM phi(Q_i)) (kept in tok[i].w) and
@@ -480,6 +492,14 @@ __global__ __launch_bounds__(kTT) void bwd_token_b(BwdArgs a) {
     for (int g = 0; g < kG; ++g) v += red[g * kD + t];
     a.ds_part[((size_t)b * a.nblk + blk) * kD + t] = v;
   }
+  // dalpha[h] = sum of the slices' shares over the batch: one wave per head.
+  if (b == 0 && blk == 0)
+    for (int h = t / 64; h < a.heads; h += kTT / 64) {
+      float v = 0.f;
+      for (int bb = t % 64; bb < a.BH / a.heads; bb += 64) v += a.da_slice[(size_t)bb * a.heads + h];
+      v = wave_sum(v);
+      if (t % 64 == 0) a.dalpha[h] = v;
+    }
 }
 
 // dQ_i = (r_i dQt_i + dz_i s) [Q_i > 0] + sum_j dz_ij k_j / 8, with
@@ -546,18 +566,25 @@ __global__ __launch_bounds__(kTT) void bwd_token_q(BwdArgs a) {
   for (int j = 0; j < 9; ++j) {
     const int c = window_cell(a, row, col, j);
     if (c < 0) continue;
-    const S* kj = Kb + (size_t)c * kD;
-    const float p = __expf(dot64(kj, f0, q) * kRs - tp.x) / tp.y;
-    const float g = p * ((1.f - alpha) * dot64(Vb + (size_t)c * kD, f0, x) - tp.z);
-    axpy16(g * kRs, kj, f0, dqt);
+    float kc[kF];
+    load16(Kb + (size_t)c * kD, f0, kc);
+    float zq = 0.f;
+#pragma unroll
+    for (int e = 0; e < kF; ++e) zq += kc[e] * q[e];
+    const float p = __expf(quad_sum(zq) * kRs - tp.x) / tp.y;
+    const float g = p * ((1.f - alpha) * dot64(Vb + (size_t)c * kD, f0, x) - tp.z) * kRs;
+#pragma unroll
+    for (int e = 0; e < kF; ++e) dqt[e] += g * kc[e];
   }
   store16(static_cast<S*>(a.dQ) + (base + i) * kD, f0, dqt);
 }
 
-// dK_j = (dM Qt_j + dKV V_j + ds) [K_j > 0] + sum_i dz_ij q_i / 8 over the
-// centres i whose window holds j (the window relation is symmetric).
+// dK_j = (dM Qt_j + dKV V_j + ds) [K_j > 0] + sum_i dz_ij q_i / 8 and
+// dV_j = w_0(j) alpha dY_j + dKV^T phi(K_j) + sum_i p_ij (1 - alpha) dY_i,
+// the local sums over the centres i whose window holds j (the window
+// relation is symmetric); both share p_ij and the rows q_i, dY_i.
 template <class S>
-__global__ __launch_bounds__(kTT) void bwd_token_k(BwdArgs a) {
+__global__ __launch_bounds__(kTT) void bwd_token_kv(BwdArgs a) {
   __shared__ float dMs[kD * kR];
   __shared__ float dKVs[kD * kR];
   __shared__ float s_sh[kD];
@@ -578,17 +605,18 @@ __global__ __launch_bounds__(kTT) void bwd_token_k(BwdArgs a) {
   load_mat_padded(dKVs, a.dmkv + (size_t)b * 2 * kD * kD + kD * kD);
   if (t < kD) {
     s_sh[t] = a.fin_s[(size_t)b * kD + t];
-    float v = 0.f;
-    for (int p = 0; p < a.nblk; ++p) v += a.ds_part[((size_t)b * a.nblk + p) * kD + t];
-    ds_sh[t] = v;
+    ds_sh[t] = sum_in_order(a.ds_part + (size_t)b * a.nblk * kD + t, kD, a.nblk);
+  }
+  float x[kF], kr[kF];
+  if (on) {
+    load16(Qb + (size_t)i * kD, f0, x);
+    load16(Kb + (size_t)i * kD, f0, kr);
+  } else {
+#pragma unroll
+    for (int e = 0; e < kF; ++e) x[e] = kr[e] = 0.f;
   }
   __syncthreads();
-  // Rows Qt_j dM^T + V_j dKV^T.
-  float x[kF];
-  if (on) load16(Qb + (size_t)i * kD, f0, x);
-  else
-#pragma unroll
-    for (int e = 0; e < kF; ++e) x[e] = 0.f;
+  // Rows Qt_j dM^T + V_j dKV^T (dK's global part) and phi(K_j) dKV (dV's).
   float den = 0.f;
 #pragma unroll
   for (int e = 0; e < kF; ++e) {
@@ -599,103 +627,72 @@ __global__ __launch_bounds__(kTT) void bwd_token_k(BwdArgs a) {
 #pragma unroll
   for (int e = 0; e < kF; ++e) rows[tk * kR + f0 + e] = x[e] * r;
   quad_lds_sync();
-  f32x4 acc[4] = {};
-  wave_mm<true>(wrows, dMs, 1.f, acc);
+  f32x4 acck[4] = {}, accv[4] = {};
+  wave_mm<true>(wrows, dMs, 1.f, acck);
   if (on) load16(Vb + (size_t)i * kD, f0, x);
   quad_lds_sync();
 #pragma unroll
   for (int e = 0; e < kF; ++e) rows[tk * kR + f0 + e] = x[e];
   quad_lds_sync();
-  wave_mm<true>(wrows, dKVs, 1.f, acc);
-  float g16[kF];
-  acc_to_quad(acc, wrows, tw, f0, g16);
-  if (!on) return;  // no barrier follows
-  float kr[kF], dk[kF];
-  load16(Kb + (size_t)i * kD, f0, kr);
-#pragma unroll
-  for (int e = 0; e < kF; ++e) dk[e] = kr[e] > 0.f ? g16[e] + ds_sh[f0 + e] : 0.f;
-  // Local: token i as the neighbour of centre c.
-  const int row = i / a.W, col = i % a.W;
-#pragma unroll 1
-  for (int j = 0; j < 9; ++j) {
-    const int c = window_cell(a, row, col, j);
-    if (c < 0) continue;
-    const float4 tc = a.tok[base + c];
-    const S* qc = Qb + (size_t)c * kD;
-    const float p = __expf(dot64(qc, f0, kr) * kRs - tc.x) / tc.y;
-    const float g = p * ((1.f - alpha) * dot64(dYb + (size_t)c * kD, f0, x) - tc.z);
-    axpy16(g * kRs, qc, f0, dk);
-  }
-  store16(static_cast<S*>(a.dK) + (base + i) * kD, f0, dk);
-}
-
-// dV_j = w_0(j) alpha dY_j + dKV^T phi(K_j) + sum_i p_ij (1 - alpha) dY_i.
-template <class S>
-__global__ __launch_bounds__(kTT) void bwd_token_v(BwdArgs a) {
-  __shared__ float dKVs[kD * kR];
-  __shared__ float rows[kBT * kR];
-  const int b = blockIdx.y, t = threadIdx.x, blk = blockIdx.x;
-  const int tk = t / kQ, qd = t % kQ, f0 = qd * kF, tw = tk % 16;
-  float* wrows = rows + (t / 64) * 16 * kR;
-  const int i = blk * kBT + tk;
-  const bool on = i < a.n;
-  const size_t base = (size_t)b * a.n;
-  const float alpha = a.alpha[b % a.heads];
-  const S* Qb = static_cast<const S*>(a.Q) + base * kD;
-  const S* Kb = static_cast<const S*>(a.K) + base * kD;
-  const S* dYb = static_cast<const S*>(a.dY) + base * kD;
-  load_mat_padded(dKVs, a.dmkv + (size_t)b * 2 * kD * kD + kD * kD);
-  float kr[kF];
-  if (on) load16(Kb + (size_t)i * kD, f0, kr);
-  else
-#pragma unroll
-    for (int e = 0; e < kF; ++e) kr[e] = 0.f;
+  wave_mm<true>(wrows, dKVs, 1.f, acck);
+  quad_lds_sync();
 #pragma unroll
   for (int e = 0; e < kF; ++e) rows[tk * kR + f0 + e] = fmaxf(kr[e], 0.f);
-  __syncthreads();
-  // Rows phi(K_j) dKV.
-  f32x4 acc[4] = {};
-  wave_mm<false>(wrows, dKVs, 1.f, acc);
-  float dv[kF];
-  acc_to_quad(acc, wrows, tw, f0, dv);
+  quad_lds_sync();
+  wave_mm<false>(wrows, dKVs, 1.f, accv);
+  float dk[kF], dv[kF];
+  acc_to_quad(acck, wrows, tw, f0, dk);
+  acc_to_quad(accv, wrows, tw, f0, dv);
   if (!on) return;  // no barrier follows
-  float dy[kF];
-  load16(dYb + (size_t)i * kD, f0, dy);
-  const float w0 = alpha * wgt(a, base + i, 0);
 #pragma unroll
-  for (int e = 0; e < kF; ++e) dv[e] += w0 * dy[e];
+  for (int e = 0; e < kF; ++e) dk[e] = kr[e] > 0.f ? dk[e] + ds_sh[f0 + e] : 0.f;
+  {
+    float dy[kF];
+    load16(dYb + (size_t)i * kD, f0, dy);
+    const float w0 = alpha * wgt(a, base + i, 0);
+#pragma unroll
+    for (int e = 0; e < kF; ++e) dv[e] += w0 * dy[e];
+  }
+  // Local: token i as the neighbour of centre c (x holds V_i).
   const int row = i / a.W, col = i % a.W;
 #pragma unroll 1
   for (int j = 0; j < 9; ++j) {
     const int c = window_cell(a, row, col, j);
     if (c < 0) continue;
     const float4 tc = a.tok[base + c];
-    const float p = __expf(dot64(Qb + (size_t)c * kD, f0, kr) * kRs - tc.x) / tc.y;
-    axpy16(p * (1.f - alpha), dYb + (size_t)c * kD, f0, dv);
+    float qc[kF], yc[kF];
+    load16(Qb + (size_t)c * kD, f0, qc);
+    load16(dYb + (size_t)c * kD, f0, yc);
+    float zq = 0.f, zy = 0.f;
+#pragma unroll
+    for (int e = 0; e < kF; ++e) {
+      zq += qc[e] * kr[e];
+      zy += yc[e] * x[e];
+    }
+    const float p = __expf(quad_sum(zq) * kRs - tc.x) / tc.y;
+    const float g = p * ((1.f - alpha) * quad_sum(zy) - tc.z) * kRs;
+    const float pv = p * (1.f - alpha);
+#pragma unroll
+    for (int e = 0; e < kF; ++e) {
+      dk[e] += g * qc[e];
+      dv[e] += pv * yc[e];
+    }
   }
+  store16(static_cast<S*>(a.dK) + (base + i) * kD, f0, dk);
   store16(static_cast<S*>(a.dV) + (base + i) * kD, f0, dv);
-}
-
-// dalpha[h] = sum over the batch of the slices' shares, in batch order.
-__global__ __launch_bounds__(256) void bwd_dalpha(BwdArgs a) {
-  for (int h = threadIdx.x; h < a.heads; h += blockDim.x) {
-    float v = 0.f;
-    for (int b = h; b < a.BH; b += a.heads) v += a.da_slice[b];
-    a.dalpha[h] = v;
-  }
 }
 
 template <class S>
 hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
   const size_t lds_a = (size_t)(kD * kR + kD + 2 * kBT * kR + kBT * kW + kBT) * sizeof(float);
   const int T1 = a.T - 1 > 0 ? a.T - 1 : 1;
-  const size_t lds_adj = ((size_t)T1 * kD * kD + kD * kD + kD * kR) * sizeof(float);
+  const size_t lds_adj = ((size_t)T1 + 2) * kD * kR * sizeof(float);
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_token_a<S>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_a);
     if (e != hipSuccess) return e;
-    const size_t lds_adj_max = ((size_t)(kMaxT - 1) * kD * kD + kD * kD + kD * kR) * sizeof(float);
+    const size_t lds_adj_max = ((size_t)kMaxT + 1) * kD * kR * sizeof(float);
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_adjoint),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_adj_max);
     if (e != hipSuccess) return e;
@@ -704,15 +701,10 @@ hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
   const dim3 tok(a.nblk, a.BH);
   if (a.T >= 2) hipLaunchKernelGGL(bwd_powers, dim3(a.BH), dim3(kAdjThreads), 0, s, a);
   hipLaunchKernelGGL(bwd_token_a<S>, tok, dim3(kTT), lds_a, s, a);
-  if (a.T >= 2)
-    hipLaunchKernelGGL(bwd_reduce_dp, dim3((T1 * kD * kD + kAdjThreads - 1) / kAdjThreads, a.BH),
-                       dim3(kAdjThreads), 0, s, a);
   hipLaunchKernelGGL(bwd_adjoint, dim3(a.BH), dim3(kAdjThreads), lds_adj, s, a);
   hipLaunchKernelGGL(bwd_token_b<S>, tok, dim3(kTT), 0, s, a);
   hipLaunchKernelGGL(bwd_token_q<S>, tok, dim3(kTT), 0, s, a);
-  hipLaunchKernelGGL(bwd_token_k<S>, tok, dim3(kTT), 0, s, a);
-  hipLaunchKernelGGL(bwd_token_v<S>, tok, dim3(kTT), 0, s, a);
-  hipLaunchKernelGGL(bwd_dalpha, dim3(1), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(bwd_token_kv<S>, tok, dim3(kTT), 0, s, a);
   return hipGetLastError();
 }
 

@@ -127,9 +127,9 @@ struct BwdArgs {
   const float* fin_m;     // [BH][64*64]
   float* pk;              // [BH][T-1][64*64]  P_k = M^(k-1) phi(K)^T V, k = 1..T-1
   float4* tok;            // [BH][n]  per token: local max, local sum, dL_i . L_i, then (a_i -> dz_i)
-  float* dp_part;         // [BH][nblk][T-1][64*64]  per-workgroup partials of dP_k (block 0: their sum)
+  float* dp_part;         // [BH][nblk][T-1][64*64]  per-workgroup partials of dP_k
   float* da_part;         // [BH][nblk]  partials of dalpha
-  float* da_slice;        // [BH]
+  float* da_slice;        // [BH]  their sums
   float* dmkv;            // [BH][2][64*64]  dM, dKV
   float* ds_part;         // [BH][nblk][64]  partials of ds
 };
