@@ -84,24 +84,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
-// Y += diag(sx) X M (kTr = false) or diag(sx) X M^T (kTr = true) for the
-// wave's 16 tokens: X their LDS rows (stride kR), M a 64 x 64 matrix in LDS
-// rows of kR floats, sx this lane's row scale (row li).  Y in accumulator
-// layout: acc[ct][e] = Y[4 lk + e][16 ct + li].  Features are taken in the
-// order 16 lk + kk, which keeps every operand read of the wave on 64
-// distinct banks (kR = 1 mod 64).
-template <bool kTr>
-__device__ __forceinline__ void wave_mm(const float* X, const float* M, float sx, f32x4 (&acc)[4]) {
-  const int ln = threadIdx.x % 64, li = ln % 16, lk = ln / 16;
-#pragma unroll 4
-  for (int kk = 0; kk < kD / 4; ++kk) {
-    const int f = 16 * lk + kk;
-    const float av = sx * X[li * kR + f];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-      acc[ct] = mfma16(av, kTr ? M[(16 * ct + li) * kR + f] : M[f * kR + 16 * ct + li], acc[ct]);
-  }
-}
 // One 16 x 16 block of X M (kTr = false) or X M^T (kTr = true): X the 16
 // rows (stride kR), column block ct; same operand order as wave_mm.
 template <bool kTr>
@@ -114,19 +96,141 @@ __device__ __forceinline__ f32x4 tile_mm(const float* X, const float* M, int ct,
   }
   return acc;
 }
-// Y from accumulator layout into the lane-quad layout through the wave's LDS
-// rows X (overwritten): lane (token tw of the wave, quarter f0) gets
-// Y[tw][f0 .. f0 + 15].
-__device__ __forceinline__ void acc_to_quad(const f32x4 (&acc)[4], float* X, int tw, int f0, float (&y)[kF]) {
+// ---------------------------------------------------------------------------
+// Token-row x matrix products of the token passes, per input type S.
+//
+// Each wave multiplies the rows of its 16 tokens (X, 16 x 64) by a 64 x 64
+// matrix staged in LDS "B-ready": Bt[n][k] is the term of output column n
+// and contraction index k, so Y = X M stages M^T and Y = X M^T stages M.
+// Y comes out in accumulator layout: acc[ct][e] = Y[4 lk + e][16 ct + li]
+// (lane 16 lk + li).
+//  * fp32 inputs: rows and matrix in fp32 (rows of kR floats), fp32 MFMA
+//    16x16x4, contraction order 16 lk + kk (every LDS read of a wave on 64
+//    distinct banks).
+//  * bf16 inputs: the token rows are exact bf16 values (phi(Q), phi(K), V,
+//    dY); the fp32 matrix is split into bf16 high and low parts
+//    (m = hi + lo + O(2^-17 m)) and Y = X hi + X lo on bf16 MFMA 16x16x32
+//    with fp32 sums: rows of kRB bf16, 8 contraction slots per lane.
+// ---------------------------------------------------------------------------
+constexpr int kRB = kD + 8;  // bf16 row (144 bytes: 16-byte aligned, conflict-free 16-byte reads)
+
+template <class S>
+struct RowsOf {
+  static constexpr bool kF32 = sizeof(S) == 4;
+  static constexpr int kRowBytes = kF32 ? kR * 4 : kRB * 2;
+  static constexpr int kBytes = kBT * kRowBytes;                          // all token rows
+  static constexpr int kMatBytes = kF32 ? kD * kR * 4 : 2 * kD * kRB * 2;  // one staged matrix
+};
+
+// Quad lane: features f0 .. f0 + 15 of token tk into the token rows.
+template <class S>
+__device__ __forceinline__ void put_row(unsigned char* rows, int tk, int f0, const float (&x)[kF]) {
+  if constexpr (RowsOf<S>::kF32) {
+    float* r = reinterpret_cast<float*>(rows) + tk * kR + f0;
+#pragma unroll
+    for (int e = 0; e < kF; ++e) r[e] = x[e];
+  } else {
+    uint16_t* r = reinterpret_cast<uint16_t*>(rows) + tk * kRB + f0;
+    u32x4 w[2];
+#pragma unroll
+    for (int e = 0; e < kF; e += 2) w[e / 8][(e % 8) / 2] = f2bf(x[e]) | ((uint32_t)f2bf(x[e + 1]) << 16);
+    reinterpret_cast<u32x4*>(r)[0] = w[0];
+    reinterpret_cast<u32x4*>(r)[1] = w[1];
+  }
+}
+
+// Whole workgroup: stage the 64 x 64 fp32 matrix src for Y = X src^T
+// (kTr) or Y = X src (!kTr).
+template <class S, bool kTr>
+__device__ __forceinline__ void stage_mat(unsigned char* dst, const float* src) {
+  for (int e = threadIdx.x * 4; e < kD * kD; e += blockDim.x * 4) {
+    const float4 v4 = *reinterpret_cast<const float4*>(src + e);
+    const float v[4] = {v4.x, v4.y, v4.z, v4.w};
+    const int r = e / kD, c = e % kD;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int at = kTr ? r * (RowsOf<S>::kF32 ? kR : kRB) + c + j : (c + j) * (RowsOf<S>::kF32 ? kR : kRB) + r;
+      if constexpr (RowsOf<S>::kF32) {
+        reinterpret_cast<float*>(dst)[at] = v[j];
+      } else {
+        const uint16_t hi = f2bf(v[j]);
+        reinterpret_cast<uint16_t*>(dst)[at] = hi;
+        reinterpret_cast<uint16_t*>(dst)[kD * kRB + at] = f2bf(v[j] - bf2f(hi));
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ f32x4 mfma16_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// acc += X Bt^T for the wave's 16 token rows X (the wave's part of the rows).
+template <class S>
+__device__ __forceinline__ void wave_mm(const unsigned char* X, const unsigned char* Bt, f32x4 (&acc)[4]) {
   const int ln = threadIdx.x % 64, li = ln % 16, lk = ln / 16;
-  quad_lds_sync();
+  if constexpr (RowsOf<S>::kF32) {
+    const float* x = reinterpret_cast<const float*>(X);
+    const float* m = reinterpret_cast<const float*>(Bt);
+#pragma unroll 4
+    for (int kk = 0; kk < kD / 4; ++kk) {
+      const int f = 16 * lk + kk;
+      const float av = x[li * kR + f];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct)
+      for (int ct = 0; ct < 4; ++ct) acc[ct] = mfma16(av, m[(16 * ct + li) * kR + f], acc[ct]);
+    }
+  } else {
+    const uint16_t* x = reinterpret_cast<const uint16_t*>(X);
+    const uint16_t* hi = reinterpret_cast<const uint16_t*>(Bt);
+    const uint16_t* lo = hi + kD * kRB;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) X[(4 * lk + e) * kR + 16 * ct + li] = acc[ct][e];
-  quad_lds_sync();
+    for (int h = 0; h < 2; ++h) {
+      const int f = 8 * lk + 32 * h;
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(x + li * kRB + f);
 #pragma unroll
-  for (int e = 0; e < kF; ++e) y[e] = X[tw * kR + f0 + e];
+      for (int ct = 0; ct < 4; ++ct) {
+        const int at = (16 * ct + li) * kRB + f;
+        acc[ct] = mfma16_bf16(av, *reinterpret_cast<const bf16x8*>(hi + at), acc[ct]);
+        acc[ct] = mfma16_bf16(av, *reinterpret_cast<const bf16x8*>(lo + at), acc[ct]);
+      }
+    }
+  }
+}
+
+// Y from accumulator layout into the lane-quad layout through the wave's
+// token rows X (overwritten): lane (token tw of the wave, quarter f0) gets
+// Y[tw][f0 .. f0 + 15].  bf16 rows are too small for 16 fp32 rows: there the
+// two column halves pass in turn through 16 rows of 33 floats.
+template <class S>
+__device__ __forceinline__ void acc_to_quad(const f32x4 (&acc)[4], unsigned char* X, int tw, int f0,
+                                            float (&y)[kF]) {
+  const int ln = threadIdx.x % 64, li = ln % 16, lk = ln / 16;
+  float* x = reinterpret_cast<float*>(X);
+  if constexpr (RowsOf<S>::kF32) {
+    quad_lds_sync();
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[(4 * lk + e) * kR + 16 * ct + li] = acc[ct][e];
+    quad_lds_sync();
+#pragma unroll
+    for (int e = 0; e < kF; ++e) y[e] = x[tw * kR + f0 + e];
+  } else {
+    constexpr int kH = 33;
+    static_assert(16 * kH * 4 <= 16 * kRB * 2, "half rows fit in the wave's bf16 rows");
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      quad_lds_sync();
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[(4 * lk + e) * kH + 16 * c2 + li] = acc[2 * h + c2][e];
+      quad_lds_sync();
+      if (f0 / 32 == h)
+#pragma unroll
+        for (int e = 0; e < kF; ++e) y[e] = x[tw * kH + f0 % 32 + e];
+    }
+  }
 }
 
 // Sum over the wave (butterfly of fixed shape: the same order every run).
@@ -428,17 +532,20 @@ __global__ __launch_bounds__(kAdjThreads) void bwd_adjoint(BwdArgs a) {
 template <class S>
 __global__ __launch_bounds__(kTT) void bwd_token_b(BwdArgs a) {
   constexpr int kG = kTT / kD;  // partial sums per feature in the ds reduction
-  __shared__ float dMs[kD * kR];
+  using RS = RowsOf<S>;
+  __shared__ __align__(16) unsigned char dMs[RS::kMatBytes];
   __shared__ float s_sh[kD];
-  __shared__ float rows[kBT * kR];
+  __shared__ __align__(16) float rows[kBT * kR];  // fp32 rows for ds; first the MFMA token rows
   __shared__ float red[kG * kD];
+  static_assert(RS::kBytes <= (int)sizeof(rows), "MFMA token rows fit");
   const int b = blockIdx.y, t = threadIdx.x, blk = blockIdx.x;
   const int tk = t / kQ, qd = t % kQ, f0 = qd * kF, tw = tk % 16;
-  float* wrows = rows + (t / 64) * 16 * kR;  // this wave's 16 token rows
+  unsigned char* trows = reinterpret_cast<unsigned char*>(rows);
+  unsigned char* wrows = trows + (t / 64) * 16 * RS::kRowBytes;  // this wave's 16 token rows
   const int i = blk * kBT + tk;
   const bool on = i < a.n;
   const size_t base = (size_t)b * a.n;
-  load_mat_padded(dMs, a.dmkv + (size_t)b * 2 * kD * kD);
+  stage_mat<S, false>(dMs, a.dmkv + (size_t)b * 2 * kD * kD);
   if (t < kD) s_sh[t] = a.fin_s[(size_t)b * kD + t];
   float u[kF], kp[kF];
   if (on) {
@@ -449,7 +556,8 @@ __global__ __launch_bounds__(kTT) void bwd_token_b(BwdArgs a) {
     for (int e = 0; e < kF; ++e) u[e] = kp[e] = 0.f;
   }
 #pragma unroll
-  for (int e = 0; e < kF; ++e) rows[tk * kR + f0 + e] = fmaxf(kp[e], 0.f);
+  for (int e = 0; e < kF; ++e) kp[e] = fmaxf(kp[e], 0.f);
+  put_row<S>(trows, tk, f0, kp);
   __syncthreads();
   float den = 0.f;
 #pragma unroll
@@ -460,9 +568,9 @@ __global__ __launch_bounds__(kTT) void bwd_token_b(BwdArgs a) {
   const float r = 1.f / (quad_sum(den) + a.eps);
   // phi(K_i)^T dM phi(Q_i): the row phi(K_i) dM, dotted with phi(Q_i).
   f32x4 acc[4] = {};
-  wave_mm<false>(wrows, dMs, 1.f, acc);
+  wave_mm<S>(wrows, dMs, acc);
   float y[kF];
-  acc_to_quad(acc, wrows, tw, f0, y);
+  acc_to_quad<S>(acc, wrows, tw, f0, y);
   float bil = 0.f;
 #pragma unroll
   for (int e = 0; e < kF; ++e) bil += y[e] * u[e];
@@ -507,13 +615,14 @@ __global__ __launch_bounds__(kTT) void bwd_token_b(BwdArgs a) {
 // of window slot j.
 template <class S>
 __global__ __launch_bounds__(kTT) void bwd_token_q(BwdArgs a) {
-  __shared__ float Ps[kD * kR];
-  __shared__ float dMs[kD * kR];
+  using RS = RowsOf<S>;
+  __shared__ __align__(16) unsigned char Ps[RS::kMatBytes];
+  __shared__ __align__(16) unsigned char dMs[RS::kMatBytes];
   __shared__ float s_sh[kD];
-  __shared__ float rows[kBT * kR];
+  __shared__ __align__(16) unsigned char trows[RS::kBytes];
   const int b = blockIdx.y, t = threadIdx.x, blk = blockIdx.x;
   const int tk = t / kQ, qd = t % kQ, f0 = qd * kF, tw = tk % 16;
-  float* wrows = rows + (t / 64) * 16 * kR;
+  unsigned char* wrows = trows + (t / 64) * 16 * RS::kRowBytes;
   const int i = blk * kBT + tk;
   const bool on = i < a.n;
   const size_t base = (size_t)b * a.n;
@@ -522,7 +631,7 @@ __global__ __launch_bounds__(kTT) void bwd_token_q(BwdArgs a) {
   const S* Kb = static_cast<const S*>(a.K) + base * kD;
   const S* Vb = static_cast<const S*>(a.V) + base * kD;
   const S* dYb = static_cast<const S*>(a.dY) + base * kD;
-  load_mat_padded(dMs, a.dmkv + (size_t)b * 2 * kD * kD);
+  stage_mat<S, false>(dMs, a.dmkv + (size_t)b * 2 * kD * kD);
   if (t < kD) s_sh[t] = a.fin_s[(size_t)b * kD + t];
   float x[kF];
   if (on) load16(Kb + (size_t)i * kD, f0, x);
@@ -530,26 +639,36 @@ __global__ __launch_bounds__(kTT) void bwd_token_q(BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < kF; ++e) x[e] = 0.f;
 #pragma unroll
-  for (int e = 0; e < kF; ++e) rows[tk * kR + f0 + e] = fmaxf(x[e], 0.f);
+  for (int e = 0; e < kF; ++e) x[e] = fmaxf(x[e], 0.f);
+  put_row<S>(trows, tk, f0, x);
   __syncthreads();
   // dQt rows: phi(K) dM, then + sum_k diag(alpha w_k) dY P_k^T.
   f32x4 acc[4] = {};
-  wave_mm<false>(wrows, dMs, 1.f, acc);
+  wave_mm<S>(wrows, dMs, acc);
   if (on) load16(dYb + (size_t)i * kD, f0, x);
-  quad_lds_sync();
+  else
 #pragma unroll
-  for (int e = 0; e < kF; ++e) rows[tk * kR + f0 + e] = x[e];
+    for (int e = 0; e < kF; ++e) x[e] = 0.f;
+  quad_lds_sync();
+  put_row<S>(trows, tk, f0, x);
   const int T1 = a.T - 1;
-  // The MFMA A operand row of this lane: token 16 (t / 64) + li.
-  const int ia = blk * kBT + (t / 64) * 16 + (t % 16);
+  // Accumulator rows 4 lk + e of this lane: tokens ib + e.
+  const int ib = blk * kBT + (t / 64) * 16 + 4 * ((t % 64) / 16);
   for (int k = 1; k <= T1; ++k) {
     __syncthreads();
-    load_mat_padded(Ps, a.pk + ((size_t)b * T1 + (k - 1)) * kD * kD);
+    stage_mat<S, true>(Ps, a.pk + ((size_t)b * T1 + (k - 1)) * kD * kD);
     __syncthreads();
-    wave_mm<true>(wrows, Ps, ia < a.n ? alpha * wgt(a, base + ia, k) : 0.f, acc);
+    f32x4 y[4] = {};
+    wave_mm<S>(wrows, Ps, y);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float f = ib + e < a.n ? alpha * wgt(a, base + ib + e, k) : 0.f;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) acc[ct][e] += f * y[ct][e];
+    }
   }
   float dqt[kF];
-  acc_to_quad(acc, wrows, tw, f0, dqt);
+  acc_to_quad<S>(acc, wrows, tw, f0, dqt);
   if (!on) return;  // no barrier follows
   const float4 tp = a.tok[base + i];  // m_i, Z_i, c_i, dz_i
   float q[kF];
@@ -585,14 +704,16 @@ __global__ __launch_bounds__(kTT) void bwd_token_q(BwdArgs a) {
 // relation is symmetric); both share p_ij and the rows q_i, dY_i.
 template <class S>
 __global__ __launch_bounds__(kTT) void bwd_token_kv(BwdArgs a) {
-  __shared__ float dMs[kD * kR];
-  __shared__ float dKVs[kD * kR];
+  using RS = RowsOf<S>;
+  __shared__ __align__(16) unsigned char dMs[RS::kMatBytes];    // for phi(Q) dM^T
+  __shared__ __align__(16) unsigned char dKVt[RS::kMatBytes];   // for V dKV^T
+  __shared__ __align__(16) unsigned char dKVs[RS::kMatBytes];   // for phi(K) dKV
   __shared__ float s_sh[kD];
   __shared__ float ds_sh[kD];
-  __shared__ float rows[kBT * kR];
+  __shared__ __align__(16) unsigned char trows[RS::kBytes];
   const int b = blockIdx.y, t = threadIdx.x, blk = blockIdx.x;
   const int tk = t / kQ, qd = t % kQ, f0 = qd * kF, tw = tk % 16;
-  float* wrows = rows + (t / 64) * 16 * kR;
+  unsigned char* wrows = trows + (t / 64) * 16 * RS::kRowBytes;
   const int i = blk * kBT + tk;
   const bool on = i < a.n;
   const size_t base = (size_t)b * a.n;
@@ -601,8 +722,10 @@ __global__ __launch_bounds__(kTT) void bwd_token_kv(BwdArgs a) {
   const S* Kb = static_cast<const S*>(a.K) + base * kD;
   const S* Vb = static_cast<const S*>(a.V) + base * kD;
   const S* dYb = static_cast<const S*>(a.dY) + base * kD;
-  load_mat_padded(dMs, a.dmkv + (size_t)b * 2 * kD * kD);
-  load_mat_padded(dKVs, a.dmkv + (size_t)b * 2 * kD * kD + kD * kD);
+  const float* dM = a.dmkv + (size_t)b * 2 * kD * kD;
+  stage_mat<S, true>(dMs, dM);
+  stage_mat<S, true>(dKVt, dM + kD * kD);
+  stage_mat<S, false>(dKVs, dM + kD * kD);
   if (t < kD) {
     s_sh[t] = a.fin_s[(size_t)b * kD + t];
     ds_sh[t] = sum_in_order(a.ds_part + (size_t)b * a.nblk * kD + t, kD, a.nblk);
@@ -615,34 +738,42 @@ __global__ __launch_bounds__(kTT) void bwd_token_kv(BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < kF; ++e) x[e] = kr[e] = 0.f;
   }
+#pragma unroll
+  for (int e = 0; e < kF; ++e) x[e] = fmaxf(x[e], 0.f);
+  put_row<S>(trows, tk, f0, x);
   __syncthreads();
-  // Rows Qt_j dM^T + V_j dKV^T (dK's global part) and phi(K_j) dKV (dV's).
+  // Rows Qt_j dM^T + V_j dKV^T (dK's global part) and phi(K_j) dKV (dV's);
+  // Qt_j = r_j phi(Q_j), with r_j applied to the product.
   float den = 0.f;
 #pragma unroll
-  for (int e = 0; e < kF; ++e) {
-    x[e] = fmaxf(x[e], 0.f);
-    den += x[e] * s_sh[f0 + e];
-  }
+  for (int e = 0; e < kF; ++e) den += x[e] * s_sh[f0 + e];
   const float r = 1.f / (quad_sum(den) + a.eps);
-#pragma unroll
-  for (int e = 0; e < kF; ++e) rows[tk * kR + f0 + e] = x[e] * r;
-  quad_lds_sync();
-  f32x4 acck[4] = {}, accv[4] = {};
-  wave_mm<true>(wrows, dMs, 1.f, acck);
+  f32x4 accq[4] = {}, acck[4] = {}, accv[4] = {};
+  wave_mm<S>(wrows, dMs, accq);
   if (on) load16(Vb + (size_t)i * kD, f0, x);
   quad_lds_sync();
+  put_row<S>(trows, tk, f0, x);
+  quad_lds_sync();
+  wave_mm<S>(wrows, dKVt, acck);
+  {
+    const int lk = (t % 64) / 16;
 #pragma unroll
-  for (int e = 0; e < kF; ++e) rows[tk * kR + f0 + e] = x[e];
-  quad_lds_sync();
-  wave_mm<true>(wrows, dKVs, 1.f, acck);
-  quad_lds_sync();
+    for (int e = 0; e < 4; ++e) {
+      const float re = __shfl(r, 4 * (4 * lk + e));  // r of accumulator row 4 lk + e
 #pragma unroll
-  for (int e = 0; e < kF; ++e) rows[tk * kR + f0 + e] = fmaxf(kr[e], 0.f);
+      for (int ct = 0; ct < 4; ++ct) acck[ct][e] += re * accq[ct][e];
+    }
+  }
+  float kp[kF];
+#pragma unroll
+  for (int e = 0; e < kF; ++e) kp[e] = fmaxf(kr[e], 0.f);
   quad_lds_sync();
-  wave_mm<false>(wrows, dKVs, 1.f, accv);
+  put_row<S>(trows, tk, f0, kp);
+  quad_lds_sync();
+  wave_mm<S>(wrows, dKVs, accv);
   float dk[kF], dv[kF];
-  acc_to_quad(acck, wrows, tw, f0, dk);
-  acc_to_quad(accv, wrows, tw, f0, dv);
+  acc_to_quad<S>(acck, wrows, tw, f0, dk);
+  acc_to_quad<S>(accv, wrows, tw, f0, dv);
   if (!on) return;  // no barrier follows
 #pragma unroll
   for (int e = 0; e < kF; ++e) dk[e] = kr[e] > 0.f ? dk[e] + ds_sh[f0 + e] : 0.f;
