@@ -311,15 +311,46 @@ __global__ __launch_bounds__(kAdjThreads) void bwd_powers(BwdArgs a) {
 // Pass A: per token the local window statistics, dY . V_i, dY . (Qt_i P_k),
 // the weight gradients and dalpha's share; per workgroup the partial sums of
 // dP_k = sum_i w_k(i) alpha Qt_i^T dY_i.
+//
+// fp32 inputs: both contractions on fp32 MFMA 16x16x4 from token rows of kR
+// floats, in a term order (features 16 lk + kk, tokens
+// 64 (kk / 16) + 16 lk + kk % 16) that keeps every operand read of a wave on
+// 64 distinct banks.
+// bf16 inputs: phi(Q) and dY are exact bf16 values, kept feature-major
+// (kTS tokens per feature row) so that a lane's 8 contraction slots over
+// tokens are one 16-byte read.  dY . (Qt_i P_k) = r_i dY_i . (phi(Q_i) P_k)
+// with P_k split into bf16 high and low parts; dP_k's operand
+// alpha w_k(i) r_i phi(Q_i) is formed per k and split the same way, against
+// the exact dY.  Both on bf16 MFMA 16x16x32 with fp32 sums.
+constexpr int kTS = kBT + 8;  // bf16 feature-major row: 528 bytes, 16-byte reads conflict-free
+
+template <class S>
+constexpr size_t token_a_lds() {
+  if constexpr (sizeof(S) == 4)
+    return (size_t)(kD * kR + kD + 2 * kBT * kR + kBT * kW + kBT) * sizeof(float);
+  else
+    return (size_t)4 * kD * kTS * 2 + RowsOf<S>::kMatBytes + ((kMaxT - 1) * kBT + kD + kBT) * sizeof(float);
+}
+
 template <class S>
 __global__ __launch_bounds__(kTT) void bwd_token_a(BwdArgs a) {
   extern __shared__ __align__(16) float sm[];
-  float* Ps = sm;                        // kD rows of kR: P_k
-  float* s_sh = Ps + kD * kR;            // kD
-  float* qt_sh = s_sh + kD;              // kBT rows of Qt (padded)
-  float* dy_sh = qt_sh + kBT * kR;       // kBT rows of dY (padded)
-  float* w_sh = dy_sh + kBT * kR;        // kBT rows of kW weights
-  float* red = w_sh + kBT * kW;          // kBT
+  constexpr bool kF32 = RowsOf<S>::kF32;
+  // fp32 layout: P_k, Qt rows, dY rows, weights.
+  float* Ps = sm;
+  float* qt_sh = Ps + kD * kR;
+  float* dy_sh = qt_sh + kBT * kR;
+  float* w_sh = dy_sh + kBT * kR;
+  // bf16 layout: split alpha w_k r phi(Q) (high, low), phi(Q), dY (all
+  // feature-major), P_k staged, per-token scales alpha w_k r.
+  uint16_t* sqh = reinterpret_cast<uint16_t*>(sm);
+  uint16_t* sql = sqh + kD * kTS;
+  uint16_t* qT = sql + kD * kTS;
+  uint16_t* dyT = qT + kD * kTS;
+  unsigned char* Pst = reinterpret_cast<unsigned char*>(dyT + kD * kTS);
+  float* stab = reinterpret_cast<float*>(Pst + RowsOf<S>::kMatBytes);
+  float* s_sh = kF32 ? w_sh + kBT * kW : stab + (kMaxT - 1) * kBT;  // kD
+  float* red = s_sh + kD;                                             // kBT
   const int b = blockIdx.y, t = threadIdx.x, blk = blockIdx.x;
   const int tk = t / kQ, qd = t % kQ, f0 = qd * kF;
   const int i = blk * kBT + tk;
@@ -331,8 +362,12 @@ __global__ __launch_bounds__(kTT) void bwd_token_a(BwdArgs a) {
   const S* Vb = static_cast<const S*>(a.V) + base * kD;
   const S* dYb = static_cast<const S*>(a.dY) + base * kD;
   if (t < kD) s_sh[t] = a.fin_s[(size_t)b * kD + t];
-  if (qd == 0)
-    for (int k = 0; k < kMaxT; ++k) w_sh[tk * kW + k] = (on && k < a.T) ? wgt(a, base + i, k) : 0.f;
+  float wk[kMaxT];
+#pragma unroll
+  for (int k = 0; k < kMaxT; ++k) wk[k] = (on && k < a.T) ? wgt(a, base + i, k) : 0.f;
+  if (kF32 && qd == 0)
+#pragma unroll
+    for (int k = 0; k < kMaxT; ++k) w_sh[tk * kW + k] = wk[k];
 
   float q[kF], dy[kF];
   float m = 0.f, Z = 1.f, dyL = 0.f, dyv = 0.f;
@@ -366,7 +401,7 @@ __global__ __launch_bounds__(kTT) void bwd_token_a(BwdArgs a) {
     for (int e = 0; e < kF; ++e) q[e] = dy[e] = 0.f;
   }
   __syncthreads();  // s_sh, w_sh
-  // Qt_i = r_i phi(Q_i).
+  // r_i = 1 / (phi(Q_i) . s + eps).
   float den = 0.f;
 #pragma unroll
   for (int e = 0; e < kF; ++e) {
@@ -374,72 +409,160 @@ __global__ __launch_bounds__(kTT) void bwd_token_a(BwdArgs a) {
     den += q[e] * s_sh[f0 + e];
   }
   const float r = 1.f / (quad_sum(den) + a.eps);
-#pragma unroll
-  for (int e = 0; e < kF; ++e) {
-    q[e] *= r;
-    qt_sh[tk * kR + f0 + e] = q[e];
-    dy_sh[tk * kR + f0 + e] = dy[e];
-  }
   float dyy[kMaxT];
 #pragma unroll
   for (int k = 0; k < kMaxT; ++k) dyy[k] = 0.f;
   const int T1 = a.T - 1;
   // MFMA roles: wave wv holds tokens 16 wv .. 16 wv + 15 (its quads) and the
-  // 16 x 16 block (ga, gc) of dP_k; lane ln = 16 lk + li.  The contractions
-  // take their terms in an order (features 16 lk + kk, tokens
-  // 64 (kk / 16) + 16 lk + kk % 16) under which every LDS operand read of a
-  // wave hits 64 distinct banks (row stride kR = 1 mod 64).
+  // 16 x 16 block (ga, gc) of dP_k; lane ln = 16 lk + li.
   const int wv = t / 64, ln = t % 64, li = ln % 16, lk = ln / 16;
   const int ga = 16 * (wv / 4), gc = 16 * (wv % 4);
+  if constexpr (kF32) {
 #pragma unroll
-  for (int k = 1; k < kMaxT; ++k) {
-    if (k > T1) break;
-    __syncthreads();
-    load_mat_padded(Ps, a.pk + ((size_t)b * T1 + (k - 1)) * kD * kD);
-    __syncthreads();
-    // dY_i . (Qt_i P_k): X = Qt P_k for the wave's 16 tokens (4 column
-    // blocks), then each row dotted with dY_i.
-    {
-      f32x4 x[4] = {};
-#pragma unroll 4
-      for (int kk = 0; kk < kD / 4; ++kk) {
-        const int f = 16 * lk + kk;
-        const float av = qt_sh[(16 * wv + li) * kR + f];
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) x[ct] = mfma16(av, Ps[f * kR + 16 * ct + li], x[ct]);
-      }
-      float part[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float* dyr = dy_sh + (16 * wv + 4 * lk + e) * kR + li;
-        float v = 0.f;
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) v += x[ct][e] * dyr[16 * ct];
-        part[e] = group_sum16(v);
-      }
-      // This lane's token 16 wv + ln / 4 is row 4 lk + li / 4 of the block.
-      const int e = li / 4;
-      dyy[k] = e == 0 ? part[0] : e == 1 ? part[1] : e == 2 ? part[2] : part[3];
+    for (int e = 0; e < kF; ++e) {
+      qt_sh[tk * kR + f0 + e] = q[e] * r;
+      dy_sh[tk * kR + f0 + e] = dy[e];
     }
-    // This workgroup's share of dP_k = sum_i alpha w_k(i) Qt_i^T dY_i.
-    {
-      f32x4 acc = {};
-#pragma unroll 8
-      for (int kk = 0; kk < kBT / 4; ++kk) {
-        const int tt = 64 * (kk / 16) + 16 * lk + kk % 16;
-        acc = mfma16(w_sh[tt * kW + k] * qt_sh[tt * kR + ga + li], dy_sh[tt * kR + gc + li], acc);
-      }
-      float* dst = a.dp_part + (((size_t)b * a.nblk + blk) * T1 + (k - 1)) * kD * kD;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dst[(ga + 4 * lk + e) * kD + gc + li] = alpha * acc[e];
+    for (int k = 1; k < kMaxT; ++k) {
+      if (k > T1) break;
+      __syncthreads();
+      load_mat_padded(Ps, a.pk + ((size_t)b * T1 + (k - 1)) * kD * kD);
+      __syncthreads();
+      // dY_i . (Qt_i P_k): X = Qt P_k for the wave's 16 tokens (4 column
+      // blocks), then each row dotted with dY_i.
+      {
+        f32x4 x[4] = {};
+#pragma unroll 4
+        for (int kk = 0; kk < kD / 4; ++kk) {
+          const int f = 16 * lk + kk;
+          const float av = qt_sh[(16 * wv + li) * kR + f];
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) x[ct] = mfma16(av, Ps[f * kR + 16 * ct + li], x[ct]);
+        }
+        float part[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float* dyr = dy_sh + (16 * wv + 4 * lk + e) * kR + li;
+          float v = 0.f;
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) v += x[ct][e] * dyr[16 * ct];
+          part[e] = group_sum16(v);
+        }
+        // This lane's token 16 wv + ln / 4 is row 4 lk + li / 4 of the block.
+        const int e = li / 4;
+        dyy[k] = e == 0 ? part[0] : e == 1 ? part[1] : e == 2 ? part[2] : part[3];
+      }
+      // This workgroup's share of dP_k = sum_i alpha w_k(i) Qt_i^T dY_i.
+      {
+        f32x4 acc = {};
+#pragma unroll 8
+        for (int kk = 0; kk < kBT / 4; ++kk) {
+          const int tt = 64 * (kk / 16) + 16 * lk + kk % 16;
+          acc = mfma16(w_sh[tt * kW + k] * qt_sh[tt * kR + ga + li], dy_sh[tt * kR + gc + li], acc);
+        }
+        float* dst = a.dp_part + (((size_t)b * a.nblk + blk) * T1 + (k - 1)) * kD * kD;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[(ga + 4 * lk + e) * kD + gc + li] = alpha * acc[e];
+      }
+    }
+  } else {
+    // Feature-major phi(Q) and dY (exact), the per-token scales.
+#pragma unroll
+    for (int e = 0; e < kF; ++e) {
+      qT[(f0 + e) * kTS + tk] = f2bf(q[e]);
+      dyT[(f0 + e) * kTS + tk] = f2bf(dy[e]);
+    }
+    if (qd == 0)
+#pragma unroll
+      for (int k = 1; k < kMaxT; ++k)
+        if (k <= T1) stab[(k - 1) * kBT + tk] = alpha * wk[k] * r;
+    quad_lds_sync();
+    // This wave's operands, fixed over k: A = phi(Q) of its 16 tokens
+    // (row li, slots 8 lk + 32 h + j) and dY in accumulator layout.
+    bf16x8 av[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        av[h][j] = __builtin_bit_cast(__bf16, qT[(8 * lk + 32 * h + j) * kTS + 16 * wv + li]);
+    float dyd[4][4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dyd[ct][e] = bf2f(dyT[(16 * ct + li) * kTS + 16 * wv + 4 * lk + e]);
+    const uint16_t* Ph = reinterpret_cast<const uint16_t*>(Pst);
+    const uint16_t* Pl = Ph + kD * kRB;
+#pragma unroll
+    for (int k = 1; k < kMaxT; ++k) {
+      if (k > T1) break;
+      __syncthreads();
+      stage_mat<S, false>(Pst, a.pk + ((size_t)b * T1 + (k - 1)) * kD * kD);
+      {
+        // alpha w_k r phi(Q), split: feature t / 16, tokens 16 (t % 16) .. + 15.
+        const int fa = t / 16, t0 = 16 * (t % 16);
+        const float* sc = stab + (k - 1) * kBT + t0;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const u32x4 qv = *reinterpret_cast<const u32x4*>(qT + fa * kTS + t0 + 8 * hh);
+          u32x4 hv, lv;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float v0 = sc[8 * hh + 2 * j] * __uint_as_float(qv[j] << 16);
+            const float v1 = sc[8 * hh + 2 * j + 1] * __uint_as_float(qv[j] & 0xffff0000u);
+            const uint16_t h0 = f2bf(v0), h1 = f2bf(v1);
+            hv[j] = h0 | ((uint32_t)h1 << 16);
+            lv[j] = f2bf(v0 - bf2f(h0)) | ((uint32_t)f2bf(v1 - bf2f(h1)) << 16);
+          }
+          *reinterpret_cast<u32x4*>(sqh + fa * kTS + t0 + 8 * hh) = hv;
+          *reinterpret_cast<u32x4*>(sql + fa * kTS + t0 + 8 * hh) = lv;
+        }
+      }
+      __syncthreads();
+      // dY_i . (Qt_i P_k) = r_i (phi(Q_i) P_k) . dY_i.
+      {
+        f32x4 x[4] = {};
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) {
+            const int at = (16 * ct + li) * kRB + 8 * lk + 32 * h;
+            x[ct] = mfma16_bf16(av[h], *reinterpret_cast<const bf16x8*>(Ph + at), x[ct]);
+            x[ct] = mfma16_bf16(av[h], *reinterpret_cast<const bf16x8*>(Pl + at), x[ct]);
+          }
+        float part[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float v = 0.f;
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) v += x[ct][e] * dyd[ct][e];
+          part[e] = group_sum16(v);
+        }
+        const int e = li / 4;
+        dyy[k] = r * (e == 0 ? part[0] : e == 1 ? part[1] : e == 2 ? part[2] : part[3]);
+      }
+      // This workgroup's share of dP_k.
+      {
+        f32x4 acc = {};
+#pragma unroll
+        for (int h = 0; h < kBT / 32; ++h) {
+          const int ta = (ga + li) * kTS + 8 * lk + 32 * h, tb = (gc + li) * kTS + 8 * lk + 32 * h;
+          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(dyT + tb);
+          acc = mfma16_bf16(*reinterpret_cast<const bf16x8*>(sqh + ta), bv, acc);
+          acc = mfma16_bf16(*reinterpret_cast<const bf16x8*>(sql + ta), bv, acc);
+        }
+        float* dst = a.dp_part + (((size_t)b * a.nblk + blk) * T1 + (k - 1)) * kD * kD;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[(ga + 4 * lk + e) * kD + gc + li] = acc[e];
+      }
     }
   }
   // Scalars of the token (every lane of the quad holds them).
   float wy = 0.f;
 #pragma unroll
   for (int k = 1; k < kMaxT; ++k)
-    if (k <= T1) wy += w_sh[tk * kW + k] * dyy[k];
-  const float dyG = w_sh[tk * kW] * dyv + wy;
+    if (k <= T1) wy += wk[k] * dyy[k];
+  const float dyG = wk[0] * dyv + wy;
   if (on && qd == 0) {
     // a_i = (sum_k w_k P_k dG_i) . phi(Q_i) = alpha / r_i * sum_k w_k dY_i . (Qt_i P_k)
     a.tok[base + i] = make_float4(m, Z, (1.f - alpha) * dyL, alpha / r * wy);
@@ -815,7 +938,7 @@ __global__ __launch_bounds__(kTT) void bwd_token_kv(BwdArgs a) {
 
 template <class S>
 hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
-  const size_t lds_a = (size_t)(kD * kR + kD + 2 * kBT * kR + kBT * kW + kBT) * sizeof(float);
+  const size_t lds_a = token_a_lds<S>();
   const int T1 = a.T - 1 > 0 ? a.T - 1 : 1;
   const size_t lds_adj = ((size_t)T1 + 2) * kD * kR * sizeof(float);
   static bool attr_set = false;
