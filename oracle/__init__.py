@@ -17,6 +17,10 @@ import.
 ``tests/test_oracle_backward_pins.py`` (finite differences, explicit n x n
 powers of S, branch isolation, planted mistakes).
 
+``oracle.predictor`` holds the per-token walk-weight predictor (a two-layer
+MLP on concat(Q_i, K_i) and a softmax), pinned by
+``tests/test_oracle_predictor_pins.py``.
+
 Every function of ``oracle.lisa`` is pinned by ``tests/test_oracle_pins.py``
 to facts other than itself (brute force on tiny grids, closed forms,
 invariants, hand-derived examples under ``tests/golden/``).  The one place
@@ -37,6 +41,7 @@ from .lisa import (  # noqa: F401
     lisa_bruteforce,
     neighbour_offsets,
 )
+from .predictor import predicted_weights, lisa_forward_mlp  # noqa: F401
 from .backward import (  # noqa: F401
     global_branch_backward,
     local_branch_backward,
