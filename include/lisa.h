@@ -130,6 +130,42 @@ lisa_status lisa_apply(const lisa_problem* p, const void* Q, const void* K, cons
                        const float* weights, float beta, const float* alpha, void* Y,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* Walk-weight predictor [note §2.4, Eq. 10; supplementary Sec. 8]: the
+ * adaptive weights of token i and head h are predicted from the token's
+ * query and key concatenated, by a two-layer MLP and a softmax over the T
+ * weights.  The note gives no widths, activation or biases; here
+ *   w_i = softmax(W2 ReLU(W1 concat(Q_i, K_i) + b1) + b2),
+ * per head, Q_i and K_i as given (before the feature map), query first.
+ *   hidden : hidden width, a multiple of 32 in [32, 128]
+ *   w1     : [heads, hidden, 2 d_h] fp32 (device)
+ *   b1     : [heads, hidden] fp32
+ *   w2     : [heads, T, hidden] fp32
+ *   b2     : [heads, T] fp32
+ * All four are 4-byte aligned device arrays owned by the caller. */
+typedef struct lisa_weight_mlp {
+  int32_t hidden;
+  const float* w1;
+  const float* b1;
+  const float* w2;
+  const float* b2;
+} lisa_weight_mlp;
+
+/* Workspace bytes for lisa_forward_mlp (the forward's workspace plus W1 in
+ * the layout the kernel reads), or 0 if the problem or hidden is invalid. */
+size_t lisa_forward_mlp_workspace_size(const lisa_problem* p, int32_t hidden);
+
+/* The forward pass with the walk weights predicted inside the output pass
+ * (no [batch, heads, n, T] weight tensor is read or written): the same Y as
+ * lisa_forward given the predictor's weights.  With bf16 inputs the first
+ * layer multiplies the exact bf16 inputs by W1 split into two bf16 parts
+ * (fp32 sums); everything else is fp32.  mlp NULL or a NULL array:
+ * LISA_ERR_NULL; hidden out of range: LISA_ERR_PARAM; other arguments and
+ * errors as for lisa_forward with weights == NULL, the workspace
+ * lisa_forward_mlp_workspace_size bytes. */
+lisa_status lisa_forward_mlp(const lisa_problem* p, const void* Q, const void* K, const void* V,
+                             const lisa_weight_mlp* mlp, const float* alpha, void* Y,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Backward pass: the gradients of lisa_forward's Y, contracted with the
  * output gradient dY, for every input.  The note trains every model it
  * reports [note §3] and gives no backward formulas; these are the exact

@@ -25,8 +25,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == [
-        "lisa_apply", "lisa_backward", "lisa_backward_workspace_size", "lisa_forward", "lisa_reduce",
-        "lisa_status_str", "lisa_workspace_size"]
+        "lisa_apply", "lisa_backward", "lisa_backward_workspace_size", "lisa_forward", "lisa_forward_mlp",
+        "lisa_forward_mlp_workspace_size", "lisa_reduce", "lisa_status_str", "lisa_workspace_size"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -170,3 +170,47 @@ def test_status_strings():
         assert s and s not in seen
         seen.add(s)
     assert lisa.lisa_status_str(42) == "unknown status"
+
+
+W1_, B1_, W2_, B2_ = (A + (16 + i) * 0x1000000 for i in range(4))
+
+
+def forward_mlp(p, hidden=64, w1=W1_, b1=B1_, w2=W2_, b2=B2_, mlp=True, q=Q, alpha=AL, ws=WS_, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lisa.lisa_forward_mlp_workspace_size(p, hidden) if p is not None else 0
+    m = lisa.WeightMlp(hidden, w1, b1, w2, b2)
+    return lib.lisa_forward_mlp(None if p is None else ctypes.byref(p), q, K, V,
+                                ctypes.byref(m) if mlp else None, alpha, Y, ws, ctypes.c_size_t(ws_bytes), None)
+
+
+def test_mlp_struct_matches_header():
+    assert ctypes.sizeof(lisa.WeightMlp) == 8 + 4 * 8
+
+
+def test_mlp_workspace_size():
+    p = prob(grid_h=40, grid_w=33)
+    for hidden in (32, 64, 128):
+        assert lisa.lisa_forward_mlp_workspace_size(p, hidden) >= lisa.lisa_workspace_size(p) + hidden * 3 * 2 * 64 * 4
+    for hidden in (0, 16, 48, 160):
+        assert lisa.lisa_forward_mlp_workspace_size(p, hidden) == 0
+    assert lisa.lisa_forward_mlp_workspace_size(prob(T=9), 64) == 0
+
+
+def test_mlp_argument_errors():
+    assert forward_mlp(None) == NULL
+    assert forward_mlp(prob(), mlp=False) == NULL
+    assert forward_mlp(prob(dtype=3)) == DTYPE
+    assert forward_mlp(prob(grid_h=0)) == SHAPE
+    assert forward_mlp(prob(d_h=32)) == UNSUP
+    assert forward_mlp(prob(T=0)) == PARAM
+    for hidden in (16, 48, 160):
+        assert forward_mlp(prob(), hidden=hidden, ws_bytes=1 << 30) == PARAM, hidden
+    for name in ("w1", "b1", "w2", "b2"):
+        assert forward_mlp(prob(), **{name: None}) == NULL, name
+    assert forward_mlp(prob(), b2=B2_ + 2) == ALIGN
+    assert forward_mlp(prob(), q=None) == NULL
+    assert forward_mlp(prob(), alpha=AL + 1) == ALIGN
+    p = prob()
+    assert forward_mlp(p, ws_bytes=lisa.lisa_workspace_size(p)) == WS
+    assert forward_mlp(p, ws=None) == WS
+

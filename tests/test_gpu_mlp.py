@@ -1,0 +1,117 @@
+"""Parity of lisa_forward_mlp (walk weights predicted inside the output pass,
+through the C ABI) with the fp64 oracle (oracle.lisa_forward_mlp), on the GPU.
+
+Tolerances as for lisa_forward (relative L2 over the output, and per
+element against |ref| + rms(ref)): 1e-5 for fp32 inputs, 2e-2 for bf16
+inputs.  With bf16 inputs the predictor's first layer multiplies the exact
+bf16 inputs by W1 split into two bf16 parts, so the weights themselves stay
+close to fp32 accuracy.
+"""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import lisa as olisa
+from vision_transformer_token_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-5, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def lisa():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from vision_transformer_token_amd import lisa as mod
+
+    return mod
+
+
+def f64(t):
+    return t.double().cpu().numpy()
+
+
+def run_gpu(lisa, x, prm, **kw):
+    d = {k: x[k].cuda() for k in ("q", "k", "v", "alpha")}
+    p = {k: v.cuda() for k, v in prm.items()}
+    y = lisa.lisa_forward_mlp(d["q"], d["k"], d["v"], grid=(x["H"], x["W"]), T=x["T"], alpha=d["alpha"],
+                              eps=x["eps"], **p, **kw)
+    torch.cuda.synchronize()
+    return y
+
+
+def run_oracle(x, prm):
+    return oracle.lisa_forward_mlp(f64(x["q"]), f64(x["k"]), f64(x["v"]), H=x["H"], W=x["W"], T=x["T"],
+                                   alpha=f64(x["alpha"]), W1=f64(prm["w1"]), b1=f64(prm["b1"]),
+                                   W2=f64(prm["w2"]), b2=f64(prm["b2"]), eps=x["eps"])
+
+
+def check(y_gpu, y_ref, dtype, label):
+    y = f64(y_gpu)
+    diff = y - y_ref
+    rel = np.linalg.norm(diff) / np.linalg.norm(y_ref)
+    el = np.max(np.abs(diff) / (np.abs(y_ref) + np.sqrt(np.mean(y_ref**2))))
+    print(f"[parity] mlp {label}: rel_l2={rel:.3e} max_el={el:.3e}", flush=True)
+    assert np.all(np.isfinite(y))
+    assert rel <= TOL[dtype] and el <= TOL[dtype], (label, rel, el)
+
+
+CASES = [
+    # name, B, heads, H, W, T, hidden, dtype
+    ("ragged-fp32", 2, 3, 10, 13, 3, 32, "fp32"),
+    ("t1-fp32", 1, 2, 6, 7, 1, 32, "fp32"),
+    ("t8-h128-fp32", 1, 1, 12, 12, 8, 128, "fp32"),
+    ("one-token", 3, 2, 1, 1, 3, 64, "fp32"),
+    ("one-row", 1, 2, 1, 40, 4, 32, "bf16"),
+    ("ragged-bf16", 2, 2, 13, 21, 3, 64, "bf16"),
+    ("t5-h96-bf16", 1, 3, 20, 15, 5, 96, "bf16"),
+    ("t2-h128-bf16", 2, 1, 17, 9, 2, 128, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_mlp_small(lisa, case):
+    name, B, heads, H, W, T, hidden, dtype = case
+    seed = zlib.crc32(name.encode()) % 1000
+    x = workloads.make_inputs(workloads.small(name, B, heads, H, W, T, dtype=dtype, seed=seed))
+    prm = workloads.mlp_params(heads, hidden, T, seed=seed + 1)
+    check(run_gpu(lisa, x, prm), run_oracle(x, prm), dtype, f"{name} [B={B} heads={heads} {H}x{W}] T={T} hidden={hidden}")
+
+
+@pytest.mark.parametrize("name", ["deit_t_224", "pvt_t_stage1"])
+def test_mlp_workload(lisa, name):
+    w = workloads.get(name)
+    x = workloads.make_inputs(w)
+    prm = workloads.mlp_params(w.heads, 64, w.T, seed=11)
+    check(run_gpu(lisa, x, prm), run_oracle(x, prm), w.dtype, w.describe() + " hidden=64")
+
+
+def test_mlp_geometric_special_case(lisa):
+    """W2 = 0 and b2 = log of the geometric weights: lisa_forward_mlp equals
+    lisa_forward with beta (two different kernels and weight paths)."""
+    w = workloads.small("geo", 2, 2, 11, 14, 4, dtype="fp32", seed=21)
+    x = workloads.make_inputs(w)
+    beta = 0.6
+    prm = workloads.mlp_params(2, 32, 4, seed=22)
+    prm["w2"] = torch.zeros_like(prm["w2"])
+    prm["b2"] = torch.from_numpy(np.tile(np.log(olisa.geometric_weights(beta, 4)), (2, 1)).astype(np.float32))
+    y_mlp = run_gpu(lisa, x, prm)
+    d = {k: x[k].cuda() for k in ("q", "k", "v", "alpha")}
+    y_geo = lisa.lisa_forward(d["q"], d["k"], d["v"], grid=(x["H"], x["W"]), T=4, alpha=d["alpha"], beta=beta,
+                              eps=x["eps"])
+    torch.cuda.synchronize()
+    rel = float((y_mlp - y_geo).norm() / y_geo.norm())
+    print(f"[parity] mlp geometric special case: rel={rel:.3e}", flush=True)
+    assert rel <= 1e-5
+
+
+def test_mlp_repeatable(lisa):
+    w = workloads.small("rep", 2, 2, 19, 23, 3, dtype="bf16", seed=3)
+    x = workloads.make_inputs(w)
+    prm = workloads.mlp_params(2, 64, 3, seed=4)
+    assert torch.equal(run_gpu(lisa, x, prm), run_gpu(lisa, x, prm))

@@ -229,8 +229,15 @@ enum class Mode { kForward, kReduce, kApply };
 // One launch of the persistent kernel, one workgroup per compute unit.
 lisa_status run(Plan pl, Mode mode, const void* Q, const void* K, const void* V,
                 const float* weights, float beta, const float* alpha, void* Y, char* ws, float eps,
-                hipStream_t s) {
+                hipStream_t s, const lisa_weight_mlp* mlp = nullptr, const void* mlp_frag = nullptr) {
   lisa::FlowArgs a{};
+  if (mlp) {
+    a.mlp_w1f = mlp_frag;
+    a.mlp_b1 = mlp->b1;
+    a.mlp_w2 = mlp->w2;
+    a.mlp_b2 = mlp->b2;
+    a.hidden = mlp->hidden;
+  }
   a.Q = Q;
   a.K = K;
   a.V = V;
@@ -249,7 +256,7 @@ lisa_status run(Plan pl, Mode mode, const void* Q, const void* K, const void* V,
   a.BH = pl.BH;
   a.eps = eps;
   a.logit_scale = (float)(1.4426950408889634 / std::sqrt((double)kD));
-  if (!plan_tiles(pl, weights != nullptr)) return LISA_ERR_UNSUPPORTED;
+  if (!plan_tiles(pl, weights != nullptr || mlp != nullptr)) return LISA_ERR_UNSUPPORTED;
   // One persistent workgroup per compute unit.
   DeviceInfo dinfo;
   if (!device_info(dinfo)) return LISA_ERR_HIP;
@@ -354,6 +361,38 @@ lisa_status lisa_apply(const lisa_problem* p, const void* Q, const void* K, cons
   (void)hipGetLastError();
   return run(pl, Mode::kApply, Q, K, V, weights, beta, alpha, Y, static_cast<char*>(workspace), p->eps,
              static_cast<hipStream_t>(stream));
+}
+
+size_t lisa_forward_mlp_workspace_size(const lisa_problem* p, int32_t hidden) {
+  Plan pl;
+  if (make_plan(p, pl) != LISA_OK || hidden < 32 || hidden > lisa::kMaxHidden || hidden % 32 != 0) return 0;
+  return up(pl.total, kAlign) + lisa::mlp_frag_bytes(pl.dtype, pl.heads, hidden);
+}
+
+lisa_status lisa_forward_mlp(const lisa_problem* p, const void* Q, const void* K, const void* V,
+                             const lisa_weight_mlp* mlp, const float* alpha, void* Y, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!mlp) return LISA_ERR_NULL;
+  Plan pl;
+  lisa_status st = make_plan(p, pl);
+  if (st != LISA_OK) return st;
+  if (mlp->hidden < 32 || mlp->hidden > lisa::kMaxHidden || mlp->hidden % 32 != 0) return LISA_ERR_PARAM;
+  if (!mlp->w1 || !mlp->b1 || !mlp->w2 || !mlp->b2) return LISA_ERR_NULL;
+  if (misaligned(mlp->w1, 4) || misaligned(mlp->b1, 4) || misaligned(mlp->w2, 4) || misaligned(mlp->b2, 4))
+    return LISA_ERR_ALIGN;
+  const size_t frag_at = up(pl.total, kAlign);
+  const size_t need = frag_at + lisa::mlp_frag_bytes(pl.dtype, pl.heads, mlp->hidden);
+  if (workspace_bytes < need) return LISA_ERR_WORKSPACE;
+  st = check_forward(p, Q, K, V, nullptr, 0.f, alpha, Y, workspace, workspace_bytes, pl);
+  if (st != LISA_OK) return st;
+  const size_t tensor = (size_t)pl.BH * pl.n * kD * pl.esize;
+  if (overlaps(Y, tensor, workspace, need)) return LISA_ERR_PARAM;
+  (void)hipGetLastError();
+  char* ws = static_cast<char*>(workspace);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (lisa::launch_mlp_prep(pl.dtype, mlp->w1, ws + frag_at, pl.heads, mlp->hidden, s) != hipSuccess)
+    return LISA_ERR_HIP;
+  return run(pl, Mode::kForward, Q, K, V, nullptr, 0.f, alpha, Y, ws, p->eps, s, mlp, ws + frag_at);
 }
 
 size_t lisa_backward_workspace_size(const lisa_problem* p) {

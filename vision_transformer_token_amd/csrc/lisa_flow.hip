@@ -163,7 +163,7 @@ __device__ __forceinline__ void tile_origin(const FlowArgs& a, int t, int& r0, i
 
 template <class Tr>
 __device__ __forceinline__ TileLayout layout_of(const FlowArgs& a) {
-  return tile_layout(a.TR, a.TC, a.weights ? a.T : 0, (int)sizeof(typename Tr::S));
+  return tile_layout(a.TR, a.TC, (a.weights || a.mlp_w1f) ? a.T : 0, (int)sizeof(typename Tr::S));
 }
 
 // Chunk j of the rank's range: first token and length.
@@ -329,15 +329,118 @@ __device__ __forceinline__ float sum_s_partials(const FlowArgs& a, int b) {
   return t;
 }
 
+// Walk weights of 32 tokens of an output tile from the predictor, into the
+// tile's weight slots: token n of the group (lanes n and n + 32) has x_n =
+// concat(Q_n, K_n) in the staged tile (its Q row `slot`, its K cell `ccell`).
+// First layer on MFMA 32x32 as W1 x^T, 32 hidden units at a time (A = W1
+// fragments, B = x: for bf16 the exact input values against W1's high and
+// low bf16 parts); each lane then holds 16 hidden units of its token, takes
+// ReLU(. + b1) and its share of W2 h; the two halves' shares add across the
+// lane pair, then + b2 and the softmax over T.
+template <class Tr>
+__device__ __forceinline__ void predict_weights(const FlowArgs& a, int b, const unsigned char* cQ,
+                                                const unsigned char* cK, int slot, int ccell, float* cW) {
+  const int lane = threadIdx.x & 63, h = lane >> 5;
+  const int head = b % a.heads, T = a.T, nhb = a.hidden / 32;
+  float p[kMaxT];
+#pragma unroll
+  for (int t = 0; t < kMaxT; ++t) p[t] = 0.f;
+#pragma unroll 1
+  for (int hb = 0; hb < nhb; ++hb) {
+    f32x16 c = {};
+    if constexpr (Tr::EPL == 8) {
+      const bf16x8* fr = static_cast<const bf16x8*>(a.mlp_w1f) + (size_t)(head * nhb + hb) * 8 * 64 * 2;
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const unsigned char* src = st < 4 ? cQ + row_off<BF16>(slot, 16 * st + 8 * h)
+                                          : cK + row_off<BF16>(ccell, 16 * (st - 4) + 8 * h);
+        const bf16x8 xb = *reinterpret_cast<const bf16x8*>(src);
+        c = mma(fr[(st * 64 + lane) * 2], xb, c);
+        c = mma(fr[(st * 64 + lane) * 2 + 1], xb, c);
+      }
+    } else {
+      const float* fr = static_cast<const float*>(a.mlp_w1f) + (size_t)(head * nhb + hb) * 64 * 64;
+#pragma unroll 8
+      for (int st = 0; st < 64; ++st) {
+        const unsigned char* src = st < 32 ? cQ + row_off<F32>(slot, 2 * st + h) : cK + row_off<F32>(ccell, 2 * (st - 32) + h);
+        const float x = *reinterpret_cast<const float*>(src);
+        c = mma(fr[st * 64 + lane], x, c);
+      }
+    }
+    const float* b1 = a.mlp_b1 + (size_t)head * a.hidden + 32 * hb;
+    const float* w2 = a.mlp_w2 + (size_t)head * T * a.hidden + 32 * hb;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int j = 8 * (i / 4) + 4 * h + i % 4;  // hidden unit of accumulator element i
+      const float hv = fmaxf(c[i] + b1[j], 0.f);
+#pragma unroll
+      for (int t = 0; t < kMaxT; ++t)
+        if (t < T) p[t] += w2[t * a.hidden + j] * hv;
+    }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < kMaxT; ++t)
+    if (t < T) {
+      p[t] += __shfl_xor(p[t], 32);
+      p[t] += a.mlp_b2[head * T + t];
+      mx = fmaxf(mx, p[t]);
+    }
+  float sum = 0.f;
+#pragma unroll
+  for (int t = 0; t < kMaxT; ++t)
+    if (t < T) {
+      p[t] = __expf(p[t] - mx);
+      sum += p[t];
+    }
+  const float inv = 1.f / sum;
+  if (h == 0)
+#pragma unroll
+    for (int t = 0; t < kMaxT; ++t)
+      if (t < T) cW[slot * T + t] = p[t] * inv;
+}
+
+// Producer wave pw, once every producer wave's DMA of output tile t has
+// landed: the predicted weights of the tile's 32-token blocks pw, pw + 4, ...
+// (blocks of 4 rows x 8 columns, as the consumers take them).
+template <class Tr>
+__device__ void predict_tile(const FlowArgs& a, int b, int t, unsigned char* buf, int pw) {
+  const TileLayout L = layout_of<Tr>(a);
+  int r0, c0;
+  tile_origin(a, t, r0, c0);
+  const int n = threadIdx.x & 31, CW = a.TC + 2;
+  const int CB = a.TC / 8, nblk = (a.TR / 4) * CB;
+  for (int blk = pw; blk < nblk; blk += kRoleWaves) {
+    const int br = blk / CB, bc = blk % CB;
+    if (r0 + 4 * br >= a.H || c0 + 8 * bc >= a.W) continue;  // no token of the block is on the grid
+    const int tr = 4 * br + (n >> 3), tc = 8 * bc + (n & 7);
+    predict_weights<Tr>(a, b, buf + L.q, buf + L.k, tr * a.TC + tc, (tr + 1) * CW + (tc + 1),
+                        reinterpret_cast<float*>(buf + L.w));
+  }
+}
+
+// The producer waves meet: each counts itself in `ready` and waits until all
+// kRoleWaves have (every producer wave takes part in every OUT stage, so the
+// count reaches the next multiple of kRoleWaves).
+__device__ __forceinline__ void producers_meet(int* ready) {
+  const int lane = threadIdx.x & 63;
+  if (lane == 0) {
+    const int target = (atomicAdd(ready, 1) / kRoleWaves + 1) * kRoleWaves;
+    while (__atomic_load_n(ready, __ATOMIC_RELAXED) < target) __builtin_amdgcn_s_sleep(1);
+  }
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Producer waves: make stage `p` ready for the consumers in `buf` and, at the
 // start of an OUT phase, in the statistics area `st`: issue the DMA, wait for
 // the dependency, load what other workgroups wrote, wait, finish.  Only
 // producer wave 0 polls the arrival counter; it then posts `tag` in `dep_ok`,
 // which the other producer waves watch in LDS.  `s_w` is this wave's 64-float
 // scratch in LDS (s of the slice whose M chunks it prepares).
-template <class Tr>
+template <class Tr, bool kMlp>
 __device__ void prepare(const FlowArgs& a, const Rank& rk, Pos p, unsigned char* buf, unsigned char* st,
-                        float* s_w, volatile int* dep_ok, int pw) {
+                        float* s_w, volatile int* dep_ok, int* mlp_ready, int pw) {
   using S = typename Tr::S;
   using L = LdsOf<Tr>;
   const int lane = threadIdx.x & 63;
@@ -397,6 +500,10 @@ __device__ void prepare(const FlowArgs& a, const Rank& rk, Pos p, unsigned char*
       }
     }
     wait_all();
+    if constexpr (kMlp) {
+      producers_meet(mlp_ready);
+      predict_tile<Tr>(a, b, rk.t0 + p.j, buf, pw);
+    }
     if (a.T >= 2) finish_tile<Tr>(a, layout_of<Tr>(a), buf, s_w, pw);
   }
 }
@@ -728,7 +835,7 @@ __device__ __forceinline__ void local_token_valu(const FlowArgs& a, const unsign
 // pair), r_i from the tile's r region and `geo` holds the geometric walk
 // weights, all in LDS.
 // ---------------------------------------------------------------------------
-template <class Tr>
+template <class Tr, bool kMlp>
 __device__ __forceinline__ void out_tile(const FlowArgs& a, int b, int t, const unsigned char* buf,
                                          const typename Tr::Frag (&fkv)[2][Tr::NQ],
                                          const typename Tr::Frag (&fm)[2][Tr::NQ], const float* geo,
@@ -760,8 +867,9 @@ __device__ __forceinline__ void out_tile(const FlowArgs& a, int b, int t, const 
     const int i = valid ? row * a.W + col : 0;
     const int ccell = (tr + 1) * CW + (tc + 1);
 
-    // This token's walk weights in LDS: its staged row, or the geometric table.
-    const float* wrow = a.weights ? cW + slot * a.T : geo;
+    // This token's walk weights in LDS: its staged or predicted row, or the
+    // geometric table.
+    const float* wrow = (kMlp || a.weights) ? cW + slot * a.T : geo;
     const float w0 = wrow[0], w1 = a.T >= 2 ? wrow[1] : 0.f;
 
     // acc = (1 - alpha) L_i: the local branch; u1 = u_1 = phi(Q_i) in
@@ -842,7 +950,7 @@ __device__ __forceinline__ void out_tile(const FlowArgs& a, int b, int t, const 
 // The OUT phase of slice b: take the slice statistics out of the statistics
 // area (fragments into registers), free the area (barrier),
 // then compute the rank's tiles, one stage each.  Returns the buffer index.
-template <class Tr>
+template <class Tr, bool kMlp>
 __device__ int consume_out(const FlowArgs& a, const Rank& rk, int b, unsigned char* smem, int bsel,
                            const float* geo, int cw) {
   using Frag = typename Tr::Frag;
@@ -863,14 +971,14 @@ __device__ int consume_out(const FlowArgs& a, const Rank& rk, int b, unsigned ch
   const unsigned nbr = neighbour_slots(tok >> 3, tok & 7, lane >> 5);
   lds_barrier();  // the statistics area may now be refilled
   for (int k = 0; k < rk.nt; ++k) {
-    out_tile<Tr>(a, b, rk.t0 + k, smem + bsel * L::kStage, fkv, fm, geo, alpha, nbr, cw);
+    out_tile<Tr, kMlp>(a, b, rk.t0 + k, smem + bsel * L::kStage, fkv, fm, geo, alpha, nbr, cw);
     lds_barrier();
     bsel ^= 1;
   }
   return bsel;
 }
 
-template <class Tr>
+template <class Tr, bool kMlp>
 __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
   using L = LdsOf<Tr>;
   extern __shared__ __align__(1024) unsigned char smem[];
@@ -879,6 +987,7 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
   __shared__ int dep_ok;                 // tag of the stage whose dependency producer wave 0 has seen met
   __shared__ int last;                   // this workgroup's ticket, later: it finished last
   __shared__ int arrivals;               // consumer waves that have arrived in the current phase
+  __shared__ int mlp_ready;              // producer waves that have met before predicting weights
   const int tid = threadIdx.x;
   const int wave = wave_id();
   const bool producer = wave < kRoleWaves;
@@ -889,6 +998,7 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
   if (tid == 0) {
     dep_ok = -1;
     arrivals = 0;
+    mlp_ready = 0;
     last = (int)bump(a.tickets + (a.xcd_groups ? blockIdx.x % kXcds : 0));
   }
   __syncthreads();
@@ -897,13 +1007,14 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
   // barriers: one per stage, plus one at the start of each OUT phase.
   if (producer) {
     Pos p = first_pos(a, rk);
-    if (p.ph != kPEnd) prepare<Tr>(a, rk, p, smem, st, s_w[rw], &dep_ok, rw);
+    if (p.ph != kPEnd) prepare<Tr, kMlp>(a, rk, p, smem, st, s_w[rw], &dep_ok, &mlp_ready, rw);
     lds_barrier();
     int bsel = 0;
     while (p.ph != kPEnd) {
       const Pos np = advance(a, rk, p);
       if (p.ph == kPOut && p.j == 0) lds_barrier();  // the consumers have taken the statistics
-      if (np.ph != kPEnd) prepare<Tr>(a, rk, np, smem + (bsel ^ 1) * L::kStage, st, s_w[rw], &dep_ok, rw);
+      if (np.ph != kPEnd)
+        prepare<Tr, kMlp>(a, rk, np, smem + (bsel ^ 1) * L::kStage, st, s_w[rw], &dep_ok, &mlp_ready, rw);
       lds_barrier();
       bsel ^= 1;
       p = np;
@@ -929,7 +1040,7 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
           }
         if (phase_len(a, rk, kPOut) > 0)
           for (int z = 0; z < nz; ++z)
-            bsel = consume_out<Tr>(a, rk, slice_of(a, rk, r, z), smem, bsel, geo_sh, rw);
+            bsel = consume_out<Tr, kMlp>(a, rk, slice_of(a, rk, r, z), smem, bsel, geo_sh, rw);
       }
     }
   }
@@ -951,24 +1062,68 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
   }
 }
 
-template <class Tr>
+template <class Tr, bool kMlp>
 hipError_t launch_typed(const FlowArgs& a, int grid, hipStream_t s) {
   constexpr int lds = LdsOf<Tr>::kTotal;
   static bool attr_set = false;
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&flow_kernel<Tr>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&flow_kernel<Tr, kMlp>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(flow_kernel<Tr>, dim3(grid), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((flow_kernel<Tr, kMlp>), dim3(grid), dim3(kThreads), lds, s, a);
   return hipGetLastError();
+}
+
+// W1 fragments for predict_weights: one thread per (head, block, step, lane).
+template <class Tr>
+__global__ __launch_bounds__(256) void mlp_prep(const float* w1, void* frag, int heads, int hidden) {
+  constexpr bool kBf16 = Tr::EPL == 8;
+  constexpr int kSteps = kBf16 ? 8 : 64;
+  const int total = heads * (hidden / 32) * kSteps * 64;
+  const int id = blockIdx.x * 256 + threadIdx.x;
+  if (id >= total) return;
+  const int lane = id % 64, st = (id / 64) % kSteps, blk = id / (64 * kSteps);  // blk = head * nhb + hb
+  const int nhb = hidden / 32, head = blk / nhb, hb = blk % nhb;
+  const int m = lane % 32, h = lane / 32;
+  const float* row = w1 + ((size_t)head * hidden + 32 * hb + m) * (2 * kD);
+  if constexpr (kBf16) {
+    bf16x8 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = row[16 * st + 8 * h + e];
+      const __bf16 vh = (__bf16)v;
+      hi[e] = vh;
+      lo[e] = (__bf16)(v - (float)vh);
+    }
+    static_cast<bf16x8*>(frag)[(size_t)id * 2] = hi;
+    static_cast<bf16x8*>(frag)[(size_t)id * 2 + 1] = lo;
+  } else {
+    static_cast<float*>(frag)[id] = row[2 * st + h];
+  }
 }
 
 }  // namespace
 
 hipError_t launch_flow(int dtype, const FlowArgs& a, int grid, hipStream_t s) {
-  return dtype == 1 ? launch_typed<BF16>(a, grid, s) : launch_typed<F32>(a, grid, s);
+  if (a.mlp_w1f) return dtype == 1 ? launch_typed<BF16, true>(a, grid, s) : launch_typed<F32, true>(a, grid, s);
+  return dtype == 1 ? launch_typed<BF16, false>(a, grid, s) : launch_typed<F32, false>(a, grid, s);
+}
+
+size_t mlp_frag_bytes(int dtype, int heads, int hidden) {
+  (void)dtype;  // bf16: high and low parts, 2 + 2 bytes per W1 element; fp32: 4 bytes
+  return (size_t)heads * hidden * 2 * kD * 4;
+}
+
+hipError_t launch_mlp_prep(int dtype, const float* w1, void* frag, int heads, int hidden, hipStream_t s) {
+  const int total = heads * (hidden / 32) * (dtype == 1 ? 8 : 64) * 64;
+  const dim3 grid((total + 255) / 256);
+  if (dtype == 1)
+    hipLaunchKernelGGL(mlp_prep<BF16>, grid, dim3(256), 0, s, w1, frag, heads, hidden);
+  else
+    hipLaunchKernelGGL(mlp_prep<F32>, grid, dim3(256), 0, s, w1, frag, heads, hidden);
+  return hipGetLastError();
 }
 
 }  // namespace lisa

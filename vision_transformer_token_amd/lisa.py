@@ -18,6 +18,9 @@ __all__ = [
     "LISA_BF16",
     "lisa_workspace_size",
     "lisa_forward",
+    "lisa_forward_mlp",
+    "lisa_forward_mlp_workspace_size",
+    "WeightMlp",
     "lisa_reduce",
     "lisa_apply",
     "lisa_status_str",
@@ -62,6 +65,18 @@ class Problem(ctypes.Structure):
     ]
 
 
+class WeightMlp(ctypes.Structure):
+    """struct lisa_weight_mlp (device pointers)."""
+
+    _fields_ = [
+        ("hidden", ctypes.c_int32),
+        ("w1", ctypes.c_void_p),
+        ("b1", ctypes.c_void_p),
+        ("w2", ctypes.c_void_p),
+        ("b2", ctypes.c_void_p),
+    ]
+
+
 _P = ctypes.POINTER(Problem)
 _vp = ctypes.c_void_p
 _lib.lisa_workspace_size.argtypes = [_P]
@@ -72,6 +87,10 @@ _lib.lisa_apply.argtypes = _lib.lisa_forward.argtypes
 _lib.lisa_apply.restype = ctypes.c_int
 _lib.lisa_reduce.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.lisa_reduce.restype = ctypes.c_int
+_lib.lisa_forward_mlp_workspace_size.argtypes = [_P, ctypes.c_int32]
+_lib.lisa_forward_mlp_workspace_size.restype = ctypes.c_size_t
+_lib.lisa_forward_mlp.argtypes = [_P, _vp, _vp, _vp, ctypes.POINTER(WeightMlp), _vp, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.lisa_forward_mlp.restype = ctypes.c_int
 _lib.lisa_backward_workspace_size.argtypes = [_P]
 _lib.lisa_backward_workspace_size.restype = ctypes.c_size_t
 _lib.lisa_backward.argtypes = [_P, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -174,6 +193,37 @@ def lisa_forward(q, k, v, *, grid, T, alpha, weights=None, beta=None, eps=1e-6, 
     return _call_forward(_lib.lisa_forward, "lisa_forward", q, k, v, grid=grid, T=T, alpha=alpha,
                          weights=weights, beta=beta, eps=eps, out=out, workspace=workspace,
                          stream=stream)
+
+
+def lisa_forward_mlp_workspace_size(problem, hidden):
+    return int(_lib.lisa_forward_mlp_workspace_size(ctypes.byref(problem), int(hidden)))
+
+
+def lisa_forward_mlp(q, k, v, *, grid, T, alpha, w1, b1, w2, b2, eps=1e-6, out=None, workspace=None,
+                     stream=None):
+    """Y = LiSA(q, k, v) with the walk weights predicted from concat(q_i, k_i)
+    by the two-layer MLP (w1 [heads, hidden, 2 d_h], b1 [heads, hidden],
+    w2 [heads, T, hidden], b2 [heads, T], fp32 GPU tensors); see include/lisa.h."""
+    _check_tensors(q=q, k=k, v=v, alpha=alpha, w1=w1, b1=b1, w2=w2, b2=b2, out=out, workspace=workspace)
+    for name, t in (("alpha", alpha), ("w1", w1), ("b1", b1), ("w2", w2), ("b2", b2)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    hidden = w1.shape[1]
+    prob = make_problem(q, v, grid=grid, T=T, eps=eps)
+    if workspace is None:
+        nbytes = lisa_forward_mlp_workspace_size(prob, hidden)
+        if nbytes == 0:
+            raise LisaError(2, "lisa_forward_mlp_workspace_size")
+        workspace = torch.zeros(nbytes, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(v)
+    mlp = WeightMlp(hidden, w1.data_ptr(), b1.data_ptr(), w2.data_ptr(), b2.data_ptr())
+    st = _lib.lisa_forward_mlp(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(mlp), _ptr(alpha),
+                               _ptr(out), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                               _stream(stream, q.device))
+    if st != LISA_OK:
+        raise LisaError(st, "lisa_forward_mlp")
+    return out
 
 
 def lisa_apply(q, k, v, *, grid, T, alpha, workspace, weights=None, beta=None, eps=1e-6, out=None,

@@ -132,5 +132,20 @@ def make_inputs(w, seed=None):
     }
 
 
+def mlp_params(heads, hidden, T, d_h=64, seed=0):
+    """Random parameters of the walk-weight predictor, as CPU fp32 tensors:
+    w1 [heads, hidden, 2 d_h], b1 [heads, hidden], w2 [heads, T, hidden],
+    b2 [heads, T].  Scales keep the hidden pre-activations and the logits of
+    order one for ReLU(N(0, 1)) queries and keys."""
+    rng = np.random.default_rng(seed)
+    f = lambda *shape, scale: torch.from_numpy((rng.standard_normal(shape) * scale).astype(np.float32))  # noqa: E731
+    return {
+        "w1": f(heads, hidden, 2 * d_h, scale=1.0 / np.sqrt(d_h)),
+        "b1": f(heads, hidden, scale=0.1),
+        "w2": f(heads, T, hidden, scale=2.0 / np.sqrt(hidden)),
+        "b2": f(heads, T, scale=0.1),
+    }
+
+
 def with_changes(w, **kw):
     return replace(w, **kw)
