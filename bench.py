@@ -233,6 +233,8 @@ def main():
                          "launch of the kernel is then a forward)")
     ap.add_argument("--backward-only", action="store_true",
                     help="time only lisa_backward (for a profiler run) and print its line")
+    ap.add_argument("--mlp-only", action="store_true",
+                    help="time only lisa_forward_mlp (predicted walk weights) and print its line")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="instead of LiSA, run 20 plain device copies of this many MiB "
@@ -353,8 +355,41 @@ def main():
                 "steps": steps, "algorithmic_bytes_per_call": w.token_heads * bb,
                 "roofline_frac": w.token_heads * bb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
+    def mlp_timing(steps, warmup, hidden=64):
+        """lisa_forward_mlp over the same input sets: the walk weights predicted
+        inside the output pass (two-layer MLP of width ``hidden``) instead of read."""
+        prm = {k: t.to(dev) for k, t in workloads.mlp_params(w.heads, hidden, w.T, d_h=w.d_h, seed=5).items()}
+        mws = torch.zeros(lisa.lisa_forward_mlp_workspace_size(prob, hidden), dtype=torch.uint8, device=dev)
+        with torch.cuda.stream(stream):
+            ys = [torch.empty_like(d["v"]) for d in sets]
+        torch.cuda.synchronize()
+
+        def fwd(j):
+            d = sets[j]
+            lisa.lisa_forward_mlp(d["q"], d["k"], d["v"], grid=(w.H, w.W), T=w.T, alpha=d["alpha"], eps=w.eps,
+                                  workspace=mws, out=ys[j], stream=stream, **prm)
+
+        for i in range(warmup):
+            fwd(i % nsets)
+        ma, mz = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ma.record(stream)
+        for i in range(steps):
+            fwd(i % nsets)
+        mz.record(stream)
+        torch.cuda.synchronize()
+        ms = ma.elapsed_time(mz) / steps
+        # Compulsory bytes without the weight tensor: Q, K, V read, Y written.
+        bb = compulsory_bytes_per_token_head(w) - (4 * w.T if w.mode == "adaptive" else 0)
+        return {"ms_per_step": ms, "value": w.token_heads / (ms * 1e-3), "unit": "token-heads/s", "steps": steps,
+                "hidden": hidden, "algorithmic_bytes_per_call": w.token_heads * bb,
+                "roofline_frac": w.token_heads * bb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
     if args.backward_only:
         print(json.dumps({"workload": w.name, "backward": backward_timing(args.steps, args.warmup)}), flush=True)
+        return
+    if args.mlp_only:
+        print(json.dumps({"workload": w.name, "forward_mlp": mlp_timing(args.steps, args.warmup)}), flush=True)
         return
 
     for i in range(args.warmup):
@@ -498,6 +533,7 @@ def main():
         out["stages_ms"] = {"forward_kernel": kernel_ms, "reduce_only": stats_ms, "apply_only": apply_ms}
     if not args.forward_only:
         out["backward"] = backward_timing(min(args.steps, 500), min(args.warmup, 50))
+        out["forward_mlp"] = mlp_timing(min(args.steps, 1000), min(args.warmup, 50))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -157,8 +157,8 @@ size_t lisa_forward_mlp_workspace_size(const lisa_problem* p, int32_t hidden);
 /* The forward pass with the walk weights predicted inside the output pass
  * (no [batch, heads, n, T] weight tensor is read or written): the same Y as
  * lisa_forward given the predictor's weights.  With bf16 inputs the first
- * layer multiplies the exact bf16 inputs by W1 split into two bf16 parts
- * (fp32 sums); everything else is fp32.  mlp NULL or a NULL array:
+ * layer multiplies the exact bf16 inputs by W1 rounded to bf16 (as the walk
+ * rounds its P_k), with fp32 sums; everything else is fp32.  mlp NULL or a NULL array:
  * LISA_ERR_NULL; hidden out of range: LISA_ERR_PARAM; other arguments and
  * errors as for lisa_forward with weights == NULL, the workspace
  * lisa_forward_mlp_workspace_size bytes. */

@@ -2,10 +2,9 @@
 through the C ABI) with the fp64 oracle (oracle.lisa_forward_mlp), on the GPU.
 
 Tolerances as for lisa_forward (relative L2 over the output, and per
-element against |ref| + rms(ref)): 1e-5 for fp32 inputs, 2e-2 for bf16
-inputs.  With bf16 inputs the predictor's first layer multiplies the exact
-bf16 inputs by W1 split into two bf16 parts, so the weights themselves stay
-close to fp32 accuracy.
+element against |ref| + rms(ref)): 1e-5 for fp32 inputs (fp32 throughout),
+2e-2 for bf16 inputs, where the predictor's first layer takes W1 rounded to
+bf16 (2^-9 relative) against the exact inputs.
 """
 
 import zlib

@@ -329,93 +329,128 @@ __device__ __forceinline__ float sum_s_partials(const FlowArgs& a, int b) {
   return t;
 }
 
-// Walk weights of 32 tokens of an output tile from the predictor, into the
-// tile's weight slots: token n of the group (lanes n and n + 32) has x_n =
-// concat(Q_n, K_n) in the staged tile (its Q row `slot`, its K cell `ccell`).
-// First layer on MFMA 32x32 as W1 x^T, 32 hidden units at a time (A = W1
-// fragments, B = x: for bf16 the exact input values against W1's high and
-// low bf16 parts); each lane then holds 16 hidden units of its token, takes
-// ReLU(. + b1) and its share of W2 h; the two halves' shares add across the
-// lane pair, then + b2 and the softmax over T.
-template <class Tr>
-__device__ __forceinline__ void predict_weights(const FlowArgs& a, int b, const unsigned char* cQ,
-                                                const unsigned char* cK, int slot, int ccell, float* cW) {
-  const int lane = threadIdx.x & 63, h = lane >> 5;
-  const int head = b % a.heads, T = a.T, nhb = a.hidden / 32;
-  float p[kMaxT];
-#pragma unroll
-  for (int t = 0; t < kMaxT; ++t) p[t] = 0.f;
-#pragma unroll 1
-  for (int hb = 0; hb < nhb; ++hb) {
-    f32x16 c = {};
-    if constexpr (Tr::EPL == 8) {
-      const bf16x8* fr = static_cast<const bf16x8*>(a.mlp_w1f) + (size_t)(head * nhb + hb) * 8 * 64 * 2;
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const unsigned char* src = st < 4 ? cQ + row_off<BF16>(slot, 16 * st + 8 * h)
-                                          : cK + row_off<BF16>(ccell, 16 * (st - 4) + 8 * h);
-        const bf16x8 xb = *reinterpret_cast<const bf16x8*>(src);
-        c = mma(fr[(st * 64 + lane) * 2], xb, c);
-        c = mma(fr[(st * 64 + lane) * 2 + 1], xb, c);
-      }
-    } else {
-      const float* fr = static_cast<const float*>(a.mlp_w1f) + (size_t)(head * nhb + hb) * 64 * 64;
-#pragma unroll 8
-      for (int st = 0; st < 64; ++st) {
-        const unsigned char* src = st < 32 ? cQ + row_off<F32>(slot, 2 * st + h) : cK + row_off<F32>(ccell, 2 * (st - 32) + h);
-        const float x = *reinterpret_cast<const float*>(src);
-        c = mma(fr[st * 64 + lane], x, c);
-      }
-    }
-    const float* b1 = a.mlp_b1 + (size_t)head * a.hidden + 32 * hb;
-    const float* w2 = a.mlp_w2 + (size_t)head * T * a.hidden + 32 * hb;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int j = 8 * (i / 4) + 4 * h + i % 4;  // hidden unit of accumulator element i
-      const float hv = fmaxf(c[i] + b1[j], 0.f);
-#pragma unroll
-      for (int t = 0; t < kMaxT; ++t)
-        if (t < T) p[t] += w2[t * a.hidden + j] * hv;
-    }
-  }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int t = 0; t < kMaxT; ++t)
-    if (t < T) {
-      p[t] += __shfl_xor(p[t], 32);
-      p[t] += a.mlp_b2[head * T + t];
-      mx = fmaxf(mx, p[t]);
-    }
-  float sum = 0.f;
-#pragma unroll
-  for (int t = 0; t < kMaxT; ++t)
-    if (t < T) {
-      p[t] = __expf(p[t] - mx);
-      sum += p[t];
-    }
-  const float inv = 1.f / sum;
-  if (h == 0)
-#pragma unroll
-    for (int t = 0; t < kMaxT; ++t)
-      if (t < T) cW[slot * T + t] = p[t] * inv;
+// The walk-weight predictor, run by the producer waves on a staged output
+// tile (its Q rows and K cells): w = softmax(W2 ReLU(W1 concat(q, k) + b1)
+// + b2) per token.  The first layer runs on MFMA 32x32 as W1 x^T, 32 hidden
+// units at a time, with W1 laid out by mlp_prep per head as the lanes read
+// it: bf16 inputs, [hidden/32][8 steps of 16 inputs][64 lanes] bf16x8 (W1
+// rounded to bf16 once, like the walk's P_k; the inputs are exact); fp32,
+// [hidden/32][64 steps of 2 inputs][64 lanes] floats.  Element i of lane
+// (n, h) of its accumulator is hidden unit 32 hb + 8 (i / 4) + i % 4 + 4 h of
+// token n: lane halves 0 and 1 hold the two contraction slots of an fp32
+// MFMA 32x32x2, so the second layer is 16 of those, A = W2 (rows past T
+// zero) and B = the hidden values; its accumulator element e of lane (n, h)
+// is logit 4 h + e of token n.  A lane's W2 and b1 operands are gathered
+// from their natural layouts together with its W1 operands.
+__host__ __device__ inline size_t mlp_head_floats(int hidden, bool bf16) {
+  return (size_t)hidden * (bf16 ? 64 : 128);
 }
 
-// Producer wave pw, once every producer wave's DMA of output tile t has
-// landed: the predicted weights of the tile's 32-token blocks pw, pw + 4, ...
-// (blocks of 4 rows x 8 columns, as the consumers take them).
 template <class Tr>
-__device__ void predict_tile(const FlowArgs& a, int b, int t, unsigned char* buf, int pw) {
+struct MlpRegs {
+  static constexpr bool kBf16 = Tr::EPL == 8;
+  bf16x8 fh[kBf16 ? 8 : 1];
+  float fw[kBf16 ? 1 : 64];
+  float w2[16], b1[16];
+  // One hidden block's operands of this lane.
+  __device__ __forceinline__ void load(const FlowArgs& a, int head, int hb) {
+    const int lane = threadIdx.x & 63, m = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int j = 32 * hb + 8 * (i / 4) + i % 4 + 4 * h;  // hidden unit of slot h, element i
+      w2[i] = m < a.T ? a.mlp_w2[((size_t)head * a.T + m) * a.hidden + j] : 0.f;
+      b1[i] = a.mlp_b1[(size_t)head * a.hidden + j];
+    }
+    const float* blk = static_cast<const float*>(a.mlp_w1f) + (size_t)head * mlp_head_floats(a.hidden, kBf16);
+    if constexpr (kBf16) {
+      const bf16x8* f = reinterpret_cast<const bf16x8*>(blk) + (size_t)hb * 8 * 64;
+#pragma unroll
+      for (int st = 0; st < 8; ++st) fh[st] = f[st * 64 + lane];
+    } else {
+#pragma unroll
+      for (int st = 0; st < 64; ++st) fw[st] = blk[((size_t)hb * 64 + st) * 64 + lane];
+    }
+  }
+};
+
+// Producer wave pw, once every producer wave's DMA of output tile t has
+// landed: the predicted weights of the tile's 32-token blocks pw and pw + 4
+// (blocks of 4 rows x 8 columns, as the consumers take them), into the
+// tile's weight slots.  pr holds hidden block 0's operands (loaded before
+// the tile's DMA was issued).
+template <class Tr>
+__device__ void predict_tile(const FlowArgs& a, int b, int t, unsigned char* buf, int pw, MlpRegs<Tr>& pr) {
+  static_assert(kMaxTileTokens / 32 <= 2 * kRoleWaves, "at most two 32-token blocks per producer wave");
   const TileLayout L = layout_of<Tr>(a);
   int r0, c0;
   tile_origin(a, t, r0, c0);
-  const int n = threadIdx.x & 31, CW = a.TC + 2;
+  const int lane = threadIdx.x & 63, n = lane & 31, h = lane >> 5, CW = a.TC + 2;
   const int CB = a.TC / 8, nblk = (a.TR / 4) * CB;
-  for (int blk = pw; blk < nblk; blk += kRoleWaves) {
-    const int br = blk / CB, bc = blk % CB;
-    if (r0 + 4 * br >= a.H || c0 + 8 * bc >= a.W) continue;  // no token of the block is on the grid
+  const int head = __builtin_amdgcn_readfirstlane(b % a.heads);
+  const int hidden = __builtin_amdgcn_readfirstlane(a.hidden), nhb = hidden / 32, T = a.T;
+  const unsigned char* cQ = buf + L.q;
+  const unsigned char* cK = buf + L.k;
+  int slot[2], ccell[2];
+  bool on[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int blk = pw + kRoleWaves * q, br = blk / CB, bc = blk % CB;
+    on[q] = blk < nblk && r0 + 4 * br < a.H && c0 + 8 * bc < a.W;  // a token of the block is on the grid
     const int tr = 4 * br + (n >> 3), tc = 8 * bc + (n & 7);
-    predict_weights<Tr>(a, b, buf + L.q, buf + L.k, tr * a.TC + tc, (tr + 1) * CW + (tc + 1),
-                        reinterpret_cast<float*>(buf + L.w));
+    slot[q] = tr * a.TC + tc;
+    ccell[q] = (tr + 1) * CW + (tc + 1);
+  }
+  f32x16 lg[2] = {};
+#pragma unroll 1
+  for (int hb = 0; hb < nhb; ++hb) {
+    if (hb > 0) pr.load(a, head, hb);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (!on[q]) continue;
+      f32x16 c = {};
+      if constexpr (MlpRegs<Tr>::kBf16) {
+        bf16x8 xb[8];
+#pragma unroll
+        for (int st = 0; st < 8; ++st)
+          xb[st] = *reinterpret_cast<const bf16x8*>(st < 4 ? cQ + row_off<BF16>(slot[q], 16 * st + 8 * h)
+                                                           : cK + row_off<BF16>(ccell[q], 16 * (st - 4) + 8 * h));
+#pragma unroll
+        for (int st = 0; st < 8; ++st) c = mma(pr.fh[st], xb[st], c);
+      } else {
+#pragma unroll
+        for (int st = 0; st < 64; ++st) {
+          const unsigned char* src = st < 32 ? cQ + row_off<F32>(slot[q], 2 * st + h)
+                                             : cK + row_off<F32>(ccell[q], 2 * (st - 32) + h);
+          c = mma(pr.fw[st], *reinterpret_cast<const float*>(src), c);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) lg[q] = mma(pr.w2[i], fmaxf(c[i] + pr.b1[i], 0.f), lg[q]);
+    }
+  }
+  float* cW = reinterpret_cast<float*>(buf + L.w);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    if (!on[q]) continue;
+    float v[4], mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int k = 4 * h + e;
+      v[e] = k < T ? lg[q][e] + a.mlp_b2[head * T + k] : 0.f;
+      if (k < T) mx = fmaxf(mx, v[e]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    float sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = 4 * h + e < T ? __expf(v[e] - mx) : 0.f;
+      sum += v[e];
+    }
+    sum += __shfl_xor(sum, 32);
+    const float inv = 1.f / sum;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (4 * h + e < T) cW[slot[q] * T + 4 * h + e] = v[e] * inv;
   }
 }
 
@@ -488,6 +523,8 @@ __device__ void prepare(const FlowArgs& a, const Rank& rk, Pos p, unsigned char*
     }
     wait_all();
   } else if (p.ph == kPOut) {
+    MlpRegs<Tr> pr;
+    if constexpr (kMlp) pr.load(a, __builtin_amdgcn_readfirstlane(b % a.heads), 0);  // lands during the DMA
     stage_tile<Tr>(a, b, rk.t0 + p.j, buf, pw);
     if (p.j == 0) {
       if (a.do_kv) dependency(kCntC);
@@ -502,7 +539,7 @@ __device__ void prepare(const FlowArgs& a, const Rank& rk, Pos p, unsigned char*
     wait_all();
     if constexpr (kMlp) {
       producers_meet(mlp_ready);
-      predict_tile<Tr>(a, b, rk.t0 + p.j, buf, pw);
+      predict_tile<Tr>(a, b, rk.t0 + p.j, buf, pw, pr);
     }
     if (a.T >= 2) finish_tile<Tr>(a, layout_of<Tr>(a), buf, s_w, pw);
   }
@@ -1076,31 +1113,28 @@ hipError_t launch_typed(const FlowArgs& a, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-// W1 fragments for predict_weights: one thread per (head, block, step, lane).
+// W1 [heads][hidden][2 d_h] rearranged per head as MlpRegs reads it: one
+// thread per (head, hidden block, lane).
 template <class Tr>
-__global__ __launch_bounds__(256) void mlp_prep(const float* w1, void* frag, int heads, int hidden) {
+__global__ __launch_bounds__(256) void mlp_prep(const float* w1, float* out, int heads, int hidden) {
   constexpr bool kBf16 = Tr::EPL == 8;
-  constexpr int kSteps = kBf16 ? 8 : 64;
-  const int total = heads * (hidden / 32) * kSteps * 64;
+  const int nhb = hidden / 32;
   const int id = blockIdx.x * 256 + threadIdx.x;
-  if (id >= total) return;
-  const int lane = id % 64, st = (id / 64) % kSteps, blk = id / (64 * kSteps);  // blk = head * nhb + hb
-  const int nhb = hidden / 32, head = blk / nhb, hb = blk % nhb;
+  if (id >= heads * nhb * 64) return;
+  const int lane = id % 64, hb = (id / 64) % nhb, head = id / (64 * nhb);
   const int m = lane % 32, h = lane / 32;
+  float* blk = out + (size_t)head * mlp_head_floats(hidden, kBf16);
   const float* row = w1 + ((size_t)head * hidden + 32 * hb + m) * (2 * kD);
   if constexpr (kBf16) {
-    bf16x8 hi, lo;
+    bf16x8* f = reinterpret_cast<bf16x8*>(blk) + (size_t)hb * 8 * 64;
+    for (int st = 0; st < 8; ++st) {
+      bf16x8 v;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float v = row[16 * st + 8 * h + e];
-      const __bf16 vh = (__bf16)v;
-      hi[e] = vh;
-      lo[e] = (__bf16)(v - (float)vh);
+      for (int e = 0; e < 8; ++e) v[e] = (__bf16)row[16 * st + 8 * h + e];
+      f[st * 64 + lane] = v;
     }
-    static_cast<bf16x8*>(frag)[(size_t)id * 2] = hi;
-    static_cast<bf16x8*>(frag)[(size_t)id * 2 + 1] = lo;
   } else {
-    static_cast<float*>(frag)[id] = row[2 * st + h];
+    for (int st = 0; st < 64; ++st) blk[((size_t)hb * 64 + st) * 64 + lane] = row[2 * st + h];
   }
 }
 
@@ -1112,17 +1146,16 @@ hipError_t launch_flow(int dtype, const FlowArgs& a, int grid, hipStream_t s) {
 }
 
 size_t mlp_frag_bytes(int dtype, int heads, int hidden) {
-  (void)dtype;  // bf16: high and low parts, 2 + 2 bytes per W1 element; fp32: 4 bytes
-  return (size_t)heads * hidden * 2 * kD * 4;
+  return (size_t)heads * mlp_head_floats(hidden, dtype == 1) * sizeof(float);
 }
 
-hipError_t launch_mlp_prep(int dtype, const float* w1, void* frag, int heads, int hidden, hipStream_t s) {
-  const int total = heads * (hidden / 32) * (dtype == 1 ? 8 : 64) * 64;
-  const dim3 grid((total + 255) / 256);
+hipError_t launch_mlp_prep(int dtype, const float* w1, void* block, int heads, int hidden, hipStream_t s) {
+  const dim3 grid((heads * (hidden / 32) * 64 + 255) / 256);
+  float* out = static_cast<float*>(block);
   if (dtype == 1)
-    hipLaunchKernelGGL(mlp_prep<BF16>, grid, dim3(256), 0, s, w1, frag, heads, hidden);
+    hipLaunchKernelGGL(mlp_prep<BF16>, grid, dim3(256), 0, s, w1, out, heads, hidden);
   else
-    hipLaunchKernelGGL(mlp_prep<F32>, grid, dim3(256), 0, s, w1, frag, heads, hidden);
+    hipLaunchKernelGGL(mlp_prep<F32>, grid, dim3(256), 0, s, w1, out, heads, hidden);
   return hipGetLastError();
 }
 

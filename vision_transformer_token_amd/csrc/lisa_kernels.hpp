@@ -98,7 +98,8 @@ struct FlowArgs {
   unsigned* tickets;      // [kXcds] rank tickets
   unsigned* err;          // error word (a dependency wait timed out)
   // Walk-weight predictor (weights == nullptr): w_i = softmax(W2 ReLU(W1 x_i + b1) + b2),
-  // x_i = concat(Q_i, K_i), per head; W1 as MFMA fragments (launch_mlp_prep).
+  // x_i = concat(Q_i, K_i), per head; W1 in the order the kernel's lanes
+  // read it (launch_mlp_prep).
   const void* mlp_w1f;    // nullptr: no predictor
   const float* mlp_b1;    // [heads][hidden]
   const float* mlp_w2;    // [heads][T][hidden]
@@ -111,11 +112,10 @@ constexpr int kMaxHidden = 128;
 // dtype: 0 = fp32, 1 = bf16 (lisa_dtype).  grid = workgroups to launch.
 hipError_t launch_flow(int dtype, const FlowArgs& a, int grid, hipStream_t s);
 
-// W1 [heads][hidden][2 d_h] (fp32) as the A operands of the predictor's
-// first layer: bf16, per (head, 32-row block, 16-wide step, lane) its high
-// and low bf16x8 parts; fp32, per (head, block, 2-wide step, lane) one float.
+// W1 [heads][hidden][2 d_h] (fp32) rearranged into the A operands of the
+// predictor's first layer, per head (bf16 inputs: W1 rounded to bf16).
 size_t mlp_frag_bytes(int dtype, int heads, int hidden);
-hipError_t launch_mlp_prep(int dtype, const float* w1, void* frag, int heads, int hidden, hipStream_t s);
+hipError_t launch_mlp_prep(int dtype, const float* w1, void* block, int heads, int hidden, hipStream_t s);
 
 // Backward pass (lisa_backward): token passes take kBwdTokens tokens per
 // workgroup, one per lane; the slice statistics come from a statistics launch
