@@ -110,7 +110,10 @@ KERNEL = "flow_kernel<bf16>"  # the one kernel of the path (one launch per forwa
 
 def _short(name):
     if "flow_kernel" in name:
-        return "flow_kernel<bf16>" if "BF16" in name else "flow_kernel<fp32>"
+        t = "bf16" if "BF16" in name else "fp32"
+        return f"flow_kernel<{t}, predictor>" if ", true>" in name else f"flow_kernel<{t}>"
+    if "mlp_prep" in name:
+        return "mlp_prep<bf16>" if "BF16" in name else "mlp_prep<fp32>"
     if "copyBuffer" in name:
         return "copyBuffer"
     m = re.search(r"(bwd_\w+)(<(unsigned short|float)>)?", name)
@@ -221,6 +224,33 @@ def summarize_backward(outdir, workload, command):
         f.write("\n".join(lines) + "\n")
 
 
+def summarize_mlp(outdir, workload, command):
+    """profiles/ summary of a rocprofv3 kernel trace of bench.py --mlp-only."""
+    from vision_transformer_token_amd import workloads
+
+    w = workloads.get(workload)
+    stats = _csv_rows(os.path.join(outdir, "prof_mlp", "mlp_kernel_stats.csv"))
+    lines = [f"# rocprofv3 kernel trace of lisa_forward_mlp (walk weights predicted, hidden 64), "
+             f"workload {w.describe()}", "", f"command: {command}", "",
+             "| kernel | calls | average ns | min ns | max ns | share |", "|---|---|---|---|---|---|"]
+    total_ns = 0.0
+    for r in stats:
+        name = _short(r["Name"])
+        if not (name.startswith("flow_kernel") or name.startswith("mlp_prep")):
+            continue
+        total_ns += float(r["AverageNs"])
+        lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} | "
+                     f"{float(r['Percentage']):.1f}% |")
+    bb = compulsory_bytes_per_token_head(w) - (4 * w.T if w.mode == "adaptive" else 0)
+    lines += ["", f"sum of the kernels' averages per call: {total_ns / 1e3:.1f} us "
+                  f"(mlp_prep lays W1 out for the kernel's lanes)",
+              f"algorithmic bytes per call: {w.token_heads * bb / 1e6:.2f} MB ({bb} B per token-head: "
+              f"no weight tensor); at 8 TB/s: {w.token_heads * bb / 8e12 * 1e6:.1f} us",
+              f"kernel source hash: {kernel_source_hash()}"]
+    with open(os.path.join(ROOT, "profiles", f"lisa_forward_mlp_{w.name}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -239,6 +269,8 @@ def main():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="instead of LiSA, run 20 plain device copies of this many MiB "
                          "(the known-size kernel that scales the FETCH_SIZE/WRITE_SIZE counters)")
+    ap.add_argument("--summarize-mlp", metavar="DIR",
+                    help="write the profiles/ summary of a lisa_forward_mlp kernel trace under DIR and exit")
     ap.add_argument("--summarize-backward", metavar="DIR",
                     help="write the profiles/ summary of a backward kernel trace under DIR and exit")
     ap.add_argument("--summarize-profiles", metavar="DIR",
@@ -259,6 +291,13 @@ def main():
                     "-o c{fetch|write} -- python3 bench.py --calibrate-copy-mib 256",
             "copy_mib": 256,
         })
+        return
+
+    if args.summarize_mlp:
+        summarize_mlp(args.summarize_mlp, args.workload,
+                      "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_mlp -o mlp -- "
+                      "python3 bench.py --mlp-only --steps 100 --warmup 10 --no-cpu-baseline --workload "
+                      + args.workload)
         return
 
     if args.summarize_backward:

@@ -1114,27 +1114,29 @@ hipError_t launch_typed(const FlowArgs& a, int grid, hipStream_t s) {
 }
 
 // W1 [heads][hidden][2 d_h] rearranged per head as MlpRegs reads it: one
-// thread per (head, hidden block, lane).
+// thread per (head, hidden block, step, lane).
 template <class Tr>
 __global__ __launch_bounds__(256) void mlp_prep(const float* w1, float* out, int heads, int hidden) {
   constexpr bool kBf16 = Tr::EPL == 8;
+  constexpr int kSteps = kBf16 ? 8 : 64;
   const int nhb = hidden / 32;
   const int id = blockIdx.x * 256 + threadIdx.x;
-  if (id >= heads * nhb * 64) return;
-  const int lane = id % 64, hb = (id / 64) % nhb, head = id / (64 * nhb);
+  if (id >= heads * nhb * kSteps * 64) return;
+  const int lane = id % 64, st = (id / 64) % kSteps, hb = (id / (64 * kSteps)) % nhb;
+  const int head = id / (64 * kSteps * nhb);
   const int m = lane % 32, h = lane / 32;
   float* blk = out + (size_t)head * mlp_head_floats(hidden, kBf16);
   const float* row = w1 + ((size_t)head * hidden + 32 * hb + m) * (2 * kD);
   if constexpr (kBf16) {
-    bf16x8* f = reinterpret_cast<bf16x8*>(blk) + (size_t)hb * 8 * 64;
-    for (int st = 0; st < 8; ++st) {
-      bf16x8 v;
+    const float4 lo4 = *reinterpret_cast<const float4*>(row + 16 * st + 8 * h);
+    const float4 hi4 = *reinterpret_cast<const float4*>(row + 16 * st + 8 * h + 4);
+    const float v[8] = {lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
+    bf16x8 r;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (__bf16)row[16 * st + 8 * h + e];
-      f[st * 64 + lane] = v;
-    }
+    for (int e = 0; e < 8; ++e) r[e] = (__bf16)v[e];
+    reinterpret_cast<bf16x8*>(blk)[((size_t)hb * 8 + st) * 64 + lane] = r;
   } else {
-    for (int st = 0; st < 64; ++st) blk[((size_t)hb * 64 + st) * 64 + lane] = row[2 * st + h];
+    blk[((size_t)hb * 64 + st) * 64 + lane] = row[2 * st + h];
   }
 }
 
@@ -1150,7 +1152,7 @@ size_t mlp_frag_bytes(int dtype, int heads, int hidden) {
 }
 
 hipError_t launch_mlp_prep(int dtype, const float* w1, void* block, int heads, int hidden, hipStream_t s) {
-  const dim3 grid((heads * (hidden / 32) * 64 + 255) / 256);
+  const dim3 grid((heads * (hidden / 32) * (dtype == 1 ? 8 : 64) * 64 + 255) / 256);
   float* out = static_cast<float*>(block);
   if (dtype == 1)
     hipLaunchKernelGGL(mlp_prep<BF16>, grid, dim3(256), 0, s, w1, out, heads, hidden);
