@@ -21,6 +21,9 @@ powers of S, branch isolation, planted mistakes).
 MLP on concat(Q_i, K_i) and a softmax), pinned by
 ``tests/test_oracle_predictor_pins.py``.
 
+``oracle.layer`` holds a LiSA attention layer (QKV projection, heads, the
+operator, output projection), pinned by ``tests/test_oracle_layer_pins.py``.
+
 Every function of ``oracle.lisa`` is pinned by ``tests/test_oracle_pins.py``
 to facts other than itself (brute force on tiny grids, closed forms,
 invariants, hand-derived examples under ``tests/golden/``).  The one place
@@ -42,6 +45,7 @@ from .lisa import (  # noqa: F401
     neighbour_offsets,
 )
 from .predictor import predicted_weights, lisa_forward_mlp  # noqa: F401
+from .layer import lisa_layer  # noqa: F401
 from .backward import (  # noqa: F401
     global_branch_backward,
     local_branch_backward,
