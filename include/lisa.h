@@ -166,6 +166,29 @@ lisa_status lisa_forward_mlp(const lisa_problem* p, const void* Q, const void* K
                              const lisa_weight_mlp* mlp, const float* alpha, void* Y,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* A LiSA attention layer around the operator [note §2.1: n tokens X are
+ * projected to Q, K, V; the operator replaces the attention of DeiT-T and
+ * PVT-T]: [Q | K | V] = X Wqkv^T + bqkv, head h taking channels
+ * 64 h .. 64 h + 63, O = lisa_forward(Q, K, V) per head, and
+ * Y = concat_h(O_h) Wo^T + bo.  C = heads * 64 (p->d_h = p->d_v = 64).
+ *   X     : [batch, n, C], dtype of the problem (device)
+ *   w_qkv : [3 C, C] (the torch Linear layout: out x in), dtype of the problem
+ *   b_qkv : [3 C] fp32
+ *   w_o   : [C, C], dtype of the problem;  b_o : [C] fp32
+ *   weights, beta, alpha : as for lisa_forward
+ *   Y     : [batch, n, C], dtype of the problem; X and Y must not overlap
+ *           each other or the workspace (LISA_ERR_PARAM)
+ * Q, K, V and O live in the workspace (lisa_attention_workspace_size bytes,
+ * 256-byte aligned, zero-filled before its first use), in the problem's
+ * dtype: with bf16 inputs each is rounded once, as between separate layers.
+ * The projections run on MFMA with fp32 sums.  Errors as for lisa_forward;
+ * X, Y and the weights need 16-byte alignment, the biases 4. */
+size_t lisa_attention_workspace_size(const lisa_problem* p);
+lisa_status lisa_attention_forward(const lisa_problem* p, const void* X, const void* w_qkv,
+                                   const float* b_qkv, const void* w_o, const float* b_o,
+                                   const float* weights, float beta, const float* alpha, void* Y,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* Backward pass: the gradients of lisa_forward's Y, contracted with the
  * output gradient dY, for every input.  The note trains every model it
  * reports [note §3] and gives no backward formulas; these are the exact

@@ -25,8 +25,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == [
-        "lisa_apply", "lisa_backward", "lisa_backward_workspace_size", "lisa_forward", "lisa_forward_mlp",
-        "lisa_forward_mlp_workspace_size", "lisa_reduce", "lisa_status_str", "lisa_workspace_size"]
+        "lisa_apply", "lisa_attention_forward", "lisa_attention_workspace_size", "lisa_backward",
+        "lisa_backward_workspace_size", "lisa_forward", "lisa_forward_mlp", "lisa_forward_mlp_workspace_size",
+        "lisa_reduce", "lisa_status_str", "lisa_workspace_size"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -214,4 +215,40 @@ def test_mlp_argument_errors():
     p = prob()
     assert forward_mlp(p, ws_bytes=lisa.lisa_workspace_size(p)) == WS
     assert forward_mlp(p, ws=None) == WS
+
+
+X_, WQ_, BQ_, WO_, BO_ = (A + (24 + i) * 0x1000000 for i in range(5))
+
+
+def attention(p, x=X_, wq=WQ_, bq=BQ_, wo=WO_, bo=BO_, w=W_, beta=0.5, alpha=AL, y=Y, ws=WS_, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lisa.lisa_attention_workspace_size(p) if p is not None else 0
+    return lib.lisa_attention_forward(None if p is None else ctypes.byref(p), x, wq, bq, wo, bo, w,
+                                      ctypes.c_float(beta), alpha, y, ws, ctypes.c_size_t(ws_bytes), None)
+
+
+def test_attention_workspace_size():
+    p = prob(grid_h=40, grid_w=33)
+    tensor = 2 * 3 * 40 * 33 * 64 * 2
+    assert lisa.lisa_attention_workspace_size(p) >= lisa.lisa_workspace_size(p) + 4 * tensor
+    assert lisa.lisa_attention_workspace_size(prob(T=9)) == 0
+
+
+def test_attention_argument_errors():
+    assert attention(None) == NULL
+    assert attention(prob(dtype=3)) == DTYPE
+    assert attention(prob(grid_h=0)) == SHAPE
+    assert attention(prob(d_h=32)) == UNSUP
+    assert attention(prob(T=9)) == PARAM
+    assert attention(prob(), w=None, beta=1.0) == PARAM
+    for name in ("x", "wq", "bq", "wo", "bo", "alpha", "y"):
+        assert attention(prob(), **{name: None}) == NULL, name
+    assert attention(prob(), x=X_ + 8) == ALIGN
+    assert attention(prob(), wo=WO_ + 4) == ALIGN
+    assert attention(prob(), bq=BQ_ + 2) == ALIGN
+    p = prob()
+    assert attention(p, ws_bytes=lisa.lisa_workspace_size(p)) == WS
+    assert attention(p, ws=None) == WS
+    assert attention(p, y=X_) == PARAM
+    assert attention(p, y=WS_) == PARAM
 

@@ -395,6 +395,61 @@ lisa_status lisa_forward_mlp(const lisa_problem* p, const void* Q, const void* K
   return run(pl, Mode::kForward, Q, K, V, nullptr, 0.f, alpha, Y, ws, p->eps, s, mlp, ws + frag_at);
 }
 
+size_t lisa_attention_workspace_size(const lisa_problem* p) {
+  Plan pl;
+  if (make_plan(p, pl) != LISA_OK) return 0;
+  const size_t tensor = up((size_t)pl.BH * pl.n * kD * pl.esize, kAlign);
+  return up(pl.total, kAlign) + 4 * tensor;  // the operator's regions, then Q, K, V, O
+}
+
+lisa_status lisa_attention_forward(const lisa_problem* p, const void* X, const void* w_qkv,
+                                   const float* b_qkv, const void* w_o, const float* b_o,
+                                   const float* weights, float beta, const float* alpha, void* Y,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  Plan pl;
+  lisa_status st = make_plan(p, pl);
+  if (st != LISA_OK) return st;
+  if (!weights && !(beta >= 0.f && beta < 1.f)) return LISA_ERR_PARAM;
+  if (!X || !w_qkv || !b_qkv || !w_o || !b_o || !alpha || !Y) return LISA_ERR_NULL;
+  if (misaligned(X, 16) || misaligned(w_qkv, 16) || misaligned(w_o, 16) || misaligned(Y, 16) ||
+      misaligned(b_qkv, 4) || misaligned(b_o, 4) || misaligned(weights, 4) || misaligned(alpha, 4))
+    return LISA_ERR_ALIGN;
+  const size_t tensor = (size_t)pl.BH * pl.n * kD * pl.esize;  // one of Q, K, V, O; also X and Y
+  const size_t at = up(pl.total, kAlign), step = up(tensor, kAlign);
+  const size_t need = at + 4 * step;
+  if (!workspace || workspace_bytes < need || misaligned(workspace, kAlign)) return LISA_ERR_WORKSPACE;
+  if (overlaps(Y, tensor, X, tensor) || overlaps(Y, tensor, workspace, need) || overlaps(X, tensor, workspace, need))
+    return LISA_ERR_PARAM;
+  (void)hipGetLastError();
+  char* ws = static_cast<char*>(workspace);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* q = ws + at;
+  char* o = ws + at + 3 * step;
+  lisa::ProjArgs pa{};
+  pa.M = p->batch * pl.n;
+  pa.K = pl.heads * kD;
+  pa.n = pl.n;
+  pa.heads = pl.heads;
+  pa.head_elems = step / pl.esize;
+  // [Q | K | V] = X Wqkv^T + bqkv, into the heads layout.
+  pa.A = X;
+  pa.Wt = w_qkv;
+  pa.bias = b_qkv;
+  pa.out = q;
+  pa.N = 3 * pa.K;
+  if (lisa::launch_proj(pl.dtype, false, pa, s) != hipSuccess) return LISA_ERR_HIP;
+  st = run(pl, Mode::kForward, q, q + step, q + 2 * step, weights, beta, alpha, o, ws, p->eps, s);
+  if (st != LISA_OK) return st;
+  // Y = concat_h(O_h) Wo^T + bo.
+  pa.A = o;
+  pa.Wt = w_o;
+  pa.bias = b_o;
+  pa.out = Y;
+  pa.N = pa.K;
+  if (lisa::launch_proj(pl.dtype, true, pa, s) != hipSuccess) return LISA_ERR_HIP;
+  return LISA_OK;
+}
+
 size_t lisa_backward_workspace_size(const lisa_problem* p) {
   Plan pl;
   return make_plan(p, pl) == LISA_OK ? pl.btotal : 0;

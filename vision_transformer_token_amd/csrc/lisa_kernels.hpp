@@ -117,6 +117,22 @@ hipError_t launch_flow(int dtype, const FlowArgs& a, int grid, hipStream_t s);
 size_t mlp_frag_bytes(int dtype, int heads, int hidden);
 hipError_t launch_mlp_prep(int dtype, const float* w1, void* block, int heads, int hidden, hipStream_t s);
 
+// Projections of the attention layer (lisa_attention_forward):
+// out[m][c] = sum_k A[m][k] Wt[c][k] + bias[c] over the K = C = 64 heads
+// channels.  QKV: A = X [M][C], c < 3C goes to Q, K or V [B][heads][n][64]
+// (head_elems apart); output: A = O [B][heads][n][64] merged by heads,
+// out = Y [M][C].
+struct ProjArgs {
+  const void* A;
+  const void* Wt;         // [N][K], the input dtype
+  const float* bias;      // [N]
+  void* out;
+  int M, N, K;            // M = B n; N = 3C (QKV) or C; K = C
+  int n, heads;
+  size_t head_elems;      // B * heads * n * 64
+};
+hipError_t launch_proj(int dtype, bool out_proj, const ProjArgs& a, hipStream_t s);
+
 // Backward pass (lisa_backward): token passes take kBwdTokens tokens per
 // workgroup, one per lane; the slice statistics come from a statistics launch
 // (fin_s, fin_kv, fin_m of FlowArgs) that ran before on the same stream.

@@ -1,0 +1,120 @@
+// The projections of a LiSA attention layer on gfx950: [Q | K | V] =
+// X Wqkv^T + bqkv split into heads, and Y = concat_h(O_h) Wo^T + bo, with
+// the operator (lisa_flow.hip) in between.
+//
+// Source: the reading note of "LiSA: Linear Stochastic Attention for
+// Long-Range Visual Modeling" (arXiv:2611.04216v2) §2.1: n tokens X are
+// projected to Q, K and V; the operator is a plug-in replacing the attention
+// of DeiT-T and PVT-T.  The layer around it is the usual ViT attention block
+// (one QKV projection with bias, heads of 64 channels in order, an output
+// projection with bias).
+//
+// Both projections are contractions over the channels on MFMA with fp32
+// sums; the head split (QKV) and merge (output) are folded into the
+// addressing, so neither is a pass of its own.  A workgroup computes a
+// 64 x 64 block of outputs, wave w its rows 16 w .. 16 w + 15 as four 16 x 16
+// MFMA blocks; both operands are read straight from HBM / L2 with 16-byte
+// loads (rows of X, of a head's O and of the torch-layout weights [out][in]
+// are contiguous along the contraction).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lisa_device.hpp"
+#include "lisa_kernels.hpp"
+
+namespace lisa {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// A[m][k]: QKV, X [M][C] row-major; output projection, O [B][heads][n][64].
+template <bool kOut>
+__device__ __forceinline__ size_t a_index(const ProjArgs& a, int m, int k) {
+  if constexpr (!kOut) return (size_t)m * a.K + k;
+  const int b = m / a.n, tok = m % a.n, h = k / kD, d = k % kD;
+  return (((size_t)b * a.heads + h) * a.n + tok) * kD + d;
+}
+// Output (m, c): QKV, channel c of [Q | K | V] into its head-major tensor;
+// output projection, Y [M][C] row-major.
+template <bool kOut>
+__device__ __forceinline__ size_t out_index(const ProjArgs& a, int m, int c) {
+  if constexpr (kOut) return (size_t)m * a.N + c;
+  const int which = c / a.K, cc = c % a.K, h = cc / kD, d = cc % kD;
+  const int b = m / a.n, tok = m % a.n;
+  return (size_t)which * a.head_elems + (((size_t)b * a.heads + h) * a.n + tok) * kD + d;
+}
+
+template <class S, bool kOut>
+__global__ __launch_bounds__(256) void proj_gemm(ProjArgs a) {
+  const int t = threadIdx.x, w = t / 64, ln = t % 64, li = ln % 16, lk = ln / 16;
+  const int m0 = blockIdx.x * 64 + 16 * w, c0 = blockIdx.y * 64;
+  const int mr = m0 + li;  // the A row of this lane's operand
+  const bool mon = mr < a.M;
+  const S* A = static_cast<const S*>(a.A);
+  const S* Wt = static_cast<const S*>(a.Wt);
+  f32x4 acc[4] = {};
+  if constexpr (sizeof(S) == 2) {
+    // bf16 MFMA 16x16x32: lane (li, lk) holds contraction slots k0 + 8 lk .. + 7.
+    for (int k0 = 0; k0 < a.K; k0 += 32) {
+      const int k = k0 + 8 * lk;
+      bf16x8 av = {};
+      if (mon) av = *reinterpret_cast<const bf16x8*>(A + a_index<kOut>(a, mr, k));
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(Wt + (size_t)(c0 + 16 * ct + li) * a.K + k);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[ct], 0, 0, 0);
+      }
+    }
+  } else {
+    // fp32 MFMA 16x16x4: four of them per 16 inputs, lane (li, lk) taking
+    // inputs k0 + 4 lk + s in the s-th (one 16-byte read each).
+    for (int k0 = 0; k0 < a.K; k0 += 16) {
+      const int k = k0 + 4 * lk;
+      float4 av = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (mon) av = *reinterpret_cast<const float4*>(A + a_index<kOut>(a, mr, k));
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const float4 bv = *reinterpret_cast<const float4*>(Wt + (size_t)(c0 + 16 * ct + li) * a.K + k);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv.w, acc[ct], 0, 0, 0);
+      }
+    }
+  }
+  // acc[ct][e] is output (m0 + 4 lk + e, c0 + 16 ct + li).
+  S* out = static_cast<S*>(a.out);
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    const int c = c0 + 16 * ct + li;
+    const float bc = a.bias[c];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = m0 + 4 * lk + e;
+      if (m >= a.M) continue;
+      const float v = acc[ct][e] + bc;
+      if constexpr (sizeof(S) == 2)
+        out[out_index<kOut>(a, m, c)] = f2bf(v);
+      else
+        out[out_index<kOut>(a, m, c)] = v;
+    }
+  }
+}
+
+template <class S>
+hipError_t launch_proj_typed(bool out_proj, const ProjArgs& a, hipStream_t s) {
+  const dim3 grid((a.M + 63) / 64, a.N / 64);
+  if (out_proj)
+    hipLaunchKernelGGL((proj_gemm<S, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((proj_gemm<S, false>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_proj(int dtype, bool out_proj, const ProjArgs& a, hipStream_t s) {
+  return dtype == 1 ? launch_proj_typed<uint16_t>(out_proj, a, s) : launch_proj_typed<float>(out_proj, a, s);
+}
+
+}  // namespace lisa

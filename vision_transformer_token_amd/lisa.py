@@ -19,6 +19,8 @@ __all__ = [
     "lisa_workspace_size",
     "lisa_forward",
     "lisa_forward_mlp",
+    "lisa_attention_forward",
+    "lisa_attention_workspace_size",
     "lisa_forward_mlp_workspace_size",
     "WeightMlp",
     "lisa_reduce",
@@ -91,6 +93,11 @@ _lib.lisa_forward_mlp_workspace_size.argtypes = [_P, ctypes.c_int32]
 _lib.lisa_forward_mlp_workspace_size.restype = ctypes.c_size_t
 _lib.lisa_forward_mlp.argtypes = [_P, _vp, _vp, _vp, ctypes.POINTER(WeightMlp), _vp, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.lisa_forward_mlp.restype = ctypes.c_int
+_lib.lisa_attention_workspace_size.argtypes = [_P]
+_lib.lisa_attention_workspace_size.restype = ctypes.c_size_t
+_lib.lisa_attention_forward.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
+                                        ctypes.c_size_t, _vp]
+_lib.lisa_attention_forward.restype = ctypes.c_int
 _lib.lisa_backward_workspace_size.argtypes = [_P]
 _lib.lisa_backward_workspace_size.restype = ctypes.c_size_t
 _lib.lisa_backward.argtypes = [_P, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -223,6 +230,39 @@ def lisa_forward_mlp(q, k, v, *, grid, T, alpha, w1, b1, w2, b2, eps=1e-6, out=N
                                _stream(stream, q.device))
     if st != LISA_OK:
         raise LisaError(st, "lisa_forward_mlp")
+    return out
+
+
+def lisa_attention_workspace_size(problem):
+    return int(_lib.lisa_attention_workspace_size(ctypes.byref(problem)))
+
+
+def lisa_attention_forward(x, w_qkv, b_qkv, w_o, b_o, *, heads, grid, T, alpha, weights=None, beta=None,
+                           eps=1e-6, out=None, workspace=None, stream=None):
+    """The LiSA attention layer: x [B, n, C] (bf16 or fp32, C = 64 heads),
+    w_qkv [3C, C] and w_o [C, C] in x's dtype, b_qkv [3C] and b_o [C] fp32;
+    see include/lisa.h."""
+    _check_tensors(x=x, w_qkv=w_qkv, b_qkv=b_qkv, w_o=w_o, b_o=b_o, alpha=alpha, weights=weights, out=out,
+                   workspace=workspace)
+    if weights is None and beta is None:
+        raise ValueError("give adaptive weights or beta")
+    B, n, C = x.shape
+    if C != 64 * heads:
+        raise ValueError("x's channels must be 64 * heads")
+    prob = Problem(B, heads, grid[0], grid[1], 64, 64, T, _dtype_code(x), eps)
+    if workspace is None:
+        nbytes = lisa_attention_workspace_size(prob)
+        if nbytes == 0:
+            raise LisaError(2, "lisa_attention_workspace_size")
+        workspace = torch.zeros(nbytes, dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty_like(x)
+    st = _lib.lisa_attention_forward(
+        ctypes.byref(prob), _ptr(x), _ptr(w_qkv), _ptr(b_qkv), _ptr(w_o), _ptr(b_o), _ptr(weights),
+        ctypes.c_float(0.0 if beta is None else beta), _ptr(alpha), _ptr(out), _ptr(workspace),
+        ctypes.c_size_t(workspace.numel()), _stream(stream, x.device))
+    if st != LISA_OK:
+        raise LisaError(st, "lisa_attention_forward")
     return out
 
 

@@ -147,5 +147,24 @@ def mlp_params(heads, hidden, T, d_h=64, seed=0):
     }
 
 
+def layer_params(w, seed=None):
+    """Input and parameters of a LiSA attention layer for workload ``w``
+    (C = 64 heads channels), as CPU tensors: x [B, n, C] and w_qkv [3C, C],
+    w_o [C, C] in the workload dtype, b_qkv [3C] and b_o [C] fp32.  The
+    projections keep Q, K, V of unit scale."""
+    rng = np.random.default_rng((w.seed if seed is None else seed) + 7)
+    C = 64 * w.heads
+    x = rng.standard_normal((w.B, w.n, C), dtype=np.float32)
+    wqkv = (rng.standard_normal((3 * C, C)) / np.sqrt(C)).astype(np.float32)
+    wo = (rng.standard_normal((C, C)) / np.sqrt(C)).astype(np.float32)
+    return {
+        "x": _to_dtype(x, w.dtype),
+        "w_qkv": _to_dtype(wqkv, w.dtype),
+        "b_qkv": torch.from_numpy((rng.standard_normal(3 * C) * 0.1).astype(np.float32)),
+        "w_o": _to_dtype(wo, w.dtype),
+        "b_o": torch.from_numpy((rng.standard_normal(C) * 0.1).astype(np.float32)),
+    }
+
+
 def with_changes(w, **kw):
     return replace(w, **kw)
