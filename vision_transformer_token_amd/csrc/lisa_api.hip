@@ -119,9 +119,13 @@ bool plan_tiles(Plan& pl, bool per_token_weights) {
 // Workgroups per slice: kRoundSlices times as many as there are workgroups
 // per slice of the grid (so that a group has that many slices to
 // interleave), at most one per 128 tokens and kMaxRanks, rounded down to a
-// power of two (the combine splits the 8192 statistics evenly).
+// power of two (the combine splits the 8192 statistics evenly).  One slice
+// per group won over two on every workload measured: fewer ranks per slice
+// write fewer partials and wait for fewer arrivals, which outweighs the
+// overlap of one slice's waits with another's stages (PVT stage 1, G = 8
+// vs 16: 49.3 vs 50.4 us; DeiT-T 384: 63.1 vs 67.5 us).
 #ifndef LISA_ROUND_SLICES
-#define LISA_ROUND_SLICES 2
+#define LISA_ROUND_SLICES 1
 #endif
 constexpr int kRoundSlices = LISA_ROUND_SLICES;
 

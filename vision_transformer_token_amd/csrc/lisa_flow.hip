@@ -175,13 +175,15 @@ __device__ __forceinline__ void chunk_of(const FlowArgs& a, const Rank& r, int j
 // ---------------------------------------------------------------------------
 // Producer side (pw = producer wave, 0..3).
 // ---------------------------------------------------------------------------
-// DMA of a KV / M chunk: its K rows, and its V (KV) or Q (M) rows.
+// DMA of a KV / M chunk: its K rows (unless the buffer still holds them),
+// and its V (KV) or Q (M) rows.
 template <class Tr>
-__device__ void stage_chunk(const FlowArgs& a, int b, bool is_m, int tok0, int nv, unsigned char* buf, int pw) {
+__device__ void stage_chunk(const FlowArgs& a, int b, bool is_m, int tok0, int nv, unsigned char* buf, int pw,
+                            bool with_k) {
   using S = typename Tr::S;
   const S* Kb = static_cast<const S*>(a.K) + ((size_t)b * a.n + tok0) * kD;
   const S* Xb = static_cast<const S*>(is_m ? a.Q : a.V) + ((size_t)b * a.n + tok0) * kD;
-  dma_rows<Tr>(buf, nv, [&](int r) { return static_cast<const void*>(Kb + (size_t)r * kD); }, pw);
+  if (with_k) dma_rows<Tr>(buf, nv, [&](int r) { return static_cast<const void*>(Kb + (size_t)r * kD); }, pw);
   dma_rows<Tr>(buf + LdsOf<Tr>::kXOff, nv, [&](int r) { return static_cast<const void*>(Xb + (size_t)r * kD); }, pw);
 }
 
@@ -229,6 +231,46 @@ __device__ void stage_tile(const FlowArgs& a, int b, int t, unsigned char* buf, 
   }
 }
 
+// bf16 rows staged by dma_rows: run j (1 KB) holds rows 8 j .. 8 j + 7 and
+// producer wave j % 4 issued it.  Lane l of wave pw takes slot l % 8 of row
+// 8 j + l / 8 in each of its runs j = pw, pw + 4, ...; that slot holds piece
+// g of the row, and since swz(r) depends only on r & 7 = l / 8 and on
+// (r >> 3) & 1 = j & 1 = pw & 1, g is the same in every run of the wave.
+// f(j, r, x, dot) is called per run with the run's eight elements of the
+// lane's piece after the ReLU, and dot = their product with s over the row
+// (s[8 g .. 8 g + 7] held in registers); runs go four at a time, all their
+// LDS reads issued before the first product.  `nrun` is wave-uniform.
+template <class F>
+__device__ __forceinline__ void bf16_row_dots(const unsigned char* base, int nrun, const float* s, int pw, F f) {
+  const int lane = threadIdx.x & 63;
+  const int slot = lane & 7, sub = lane >> 3;
+  const int g = (slot ^ swz(8 * pw + sub)) & 7;
+  const float4 s0 = *reinterpret_cast<const float4*>(s + 8 * g);
+  const float4 s1 = *reinterpret_cast<const float4*>(s + 8 * g + 4);
+  const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  for (int j0 = pw; j0 < nrun; j0 += 16) {
+    uint4 raw[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (j0 + 4 * u < nrun) raw[u] = *reinterpret_cast<const uint4*>(base + (8 * (j0 + 4 * u) + sub) * 128 + slot * 16);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + 4 * u;
+      if (j < nrun) {
+        const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+        float x[8];
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          x[e] = fmaxf(__uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16)), 0.f);
+          dot += x[e] * sv[e];
+        }
+        f(j, 8 * j + sub, x, group_sum8(dot));
+      }
+    }
+  }
+}
+
 // After the wave's own DMA has landed: zero the chunk's rows [nv, nvr) (the
 // sweeps read whole 16-row steps) and, for M chunks, rewrite each Q row as
 // r_j phi(Q_j) with r_j = 1 / (phi(Q_j) . s + eps).  A wave only touches the
@@ -242,6 +284,23 @@ __device__ void finish_chunk(const FlowArgs& a, int nv, unsigned char* buf, cons
   unsigned char* bK = buf;
   unsigned char* bX = buf + LdsOf<Tr>::kXOff;
   const int slot = lane % Tr::PPR;
+  if constexpr (kIsM && Tr::EPP == 8) {
+    bf16_row_dots(bX, nvr / RPR, s, pw, [&](int, int r, float (&x)[8], float dot) {
+      uint4* pK = reinterpret_cast<uint4*>(bK + r * Tr::RB + slot * 16);
+      uint4* pX = reinterpret_cast<uint4*>(bX + r * Tr::RB + slot * 16);
+      if (r < nv) {
+        const float rr = 1.f / (dot + a.eps);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] *= rr;
+        store4(reinterpret_cast<uint16_t*>(pX), x);
+        store4(reinterpret_cast<uint16_t*>(pX) + 4, x + 4);
+      } else {
+        *pK = make_uint4(0, 0, 0, 0);
+        *pX = make_uint4(0, 0, 0, 0);
+      }
+    });
+    return;
+  }
 #pragma unroll 2
   for (int j = pw; j * RPR < nvr; j += 4) {
     if (!kIsM && (j + 1) * RPR <= nv) continue;  // nothing to zero in this run
@@ -294,6 +353,12 @@ __device__ void finish_tile(const FlowArgs& a, const TileLayout& L, unsigned cha
   const int slot = lane % Tr::PPR;
   const unsigned char* bQ = buf + L.q;
   float* rr = reinterpret_cast<float*>(buf + L.r);
+  if constexpr (Tr::EPP == 8) {
+    bf16_row_dots(bQ, L.tokens / RPR, s, pw, [&](int, int r, float (&)[8], float dot) {
+      if (slot == 0) rr[r] = 1.f / (dot + a.eps);
+    });
+    return;
+  }
 #pragma unroll 2
   for (int j = pw; j * RPR < L.tokens; j += 4) {
     const int r = j * RPR + lane / Tr::PPR;
@@ -471,17 +536,19 @@ __device__ __forceinline__ void producers_meet(int* ready) {
 // start of an OUT phase, in the statistics area `st`: issue the DMA, wait for
 // the dependency, load what other workgroups wrote, wait, finish.  Only
 // producer wave 0 polls the arrival counter; it then posts `tag` in `dep_ok`,
-// which the other producer waves watch in LDS.  `s_w` is this wave's 64-float
-// scratch in LDS (s of the slice whose M chunks it prepares).
+// which the other producer waves watch in LDS.  `s_sl` holds s of each slice
+// of the round in LDS (row z for slice z); every producer wave forms the same
+// fixed-order sum and writes the same values.
 template <class Tr, bool kMlp>
 __device__ void prepare(const FlowArgs& a, const Rank& rk, Pos p, unsigned char* buf, unsigned char* st,
-                        float* s_w, volatile int* dep_ok, int* mlp_ready, int pw) {
+                        float (*s_sl)[kD], volatile int* dep_ok, int* mlp_ready, int pw) {
   using S = typename Tr::S;
   using L = LdsOf<Tr>;
   const int lane = threadIdx.x & 63;
   const int b = slice_of(a, rk, p.r, p.z);
   const unsigned* cnt = a.slice_cnt + (size_t)b * kCntStride;
   const unsigned full = a.G;
+  float* s_w = s_sl[p.z];
   auto dependency = [&](int counter) {
     const int tag = b * 4 + p.ph;
     if (pw == 0) {
@@ -497,7 +564,14 @@ __device__ void prepare(const FlowArgs& a, const Rank& rk, Pos p, unsigned char*
     const bool is_m = p.ph == kPM;
     int tok0, nv;
     chunk_of(a, rk, p.j, tok0, nv);
-    stage_chunk<Tr>(a, b, is_m, tok0, nv, buf, pw);
+    // Stages alternate between the two buffers, and a round runs the KV
+    // chunks of all its slices, then their M chunks in the same order.  When
+    // the round has two KV stages (one slice of two chunks, or two slices of
+    // one), M chunk j lands in the buffer that KV chunk j used two stages
+    // before: its K rows (ReLU applied on read, tail rows zeroed) are still
+    // there, and only the Q rows are fetched.
+    const bool keep_k = is_m && rk.nch * round_slices(a, rk, p.r) == 2;
+    stage_chunk<Tr>(a, b, is_m, tok0, nv, buf, pw, !keep_k);
     if (is_m && p.j == 0) {
       dependency(kCntKV);
       const float sv = sum_s_partials(a, b);
@@ -526,13 +600,21 @@ __device__ void prepare(const FlowArgs& a, const Rank& rk, Pos p, unsigned char*
     MlpRegs<Tr> pr;
     if constexpr (kMlp) pr.load(a, __builtin_amdgcn_readfirstlane(b % a.heads), 0);  // lands during the DMA
     stage_tile<Tr>(a, b, rk.t0 + p.j, buf, pw);
-    if (p.j == 0) {
+    // The statistics fragments, wanted once per slice.  With an M phase this
+    // round, s is already in s_w (formed for the M chunks), so the tile's r_i
+    // and predicted weights are computed before waiting for the combine;
+    // otherwise s comes from the workspace with the fragments.
+    auto load_stats = [&]() {
+      dma_linear_coherent(st, static_cast<const S*>(a.frag_kv) + (size_t)b * (kD * kD), L::kFragBytes, pw);
+      if (a.T >= 3)
+        dma_linear_coherent(st + L::kFragBytes, static_cast<const S*>(a.frag_m) + (size_t)b * (kD * kD),
+                            L::kFragBytes, pw);
+    };
+    const bool s_known = a.do_m;  // do_m implies do_kv and T >= 3
+    if (p.j == 0 && !s_known) {
       if (a.do_kv) dependency(kCntC);
       if (a.T >= 2) {
-        dma_linear_coherent(st, static_cast<const S*>(a.frag_kv) + (size_t)b * (kD * kD), L::kFragBytes, pw);
-        if (a.T >= 3)
-          dma_linear_coherent(st + L::kFragBytes, static_cast<const S*>(a.frag_m) + (size_t)b * (kD * kD),
-                              L::kFragBytes, pw);
+        load_stats();
         s_w[lane] = get(a.fin_s + (size_t)b * kD + lane);  // kept for the slice's later tiles
       }
     }
@@ -542,6 +624,11 @@ __device__ void prepare(const FlowArgs& a, const Rank& rk, Pos p, unsigned char*
       predict_tile<Tr>(a, b, rk.t0 + p.j, buf, pw, pr);
     }
     if (a.T >= 2) finish_tile<Tr>(a, layout_of<Tr>(a), buf, s_w, pw);
+    if (p.j == 0 && s_known) {
+      dependency(kCntC);
+      load_stats();
+      wait_all();
+    }
   }
 }
 
@@ -563,14 +650,44 @@ __device__ __forceinline__ void sweep_chunk(const unsigned char* buf, int nv, in
   const int nvr = (nv + 15) & ~15;
   const unsigned char* bK = buf;
   const unsigned char* bX = buf + LdsOf<Tr>::kXOff;
-#pragma unroll 2
-  for (int kk = 0; kk < nvr; kk += 16) {
-    if constexpr (Tr::EPL == 8) {
-      const bf16x8 A = as_bf16(rows_bits<true>(bK, kk, 32 * mb));
-      const bf16x8 B = as_bf16(rows_bits<false>(bX, kk, 32 * nb));
-      acc = mma(A, B, acc);
-      if (!kIsM && nb == 0) acc_s = mma(A, as_bf16((v8s)(short)0x3f80), acc_s);  // ones: bf16 1.0
-    } else {
+  if constexpr (Tr::EPL == 8) {
+    // Steps of 16 rows in batches of U: every operand read of a batch is
+    // issued before its first MFMA, so the LDS latency is paid once per batch.
+    const bf16x8 ones = as_bf16((v8s)(short)0x3f80);  // bf16 1.0
+    auto batch = [&](auto u_tag, auto s_tag, int kk) {
+      constexpr int U = decltype(u_tag)::value;
+      constexpr bool kS = decltype(s_tag)::value;
+      v8s A[U], B[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        A[u] = rows_bits<true>(bK, kk + 16 * u, 32 * mb);
+        B[u] = rows_bits<false>(bX, kk + 16 * u, 32 * nb);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        acc = mma(as_bf16(A[u]), as_bf16(B[u]), acc);
+        if constexpr (kS) acc_s = mma(as_bf16(A[u]), ones, acc_s);
+      }
+    };
+    auto sweep = [&](auto s_tag) {
+      int kk = 0;
+      for (; kk + 128 <= nvr; kk += 128) batch(std::integral_constant<int, 8>{}, s_tag, kk);
+      if (kk + 64 <= nvr) {
+        batch(std::integral_constant<int, 4>{}, s_tag, kk);
+        kk += 64;
+      }
+      if (kk + 32 <= nvr) {
+        batch(std::integral_constant<int, 2>{}, s_tag, kk);
+        kk += 32;
+      }
+      if (kk < nvr) batch(std::integral_constant<int, 1>{}, s_tag, kk);
+    };
+    if (!kIsM && nb == 0)  // these waves also sum phi(K) (s) against a ones operand
+      sweep(std::true_type{});
+    else
+      sweep(std::false_type{});
+  } else {
+    for (int kk = 0; kk < nvr; kk += 16) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int r = kk + 8 * h + q;
@@ -1019,7 +1136,7 @@ template <class Tr, bool kMlp>
 __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
   using L = LdsOf<Tr>;
   extern __shared__ __align__(1024) unsigned char smem[];
-  __shared__ float s_w[kRoleWaves][kD];  // producers: s of the slice whose M chunks they prepare
+  __shared__ __align__(16) float s_sl[4][kD];  // producers: s of each slice of the round (Z <= 4)
   __shared__ float geo_sh[kMaxT];        // geometric walk weights
   __shared__ int dep_ok;                 // tag of the stage whose dependency producer wave 0 has seen met
   __shared__ int last;                   // this workgroup's ticket, later: it finished last
@@ -1044,14 +1161,14 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
   // barriers: one per stage, plus one at the start of each OUT phase.
   if (producer) {
     Pos p = first_pos(a, rk);
-    if (p.ph != kPEnd) prepare<Tr, kMlp>(a, rk, p, smem, st, s_w[rw], &dep_ok, &mlp_ready, rw);
+    if (p.ph != kPEnd) prepare<Tr, kMlp>(a, rk, p, smem, st, s_sl, &dep_ok, &mlp_ready, rw);
     lds_barrier();
     int bsel = 0;
     while (p.ph != kPEnd) {
       const Pos np = advance(a, rk, p);
       if (p.ph == kPOut && p.j == 0) lds_barrier();  // the consumers have taken the statistics
       if (np.ph != kPEnd)
-        prepare<Tr, kMlp>(a, rk, np, smem + (bsel ^ 1) * L::kStage, st, s_w[rw], &dep_ok, &mlp_ready, rw);
+        prepare<Tr, kMlp>(a, rk, np, smem + (bsel ^ 1) * L::kStage, st, s_sl, &dep_ok, &mlp_ready, rw);
       lds_barrier();
       bsel ^= 1;
       p = np;
