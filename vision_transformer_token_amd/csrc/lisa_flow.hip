@@ -237,7 +237,8 @@ __device__ void stage_tile(const FlowArgs& a, int b, int t, unsigned char* buf, 
 // g of the row, and since swz(r) depends only on r & 7 = l / 8 and on
 // (r >> 3) & 1 = j & 1 = pw & 1, g is the same in every run of the wave.
 // f(j, r, x, dot) is called per run with the run's eight elements of the
-// lane's piece after the ReLU, and dot = their product with s over the row
+// lane's piece after the ReLU (applied to the bf16 bits: a negative bf16 is
+// a negative int16), and dot = their product with s over the row
 // (s[8 g .. 8 g + 7] held in registers); runs go four at a time, all their
 // LDS reads issued before the first product.  `nrun` is wave-uniform.
 template <class F>
@@ -257,12 +258,13 @@ __device__ __forceinline__ void bf16_row_dots(const unsigned char* base, int nru
     for (int u = 0; u < 4; ++u) {
       const int j = j0 + 4 * u;
       if (j < nrun) {
-        const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+        const v8s bits = __builtin_elementwise_max(__builtin_bit_cast(v8s, raw[u]), (v8s)0);
+        const u32x4 w = __builtin_bit_cast(u32x4, bits);
         float x[8];
         float dot = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          x[e] = fmaxf(__uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16)), 0.f);
+          x[e] = __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
           dot += x[e] * sv[e];
         }
         f(j, 8 * j + sub, x, group_sum8(dot));
@@ -289,11 +291,11 @@ __device__ void finish_chunk(const FlowArgs& a, int nv, unsigned char* buf, cons
       uint4* pK = reinterpret_cast<uint4*>(bK + r * Tr::RB + slot * 16);
       uint4* pX = reinterpret_cast<uint4*>(bX + r * Tr::RB + slot * 16);
       if (r < nv) {
-        const float rr = 1.f / (dot + a.eps);
+        const float rr = __builtin_amdgcn_rcpf(dot + a.eps);
+        u32x4 o;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] *= rr;
-        store4(reinterpret_cast<uint16_t*>(pX), x);
-        store4(reinterpret_cast<uint16_t*>(pX) + 4, x + 4);
+        for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(x[2 * e] * rr, x[2 * e + 1] * rr);
+        *reinterpret_cast<u32x4*>(pX) = o;
       } else {
         *pK = make_uint4(0, 0, 0, 0);
         *pX = make_uint4(0, 0, 0, 0);
@@ -355,7 +357,7 @@ __device__ void finish_tile(const FlowArgs& a, const TileLayout& L, unsigned cha
   float* rr = reinterpret_cast<float*>(buf + L.r);
   if constexpr (Tr::EPP == 8) {
     bf16_row_dots(bQ, L.tokens / RPR, s, pw, [&](int, int r, float (&)[8], float dot) {
-      if (slot == 0) rr[r] = 1.f / (dot + a.eps);
+      if (slot == 0) rr[r] = __builtin_amdgcn_rcpf(dot + a.eps);
     });
     return;
   }
