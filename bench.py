@@ -390,9 +390,34 @@ def main():
         torch.cuda.synchronize()
         ms = ba.elapsed_time(bz) / steps
         bb = compulsory_bytes_backward(w)
+
+        # A training step's pair: the forward, then the backward on its
+        # workspace, either recomputing the statistics (lisa_backward) or
+        # taking the forward's (lisa_backward_after_forward).
+        def pair(j, after):
+            d = sets[j]
+            lisa.lisa_forward(d["q"], d["k"], d["v"], grid=(w.H, w.W), T=w.T, alpha=d["alpha"],
+                              weights=d["weights"], beta=x["beta"], eps=w.eps, out=d["y"], workspace=bws,
+                              stream=stream)
+            fn = lisa.lisa_backward_after_forward if after else lisa.lisa_backward
+            fn(d["q"], d["k"], d["v"], dys[j], grid=(w.H, w.W), T=w.T, alpha=d["alpha"], weights=d["weights"],
+               beta=x["beta"], eps=w.eps, workspace=bws, out=outs[j], stream=stream)
+
+        pair_ms = {}
+        for after in (False, True):
+            for i in range(min(warmup, 20)):
+                pair(i % nsets, after)
+            torch.cuda.synchronize()
+            ba.record(stream)
+            for i in range(steps):
+                pair(i % nsets, after)
+            bz.record(stream)
+            torch.cuda.synchronize()
+            pair_ms[after] = ba.elapsed_time(bz) / steps
         return {"ms_per_step": ms, "value": w.token_heads / (ms * 1e-3), "unit": "token-heads/s",
                 "steps": steps, "algorithmic_bytes_per_call": w.token_heads * bb,
-                "roofline_frac": w.token_heads * bb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                "roofline_frac": w.token_heads * bb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "forward_backward_ms": pair_ms[False], "forward_backward_after_forward_ms": pair_ms[True]}
 
     def mlp_timing(steps, warmup, hidden=64):
         """lisa_forward_mlp over the same input sets: the walk weights predicted

@@ -213,6 +213,22 @@ lisa_status lisa_backward(const lisa_problem* p, const void* Q, const void* K, c
                           void* dQ, void* dK, void* dV, float* dweights, float* dalpha,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* The gradients of lisa_backward, for a training step whose forward pass
+ * (lisa_forward, lisa_forward_mlp or lisa_reduce) ran just before on the
+ * same problem and the same Q, K, V, with this workspace, on this stream:
+ * with T >= 3 the slice statistics s, phi(K)^T V and M that call left in the
+ * workspace are used as they are and the statistics launch is skipped (with
+ * T < 3 the forward forms no M, and they are recomputed as lisa_backward
+ * does).  The results equal lisa_backward's bit for bit.  No other call may
+ * use the workspace in between: the library cannot check this, and
+ * statistics of other inputs give wrong gradients without an error.
+ * Arguments, errors and workspace as for lisa_backward. */
+lisa_status lisa_backward_after_forward(const lisa_problem* p, const void* Q, const void* K, const void* V,
+                                        const float* weights, float beta, const float* alpha,
+                                        const void* dY, void* dQ, void* dK, void* dV, float* dweights,
+                                        float* dalpha, void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* lisa_status_str(lisa_status s);
 

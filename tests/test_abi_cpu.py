@@ -26,6 +26,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == [
         "lisa_apply", "lisa_attention_forward", "lisa_attention_workspace_size", "lisa_backward",
+        "lisa_backward_after_forward",
         "lisa_backward_workspace_size", "lisa_forward", "lisa_forward_mlp", "lisa_forward_mlp_workspace_size",
         "lisa_reduce", "lisa_status_str", "lisa_workspace_size"]
 
@@ -125,12 +126,15 @@ def test_reduce_argument_errors():
 DY, DQ, DK, DV, DW, DA = (A + (8 + i) * 0x1000000 for i in range(6))
 
 
+BACKWARD_FN = [lib.lisa_backward]
+
+
 def backward(p, q=Q, k=K, v=V, w=W_, beta=0.5, alpha=AL, dy=DY, dq=DQ, dk=DK, dv=DV, dw=DW, da=DA, ws=WS_,
              ws_bytes=None):
     if ws_bytes is None:
         ws_bytes = lisa.lisa_backward_workspace_size(p) if p is not None else 0
-    return lib.lisa_backward(None if p is None else ctypes.byref(p), q, k, v, w, ctypes.c_float(beta), alpha,
-                             dy, dq, dk, dv, dw, da, ws, ctypes.c_size_t(ws_bytes), None)
+    return BACKWARD_FN[0](None if p is None else ctypes.byref(p), q, k, v, w, ctypes.c_float(beta), alpha,
+                          dy, dq, dk, dv, dw, da, ws, ctypes.c_size_t(ws_bytes), None)
 
 
 def test_backward_workspace_covers_the_forward():
@@ -140,7 +144,15 @@ def test_backward_workspace_covers_the_forward():
     assert lisa.lisa_backward_workspace_size(prob(T=9)) == 0
 
 
-def test_backward_argument_errors():
+@pytest.fixture(params=["lisa_backward", "lisa_backward_after_forward"])
+def backward_entry(request):
+    """Both backward entry points check their arguments the same way."""
+    BACKWARD_FN[0] = getattr(lib, request.param)
+    yield request.param
+    BACKWARD_FN[0] = lib.lisa_backward
+
+
+def test_backward_argument_errors(backward_entry):
     assert backward(None) == NULL
     assert backward(prob(dtype=3)) == DTYPE
     assert backward(prob(grid_w=-1)) == SHAPE

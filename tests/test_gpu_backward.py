@@ -127,3 +127,51 @@ def test_backward_deterministic(lisa):
     a, b = run_gpu(lisa, x, dy), run_gpu(lisa, x, dy)
     for key in ("dq", "dk", "dv", "dweights", "dalpha"):
         assert torch.equal(a[key], b[key]), key
+
+
+AFTER = [
+    # name, B, heads, H, W, T, dtype, weights mode, the call that leaves the statistics
+    ("after-forward-bf16", 2, 2, 13, 21, 3, "bf16", "adaptive", "forward"),
+    ("after-forward-fp32-geo", 1, 2, 17, 9, 5, "fp32", "geometric", "forward"),
+    ("after-forward-t2", 2, 1, 9, 11, 2, "fp32", "adaptive", "forward"),  # T < 3: recomputed
+    ("after-reduce", 1, 3, 20, 15, 4, "bf16", "adaptive", "reduce"),
+    ("after-forward-mlp", 2, 1, 12, 17, 3, "bf16", "adaptive", "mlp"),
+    ("after-forward-pvt", 32, 1, 56, 56, 3, "bf16", "adaptive", "forward"),
+]
+
+
+@pytest.mark.parametrize("case", AFTER, ids=[c[0] for c in AFTER])
+def test_backward_after_forward_equals_backward(lisa, case):
+    """lisa_backward_after_forward on the workspace a forward (or reduce) of the
+    same inputs just used gives lisa_backward's gradients bit for bit."""
+    name, B, heads, H, W, T, dtype, mode, first = case
+    w = workloads.small(name, B, heads, H, W, T, dtype=dtype, mode=mode, seed=zlib.crc32(name.encode()) % 1000)
+    x = workloads.make_inputs(w)
+    dy = make_dy(x, 23).cuda()
+    d = {k: (x[k].cuda() if isinstance(x[k], torch.Tensor) else x[k]) for k in ("q", "k", "v", "weights", "alpha")}
+    kw = dict(grid=(H, W), T=T, alpha=d["alpha"], weights=d["weights"], beta=x["beta"], eps=x["eps"])
+    prob = lisa.make_problem(d["q"], d["v"], grid=(H, W), T=T, eps=x["eps"])
+    nbytes = lisa.lisa_backward_workspace_size(prob)
+    if first == "mlp":
+        nbytes = max(nbytes, lisa.lisa_forward_mlp_workspace_size(prob, 64))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    # Leave other statistics in the workspace first, so that a skipped
+    # recomputation that should not have been skipped shows.
+    lisa.lisa_reduce(d["k"], d["q"], -d["v"], grid=(H, W), eps=x["eps"], T=T, workspace=ws, outputs=False)
+    if first == "forward":
+        lisa.lisa_forward(d["q"], d["k"], d["v"], workspace=ws, **kw)
+    elif first == "reduce":
+        lisa.lisa_reduce(d["q"], d["k"], d["v"], grid=(H, W), eps=x["eps"], T=T, workspace=ws, outputs=False)
+    else:
+        prm = {k: t.cuda() for k, t in workloads.mlp_params(heads, 64, T, seed=7).items()}
+        lisa.lisa_forward_mlp(d["q"], d["k"], d["v"], grid=(H, W), T=T, alpha=d["alpha"], eps=x["eps"],
+                              workspace=ws, **prm)
+    got = lisa.lisa_backward_after_forward(d["q"], d["k"], d["v"], dy, workspace=ws, **kw)
+    ref = lisa.lisa_backward(d["q"], d["k"], d["v"], dy, **kw)
+    torch.cuda.synchronize()
+    print(f"[parity] backward after {first}: {w.describe()}", flush=True)
+    for key in ("dq", "dk", "dv", "dweights", "dalpha"):
+        if ref[key] is None:
+            assert got[key] is None, key
+        else:
+            assert torch.equal(got[key], ref[key]), key

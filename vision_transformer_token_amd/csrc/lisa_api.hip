@@ -459,10 +459,14 @@ size_t lisa_backward_workspace_size(const lisa_problem* p) {
   return make_plan(p, pl) == LISA_OK ? pl.btotal : 0;
 }
 
-lisa_status lisa_backward(const lisa_problem* p, const void* Q, const void* K, const void* V,
-                          const float* weights, float beta, const float* alpha, const void* dY, void* dQ,
-                          void* dK, void* dV, float* dweights, float* dalpha, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+// The backward pass; with have_stats the slice statistics of a preceding
+// forward (or reduce) of the same problem and inputs are taken from the
+// workspace instead of recomputed, when that call formed all of them (T >= 3:
+// with T < 3 the forward forms no M).
+static lisa_status backward_common(const lisa_problem* p, const void* Q, const void* K, const void* V,
+                                   const float* weights, float beta, const float* alpha, const void* dY,
+                                   void* dQ, void* dK, void* dV, float* dweights, float* dalpha,
+                                   void* workspace, size_t workspace_bytes, void* stream, bool have_stats) {
   Plan pl;
   lisa_status st = make_plan(p, pl);
   if (st != LISA_OK) return st;
@@ -493,8 +497,10 @@ lisa_status lisa_backward(const lisa_problem* p, const void* Q, const void* K, c
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   // The slice statistics s, phi(K)^T V and M, as lisa_reduce forms them.
-  st = run(pl, Mode::kReduce, Q, K, V, nullptr, 0.f, nullptr, nullptr, ws, p->eps, s);
-  if (st != LISA_OK) return st;
+  if (!(have_stats && pl.T >= 3)) {
+    st = run(pl, Mode::kReduce, Q, K, V, nullptr, 0.f, nullptr, nullptr, ws, p->eps, s);
+    if (st != LISA_OK) return st;
+  }
   lisa::BwdArgs a{};
   a.Q = Q;
   a.K = K;
@@ -530,6 +536,22 @@ lisa_status lisa_backward(const lisa_problem* p, const void* Q, const void* K, c
   a.ds_part = reinterpret_cast<float*>(ws + pl.b_ds);
   if (lisa::launch_backward(pl.dtype, a, s) != hipSuccess) return LISA_ERR_HIP;
   return LISA_OK;
+}
+
+lisa_status lisa_backward(const lisa_problem* p, const void* Q, const void* K, const void* V,
+                          const float* weights, float beta, const float* alpha, const void* dY, void* dQ,
+                          void* dK, void* dV, float* dweights, float* dalpha, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return backward_common(p, Q, K, V, weights, beta, alpha, dY, dQ, dK, dV, dweights, dalpha, workspace,
+                         workspace_bytes, stream, false);
+}
+
+lisa_status lisa_backward_after_forward(const lisa_problem* p, const void* Q, const void* K, const void* V,
+                                        const float* weights, float beta, const float* alpha, const void* dY,
+                                        void* dQ, void* dK, void* dV, float* dweights, float* dalpha,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_common(p, Q, K, V, weights, beta, alpha, dY, dQ, dK, dV, dweights, dalpha, workspace,
+                         workspace_bytes, stream, true);
 }
 
 const char* lisa_status_str(lisa_status s) {

@@ -103,6 +103,8 @@ _lib.lisa_backward_workspace_size.restype = ctypes.c_size_t
 _lib.lisa_backward.argtypes = [_P, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                _vp, ctypes.c_size_t, _vp]
 _lib.lisa_backward.restype = ctypes.c_int
+_lib.lisa_backward_after_forward.argtypes = _lib.lisa_backward.argtypes
+_lib.lisa_backward_after_forward.restype = ctypes.c_int
 _lib.lisa_status_str.argtypes = [ctypes.c_int]
 _lib.lisa_status_str.restype = ctypes.c_char_p
 
@@ -310,6 +312,24 @@ def lisa_backward(q, k, v, dy, *, grid, T, alpha, weights=None, beta=None, eps=1
     bytes) is allocated when not given; ``out`` (a dict like the result)
     supplies the output tensors.
     """
+    return _backward(_lib.lisa_backward, "lisa_backward", q, k, v, dy, grid=grid, T=T, alpha=alpha,
+                     weights=weights, beta=beta, eps=eps, workspace=workspace, out=out, stream=stream)
+
+
+def lisa_backward_after_forward(q, k, v, dy, *, grid, T, alpha, workspace, weights=None, beta=None, eps=1e-6,
+                                out=None, stream=None):
+    """lisa_backward that reuses the slice statistics a lisa_forward (or
+    lisa_forward_mlp, lisa_reduce) of the same problem and inputs left in
+    ``workspace`` (lisa_backward_workspace_size bytes) just before; see
+    include/lisa.h.  Same results as lisa_backward."""
+    if workspace is None:
+        raise ValueError("lisa_backward_after_forward needs the forward's workspace")
+    return _backward(_lib.lisa_backward_after_forward, "lisa_backward_after_forward", q, k, v, dy, grid=grid,
+                     T=T, alpha=alpha, weights=weights, beta=beta, eps=eps, workspace=workspace, out=out,
+                     stream=stream)
+
+
+def _backward(fn, name, q, k, v, dy, *, grid, T, alpha, weights, beta, eps, workspace, out, stream):
     _check_tensors(q=q, k=k, v=v, dy=dy, alpha=alpha, weights=weights, workspace=workspace)
     if weights is not None and weights.dtype != torch.float32:
         raise TypeError("weights must be float32")
@@ -332,14 +352,14 @@ def lisa_backward(q, k, v, dy, *, grid, T, alpha, weights=None, beta=None, eps=1
             "dalpha": torch.empty_like(alpha),
         }
     _check_tensors(**{k_: t for k_, t in out.items()})
-    st = _lib.lisa_backward(
+    st = fn(
         ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(weights),
         ctypes.c_float(0.0 if beta is None else beta), _ptr(alpha), _ptr(dy), _ptr(out["dq"]),
         _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dweights"]), _ptr(out["dalpha"]), _ptr(workspace),
         ctypes.c_size_t(workspace.numel()), _stream(stream, q.device),
     )
     if st != LISA_OK:
-        raise LisaError(st, "lisa_backward")
+        raise LisaError(st, name)
     return out
 
 
