@@ -116,6 +116,10 @@ def _short(name):
         return "mlp_prep<bf16>" if "BF16" in name else "mlp_prep<fp32>"
     if "copyBuffer" in name:
         return "copyBuffer"
+    m = re.search(r"proj_gemm<(unsigned short|float), (true|false)>", name)
+    if m:
+        return f"proj_gemm<{'bf16' if m.group(1) == 'unsigned short' else 'fp32'}, " \
+               f"{'output' if m.group(2) == 'true' else 'qkv'}>"
     m = re.search(r"(bwd_\w+)(<(unsigned short|float)>)?", name)
     if m:
         return m.group(1) + ({"unsigned short": "<bf16>", "float": "<fp32>"}.get(m.group(3), ""))
@@ -224,6 +228,43 @@ def summarize_backward(outdir, workload, command):
         f.write("\n".join(lines) + "\n")
 
 
+def compulsory_bytes_layer(w):
+    """Per token (not token-head): the layer input X read and its output Y
+    written once (C = 64 heads channels each), and the adaptive weights read
+    (4 T bytes per token-head).  Q, K, V and the heads' outputs, which the
+    unfused layer keeps in HBM, are not counted: they count against it."""
+    esize = 2 if w.dtype == "bf16" else 4
+    C = 64 * w.heads
+    return 2 * C * esize + (4 * w.T * w.heads if w.mode == "adaptive" else 0)
+
+
+def summarize_layer(outdir, workload, command):
+    """profiles/ summary of a rocprofv3 kernel trace of bench.py --layer-only."""
+    from vision_transformer_token_amd import workloads
+
+    w = workloads.get(workload)
+    stats = _csv_rows(os.path.join(outdir, "prof_layer", "layer_kernel_stats.csv"))
+    lines = [f"# rocprofv3 kernel trace of lisa_attention_forward (QKV projection, LiSA, output projection), "
+             f"workload {w.describe()}, C = {64 * w.heads}", "", f"command: {command}", "",
+             "| kernel | calls | average ns | min ns | max ns | share |", "|---|---|---|---|---|---|"]
+    total_ns = 0.0
+    for r in stats:
+        name = _short(r["Name"])
+        if not (name.startswith("flow_kernel") or name.startswith("proj_gemm")):
+            continue
+        total_ns += float(r["AverageNs"])
+        lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} | "
+                     f"{float(r['Percentage']):.1f}% |")
+    bb = compulsory_bytes_layer(w)
+    tok = w.B * w.n
+    lines += ["", f"sum of the kernels' averages per call: {total_ns / 1e3:.1f} us",
+              f"algorithmic bytes per call: {tok * bb / 1e6:.2f} MB ({bb} B per token: X read, Y written, "
+              f"weights); at 8 TB/s: {tok * bb / 8e12 * 1e6:.1f} us",
+              f"kernel source hash: {kernel_source_hash()}"]
+    with open(os.path.join(ROOT, "profiles", f"lisa_attention_forward_{w.name}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def summarize_mlp(outdir, workload, command):
     """profiles/ summary of a rocprofv3 kernel trace of bench.py --mlp-only."""
     from vision_transformer_token_amd import workloads
@@ -263,6 +304,10 @@ def main():
                          "launch of the kernel is then a forward)")
     ap.add_argument("--backward-only", action="store_true",
                     help="time only lisa_backward (for a profiler run) and print its line")
+    ap.add_argument("--layer-only", action="store_true",
+                    help="time only lisa_attention_forward (for a profiler run) and print its line")
+    ap.add_argument("--summarize-layer", metavar="DIR",
+                    help="write the profiles/ summary of a layer kernel trace under DIR and exit")
     ap.add_argument("--mlp-only", action="store_true",
                     help="time only lisa_forward_mlp (predicted walk weights) and print its line")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -291,6 +336,13 @@ def main():
                     "-o c{fetch|write} -- python3 bench.py --calibrate-copy-mib 256",
             "copy_mib": 256,
         })
+        return
+
+    if args.summarize_layer:
+        summarize_layer(args.summarize_layer, args.workload,
+                        "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_layer -o layer -- "
+                        "python3 bench.py --layer-only --steps 100 --warmup 10 --no-cpu-baseline --workload "
+                        + args.workload)
         return
 
     if args.summarize_mlp:
@@ -449,11 +501,47 @@ def main():
                 "hidden": hidden, "algorithmic_bytes_per_call": w.token_heads * bb,
                 "roofline_frac": w.token_heads * bb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
+    def layer_timing(steps, warmup):
+        """lisa_attention_forward (QKV projection, LiSA, output projection) at the
+        workload's shape, C = 64 heads channels, over rotating layer inputs."""
+        prm = workloads.layer_params(w)
+        dp = {k: t.to(dev) for k, t in prm.items() if k != "x"}
+        lws = torch.zeros(lisa.lisa_attention_workspace_size(prob), dtype=torch.uint8, device=dev)
+        with torch.cuda.stream(stream):
+            xs = [prm["x"].to(dev) for _ in range(nsets)]
+            ys = [torch.empty_like(xx) for xx in xs]
+        torch.cuda.synchronize()
+
+        def layer(j):
+            d = sets[j]
+            lisa.lisa_attention_forward(xs[j], dp["w_qkv"], dp["b_qkv"], dp["w_o"], dp["b_o"], heads=w.heads,
+                                        grid=(w.H, w.W), T=w.T, alpha=d["alpha"], weights=d["weights"],
+                                        beta=x["beta"], eps=w.eps, out=ys[j], workspace=lws, stream=stream)
+
+        for i in range(warmup):
+            layer(i % nsets)
+        la, lz = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        la.record(stream)
+        for i in range(steps):
+            layer(i % nsets)
+        lz.record(stream)
+        torch.cuda.synchronize()
+        ms = la.elapsed_time(lz) / steps
+        bb = compulsory_bytes_layer(w)
+        tok = w.B * w.n
+        return {"ms_per_step": ms, "value": w.token_heads / (ms * 1e-3), "unit": "token-heads/s", "steps": steps,
+                "channels": 64 * w.heads, "algorithmic_bytes_per_call": tok * bb,
+                "roofline_frac": tok * bb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
     if args.backward_only:
         print(json.dumps({"workload": w.name, "backward": backward_timing(args.steps, args.warmup)}), flush=True)
         return
     if args.mlp_only:
         print(json.dumps({"workload": w.name, "forward_mlp": mlp_timing(args.steps, args.warmup)}), flush=True)
+        return
+    if args.layer_only:
+        print(json.dumps({"workload": w.name, "layer": layer_timing(args.steps, args.warmup)}), flush=True)
         return
 
     for i in range(args.warmup):
@@ -515,7 +603,8 @@ def main():
         del src, dst
 
     # The same K forwards with events around each launch on the stream it runs
-    # on: the kernel's average launch duration, for the roofline.
+    # on: each launch in isolation (an event between launches adds a gap), for
+    # comparison with the two halves below.
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
@@ -581,7 +670,10 @@ def main():
         out["copy_gbs"] = copy_gbs
         out["path_copy_frac"] = path_gbs / copy_gbs
     if kernel_ms is not None:
-        achieved = th * bpt / (kernel_ms * 1e-3) / 1e9
+        # One launch of the kernel per step, back to back on `stream`: its
+        # average launch duration is the timed region's elapsed time (events
+        # on that stream) over the K launches.
+        achieved = th * bpt / (step_ms * 1e-3) / 1e9
         traffic = load_counters(w, KERNEL)
         out["roofline"] = {
             "bound": "hbm",
@@ -591,13 +683,15 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
-            "kernel_ms": kernel_ms,
+            "kernel_ms": step_ms,
+            "isolated_launch_ms": kernel_ms,
             "algorithmic_bytes_per_launch": th * bpt,
         }
         out["stages_ms"] = {"forward_kernel": kernel_ms, "reduce_only": stats_ms, "apply_only": apply_ms}
     if not args.forward_only:
         out["backward"] = backward_timing(min(args.steps, 500), min(args.warmup, 50))
         out["forward_mlp"] = mlp_timing(min(args.steps, 1000), min(args.warmup, 50))
+        out["layer"] = layer_timing(min(args.steps, 500), min(args.warmup, 50))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -15,7 +15,12 @@
 // 64 x 64 block of outputs, wave w its rows 16 w .. 16 w + 15 as four 16 x 16
 // MFMA blocks; both operands are read straight from HBM / L2 with 16-byte
 // loads (rows of X, of a head's O and of the torch-layout weights [out][in]
-// are contiguous along the contraction).
+// are contiguous along the contraction).  The 64 outputs of a row in a block
+// are contiguous in the output too (one head's channels of Q, K or V, or a
+// stretch of a row of Y): each wave turns its accumulators into rows through
+// LDS and writes them with 16-byte stores.  Workgroups that share a block row
+// of the input are consecutive (the column block varies fastest), so the
+// input is read from HBM about once and from L2 by the others.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -44,10 +49,14 @@ __device__ __forceinline__ size_t out_index(const ProjArgs& a, int m, int c) {
   return (size_t)which * a.head_elems + (((size_t)b * a.heads + h) * a.n + tok) * kD + d;
 }
 
+constexpr int kRowPad = 68;  // floats per LDS row: four lane groups 272 floats apart, on distinct banks
+
 template <class S, bool kOut>
 __global__ __launch_bounds__(256) void proj_gemm(ProjArgs a) {
+  __shared__ __align__(16) float rows[4][16 * kRowPad];
   const int t = threadIdx.x, w = t / 64, ln = t % 64, li = ln % 16, lk = ln / 16;
-  const int m0 = blockIdx.x * 64 + 16 * w, c0 = blockIdx.y * 64;
+  const int nct = a.N / 64;
+  const int m0 = (int)(blockIdx.x / nct) * 64 + 16 * w, c0 = (int)(blockIdx.x % nct) * 64;
   const int mr = m0 + li;  // the A row of this lane's operand
   const bool mon = mr < a.M;
   const S* A = static_cast<const S*>(a.A);
@@ -82,28 +91,51 @@ __global__ __launch_bounds__(256) void proj_gemm(ProjArgs a) {
       }
     }
   }
-  // acc[ct][e] is output (m0 + 4 lk + e, c0 + 16 ct + li).
-  S* out = static_cast<S*>(a.out);
+  // acc[ct][e] is output (m0 + 4 lk + e, c0 + 16 ct + li): plus the bias,
+  // into the wave's 16 LDS rows; then lane ln writes columns 16 (ln % 4) ..
+  // + 15 of row m0 + ln / 4.
+  float* rw = rows[w];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
-    const int c = c0 + 16 * ct + li;
-    const float bc = a.bias[c];
+    const float bc = a.bias[c0 + 16 * ct + li];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rw[(4 * lk + e) * kRowPad + 16 * ct + li] = acc[ct][e] + bc;
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+  const int r = ln / 4, q = ln % 4;
+  const int m = m0 + r;
+  if (m >= a.M) return;
+  float v[16];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float4 x = *reinterpret_cast<const float4*>(rw + r * kRowPad + 16 * q + 4 * j);
+    v[4 * j] = x.x;
+    v[4 * j + 1] = x.y;
+    v[4 * j + 2] = x.z;
+    v[4 * j + 3] = x.w;
+  }
+  S* dst = static_cast<S*>(a.out) + out_index<kOut>(a, m, c0 + 16 * q);
+  if constexpr (sizeof(S) == 2) {
+    u32x4 o0, o1;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int m = m0 + 4 * lk + e;
-      if (m >= a.M) continue;
-      const float v = acc[ct][e] + bc;
-      if constexpr (sizeof(S) == 2)
-        out[out_index<kOut>(a, m, c)] = f2bf(v);
-      else
-        out[out_index<kOut>(a, m, c)] = v;
+      o0[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+      o1[e] = pack_bf16x2(v[8 + 2 * e], v[8 + 2 * e + 1]);
     }
+    reinterpret_cast<u32x4*>(dst)[0] = o0;
+    reinterpret_cast<u32x4*>(dst)[1] = o1;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      reinterpret_cast<float4*>(dst)[j] = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
   }
 }
 
 template <class S>
 hipError_t launch_proj_typed(bool out_proj, const ProjArgs& a, hipStream_t s) {
-  const dim3 grid((a.M + 63) / 64, a.N / 64);
+  const dim3 grid((unsigned)((a.M + 63) / 64) * (unsigned)(a.N / 64));
   if (out_proj)
     hipLaunchKernelGGL((proj_gemm<S, true>), grid, dim3(256), 0, s, a);
   else
