@@ -18,8 +18,10 @@
 // are contiguous along the contraction).  The 64 outputs of a row in a block
 // are contiguous in the output too (one head's channels of Q, K or V, or a
 // stretch of a row of Y): each wave turns its accumulators into rows through
-// LDS and writes them with 16-byte stores.  Workgroups that share a block row
-// of the input are consecutive (the column block varies fastest), so the
+// LDS and writes them with 16-byte stores.  A workgroup takes four 64-row
+// blocks of one column block, so each weight operand it reads serves four
+// MFMAs and four blocks' input loads are in flight together; workgroups that
+// share input rows are consecutive (the column block varies fastest), so the
 // input is read from HBM about once and from L2 by the others.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -50,92 +52,116 @@ __device__ __forceinline__ size_t out_index(const ProjArgs& a, int m, int c) {
 }
 
 constexpr int kRowPad = 68;  // floats per LDS row: four lane groups 272 floats apart, on distinct banks
+constexpr int kProjTiles = 4;  // 64-row tiles per workgroup: each weight operand read serves four
 
 template <class S, bool kOut>
 __global__ __launch_bounds__(256) void proj_gemm(ProjArgs a) {
   __shared__ __align__(16) float rows[4][16 * kRowPad];
   const int t = threadIdx.x, w = t / 64, ln = t % 64, li = ln % 16, lk = ln / 16;
   const int nct = a.N / 64;
-  const int m0 = (int)(blockIdx.x / nct) * 64 + 16 * w, c0 = (int)(blockIdx.x % nct) * 64;
-  const int mr = m0 + li;  // the A row of this lane's operand
-  const bool mon = mr < a.M;
+  const int c0 = (int)(blockIdx.x % nct) * 64;
+  const int mb = (int)(blockIdx.x / nct) * (64 * kProjTiles) + 16 * w;  // wave's rows in tile r: mb + 64 r + 0..15
   const S* A = static_cast<const S*>(a.A);
   const S* Wt = static_cast<const S*>(a.Wt);
-  f32x4 acc[4] = {};
+  f32x4 acc[kProjTiles][4] = {};
   if constexpr (sizeof(S) == 2) {
     // bf16 MFMA 16x16x32: lane (li, lk) holds contraction slots k0 + 8 lk .. + 7.
     for (int k0 = 0; k0 < a.K; k0 += 32) {
       const int k = k0 + 8 * lk;
-      bf16x8 av = {};
-      if (mon) av = *reinterpret_cast<const bf16x8*>(A + a_index<kOut>(a, mr, k));
+      bf16x8 bv[4], av[kProjTiles];
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(Wt + (size_t)(c0 + 16 * ct + li) * a.K + k);
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[ct], 0, 0, 0);
+      for (int ct = 0; ct < 4; ++ct) bv[ct] = *reinterpret_cast<const bf16x8*>(Wt + (size_t)(c0 + 16 * ct + li) * a.K + k);
+#pragma unroll
+      for (int r = 0; r < kProjTiles; ++r) {
+        const int mr = mb + 64 * r + li;
+        av[r] = bf16x8{};
+        if (mr < a.M) av[r] = *reinterpret_cast<const bf16x8*>(A + a_index<kOut>(a, mr, k));
       }
+#pragma unroll
+      for (int r = 0; r < kProjTiles; ++r)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+          acc[r][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[r], bv[ct], acc[r][ct], 0, 0, 0);
     }
   } else {
     // fp32 MFMA 16x16x4: four of them per 16 inputs, lane (li, lk) taking
     // inputs k0 + 4 lk + s in the s-th (one 16-byte read each).
     for (int k0 = 0; k0 < a.K; k0 += 16) {
       const int k = k0 + 4 * lk;
-      float4 av = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (mon) av = *reinterpret_cast<const float4*>(A + a_index<kOut>(a, mr, k));
+      float4 bv[4], av[kProjTiles];
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const float4 bv = *reinterpret_cast<const float4*>(Wt + (size_t)(c0 + 16 * ct + li) * a.K + k);
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, acc[ct], 0, 0, 0);
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, acc[ct], 0, 0, 0);
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, acc[ct], 0, 0, 0);
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv.w, acc[ct], 0, 0, 0);
+      for (int ct = 0; ct < 4; ++ct) bv[ct] = *reinterpret_cast<const float4*>(Wt + (size_t)(c0 + 16 * ct + li) * a.K + k);
+#pragma unroll
+      for (int r = 0; r < kProjTiles; ++r) {
+        const int mr = mb + 64 * r + li;
+        av[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (mr < a.M) av[r] = *reinterpret_cast<const float4*>(A + a_index<kOut>(a, mr, k));
+      }
+#pragma unroll
+      for (int r = 0; r < kProjTiles; ++r)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          acc[r][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[r].x, bv[ct].x, acc[r][ct], 0, 0, 0);
+          acc[r][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[r].y, bv[ct].y, acc[r][ct], 0, 0, 0);
+          acc[r][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[r].z, bv[ct].z, acc[r][ct], 0, 0, 0);
+          acc[r][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[r].w, bv[ct].w, acc[r][ct], 0, 0, 0);
+        }
+    }
+  }
+  // acc[r][ct][e] is output (mb + 64 r + 4 lk + e, c0 + 16 ct + li): plus the
+  // bias, into the wave's 16 LDS rows; then lane ln writes columns
+  // 16 (ln % 4) .. + 15 of row mb + 64 r + ln / 4.  The wave's LDS accesses
+  // complete in order, so tile r + 1's writes follow tile r's reads.
+  float* rw = rows[w];
+  float bc[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) bc[ct] = a.bias[c0 + 16 * ct + li];
+  const int rr = ln / 4, q = ln % 4;
+#pragma unroll
+  for (int r = 0; r < kProjTiles; ++r) {
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rw[(4 * lk + e) * kRowPad + 16 * ct + li] = acc[r][ct][e] + bc[ct];
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 x = *reinterpret_cast<const float4*>(rw + rr * kRowPad + 16 * q + 4 * j);
+      v[4 * j] = x.x;
+      v[4 * j + 1] = x.y;
+      v[4 * j + 2] = x.z;
+      v[4 * j + 3] = x.w;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // the reads are done before the next tile's writes
+    __builtin_amdgcn_wave_barrier();
+    const int m = mb + 64 * r + rr;
+    if (m < a.M) {
+      S* dst = static_cast<S*>(a.out) + out_index<kOut>(a, m, c0 + 16 * q);
+      if constexpr (sizeof(S) == 2) {
+        u32x4 o0, o1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o0[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+          o1[e] = pack_bf16x2(v[8 + 2 * e], v[8 + 2 * e + 1]);
+        }
+        reinterpret_cast<u32x4*>(dst)[0] = o0;
+        reinterpret_cast<u32x4*>(dst)[1] = o1;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          reinterpret_cast<float4*>(dst)[j] = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
       }
     }
-  }
-  // acc[ct][e] is output (m0 + 4 lk + e, c0 + 16 ct + li): plus the bias,
-  // into the wave's 16 LDS rows; then lane ln writes columns 16 (ln % 4) ..
-  // + 15 of row m0 + ln / 4.
-  float* rw = rows[w];
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    const float bc = a.bias[c0 + 16 * ct + li];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) rw[(4 * lk + e) * kRowPad + 16 * ct + li] = acc[ct][e] + bc;
-  }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's LDS writes are done
-  __builtin_amdgcn_wave_barrier();
-  const int r = ln / 4, q = ln % 4;
-  const int m = m0 + r;
-  if (m >= a.M) return;
-  float v[16];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float4 x = *reinterpret_cast<const float4*>(rw + r * kRowPad + 16 * q + 4 * j);
-    v[4 * j] = x.x;
-    v[4 * j + 1] = x.y;
-    v[4 * j + 2] = x.z;
-    v[4 * j + 3] = x.w;
-  }
-  S* dst = static_cast<S*>(a.out) + out_index<kOut>(a, m, c0 + 16 * q);
-  if constexpr (sizeof(S) == 2) {
-    u32x4 o0, o1;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      o0[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
-      o1[e] = pack_bf16x2(v[8 + 2 * e], v[8 + 2 * e + 1]);
-    }
-    reinterpret_cast<u32x4*>(dst)[0] = o0;
-    reinterpret_cast<u32x4*>(dst)[1] = o1;
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      reinterpret_cast<float4*>(dst)[j] = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
   }
 }
 
 template <class S>
 hipError_t launch_proj_typed(bool out_proj, const ProjArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((a.M + 63) / 64) * (unsigned)(a.N / 64));
+  const dim3 grid((unsigned)((a.M + 64 * kProjTiles - 1) / (64 * kProjTiles)) * (unsigned)(a.N / 64));
   if (out_proj)
     hipLaunchKernelGGL((proj_gemm<S, true>), grid, dim3(256), 0, s, a);
   else
