@@ -58,6 +58,36 @@ __device__ __forceinline__ void store16(S* row, int f0, const float (&x)[kF]) {
 #pragma unroll
   for (int e = 0; e < kF; e += 4) store4(row + f0 + e, &x[e]);
 }
+// This lane's 16 features of a row as loaded (bf16 kept packed: half the
+// registers of floats), for the window gathers that hold several rows.
+template <class S>
+struct Piece;
+template <>
+struct Piece<uint16_t> {
+  uint4 w[2];
+  __device__ __forceinline__ void load(const uint16_t* row, int f0) {
+    w[0] = *reinterpret_cast<const uint4*>(row + f0);
+    w[1] = *reinterpret_cast<const uint4*>(row + f0 + 8);
+  }
+  __device__ __forceinline__ float operator[](int e) const {  // e: a compile-time constant after unrolling
+    const uint4& v = w[e >> 3];
+    const uint32_t x = (e & 6) == 0 ? v.x : (e & 6) == 2 ? v.y : (e & 6) == 4 ? v.z : v.w;
+    return __uint_as_float((e & 1) ? (x & 0xffff0000u) : (x << 16));
+  }
+};
+template <>
+struct Piece<float> {
+  float4 w[4];
+  __device__ __forceinline__ void load(const float* row, int f0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const float4*>(row + f0 + 4 * j);
+  }
+  __device__ __forceinline__ float operator[](int e) const {
+    const float4& v = w[e >> 2];
+    return (e & 3) == 0 ? v.x : (e & 3) == 1 ? v.y : (e & 3) == 2 ? v.z : v.w;
+  }
+};
+
 // Sum over the lane quad of a token (every lane of the quad gets it).
 __device__ __forceinline__ float quad_sum(float x) { return dpp_add(dpp_add(x, 0xB1), 0x4E); }
 // x . row over all 64 features (quad-reduced).
@@ -376,22 +406,46 @@ __global__ __launch_bounds__(kTT) void bwd_token_a(BwdArgs a) {
     load16(dYb + (size_t)i * kD, f0, dy);
     // Local branch at token i: window logits, their max and sum, dY . L_i.
     const int row = i / a.W, col = i % a.W;
+    // The window's rows three at a time (one grid row of it), loaded without
+    // branches: an off-grid cell loads token i's own row and its result is
+    // masked.  Sums run over j = 0 .. 8 in order, as over the valid cells.
+    int cw[9];
+#pragma unroll
+    for (int j = 0; j < 9; ++j) cw[j] = window_cell(a, row, col, j);
     float z[9];
     m = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 9; ++j) {
-      const int c = window_cell(a, row, col, j);
-      z[j] = c >= 0 ? dot64(Kb + (size_t)c * kD, f0, q) * kRs : -INFINITY;
-      m = fmaxf(m, z[j]);
+    for (int g0 = 0; g0 < 9; g0 += 3) {
+      Piece<S> y[3];
+#pragma unroll
+      for (int u = 0; u < 3; ++u) y[u].load(Kb + (size_t)(cw[g0 + u] >= 0 ? cw[g0 + u] : i) * kD, f0);
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < kF; ++e) acc += q[e] * y[u][e];
+        const float d = quad_sum(acc);
+        z[g0 + u] = cw[g0 + u] >= 0 ? d * kRs : -INFINITY;
+        m = fmaxf(m, z[g0 + u]);
+      }
     }
     Z = 0.f;
 #pragma unroll
-    for (int j = 0; j < 9; ++j) {
-      const int c = window_cell(a, row, col, j);
-      if (c >= 0) {
-        const float e = __expf(z[j] - m);
-        Z += e;
-        dyL += e * dot64(Vb + (size_t)c * kD, f0, dy);
+    for (int g0 = 0; g0 < 9; g0 += 3) {
+      Piece<S> y[3];
+#pragma unroll
+      for (int u = 0; u < 3; ++u) y[u].load(Vb + (size_t)(cw[g0 + u] >= 0 ? cw[g0 + u] : i) * kD, f0);
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < kF; ++e) acc += dy[e] * y[u][e];
+        const float d = quad_sum(acc);
+        if (cw[g0 + u] >= 0) {
+          const float e = __expf(z[g0 + u] - m);
+          Z += e;
+          dyL += e * d;
+        }
       }
     }
     dyL /= Z;
