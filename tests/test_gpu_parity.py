@@ -90,6 +90,11 @@ RAGGED = [
     (1, 1, 70, 70, 3, "bf16", "adaptive"),   # 4900 tokens: two-level combine
     (1, 1, 41, 45, 7, "fp32", "adaptive"),
     (1, 1, 260, 260, 3, "bf16", "adaptive"),  # > 65536 tokens: enlarged chunks
+    # More slices than workgroups: groups take two slices per round; with one
+    # chunk per slice the M chunks keep the K rows their KV chunk staged.
+    (96, 3, 14, 14, 3, "bf16", "adaptive"),
+    (96, 3, 14, 14, 5, "fp32", "geometric"),
+    (130, 2, 9, 11, 4, "bf16", "adaptive"),
 ]
 
 
