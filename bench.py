@@ -415,8 +415,10 @@ def main():
                         weights=d["weights"], beta=x["beta"], eps=w.eps, out=d["y"], workspace=ws,
                         stream=stream)
 
-    def backward_timing(steps, warmup):
-        """lisa_backward over the same input sets (dY drawn once per set)."""
+    def backward_timing(steps, warmup, pairs=True):
+        """lisa_backward over the same input sets (dY drawn once per set); with
+        ``pairs``, also forward + backward pairs (the profiler run leaves them out,
+        so that its trace holds lisa_backward's launches only)."""
         bws = torch.zeros(lisa.lisa_backward_workspace_size(prob), dtype=torch.uint8, device=dev)
         with torch.cuda.stream(stream):
             dys = [torch.randn(d["v"].shape, device=dev, dtype=torch.float32).to(d["v"].dtype) for d in sets]
@@ -455,8 +457,8 @@ def main():
             fn(d["q"], d["k"], d["v"], dys[j], grid=(w.H, w.W), T=w.T, alpha=d["alpha"], weights=d["weights"],
                beta=x["beta"], eps=w.eps, workspace=bws, out=outs[j], stream=stream)
 
-        pair_ms = {}
-        for after in (False, True):
+        pair_ms = {False: None, True: None}
+        for after in ((False, True) if pairs else ()):
             for i in range(min(warmup, 20)):
                 pair(i % nsets, after)
             torch.cuda.synchronize()
@@ -535,7 +537,8 @@ def main():
                 "roofline_frac": tok * bb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
     if args.backward_only:
-        print(json.dumps({"workload": w.name, "backward": backward_timing(args.steps, args.warmup)}), flush=True)
+        print(json.dumps({"workload": w.name, "backward": backward_timing(args.steps, args.warmup, pairs=False)}),
+              flush=True)
         return
     if args.mlp_only:
         print(json.dumps({"workload": w.name, "forward_mlp": mlp_timing(args.steps, args.warmup)}), flush=True)
