@@ -45,9 +45,11 @@
  *     (batch, head) slice into) wait for each other.  Ranks are handed out in
  *     the order workgroups start, so a call always completes when it can
  *     eventually run one group at a time; work on other streams only delays
- *     it.  A wait that lasts about 0.1 s is abandoned (the call then finishes
- *     with undefined Y); that only happens if other work keeps a group's
- *     workgroups from starting for that long.
+ *     it.  A wait that lasts more than about half a second is abandoned (the
+ *     call then finishes with undefined Y); that only happens if other work keeps a group's
+ *     workgroups from starting for that long.  The call cannot report it when
+ *     it returns (the work is asynchronous); it raises a flag in the
+ *     workspace, which lisa_workspace_check reads and clears.
  *   - Arithmetic: fp32 accumulation throughout.  With LISA_BF16 inputs the
  *     matrix products run on bf16 MFMA with fp32 accumulation, and the
  *     operands the library derives itself (r_i phi(Q_i), powers of M applied
@@ -74,7 +76,8 @@ typedef enum lisa_status {
   LISA_ERR_UNSUPPORTED = 5, /* d_h or d_v other than 64, or batch*heads > 65535 */
   LISA_ERR_WORKSPACE = 6,   /* workspace NULL, too small or not 256-byte aligned */
   LISA_ERR_ALIGN = 7,       /* Q, K, V, Y not 16-byte or weights/alpha/outputs not 4-byte aligned */
-  LISA_ERR_HIP = 8          /* a HIP launch or copy failed */
+  LISA_ERR_HIP = 8,         /* a HIP launch or copy failed */
+  LISA_ERR_STALLED = 9      /* a call abandoned a wait: its outputs are undefined (lisa_workspace_check) */
 } lisa_status;
 
 typedef enum lisa_dtype { LISA_FP32 = 0, LISA_BF16 = 1 } lisa_dtype;
@@ -228,6 +231,18 @@ lisa_status lisa_backward_after_forward(const lisa_problem* p, const void* Q, co
                                         const void* dY, void* dQ, void* dK, void* dV, float* dweights,
                                         float* dalpha, void* workspace, size_t workspace_bytes,
                                         void* stream);
+
+/* Whether a call on `workspace` abandoned a wait (see Scheduling above).
+ * Unlike the other entry points this call synchronises: it waits for the
+ * work enqueued on `stream` so far, reads the workspace's stall flag, clears
+ * it, and returns LISA_ERR_STALLED if it was set (the outputs of the calls on
+ * this workspace since the previous check are then undefined; the workspace
+ * itself is ready for further calls), else LISA_OK.  The flag is word 1 of
+ * the launch counters at the start of every workspace, whose place no
+ * problem moves.  Errors: NULL workspace (LISA_ERR_NULL), fewer than 256
+ * bytes or not 256-byte aligned (LISA_ERR_WORKSPACE), a failed HIP call
+ * (LISA_ERR_HIP). */
+lisa_status lisa_workspace_check(void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* lisa_status_str(lisa_status s);

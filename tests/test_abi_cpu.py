@@ -28,7 +28,7 @@ def test_header_declares_the_entry_points():
         "lisa_apply", "lisa_attention_forward", "lisa_attention_workspace_size", "lisa_backward",
         "lisa_backward_after_forward",
         "lisa_backward_workspace_size", "lisa_forward", "lisa_forward_mlp", "lisa_forward_mlp_workspace_size",
-        "lisa_reduce", "lisa_status_str", "lisa_workspace_size"]
+        "lisa_reduce", "lisa_status_str", "lisa_workspace_check", "lisa_workspace_size"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -178,11 +178,19 @@ def test_backward_argument_errors(backward_entry):
 
 def test_status_strings():
     seen = set()
-    for code in range(9):
+    for code in range(10):
         s = lisa.lisa_status_str(code)
         assert s and s not in seen
         seen.add(s)
     assert lisa.lisa_status_str(42) == "unknown status"
+
+
+def test_workspace_check_argument_errors():
+    """Checked before any HIP call: no device is touched."""
+    check = lib.lisa_workspace_check
+    assert check(None, ctypes.c_size_t(4096), None) == NULL
+    assert check(WS_, ctypes.c_size_t(255), None) == WS
+    assert check(WS_ + 128, ctypes.c_size_t(4096), None) == WS
 
 
 W1_, B1_, W2_, B2_ = (A + (16 + i) * 0x1000000 for i in range(4))

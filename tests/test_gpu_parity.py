@@ -6,6 +6,8 @@ accumulation.  Every workload preset runs at full size; the oracle computes
 the whole output in fp64 on the host.
 """
 
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -238,3 +240,28 @@ def test_graph_replay_matches_eager(lisa):
         torch.cuda.synchronize()
         assert torch.equal(out, ya), f"replay {rep}"
         assert torch.equal(gpu_y(lisa, db, workspace=ws), yb), f"eager call after replay {rep}"
+
+
+def test_abandoned_wait_is_reported_and_cleared(lisa):
+    """lisa_workspace_check: clear after normal calls, set after a call whose
+    dependency wait was abandoned.  The condition is forced from the host: the
+    rank tickets (word 8 of the launch counters at the start of the workspace)
+    start at 1, so the first group of a PVT stage-1 forward (8 ranks per
+    slice, one ticket counter) never gets its rank 0, and its other ranks give
+    up waiting for it after the kernel's own bound; every workgroup still
+    finishes, and the last one resets the counters."""
+    w = workloads.get("pvt_t_stage1")
+    d = to_dev(workloads.make_inputs(w))
+    prob = lisa.make_problem(d["q"], d["v"], grid=(w.H, w.W), T=w.T, eps=w.eps)
+    ws = lisa.new_workspace(prob, d["q"].device)
+    y0 = gpu_y(lisa, d, workspace=ws)
+    assert lisa.lisa_workspace_check(ws) == lisa.LISA_OK
+    ws.view(torch.int32)[8] = 1
+    t0 = time.time()
+    gpu_y(lisa, d, workspace=ws)
+    print(f"[stall] forward with a missing rank: {time.time() - t0:.2f} s", flush=True)
+    assert lisa.lisa_workspace_check(ws) == lisa.LISA_ERR_STALLED
+    assert lisa.lisa_workspace_check(ws) == lisa.LISA_OK
+    assert int(ws.view(torch.int32)[8].item()) == 0
+    y1 = gpu_y(lisa, d, workspace=ws)
+    assert torch.equal(y0, y1)

@@ -538,6 +538,23 @@ static lisa_status backward_common(const lisa_problem* p, const void* Q, const v
   return LISA_OK;
 }
 
+lisa_status lisa_workspace_check(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace) return LISA_ERR_NULL;
+  if (workspace_bytes < 256 || misaligned(workspace, kAlign)) return LISA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // The stall flag: word 1 of the launch counters at offset 0 (the kernel's
+  // error word, raised by an abandoned dependency wait).
+  unsigned* flag = static_cast<unsigned*>(workspace) + 1;
+  unsigned v = 0;
+  if (hipMemcpyAsync(&v, flag, sizeof(v), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return LISA_ERR_HIP;
+  if (v == 0) return LISA_OK;
+  if (hipMemsetAsync(flag, 0, sizeof(unsigned), s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess)
+    return LISA_ERR_HIP;
+  return LISA_ERR_STALLED;
+}
+
 lisa_status lisa_backward(const lisa_problem* p, const void* Q, const void* K, const void* V,
                           const float* weights, float beta, const float* alpha, const void* dY, void* dQ,
                           void* dK, void* dV, float* dweights, float* dalpha, void* workspace,
@@ -565,6 +582,7 @@ const char* lisa_status_str(lisa_status s) {
     case LISA_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
     case LISA_ERR_ALIGN: return "misaligned pointer (Q, K, V, Y need 16 bytes; fp32 arrays 4)";
     case LISA_ERR_HIP: return "a HIP launch or copy failed";
+    case LISA_ERR_STALLED: return "a call abandoned a dependency wait; its outputs are undefined";
   }
   return "unknown status";
 }

@@ -29,11 +29,17 @@ __all__ = [
     "make_problem",
     "new_workspace",
     "library_path",
+    "lisa_workspace_check",
+    "lisa_backward",
+    "lisa_backward_after_forward",
+    "lisa_backward_workspace_size",
+    "LISA_ERR_STALLED",
 ]
 
 LISA_FP32 = 0
 LISA_BF16 = 1
 LISA_OK = 0
+LISA_ERR_STALLED = 9
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -105,6 +111,8 @@ _lib.lisa_backward.argtypes = [_P, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp,
 _lib.lisa_backward.restype = ctypes.c_int
 _lib.lisa_backward_after_forward.argtypes = _lib.lisa_backward.argtypes
 _lib.lisa_backward_after_forward.restype = ctypes.c_int
+_lib.lisa_workspace_check.argtypes = [_vp, ctypes.c_size_t, _vp]
+_lib.lisa_workspace_check.restype = ctypes.c_int
 _lib.lisa_status_str.argtypes = [ctypes.c_int]
 _lib.lisa_status_str.restype = ctypes.c_char_p
 
@@ -361,6 +369,18 @@ def _backward(fn, name, q, k, v, dy, *, grid, T, alpha, weights, beta, eps, work
     if st != LISA_OK:
         raise LisaError(st, name)
     return out
+
+
+def lisa_workspace_check(workspace, stream=None):
+    """Synchronise ``stream`` and read (and clear) the workspace's stall flag;
+    see include/lisa.h.  Returns LISA_OK, or LISA_ERR_STALLED when a call on
+    this workspace abandoned a wait (its outputs are then undefined)."""
+    _check_tensors(workspace=workspace)
+    st = _lib.lisa_workspace_check(_ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                                   _stream(stream, workspace.device))
+    if st not in (LISA_OK, LISA_ERR_STALLED):
+        raise LisaError(st, "lisa_workspace_check")
+    return st
 
 
 # Raw entry points for callers that marshal their own pointers (tests, bench).
