@@ -576,7 +576,30 @@ __device__ void prepare(const FlowArgs& a, const Rank& rk, Pos p, unsigned char*
     stage_chunk<Tr>(a, b, is_m, tok0, nv, buf, pw, !keep_k);
     if (is_m && p.j == 0) {
       dependency(kCntKV);
-      const float sv = sum_s_partials(a, b);
+      // s = the sum of the G partials.  Up to 16 partials: every producer
+      // wave sums them all, one round of loads.  More: wave pw sums partials
+      // pw, pw + 4, ..., sixteen loads in flight at a time, and the four sums
+      // meet in the statistics area (free until the OUT phase), added in wave
+      // order.
+      float sv;
+      if (a.G <= 16) {
+        sv = sum_s_partials(a, b);
+      } else {
+        const float* ps = a.part_s + (size_t)b * a.G * kD + lane;
+        const int np = (a.G - pw + kRoleWaves - 1) / kRoleWaves;  // partials of this wave
+        float t = 0.f;
+        for (int q0 = 0; q0 < np; q0 += 16) {
+          float x[16];
+#pragma unroll
+          for (int q = 0; q < 16; ++q) x[q] = get(ps + (size_t)min(pw + kRoleWaves * (q0 + q), a.G - 1) * kD);
+#pragma unroll
+          for (int q = 0; q < 16; ++q) t += (q0 + q < np) ? x[q] : 0.f;
+        }
+        float* sc = reinterpret_cast<float*>(st);
+        sc[pw * kD + lane] = t;
+        producers_meet(mlp_ready);
+        sv = ((sc[lane] + sc[kD + lane]) + sc[2 * kD + lane]) + sc[3 * kD + lane];
+      }
       s_w[lane] = sv;
       if (rk.g == 0 && pw == 0) put(a.fin_s + (size_t)b * kD + lane, sv);
     }
