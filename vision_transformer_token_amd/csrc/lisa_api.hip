@@ -63,7 +63,7 @@ struct Plan {
   int chunk = 0;                                 // tokens per KV / M stage
   int TR = 0, TC = 0, tiles_x = 0, ntiles = 0;   // output tiles per slice
   // workspace layout (byte offsets)
-  size_t slice_cnt = 0, done_cnt = 0, part_s = 0, part_kv = 0, part_m = 0, fin_s = 0, fin_kv = 0,
+  size_t slice_cnt = 0, sub_cnt = 0, done_cnt = 0, part_s = 0, part_kv = 0, part_m = 0, fin_s = 0, fin_kv = 0,
          fin_m = 0, frag_kv = 0, frag_m = 0, total = 0;
   // backward regions, after the forward's (lisa_backward_workspace_size)
   int nblk = 0;
@@ -171,6 +171,7 @@ lisa_status make_plan(const lisa_problem* p, Plan& pl) {
   // problem's data written over a counter (each call leaves them at zero).
   pl.done_cnt = take(32 * sizeof(unsigned));
   pl.slice_cnt = take((size_t)kMaxSlices * lisa::kCntStride * sizeof(unsigned));
+  pl.sub_cnt = take((size_t)lisa::kMaxSubSlices * 3 * lisa::kMaxSubs * lisa::kCntStride * sizeof(unsigned));
   pl.part_s = take(BH * G * vec);
   pl.part_kv = take(BH * G * mat);
   pl.part_m = take(BH * G * mat);
@@ -302,6 +303,10 @@ lisa_status run(Plan pl, Mode mode, const void* Q, const void* K, const void* V,
   a.frag_kv = ws + pl.frag_kv;
   a.frag_m = ws + pl.frag_m;
   a.slice_cnt = reinterpret_cast<unsigned*>(ws + pl.slice_cnt);
+  a.sub_cnt = reinterpret_cast<unsigned*>(ws + pl.sub_cnt);
+  // Arrivals per group of kSubRanks ranks from 64 ranks per slice on (with
+  // 32 the one counter measured faster), bf16 without the predictor.
+  a.grouped = (pl.G >= 64 && pl.BH <= lisa::kMaxSubSlices && pl.dtype == LISA_BF16 && !mlp) ? 1 : 0;
   a.done_cnt = reinterpret_cast<unsigned*>(ws + pl.done_cnt);
   a.err = a.done_cnt + 1;
   a.tickets = a.done_cnt + 8;

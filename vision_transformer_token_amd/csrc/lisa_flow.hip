@@ -138,6 +138,33 @@ __device__ void wait_for(const unsigned* c, unsigned target, unsigned* err) {
   }
 }
 
+// The same wait for a phase counted per group of kSubRanks ranks: lane k of
+// the calling wave (all 64 lanes call) reads group k's counter, until every
+// group's counter has reached kSubRanks; bounded like wait_for.
+__device__ void wait_for_groups(const unsigned* base, int ngroups, unsigned* err) {
+  const int lane = threadIdx.x & 63;
+  const unsigned* c = base + (size_t)min(lane, ngroups - 1) * kCntStride;
+  unsigned spins = 0;
+  for (;;) {
+    const bool done = lane >= ngroups || get(c) >= (unsigned)kSubRanks;
+    if (__all(done)) break;
+    __builtin_amdgcn_s_sleep(10);
+    ++spins;
+    if ((spins & 255u) == 0 && __builtin_amdgcn_readfirstlane(get(err))) break;
+    if (spins > (1u << 21)) {
+      if (lane == 0) put(err, 1u);
+      break;
+    }
+  }
+}
+
+// The counter a rank's arrival for phase `counter` of slice b goes to.
+template <bool kGrouped>
+__device__ __forceinline__ unsigned* arrival_counter(const FlowArgs& a, const Rank& rk, int b, int counter) {
+  if constexpr (kGrouped) return a.sub_cnt + (((size_t)b * 3 + counter) * kMaxSubs + rk.g / kSubRanks) * kCntStride;
+  return a.slice_cnt + (size_t)b * kCntStride + counter;
+}
+
 // A rank's arrival for one phase.  Each consumer wave, after its own stores
 // have completed, counts itself in LDS (`waves`); the last of the kRoleWaves
 // waves bumps the slice counter once, so a slice's counter reaches G.  That
@@ -541,7 +568,7 @@ __device__ __forceinline__ void producers_meet(int* ready) {
 // which the other producer waves watch in LDS.  `s_sl` holds s of each slice
 // of the round in LDS (row z for slice z); every producer wave forms the same
 // fixed-order sum and writes the same values.
-template <class Tr, bool kMlp>
+template <class Tr, bool kMlp, bool kGrouped>
 __device__ void prepare(const FlowArgs& a, const Rank& rk, Pos p, unsigned char* buf, unsigned char* st,
                         float (*s_sl)[kD], volatile int* dep_ok, int* mlp_ready, int pw) {
   using S = typename Tr::S;
@@ -554,7 +581,10 @@ __device__ void prepare(const FlowArgs& a, const Rank& rk, Pos p, unsigned char*
   auto dependency = [&](int counter) {
     const int tag = b * 4 + p.ph;
     if (pw == 0) {
-      if (lane == 0) {
+      if constexpr (kGrouped) {
+        wait_for_groups(a.sub_cnt + ((size_t)b * 3 + counter) * kMaxSubs * kCntStride, a.G / kSubRanks, a.err);
+        if (lane == 0) *dep_ok = tag;
+      } else if (lane == 0) {
         wait_for(&cnt[counter], full, a.err);
         *dep_ok = tag;
       }
@@ -727,7 +757,7 @@ __device__ __forceinline__ void sweep_chunk(const unsigned char* buf, int nv, in
 
 // The KV or M phase of slice b: the rank's chunks, one stage each, then its
 // partial (coherent stores) and the wave's arrival.
-template <class Tr, bool kIsM>
+template <class Tr, bool kIsM, bool kGrouped>
 __device__ int consume_sweep(const FlowArgs& a, const Rank& rk, int b, unsigned char* smem, int bsel, int cw,
                              int* waves) {
   using L = LdsOf<Tr>;
@@ -752,7 +782,7 @@ __device__ int consume_sweep(const FlowArgs& a, const Rank& rk, int b, unsigned 
     for (int i = 0; i < 16; ++i) put(ps + 32 * mb + 8 * (i >> 2) + 4 * h + (i & 3), acc_s[i]);
   }
   wait_all();
-  arrive_rank(a.slice_cnt + (size_t)b * kCntStride + (kIsM ? kCntM : kCntKV), waves);
+  arrive_rank(arrival_counter<kGrouped>(a, rk, b, kIsM ? kCntM : kCntKV), waves);
   lds_barrier();
   return bsel ^ 1;
 }
@@ -779,7 +809,7 @@ __device__ __forceinline__ void store_stat(float* fin, void* frag, int e, float 
 // the two matrices, so the matrix choice stays wave-uniform.  With E < 256,
 // TPE = 256 / E threads share an element (partials p = q, q + TPE, ...) and
 // combine by a fixed xor tree.
-template <class Tr>
+template <class Tr, bool kGrouped>
 __device__ void consume_combine(const FlowArgs& a, const Rank& rk, int b, const unsigned char* buf, int ct,
                                 int* waves) {
   using S = typename Tr::S;
@@ -811,7 +841,7 @@ __device__ void consume_combine(const FlowArgs& a, const Rank& rk, int b, const 
     if (q == 0) store_stat<Tr>(fin, frag, (rk.e0 + e) & (kD * kD - 1), v);
   }
   wait_all();
-  arrive_rank(a.slice_cnt + (size_t)b * kCntStride + kCntC, waves);
+  arrive_rank(arrival_counter<kGrouped>(a, rk, b, kCntC), waves);
   lds_barrier();
 }
 
@@ -1157,7 +1187,7 @@ __device__ int consume_out(const FlowArgs& a, const Rank& rk, int b, unsigned ch
   return bsel;
 }
 
-template <class Tr, bool kMlp>
+template <class Tr, bool kMlp, bool kGrouped>
 __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
   using L = LdsOf<Tr>;
   extern __shared__ __align__(1024) unsigned char smem[];
@@ -1186,14 +1216,14 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
   // barriers: one per stage, plus one at the start of each OUT phase.
   if (producer) {
     Pos p = first_pos(a, rk);
-    if (p.ph != kPEnd) prepare<Tr, kMlp>(a, rk, p, smem, st, s_sl, &dep_ok, &mlp_ready, rw);
+    if (p.ph != kPEnd) prepare<Tr, kMlp, kGrouped>(a, rk, p, smem, st, s_sl, &dep_ok, &mlp_ready, rw);
     lds_barrier();
     int bsel = 0;
     while (p.ph != kPEnd) {
       const Pos np = advance(a, rk, p);
       if (p.ph == kPOut && p.j == 0) lds_barrier();  // the consumers have taken the statistics
       if (np.ph != kPEnd)
-        prepare<Tr, kMlp>(a, rk, np, smem + (bsel ^ 1) * L::kStage, st, s_sl, &dep_ok, &mlp_ready, rw);
+        prepare<Tr, kMlp, kGrouped>(a, rk, np, smem + (bsel ^ 1) * L::kStage, st, s_sl, &dep_ok, &mlp_ready, rw);
       lds_barrier();
       bsel ^= 1;
       p = np;
@@ -1207,13 +1237,13 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
         const int nz = round_slices(a, rk, r);
         if (phase_len(a, rk, kPKV) > 0)
           for (int z = 0; z < nz; ++z)
-            bsel = consume_sweep<Tr, false>(a, rk, slice_of(a, rk, r, z), smem, bsel, rw, &arrivals);
+            bsel = consume_sweep<Tr, false, kGrouped>(a, rk, slice_of(a, rk, r, z), smem, bsel, rw, &arrivals);
         if (phase_len(a, rk, kPM) > 0)
           for (int z = 0; z < nz; ++z)
-            bsel = consume_sweep<Tr, true>(a, rk, slice_of(a, rk, r, z), smem, bsel, rw, &arrivals);
+            bsel = consume_sweep<Tr, true, kGrouped>(a, rk, slice_of(a, rk, r, z), smem, bsel, rw, &arrivals);
         if (phase_len(a, rk, kPC) > 0)
           for (int z = 0; z < nz; ++z) {
-            consume_combine<Tr>(a, rk, slice_of(a, rk, r, z), smem + bsel * L::kStage, tid - kRoleWaves * 64,
+            consume_combine<Tr, kGrouped>(a, rk, slice_of(a, rk, r, z), smem + bsel * L::kStage, tid - kRoleWaves * 64,
                                 &arrivals);
             bsel ^= 1;
           }
@@ -1234,6 +1264,8 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
   if (last) {
     for (int i = tid; i < a.BH * kCntWords; i += kThreads)
       put(a.slice_cnt + (size_t)(i / kCntWords) * kCntStride + i % kCntWords, 0u);
+    if constexpr (kGrouped)
+      for (int i = tid; i < a.BH * 3 * kMaxSubs; i += kThreads) put(a.sub_cnt + (size_t)i * kCntStride, 0u);
     if (tid < kXcds) put(a.tickets + tid, 0u);
     wait_all();
     __syncthreads();
@@ -1241,17 +1273,17 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
   }
 }
 
-template <class Tr, bool kMlp>
+template <class Tr, bool kMlp, bool kGrouped = false>
 hipError_t launch_typed(const FlowArgs& a, int grid, hipStream_t s) {
   constexpr int lds = LdsOf<Tr>::kTotal;
   static bool attr_set = false;
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&flow_kernel<Tr, kMlp>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&flow_kernel<Tr, kMlp, kGrouped>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((flow_kernel<Tr, kMlp>), dim3(grid), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((flow_kernel<Tr, kMlp, kGrouped>), dim3(grid), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -1285,6 +1317,9 @@ __global__ __launch_bounds__(256) void mlp_prep(const float* w1, float* out, int
 }  // namespace
 
 hipError_t launch_flow(int dtype, const FlowArgs& a, int grid, hipStream_t s) {
+  // Arrivals counted per group of ranks: a variant of the bf16 kernel of its
+  // own, so that the others compile exactly as without it.
+  if (a.grouped) return launch_typed<BF16, false, true>(a, grid, s);
   if (a.mlp_w1f) return dtype == 1 ? launch_typed<BF16, true>(a, grid, s) : launch_typed<F32, true>(a, grid, s);
   return dtype == 1 ? launch_typed<BF16, false>(a, grid, s) : launch_typed<F32, false>(a, grid, s);
 }

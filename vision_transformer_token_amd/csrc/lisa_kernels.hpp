@@ -16,6 +16,13 @@ constexpr int kMaxRanks = 256;  // G <= 256: each rank combines >= 32 elements
 constexpr int kMaxTileTokens = 256;
 constexpr int kCntWords = 4;    // arrival counters per (batch, head) slice: KV, M, C (+ pad)
 constexpr int kCntStride = 32;  // words between slices: each slice's counters on their own 128-byte line
+// With more than kSubRanks ranks per slice, a phase's arrivals are counted per
+// group of kSubRanks ranks, each group's counter on its own 128-byte line
+// (slices < kMaxSubSlices, groups < kMaxSubs); a wait then reads every
+// group's counter at once.
+constexpr int kSubRanks = 16;
+constexpr int kMaxSubSlices = 8;
+constexpr int kMaxSubs = 256 / kSubRanks;
 
 // LDS of one workgroup, per element size ES: two staging buffers of kStage
 // bytes that the DMA of the next stage and the compute of the current one
@@ -94,6 +101,8 @@ struct FlowArgs {
   void* frag_kv;          // [BH][64*64] elements of the input dtype
   void* frag_m;           // [BH][64*64]
   unsigned* slice_cnt;    // [BH][kCntStride], words 0..kCntWords-1 used
+  unsigned* sub_cnt;      // [kMaxSubSlices][3][kMaxSubs][kCntStride], word 0 of each line used
+  int grouped;            // arrivals counted per group of kSubRanks ranks (sub_cnt)
   unsigned* done_cnt;     // finished workgroups
   unsigned* tickets;      // [kXcds] rank tickets
   unsigned* err;          // error word (a dependency wait timed out)
