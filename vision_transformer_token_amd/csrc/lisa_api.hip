@@ -304,9 +304,14 @@ lisa_status run(Plan pl, Mode mode, const void* Q, const void* K, const void* V,
   a.frag_m = ws + pl.frag_m;
   a.slice_cnt = reinterpret_cast<unsigned*>(ws + pl.slice_cnt);
   a.sub_cnt = reinterpret_cast<unsigned*>(ws + pl.sub_cnt);
-  // Arrivals per group of kSubRanks ranks from 64 ranks per slice on (with
-  // 32 the one counter measured faster), bf16 without the predictor.
-  a.grouped = (pl.G >= 64 && pl.BH <= lisa::kMaxSubSlices && pl.dtype == LISA_BF16 && !mlp) ? 1 : 0;
+  // Kernel variant (bf16 without the predictor): arrivals per group of
+  // kSubRanks ranks from 64 ranks per slice on (with 32 the one counter
+  // measured faster); with one rank per slice, a combine that writes the
+  // statistics in whole rows and fragment lanes.
+  const bool variants = pl.dtype == LISA_BF16 && !mlp;
+  a.variant = (variants && pl.G >= 64 && pl.BH <= lisa::kMaxSubSlices) ? lisa::kVarGrouped
+              : (variants && pl.G == 1)                                 ? lisa::kVarSolo
+                                                                        : lisa::kVarPlain;
   a.done_cnt = reinterpret_cast<unsigned*>(ws + pl.done_cnt);
   a.err = a.done_cnt + 1;
   a.tickets = a.done_cnt + 8;

@@ -159,9 +159,9 @@ __device__ void wait_for_groups(const unsigned* base, int ngroups, unsigned* err
 }
 
 // The counter a rank's arrival for phase `counter` of slice b goes to.
-template <bool kGrouped>
+template <int kVar>
 __device__ __forceinline__ unsigned* arrival_counter(const FlowArgs& a, const Rank& rk, int b, int counter) {
-  if constexpr (kGrouped) return a.sub_cnt + (((size_t)b * 3 + counter) * kMaxSubs + rk.g / kSubRanks) * kCntStride;
+  if constexpr (kVar == kVarGrouped) return a.sub_cnt + (((size_t)b * 3 + counter) * kMaxSubs + rk.g / kSubRanks) * kCntStride;
   return a.slice_cnt + (size_t)b * kCntStride + counter;
 }
 
@@ -568,7 +568,7 @@ __device__ __forceinline__ void producers_meet(int* ready) {
 // which the other producer waves watch in LDS.  `s_sl` holds s of each slice
 // of the round in LDS (row z for slice z); every producer wave forms the same
 // fixed-order sum and writes the same values.
-template <class Tr, bool kMlp, bool kGrouped>
+template <class Tr, bool kMlp, int kVar>
 __device__ void prepare(const FlowArgs& a, const Rank& rk, Pos p, unsigned char* buf, unsigned char* st,
                         float (*s_sl)[kD], volatile int* dep_ok, int* mlp_ready, int pw) {
   using S = typename Tr::S;
@@ -581,7 +581,7 @@ __device__ void prepare(const FlowArgs& a, const Rank& rk, Pos p, unsigned char*
   auto dependency = [&](int counter) {
     const int tag = b * 4 + p.ph;
     if (pw == 0) {
-      if constexpr (kGrouped) {
+      if constexpr (kVar == kVarGrouped) {
         wait_for_groups(a.sub_cnt + ((size_t)b * 3 + counter) * kMaxSubs * kCntStride, a.G / kSubRanks, a.err);
         if (lane == 0) *dep_ok = tag;
       } else if (lane == 0) {
@@ -757,7 +757,7 @@ __device__ __forceinline__ void sweep_chunk(const unsigned char* buf, int nv, in
 
 // The KV or M phase of slice b: the rank's chunks, one stage each, then its
 // partial (coherent stores) and the wave's arrival.
-template <class Tr, bool kIsM, bool kGrouped>
+template <class Tr, bool kIsM, int kVar>
 __device__ int consume_sweep(const FlowArgs& a, const Rank& rk, int b, unsigned char* smem, int bsel, int cw,
                              int* waves) {
   using L = LdsOf<Tr>;
@@ -782,7 +782,7 @@ __device__ int consume_sweep(const FlowArgs& a, const Rank& rk, int b, unsigned 
     for (int i = 0; i < 16; ++i) put(ps + 32 * mb + 8 * (i >> 2) + 4 * h + (i & 3), acc_s[i]);
   }
   wait_all();
-  arrive_rank(arrival_counter<kGrouped>(a, rk, b, kIsM ? kCntM : kCntKV), waves);
+  arrive_rank(arrival_counter<kVar>(a, rk, b, kIsM ? kCntM : kCntKV), waves);
   lds_barrier();
   return bsel ^ 1;
 }
@@ -809,7 +809,7 @@ __device__ __forceinline__ void store_stat(float* fin, void* frag, int e, float 
 // the two matrices, so the matrix choice stays wave-uniform.  With E < 256,
 // TPE = 256 / E threads share an element (partials p = q, q + TPE, ...) and
 // combine by a fixed xor tree.
-template <class Tr, bool kGrouped>
+template <class Tr, int kVar>
 __device__ void consume_combine(const FlowArgs& a, const Rank& rk, int b, const unsigned char* buf, int ct,
                                 int* waves) {
   using S = typename Tr::S;
@@ -819,7 +819,41 @@ __device__ void consume_combine(const FlowArgs& a, const Rank& rk, int b, const 
     fin = (m ? a.fin_m : a.fin_kv) + (size_t)b * (kD * kD);
     frag = static_cast<S*>(m ? a.frag_m : a.frag_kv) + (size_t)b * (kD * kD);
   };
-  if (rk.E >= kRoleWaves * 64) {
+  if constexpr (kVar == kVarSolo) {
+    // One rank per slice (bf16): the staged partial is the statistics
+    // themselves, [phi(K)^T V | M] row by row.  fp32 rows with 16-byte
+    // stores; each fragment lane's eight bf16 (store_stat's layout) gathered
+    // from LDS and written as four coherent words.  Values are formed as
+    // 0 + x, as the sum over one partial elsewhere.
+    for (int i = ct; i < 2 * kD * kD / 4; i += kRoleWaves * 64) {
+      const int f = 4 * i;
+      float* fin = (f < kD * kD ? a.fin_kv : a.fin_m) + (size_t)b * (kD * kD) + (f & (kD * kD - 1));
+      const float4 x = *reinterpret_cast<const float4*>(stg + f);
+      *reinterpret_cast<float4*>(fin) = make_float4(0.f + x.x, 0.f + x.y, 0.f + x.z, 0.f + x.w);
+    }
+    constexpr int kPieces = 2 * Tr::NQ * 64;  // per matrix: (mb, q, lane), eight elements each
+    for (int pc = ct; pc < 2 * kPieces; pc += kRoleWaves * 64) {
+      const int mat = pc / kPieces, rem = pc % kPieces;
+      const int mb = rem / (Tr::NQ * 64), q = (rem / 64) % Tr::NQ, ln = rem % 64;
+      const int c = 32 * mb + (ln & 31), h = ln >> 5;
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        float x2[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int vs = 8 * q + j + t;  // accumulator slot: row 32 (vs / 16) + 8 (vs / 4 % 4) + 4 h + vs % 4
+          const int r = 32 * (vs >> 4) + 8 * ((vs >> 2) & 3) + 4 * h + (vs & 3);
+          x2[t] = 0.f + stg[mat * (kD * kD) + r * kD + c];
+        }
+        w[j / 2] = pack_bf16x2(x2[0], x2[1]);
+      }
+      uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<S*>(mat ? a.frag_m : a.frag_kv) + (size_t)b * (kD * kD)) +
+                      (size_t)rem * 4;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) put(dst + k, w[k]);
+    }
+  } else if (rk.E >= kRoleWaves * 64) {
     for (int e0 = 0; e0 < rk.E; e0 += kRoleWaves * 64) {
       float* fin;
       void* frag;
@@ -841,7 +875,7 @@ __device__ void consume_combine(const FlowArgs& a, const Rank& rk, int b, const 
     if (q == 0) store_stat<Tr>(fin, frag, (rk.e0 + e) & (kD * kD - 1), v);
   }
   wait_all();
-  arrive_rank(arrival_counter<kGrouped>(a, rk, b, kCntC), waves);
+  arrive_rank(arrival_counter<kVar>(a, rk, b, kCntC), waves);
   lds_barrier();
 }
 
@@ -1187,7 +1221,7 @@ __device__ int consume_out(const FlowArgs& a, const Rank& rk, int b, unsigned ch
   return bsel;
 }
 
-template <class Tr, bool kMlp, bool kGrouped>
+template <class Tr, bool kMlp, int kVar>
 __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
   using L = LdsOf<Tr>;
   extern __shared__ __align__(1024) unsigned char smem[];
@@ -1216,14 +1250,14 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
   // barriers: one per stage, plus one at the start of each OUT phase.
   if (producer) {
     Pos p = first_pos(a, rk);
-    if (p.ph != kPEnd) prepare<Tr, kMlp, kGrouped>(a, rk, p, smem, st, s_sl, &dep_ok, &mlp_ready, rw);
+    if (p.ph != kPEnd) prepare<Tr, kMlp, kVar>(a, rk, p, smem, st, s_sl, &dep_ok, &mlp_ready, rw);
     lds_barrier();
     int bsel = 0;
     while (p.ph != kPEnd) {
       const Pos np = advance(a, rk, p);
       if (p.ph == kPOut && p.j == 0) lds_barrier();  // the consumers have taken the statistics
       if (np.ph != kPEnd)
-        prepare<Tr, kMlp, kGrouped>(a, rk, np, smem + (bsel ^ 1) * L::kStage, st, s_sl, &dep_ok, &mlp_ready, rw);
+        prepare<Tr, kMlp, kVar>(a, rk, np, smem + (bsel ^ 1) * L::kStage, st, s_sl, &dep_ok, &mlp_ready, rw);
       lds_barrier();
       bsel ^= 1;
       p = np;
@@ -1237,13 +1271,13 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
         const int nz = round_slices(a, rk, r);
         if (phase_len(a, rk, kPKV) > 0)
           for (int z = 0; z < nz; ++z)
-            bsel = consume_sweep<Tr, false, kGrouped>(a, rk, slice_of(a, rk, r, z), smem, bsel, rw, &arrivals);
+            bsel = consume_sweep<Tr, false, kVar>(a, rk, slice_of(a, rk, r, z), smem, bsel, rw, &arrivals);
         if (phase_len(a, rk, kPM) > 0)
           for (int z = 0; z < nz; ++z)
-            bsel = consume_sweep<Tr, true, kGrouped>(a, rk, slice_of(a, rk, r, z), smem, bsel, rw, &arrivals);
+            bsel = consume_sweep<Tr, true, kVar>(a, rk, slice_of(a, rk, r, z), smem, bsel, rw, &arrivals);
         if (phase_len(a, rk, kPC) > 0)
           for (int z = 0; z < nz; ++z) {
-            consume_combine<Tr, kGrouped>(a, rk, slice_of(a, rk, r, z), smem + bsel * L::kStage, tid - kRoleWaves * 64,
+            consume_combine<Tr, kVar>(a, rk, slice_of(a, rk, r, z), smem + bsel * L::kStage, tid - kRoleWaves * 64,
                                 &arrivals);
             bsel ^= 1;
           }
@@ -1264,7 +1298,7 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
   if (last) {
     for (int i = tid; i < a.BH * kCntWords; i += kThreads)
       put(a.slice_cnt + (size_t)(i / kCntWords) * kCntStride + i % kCntWords, 0u);
-    if constexpr (kGrouped)
+    if constexpr (kVar == kVarGrouped)
       for (int i = tid; i < a.BH * 3 * kMaxSubs; i += kThreads) put(a.sub_cnt + (size_t)i * kCntStride, 0u);
     if (tid < kXcds) put(a.tickets + tid, 0u);
     wait_all();
@@ -1273,17 +1307,17 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
   }
 }
 
-template <class Tr, bool kMlp, bool kGrouped = false>
+template <class Tr, bool kMlp, int kVar = kVarPlain>
 hipError_t launch_typed(const FlowArgs& a, int grid, hipStream_t s) {
   constexpr int lds = LdsOf<Tr>::kTotal;
   static bool attr_set = false;
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&flow_kernel<Tr, kMlp, kGrouped>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&flow_kernel<Tr, kMlp, kVar>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((flow_kernel<Tr, kMlp, kGrouped>), dim3(grid), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((flow_kernel<Tr, kMlp, kVar>), dim3(grid), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -1317,9 +1351,10 @@ __global__ __launch_bounds__(256) void mlp_prep(const float* w1, float* out, int
 }  // namespace
 
 hipError_t launch_flow(int dtype, const FlowArgs& a, int grid, hipStream_t s) {
-  // Arrivals counted per group of ranks: a variant of the bf16 kernel of its
-  // own, so that the others compile exactly as without it.
-  if (a.grouped) return launch_typed<BF16, false, true>(a, grid, s);
+  // The bf16 kernel's variants for many ranks per slice and for one, each a
+  // kernel of its own, so that the others compile exactly as without them.
+  if (a.variant == kVarGrouped) return launch_typed<BF16, false, kVarGrouped>(a, grid, s);
+  if (a.variant == kVarSolo) return launch_typed<BF16, false, kVarSolo>(a, grid, s);
   if (a.mlp_w1f) return dtype == 1 ? launch_typed<BF16, true>(a, grid, s) : launch_typed<F32, true>(a, grid, s);
   return dtype == 1 ? launch_typed<BF16, false>(a, grid, s) : launch_typed<F32, false>(a, grid, s);
 }

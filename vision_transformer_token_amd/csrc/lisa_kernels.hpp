@@ -23,6 +23,8 @@ constexpr int kCntStride = 32;  // words between slices: each slice's counters o
 constexpr int kSubRanks = 16;
 constexpr int kMaxSubSlices = 8;
 constexpr int kMaxSubs = 256 / kSubRanks;
+// Kernel variants (bf16 without the predictor; FlowArgs::variant).
+constexpr int kVarPlain = 0, kVarGrouped = 1, kVarSolo = 2;
 
 // LDS of one workgroup, per element size ES: two staging buffers of kStage
 // bytes that the DMA of the next stage and the compute of the current one
@@ -102,7 +104,8 @@ struct FlowArgs {
   void* frag_m;           // [BH][64*64]
   unsigned* slice_cnt;    // [BH][kCntStride], words 0..kCntWords-1 used
   unsigned* sub_cnt;      // [kMaxSubSlices][3][kMaxSubs][kCntStride], word 0 of each line used
-  int grouped;            // arrivals counted per group of kSubRanks ranks (sub_cnt)
+  int variant;            // kVarPlain, kVarGrouped (arrivals per group of kSubRanks ranks, sub_cnt),
+                          // kVarSolo (one rank per slice: the combine writes the statistics directly)
   unsigned* done_cnt;     // finished workgroups
   unsigned* tickets;      // [kXcds] rank tickets
   unsigned* err;          // error word (a dependency wait timed out)
