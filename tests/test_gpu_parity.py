@@ -97,6 +97,7 @@ RAGGED = [
     (96, 3, 14, 14, 3, "bf16", "adaptive"),
     (96, 3, 14, 14, 5, "fp32", "geometric"),
     (130, 2, 9, 11, 4, "bf16", "adaptive"),
+    (1, 1, 24, 24, 3, "bf16", "adaptive"),    # four ranks per slice
 ]
 
 
