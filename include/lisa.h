@@ -71,7 +71,8 @@ typedef enum lisa_status {
   LISA_OK = 0,
   LISA_ERR_NULL = 1,        /* a required pointer is NULL */
   LISA_ERR_SHAPE = 2,       /* a dimension is <= 0 or too large */
-  LISA_ERR_PARAM = 3,       /* T outside 1..8, beta outside [0,1), eps <= 0 or not finite */
+  LISA_ERR_PARAM = 3,       /* T outside 1..16 (1..8 with the predictor and the backward),
+                               beta outside [0,1), eps <= 0 or not finite */
   LISA_ERR_DTYPE = 4,       /* dtype is not LISA_FP32 / LISA_BF16 */
   LISA_ERR_UNSUPPORTED = 5, /* d_h or d_v other than 64, or batch*heads > 65535 */
   LISA_ERR_WORKSPACE = 6,   /* workspace NULL, too small or not 256-byte aligned */
@@ -90,7 +91,8 @@ typedef struct lisa_problem {
   int32_t grid_w; /* W >= 1; H * W <= 2^24 */
   int32_t d_h;    /* query/key width: 64 */
   int32_t d_v;    /* value width: 64 */
-  int32_t T;      /* walk terms k = 0..T-1, 1 <= T <= 8 */
+  int32_t T;      /* walk terms k = 0..T-1, 1 <= T <= 16; at most 8 for
+                     lisa_forward_mlp and the backward entry points */
   int32_t dtype;  /* lisa_dtype of Q, K, V, Y */
   float eps;      /* row-normaliser stabiliser, finite and > 0 */
 } lisa_problem;
@@ -154,7 +156,8 @@ typedef struct lisa_weight_mlp {
 } lisa_weight_mlp;
 
 /* Workspace bytes for lisa_forward_mlp (the forward's workspace plus W1 in
- * the layout the kernel reads), or 0 if the problem or hidden is invalid. */
+ * the layout the kernel reads), or 0 if the problem or hidden is invalid
+ * (T > 8 included). */
 size_t lisa_forward_mlp_workspace_size(const lisa_problem* p, int32_t hidden);
 
 /* The forward pass with the walk weights predicted inside the output pass
@@ -162,7 +165,7 @@ size_t lisa_forward_mlp_workspace_size(const lisa_problem* p, int32_t hidden);
  * lisa_forward given the predictor's weights.  With bf16 inputs the first
  * layer multiplies the exact bf16 inputs by W1 rounded to bf16 (as the walk
  * rounds its P_k), with fp32 sums; everything else is fp32.  mlp NULL or a NULL array:
- * LISA_ERR_NULL; hidden out of range: LISA_ERR_PARAM; other arguments and
+ * LISA_ERR_NULL; hidden out of range or T > 8: LISA_ERR_PARAM; other arguments and
  * errors as for lisa_forward with weights == NULL, the workspace
  * lisa_forward_mlp_workspace_size bytes. */
 lisa_status lisa_forward_mlp(const lisa_problem* p, const void* Q, const void* K, const void* V,
@@ -207,7 +210,8 @@ lisa_status lisa_attention_forward(const lisa_problem* p, const void* X, const v
  *              gradient for beta is formed)
  *   dalpha   : [heads] fp32 gradient of alpha (summed over the batch)
  * Outputs must not overlap any input, each other or the workspace
- * (LISA_ERR_PARAM).  Workspace: lisa_backward_workspace_size bytes, 256-byte
+ * (LISA_ERR_PARAM), as is T > 8.  Workspace: lisa_backward_workspace_size
+ * bytes (0 for an invalid problem or T > 8), 256-byte
  * aligned, zero-filled before its first use like lisa_forward's; it also
  * serves lisa_forward, lisa_reduce and lisa_apply of the same problem. */
 size_t lisa_backward_workspace_size(const lisa_problem* p);

@@ -82,7 +82,7 @@ def test_forward_argument_errors(fn):
         assert forward(prob(**bad), fn=f) == SHAPE, bad
     for bad in (dict(d_h=32), dict(d_v=128), dict(batch=300, heads=300)):
         assert forward(prob(**bad), fn=f) == UNSUP, bad
-    for bad in (dict(T=0), dict(T=9), dict(eps=0.0), dict(eps=-1e-6), dict(eps=math.nan),
+    for bad in (dict(T=0), dict(T=17), dict(eps=0.0), dict(eps=-1e-6), dict(eps=math.nan),
                 dict(eps=math.inf)):
         assert forward(prob(**bad), fn=f) == PARAM, bad
     for beta in (1.0, -0.1, math.nan):
@@ -142,6 +142,9 @@ def test_backward_workspace_covers_the_forward():
         p = prob(T=T, grid_h=40, grid_w=33)
         assert lisa.lisa_backward_workspace_size(p) >= lisa.lisa_workspace_size(p) > 0
     assert lisa.lisa_backward_workspace_size(prob(T=9)) == 0
+    # The forward takes up to 16 walk terms, the backward up to 8.
+    assert lisa.lisa_workspace_size(prob(T=16)) > 0
+    assert lisa.lisa_workspace_size(prob(T=17)) == 0
 
 
 @pytest.fixture(params=["lisa_backward", "lisa_backward_after_forward"])
@@ -225,6 +228,7 @@ def test_mlp_argument_errors():
     assert forward_mlp(prob(grid_h=0)) == SHAPE
     assert forward_mlp(prob(d_h=32)) == UNSUP
     assert forward_mlp(prob(T=0)) == PARAM
+    assert forward_mlp(prob(T=9), ws_bytes=1 << 30) == PARAM
     for hidden in (16, 48, 160):
         assert forward_mlp(prob(), hidden=hidden, ws_bytes=1 << 30) == PARAM, hidden
     for name in ("w1", "b1", "w2", "b2"):
@@ -251,7 +255,8 @@ def test_attention_workspace_size():
     p = prob(grid_h=40, grid_w=33)
     tensor = 2 * 3 * 40 * 33 * 64 * 2
     assert lisa.lisa_attention_workspace_size(p) >= lisa.lisa_workspace_size(p) + 4 * tensor
-    assert lisa.lisa_attention_workspace_size(prob(T=9)) == 0
+    assert lisa.lisa_attention_workspace_size(prob(T=17)) == 0
+    assert lisa.lisa_attention_workspace_size(prob(T=16)) > 0
 
 
 def test_attention_argument_errors():
@@ -259,7 +264,7 @@ def test_attention_argument_errors():
     assert attention(prob(dtype=3)) == DTYPE
     assert attention(prob(grid_h=0)) == SHAPE
     assert attention(prob(d_h=32)) == UNSUP
-    assert attention(prob(T=9)) == PARAM
+    assert attention(prob(T=17)) == PARAM
     assert attention(prob(), w=None, beta=1.0) == PARAM
     for name in ("x", "wq", "bq", "wo", "bo", "alpha", "y"):
         assert attention(prob(), **{name: None}) == NULL, name

@@ -98,6 +98,11 @@ RAGGED = [
     (96, 3, 14, 14, 5, "fp32", "geometric"),
     (130, 2, 9, 11, 4, "bf16", "adaptive"),
     (1, 1, 24, 24, 3, "bf16", "adaptive"),    # four ranks per slice
+    # More than eight walk terms (the forward takes up to 16).
+    (2, 1, 13, 17, 12, "bf16", "geometric"),
+    (1, 2, 20, 23, 16, "fp32", "adaptive"),
+    (1, 1, 56, 56, 16, "bf16", "adaptive"),
+    (2, 1, 9, 33, 9, "fp32", "geometric"),
 ]
 
 
@@ -117,6 +122,19 @@ def test_each_walk_term_alone(lisa, dtype):
     w = workloads.small("onehot", 2, 1, 9, 11, T, dtype=dtype, alpha=1.0, seed=31)
     x = workloads.make_inputs(w)
     for k in range(T):
+        wt = torch.zeros_like(x["weights"])
+        wt[..., k] = 1.0
+        xk = dict(x, weights=wt)
+        check(gpu_y(lisa, to_dev(xk)), oracle_y(xk), dtype, f"S^{k} V {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_highest_walk_terms_alone(lisa, dtype):
+    """T = 16: one-hot weights on terms past the eighth (S^9 V, S^15 V)."""
+    T = 16
+    w = workloads.small("onehot16", 1, 2, 10, 13, T, dtype=dtype, alpha=1.0, seed=37)
+    x = workloads.make_inputs(w)
+    for k in (9, 15):
         wt = torch.zeros_like(x["weights"])
         wt[..., k] = 1.0
         xk = dict(x, weights=wt)

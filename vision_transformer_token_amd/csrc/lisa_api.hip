@@ -379,7 +379,9 @@ lisa_status lisa_apply(const lisa_problem* p, const void* Q, const void* K, cons
 
 size_t lisa_forward_mlp_workspace_size(const lisa_problem* p, int32_t hidden) {
   Plan pl;
-  if (make_plan(p, pl) != LISA_OK || hidden < 32 || hidden > lisa::kMaxHidden || hidden % 32 != 0) return 0;
+  if (make_plan(p, pl) != LISA_OK || pl.T > lisa::kMaxTBwd || hidden < 32 || hidden > lisa::kMaxHidden ||
+      hidden % 32 != 0)
+    return 0;
   return up(pl.total, kAlign) + lisa::mlp_frag_bytes(pl.dtype, pl.heads, hidden);
 }
 
@@ -390,6 +392,7 @@ lisa_status lisa_forward_mlp(const lisa_problem* p, const void* Q, const void* K
   Plan pl;
   lisa_status st = make_plan(p, pl);
   if (st != LISA_OK) return st;
+  if (pl.T > lisa::kMaxTBwd) return LISA_ERR_PARAM;
   if (mlp->hidden < 32 || mlp->hidden > lisa::kMaxHidden || mlp->hidden % 32 != 0) return LISA_ERR_PARAM;
   if (!mlp->w1 || !mlp->b1 || !mlp->w2 || !mlp->b2) return LISA_ERR_NULL;
   if (misaligned(mlp->w1, 4) || misaligned(mlp->b1, 4) || misaligned(mlp->w2, 4) || misaligned(mlp->b2, 4))
@@ -466,7 +469,7 @@ lisa_status lisa_attention_forward(const lisa_problem* p, const void* X, const v
 
 size_t lisa_backward_workspace_size(const lisa_problem* p) {
   Plan pl;
-  return make_plan(p, pl) == LISA_OK ? pl.btotal : 0;
+  return make_plan(p, pl) == LISA_OK && pl.T <= lisa::kMaxTBwd ? pl.btotal : 0;
 }
 
 // The backward pass; with have_stats the slice statistics of a preceding
@@ -480,6 +483,7 @@ static lisa_status backward_common(const lisa_problem* p, const void* Q, const v
   Plan pl;
   lisa_status st = make_plan(p, pl);
   if (st != LISA_OK) return st;
+  if (pl.T > lisa::kMaxTBwd) return LISA_ERR_PARAM;
   if (!weights && !(beta >= 0.f && beta < 1.f)) return LISA_ERR_PARAM;
   if (!Q || !K || !V || !alpha || !dY || !dQ || !dK || !dV || !dalpha) return LISA_ERR_NULL;
   if (misaligned(Q, 16) || misaligned(K, 16) || misaligned(V, 16) || misaligned(dY, 16) ||
@@ -525,7 +529,7 @@ static lisa_status backward_common(const lisa_problem* p, const void* Q, const v
   a.dalpha = dalpha;
   const double b = weights ? 0.0 : (double)beta;
   const double norm = (1.0 - b) / (1.0 - std::pow(b, pl.T));
-  for (int k = 0; k < lisa::kMaxT; ++k) a.geo[k] = k < pl.T ? (float)(norm * std::pow(b, k)) : 0.f;
+  for (int k = 0; k < lisa::kMaxTBwd; ++k) a.geo[k] = k < pl.T ? (float)(norm * std::pow(b, k)) : 0.f;
   a.H = pl.H;
   a.W = pl.W;
   a.n = pl.n;

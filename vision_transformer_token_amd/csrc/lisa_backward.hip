@@ -45,7 +45,7 @@ constexpr int kAdjThreads = 1024;  // per-slice kernels: wave w owns rows 16 (w 
 constexpr int kQ = 4;                // lanes per token
 constexpr int kF = kD / kQ;          // features per lane
 constexpr int kTT = kBT * kQ;        // threads of a token-pass workgroup
-constexpr int kW = kMaxT + 1;        // padded LDS row of a token's walk weights
+constexpr int kW = kMaxTBwd + 1;        // padded LDS row of a token's walk weights
 
 // This lane's 16 features of a row.
 template <class S>
@@ -359,7 +359,7 @@ constexpr size_t token_a_lds() {
   if constexpr (sizeof(S) == 4)
     return (size_t)(kD * kR + kD + 2 * kBT * kR + kBT * kW + kBT) * sizeof(float);
   else
-    return (size_t)4 * kD * kTS * 2 + RowsOf<S>::kMatBytes + ((kMaxT - 1) * kBT + kD + kBT) * sizeof(float);
+    return (size_t)4 * kD * kTS * 2 + RowsOf<S>::kMatBytes + ((kMaxTBwd - 1) * kBT + kD + kBT) * sizeof(float);
 }
 
 template <class S>
@@ -379,7 +379,7 @@ __global__ __launch_bounds__(kTT) void bwd_token_a(BwdArgs a) {
   uint16_t* dyT = qT + kD * kTS;
   unsigned char* Pst = reinterpret_cast<unsigned char*>(dyT + kD * kTS);
   float* stab = reinterpret_cast<float*>(Pst + RowsOf<S>::kMatBytes);
-  float* s_sh = kF32 ? w_sh + kBT * kW : stab + (kMaxT - 1) * kBT;  // kD
+  float* s_sh = kF32 ? w_sh + kBT * kW : stab + (kMaxTBwd - 1) * kBT;  // kD
   float* red = s_sh + kD;                                             // kBT
   const int b = blockIdx.y, t = threadIdx.x, blk = blockIdx.x;
   const int tk = t / kQ, qd = t % kQ, f0 = qd * kF;
@@ -392,12 +392,12 @@ __global__ __launch_bounds__(kTT) void bwd_token_a(BwdArgs a) {
   const S* Vb = static_cast<const S*>(a.V) + base * kD;
   const S* dYb = static_cast<const S*>(a.dY) + base * kD;
   if (t < kD) s_sh[t] = a.fin_s[(size_t)b * kD + t];
-  float wk[kMaxT];
+  float wk[kMaxTBwd];
 #pragma unroll
-  for (int k = 0; k < kMaxT; ++k) wk[k] = (on && k < a.T) ? wgt(a, base + i, k) : 0.f;
+  for (int k = 0; k < kMaxTBwd; ++k) wk[k] = (on && k < a.T) ? wgt(a, base + i, k) : 0.f;
   if (kF32 && qd == 0)
 #pragma unroll
-    for (int k = 0; k < kMaxT; ++k) w_sh[tk * kW + k] = wk[k];
+    for (int k = 0; k < kMaxTBwd; ++k) w_sh[tk * kW + k] = wk[k];
 
   float q[kF], dy[kF];
   float m = 0.f, Z = 1.f, dyL = 0.f, dyv = 0.f;
@@ -463,9 +463,9 @@ __global__ __launch_bounds__(kTT) void bwd_token_a(BwdArgs a) {
     den += q[e] * s_sh[f0 + e];
   }
   const float r = 1.f / (quad_sum(den) + a.eps);
-  float dyy[kMaxT];
+  float dyy[kMaxTBwd];
 #pragma unroll
-  for (int k = 0; k < kMaxT; ++k) dyy[k] = 0.f;
+  for (int k = 0; k < kMaxTBwd; ++k) dyy[k] = 0.f;
   const int T1 = a.T - 1;
   // MFMA roles: wave wv holds tokens 16 wv .. 16 wv + 15 (its quads) and the
   // 16 x 16 block (ga, gc) of dP_k; lane ln = 16 lk + li.
@@ -478,7 +478,7 @@ __global__ __launch_bounds__(kTT) void bwd_token_a(BwdArgs a) {
       dy_sh[tk * kR + f0 + e] = dy[e];
     }
 #pragma unroll
-    for (int k = 1; k < kMaxT; ++k) {
+    for (int k = 1; k < kMaxTBwd; ++k) {
       if (k > T1) break;
       __syncthreads();
       load_mat_padded(Ps, a.pk + ((size_t)b * T1 + (k - 1)) * kD * kD);
@@ -529,7 +529,7 @@ __global__ __launch_bounds__(kTT) void bwd_token_a(BwdArgs a) {
     }
     if (qd == 0)
 #pragma unroll
-      for (int k = 1; k < kMaxT; ++k)
+      for (int k = 1; k < kMaxTBwd; ++k)
         if (k <= T1) stab[(k - 1) * kBT + tk] = alpha * wk[k] * r;
     quad_lds_sync();
     // This wave's operands, fixed over k: A = phi(Q) of its 16 tokens
@@ -548,7 +548,7 @@ __global__ __launch_bounds__(kTT) void bwd_token_a(BwdArgs a) {
     const uint16_t* Ph = reinterpret_cast<const uint16_t*>(Pst);
     const uint16_t* Pl = Ph + kD * kRB;
 #pragma unroll
-    for (int k = 1; k < kMaxT; ++k) {
+    for (int k = 1; k < kMaxTBwd; ++k) {
       if (k > T1) break;
       __syncthreads();
       stage_mat<S, false>(Pst, a.pk + ((size_t)b * T1 + (k - 1)) * kD * kD);
@@ -614,7 +614,7 @@ __global__ __launch_bounds__(kTT) void bwd_token_a(BwdArgs a) {
   // Scalars of the token (every lane of the quad holds them).
   float wy = 0.f;
 #pragma unroll
-  for (int k = 1; k < kMaxT; ++k)
+  for (int k = 1; k < kMaxTBwd; ++k)
     if (k <= T1) wy += wk[k] * dyy[k];
   const float dyG = wk[0] * dyv + wy;
   if (on && qd == 0) {
@@ -624,7 +624,7 @@ __global__ __launch_bounds__(kTT) void bwd_token_a(BwdArgs a) {
       float* dw = a.dweights + (base + i) * a.T;
       dw[0] = alpha * dyv;
 #pragma unroll
-      for (int k = 1; k < kMaxT; ++k)
+      for (int k = 1; k < kMaxTBwd; ++k)
         if (k <= T1) dw[k] = alpha * dyy[k];
     }
   }
@@ -1000,7 +1000,7 @@ hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_token_a<S>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_a);
     if (e != hipSuccess) return e;
-    const size_t lds_adj_max = ((size_t)kMaxT + 1) * kD * kR * sizeof(float);
+    const size_t lds_adj_max = ((size_t)kMaxTBwd + 1) * kD * kR * sizeof(float);
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_adjoint),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_adj_max);
     if (e != hipSuccess) return e;

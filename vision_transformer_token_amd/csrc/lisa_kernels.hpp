@@ -8,7 +8,8 @@
 namespace lisa {
 
 constexpr int kD = 64;          // d_h = d_v supported by the kernel
-constexpr int kMaxT = 8;        // walk terms k = 0..T-1
+constexpr int kMaxT = 16;       // walk terms k = 0..T-1 of the forward
+constexpr int kMaxTBwd = 8;     // of the backward and the walk-weight predictor
 constexpr int kThreads = 512;   // 8 waves of 64 per workgroup: 4 producers, 4 consumers
 constexpr int kRoleWaves = 4;   // waves per role
 constexpr int kXcds = 8;        // workgroup w runs on XCD w % 8
@@ -162,7 +163,7 @@ struct BwdArgs {
   void* dV;
   float* dweights;        // [BH][n][T] or nullptr
   float* dalpha;          // [heads]
-  float geo[kMaxT];
+  float geo[kMaxTBwd];
   int H, W, n, T, heads, BH, nblk;  // nblk = ceil(n / kBwdTokens)
   float eps;
   const float* fin_s;     // [BH][64]
