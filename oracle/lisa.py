@@ -9,7 +9,10 @@ the surrounding prose, and the readings are listed here:
 
   R1  phi = ReLU, applied to Q and K of the global branch only [note §2.1].
       The local branch uses Q and K as given (the note does not say it uses
-      phi there).
+      phi there).  The alternative the note's supplementary comparison names
+      (ELU, Table 8) is read as phi(x) = ELU(x) + 1 = x + 1 (x > 0), e^x
+      (x <= 0): the shift keeps every feature positive, so S stays a
+      row-stochastic walk matrix; ELU alone could make row sums vanish.
   R2  s = sum_j phi(K_j); r_i = 1 / (phi(Q_i) . s + eps); Qt = diag(r) phi(Q);
       S = Qt phi(K)^T.  The note only says a tiny stabilising term is ignored
       when calling S row-stochastic [note §2.2]; eps sits in the row
@@ -66,9 +69,18 @@ __all__ = [
 ]
 
 
-def feature_map(x):
-    """phi(x) = ReLU(x), the default non-negative feature map [note §2.1]."""
-    return np.maximum(np.asarray(x, dtype=np.float64), 0.0)
+FEATURES = ("relu", "elu")
+
+
+def feature_map(x, feature="relu"):
+    """phi(x): ReLU(x), the default non-negative feature map [note §2.1], or
+    ELU(x) + 1 with feature="elu" (the supplementary alternative, Table 8)."""
+    x = np.asarray(x, dtype=np.float64)
+    if feature == "relu":
+        return np.maximum(x, 0.0)
+    if feature == "elu":
+        return np.where(x > 0.0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+    raise ValueError(f"feature must be one of {FEATURES}")
 
 
 def geometric_weights(beta, T):
@@ -103,21 +115,21 @@ def walk_weights(n, T, weights=None, beta=None):
     return np.broadcast_to(geometric_weights(beta, T), (n, T))
 
 
-def normaliser(Q, K, eps):
+def normaliser(Q, K, eps, feature="relu"):
     """Column sum s of phi(K) and row normaliser r of one (batch, head) slice.
 
     s = sum_j phi(K_j) and r_i = 1 / (phi(Q_i) . s + eps), so that
     Qt = diag(r) phi(Q) turns S = Qt phi(K)^T into a row-stochastic matrix up
     to the eps term [note §2.2].  Returns (phi(Q), phi(K), s, r).
     """
-    Qp = feature_map(Q)
-    Kp = feature_map(K)
+    Qp = feature_map(Q, feature)
+    Kp = feature_map(K, feature)
     s = Kp.sum(axis=0)
     r = 1.0 / (Qp @ s + eps)
     return Qp, Kp, s, r
 
 
-def stats(Q, K, V, eps):
+def stats(Q, K, V, eps, feature="relu"):
     """The d_h-space statistics of one slice: (s, K^T V, M = K^T Qt).
 
     These are the only quantities that depend on all tokens [note §2.3,
@@ -125,12 +137,12 @@ def stats(Q, K, V, eps):
     n x n matrix S.
     """
     V = np.asarray(V, dtype=np.float64)
-    Qp, Kp, s, r = normaliser(Q, K, eps)
+    Qp, Kp, s, r = normaliser(Q, K, eps, feature)
     Qt = r[:, None] * Qp
     return s, Kp.T @ V, Kp.T @ Qt
 
 
-def global_branch(Q, K, V, w, eps):
+def global_branch(Q, K, V, w, eps, feature="relu"):
     """G = sum_{k<T} diag(w[:, k]) S^k V for one slice, without forming S.
 
     Uses S^k V = Qt M^(k-1) (K^T V) for k >= 1 [note §2.3, Eq. 8]: the
@@ -142,7 +154,7 @@ def global_branch(Q, K, V, w, eps):
     V = np.asarray(V, dtype=np.float64)
     w = np.asarray(w, dtype=np.float64)
     T = w.shape[1]
-    Qp, Kp, s, r = normaliser(Q, K, eps)
+    Qp, Kp, s, r = normaliser(Q, K, eps, feature)
     Qt = r[:, None] * Qp
     M = Kp.T @ Qt
     P = Kp.T @ V  # P_1
@@ -245,13 +257,13 @@ def _check(Q, K, V, H, W, T, alpha, weights, beta):
     return Q, K, V, alpha, weights
 
 
-def lisa_forward(Q, K, V, *, H, W, T, alpha, weights=None, beta=None, eps=1e-6):
+def lisa_forward(Q, K, V, *, H, W, T, alpha, weights=None, beta=None, eps=1e-6, feature="relu"):
     """LiSA forward pass, [B, heads, n, d] float64 in and out.
 
     Per (batch, head): global branch (low-rank form), local branch, alpha-mix.
     ``weights`` are adaptive per-token weights [B, heads, n, T]; without them
     the geometric weights of ``beta`` are used.  ``alpha`` has one entry per
-    head.
+    head.  ``feature`` picks phi of the global branch ("relu" or "elu").
     """
     Q, K, V, alpha, weights = _check(Q, K, V, H, W, T, alpha, weights, beta)
     B, heads, n, _ = Q.shape
@@ -259,13 +271,13 @@ def lisa_forward(Q, K, V, *, H, W, T, alpha, weights=None, beta=None, eps=1e-6):
     for b in range(B):
         for h in range(heads):
             w = walk_weights(n, T, None if weights is None else weights[b, h], beta)
-            G = global_branch(Q[b, h], K[b, h], V[b, h], w, eps)
+            G = global_branch(Q[b, h], K[b, h], V[b, h], w, eps, feature)
             L = local_branch(Q[b, h], K[b, h], V[b, h], H, W)
             Y[b, h] = mix(G, L, alpha[h])
     return Y
 
 
-def lisa_bruteforce(Q, K, V, *, H, W, T, alpha, weights=None, beta=None, eps=1e-6):
+def lisa_bruteforce(Q, K, V, *, H, W, T, alpha, weights=None, beta=None, eps=1e-6, feature="relu"):
     """The same forward pass with every n x n matrix formed explicitly.
 
     Global: S = Qt phi(K)^T built densely [note §2.2] and its powers S^k by
@@ -287,7 +299,14 @@ def lisa_bruteforce(Q, K, V, *, H, W, T, alpha, weights=None, beta=None, eps=1e-
         for h in range(heads):
             q, k, v = Q[b, h], K[b, h], V[b, h]
             w = walk_weights(n, T, None if weights is None else weights[b, h], beta)
-            qp, kp = np.maximum(q, 0.0), np.maximum(k, 0.0)
+            if feature == "relu":
+                qp, kp = np.maximum(q, 0.0), np.maximum(k, 0.0)
+            elif feature == "elu":
+                # ELU(x) + 1, written from its definition: alpha (e^x - 1) below zero, x above.
+                qp = np.where(q > 0, q, np.expm1(np.minimum(q, 0.0))) + 1.0
+                kp = np.where(k > 0, k, np.expm1(np.minimum(k, 0.0))) + 1.0
+            else:
+                raise ValueError("unknown feature map")
             S = (qp @ kp.T) / (qp @ kp.sum(axis=0) + eps)[:, None]
             Sk = np.eye(n)
             G = np.zeros_like(v)

@@ -240,6 +240,62 @@ def test_one_hop_is_linear_attention():
     np.testing.assert_allclose(G, num / den[:, None], rtol=1e-12, atol=1e-14)
 
 
+# --------------------------------------------------------------------------
+# The ELU feature map (note §2.1: the supplementary comparison of ELU and
+# ReLU, Table 8), read as phi(x) = ELU(x) + 1.
+# --------------------------------------------------------------------------
+def test_elu_feature_is_torch_elu_plus_one():
+    import torch
+
+    x = np.concatenate([np.linspace(-30.0, 30.0, 2001), [0.0, -0.0, 1e-300, -1e-300]])
+    ref = torch.nn.functional.elu(torch.from_numpy(x), alpha=1.0).numpy() + 1.0
+    # torch forms expm1(x) + 1, which rounds tiny e^x to within one ulp of 1.
+    np.testing.assert_allclose(olisa.feature_map(x, "elu"), ref, rtol=1e-15, atol=2.3e-16)
+    assert np.all(olisa.feature_map(x, "elu") > 0)
+    with pytest.raises(ValueError):
+        olisa.feature_map(x, "gelu")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_lowrank_equals_bruteforce_elu(seed):
+    rng = np.random.default_rng(500 + seed)
+    H, W = int(rng.integers(1, 7)), int(rng.integers(1, 7))
+    T = int(rng.integers(1, 17))
+    p = _rand_problem(rng, 1, 2, H, W, 8, 5, T, adaptive=bool(seed % 2))
+    kw = dict(H=H, W=W, T=T, alpha=p["alpha"], weights=p["weights"], beta=p["beta"], eps=1e-6,
+              feature="elu")
+    a = oracle.lisa_forward(p["Q"], p["K"], p["V"], **kw)
+    b = oracle.lisa_bruteforce(p["Q"], p["K"], p["V"], **kw)
+    assert _rel(a, b) < 1e-11
+    # ELU differs from ReLU on these inputs (half of them are negative).
+    c = oracle.lisa_forward(p["Q"], p["K"], p["V"], **dict(kw, feature="relu"))
+    assert T == 1 or _rel(a, c) > 1e-3
+
+
+def test_one_hop_with_elu_is_linear_attention():
+    """One hop with phi = ELU + 1 is the linear attention of the elu(x) + 1
+    feature map, written here with torch's ELU."""
+    import torch
+
+    rng = np.random.default_rng(14)
+    n = 30
+    Q, K, V = _rand_slice(rng, n, 8, 6)
+    w = np.zeros((n, 2))
+    w[:, 1] = 1.0
+    eps = 1e-6
+    G = olisa.global_branch(Q, K, V, w, eps, "elu")
+    elu1 = lambda x: torch.nn.functional.elu(torch.from_numpy(x)).numpy() + 1.0
+    Qp, Kp = elu1(Q), elu1(K)
+    num = np.stack([Qp[i] @ sum(np.outer(Kp[j], V[j]) for j in range(n)) for i in range(n)])
+    den = np.array([Qp[i] @ Kp.sum(0) + eps for i in range(n)])
+    np.testing.assert_allclose(G, num / den[:, None], rtol=1e-12, atol=1e-14)
+    # Every feature is positive, so S is row-stochastic up to eps r_i.
+    Qp_, Kp_, s, r = olisa.normaliser(Q, K, eps, "elu")
+    S = (r[:, None] * Qp_) @ Kp_.T
+    np.testing.assert_allclose(S.sum(1), 1.0 - eps * r, rtol=0, atol=1e-13)
+    assert np.all(S > 0)
+
+
 def test_scale_invariance_of_global_branch():
     rng = np.random.default_rng(13)
     Q, K, V = _rand_slice(rng, 30, 8, 8, relu=True)
@@ -363,7 +419,7 @@ def test_hand_example_1x2():
 # Planted mistakes: each plausible slip in the oracle must fail a pin above.
 # The mistakes are planted in a monkeypatched copy, on the CPU.
 # --------------------------------------------------------------------------
-def _global_transposed_M(Q, K, V, w, eps):
+def _global_transposed_M(Q, K, V, w, eps, feature="relu"):
     Qp, Kp, s, r = olisa.normaliser(Q, K, eps)
     Qt = r[:, None] * Qp
     M = Qt.T @ Kp  # slip: Qt^T K instead of K^T Qt
@@ -375,7 +431,7 @@ def _global_transposed_M(Q, K, V, w, eps):
     return G
 
 
-def _global_no_self_term(Q, K, V, w, eps):
+def _global_no_self_term(Q, K, V, w, eps, feature="relu"):
     Qp, Kp, s, r = olisa.normaliser(Q, K, eps)
     Qt = r[:, None] * Qp
     M = Kp.T @ Qt
@@ -387,7 +443,7 @@ def _global_no_self_term(Q, K, V, w, eps):
     return G
 
 
-def _global_power_order(Q, K, V, w, eps):
+def _global_power_order(Q, K, V, w, eps, feature="relu"):
     Qp, Kp, s, r = olisa.normaliser(Q, K, eps)
     Qt = r[:, None] * Qp
     M = Kp.T @ Qt
