@@ -7,7 +7,9 @@
  * row-major grid order (token i = row * grid_w + col):
  *
  *   global branch  [note §2.1-§2.3]
- *     phi = ReLU;  s = sum_j phi(K_j);  r_i = 1 / (phi(Q_i) . s + eps)
+ *     phi = ReLU (or ELU + 1, lisa_problem.feature; the note's
+ *     supplementary comparison of the two, Table 8);
+ *     s = sum_j phi(K_j);  r_i = 1 / (phi(Q_i) . s + eps)
  *     Qt = diag(r) phi(Q);  S = Qt phi(K)^T   (row-stochastic up to eps)
  *     G  = sum_{k=0}^{T-1} diag(w_k) S^k V,  S^0 = I,
  *     computed as S^k V = Qt M^(k-1) (phi(K)^T V) with M = phi(K)^T Qt
@@ -83,6 +85,12 @@ typedef enum lisa_status {
 
 typedef enum lisa_dtype { LISA_FP32 = 0, LISA_BF16 = 1 } lisa_dtype;
 
+/* Feature map phi of the global branch: ReLU(x), or ELU(x) + 1 (x + 1 above
+ * zero, e^x at or below; positive, so S stays row-stochastic).  With bf16
+ * inputs the ELU features are rounded to bf16 before the products, as the
+ * inputs are. */
+typedef enum lisa_feature { LISA_FEATURE_RELU = 0, LISA_FEATURE_ELU = 1 } lisa_feature;
+
 /* Problem description.  n = grid_h * grid_w tokens per (batch, head). */
 typedef struct lisa_problem {
   int32_t batch;  /* B >= 1 */
@@ -95,6 +103,9 @@ typedef struct lisa_problem {
                      lisa_forward_mlp and the backward entry points */
   int32_t dtype;  /* lisa_dtype of Q, K, V, Y */
   float eps;      /* row-normaliser stabiliser, finite and > 0 */
+  int32_t feature; /* lisa_feature (0, ReLU, when zero-initialised); another
+                      value: LISA_ERR_PARAM; ELU with lisa_forward_mlp or the
+                      backward entry points: LISA_ERR_UNSUPPORTED */
 } lisa_problem;
 
 /* Bytes of device workspace the calls below need for problem *p; 0 if *p is

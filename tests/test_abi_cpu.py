@@ -37,7 +37,13 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_problem_struct_matches_header():
-    assert ctypes.sizeof(lisa.Problem) == 9 * 4
+    import re
+
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "lisa.h")).read()
+    body = hdr[hdr.index("typedef struct lisa_problem {"):hdr.index("} lisa_problem;")]
+    names = re.findall(r"^\s*(?:int32_t|float)\s+(\w+);", body, re.M)
+    assert names == [f[0] for f in lisa.Problem._fields_]
+    assert ctypes.sizeof(lisa.Problem) == 4 * len(names) == 40
 
 
 def prob(**kw):
@@ -82,7 +88,7 @@ def test_forward_argument_errors(fn):
         assert forward(prob(**bad), fn=f) == SHAPE, bad
     for bad in (dict(d_h=32), dict(d_v=128), dict(batch=300, heads=300)):
         assert forward(prob(**bad), fn=f) == UNSUP, bad
-    for bad in (dict(T=0), dict(T=17), dict(eps=0.0), dict(eps=-1e-6), dict(eps=math.nan),
+    for bad in (dict(T=0), dict(T=17), dict(feature=2), dict(feature=-1), dict(eps=0.0), dict(eps=-1e-6), dict(eps=math.nan),
                 dict(eps=math.inf)):
         assert forward(prob(**bad), fn=f) == PARAM, bad
     for beta in (1.0, -0.1, math.nan):
@@ -145,6 +151,9 @@ def test_backward_workspace_covers_the_forward():
     # The forward takes up to 16 walk terms, the backward up to 8.
     assert lisa.lisa_workspace_size(prob(T=16)) > 0
     assert lisa.lisa_workspace_size(prob(T=17)) == 0
+    # The ELU feature map: forward only.
+    assert lisa.lisa_workspace_size(prob(feature=1)) == lisa.lisa_workspace_size(prob())
+    assert lisa.lisa_backward_workspace_size(prob(feature=1)) == 0
 
 
 @pytest.fixture(params=["lisa_backward", "lisa_backward_after_forward"])
@@ -161,6 +170,7 @@ def test_backward_argument_errors(backward_entry):
     assert backward(prob(grid_w=-1)) == SHAPE
     assert backward(prob(d_h=32)) == UNSUP
     assert backward(prob(T=9)) == PARAM
+    assert backward(prob(feature=1), ws_bytes=1 << 30) == UNSUP
     assert backward(prob(), w=None, beta=1.0) == PARAM
     for name in ("q", "k", "v", "alpha", "dy", "dq", "dk", "dv", "da"):
         assert backward(prob(), **{name: None}) == NULL, name
@@ -229,6 +239,8 @@ def test_mlp_argument_errors():
     assert forward_mlp(prob(d_h=32)) == UNSUP
     assert forward_mlp(prob(T=0)) == PARAM
     assert forward_mlp(prob(T=9), ws_bytes=1 << 30) == PARAM
+    assert forward_mlp(prob(feature=1), ws_bytes=1 << 30) == UNSUP
+    assert lisa.lisa_forward_mlp_workspace_size(prob(feature=1), 64) == 0
     for hidden in (16, 48, 160):
         assert forward_mlp(prob(), hidden=hidden, ws_bytes=1 << 30) == PARAM, hidden
     for name in ("w1", "b1", "w2", "b2"):

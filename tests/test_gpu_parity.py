@@ -115,6 +115,64 @@ def test_ragged_and_edge_shapes(lisa, case):
     check(gpu_y(lisa, to_dev(x)), oracle_y(x), dtype, str(case))
 
 
+ELU = [
+    # (B, heads, H, W, T, dtype, mode): phi = ELU + 1 on Q, K with negative entries
+    (2, 2, 13, 17, 3, "bf16", "adaptive"),
+    (1, 1, 13, 17, 5, "fp32", "adaptive"),
+    (2, 1, 9, 33, 4, "fp32", "geometric"),
+    (1, 1, 1, 1, 3, "bf16", "adaptive"),
+    (4, 1, 56, 56, 3, "bf16", "adaptive"),    # PVT stage-1 grid
+    (1, 1, 70, 70, 6, "bf16", "geometric"),   # many ranks per slice, ragged chunk tails
+    (96, 3, 14, 14, 3, "bf16", "adaptive"),   # one rank per slice
+    (1, 2, 20, 23, 12, "fp32", "adaptive"),
+]
+
+
+@pytest.mark.parametrize("case", ELU, ids=[f"{c[0]}x{c[1]}_{c[2]}x{c[3]}_T{c[4]}_{c[5]}_{c[6]}" for c in ELU])
+def test_elu_feature_map(lisa, case):
+    B, heads, H, W, T, dtype, mode = case
+    w = workloads.small("elu", B, heads, H, W, T, dtype=dtype, mode=mode, beta=0.6, seed=11 + H * 17 + W)
+    x = workloads.make_inputs(w)
+    g = torch.Generator().manual_seed(1000 + H * W + T)
+    for key in ("q", "k"):
+        x[key] = torch.randn(x[key].shape, generator=g).to(x[key].dtype)
+    y_ref = oracle.lisa_forward(f64(x["q"]), f64(x["k"]), f64(x["v"]), H=H, W=W, T=T, alpha=f64(x["alpha"]),
+                                weights=f64(x["weights"]), beta=x["beta"], eps=x["eps"], feature="elu")
+    check(gpu_y(lisa, to_dev(x), feature="elu"), y_ref, dtype, f"elu {case}")
+    if T >= 2 and H * W > 1:
+        # S V alone (alpha = 1, one-hot weights on k = 1) tells the feature
+        # maps apart far beyond the ELU path's own error (with one token they
+        # coincide).
+        onehot = torch.zeros(B, heads, H * W, T)
+        onehot[..., 1] = 1.0
+        xg = dict(x, alpha=torch.ones_like(x["alpha"]), weights=onehot)
+        yg_ref = oracle.lisa_forward(f64(xg["q"]), f64(xg["k"]), f64(xg["v"]), H=H, W=W, T=T,
+                                     alpha=f64(xg["alpha"]), weights=f64(xg["weights"]), beta=xg["beta"],
+                                     eps=xg["eps"], feature="elu")
+        e_elu = check(gpu_y(lisa, to_dev(xg), feature="elu"), yg_ref, dtype, f"elu global {case}")
+        y_relu = gpu_y(lisa, to_dev(xg)).double().cpu().numpy()
+        e_relu = np.linalg.norm(y_relu - yg_ref) / np.linalg.norm(yg_ref)
+        print(f"[parity] relu vs elu oracle: {e_relu:.3e} (elu path {e_elu:.3e})", flush=True)
+        assert e_relu > 5 * max(e_elu, 1e-6)
+
+
+def test_elu_statistics_stage(lisa):
+    """lisa_reduce with phi = ELU + 1: s, phi(K)^T V and M against the oracle."""
+    w = workloads.small("elu_stats", 2, 1, 33, 29, 3, dtype="fp32", seed=5)
+    x = workloads.make_inputs(w)
+    g = torch.Generator().manual_seed(77)
+    for key in ("q", "k"):
+        x[key] = torch.randn(x[key].shape, generator=g)
+    d = to_dev(x)
+    s, kv, m = lisa.lisa_reduce(d["q"], d["k"], d["v"], grid=(w.H, w.W), eps=w.eps, T=3, feature="elu")
+    torch.cuda.synchronize()
+    for b in range(2):
+        rs, rkv, rm = olisa.stats(f64(x["q"])[b, 0], f64(x["k"])[b, 0], f64(x["v"])[b, 0], w.eps, "elu")
+        for got, ref in ((s[b, 0], rs), (kv[b, 0], rkv), (m[b, 0], rm)):
+            got = got.double().cpu().numpy()
+            assert np.linalg.norm(got - ref) <= 1e-5 * np.linalg.norm(ref)
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_each_walk_term_alone(lisa, dtype):
     """One-hot weights e_k isolate S^k V; alpha = 1 isolates the global branch."""

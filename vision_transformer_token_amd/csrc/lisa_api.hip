@@ -55,7 +55,7 @@ constexpr size_t kMaxSlices = 65535;  // batch * heads limit
 size_t up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Plan {
-  int BH = 0, n = 0, H = 0, W = 0, T = 0, dtype = 0, heads = 0;
+  int BH = 0, n = 0, H = 0, W = 0, T = 0, dtype = 0, heads = 0, feature = 0;
   size_t esize = 0;
   int gmax = 1;                                  // ranks per slice the partials are sized for
   int grid = 0;                                  // workgroups (one per compute unit)
@@ -81,6 +81,7 @@ lisa_status check_problem(const lisa_problem* p) {
   if ((int64_t)p->batch * p->heads > (int64_t)kMaxSlices) return LISA_ERR_UNSUPPORTED;
   if (p->T < 1 || p->T > lisa::kMaxT) return LISA_ERR_PARAM;
   if (!std::isfinite(p->eps) || !(p->eps > 0.f)) return LISA_ERR_PARAM;
+  if (p->feature != LISA_FEATURE_RELU && p->feature != LISA_FEATURE_ELU) return LISA_ERR_PARAM;
   return LISA_OK;
 }
 
@@ -150,6 +151,7 @@ lisa_status make_plan(const lisa_problem* p, Plan& pl) {
   pl.n = p->grid_h * p->grid_w;
   pl.T = p->T;
   pl.dtype = p->dtype;
+  pl.feature = p->feature;
   pl.esize = p->dtype == LISA_BF16 ? 2 : 4;
   // The partials are sized for the most ranks any grid can give a slice
   // (the launch picks G <= gmax from the device's compute units).
@@ -308,8 +310,10 @@ lisa_status run(Plan pl, Mode mode, const void* Q, const void* K, const void* V,
   // kSubRanks ranks from 64 ranks per slice on (with 32 the one counter
   // measured faster); with one rank per slice, a combine that writes the
   // statistics in whole rows and fragment lanes.
+  // The ELU feature map has kernels of its own (plain arrivals and combine).
   const bool variants = pl.dtype == LISA_BF16 && !mlp;
-  a.variant = (variants && pl.G >= 64 && pl.BH <= lisa::kMaxSubSlices) ? lisa::kVarGrouped
+  a.variant = pl.feature == LISA_FEATURE_ELU                             ? lisa::kVarElu
+              : (variants && pl.G >= 64 && pl.BH <= lisa::kMaxSubSlices) ? lisa::kVarGrouped
               : (variants && pl.G == 1)                                 ? lisa::kVarSolo
                                                                         : lisa::kVarPlain;
   a.done_cnt = reinterpret_cast<unsigned*>(ws + pl.done_cnt);
@@ -379,7 +383,8 @@ lisa_status lisa_apply(const lisa_problem* p, const void* Q, const void* K, cons
 
 size_t lisa_forward_mlp_workspace_size(const lisa_problem* p, int32_t hidden) {
   Plan pl;
-  if (make_plan(p, pl) != LISA_OK || pl.T > lisa::kMaxTBwd || hidden < 32 || hidden > lisa::kMaxHidden ||
+  if (make_plan(p, pl) != LISA_OK || pl.T > lisa::kMaxTBwd || pl.feature != LISA_FEATURE_RELU || hidden < 32 ||
+      hidden > lisa::kMaxHidden ||
       hidden % 32 != 0)
     return 0;
   return up(pl.total, kAlign) + lisa::mlp_frag_bytes(pl.dtype, pl.heads, hidden);
@@ -393,6 +398,7 @@ lisa_status lisa_forward_mlp(const lisa_problem* p, const void* Q, const void* K
   lisa_status st = make_plan(p, pl);
   if (st != LISA_OK) return st;
   if (pl.T > lisa::kMaxTBwd) return LISA_ERR_PARAM;
+  if (pl.feature != LISA_FEATURE_RELU) return LISA_ERR_UNSUPPORTED;
   if (mlp->hidden < 32 || mlp->hidden > lisa::kMaxHidden || mlp->hidden % 32 != 0) return LISA_ERR_PARAM;
   if (!mlp->w1 || !mlp->b1 || !mlp->w2 || !mlp->b2) return LISA_ERR_NULL;
   if (misaligned(mlp->w1, 4) || misaligned(mlp->b1, 4) || misaligned(mlp->w2, 4) || misaligned(mlp->b2, 4))
@@ -469,7 +475,7 @@ lisa_status lisa_attention_forward(const lisa_problem* p, const void* X, const v
 
 size_t lisa_backward_workspace_size(const lisa_problem* p) {
   Plan pl;
-  return make_plan(p, pl) == LISA_OK && pl.T <= lisa::kMaxTBwd ? pl.btotal : 0;
+  return make_plan(p, pl) == LISA_OK && pl.T <= lisa::kMaxTBwd && pl.feature == LISA_FEATURE_RELU ? pl.btotal : 0;
 }
 
 // The backward pass; with have_stats the slice statistics of a preceding
@@ -484,6 +490,7 @@ static lisa_status backward_common(const lisa_problem* p, const void* Q, const v
   lisa_status st = make_plan(p, pl);
   if (st != LISA_OK) return st;
   if (pl.T > lisa::kMaxTBwd) return LISA_ERR_PARAM;
+  if (pl.feature != LISA_FEATURE_RELU) return LISA_ERR_UNSUPPORTED;
   if (!weights && !(beta >= 0.f && beta < 1.f)) return LISA_ERR_PARAM;
   if (!Q || !K || !V || !alpha || !dY || !dQ || !dK || !dV || !dalpha) return LISA_ERR_NULL;
   if (misaligned(Q, 16) || misaligned(K, 16) || misaligned(V, 16) || misaligned(dY, 16) ||

@@ -224,6 +224,20 @@ __device__ __forceinline__ v4s tr_read(const unsigned char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p);
 }
 __device__ __forceinline__ v4s relu4(v4s x) { return __builtin_elementwise_max(x, (v4s)0); }
+// The other feature map, phi(x) = ELU(x) + 1: x + 1 above zero, e^x at or
+// below it (0 at -inf, which therefore pads rows that must add nothing).
+__device__ __forceinline__ float elu1(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+template <bool kElu>
+__device__ __forceinline__ float feat(float x) { return kElu ? elu1(x) : fmaxf(x, 0.f); }
+// elu1 of four bf16 values given as bits, rounded back to bf16 (to nearest even).
+__device__ __forceinline__ v4s elu1_bits(v4s x) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 w = __builtin_bit_cast(u32x2, x);
+  u32x2 o;
+  o[0] = pack_bf16x2(elu1(__uint_as_float(w[0] << 16)), elu1(__uint_as_float(w[0] & 0xffff0000u)));
+  o[1] = pack_bf16x2(elu1(__uint_as_float(w[1] << 16)), elu1(__uint_as_float(w[1] & 0xffff0000u)));
+  return __builtin_bit_cast(v4s, o);
+}
 __device__ __forceinline__ v8s join(v4s lo, v4s hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
@@ -236,6 +250,7 @@ __device__ __forceinline__ bf16x8 as_bf16(v8s x) { return __builtin_bit_cast(bf1
 // takes 8..11 from the upper half, which takes 4..7 in exchange: the upper
 // half of dwords 0, 1 trades places with the lower half of dwords 2, 3.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+template <bool kElu = false>
 __device__ __forceinline__ v8s relu_to_slots(v8s x) {
   u32x4 w = __builtin_bit_cast(u32x4, x);
   const auto p = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
@@ -244,6 +259,11 @@ __device__ __forceinline__ v8s relu_to_slots(v8s x) {
   w[2] = p[1];
   w[1] = q[0];
   w[3] = q[1];
+  if constexpr (kElu) {
+    const v8s y = __builtin_bit_cast(v8s, w);
+    return join(elu1_bits(__builtin_shufflevector(y, y, 0, 1, 2, 3)),
+                elu1_bits(__builtin_shufflevector(y, y, 4, 5, 6, 7)));
+  }
   return __builtin_elementwise_max(__builtin_bit_cast(v8s, w), (v8s)0);
 }
 
@@ -264,15 +284,19 @@ __device__ __forceinline__ void apply_bits(const bf16x8 (&fr)[2][4], const v8s (
 }
 
 // Bits of X[row0 + 8h + e][col0 + m] (bf16 rows of a staged region), e = 0..7;
-// with kRelu the values are clamped at zero (a negative bf16 is a negative int16).
-template <bool kRelu>
+// with kRelu the values are clamped at zero (a negative bf16 is a negative int16),
+// with kElu as well they go through elu1 instead.
+template <bool kRelu, bool kElu = false>
 __device__ __forceinline__ v8s rows_bits(const unsigned char* base, int row0, int col0) {
   const int L = threadIdx.x & 63, i = L & 15, g = L >> 4;
   const int col = col0 + 16 * (g & 1) + 4 * (i & 3);
   const int r = row0 + 8 * (g >> 1) + (i >> 2);
   v4s lo = tr_read(base + row_off<BF16>(r, col));
   v4s hi = tr_read(base + row_off<BF16>(r + 4, col));
-  if (kRelu) {
+  if constexpr (kRelu && kElu) {
+    lo = elu1_bits(lo);
+    hi = elu1_bits(hi);
+  } else if (kRelu) {
     lo = relu4(lo);
     hi = relu4(hi);
   }

@@ -268,7 +268,7 @@ __device__ void stage_tile(const FlowArgs& a, int b, int t, unsigned char* buf, 
 // a negative int16), and dot = their product with s over the row
 // (s[8 g .. 8 g + 7] held in registers); runs go four at a time, all their
 // LDS reads issued before the first product.  `nrun` is wave-uniform.
-template <class F>
+template <bool kElu = false, class F>
 __device__ __forceinline__ void bf16_row_dots(const unsigned char* base, int nrun, const float* s, int pw, F f) {
   const int lane = threadIdx.x & 63;
   const int slot = lane & 7, sub = lane >> 3;
@@ -285,13 +285,15 @@ __device__ __forceinline__ void bf16_row_dots(const unsigned char* base, int nru
     for (int u = 0; u < 4; ++u) {
       const int j = j0 + 4 * u;
       if (j < nrun) {
-        const v8s bits = __builtin_elementwise_max(__builtin_bit_cast(v8s, raw[u]), (v8s)0);
+        const v8s bits = kElu ? __builtin_bit_cast(v8s, raw[u])
+                              : __builtin_elementwise_max(__builtin_bit_cast(v8s, raw[u]), (v8s)0);
         const u32x4 w = __builtin_bit_cast(u32x4, bits);
         float x[8];
         float dot = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           x[e] = __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
+          if (kElu) x[e] = elu1(x[e]);
           dot += x[e] * sv[e];
         }
         f(j, 8 * j + sub, x, group_sum8(dot));
@@ -305,16 +307,18 @@ __device__ __forceinline__ void bf16_row_dots(const unsigned char* base, int nru
 // r_j phi(Q_j) with r_j = 1 / (phi(Q_j) . s + eps).  A wave only touches the
 // 1 KB runs it issued itself (run j belongs to wave j % 4): each lane holds
 // one 16-byte piece, and the lanes of a row reduce the dot product together.
-template <class Tr, bool kIsM>
+template <class Tr, bool kIsM, bool kElu = false>
 __device__ void finish_chunk(const FlowArgs& a, int nv, unsigned char* buf, const float* s, int pw) {
   constexpr int RPR = 1024 / Tr::RB;  // rows per run
+  // K rows past the chunk: phi of the pad is 0 (ReLU of 0, ELU + 1 of -inf).
+  constexpr unsigned kPad = !kElu ? 0u : Tr::EPP == 8 ? 0xff80ff80u : 0xff800000u;
   const int lane = threadIdx.x & 63;
   const int nvr = (nv + 15) & ~15;
   unsigned char* bK = buf;
   unsigned char* bX = buf + LdsOf<Tr>::kXOff;
   const int slot = lane % Tr::PPR;
   if constexpr (kIsM && Tr::EPP == 8) {
-    bf16_row_dots(bX, nvr / RPR, s, pw, [&](int, int r, float (&x)[8], float dot) {
+    bf16_row_dots<kElu>(bX, nvr / RPR, s, pw, [&](int, int r, float (&x)[8], float dot) {
       uint4* pK = reinterpret_cast<uint4*>(bK + r * Tr::RB + slot * 16);
       uint4* pX = reinterpret_cast<uint4*>(bX + r * Tr::RB + slot * 16);
       if (r < nv) {
@@ -324,7 +328,7 @@ __device__ void finish_chunk(const FlowArgs& a, int nv, unsigned char* buf, cons
         for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(x[2 * e] * rr, x[2 * e + 1] * rr);
         *reinterpret_cast<u32x4*>(pX) = o;
       } else {
-        *pK = make_uint4(0, 0, 0, 0);
+        *pK = make_uint4(kPad, kPad, kPad, kPad);
         *pX = make_uint4(0, 0, 0, 0);
       }
     });
@@ -348,7 +352,7 @@ __device__ void finish_chunk(const FlowArgs& a, int nv, unsigned char* buf, cons
       float dot = 0.f;
 #pragma unroll
       for (int e = 0; e < Tr::EPP; ++e) {
-        x[e] = fmaxf(x[e], 0.f);
+        x[e] = feat<kElu>(x[e]);
         dot += x[e] * s[g * Tr::EPP + e];
       }
       dot = Tr::PPR == 8 ? group_sum8(dot) : group_sum16(dot);
@@ -365,7 +369,7 @@ __device__ void finish_chunk(const FlowArgs& a, int nv, unsigned char* buf, cons
       }
     }
     if (r >= nv) {
-      *pK = make_uint4(0, 0, 0, 0);
+      *pK = make_uint4(kPad, kPad, kPad, kPad);
       *pX = make_uint4(0, 0, 0, 0);
     }
   }
@@ -375,7 +379,7 @@ __device__ void finish_chunk(const FlowArgs& a, int nv, unsigned char* buf, cons
 // . s + eps) for the Q rows of the 1 KB runs it issued (run j belongs to
 // wave j % 4), written to the tile's r region.  The lanes of a row each take
 // one 16-byte piece and reduce the dot product together.
-template <class Tr>
+template <class Tr, bool kElu = false>
 __device__ void finish_tile(const FlowArgs& a, const TileLayout& L, unsigned char* buf, const float* s, int pw) {
   constexpr int RPR = 1024 / Tr::RB;  // rows per run
   const int lane = threadIdx.x & 63;
@@ -383,7 +387,7 @@ __device__ void finish_tile(const FlowArgs& a, const TileLayout& L, unsigned cha
   const unsigned char* bQ = buf + L.q;
   float* rr = reinterpret_cast<float*>(buf + L.r);
   if constexpr (Tr::EPP == 8) {
-    bf16_row_dots(bQ, L.tokens / RPR, s, pw, [&](int, int r, float (&)[8], float dot) {
+    bf16_row_dots<kElu>(bQ, L.tokens / RPR, s, pw, [&](int, int r, float (&)[8], float dot) {
       if (slot == 0) rr[r] = __builtin_amdgcn_rcpf(dot + a.eps);
     });
     return;
@@ -402,7 +406,7 @@ __device__ void finish_tile(const FlowArgs& a, const TileLayout& L, unsigned cha
     }
     float dot = 0.f;
 #pragma unroll
-    for (int e = 0; e < Tr::EPP; ++e) dot += fmaxf(x[e], 0.f) * s[g * Tr::EPP + e];
+    for (int e = 0; e < Tr::EPP; ++e) dot += feat<kElu>(x[e]) * s[g * Tr::EPP + e];
     dot = Tr::PPR == 8 ? group_sum8(dot) : group_sum16(dot);
     if (slot == 0) rr[r] = 1.f / (dot + a.eps);
   }
@@ -635,9 +639,9 @@ __device__ void prepare(const FlowArgs& a, const Rank& rk, Pos p, unsigned char*
     }
     wait_all();
     if (is_m)
-      finish_chunk<Tr, true>(a, nv, buf, s_w, pw);
+      finish_chunk<Tr, true, kVar == kVarElu>(a, nv, buf, s_w, pw);
     else
-      finish_chunk<Tr, false>(a, nv, buf, s_w, pw);
+      finish_chunk<Tr, false, kVar == kVarElu>(a, nv, buf, s_w, pw);
   } else if (p.ph == kPC) {
     dependency(a.do_m ? kCntM : kCntKV);
     if (!a.do_m && rk.g == 0 && pw == 0) put(a.fin_s + (size_t)b * kD + lane, sum_s_partials(a, b));
@@ -678,7 +682,7 @@ __device__ void prepare(const FlowArgs& a, const Rank& rk, Pos p, unsigned char*
       producers_meet(mlp_ready);
       predict_tile<Tr>(a, b, rk.t0 + p.j, buf, pw, pr);
     }
-    if (a.T >= 2) finish_tile<Tr>(a, layout_of<Tr>(a), buf, s_w, pw);
+    if (a.T >= 2) finish_tile<Tr, kVar == kVarElu>(a, layout_of<Tr>(a), buf, s_w, pw);
     if (p.j == 0 && s_known) {
       dependency(kCntC);
       load_stats();
@@ -698,7 +702,7 @@ __device__ __forceinline__ float lds_elem(const unsigned char* base, int r, int 
 // One chunk of a KV / M sweep, accumulated into acc (and acc_s: s, KV only).
 // Wave cw owns block (cw / 2, cw % 2) of the 64x64 result; A = phi(K) rows,
 // B = V rows (KV) or the rescaled Q rows (M); rows past the chunk are zero.
-template <class Tr, bool kIsM>
+template <class Tr, bool kIsM, bool kElu = false>
 __device__ __forceinline__ void sweep_chunk(const unsigned char* buf, int nv, int cw, f32x16& acc, f32x16& acc_s) {
   const int lane = threadIdx.x & 63;
   const int m = lane & 31, h = lane >> 5, mb = cw >> 1, nb = cw & 1;
@@ -715,7 +719,7 @@ __device__ __forceinline__ void sweep_chunk(const unsigned char* buf, int nv, in
       v8s A[U], B[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        A[u] = rows_bits<true>(bK, kk + 16 * u, 32 * mb);
+        A[u] = rows_bits<true, kElu>(bK, kk + 16 * u, 32 * mb);
         B[u] = rows_bits<false>(bX, kk + 16 * u, 32 * nb);
       }
 #pragma unroll
@@ -746,7 +750,7 @@ __device__ __forceinline__ void sweep_chunk(const unsigned char* buf, int nv, in
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int r = kk + 8 * h + q;
-        const float A = fmaxf(lds_elem(bK, r, 32 * mb + m, Tr{}), 0.f);
+        const float A = feat<kElu>(lds_elem(bK, r, 32 * mb + m, Tr{}));
         const float B = lds_elem(bX, r, 32 * nb + m, Tr{});
         acc = mma(A, B, acc);
         if (!kIsM && nb == 0) acc_s = mma(A, 1.f, acc_s);
@@ -767,7 +771,7 @@ __device__ int consume_sweep(const FlowArgs& a, const Rank& rk, int b, unsigned 
   for (int j = 0; j < rk.nch; ++j) {
     int tok0, nv;
     chunk_of(a, rk, j, tok0, nv);
-    sweep_chunk<Tr, kIsM>(smem + bsel * L::kStage, nv, cw, acc, acc_s);
+    sweep_chunk<Tr, kIsM, kVar == kVarElu>(smem + bsel * L::kStage, nv, cw, acc, acc_s);
     if (j + 1 < rk.nch) {
       lds_barrier();
       bsel ^= 1;
@@ -1078,7 +1082,7 @@ __device__ __forceinline__ void local_token_valu(const FlowArgs& a, const unsign
 // pair), r_i from the tile's r region and `geo` holds the geometric walk
 // weights, all in LDS.
 // ---------------------------------------------------------------------------
-template <class Tr, bool kMlp>
+template <class Tr, bool kMlp, bool kElu = false>
 __device__ __forceinline__ void out_tile(const FlowArgs& a, int b, int t, const unsigned char* buf,
                                          const typename Tr::Frag (&fkv)[2][Tr::NQ],
                                          const typename Tr::Frag (&fm)[2][Tr::NQ], const float* geo,
@@ -1126,14 +1130,14 @@ __device__ __forceinline__ void out_tile(const FlowArgs& a, int b, int t, const 
       for (int kb = 0; kb < 4; ++kb) qB[kb] = *reinterpret_cast<const bf16x8*>(cQ + row_off<BF16>(slot, 16 * kb + 8 * h));
       local_block_mfma(a, cK, cV, CW, r0, c0, br, bc, nbr, qB, 1.f - alpha, acc);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) u1[kb] = relu_to_slots(__builtin_bit_cast(v8s, qB[kb]));
+      for (int kb = 0; kb < 4; ++kb) u1[kb] = relu_to_slots<kElu>(__builtin_bit_cast(v8s, qB[kb]));
     } else {
       float q[32];
 #pragma unroll
       for (int c = 0; c < 8; ++c) load4(reinterpret_cast<const S*>(cQ + row_off<Tr>(slot, dimof(4 * c, h))), &q[4 * c]);
       local_token_valu<Tr>(a, cK, cV, CW, ccell, row, col, q, 1.f - alpha, acc);
 #pragma unroll
-      for (int v = 0; v < 32; ++v) u1[v] = fmaxf(q[v], 0.f);
+      for (int v = 0; v < 32; ++v) u1[v] = feat<kElu>(q[v]);
     }
 
     // + alpha w_0(i) V_i: the k = 0 term of the walk.
@@ -1193,7 +1197,7 @@ __device__ __forceinline__ void out_tile(const FlowArgs& a, int b, int t, const 
 // The OUT phase of slice b: take the slice statistics out of the statistics
 // area (fragments into registers), free the area (barrier),
 // then compute the rank's tiles, one stage each.  Returns the buffer index.
-template <class Tr, bool kMlp>
+template <class Tr, bool kMlp, bool kElu = false>
 __device__ int consume_out(const FlowArgs& a, const Rank& rk, int b, unsigned char* smem, int bsel,
                            const float* geo, int cw) {
   using Frag = typename Tr::Frag;
@@ -1214,7 +1218,7 @@ __device__ int consume_out(const FlowArgs& a, const Rank& rk, int b, unsigned ch
   const unsigned nbr = neighbour_slots(tok >> 3, tok & 7, lane >> 5);
   lds_barrier();  // the statistics area may now be refilled
   for (int k = 0; k < rk.nt; ++k) {
-    out_tile<Tr, kMlp>(a, b, rk.t0 + k, smem + bsel * L::kStage, fkv, fm, geo, alpha, nbr, cw);
+    out_tile<Tr, kMlp, kElu>(a, b, rk.t0 + k, smem + bsel * L::kStage, fkv, fm, geo, alpha, nbr, cw);
     lds_barrier();
     bsel ^= 1;
   }
@@ -1283,7 +1287,7 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
           }
         if (phase_len(a, rk, kPOut) > 0)
           for (int z = 0; z < nz; ++z)
-            bsel = consume_out<Tr, kMlp>(a, rk, slice_of(a, rk, r, z), smem, bsel, geo_sh, rw);
+            bsel = consume_out<Tr, kMlp, kVar == kVarElu>(a, rk, slice_of(a, rk, r, z), smem, bsel, geo_sh, rw);
       }
     }
   }
@@ -1351,10 +1355,13 @@ __global__ __launch_bounds__(256) void mlp_prep(const float* w1, float* out, int
 }  // namespace
 
 hipError_t launch_flow(int dtype, const FlowArgs& a, int grid, hipStream_t s) {
-  // The bf16 kernel's variants for many ranks per slice and for one, each a
-  // kernel of its own, so that the others compile exactly as without them.
+  // The bf16 kernel's variants for many ranks per slice and for one, and the
+  // ELU feature map's kernels, each a kernel of its own, so that the others
+  // compile exactly as without them.
   if (a.variant == kVarGrouped) return launch_typed<BF16, false, kVarGrouped>(a, grid, s);
   if (a.variant == kVarSolo) return launch_typed<BF16, false, kVarSolo>(a, grid, s);
+  if (a.variant == kVarElu)
+    return dtype == 1 ? launch_typed<BF16, false, kVarElu>(a, grid, s) : launch_typed<F32, false, kVarElu>(a, grid, s);
   if (a.mlp_w1f) return dtype == 1 ? launch_typed<BF16, true>(a, grid, s) : launch_typed<F32, true>(a, grid, s);
   return dtype == 1 ? launch_typed<BF16, false>(a, grid, s) : launch_typed<F32, false>(a, grid, s);
 }

@@ -24,8 +24,10 @@ constexpr int kCntStride = 32;  // words between slices: each slice's counters o
 constexpr int kSubRanks = 16;
 constexpr int kMaxSubSlices = 8;
 constexpr int kMaxSubs = 256 / kSubRanks;
-// Kernel variants (bf16 without the predictor; FlowArgs::variant).
-constexpr int kVarPlain = 0, kVarGrouped = 1, kVarSolo = 2;
+// Kernel variants (without the predictor; FlowArgs::variant): arrivals per
+// group and the one-rank combine (bf16), the ELU feature map (both dtypes,
+// plain arrivals and combine).
+constexpr int kVarPlain = 0, kVarGrouped = 1, kVarSolo = 2, kVarElu = 3;
 
 // LDS of one workgroup, per element size ES: two staging buffers of kStage
 // bytes that the DMA of the next stage and the compute of the current one
@@ -106,7 +108,8 @@ struct FlowArgs {
   unsigned* slice_cnt;    // [BH][kCntStride], words 0..kCntWords-1 used
   unsigned* sub_cnt;      // [kMaxSubSlices][3][kMaxSubs][kCntStride], word 0 of each line used
   int variant;            // kVarPlain, kVarGrouped (arrivals per group of kSubRanks ranks, sub_cnt),
-                          // kVarSolo (one rank per slice: the combine writes the statistics directly)
+                          // kVarSolo (one rank per slice: the combine writes the statistics directly),
+                          // kVarElu (phi = ELU + 1 instead of ReLU)
   unsigned* done_cnt;     // finished workgroups
   unsigned* tickets;      // [kXcds] rank tickets
   unsigned* err;          // error word (a dependency wait timed out)

@@ -70,7 +70,12 @@ class Problem(ctypes.Structure):
         ("T", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("eps", ctypes.c_float),
+        ("feature", ctypes.c_int32),
     ]
+
+
+# lisa_feature: phi of the global branch.
+FEATURES = {"relu": 0, "elu": 1}
 
 
 class WeightMlp(ctypes.Structure):
@@ -135,11 +140,12 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
 
 
-def make_problem(q, v, *, grid, T, eps=1e-6):
-    """Problem for q [B, heads, n, d_h] and v [B, heads, n, d_v] on an H x W grid."""
+def make_problem(q, v, *, grid, T, eps=1e-6, feature="relu"):
+    """Problem for q [B, heads, n, d_h] and v [B, heads, n, d_v] on an H x W
+    grid; ``feature`` is phi of the global branch, "relu" or "elu" (ELU + 1)."""
     H, W = grid
     B, heads, n, d_h = q.shape
-    return Problem(B, heads, H, W, d_h, v.shape[-1], T, _dtype_code(q), eps)
+    return Problem(B, heads, H, W, d_h, v.shape[-1], T, _dtype_code(q), eps, FEATURES[feature])
 
 
 def lisa_workspace_size(problem):
@@ -175,7 +181,7 @@ def _check_tensors(**ts):
 
 
 def _call_forward(fn, where, q, k, v, *, grid, T, alpha, weights=None, beta=None, eps=1e-6,
-                  out=None, workspace=None, stream=None):
+                  out=None, workspace=None, stream=None, feature="relu"):
     _check_tensors(q=q, k=k, v=v, alpha=alpha, weights=weights, out=out, workspace=workspace)
     if weights is not None and weights.dtype != torch.float32:
         raise TypeError("weights must be float32")
@@ -183,7 +189,7 @@ def _call_forward(fn, where, q, k, v, *, grid, T, alpha, weights=None, beta=None
         raise TypeError("alpha must be float32")
     if weights is None and beta is None:
         raise ValueError("give adaptive weights or beta")
-    prob = make_problem(q, v, grid=grid, T=T, eps=eps)
+    prob = make_problem(q, v, grid=grid, T=T, eps=eps, feature=feature)
     if out is None:
         out = torch.empty_like(v)
     if workspace is None:
@@ -199,7 +205,7 @@ def _call_forward(fn, where, q, k, v, *, grid, T, alpha, weights=None, beta=None
 
 
 def lisa_forward(q, k, v, *, grid, T, alpha, weights=None, beta=None, eps=1e-6, out=None,
-                 workspace=None, stream=None):
+                 workspace=None, stream=None, feature="relu"):
     """Y = LiSA(q, k, v) on the GPU; see include/lisa.h.
 
     q, k: [B, heads, n, 64], v: [B, heads, n, 64], bf16 or fp32, contiguous
@@ -209,7 +215,7 @@ def lisa_forward(q, k, v, *, grid, T, alpha, weights=None, beta=None, eps=1e-6, 
     """
     return _call_forward(_lib.lisa_forward, "lisa_forward", q, k, v, grid=grid, T=T, alpha=alpha,
                          weights=weights, beta=beta, eps=eps, out=out, workspace=workspace,
-                         stream=stream)
+                         stream=stream, feature=feature)
 
 
 def lisa_forward_mlp_workspace_size(problem, hidden):
@@ -248,7 +254,7 @@ def lisa_attention_workspace_size(problem):
 
 
 def lisa_attention_forward(x, w_qkv, b_qkv, w_o, b_o, *, heads, grid, T, alpha, weights=None, beta=None,
-                           eps=1e-6, out=None, workspace=None, stream=None):
+                           eps=1e-6, out=None, workspace=None, stream=None, feature="relu"):
     """The LiSA attention layer: x [B, n, C] (bf16 or fp32, C = 64 heads),
     w_qkv [3C, C] and w_o [C, C] in x's dtype, b_qkv [3C] and b_o [C] fp32;
     see include/lisa.h."""
@@ -259,7 +265,7 @@ def lisa_attention_forward(x, w_qkv, b_qkv, w_o, b_o, *, heads, grid, T, alpha, 
     B, n, C = x.shape
     if C != 64 * heads:
         raise ValueError("x's channels must be 64 * heads")
-    prob = Problem(B, heads, grid[0], grid[1], 64, 64, T, _dtype_code(x), eps)
+    prob = Problem(B, heads, grid[0], grid[1], 64, 64, T, _dtype_code(x), eps, FEATURES[feature])
     if workspace is None:
         nbytes = lisa_attention_workspace_size(prob)
         if nbytes == 0:
@@ -277,17 +283,17 @@ def lisa_attention_forward(x, w_qkv, b_qkv, w_o, b_o, *, heads, grid, T, alpha, 
 
 
 def lisa_apply(q, k, v, *, grid, T, alpha, workspace, weights=None, beta=None, eps=1e-6, out=None,
-               stream=None):
+               stream=None, feature="relu"):
     """Output stage alone, from the statistics a previous lisa_reduce left in ``workspace``."""
     return _call_forward(_lib.lisa_apply, "lisa_apply", q, k, v, grid=grid, T=T, alpha=alpha,
                          weights=weights, beta=beta, eps=eps, out=out, workspace=workspace,
-                         stream=stream)
+                         stream=stream, feature=feature)
 
 
-def lisa_reduce(q, k, v, *, grid, eps=1e-6, T=3, workspace=None, outputs=True, stream=None):
+def lisa_reduce(q, k, v, *, grid, eps=1e-6, T=3, workspace=None, outputs=True, stream=None, feature="relu"):
     """Statistics stage: returns (s, phi(K)^T V, M) as fp32 tensors, or None if not ``outputs``."""
     _check_tensors(q=q, k=k, v=v, workspace=workspace)
-    prob = make_problem(q, v, grid=grid, T=T, eps=eps)
+    prob = make_problem(q, v, grid=grid, T=T, eps=eps, feature=feature)
     if workspace is None:
         workspace = new_workspace(prob, q.device)
     B, heads = q.shape[:2]
