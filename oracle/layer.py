@@ -42,11 +42,13 @@ def merge_heads(t):
     return t.transpose(0, 2, 1, 3).reshape(B, n, heads * d)
 
 
-def lisa_layer(X, Wqkv, bqkv, Wo, bo, *, heads, H, W, T, alpha, weights=None, beta=None, eps=1e-6):
-    """Y [B, n, C] of the LiSA attention layer (A1-A4), float64."""
+def lisa_layer(X, Wqkv, bqkv, Wo, bo, *, heads, H, W, T, alpha, weights=None, beta=None, eps=1e-6,
+               feature="relu"):
+    """Y [B, n, C] of the LiSA attention layer (A1-A4), float64; ``feature``
+    is phi of the operator's global branch."""
     X = np.asarray(X, dtype=np.float64)
     C = X.shape[-1]
     qkv = X @ np.asarray(Wqkv, np.float64).T + np.asarray(bqkv, np.float64)
     q, k, v = (split_heads(qkv[..., i * C:(i + 1) * C], heads) for i in range(3))
-    y = lisa_forward(q, k, v, H=H, W=W, T=T, alpha=alpha, weights=weights, beta=beta, eps=eps)
+    y = lisa_forward(q, k, v, H=H, W=W, T=T, alpha=alpha, weights=weights, beta=beta, eps=eps, feature=feature)
     return merge_heads(y) @ np.asarray(Wo, np.float64).T + np.asarray(bo, np.float64)

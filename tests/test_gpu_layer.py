@@ -39,14 +39,15 @@ def f64(t):
     return None if t is None else t.double().cpu().numpy()
 
 
-def run(lisa, w, x, prm):
+def run(lisa, w, x, prm, feature="relu"):
     d = {k: v.cuda() for k, v in prm.items()}
     y = lisa.lisa_attention_forward(d["x"], d["w_qkv"], d["b_qkv"], d["w_o"], d["b_o"], heads=w.heads,
                                     grid=(w.H, w.W), T=w.T, alpha=x["alpha"].cuda(),
                                     weights=None if x["weights"] is None else x["weights"].cuda(),
-                                    beta=x["beta"], eps=w.eps)
+                                    beta=x["beta"], eps=w.eps, feature=feature)
     torch.cuda.synchronize()
-    kw = dict(H=w.H, W=w.W, T=w.T, alpha=f64(x["alpha"]), weights=f64(x["weights"]), beta=x["beta"], eps=w.eps)
+    kw = dict(H=w.H, W=w.W, T=w.T, alpha=f64(x["alpha"]), weights=f64(x["weights"]), beta=x["beta"], eps=w.eps,
+              feature=feature)
     ref = oracle.lisa_layer(f64(prm["x"]), f64(prm["w_qkv"]), f64(prm["b_qkv"]), f64(prm["w_o"]), f64(prm["b_o"]),
                             heads=w.heads, **kw)
     if w.dtype == "fp32":
@@ -92,6 +93,20 @@ def test_layer_small(lisa, case):
     x = workloads.make_inputs(w)
     y, ref, unrounded = run(lisa, w, x, workloads.layer_params(w))
     check(y, ref, unrounded, dtype, w.describe())
+
+
+@pytest.mark.parametrize("case", [("elu-fp32", 2, 2, 10, 13, 3, "fp32", "adaptive"),
+                                  ("elu-bf16", 2, 3, 13, 21, 4, "bf16", "geometric")], ids=lambda c: c[0])
+def test_layer_elu(lisa, case):
+    """The layer with phi = ELU + 1 (its projected Q, K are signed)."""
+    name, B, heads, H, W, T, dtype, mode = case
+    w = workloads.small(name, B, heads, H, W, T, dtype=dtype, mode=mode, seed=zlib.crc32(name.encode()) % 1000)
+    x = workloads.make_inputs(w)
+    prm = workloads.layer_params(w)
+    y, ref, unrounded = run(lisa, w, x, prm, feature="elu")
+    check(y, ref, unrounded, dtype, "elu " + w.describe())
+    y_relu, _, _ = run(lisa, w, x, prm)
+    assert not np.allclose(y_relu, y, rtol=0, atol=1e-3 * np.abs(y).max())
 
 
 @pytest.mark.parametrize("name", ["deit_t_224", "pvt_t_stage1"])
