@@ -103,6 +103,8 @@ RAGGED = [
     (1, 2, 20, 23, 16, "fp32", "adaptive"),
     (1, 1, 56, 56, 16, "bf16", "adaptive"),
     (2, 1, 9, 33, 9, "fp32", "geometric"),
+    # 128 ranks per slice with fp32 inputs (the plain combine at many ranks).
+    (1, 1, 128, 128, 4, "fp32", "adaptive"),
 ]
 
 
@@ -125,6 +127,8 @@ ELU = [
     (1, 1, 70, 70, 6, "bf16", "geometric"),   # many ranks per slice, ragged chunk tails
     (96, 3, 14, 14, 3, "bf16", "adaptive"),   # one rank per slice
     (1, 2, 20, 23, 12, "fp32", "adaptive"),
+    (1, 1, 128, 128, 5, "bf16", "adaptive"),  # 128 ranks per slice
+    (1, 1, 128, 128, 4, "fp32", "geometric"),
 ]
 
 
@@ -273,13 +277,21 @@ def test_side_stream(lisa):
     check(y, oracle_y(x), "bf16", "side stream")
 
 
-@pytest.mark.parametrize("name", ["pvt_t_stage1", "long_range_200x320"])
-def test_constant_values_give_constant_output(lisa, name):
-    """V = 1 gives Y = 1 up to eps r_i (row sums of S) and bf16 rounding."""
+@pytest.mark.parametrize("name,feature", [("pvt_t_stage1", "relu"), ("long_range_200x320", "relu"),
+                                          ("pvt_t_stage1", "elu")])
+def test_constant_values_give_constant_output(lisa, name, feature):
+    """V = 1 gives Y = 1 up to eps r_i (row sums of S) and bf16 rounding.
+    With ELU + 1 features the rows of S are stochastic only if r_i, the rows
+    of M and the projected queries all use the same (bf16-rounded) features."""
     w = workloads.get(name)
     x = workloads.make_inputs(w)
+    if feature == "elu":
+        g = torch.Generator().manual_seed(3)
+        for key in ("q", "k"):
+            x[key] = torch.randn(x[key].shape, generator=g).to(x[key].dtype)
     x["v"] = torch.ones_like(x["v"])
-    y = f64(gpu_y(lisa, to_dev(x)))
+    y = f64(gpu_y(lisa, to_dev(x), feature=feature))
+    print(f"[parity] constant V {name} {feature}: max |Y - 1| = {np.max(np.abs(y - 1.0)):.3e}", flush=True)
     assert np.max(np.abs(y - 1.0)) <= 2.0**-8
 
 

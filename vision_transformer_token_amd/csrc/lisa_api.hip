@@ -26,7 +26,7 @@ constexpr size_t kAlign = 256;
 struct DeviceInfo {
   int cus, xccs;
 };
-constexpr int kMaxDevices = 64;
+using lisa::kMaxDevices;
 std::atomic<int> g_dev_cus[kMaxDevices];
 std::atomic<int> g_dev_xccs[kMaxDevices];
 

@@ -283,13 +283,7 @@ __device__ __forceinline__ float sum_in_order(const float* x, size_t stride, int
   return v;
 }
 
-// Whole workgroup: copy a 64 x 64 fp32 matrix into LDS.
-__device__ __forceinline__ void load_mat(float* dst, const float* src) {
-  for (int e = threadIdx.x * 4; e < kD * kD; e += blockDim.x * 4)
-    *reinterpret_cast<float4*>(dst + e) = *reinterpret_cast<const float4*>(src + e);
-}
-
-// The same into rows of kR floats.
+// Whole workgroup: copy a 64 x 64 fp32 matrix into LDS rows of kR floats.
 __device__ __forceinline__ void load_mat_padded(float* dst, const float* src) {
   for (int e = threadIdx.x * 4; e < kD * kD; e += blockDim.x * 4) {
     const float4 v = *reinterpret_cast<const float4*>(src + e);
@@ -995,17 +989,12 @@ hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
   const size_t lds_a = token_a_lds<S>();
   const int T1 = a.T - 1 > 0 ? a.T - 1 : 1;
   const size_t lds_adj = ((size_t)T1 + 2) * kD * kR * sizeof(float);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_token_a<S>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_a);
-    if (e != hipSuccess) return e;
-    const size_t lds_adj_max = ((size_t)kMaxTBwd + 1) * kD * kR * sizeof(float);
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_adjoint),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_adj_max);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<bool> lds_set_a[kMaxDevices], lds_set_adj[kMaxDevices];
+  hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(&bwd_token_a<S>), (int)lds_a, lds_set_a);
+  if (e != hipSuccess) return e;
+  const size_t lds_adj_max = ((size_t)kMaxTBwd + 1) * kD * kR * sizeof(float);
+  e = ensure_lds_limit(reinterpret_cast<const void*>(&bwd_adjoint), (int)lds_adj_max, lds_set_adj);
+  if (e != hipSuccess) return e;
   const dim3 tok(a.nblk, a.BH);
   if (a.T >= 2) hipLaunchKernelGGL(bwd_powers, dim3(a.BH), dim3(kAdjThreads), 0, s, a);
   hipLaunchKernelGGL(bwd_token_a<S>, tok, dim3(kTT), lds_a, s, a);

@@ -136,6 +136,9 @@ __device__ void wait_for(const unsigned* c, unsigned target, unsigned* err) {
       break;
     }
   }
+  // The data the count announces is read only after this point: the
+  // compiler may not move those (relaxed) loads above the poll.
+  asm volatile("" ::: "memory");
 }
 
 // The same wait for a phase counted per group of kSubRanks ranks: lane k of
@@ -156,6 +159,7 @@ __device__ void wait_for_groups(const unsigned* base, int ngroups, unsigned* err
       break;
     }
   }
+  asm volatile("" ::: "memory");  // as in wait_for
 }
 
 // The counter a rank's arrival for phase `counter` of slice b goes to.
@@ -264,9 +268,10 @@ __device__ void stage_tile(const FlowArgs& a, int b, int t, unsigned char* buf, 
 // g of the row, and since swz(r) depends only on r & 7 = l / 8 and on
 // (r >> 3) & 1 = j & 1 = pw & 1, g is the same in every run of the wave.
 // f(j, r, x, dot) is called per run with the run's eight elements of the
-// lane's piece after the ReLU (applied to the bf16 bits: a negative bf16 is
-// a negative int16), and dot = their product with s over the row
-// (s[8 g .. 8 g + 7] held in registers); runs go four at a time, all their
+// lane's piece after the feature map (ReLU applied to the bf16 bits: a
+// negative bf16 is a negative int16; ELU + 1 rounded back to bf16), and
+// dot = their product with s over the row (s[8 g .. 8 g + 7] held in
+// registers); runs go four at a time, all their
 // LDS reads issued before the first product.  `nrun` is wave-uniform.
 template <bool kElu = false, class F>
 __device__ __forceinline__ void bf16_row_dots(const unsigned char* base, int nrun, const float* s, int pw, F f) {
@@ -293,7 +298,10 @@ __device__ __forceinline__ void bf16_row_dots(const unsigned char* base, int nru
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           x[e] = __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
-          if (kElu) x[e] = elu1(x[e]);
+          // ELU + 1 features rounded to bf16, as the s sweep and the output's
+          // u_1 take them (elu1_bits): r_j and the rows of M then use the same
+          // features, and the rows of S stay stochastic.
+          if (kElu) x[e] = bf2f(f2bf(elu1(x[e])));
           dot += x[e] * sv[e];
         }
         f(j, 8 * j + sub, x, group_sum8(dot));
@@ -595,6 +603,9 @@ __device__ void prepare(const FlowArgs& a, const Rank& rk, Pos p, unsigned char*
     } else if (lane == 0) {
       while (*dep_ok != tag) __builtin_amdgcn_s_sleep(1);  // wave 0 always posts
     }
+    // Loads of the data the dependency announces stay below the wait.
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
   };
   if (p.ph == kPKV || p.ph == kPM) {
     const bool is_m = p.ph == kPM;
@@ -1314,13 +1325,9 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
 template <class Tr, bool kMlp, int kVar = kVarPlain>
 hipError_t launch_typed(const FlowArgs& a, int grid, hipStream_t s) {
   constexpr int lds = LdsOf<Tr>::kTotal;
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&flow_kernel<Tr, kMlp, kVar>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<bool> lds_set[kMaxDevices];
+  const hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(&flow_kernel<Tr, kMlp, kVar>), lds, lds_set);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((flow_kernel<Tr, kMlp, kVar>), dim3(grid), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }

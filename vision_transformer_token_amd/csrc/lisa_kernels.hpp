@@ -5,7 +5,26 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace lisa {
+
+// A kernel's limit on dynamic LDS beyond 64 KB, set once per device: the
+// attribute belongs to the device current at the call, so each device that
+// runs the kernel needs its own.  `done` is the kernel's own table (static
+// storage, zero at load).  Two threads making the first call on one device
+// both set it, which is harmless; devices past the table set it every call.
+constexpr int kMaxDevices = 64;
+inline hipError_t ensure_lds_limit(const void* fn, int bytes, std::atomic<bool> (&done)[kMaxDevices]) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool tracked = dev >= 0 && dev < kMaxDevices;
+  if (tracked && done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && tracked) done[dev].store(true, std::memory_order_release);
+  return e;
+}
 
 constexpr int kD = 64;          // d_h = d_v supported by the kernel
 constexpr int kMaxT = 16;       // walk terms k = 0..T-1 of the forward
