@@ -80,7 +80,8 @@ typedef enum lisa_status {
   LISA_ERR_WORKSPACE = 6,   /* workspace NULL, too small or not 256-byte aligned */
   LISA_ERR_ALIGN = 7,       /* Q, K, V, Y not 16-byte or weights/alpha/outputs not 4-byte aligned */
   LISA_ERR_HIP = 8,         /* a HIP launch or copy failed */
-  LISA_ERR_STALLED = 9      /* a call abandoned a wait: its outputs are undefined (lisa_workspace_check) */
+  LISA_ERR_STALLED = 9,     /* a call abandoned a wait: its outputs are undefined (lisa_workspace_check) */
+  LISA_ERR_SCRATCH = 10     /* the problem does not fit lisa_forward_noalloc's fixed scratch */
 } lisa_status;
 
 typedef enum lisa_dtype { LISA_FP32 = 0, LISA_BF16 = 1 } lisa_dtype;
@@ -124,6 +125,32 @@ size_t lisa_workspace_size(const lisa_problem* p);
 lisa_status lisa_forward(const lisa_problem* p, const void* Q, const void* K, const void* V,
                          const float* weights, float beta, const float* alpha, void* Y,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* lisa_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Arguments as for lisa_forward, without a workspace: the launch counters,
+ * rank partials and statistics live in a fixed array of the library, 32 MiB
+ * of device memory per GPU, which each GPU that runs this call holds until
+ * the process ends.  The call allocates nothing (no hipMalloc, no library
+ * routine that allocates) and, like lisa_forward, only enqueues work.
+ *   - Limit: at most 8192 (batch, head) slices, and counters plus partials
+ *     for the device's launch within 32 MiB (PVT-T stage 1, B = 32: 10 MB;
+ *     one 200 x 320 sequence: 9 MB); a larger problem returns
+ *     LISA_ERR_SCRATCH before anything is enqueued.
+ *   - Every call on one GPU shares that GPU's array and finds the previous
+ *     call's contents there; each completed call leaves the words that must
+ *     start at zero (counters, tickets, the stall flag) at zero.  Calls that
+ *     overlap on one GPU (other streams, other host threads) race and give
+ *     undefined results: order them on one stream.
+ *   - An abandoned wait (see Scheduling above) is not reported: with no
+ *     workspace there is nothing for lisa_workspace_check to read, and the
+ *     call clears the flag when it finishes.
+ *   - Same kernels and results as lisa_forward for the same problem and
+ *     inputs; the statistics are not left anywhere the other entry points
+ *     (lisa_apply, lisa_backward_after_forward) can read. */
+lisa_status lisa_forward_noalloc(const lisa_problem* p, const void* Q, const void* K, const void* V,
+                                 const float* weights, float beta, const float* alpha, void* Y,
+                                 void* stream);
 
 /* First stage alone: the d_h-space statistics of every (batch, head)
  * [note §2.3 Eq. 8]:

@@ -28,6 +28,7 @@ def test_header_declares_the_entry_points():
         "lisa_apply", "lisa_attention_forward", "lisa_attention_workspace_size", "lisa_backward",
         "lisa_backward_after_forward",
         "lisa_backward_workspace_size", "lisa_forward", "lisa_forward_mlp", "lisa_forward_mlp_workspace_size",
+        "lisa_forward_noalloc",
         "lisa_reduce", "lisa_status_str", "lisa_workspace_check", "lisa_workspace_size"]
 
 
@@ -191,7 +192,7 @@ def test_backward_argument_errors(backward_entry):
 
 def test_status_strings():
     seen = set()
-    for code in range(10):
+    for code in range(11):
         s = lisa.lisa_status_str(code)
         assert s and s not in seen
         seen.add(s)
@@ -289,3 +290,24 @@ def test_attention_argument_errors():
     assert attention(p, y=X_) == PARAM
     assert attention(p, y=WS_) == PARAM
 
+
+
+def test_forward_noalloc_argument_errors():
+    """lisa_forward_noalloc: every check that needs no device comes first, so
+    these fail before any HIP call (no GPU here)."""
+    f = lib.lisa_forward_noalloc
+
+    def call(p, q=Q, k=K, v=V, w=W_, beta=0.5, alpha=AL, y=Y):
+        return f(None if p is None else ctypes.byref(p), q, k, v, w, ctypes.c_float(beta), alpha, y, None)
+
+    assert call(None) == NULL
+    assert call(prob(batch=0)) == SHAPE
+    assert call(prob(d_h=32)) == UNSUP
+    assert call(prob(T=0)) == PARAM
+    assert call(prob(), w=None, beta=1.0) == PARAM
+    assert call(prob(), q=None) == NULL
+    assert call(prob(), y=None) == NULL
+    assert call(prob(), v=V + 8) == ALIGN
+    assert call(prob(), y=Q) == PARAM
+    # More (batch, head) slices than the fixed scratch's counters cover.
+    assert call(prob(batch=8193, heads=1, grid_h=1, grid_w=1)) == lisa.LISA_ERR_SCRATCH

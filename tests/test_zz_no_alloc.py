@@ -1,0 +1,70 @@
+"""lisa_forward_noalloc (no workspace: the library's fixed device scratch)
+against lisa_forward with a workspace, on the GPU, through the C ABI.
+
+Two calls in a row, the second on a smaller problem, so that the second call
+runs on the scratch the first one left behind; each must give lisa_forward's
+output bit for bit (same kernels, same plan).  A problem too large for the
+scratch is refused before anything is enqueued.
+"""
+
+import pytest
+import torch
+
+from vision_transformer_token_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lisa():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from vision_transformer_token_amd import lisa as mod
+
+    return mod
+
+
+def dev(x):
+    return {k: (x[k].cuda() if isinstance(x[k], torch.Tensor) else x[k]) for k in x}
+
+
+def both(lisa, w, x):
+    d = dev(x)
+    kw = dict(grid=(w.H, w.W), T=w.T, alpha=d["alpha"], weights=d["weights"], beta=d["beta"], eps=w.eps)
+    y_ws = lisa.lisa_forward(d["q"], d["k"], d["v"], **kw)
+    y_na = lisa.lisa_forward_noalloc(d["q"], d["k"], d["v"], **kw)
+    torch.cuda.synchronize()
+    return y_ws, y_na
+
+
+def test_noalloc_equals_forward_on_two_calls(lisa):
+    cases = [workloads.get("pvt_t_stage1"),
+             workloads.small("noalloc-small", 2, 3, 13, 17, 4, dtype="bf16", seed=61)]
+    for w in cases:
+        x = workloads.make_inputs(w)
+        y_ws, y_na = both(lisa, w, x)
+        print(f"[noalloc] {w.describe()}: equal={torch.equal(y_ws, y_na)}", flush=True)
+        assert torch.isfinite(y_na.float()).all()
+        assert torch.equal(y_ws, y_na), w.describe()
+
+
+def test_noalloc_many_ranks_then_fp32(lisa):
+    """A long sequence (grouped arrivals, 256 ranks) then a small fp32 problem
+    with geometric weights on the same scratch."""
+    cases = [workloads.get("long_range_200x320"),
+             workloads.small("noalloc-fp32", 1, 2, 9, 11, 3, dtype="fp32", mode="geometric", beta=0.4, seed=62)]
+    for w in cases:
+        x = workloads.make_inputs(w)
+        y_ws, y_na = both(lisa, w, x)
+        print(f"[noalloc] {w.describe()}: equal={torch.equal(y_ws, y_na)}", flush=True)
+        assert torch.equal(y_ws, y_na), w.describe()
+
+
+def test_noalloc_refuses_problem_larger_than_scratch(lisa):
+    # 4096 slices of 56 x 56 tokens: one rank per slice, 4096 * 32 KB of partials > 32 MiB.
+    w = workloads.small("noalloc-big", 4096, 1, 56, 56, 3, dtype="bf16", seed=63)
+    q = torch.zeros(w.B, 1, w.n, 64, dtype=torch.bfloat16, device="cuda")
+    alpha = torch.full((1,), 0.5, device="cuda")
+    with pytest.raises(lisa.LisaError) as e:
+        lisa.lisa_forward_noalloc(q, q, q, grid=(w.H, w.W), T=3, alpha=alpha, beta=0.5, out=torch.empty_like(q))
+    assert e.value.status == lisa.LISA_ERR_SCRATCH

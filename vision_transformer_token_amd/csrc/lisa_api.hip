@@ -141,6 +141,36 @@ int plan_ranks(int grid, int BH, int n) {
   return G;
 }
 
+// The forward's regions of a workspace, from offset 0: the launch counters
+// first, sized for `counter_slices` slices, at offsets and sizes that do not
+// depend on the problem (a workspace reused by problems of other shapes
+// never has another problem's data written over a counter; each call leaves
+// them at zero); then the rank partials for pl.gmax ranks per slice and the
+// statistics.  Sets pl.total and returns it.
+size_t layout_forward(Plan& pl, size_t counter_slices) {
+  const size_t BH = pl.BH, G = pl.gmax;
+  const size_t mat = kD * kD * sizeof(float), vec = kD * sizeof(float);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = up(o + bytes, kAlign);
+    return at;
+  };
+  pl.done_cnt = take(32 * sizeof(unsigned));
+  pl.slice_cnt = take(counter_slices * lisa::kCntStride * sizeof(unsigned));
+  pl.sub_cnt = take((size_t)lisa::kMaxSubSlices * 3 * lisa::kMaxSubs * lisa::kCntStride * sizeof(unsigned));
+  pl.part_s = take(BH * G * vec);
+  pl.part_kv = take(BH * G * mat);
+  pl.part_m = take(BH * G * mat);
+  pl.fin_s = take(BH * vec);
+  pl.fin_kv = take(BH * mat);
+  pl.fin_m = take(BH * mat);
+  pl.frag_kv = take(BH * kD * kD * pl.esize);
+  pl.frag_m = take(BH * kD * kD * pl.esize);
+  pl.total = o;
+  return o;
+}
+
 lisa_status make_plan(const lisa_problem* p, Plan& pl) {
   const lisa_status st = check_problem(p);
   if (st != LISA_OK) return st;
@@ -160,29 +190,14 @@ lisa_status make_plan(const lisa_problem* p, Plan& pl) {
   // rows (a multiple of 16 tokens: the MFMA sweep reads whole 16-row steps).
   pl.chunk = pl.esize == 2 ? lisa::Lds<2>::kChunk : lisa::Lds<4>::kChunk;
 
-  const size_t BH = pl.BH, G = pl.gmax;
+  size_t o = layout_forward(pl, kMaxSlices);
+  const size_t BH = pl.BH;
   const size_t mat = kD * kD * sizeof(float), vec = kD * sizeof(float);
-  size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
     o = up(o + bytes, kAlign);
     return at;
   };
-  // Counters first, at offsets and sizes that do not depend on the problem:
-  // a workspace reused by problems of other shapes never has another
-  // problem's data written over a counter (each call leaves them at zero).
-  pl.done_cnt = take(32 * sizeof(unsigned));
-  pl.slice_cnt = take((size_t)kMaxSlices * lisa::kCntStride * sizeof(unsigned));
-  pl.sub_cnt = take((size_t)lisa::kMaxSubSlices * 3 * lisa::kMaxSubs * lisa::kCntStride * sizeof(unsigned));
-  pl.part_s = take(BH * G * vec);
-  pl.part_kv = take(BH * G * mat);
-  pl.part_m = take(BH * G * mat);
-  pl.fin_s = take(BH * vec);
-  pl.fin_kv = take(BH * mat);
-  pl.fin_m = take(BH * mat);
-  pl.frag_kv = take(BH * kD * kD * pl.esize);
-  pl.frag_m = take(BH * kD * kD * pl.esize);
-  pl.total = o;
   // Backward: P_1..P_(T-1); per-token scalars; per-workgroup partials of dP_k,
   // dalpha and ds; each slice's dalpha, dM and dKV.
   const size_t T1 = pl.T > 1 ? (size_t)pl.T - 1 : 1;
@@ -236,8 +251,10 @@ enum class Mode { kForward, kReduce, kApply };
 // One launch of the persistent kernel, one workgroup per compute unit.
 lisa_status run(Plan pl, Mode mode, const void* Q, const void* K, const void* V,
                 const float* weights, float beta, const float* alpha, void* Y, char* ws, float eps,
-                hipStream_t s, const lisa_weight_mlp* mlp = nullptr, const void* mlp_frag = nullptr) {
+                hipStream_t s, const lisa_weight_mlp* mlp = nullptr, const void* mlp_frag = nullptr,
+                bool clear_err = false) {
   lisa::FlowArgs a{};
+  a.clear_err = clear_err ? 1 : 0;
   if (mlp) {
     a.mlp_w1f = mlp_frag;
     a.mlp_b1 = mlp->b1;
@@ -323,6 +340,40 @@ lisa_status run(Plan pl, Mode mode, const void* Q, const void* K, const void* V,
   return LISA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Fixed scratch of lisa_forward_noalloc: the launch counters, rank partials
+// and statistics that lisa_forward keeps in the caller's workspace live in
+// this array instead.  Each device that runs the library holds its own copy
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: the device address of the current device's copy comes
+// from hipGetSymbolAddress, once per device, and only that address is used.
+// The array is zero when the code object loads, and every completed call
+// leaves its counters (and, for this entry point, the stall flag) at zero.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(32) << 20;
+constexpr size_t kScratchSlices = 8192;  // (batch, head) slices its counters cover
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::atomic<char*> g_scratch[kMaxDevices];
+
+// The current device's copy of `scratch` (looked up on the device's first
+// call; a racing second lookup stores the same address).
+lisa_status scratch_address(char** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return LISA_ERR_HIP;
+  if (dev < kMaxDevices) {
+    char* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p) {
+      *out = p;
+      return LISA_OK;
+    }
+  }
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return LISA_ERR_HIP;
+  if (dev < kMaxDevices) g_scratch[dev].store(static_cast<char*>(ptr), std::memory_order_release);
+  *out = static_cast<char*>(ptr);
+  return LISA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -341,6 +392,34 @@ lisa_status lisa_forward(const lisa_problem* p, const void* Q, const void* K, co
   (void)hipGetLastError();  // clear a stale error so that ours are reported alone
   return run(pl, Mode::kForward, Q, K, V, weights, beta, alpha, Y, static_cast<char*>(workspace),
              p->eps, static_cast<hipStream_t>(stream));
+}
+
+lisa_status lisa_forward_noalloc(const lisa_problem* p, const void* Q, const void* K, const void* V,
+                                 const float* weights, float beta, const float* alpha, void* Y, void* stream) {
+  Plan pl;
+  lisa_status st = make_plan(p, pl);
+  if (st != LISA_OK) return st;
+  if (!weights && !(beta >= 0.f && beta < 1.f)) return LISA_ERR_PARAM;
+  if (!Q || !K || !V || !alpha || !Y) return LISA_ERR_NULL;
+  if (misaligned(Q, 16) || misaligned(K, 16) || misaligned(V, 16) || misaligned(Y, 16) ||
+      misaligned(weights, 4) || misaligned(alpha, 4))
+    return LISA_ERR_ALIGN;
+  const size_t tensor = (size_t)pl.BH * pl.n * kD * pl.esize;
+  if (overlaps(Y, tensor, Q, tensor) || overlaps(Y, tensor, K, tensor) || overlaps(Y, tensor, V, tensor))
+    return LISA_ERR_PARAM;
+  if ((size_t)pl.BH > kScratchSlices) return LISA_ERR_SCRATCH;
+  (void)hipGetLastError();
+  // The partials for exactly the ranks this device's launch gives a slice
+  // (run() picks the same number), not for the most any device could.
+  DeviceInfo dinfo;
+  if (!device_info(dinfo)) return LISA_ERR_HIP;
+  pl.gmax = plan_ranks(dinfo.cus, pl.BH, pl.n);
+  if (layout_forward(pl, kScratchSlices) > kScratchBytes) return LISA_ERR_SCRATCH;
+  char* base = nullptr;
+  st = scratch_address(&base);
+  if (st != LISA_OK) return st;
+  return run(pl, Mode::kForward, Q, K, V, weights, beta, alpha, Y, base, p->eps, static_cast<hipStream_t>(stream),
+             nullptr, nullptr, /*clear_err=*/true);
 }
 
 lisa_status lisa_reduce(const lisa_problem* p, const void* Q, const void* K, const void* V,
@@ -604,6 +683,8 @@ const char* lisa_status_str(lisa_status s) {
     case LISA_ERR_ALIGN: return "misaligned pointer (Q, K, V, Y need 16 bytes; fp32 arrays 4)";
     case LISA_ERR_HIP: return "a HIP launch or copy failed";
     case LISA_ERR_STALLED: return "a call abandoned a dependency wait; its outputs are undefined";
+    case LISA_ERR_SCRATCH:
+      return "problem too large for lisa_forward_noalloc's fixed 32 MiB scratch (at most 8192 slices)";
   }
   return "unknown status";
 }

@@ -1316,6 +1316,7 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
     if constexpr (kVar == kVarGrouped)
       for (int i = tid; i < a.BH * 3 * kMaxSubs; i += kThreads) put(a.sub_cnt + (size_t)i * kCntStride, 0u);
     if (tid < kXcds) put(a.tickets + tid, 0u);
+    if (a.clear_err && tid == 0) put(a.err, 0u);
     wait_all();
     __syncthreads();
     if (tid == 0) put(a.done_cnt, 0u);

@@ -132,6 +132,7 @@ struct FlowArgs {
   unsigned* done_cnt;     // finished workgroups
   unsigned* tickets;      // [kXcds] rank tickets
   unsigned* err;          // error word (a dependency wait timed out)
+  int clear_err;          // the last workgroup also clears the error word (no workspace to check it in)
   // Walk-weight predictor (weights == nullptr): w_i = softmax(W2 ReLU(W1 x_i + b1) + b2),
   // x_i = concat(Q_i, K_i), per head; W1 in the order the kernel's lanes
   // read it (launch_mlp_prep).

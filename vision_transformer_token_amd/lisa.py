@@ -34,12 +34,15 @@ __all__ = [
     "lisa_backward_after_forward",
     "lisa_backward_workspace_size",
     "LISA_ERR_STALLED",
+    "LISA_ERR_SCRATCH",
+    "lisa_forward_noalloc",
 ]
 
 LISA_FP32 = 0
 LISA_BF16 = 1
 LISA_OK = 0
 LISA_ERR_STALLED = 9
+LISA_ERR_SCRATCH = 10
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -96,6 +99,8 @@ _lib.lisa_workspace_size.argtypes = [_P]
 _lib.lisa_workspace_size.restype = ctypes.c_size_t
 _lib.lisa_forward.argtypes = [_P, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.lisa_forward.restype = ctypes.c_int
+_lib.lisa_forward_noalloc.argtypes = [_P, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp]
+_lib.lisa_forward_noalloc.restype = ctypes.c_int
 _lib.lisa_apply.argtypes = _lib.lisa_forward.argtypes
 _lib.lisa_apply.restype = ctypes.c_int
 _lib.lisa_reduce.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
@@ -216,6 +221,29 @@ def lisa_forward(q, k, v, *, grid, T, alpha, weights=None, beta=None, eps=1e-6, 
     return _call_forward(_lib.lisa_forward, "lisa_forward", q, k, v, grid=grid, T=T, alpha=alpha,
                          weights=weights, beta=beta, eps=eps, out=out, workspace=workspace,
                          stream=stream, feature=feature)
+
+
+def lisa_forward_noalloc(q, k, v, *, grid, T, alpha, weights=None, beta=None, eps=1e-6, out=None, stream=None,
+                         feature="relu"):
+    """lisa_forward without a workspace (the library's fixed device scratch;
+    nothing is allocated by the call itself; ``out`` is allocated here when
+    not given); see include/lisa.h."""
+    _check_tensors(q=q, k=k, v=v, alpha=alpha, weights=weights, out=out)
+    if weights is not None and weights.dtype != torch.float32:
+        raise TypeError("weights must be float32")
+    if alpha.dtype != torch.float32:
+        raise TypeError("alpha must be float32")
+    if weights is None and beta is None:
+        raise ValueError("give adaptive weights or beta")
+    prob = make_problem(q, v, grid=grid, T=T, eps=eps, feature=feature)
+    if out is None:
+        out = torch.empty_like(v)
+    st = _lib.lisa_forward_noalloc(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(weights),
+                                   ctypes.c_float(0.0 if beta is None else beta), _ptr(alpha), _ptr(out),
+                                   _stream(stream, q.device))
+    if st != LISA_OK:
+        raise LisaError(st, "lisa_forward_noalloc")
+    return out
 
 
 def lisa_forward_mlp_workspace_size(problem, hidden):
