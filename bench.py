@@ -105,10 +105,13 @@ def _csv_rows(path):
         return list(csv.DictReader(f))
 
 
-KERNEL = "flow_kernel<bf16>"  # the one kernel of the path (one launch per forward)
+# The one kernel of the path (one launch per forward), by lisa_schedule.
+KERNELS = {"streaming": "flow_kernel<bf16>", "resident": "resident_kernel"}
 
 
 def _short(name):
+    if "resident_kernel" in name:
+        return "resident_kernel"
     if "flow_kernel" in name:
         t = "bf16" if "BF16" in name else "fp32"
         return f"flow_kernel<{t}, predictor>" if ", true>" in name else f"flow_kernel<{t}>"
@@ -310,6 +313,10 @@ def main():
                     help="write the profiles/ summary of a layer kernel trace under DIR and exit")
     ap.add_argument("--mlp-only", action="store_true",
                     help="time only lisa_forward_mlp (predicted walk weights) and print its line")
+    ap.add_argument("--phases", action="store_true",
+                    help="print the stage timeline of lisa_forward_phases over --steps cold calls and exit")
+    ap.add_argument("--schedule", default="auto", choices=["auto", "streaming", "resident"],
+                    help="forward kernel (lisa_schedule); auto is the library's choice")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="instead of LiSA, run 20 plain device copies of this many MiB "
@@ -397,23 +404,25 @@ def main():
                  for key in ("q", "k", "v", "weights", "alpha")}
             d["y"] = torch.empty_like(d["v"])
             sets.append(d)
-        prob = lisa.make_problem(sets[0]["q"], sets[0]["v"], grid=(w.H, w.W), T=w.T, eps=w.eps)
+        prob = lisa.make_problem(sets[0]["q"], sets[0]["v"], grid=(w.H, w.W), T=w.T, eps=w.eps,
+                                 schedule=args.schedule)
         ws = lisa.new_workspace(prob, dev)
     torch.cuda.synchronize()
+    kernel_name = KERNELS[lisa.lisa_forward_schedule(prob)]
 
     def forward(d):
         lisa.lisa_forward(d["q"], d["k"], d["v"], grid=(w.H, w.W), T=w.T, alpha=d["alpha"],
                           weights=d["weights"], beta=x["beta"], eps=w.eps, out=d["y"], workspace=ws,
-                          stream=stream)
+                          stream=stream, schedule=args.schedule)
 
     def reduce(d):
         lisa.lisa_reduce(d["q"], d["k"], d["v"], grid=(w.H, w.W), eps=w.eps, T=w.T, workspace=ws,
-                         outputs=False, stream=stream)
+                         outputs=False, stream=stream, schedule=args.schedule)
 
     def apply(d):
         lisa.lisa_apply(d["q"], d["k"], d["v"], grid=(w.H, w.W), T=w.T, alpha=d["alpha"],
                         weights=d["weights"], beta=x["beta"], eps=w.eps, out=d["y"], workspace=ws,
-                        stream=stream)
+                        stream=stream, schedule=args.schedule)
 
     def backward_timing(steps, warmup, pairs=True):
         """lisa_backward over the same input sets (dY drawn once per set); with
@@ -561,29 +570,91 @@ def main():
                 ows = lisa.new_workspace(oprob, dev)
             torch.cuda.synchronize()
 
-            def ofwd(d):
-                lisa.lisa_forward(d["q"], d["k"], d["v"], grid=(ow.H, ow.W), T=ow.T, alpha=d["alpha"],
-                                  weights=d["weights"], beta=ox["beta"], eps=ow.eps, out=d["y"], workspace=ows,
-                                  stream=stream)
+            def timed(schedule):
+                def ofwd(d):
+                    lisa.lisa_forward(d["q"], d["k"], d["v"], grid=(ow.H, ow.W), T=ow.T, alpha=d["alpha"],
+                                      weights=d["weights"], beta=ox["beta"], eps=ow.eps, out=d["y"],
+                                      workspace=ows, stream=stream, schedule=schedule)
 
-            for i in range(warmup):
-                ofwd(osets[i % on])
-            oa, oz = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            oa.record(stream)
-            for i in range(steps):
-                ofwd(osets[i % on])
-            oz.record(stream)
-            torch.cuda.synchronize()
-            ms = oa.elapsed_time(oz) / steps
+                for i in range(warmup):
+                    ofwd(osets[i % on])
+                oa, oz = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                oa.record(stream)
+                for i in range(steps):
+                    ofwd(osets[i % on])
+                oz.record(stream)
+                torch.cuda.synchronize()
+                return oa.elapsed_time(oz) / steps
+
+            ms = timed(args.schedule)
+            # Each kernel alone, where it takes the problem: the evidence for
+            # the library's default.
+            by = {}
+            for sched in ("streaming", "resident"):
+                try:
+                    lisa.lisa_forward_schedule(lisa.make_problem(osets[0]["q"], osets[0]["v"], grid=(ow.H, ow.W),
+                                                                 T=ow.T, eps=ow.eps, schedule=sched))
+                    by[sched] = timed(sched)
+                except lisa.LisaError:
+                    by[sched] = None
             bb = compulsory_bytes_per_token_head(ow)
             rec[name] = {"ms_per_step": ms, "value": ow.token_heads / (ms * 1e-3), "unit": "token-heads/s",
                          "steps": steps, "token_heads": ow.token_heads, "n": ow.n, "T": ow.T,
+                         "kernel": KERNELS[lisa.lisa_forward_schedule(lisa.make_problem(
+                             osets[0]["q"], osets[0]["v"], grid=(ow.H, ow.W), T=ow.T, eps=ow.eps,
+                             schedule=args.schedule))],
+                         "ms_per_step_by_schedule": by,
                          "algorithmic_bytes_per_call": ow.token_heads * bb,
                          "roofline_frac": ow.token_heads * bb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
             del osets, ows
             torch.cuda.synchronize()
         return rec
+
+    def phases_timing(calls, warmup):
+        """The stage timeline of lisa_forward_phases over `calls` cold calls
+        (rotating input sets): per stage, the median and 90th percentile over
+        the active workgroups of the time since the first workgroup started,
+        averaged over the calls, in microseconds."""
+        import numpy as np
+
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        stamps = torch.zeros(cus * lisa.LISA_PHASES, dtype=torch.int64, device=dev)
+
+        def call(d):
+            lisa.lisa_forward_phases(d["q"], d["k"], d["v"], grid=(w.H, w.W), T=w.T, alpha=d["alpha"],
+                                     weights=d["weights"], beta=x["beta"], eps=w.eps, out=d["y"], workspace=ws,
+                                     stream=stream, stamps=stamps)
+
+        for i in range(warmup):
+            forward(sets[i % nsets])
+        med, p90, rows = [], [], None
+        for i in range(calls):
+            stamps.fill_(0)
+            torch.cuda.synchronize()
+            call(sets[i % nsets])
+            torch.cuda.synchronize()
+            st = stamps.view(cus, lisa.LISA_PHASES).cpu().numpy()
+            active = st[:, 0] > 0
+            rank = st[:, lisa.LISA_PHASES - 1]
+            active &= (rank >> 32) != 0xFFFFFFFF  # idle workgroups carry group -1
+            a_st = st[active][:, :len(lisa.STAGES)].astype(np.float64)
+            t0 = a_st[:, 0].min()
+            rel = (a_st - t0) / 100.0  # 100 MHz clock -> microseconds
+            rel[a_st == 0] = np.nan  # stages the problem does not have
+            med.append(np.nanmedian(rel, axis=0))
+            p90.append(np.nanpercentile(rel, 90, axis=0))
+            rows = int(active.sum())
+        med, p90 = np.nanmean(np.array(med), axis=0), np.nanmean(np.array(p90), axis=0)
+        return {"workgroups": rows, "calls": calls,
+                "stages": {name: {"median_us": None if np.isnan(m) else round(float(m), 3),
+                                  "p90_us": None if np.isnan(q) else round(float(q), 3)}
+                           for name, m, q in zip(lisa.STAGES, med, p90)}}
+
+    if args.phases:
+        rec = phases_timing(args.steps, args.warmup)
+        print(json.dumps({"workload": w.name, "phases": rec}), flush=True)
+        return
 
     if args.backward_only:
         print(json.dumps({"workload": w.name, "backward": backward_timing(args.steps, args.warmup, pairs=False)}),
@@ -726,10 +797,10 @@ def main():
         # average launch duration is the timed region's elapsed time (events
         # on that stream) over the K launches.
         achieved = th * bpt / (step_ms * 1e-3) / 1e9
-        traffic = load_counters(w, KERNEL)
+        traffic = load_counters(w, kernel_name)
         out["roofline"] = {
             "bound": "hbm",
-            "kernel": KERNEL,
+            "kernel": kernel_name,
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -92,6 +92,23 @@ typedef enum lisa_dtype { LISA_FP32 = 0, LISA_BF16 = 1 } lisa_dtype;
  * inputs are. */
 typedef enum lisa_feature { LISA_FEATURE_RELU = 0, LISA_FEATURE_ELU = 1 } lisa_feature;
 
+/* Which forward kernel runs the pass.  Both compute the same quantities in
+ * the same precision; they differ in schedule and so in the order of the
+ * fp32 sums over tokens.
+ *   AUTO      : the library's choice for the problem and device (zero).
+ *   STREAMING : workgroups stream tiles through LDS in three passes over K
+ *               (statistics, then the rescaled keys, then the output).
+ *   RESIDENT  : each workgroup holds its tile of Q, K, V on chip for the
+ *               whole pass (bf16 ReLU problems whose tiles fit: T <= 8,
+ *               no predictor); LISA_ERR_UNSUPPORTED where it does not apply.
+ * lisa_forward, lisa_reduce, lisa_apply and lisa_forward_mlp of one problem
+ * (same struct, same device) take the same kernel and so form the same sums. */
+typedef enum lisa_schedule {
+  LISA_SCHEDULE_AUTO = 0,
+  LISA_SCHEDULE_STREAMING = 1,
+  LISA_SCHEDULE_RESIDENT = 2
+} lisa_schedule;
+
 /* Problem description.  n = grid_h * grid_w tokens per (batch, head). */
 typedef struct lisa_problem {
   int32_t batch;  /* B >= 1 */
@@ -107,11 +124,22 @@ typedef struct lisa_problem {
   int32_t feature; /* lisa_feature (0, ReLU, when zero-initialised); another
                       value: LISA_ERR_PARAM; ELU with lisa_forward_mlp or the
                       backward entry points: LISA_ERR_UNSUPPORTED */
+  int32_t schedule; /* lisa_schedule (AUTO when zero-initialised); another
+                       value: LISA_ERR_PARAM */
 } lisa_problem;
 
 /* Bytes of device workspace the calls below need for problem *p; 0 if *p is
  * invalid (or p is NULL).  Host only; enqueues nothing. */
 size_t lisa_workspace_size(const lisa_problem* p);
+
+/* The kernel lisa_forward runs for *p on the current device:
+ * *schedule = LISA_SCHEDULE_STREAMING or LISA_SCHEDULE_RESIDENT (p->schedule
+ * resolved; AUTO depends on the device's compute units).  Status as the
+ * forward's checks of *p; LISA_ERR_NULL if schedule is NULL;
+ * LISA_ERR_UNSUPPORTED if p->schedule is RESIDENT and that kernel does not
+ * take the problem; LISA_ERR_HIP if no device is visible.  Host only;
+ * enqueues nothing. */
+lisa_status lisa_forward_schedule(const lisa_problem* p, int32_t* schedule);
 
 /* The whole LiSA forward pass: Y = alpha G + (1 - alpha) L (see top).
  *   weights : [batch, heads, n, T] fp32 adaptive step weights w_k(i)
@@ -151,6 +179,45 @@ lisa_status lisa_forward(const lisa_problem* p, const void* Q, const void* K, co
 lisa_status lisa_forward_noalloc(const lisa_problem* p, const void* Q, const void* K, const void* V,
                                  const float* weights, float beta, const float* alpha, void* Y,
                                  void* stream);
+
+/* lisa_forward that also records when each workgroup of the launch reached
+ * each stage of the pass, for performance analysis [the stages of note §2.3
+ * Eq. 8 / Algorithm 1: the statistics sweeps, their sums, the output].
+ * Same arguments, work and Y as lisa_forward, plus
+ *   stamps       : device array of stamps_count uint64_t (8-byte aligned);
+ *                  workgroup w writes entry w * LISA_PHASES + k when it
+ *                  reaches stage k (LISA_STAGE_*) of its first slice: the
+ *                  device's constant 100 MHz clock (s_memrealtime); entry
+ *                  w * LISA_PHASES + LISA_PHASES - 1 holds its group (high
+ *                  32 bits) and its rank in the group (low).  A stage the
+ *                  problem does not have leaves its entry as it was.
+ *   stamps_count : at least (compute units) * LISA_PHASES, else LISA_ERR_PARAM.
+ * Runs the resident kernel (LISA_SCHEDULE_RESIDENT) whatever p->schedule
+ * asks, except STREAMING; only for problems it takes (bf16, ReLU features,
+ * T <= 8, grids whose tiles fit a workgroup).  Others, and STREAMING, return
+ * LISA_ERR_UNSUPPORTED before anything is enqueued. */
+#define LISA_PHASES 16
+enum {
+  LISA_STAGE_START = 0,  /* rank taken */
+  LISA_STAGE_STAGED,     /* K, V cells, weights, Q in LDS / registers */
+  LISA_STAGE_KV,         /* partial of s and phi(K)^T V published */
+  LISA_STAGE_LOCAL,      /* local branch and k = 0 term done */
+  LISA_STAGE_S,          /* every rank's KV partial arrived; s formed */
+  LISA_STAGE_M,          /* partial of M published */
+  LISA_STAGE_MWAIT,      /* every rank's M partial arrived */
+  LISA_STAGE_COMBINE,    /* this rank's share of the statistics written */
+  LISA_STAGE_CWAIT,      /* every rank's share arrived */
+  LISA_STAGE_FRAGS,      /* statistics fragments loaded */
+  LISA_STAGE_OUT,        /* Y of every slice written */
+  LISA_STAGE_END,        /* workgroup done */
+  LISA_STAGE_KVSWEEP,    /* products of the KV sweep done, before publishing */
+  LISA_STAGE_CSTAGED,    /* this rank's share of every partial loaded */
+  LISA_STAGE_CSUMMED     /* that share summed, before it is written */
+};
+lisa_status lisa_forward_phases(const lisa_problem* p, const void* Q, const void* K, const void* V,
+                                const float* weights, float beta, const float* alpha, void* Y,
+                                void* workspace, size_t workspace_bytes, uint64_t* stamps,
+                                size_t stamps_count, void* stream);
 
 /* First stage alone: the d_h-space statistics of every (batch, head)
  * [note §2.3 Eq. 8]:

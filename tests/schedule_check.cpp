@@ -1,0 +1,133 @@
+// CPU check of the resident forward kernel's static schedule
+// (vision_transformer_token_amd/csrc/lisa_resident.hpp), built by
+// tests/test_schedule_cpu.py with hipcc for the host only.
+//
+// For each problem given on the command line as "H W T gcap" it plans the
+// tiling with res_plan (as the library does) and checks, for every tile:
+//   - the tiles' token slots cover every grid token exactly once;
+//   - every on-grid cell of a tile token's 3x3 window is staged (res_cell does
+//     not clamp it), and every clamped window cell of any slot (valid or
+//     masked) is a staged cell;
+//   - slot-table rows, DMA runs, the zero row, the weight runs and the
+//     rescaled-Q rows stay inside their LDS regions, the regions do not
+//     overlap, and the layout fits the workgroup's LDS;
+//   - the sweep steps read only slots of the tile; the combine ranges of the
+//     G ranks partition the statistics.
+// Prints one line per problem ("ok ..." or "FAIL ...") and exits non-zero on
+// any failure.
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+
+#include "lisa_resident.hpp"
+
+using namespace lisa;
+
+static int fails = 0;
+#define CHECK(cond, ...)                         \
+  do {                                           \
+    if (!(cond)) {                               \
+      if (fails < 20) {                          \
+        std::printf("FAIL %s: ", #cond);         \
+        std::printf(__VA_ARGS__);                \
+        std::printf("\n");                       \
+      }                                          \
+      ++fails;                                   \
+    }                                            \
+  } while (0)
+
+static void check(int H, int W, int T, int gcap) {
+  ResPlan p;
+  if (!res_plan(H, W, T, true, gcap, p)) {
+    std::printf("none %d %d %d %d\n", H, W, T, gcap);
+    return;
+  }
+  const int before = fails;
+  const ResLayout& L = p.L;
+  const int slots = p.nblk * 32;
+  CHECK(p.G >= 1 && p.G <= gcap, "G %d", p.G);
+  CHECK(p.nblk <= kResMaxBlocks, "nblk %d", p.nblk);
+  CHECK(L.total <= kResLdsMax, "lds %d", L.total);
+  // Regions in order, disjoint, and each large enough.
+  const int krows = L.zrow + 1;
+  CHECK(L.k == 0 && L.v >= L.k + krows * kResRowBytes, "k region");
+  // The combine stages its share of all G partials (nstat floats in all) there.
+  CHECK(L.v - L.k >= kResCombineFloats * 4, "k region holds the combine's staging (and the statistics' rows)");
+  CHECK(L.w >= L.v + krows * kResRowBytes && L.w >= L.v + slots * kResRowBytes, "v region");
+  CHECK(L.tab >= L.w + res_up(slots * T, 64) * 4, "w region");
+  CHECK(L.s >= L.tab + slots * 2, "tab region");
+  CHECK(L.scr >= L.s + 64 * 4, "s region");
+  CHECK(L.total >= L.scr + kResScratch && L.total >= L.scr + 2 * 64 * 64 * 2, "scr region");
+  CHECK(L.k % 1024 == 0 && L.v % 1024 == 0 && L.w % 256 == 0 && L.tab % 16 == 0 && L.s % 16 == 0 &&
+            L.scr % 16 == 0,
+        "alignment");
+  std::vector<int> owner((size_t)H * W, -1);
+  for (int g = 0; g < p.G; ++g) {
+    const ResTile t = res_tile(p, g);
+    CHECK(t.th >= 1 && t.tw >= 1, "empty tile %d", g);
+    const int cells = t.SR * t.SC;
+    CHECK(t.SR <= p.SR && t.SC <= p.SC && cells <= p.SR * p.SC, "staged %dx%d", t.SR, t.SC);
+    CHECK(t.sr0 >= 0 && t.sc0 >= 0 && t.sr0 + t.SR <= H && t.sc0 + t.SC <= W, "staged region off grid");
+    // DMA of the cells: whole 1 KB runs end before the zero row.
+    CHECK(res_up(cells, 8) <= L.zrow, "dma runs reach the zero row");
+    for (int s = 0; s < slots; ++s) {
+      int tr, tc;
+      const bool on = res_slot(p, t, s, tr, tc);
+      CHECK(tr >= 0 && tc >= 0 && tr < 4 * p.BR && tc < 8 * p.BC, "slot coordinates");
+      if (on) {
+        const int row = t.r0 + tr, col = t.c0 + tc;
+        CHECK(row < H && col < W, "slot off grid");
+        int& o = owner[(size_t)row * W + col];
+        CHECK(o == -1, "token %d,%d covered twice", row, col);
+        o = g;
+        // Every on-grid window cell is staged, at the right place.
+        for (int dr = -1; dr <= 1; ++dr)
+          for (int dc = -1; dc <= 1; ++dc) {
+            const int r2 = row + dr, c2 = col + dc;
+            if (r2 < 0 || r2 >= H || c2 < 0 || c2 >= W) continue;
+            CHECK(r2 >= t.sr0 && r2 < t.sr0 + t.SR && c2 >= t.sc0 && c2 < t.sc0 + t.SC,
+                  "neighbour %d,%d of %d,%d not staged", r2, c2, row, col);
+            CHECK(res_cell(t, r2, c2) == (r2 - t.sr0) * t.SC + (c2 - t.sc0), "cell index");
+          }
+      }
+      // The slot table's row and the block's window cells stay in the K / V regions.
+      const int tabrow = on ? res_cell(t, t.r0 + tr, t.c0 + tc) : L.zrow;
+      CHECK(tabrow >= 0 && tabrow <= L.zrow, "table row %d", tabrow);
+      const int blk = s >> 5, br = blk / p.BC, bc = blk % p.BC;
+      for (int c = 0; c < 64; ++c) {
+        const int cc = c < 59 ? c : 59;
+        const int wc = res_cell(t, t.r0 + 4 * br - 1 + cc / 10, t.c0 + 8 * bc - 1 + cc % 10);
+        CHECK(wc >= 0 && wc < cells, "window cell %d", wc);
+      }
+    }
+    // Weights: runs of 64 floats over slots * T values.
+    CHECK(res_up(slots * T, 64) * 4 <= L.tab - L.w, "weight runs");
+  }
+  for (int r = 0; r < H; ++r)
+    for (int c = 0; c < W; ++c) CHECK(owner[(size_t)r * W + c] >= 0, "token %d,%d uncovered", r, c);
+  // Combine ranges partition the statistics, for both sizes, and each rank's
+  // staging ([G][E] floats) fits the K region and its loads.
+  for (int nstat : {4096, 8192}) {
+    int next = 0;
+    for (int g = 0; g < p.G; ++g) {
+      int e0, e1;
+      res_combine_range(nstat, p.G, g, e0, e1);
+      CHECK(e0 == next && e1 >= e0, "combine range %d", g);
+      CHECK((e1 - e0) * p.G <= kResCombineFloats && (e1 - e0) * p.G * 4 <= L.v - L.k, "combine staging %d",
+            (e1 - e0) * p.G);
+      CHECK(e1 - e0 >= 16, "combine share %d", e1 - e0);  // the float quotient q / E stays exact
+      next = e1;
+    }
+    CHECK(next == nstat, "combine end %d", next);
+  }
+  if (fails == before)
+    std::printf("ok %d %d %d %d: G=%d tiles %dx%d of %dx%d, %d blocks, staged %dx%d, lds %d\n", H, W, T, gcap, p.G,
+                p.ty, p.tx, p.TR, p.TC, p.nblk, p.SR, p.SC, L.total);
+}
+
+int main(int argc, char** argv) {
+  for (int i = 1; i + 3 < argc; i += 4) check(std::atoi(argv[i]), std::atoi(argv[i + 1]), std::atoi(argv[i + 2]),
+                                                std::atoi(argv[i + 3]));
+  if (fails) std::printf("%d failures\n", fails);
+  return fails ? 1 : 0;
+}

@@ -28,7 +28,7 @@ def test_header_declares_the_entry_points():
         "lisa_apply", "lisa_attention_forward", "lisa_attention_workspace_size", "lisa_backward",
         "lisa_backward_after_forward",
         "lisa_backward_workspace_size", "lisa_forward", "lisa_forward_mlp", "lisa_forward_mlp_workspace_size",
-        "lisa_forward_noalloc",
+        "lisa_forward_noalloc", "lisa_forward_phases", "lisa_forward_schedule",
         "lisa_reduce", "lisa_status_str", "lisa_workspace_check", "lisa_workspace_size"]
 
 
@@ -44,7 +44,7 @@ def test_problem_struct_matches_header():
     body = hdr[hdr.index("typedef struct lisa_problem {"):hdr.index("} lisa_problem;")]
     names = re.findall(r"^\s*(?:int32_t|float)\s+(\w+);", body, re.M)
     assert names == [f[0] for f in lisa.Problem._fields_]
-    assert ctypes.sizeof(lisa.Problem) == 4 * len(names) == 40
+    assert ctypes.sizeof(lisa.Problem) == 4 * len(names) == 44
 
 
 def prob(**kw):
@@ -90,7 +90,7 @@ def test_forward_argument_errors(fn):
     for bad in (dict(d_h=32), dict(d_v=128), dict(batch=300, heads=300)):
         assert forward(prob(**bad), fn=f) == UNSUP, bad
     for bad in (dict(T=0), dict(T=17), dict(feature=2), dict(feature=-1), dict(eps=0.0), dict(eps=-1e-6), dict(eps=math.nan),
-                dict(eps=math.inf)):
+                dict(eps=math.inf), dict(schedule=3), dict(schedule=-1)):
         assert forward(prob(**bad), fn=f) == PARAM, bad
     for beta in (1.0, -0.1, math.nan):
         assert forward(prob(), w=None, beta=beta, fn=f) == PARAM
@@ -311,3 +311,13 @@ def test_forward_noalloc_argument_errors():
     assert call(prob(), y=Q) == PARAM
     # More (batch, head) slices than the fixed scratch's counters cover.
     assert call(prob(batch=8193, heads=1, grid_h=1, grid_w=1)) == lisa.LISA_ERR_SCRATCH
+
+
+def test_forward_schedule_argument_errors():
+    """lisa_forward_schedule checks the problem before it looks for a device."""
+    out = ctypes.c_int32(-1)
+    assert lib.lisa_forward_schedule(None, ctypes.byref(out)) == NULL
+    assert lib.lisa_forward_schedule(ctypes.byref(prob(schedule=3)), ctypes.byref(out)) == PARAM
+    assert lib.lisa_forward_schedule(ctypes.byref(prob(T=0)), ctypes.byref(out)) == PARAM
+    assert lib.lisa_forward_schedule(ctypes.byref(prob()), None) == NULL
+    assert out.value == -1

@@ -70,11 +70,34 @@ def check(y_gpu, y_ref, dtype, label):
     return rel
 
 
+SCHEDULES = ["streaming", "resident"]
+
+
+def gpu_y_sched(lisa, d, schedule, **kw):
+    """gpu_y on one kernel.  The resident kernel takes bf16 problems with at
+    most eight walk terms; it must refuse the others before enqueuing
+    anything, and may refuse a grid whose tiles do not fit a workgroup."""
+    if schedule == "resident" and (d["q"].dtype != torch.bfloat16 or d["T"] > 8):
+        with pytest.raises(lisa.LisaError) as e:
+            gpu_y(lisa, d, schedule=schedule, **kw)
+        assert e.value.status == lisa.LISA_ERR_UNSUPPORTED
+        return None
+    try:
+        return gpu_y(lisa, d, schedule=schedule, **kw)
+    except lisa.LisaError as e:
+        if schedule == "resident" and e.status == lisa.LISA_ERR_UNSUPPORTED:
+            pytest.skip("the resident kernel's tiles do not fit this grid")
+        raise
+
+
+@pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("name", list(workloads.WORKLOADS))
-def test_workload_parity(lisa, name):
+def test_workload_parity(lisa, name, schedule):
     w = workloads.get(name)
     x = workloads.make_inputs(w)
-    check(gpu_y(lisa, to_dev(x)), oracle_y(x), w.dtype, w.describe())
+    y = gpu_y_sched(lisa, to_dev(x), schedule)
+    if y is not None:
+        check(y, oracle_y(x), w.dtype, f"{w.describe()} {schedule}")
 
 
 RAGGED = [
@@ -108,13 +131,16 @@ RAGGED = [
 ]
 
 
+@pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("case", RAGGED, ids=[f"{c[0]}x{c[1]}_{c[2]}x{c[3]}_T{c[4]}_{c[5]}_{c[6]}" for c in RAGGED])
-def test_ragged_and_edge_shapes(lisa, case):
+def test_ragged_and_edge_shapes(lisa, case, schedule):
     B, heads, H, W, T, dtype, mode = case
     w = workloads.small("ragged", B, heads, H, W, T, dtype=dtype, mode=mode, beta=0.6,
                         seed=7 + H * 131 + W)
     x = workloads.make_inputs(w)
-    check(gpu_y(lisa, to_dev(x)), oracle_y(x), dtype, str(case))
+    y = gpu_y_sched(lisa, to_dev(x), schedule)
+    if y is not None:
+        check(y, oracle_y(x), dtype, f"{case} {schedule}")
 
 
 ELU = [
@@ -211,13 +237,16 @@ def test_alpha_isolates_branches(lisa, dtype):
         check(gpu_y(lisa, to_dev(x)), oracle_y(x), dtype, f"alpha={a} {dtype}")
 
 
-@pytest.mark.parametrize("name", ["tiny_oracle_14x14", "deit_t_224", "pvt_t_stage1", "long_range_200x320"])
-def test_statistics_stage(lisa, name):
+@pytest.mark.parametrize("name,schedule", [("tiny_oracle_14x14", "auto"), ("deit_t_224", "streaming"),
+                                           ("deit_t_224", "resident"), ("pvt_t_stage1", "streaming"),
+                                           ("pvt_t_stage1", "resident"), ("long_range_200x320", "streaming"),
+                                           ("long_range_200x320", "resident")])
+def test_statistics_stage(lisa, name, schedule):
     """lisa_reduce: s, phi(K)^T V and M against the oracle's statistics."""
     w = workloads.get(name)
     x = workloads.make_inputs(w)
     d = to_dev(x)
-    s, kv, m = lisa.lisa_reduce(d["q"], d["k"], d["v"], grid=(w.H, w.W), eps=w.eps, T=w.T)
+    s, kv, m = lisa.lisa_reduce(d["q"], d["k"], d["v"], grid=(w.H, w.W), eps=w.eps, T=w.T, schedule=schedule)
     torch.cuda.synchronize()
     q, k, v = f64(x["q"]), f64(x["k"]), f64(x["v"])
     tol_s = 1e-5
@@ -229,22 +258,63 @@ def test_statistics_stage(lisa, name):
             for j, (g, r) in enumerate(((s[b, h], rs), (kv[b, h], rkv), (m[b, h], rm))):
                 e = np.linalg.norm(f64(g) - r) / np.linalg.norm(r)
                 worst[j] = max(worst[j], e)
-    print(f"[parity] stats {name}: s={worst[0]:.2e} kv={worst[1]:.2e} m={worst[2]:.2e}", flush=True)
+    print(f"[parity] stats {name} {schedule}: s={worst[0]:.2e} kv={worst[1]:.2e} m={worst[2]:.2e}", flush=True)
     assert worst[0] <= tol_s and worst[1] <= tol_s and worst[2] <= tol_m
 
 
-def test_reduce_then_apply_equals_forward(lisa):
-    w = workloads.get("pvt_t_stage1")
+@pytest.mark.parametrize("schedule", SCHEDULES)
+@pytest.mark.parametrize("name", ["pvt_t_stage1", "deit_t_224", "long_range_200x320"])
+def test_reduce_then_apply_equals_forward(lisa, name, schedule):
+    w = workloads.get(name)
     d = to_dev(workloads.make_inputs(w))
-    y1 = gpu_y(lisa, d)
-    prob = lisa.make_problem(d["q"], d["v"], grid=(w.H, w.W), T=w.T, eps=w.eps)
+    y1 = gpu_y(lisa, d, schedule=schedule)
+    prob = lisa.make_problem(d["q"], d["v"], grid=(w.H, w.W), T=w.T, eps=w.eps, schedule=schedule)
     ws = lisa.new_workspace(prob, d["q"].device)
     lisa.lisa_reduce(d["q"], d["k"], d["v"], grid=(w.H, w.W), eps=w.eps, T=w.T, workspace=ws,
-                     outputs=False)
+                     outputs=False, schedule=schedule)
     y2 = lisa.lisa_apply(d["q"], d["k"], d["v"], grid=(w.H, w.W), T=w.T, alpha=d["alpha"],
-                         weights=d["weights"], eps=w.eps, workspace=ws)
+                         weights=d["weights"], eps=w.eps, workspace=ws, schedule=schedule)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+def test_auto_schedule_runs_the_kernel_it_reports(lisa):
+    """The default runs the kernel lisa_forward_schedule names: its output
+    equals that kernel's bit for bit (the two kernels sum in different
+    orders)."""
+    for name in ("pvt_t_stage1", "deit_t_224", "long_range_200x320", "tiny_oracle_14x14"):
+        w = workloads.get(name)
+        d = to_dev(workloads.make_inputs(w))
+        kind = lisa.lisa_forward_schedule(lisa.make_problem(d["q"], d["v"], grid=(w.H, w.W), T=w.T, eps=w.eps))
+        assert kind in ("streaming", "resident")
+        if w.dtype == "fp32":
+            assert kind == "streaming"
+        assert torch.equal(gpu_y(lisa, d), gpu_y(lisa, d, schedule=kind)), name
+    prob = lisa.make_problem(d["q"], d["v"], grid=(w.H, w.W), T=w.T, eps=w.eps, schedule="resident")
+    with pytest.raises(lisa.LisaError) as e:
+        lisa.lisa_forward_schedule(prob)  # fp32: not the resident kernel's
+    assert e.value.status == lisa.LISA_ERR_UNSUPPORTED
+
+
+def test_phases_timeline_is_ordered(lisa):
+    """lisa_forward_phases: the same Y as the resident kernel's lisa_forward,
+    and each workgroup's stages in order of time."""
+    for name in ("pvt_t_stage1", "deit_t_224", "long_range_200x320"):
+        w = workloads.get(name)
+        d = to_dev(workloads.make_inputs(w))
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        stamps = torch.full((cus * lisa.LISA_PHASES,), -1, dtype=torch.int64, device="cuda")
+        y = lisa.lisa_forward_phases(d["q"], d["k"], d["v"], grid=(w.H, w.W), T=w.T, alpha=d["alpha"],
+                                     stamps=stamps, weights=d["weights"], eps=w.eps)
+        torch.cuda.synchronize()
+        assert torch.equal(y, gpu_y(lisa, d, schedule="resident")), name
+        st = stamps.view(cus, lisa.LISA_PHASES).cpu().numpy()
+        order = ["start", "staged", "kvsweep", "kv", "local", "m", "out", "end"]
+        idx = [lisa.STAGES.index(k) for k in order]
+        working = st[:, lisa.STAGES.index("staged")] >= 0  # workgroups with a slice
+        assert working.any(), name
+        seq = st[working][:, idx]
+        assert np.all(np.diff(seq, axis=1) >= 0), name
 
 
 def test_deterministic_and_workspace_reuse(lisa):

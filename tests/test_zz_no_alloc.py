@@ -28,22 +28,24 @@ def dev(x):
     return {k: (x[k].cuda() if isinstance(x[k], torch.Tensor) else x[k]) for k in x}
 
 
-def both(lisa, w, x):
+def both(lisa, w, x, schedule="auto"):
     d = dev(x)
-    kw = dict(grid=(w.H, w.W), T=w.T, alpha=d["alpha"], weights=d["weights"], beta=d["beta"], eps=w.eps)
+    kw = dict(grid=(w.H, w.W), T=w.T, alpha=d["alpha"], weights=d["weights"], beta=d["beta"], eps=w.eps,
+              schedule=schedule)
     y_ws = lisa.lisa_forward(d["q"], d["k"], d["v"], **kw)
     y_na = lisa.lisa_forward_noalloc(d["q"], d["k"], d["v"], **kw)
     torch.cuda.synchronize()
     return y_ws, y_na
 
 
-def test_noalloc_equals_forward_on_two_calls(lisa):
+@pytest.mark.parametrize("schedule", ["auto", "streaming", "resident"])
+def test_noalloc_equals_forward_on_two_calls(lisa, schedule):
     cases = [workloads.get("pvt_t_stage1"),
              workloads.small("noalloc-small", 2, 3, 13, 17, 4, dtype="bf16", seed=61)]
     for w in cases:
         x = workloads.make_inputs(w)
-        y_ws, y_na = both(lisa, w, x)
-        print(f"[noalloc] {w.describe()}: equal={torch.equal(y_ws, y_na)}", flush=True)
+        y_ws, y_na = both(lisa, w, x, schedule)
+        print(f"[noalloc] {w.describe()} {schedule}: equal={torch.equal(y_ws, y_na)}", flush=True)
         assert torch.isfinite(y_na.float()).all()
         assert torch.equal(y_ws, y_na), w.describe()
 

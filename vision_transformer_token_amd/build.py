@@ -10,7 +10,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", f) for f in ("lisa_flow.hip", "lisa_backward.hip", "lisa_layer.hip", "lisa_api.hip")]
+SOURCES = [os.path.join(PKG, "csrc", f) for f in ("lisa_flow.hip", "lisa_resident.hip", "lisa_backward.hip", "lisa_layer.hip", "lisa_api.hip")]
 LIB = os.path.join(PKG, "liblisa.so")
 
 HIPCC_FLAGS = [

@@ -55,7 +55,7 @@ constexpr size_t kMaxSlices = 65535;  // batch * heads limit
 size_t up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Plan {
-  int BH = 0, n = 0, H = 0, W = 0, T = 0, dtype = 0, heads = 0, feature = 0;
+  int BH = 0, n = 0, H = 0, W = 0, T = 0, dtype = 0, heads = 0, feature = 0, schedule = 0;
   size_t esize = 0;
   int gmax = 1;                                  // ranks per slice the partials are sized for
   int grid = 0;                                  // workgroups (one per compute unit)
@@ -82,6 +82,9 @@ lisa_status check_problem(const lisa_problem* p) {
   if (p->T < 1 || p->T > lisa::kMaxT) return LISA_ERR_PARAM;
   if (!std::isfinite(p->eps) || !(p->eps > 0.f)) return LISA_ERR_PARAM;
   if (p->feature != LISA_FEATURE_RELU && p->feature != LISA_FEATURE_ELU) return LISA_ERR_PARAM;
+  if (p->schedule != LISA_SCHEDULE_AUTO && p->schedule != LISA_SCHEDULE_STREAMING &&
+      p->schedule != LISA_SCHEDULE_RESIDENT)
+    return LISA_ERR_PARAM;
   return LISA_OK;
 }
 
@@ -182,6 +185,7 @@ lisa_status make_plan(const lisa_problem* p, Plan& pl) {
   pl.T = p->T;
   pl.dtype = p->dtype;
   pl.feature = p->feature;
+  pl.schedule = p->schedule;
   pl.esize = p->dtype == LISA_BF16 ? 2 : 4;
   // The partials are sized for the most ranks any grid can give a slice
   // (the launch picks G <= gmax from the device's compute units).
@@ -248,11 +252,88 @@ lisa_status check_forward(const lisa_problem* p, const void* Q, const void* K, c
 
 enum class Mode { kForward, kReduce, kApply };
 
+// Whether the resident kernel takes the problem, and its tiling: bf16 inputs,
+// ReLU features, no predictor, at most kResMaxT walk terms, and a tiling
+// whose tiles fit a workgroup (res_plan).  Ranks per slice: at most the
+// compute units per slice, and at most the workspace's partials (one rank per
+// 128 tokens).  The tiling does not depend on the weights or on the call
+// (the weight region is always laid out), so lisa_forward, lisa_reduce,
+// lisa_apply and the backward's statistics of one problem all cut the slices
+// the same way and form the same fixed-order sums.
+bool resident_fits(const Plan& pl, int cus, bool mlp, lisa::ResPlan& rp) {
+  if (pl.dtype != LISA_BF16 || pl.feature != LISA_FEATURE_RELU || mlp || pl.T > lisa::kResMaxT) return false;
+  const int gcap = std::min(std::max(1, cus / pl.BH), plan_ranks(lisa::kMaxRanks, kRoundSlices, pl.n));
+  return lisa::res_plan(pl.H, pl.W, pl.T, true, gcap, rp);
+}
+
+// The default between the two kernels where both apply.  Measured on MI355X
+// (256 CUs, bf16, T = 3 or 5): where a slice has one rank the two are even
+// (DeiT-T at 224, 192 slices of 14 x 14: 37.4 against 37.2 us); with several
+// ranks per slice the resident kernel's serial stages still cost more than
+// the streaming kernel's overlapped ones (PVT-T stage 1, 32 slices of
+// 56 x 56 on eight ranks each: 52 against 47 us; one 200 x 320 slice: 61
+// against 51 us).
+bool resident_preferred(const lisa::ResPlan& rp) { return rp.G == 1; }
+
+// Whether the resident kernel runs the problem: where it fits, when asked
+// for, and by default where it is the faster of the two kernels.
+bool resident_plan(const Plan& pl, int cus, bool mlp, lisa::ResPlan& rp) {
+  if (pl.schedule == LISA_SCHEDULE_STREAMING || !resident_fits(pl, cus, mlp, rp)) return false;
+  if (pl.schedule == LISA_SCHEDULE_RESIDENT) return true;
+  return resident_preferred(rp);
+}
+
+// One launch of the resident kernel, one workgroup per compute unit.
+lisa_status run_resident(const Plan& pl, const lisa::ResPlan& rp, int cus, Mode mode, const void* Q, const void* K,
+                         const void* V, const float* weights, float beta, const float* alpha, void* Y, char* ws,
+                         float eps, hipStream_t s, bool clear_err, unsigned long long* stamps = nullptr) {
+  lisa::ResArgs a{};
+  a.stamps = stamps;
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.weights = weights;
+  a.alpha = alpha;
+  a.Y = Y;
+  const double b = weights ? 0.0 : (double)beta;
+  const double norm = (1.0 - b) / (1.0 - std::pow(b, pl.T));
+  for (int k = 0; k < lisa::kMaxT; ++k) a.geo[k] = k < pl.T ? (float)(norm * std::pow(b, k)) : 0.f;
+  a.n = pl.n;
+  a.heads = pl.heads;
+  a.BH = pl.BH;
+  a.eps = eps;
+  a.logit_scale = (float)(1.4426950408889634 / std::sqrt((double)kD));
+  a.p = rp;
+  a.S = cus / rp.G;
+  a.xcd_groups = 0;
+  a.mode = mode == Mode::kForward ? lisa::kResForward : mode == Mode::kReduce ? lisa::kResReduce : lisa::kResApply;
+  a.do_kv = (mode == Mode::kReduce || (mode == Mode::kForward && pl.T >= 2)) ? 1 : 0;
+  a.do_m = (mode == Mode::kReduce || (mode == Mode::kForward && pl.T >= 3)) ? 1 : 0;
+  a.per_token = weights != nullptr ? 1 : 0;
+  a.grouped = (rp.G >= 64 && pl.BH <= lisa::kMaxSubSlices) ? 1 : 0;
+  a.part_s = reinterpret_cast<float*>(ws + pl.part_s);
+  a.part_kv = reinterpret_cast<float*>(ws + pl.part_kv);
+  a.part_m = reinterpret_cast<float*>(ws + pl.part_m);
+  a.fin_s = reinterpret_cast<float*>(ws + pl.fin_s);
+  a.fin_kv = reinterpret_cast<float*>(ws + pl.fin_kv);
+  a.fin_m = reinterpret_cast<float*>(ws + pl.fin_m);
+  a.frag_kv = ws + pl.frag_kv;
+  a.frag_m = ws + pl.frag_m;
+  a.slice_cnt = reinterpret_cast<unsigned*>(ws + pl.slice_cnt);
+  a.sub_cnt = reinterpret_cast<unsigned*>(ws + pl.sub_cnt);
+  a.done_cnt = reinterpret_cast<unsigned*>(ws + pl.done_cnt);
+  a.err = a.done_cnt + 1;
+  a.tickets = a.done_cnt + 8;
+  a.clear_err = clear_err ? 1 : 0;
+  if (lisa::launch_resident(a, cus, s) != hipSuccess) return LISA_ERR_HIP;
+  return LISA_OK;
+}
+
 // One launch of the persistent kernel, one workgroup per compute unit.
 lisa_status run(Plan pl, Mode mode, const void* Q, const void* K, const void* V,
                 const float* weights, float beta, const float* alpha, void* Y, char* ws, float eps,
                 hipStream_t s, const lisa_weight_mlp* mlp = nullptr, const void* mlp_frag = nullptr,
-                bool clear_err = false) {
+                bool clear_err = false, unsigned long long* stamps = nullptr) {
   lisa::FlowArgs a{};
   a.clear_err = clear_err ? 1 : 0;
   if (mlp) {
@@ -280,10 +361,17 @@ lisa_status run(Plan pl, Mode mode, const void* Q, const void* K, const void* V,
   a.BH = pl.BH;
   a.eps = eps;
   a.logit_scale = (float)(1.4426950408889634 / std::sqrt((double)kD));
-  if (!plan_tiles(pl, weights != nullptr || mlp != nullptr)) return LISA_ERR_UNSUPPORTED;
   // One persistent workgroup per compute unit.
   DeviceInfo dinfo;
   if (!device_info(dinfo)) return LISA_ERR_HIP;
+  lisa::ResPlan rp;
+  if (resident_plan(pl, dinfo.cus, mlp != nullptr, rp))
+    return run_resident(pl, rp, dinfo.cus, mode, Q, K, V, weights, beta, alpha, Y, ws, eps, s, clear_err, stamps);
+  // The resident kernel asked for and not applicable (the predictor's output
+  // pass after a resident reduce is the streaming kernel's by design).
+  if (pl.schedule == LISA_SCHEDULE_RESIDENT && !mlp) return LISA_ERR_UNSUPPORTED;
+  if (stamps) return LISA_ERR_UNSUPPORTED;  // the stage timeline is the resident kernel's
+  if (!plan_tiles(pl, weights != nullptr || mlp != nullptr)) return LISA_ERR_UNSUPPORTED;
   pl.grid = dinfo.cus;
   pl.G = plan_ranks(pl.grid, pl.BH, pl.n);
   if (pl.G > pl.gmax) pl.G = pl.gmax;
@@ -383,6 +471,23 @@ size_t lisa_workspace_size(const lisa_problem* p) {
   return make_plan(p, pl) == LISA_OK ? pl.total : 0;
 }
 
+lisa_status lisa_forward_schedule(const lisa_problem* p, int32_t* schedule) {
+  Plan pl;
+  const lisa_status st = make_plan(p, pl);
+  if (st != LISA_OK) return st;
+  if (!schedule) return LISA_ERR_NULL;
+  DeviceInfo dinfo;
+  if (!device_info(dinfo)) return LISA_ERR_HIP;
+  lisa::ResPlan rp;
+  if (resident_plan(pl, dinfo.cus, false, rp)) {
+    *schedule = LISA_SCHEDULE_RESIDENT;
+    return LISA_OK;
+  }
+  if (pl.schedule == LISA_SCHEDULE_RESIDENT) return LISA_ERR_UNSUPPORTED;
+  *schedule = LISA_SCHEDULE_STREAMING;
+  return LISA_OK;
+}
+
 lisa_status lisa_forward(const lisa_problem* p, const void* Q, const void* K, const void* V,
                          const float* weights, float beta, const float* alpha, void* Y,
                          void* workspace, size_t workspace_bytes, void* stream) {
@@ -392,6 +497,29 @@ lisa_status lisa_forward(const lisa_problem* p, const void* Q, const void* K, co
   (void)hipGetLastError();  // clear a stale error so that ours are reported alone
   return run(pl, Mode::kForward, Q, K, V, weights, beta, alpha, Y, static_cast<char*>(workspace),
              p->eps, static_cast<hipStream_t>(stream));
+}
+
+lisa_status lisa_forward_phases(const lisa_problem* p, const void* Q, const void* K, const void* V,
+                                const float* weights, float beta, const float* alpha, void* Y, void* workspace,
+                                size_t workspace_bytes, uint64_t* stamps, size_t stamps_count, void* stream) {
+  Plan pl;
+  const lisa_status st = check_forward(p, Q, K, V, weights, beta, alpha, Y, workspace, workspace_bytes, pl);
+  if (st != LISA_OK) return st;
+  if (!stamps) return LISA_ERR_NULL;
+  if (misaligned(stamps, 8)) return LISA_ERR_ALIGN;
+  (void)hipGetLastError();
+  DeviceInfo dinfo;
+  if (!device_info(dinfo)) return LISA_ERR_HIP;
+  if (stamps_count < (size_t)dinfo.cus * LISA_PHASES) return LISA_ERR_PARAM;
+  // The timeline is the resident kernel's: it runs wherever it fits.
+  if (pl.schedule == LISA_SCHEDULE_STREAMING) return LISA_ERR_UNSUPPORTED;
+  pl.schedule = LISA_SCHEDULE_RESIDENT;
+  lisa::ResPlan rp;
+  if (!resident_plan(pl, dinfo.cus, false, rp)) return LISA_ERR_UNSUPPORTED;
+  static_assert(LISA_PHASES == lisa::kResPhases, "stage count");
+  return run(pl, Mode::kForward, Q, K, V, weights, beta, alpha, Y, static_cast<char*>(workspace), p->eps,
+             static_cast<hipStream_t>(stream), nullptr, nullptr, false,
+             reinterpret_cast<unsigned long long*>(stamps));
 }
 
 lisa_status lisa_forward_noalloc(const lisa_problem* p, const void* Q, const void* K, const void* V,
@@ -413,7 +541,8 @@ lisa_status lisa_forward_noalloc(const lisa_problem* p, const void* Q, const voi
   // (run() picks the same number), not for the most any device could.
   DeviceInfo dinfo;
   if (!device_info(dinfo)) return LISA_ERR_HIP;
-  pl.gmax = plan_ranks(dinfo.cus, pl.BH, pl.n);
+  lisa::ResPlan rp;
+  pl.gmax = resident_plan(pl, dinfo.cus, false, rp) ? rp.G : plan_ranks(dinfo.cus, pl.BH, pl.n);
   if (layout_forward(pl, kScratchSlices) > kScratchBytes) return LISA_ERR_SCRATCH;
   char* base = nullptr;
   st = scratch_address(&base);
@@ -494,6 +623,20 @@ lisa_status lisa_forward_mlp(const lisa_problem* p, const void* Q, const void* K
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (lisa::launch_mlp_prep(pl.dtype, mlp->w1, ws + frag_at, pl.heads, mlp->hidden, s) != hipSuccess)
     return LISA_ERR_HIP;
+  // Where the resident kernel forms this problem's statistics for the other
+  // entry points, it forms them here too (the statistics alone), and the
+  // predictor's output pass reads them from the workspace: the statistics a
+  // backward pass may take over are then those lisa_backward forms.
+  DeviceInfo dinfo;
+  if (!device_info(dinfo)) return LISA_ERR_HIP;
+  lisa::ResPlan rp;
+  const bool resident = pl.T >= 2 && resident_plan(pl, dinfo.cus, false, rp);
+  if (pl.schedule == LISA_SCHEDULE_RESIDENT && !resident) return LISA_ERR_UNSUPPORTED;
+  if (resident) {
+    st = run(pl, Mode::kReduce, Q, K, V, nullptr, 0.f, nullptr, nullptr, ws, p->eps, s);
+    if (st != LISA_OK) return st;
+    return run(pl, Mode::kApply, Q, K, V, nullptr, 0.f, alpha, Y, ws, p->eps, s, mlp, ws + frag_at);
+  }
   return run(pl, Mode::kForward, Q, K, V, nullptr, 0.f, alpha, Y, ws, p->eps, s, mlp, ws + frag_at);
 }
 

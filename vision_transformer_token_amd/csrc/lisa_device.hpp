@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "lisa_kernels.hpp"
+
 namespace lisa {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
@@ -171,6 +173,9 @@ __device__ __forceinline__ void dma16_coherent(const void* g, unsigned m0) {
 }
 __device__ __forceinline__ void dma4(const void* g, unsigned m0) {
   asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(m0) : "memory");
+}
+__device__ __forceinline__ void dma4_coherent(const void* g, unsigned m0) {
+  asm volatile("global_load_lds_dword %0, off sc1" ::"v"(g), "{m0}"(m0) : "memory");
 }
 
 // DMA `nrow` rows into `lds` (a multiple of 1 KB is written: the last run is
@@ -347,5 +352,114 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ unsigned bump(unsigned* cnt) {
   return __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// ---------------------------------------------------------------------------
+// Dependency waits between the workgroups of one launch.
+// ---------------------------------------------------------------------------
+// Spin (one lane) until *c >= target.  The wait is bounded (about a second);
+// on giving up it raises the error word, after which every later wait of the
+// launch returns at once, so the launch always finishes.
+__device__ inline void wait_for(const unsigned* c, unsigned target, unsigned* err) {
+  unsigned spins = 0;
+  // About 0.27 us between polls: every poll is a device-wide load of the
+  // line the arrivals update, and with hundreds of workgroups polling one
+  // slice (one long sequence) denser polling slows the arrivals themselves.
+  while (get(c) < target) {
+    __builtin_amdgcn_s_sleep(10);
+    if ((++spins & 255u) == 0 && get(err)) break;
+    if (spins > (1u << 21)) {
+      put(err, 1u);
+      break;
+    }
+  }
+  // The data the count announces is read only after this point: the
+  // compiler may not move those (relaxed) loads above the poll.
+  asm volatile("" ::: "memory");
+}
+
+// The same wait for a phase counted per group of kSubRanks ranks: lane k of
+// the calling wave (all 64 lanes call) reads group k's counter, until every
+// group's counter has reached kSubRanks; bounded like wait_for.
+__device__ inline void wait_for_groups(const unsigned* base, int ngroups, unsigned* err) {
+  const int lane = threadIdx.x & 63;
+  const unsigned* c = base + (size_t)min(lane, ngroups - 1) * kCntStride;
+  unsigned spins = 0;
+  for (;;) {
+    const bool done = lane >= ngroups || get(c) >= (unsigned)kSubRanks;
+    if (__all(done)) break;
+    __builtin_amdgcn_s_sleep(10);
+    ++spins;
+    if ((spins & 255u) == 0 && __builtin_amdgcn_readfirstlane(get(err))) break;
+    if (spins > (1u << 21)) {
+      if (lane == 0) put(err, 1u);
+      break;
+    }
+  }
+  asm volatile("" ::: "memory");  // as in wait_for
+}
+
+// ---------------------------------------------------------------------------
+// The 3x3 local branch on MFMA works on blocks of 4 x 8 tokens, whose windows
+// lie in a 6 x 10 window of cells; these map the MFMA's logit slots to cells.
+// ---------------------------------------------------------------------------
+// Window slots of the MFMA local branch: logit slot v (0..31) of lane half h
+// holds window cell c = 32 (v >> 4) + 8 ((v & 15) >> 2) + (v & 3) + 4 h of
+// the block's 6x10 window (cells 60..63 are padding).
+__host__ __device__ constexpr int slot_cell(int v, int h) {
+  return 32 * (v >> 4) + 8 * ((v & 15) >> 2) + (v & 3) + 4 * h;
+}
+// Slots of half h whose cell lies in window row wr / window column wc.
+__host__ __device__ constexpr unsigned row_slots(int h, int wr) {
+  unsigned m = 0;
+  for (int v = 0; v < 32; ++v)
+    if (slot_cell(v, h) < 60 && slot_cell(v, h) / 10 == wr) m |= 1u << v;
+  return m;
+}
+__host__ __device__ constexpr unsigned col_slots(int h, int wc) {
+  unsigned m = 0;
+  for (int v = 0; v < 32; ++v)
+    if (slot_cell(v, h) < 60 && slot_cell(v, h) % 10 == wc) m |= 1u << v;
+  return m;
+}
+
+// Slots that hold the 3x3 neighbourhood of block token (ta, tb) (window
+// rows ta..ta+2, columns tb..tb+2) for lane half h.
+__device__ __forceinline__ unsigned neighbour_slots(int ta, int tb, int h) {
+  unsigned r0 = 0, r1 = 0, k0 = 0, k1 = 0;
+#pragma unroll
+  for (int wr = 0; wr < 6; ++wr)
+    if ((unsigned)(wr - ta) <= 2u) {
+      r0 |= row_slots(0, wr);
+      r1 |= row_slots(1, wr);
+    }
+#pragma unroll
+  for (int wc = 0; wc < 10; ++wc)
+    if ((unsigned)(wc - tb) <= 2u) {
+      k0 |= col_slots(0, wc);
+      k1 |= col_slots(1, wc);
+    }
+  return h ? (r1 & k1) : (r0 & k0);
+}
+
+// Slots whose cell lies on the grid, from the window's on-grid rows and
+// columns (bit masks, wave-uniform).
+__device__ __forceinline__ unsigned grid_slots(unsigned rowbits, unsigned colbits, int h) {
+  if (rowbits == 0x3fu && colbits == 0x3ffu) return ~0u;
+  unsigned r0 = 0, r1 = 0, k0 = 0, k1 = 0;
+#pragma unroll
+  for (int wr = 0; wr < 6; ++wr)
+    if ((rowbits >> wr) & 1u) {
+      r0 |= row_slots(0, wr);
+      r1 |= row_slots(1, wr);
+    }
+#pragma unroll
+  for (int wc = 0; wc < 10; ++wc)
+    if ((colbits >> wc) & 1u) {
+      k0 |= col_slots(0, wc);
+      k1 |= col_slots(1, wc);
+    }
+  return h ? (r1 & k1) : (r0 & k0);
+}
+
 
 }  // namespace lisa

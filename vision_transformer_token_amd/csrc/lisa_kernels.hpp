@@ -7,6 +7,8 @@
 
 #include <atomic>
 
+#include "lisa_resident.hpp"
+
 namespace lisa {
 
 // A kernel's limit on dynamic LDS beyond 64 KB, set once per device: the
@@ -144,6 +146,69 @@ struct FlowArgs {
 };
 
 constexpr int kMaxHidden = 128;
+
+// The resident forward kernel (lisa_resident.hip): one tile of a slice per
+// rank, staged on chip once (ResPlan).  Modes: the whole forward, the
+// statistics alone (lisa_reduce), the output alone from statistics in the
+// workspace (lisa_apply).
+enum { kResForward = 0, kResReduce = 1, kResApply = 2 };
+struct ResArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const float* weights;   // [BH][n][T] or nullptr (geometric: geo)
+  const float* alpha;     // [heads]
+  void* Y;
+  float geo[kMaxT];
+  int n, heads, BH;
+  float eps;
+  float logit_scale;      // log2(e) / sqrt(d_h)
+  int S;                  // groups of G ranks
+  int xcd_groups;         // a group's ranks on one XCD (tickets per XCD)
+  int mode;
+  int do_kv, do_m;        // statistics formed by this launch
+  int per_token;          // weights per token (LDS region [slot][T]) instead of geo
+  int grouped;            // arrivals counted per group of kSubRanks ranks (sub_cnt)
+  ResPlan p;
+  float* part_s;          // [BH][G][64]
+  float* part_kv;         // [BH][G][64*64]
+  float* part_m;          // [BH][G][64*64]
+  float* fin_s;           // [BH][64]
+  float* fin_kv;          // [BH][64*64]
+  float* fin_m;           // [BH][64*64]
+  void* frag_kv;          // [BH][64*64] bf16, MFMA A-operand fragment order
+  void* frag_m;
+  unsigned* slice_cnt;    // [BH][kCntStride]
+  unsigned* sub_cnt;      // [kMaxSubSlices][3][kMaxSubs][kCntStride]
+  unsigned* done_cnt;
+  unsigned* tickets;      // [kXcds]
+  unsigned* err;
+  int clear_err;
+  // Optional stage timeline: workgroup w writes the constant-clock counter
+  // (s_memrealtime, 100 MHz) at stage k of its first slice to
+  // stamps[w * kResPhases + k] (kResStamp*), and its group and rank to the
+  // last entry.
+  unsigned long long* stamps;
+};
+enum {
+  kResStampStart = 0,   // ticket taken
+  kResStampStaged,      // K, V cells, weights and Q landed
+  kResStampKV,          // KV partial published
+  kResStampLocal,       // local branch done
+  kResStampS,           // every KV partial arrived, s formed
+  kResStampM,           // M partial published
+  kResStampMWait,       // every M partial arrived
+  kResStampComb,        // share of the statistics written
+  kResStampCWait,       // every share arrived
+  kResStampFrags,       // statistics fragments in LDS
+  kResStampOut,         // Y written
+  kResStampEnd,         // last barrier of the workgroup
+  kResStampKVSweep,     // products of the KV sweep done (before the partial is published)
+  kResStampCStaged,     // the combine's share of every rank's partial in LDS
+  kResStampCSummed,     // the combine's share summed
+  kResPhases = 16
+};
+hipError_t launch_resident(const ResArgs& a, int grid, hipStream_t s);
 
 // dtype: 0 = fp32, 1 = bf16 (lisa_dtype).  grid = workgroups to launch.
 hipError_t launch_flow(int dtype, const FlowArgs& a, int grid, hipStream_t s);

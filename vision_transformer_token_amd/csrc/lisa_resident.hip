@@ -1,0 +1,831 @@
+// The LiSA forward pass on gfx950 with every rank's tile resident on chip.
+//
+// Method: reading note "LiSA:面向长程视觉建模的线性随机注意力" (arXiv:2611.04216v2),
+// §2.1-§2.4.  Per (batch, head) slice with n tokens of width 64:
+//   statistics (Eq. 8): s = sum_j phi(K_j), phi(K)^T V, M = phi(K)^T Qt with
+//     Qt_j = r_j phi(Q_j), r_j = 1 / (phi(Q_j) . s + eps), phi = ReLU;
+//   global branch: G_i = w_0(i) V_i + r_i sum_{k=1}^{T-1} w_k(i) (phi(Q_i) M^(k-1)) (phi(K)^T V);
+//   local branch: L_i = softmax over the clipped 3x3 window of q_i . k_j / sqrt(d_h), times V;
+//   Y_i = alpha G_i + (1 - alpha) L_i.
+//
+// Schedule (lisa_resident.hpp): the G ranks of a group cut each slice into G
+// tiles.  A rank stages its tile's K and V cells (with a one-cell halo) in LDS
+// and its tokens' Q in registers once, then, with no further input reads:
+//   KV sweep over its tokens -> partial of s and phi(K)^T V, published;
+//   local branch of its tokens and the walk's k = 0 term, kept in registers
+//     (this runs while the other ranks' partials arrive);
+//   after all KV partials: s, r_i, Qt rows written over the V cells, M sweep
+//     over its tokens -> partial of M, published;
+//   after all M partials: its share of the fixed-order sum of the partials
+//     (statistics as fp32 and as MFMA fragments), published;
+//   after all shares: the walk of its tokens on MFMA, Y written once.
+// All four waves (one per SIMD, 512 registers each) do every step; waits on
+// other ranks are polled by one wave while the others sit at the workgroup
+// barrier.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "lisa_device.hpp"
+#include "lisa_kernels.hpp"
+#include "lisa_resident.hpp"
+
+namespace lisa {
+namespace {
+
+enum ResCounter { kRcKV = 0, kRcM = 1, kRcC = 2 };
+constexpr int kFragBytes = kD * kD * 2;  // one 64 x 64 matrix as bf16 MFMA fragments
+
+struct ResRank {
+  int group, g;  // group (-1: idle workgroup), rank within the group (= tile of the slice)
+};
+
+// Ranks are handed out in the order workgroups start (a ticket per XCD when
+// groups stay within an XCD), so a group only ever waits for workgroups that
+// are already running.
+__device__ __forceinline__ ResRank res_rank(const ResArgs& a, int ticket) {
+  ResRank r;
+  const int G = a.p.G;
+  if (a.xcd_groups) {
+    const int per = a.S / kXcds;
+    r.group = ticket / G < per ? (int)(blockIdx.x % kXcds) * per + ticket / G : -1;
+  } else {
+    r.group = ticket / G < a.S ? ticket / G : -1;
+  }
+  r.g = ticket % G;
+  return r;
+}
+
+// One of two base pointers by a per-lane choice.  Both values are first
+// pinned in scalar registers: left to itself the compiler selects between the
+// two fields of the argument block and re-reads the pointer from memory, a
+// full memory round trip, at every use.
+template <class P>
+__device__ __forceinline__ P* pick(P* p0, P* p1, bool second) {
+  uint64_t x0 = reinterpret_cast<uint64_t>(p0), x1 = reinterpret_cast<uint64_t>(p1);
+  asm volatile("" : "+s"(x0), "+s"(x1));
+  return reinterpret_cast<P*>(second ? x1 : x0);
+}
+
+// Stage timeline (ResArgs::stamps): thread 0 of the workgroup, first slice only.
+__device__ __forceinline__ void res_stamp(const ResArgs& a, bool first, int k) {
+  if (a.stamps && first && threadIdx.x == 0)
+    a.stamps[(size_t)blockIdx.x * kResPhases + k] = __builtin_amdgcn_s_memrealtime();
+}
+
+__device__ __forceinline__ unsigned* res_counter(const ResArgs& a, int b, int g, int c) {
+  if (a.grouped) return a.sub_cnt + (((size_t)b * 3 + c) * kMaxSubs + g / kSubRanks) * kCntStride;
+  return a.slice_cnt + (size_t)b * kCntStride + c;
+}
+
+// This rank's arrival on counter c of slice b, once every wave's stores have
+// completed (each wave waits for its own, then the workgroup meets).
+__device__ void res_arrive(const ResArgs& a, int b, int g, int c) {
+  wait_all();
+  __syncthreads();
+  if (threadIdx.x == 0) (void)bump(res_counter(a, b, g, c));
+}
+
+// Wait until all G ranks of slice b have arrived on counter c: wave 0 polls
+// (lane k reads group k's counter when arrivals are counted per group of
+// kSubRanks ranks), the other waves wait at the barrier.  Bounded like
+// wait_for: giving up raises the error word.
+__device__ void res_wait(const ResArgs& a, int b, int c) {
+  if (threadIdx.x < 64) {
+    if (a.grouped) {
+      const int lane = threadIdx.x, ng = res_cdiv(a.p.G, kSubRanks), k = min(lane, ng - 1);
+      const unsigned* cnt = a.sub_cnt + (((size_t)b * 3 + c) * kMaxSubs + k) * kCntStride;
+      const unsigned target = (unsigned)min(kSubRanks, a.p.G - kSubRanks * k);
+      unsigned spins = 0;
+      for (;;) {
+        const bool done = lane >= ng || get(cnt) >= target;
+        if (__all(done)) break;
+        __builtin_amdgcn_s_sleep(10);
+        ++spins;
+        if ((spins & 255u) == 0 && __builtin_amdgcn_readfirstlane(get(a.err))) break;
+        if (spins > (1u << 21)) {
+          if (lane == 0) put(a.err, 1u);
+          break;
+        }
+      }
+      asm volatile("" ::: "memory");
+    } else if (threadIdx.x == 0) {
+      wait_for(a.slice_cnt + (size_t)b * kCntStride + c, (unsigned)a.p.G, a.err);
+    }
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Staging.
+// ---------------------------------------------------------------------------
+// DMA of one tensor's staged cells of tile t (staged row r = cell r of the
+// SR x SC region, row-major) into swizzled 128-byte rows, 1 KB per wave
+// instruction, waves taking runs in turn; the last run is padded with copies
+// of the last cell.
+__device__ void res_dma_cells(unsigned char* lds, const uint16_t* src, int W, const ResTile& t, int wave) {
+  const int lane = threadIdx.x & 63;
+  const int nrow = t.SR * t.SC;
+  const float inv_sc = 1.f / (float)t.SC;
+  for (int base = wave * 64; base < nrow * 8; base += 64 * kResWaves) {
+    const int P = base + lane;
+    const int r = min(P >> 3, nrow - 1);
+    const int g = ((P & 7) ^ swz(P >> 3)) & 7;  // the 16-byte piece this slot holds
+    const int rr = div_small(r, inv_sc);
+    const size_t tok = (size_t)(t.sr0 + rr) * W + (t.sc0 + (r - rr * t.SC));
+    dma16(src + tok * kD + g * 8, lds_addr(lds + base * 16));
+  }
+}
+
+// DMA of the per-token walk weights of the tile's slots ([slot][T] fp32),
+// 4 bytes per lane; a masked slot takes the tile origin's row.
+__device__ void res_dma_weights(unsigned char* lds, const float* wb, const ResPlan& p, const ResTile& t,
+                                int wave) {
+  const int lane = threadIdx.x & 63;
+  const int T = p.T, cnt = p.nblk * 32 * T;
+  const float inv_t = 1.f / (float)T;
+  for (int e0 = wave * 64; e0 < cnt; e0 += 64 * kResWaves) {
+    const int e = min(e0 + lane, cnt - 1);
+    const int s = div_small(e, inv_t);
+    int tr, tc;
+    const bool on = res_slot(p, t, s, tr, tc);
+    const size_t tok = on ? (size_t)(t.r0 + tr) * p.W + (t.c0 + tc) : (size_t)t.r0 * p.W + t.c0;
+    dma4(wb + tok * T + (e - s * T), lds_addr(lds + e0 * 4));
+  }
+}
+
+// The staged cell of each slot's token (the zero row for a masked slot).
+__device__ void res_slot_table(uint16_t* tab, const ResPlan& p, const ResTile& t) {
+  for (int s = threadIdx.x; s < p.nblk * 32; s += kResThreads) {
+    int tr, tc;
+    tab[s] = (uint16_t)(res_slot(p, t, s, tr, tc) ? res_cell(t, t.r0 + tr, t.c0 + tc) : p.L.zrow);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Sweeps: contractions over the tile's token slots on MFMA.
+// ---------------------------------------------------------------------------
+// Operand bits of X[row(8h + e)][col0 + m], e = 0..7, for 16 slots whose
+// staged rows lane (i, g) of the wave supplies (ra for the first read, rb for
+// the second); see rows_bits for the lane pattern of ds_read_b64_tr_b16.
+__device__ __forceinline__ v8s rows_at(const unsigned char* base, int ra, int rb, int col) {
+  return join(tr_read(base + row_off<BF16>(ra, col)), tr_read(base + row_off<BF16>(rb, col)));
+}
+
+// Steps [k0, k1) of 16 slots: acc += phi(K)^T X over the slots, X = the
+// slots' V cells (KV sweep) or their rescaled Q rows (M sweep, by slot), and
+// acc_s += phi(K)^T 1 when kWithS.  Wave output block (mb, nb) of 32 x 32.
+// Steps go in batches of 8, then 4 and 2 (k1 - k0 is even): every operand
+// read of a batch (slot-table rows first, then the transposed reads) is
+// issued before its first MFMA, and even and odd steps accumulate into two
+// chains that are added at the end.
+template <bool kIsM, bool kWithS>
+__device__ __forceinline__ void res_sweep(const unsigned char* smem, const ResLayout& L, int k0, int k1, int mb,
+                                          int nb, f32x16& acc, f32x16& acc_s) {
+  const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
+  const int colA = 32 * mb + 16 * (g & 1) + 4 * (i & 3);
+  const int colB = 32 * nb + 16 * (g & 1) + 4 * (i & 3);
+  const uint16_t* tab = reinterpret_cast<const uint16_t*>(smem + L.tab);
+  const unsigned char* bK = smem + L.k;
+  const unsigned char* bX = smem + L.v;
+  const bf16x8 ones = as_bf16((v8s)(short)0x3f80);  // bf16 1.0
+  f32x16 acc2 = {}, acc_s2 = {};
+  auto batch = [&](auto u_tag, int k) {
+    constexpr int U = decltype(u_tag)::value;
+    int ra[U], rb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s1 = 16 * (k + u) + 8 * (g >> 1) + (i >> 2);
+      ra[u] = tab[s1];
+      rb[u] = tab[s1 + 4];
+    }
+    v8s A[U], B[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s1 = 16 * (k + u) + 8 * (g >> 1) + (i >> 2);
+      A[u] = __builtin_elementwise_max(rows_at(bK, ra[u], rb[u], colA), (v8s)0);  // ReLU on the bf16 bits
+      B[u] = kIsM ? rows_at(bX, s1, s1 + 4, colB) : rows_at(bX, ra[u], rb[u], colB);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      f32x16& c = (u & 1) ? acc2 : acc;
+      c = mma(as_bf16(A[u]), as_bf16(B[u]), c);
+      if constexpr (kWithS) {
+        f32x16& cs = (u & 1) ? acc_s2 : acc_s;
+        cs = mma(as_bf16(A[u]), ones, cs);
+      }
+    }
+  };
+  int k = k0;
+  for (; k + 8 <= k1; k += 8) batch(std::integral_constant<int, 8>{}, k);
+  if (k + 4 <= k1) {
+    batch(std::integral_constant<int, 4>{}, k);
+    k += 4;
+  }
+  if (k + 2 <= k1) batch(std::integral_constant<int, 2>{}, k);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    acc[r] += acc2[r];
+    acc_s[r] += acc_s2[r];
+  }
+}
+
+// One sweep of the rank's slots by the four waves (wave w: output block w of
+// the 64 x 64 result, every slot) and the publication of its partial:
+// [phi(K)^T V or M] as fp32 rows, and s (KV sweep, waves of the first column
+// block) as 64 fp32.
+template <bool kIsM>
+__device__ void res_sweep_publish(const ResArgs& a, unsigned char* smem, int b, int g) {
+  const ResLayout& L = a.p.L;
+  const int wave = wave_id(), lane = threadIdx.x & 63, m = lane & 31, h = lane >> 5;
+  const int mb = wave >> 1, nb = wave & 1;
+  const bool with_s = !kIsM && nb == 0;
+  f32x16 acc = {}, acc_s = {};
+  // The ones product (s) as a variant of its own: no branch among the MFMAs.
+  if (with_s)
+    res_sweep<kIsM, true>(smem, L, 0, a.p.nblk * 2, mb, nb, acc, acc_s);
+  else
+    res_sweep<kIsM, false>(smem, L, 0, a.p.nblk * 2, mb, nb, acc, acc_s);
+  if (!kIsM) res_stamp(a, b < a.S, kResStampKVSweep);
+  float* part = (kIsM ? a.part_m : a.part_kv) + ((size_t)b * a.p.G + g) * (kD * kD);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) put(part + (32 * mb + 8 * (i >> 2) + 4 * h + (i & 3)) * kD + 32 * nb + m, acc[i]);
+  if (with_s && m == 0) {
+    float* ps = a.part_s + ((size_t)b * a.p.G + g) * kD;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) put(ps + 32 * mb + 8 * (i >> 2) + 4 * h + (i & 3), acc_s[i]);
+  }
+  res_arrive(a, b, g, kIsM ? kRcM : kRcKV);
+}
+
+// s = the fixed-order sum of the slice's G partials, into LDS: wave w sums
+// partials w, w + 4, ... (sixteen loads in flight at a time), then wave 0
+// adds the four sums in wave order.
+__device__ void res_sum_s(const ResArgs& a, unsigned char* smem, int b) {
+  const int wave = wave_id(), lane = threadIdx.x & 63, G = a.p.G;
+  float* sw = reinterpret_cast<float*>(smem + a.p.L.scr);  // [waves][64]
+  const float* ps = a.part_s + (size_t)b * G * kD + lane;
+  const int np = (G - wave + kResWaves - 1) / kResWaves;
+  float t = 0.f;
+  for (int q0 = 0; q0 < np; q0 += 16) {
+    float x[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) x[q] = get(ps + (size_t)min(wave + kResWaves * (q0 + q), G - 1) * kD);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) t += (q0 + q < np) ? x[q] : 0.f;
+  }
+  sw[wave * kD + lane] = t;
+  lds_barrier();
+  if (wave == 0) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kResWaves; ++w) v += sw[w * kD + lane];
+    reinterpret_cast<float*>(smem + a.p.L.s)[lane] = v;
+  }
+  lds_barrier();
+}
+
+// Store element e = 64 r + c of one statistics matrix as fp32 at fin[e] and
+// as bf16 in its MFMA A-operand fragment slot of frag: fragment (mb, q, lane,
+// j) holds X[dimof(8 q + j, lane / 32)][32 mb + lane % 32].
+__device__ __forceinline__ void res_store_stat(float* fin, uint16_t* frag, int e, float v) {
+  const int r = e >> 6, c = e & 63;
+  fin[e] = v;
+  const int vs = 16 * (r >> 5) + 4 * ((r >> 3) & 3) + (r & 3);
+  const int ln = (c & 31) + 32 * ((r >> 2) & 1);
+  const int idx = (((c >> 5) * 4 + vs / 8) * 64 + ln) * 8 + vs % 8;
+  __hip_atomic_store(frag + idx, f2bf(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One element's total of the combine: the statistics as fp32 rows
+// (consecutive threads, consecutive elements), which the ranks read back;
+// the bf16 fragment slot too when only the statistics are asked for (another
+// kernel's output pass may read them).  With one rank the staged element is
+// the total: it is kept there, in place, for this rank's output.
+__device__ __forceinline__ void res_combine_store(const ResArgs& a, float* stg, int b, int G, int e0, int e, int ec,
+                                                  float v, bool frags) {
+  const int f = e0 + e;
+  const bool m = f >= kD * kD;
+  float* fin = pick(a.fin_kv, a.fin_m, m) + (size_t)b * (kD * kD);
+  put(fin + (f & (kD * kD - 1)), v);
+  if (frags)
+    res_store_stat(fin, pick(static_cast<uint16_t*>(a.frag_kv), static_cast<uint16_t*>(a.frag_m), m) + (size_t)b * (kD * kD),
+                   f & (kD * kD - 1), v);
+  if (G == 1) stg[ec] = v;
+}
+
+// Rank g's share of the slice statistics: elements [e0, e1) of the flattened
+// [phi(K)^T V | M] (nstat = 4096 or 8192 of them) summed over the G partials.
+// The G partials' elements (G E <= nstat + G floats) are first staged in the
+// K region (free after the sweeps) as [G][E] floats: each thread issues its
+// loads at once (a single round trip), then writes them to LDS.
+// Then tpe threads share an element (partials q, q + tpe, ... each) and
+// combine by a fixed xor tree, so the order of additions depends on G alone.
+// With one rank per slice the totals stay in the staging, in row order,
+// where the output takes them.
+__device__ void res_combine(const ResArgs& a, unsigned char* smem, int b, int g, int nstat) {
+  const int tid = threadIdx.x, G = a.p.G;
+  int e0, e1;
+  res_combine_range(nstat, G, g, e0, e1);
+  const int E = e1 - e0, total = G * E;
+  float* stg = reinterpret_cast<float*>(smem + a.p.L.k);
+  // q -> (partial p, element e) with p = floor(q / E): q < 8192 and E >= 16,
+  // so (q + 1/2) / E in float stays well within 1/(2E) of the exact quotient.
+  const float inv_e = 1.f / (float)E;
+  constexpr int kPer = (kResCombineFloats + kResThreads - 1) / kResThreads;  // loads per thread (total <= G E)
+  float x[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int q = min(tid + kResThreads * i, total - 1);
+    const int pp = (int)(((float)q + 0.5f) * inv_e), f = e0 + (q - pp * E);
+    x[i] = get(pick(a.part_kv, a.part_m, f >= kD * kD) + ((size_t)b * G + pp) * (kD * kD) + (f & (kD * kD - 1)));
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    if (tid + kResThreads * i < total) stg[tid + kResThreads * i] = x[i];
+  __syncthreads();
+  res_stamp(a, b < a.S, kResStampCStaged);
+  int tpe = 1;
+  while (tpe < 64 && 2 * tpe * E <= kResThreads) tpe *= 2;
+  const int per = kResThreads / tpe;
+  const bool frags = a.mode == kResReduce;
+  // Four elements at a time, their staged partials read four at a time (up
+  // to sixteen LDS reads in flight); each element's partials are added in
+  // the order q, q + tpe, ...
+  const int q = tid % tpe;
+  for (int base = 0; base < E; base += 4 * per) {
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    int ec[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ec[k] = min(base + k * per + tid / tpe, E - 1);
+    for (int p0 = q; p0 < G; p0 += 4 * tpe) {
+      float x[4][4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[k][u] = p0 + u * tpe < G ? stg[(p0 + u * tpe) * E + ec[k]] : 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[k] += x[k][u];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      for (int o = 1; o < tpe; o <<= 1) v[k] += __shfl_xor(v[k], o);
+    __syncthreads();  // every read of this round is done before totals are written back (one rank)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = base + k * per + tid / tpe;
+      if (e < E && q == 0) res_combine_store(a, stg, b, G, e0, e, ec[k], v[k], frags);
+    }
+  }
+  if (g == 0 && tid < kD) put(a.fin_s + (size_t)b * kD + tid, reinterpret_cast<const float*>(smem + a.p.L.s)[tid]);
+  res_stamp(a, b < a.S, kResStampCSummed);
+}
+
+// The slice statistics [phi(K)^T V | M] as fp32 rows (nstat floats) from the
+// workspace into the K region: 8-byte coherent loads, all in flight at once.
+__device__ void res_stats_to_lds(const ResArgs& a, unsigned char* smem, int b, int nstat) {
+  const int tid = threadIdx.x;
+  uint64_t* dst = reinterpret_cast<uint64_t*>(smem + a.p.L.k);
+  constexpr int kPer = 2 * kD * kD / 2 / kResThreads;  // 8-byte pieces per thread
+  uint64_t x[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int q = tid + kResThreads * i;  // piece q: elements 2 q, 2 q + 1
+    const float* src = pick(a.fin_kv, a.fin_m, 2 * q >= kD * kD) + (size_t)b * (kD * kD) + ((2 * q) & (kD * kD - 1));
+    x[i] = 2 * q < nstat ? get64(src) : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    if (2 * (tid + kResThreads * i) < nstat) dst[tid + kResThreads * i] = x[i];
+}
+
+// MFMA A-operand fragments (bf16, 8 KB) of a 64 x 64 matrix from its fp32
+// rows in LDS: piece (mb, q, lane) holds X[dimof(8 q + j, lane / 32)][32 mb +
+// lane % 32], j = 0..7, as 16 bytes.
+__device__ void res_frags_from_rows(const float* st, unsigned char* frag) {
+  uint4* dst = reinterpret_cast<uint4*>(frag);
+  for (int pc = threadIdx.x; pc < 512; pc += kResThreads) {
+    const int mb = pc >> 8, q = (pc >> 6) & 3, ln = pc & 63;
+    const int c = 32 * mb + (ln & 31), h = ln >> 5;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      float x2[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int vs = 8 * q + j + t;
+        x2[t] = st[(32 * (vs >> 4) + 8 * ((vs >> 2) & 3) + 4 * h + (vs & 3)) * kD + c];
+      }
+      w[j / 2] = pack_bf16x2(x2[0], x2[1]);
+    }
+    dst[pc] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Local branch and output (per 4 x 8 block; one token per lane pair, 32
+// features per lane in accumulator layout).
+// ---------------------------------------------------------------------------
+// Local branch of block blk of tile t on MFMA: logits C[cell][token] =
+// K_win Q_blk^T over the block's 6 x 10 window of cells (60, padded to 64),
+// masked softmax, then L^T = V_win^T P^T with the probabilities as the B
+// operand and V from transposed LDS reads; the denominator is the same
+// product against an all-ones operand.  A window cell off the grid, or past
+// the staged region (only masked tokens see those), reads a clamped staged
+// cell and is masked.
+__device__ void res_local(const ResArgs& a, const ResTile& t, const unsigned char* cK, const unsigned char* cV,
+                          int blk, const bf16x8 (&qB)[4], float scale, float (&L)[32]) {
+  const ResPlan& p = a.p;
+  const int lane = threadIdx.x & 63, n = lane & 31, h = lane >> 5;
+  const int i16 = lane & 15, g = lane >> 4;
+  const int br = blk / p.BC, bc = blk % p.BC;
+  const int gr0 = t.r0 + 4 * br - 1, gc0 = t.c0 + 8 * bc - 1;  // window origin on the grid
+  auto wcell = [&](int c) {
+    c = min(c, 59);
+    return res_cell(t, gr0 + c / 10, gc0 + c % 10);
+  };
+  f32x16 lg[2] = {};
+  const int sc0 = wcell(n), sc1 = wcell(32 + n);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const bf16x8 A0 = *reinterpret_cast<const bf16x8*>(cK + row_off<BF16>(sc0, 16 * kb + 8 * h));
+    const bf16x8 A1 = *reinterpret_cast<const bf16x8*>(cK + row_off<BF16>(sc1, 16 * kb + 8 * h));
+    lg[0] = mma(A0, qB[kb], lg[0]);
+    lg[1] = mma(A1, qB[kb], lg[1]);
+  }
+  // The window's on-grid rows and columns (wave-uniform), formed without a
+  // branch so that two blocks' local branches stay one stretch of code.
+  unsigned rowbits = 0, colbits = 0;
+#pragma unroll
+  for (int wr = 0; wr < 6; ++wr) rowbits |= (unsigned)(gr0 + wr >= 0 && gr0 + wr < p.H) << wr;
+#pragma unroll
+  for (int wc = 0; wc < 10; ++wc) colbits |= (unsigned)(gc0 + wc >= 0 && gc0 + wc < p.W) << wc;
+  unsigned r0m = 0, r1m = 0, k0m = 0, k1m = 0;
+#pragma unroll
+  for (int wr = 0; wr < 6; ++wr) {
+    const unsigned on = 0u - ((rowbits >> wr) & 1u);
+    r0m |= row_slots(0, wr) & on;
+    r1m |= row_slots(1, wr) & on;
+  }
+#pragma unroll
+  for (int wc = 0; wc < 10; ++wc) {
+    const unsigned on = 0u - ((colbits >> wc) & 1u);
+    k0m |= col_slots(0, wc) & on;
+    k1m |= col_slots(1, wc) & on;
+  }
+  const unsigned valid = neighbour_slots(n >> 3, n & 7, h) & (h ? (r1m & k1m) : (r0m & k0m));
+  float pr[32];
+  float mx = -1e30f;  // finite: a masked token may have no valid slot
+#pragma unroll
+  for (int v = 0; v < 32; ++v) {
+    const unsigned keep = (unsigned)__builtin_amdgcn_sbfe((int)valid, v, 1);
+    pr[v] = __uint_as_float((__float_as_uint(lg[v >> 4][v & 15]) & keep) | (0xff800000u & ~keep));
+    mx = fmaxf(mx, pr[v]);
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float off = -mx * a.logit_scale;  // exp2((l - max) log2(e) / sqrt(d_h)); exp2(-inf) = 0
+  bf16x8 Bp[4];
+#pragma unroll
+  for (int v = 0; v < 32; ++v)
+    Bp[v >> 3][v & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(pr[v], a.logit_scale, off));
+  f32x16 la[2] = {}, lden = {};
+  const bf16x8 ones = as_bf16((v8s)(short)0x3f80);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    lden = mma(ones, Bp[kb], lden);
+    const int cA = wcell(16 * kb + 4 * (g >> 1) + (i16 >> 2));
+    const int cB = wcell(16 * kb + 8 + 4 * (g >> 1) + (i16 >> 2));
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int d = 32 * db + 16 * (g & 1) + 4 * (i16 & 3);
+      const bf16x8 A = as_bf16(join(tr_read(cV + row_off<BF16>(cA, d)), tr_read(cV + row_off<BF16>(cB, d))));
+      la[db] = mma(A, Bp[kb], la[db]);
+    }
+  }
+  const float inv = scale * __builtin_amdgcn_rcpf(lden[0]);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    L[v] = la[0][v] * inv;
+    L[16 + v] = la[1][v] * inv;
+  }
+}
+
+// y = x X for X given as A-operand fragments in LDS (frag: (mb, q, lane) ->
+// 16 bytes), x as the bits of its B operands (slot order).
+__device__ __forceinline__ void res_apply_bits(const unsigned char* frag, const v8s (&x)[4], float (&y)[32]) {
+  const int lane = threadIdx.x & 63;
+  // The fragment reads stay next to their products: hoisted out of the
+  // per-block and per-term loops, the 16 operands would hold 64 registers.
+  asm volatile("" : "+v"(frag));
+  f32x16 c0 = {}, c1 = {};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(frag + ((0 * 4 + q) * 64 + lane) * 16);
+    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(frag + ((1 * 4 + q) * 64 + lane) * 16);
+    const bf16x8 bx = as_bf16(x[q]);
+    c0 = mma(a0, bx, c0);
+    c1 = mma(a1, bx, c1);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    y[i] = c0[i];
+    y[16 + i] = c1[i];
+  }
+}
+// The same for x in accumulator layout as fp32 (rounded to bf16 here).
+__device__ __forceinline__ void res_apply(const unsigned char* frag, const float (&x)[32], float (&y)[32]) {
+  v8s b[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) b[q] = __builtin_bit_cast(v8s, operand(x, q, BF16{}));
+  res_apply_bits(frag, b, y);
+}
+
+// ---------------------------------------------------------------------------
+// The kernel.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
+  extern __shared__ __align__(1024) unsigned char smem[];
+  __shared__ int ticket;
+  __shared__ float geo[kMaxT];  // geometric walk weights
+  const ResPlan& p = a.p;
+  const ResLayout& L = p.L;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63, n = lane & 31, h = lane >> 5;
+
+  if (tid == 0) ticket = (int)bump(a.tickets + (a.xcd_groups ? blockIdx.x % kXcds : 0));
+  if (tid < kMaxT) geo[tid] = a.geo[tid];
+  __syncthreads();
+  const ResRank rk = res_rank(a, ticket);
+  res_stamp(a, true, kResStampStart);
+  if (a.stamps && tid == 0)
+    a.stamps[(size_t)blockIdx.x * kResPhases + kResPhases - 1] = ((unsigned long long)(unsigned)rk.group << 32) | (unsigned)rk.g;
+  const bool fwd = a.mode != kResReduce;  // local branch and output
+  const bool stats = a.mode != kResApply;  // sweeps and combine
+
+  if (rk.group >= 0) {
+    res_slot_table(reinterpret_cast<uint16_t*>(smem + L.tab), p, res_tile(p, rk.g));
+    // This wave's blocks: wave + 4 j, j < nown.
+    constexpr int kNB = kResMaxBlocks / kResWaves;
+    const int nown = min(kNB, (p.nblk - wave + kResWaves - 1) / kResWaves);
+    const int nstat = a.do_m ? 2 * kD * kD : kD * kD;
+
+    for (int b = rk.group; b < a.BH; b += a.S) {
+      // The tile is the same for every slice, but what depends on it per lane
+      // (window cells, masks, token indices) is cheap to recompute and would
+      // otherwise be held in registers across the whole loop: the rank index
+      // is passed through an empty asm so that nothing derived from it is
+      // hoisted out of the loop.
+      int gi = rk.g;
+      asm volatile("" : "+s"(gi));
+      const ResTile t = res_tile(p, gi);
+      const bool first = b == rk.group;
+      const size_t base = (size_t)b * a.n;
+      const uint16_t* Qb = static_cast<const uint16_t*>(a.Q) + base * kD;
+      const uint16_t* Kb = static_cast<const uint16_t*>(a.K) + base * kD;
+      const uint16_t* Vb = static_cast<const uint16_t*>(a.V) + base * kD;
+      const float alpha = fwd ? a.alpha[b % a.heads] : 0.f;
+      __syncthreads();  // the previous slice's readers of every region are done
+      // Zero rows (masked slots read them in the sweeps).
+      if (tid < 16) {
+        reinterpret_cast<uint4*>(smem + L.k + L.zrow * kResRowBytes)[tid & 7] = make_uint4(0, 0, 0, 0);
+        reinterpret_cast<uint4*>(smem + L.v + L.zrow * kResRowBytes)[tid & 7] = make_uint4(0, 0, 0, 0);
+      }
+      // Stage: K and V cells, the weights; Q of this wave's blocks into registers.
+      res_dma_cells(smem + L.k, Kb, p.W, t, wave);
+      res_dma_cells(smem + L.v, Vb, p.W, t, wave);
+      if (fwd && a.per_token) res_dma_weights(smem + L.w, a.weights + base * p.T, p, t, wave);
+      // Blocks go in pairs (two independent chains for the scheduler to
+      // interleave); when the wave has an odd number of blocks, the last
+      // pair's second block repeats the first: computed, never stored.
+      bf16x8 qB[kNB][4];
+      int slot[kNB], blkid[kNB];
+      bool valid[kNB];
+#pragma unroll
+      for (int j = 0; j < kNB; ++j) {
+        const int jj = (j < nown || (j & 1) == 0) ? j : j - 1;
+        blkid[j] = wave + kResWaves * jj;
+        slot[j] = blkid[j] * 32 + n;
+        int tr = 0, tc = 0;
+        const bool on = blkid[j] < p.nblk && res_slot(p, t, slot[j], tr, tc);
+        valid[j] = j < nown && on;
+        const size_t tok = on ? (size_t)(t.r0 + tr) * p.W + (t.c0 + tc) : (size_t)t.r0 * p.W + t.c0;
+        if ((j & ~1) < nown) {
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+            qB[j][kb] = *reinterpret_cast<const bf16x8*>(Qb + tok * kD + 16 * kb + 8 * h);
+        }
+      }
+      wait_all();
+      __syncthreads();
+      res_stamp(a, first, kResStampStaged);
+
+      // KV sweep: partials of s and phi(K)^T V.
+      if (stats && a.do_kv) res_sweep_publish<false>(a, smem, b, rk.g);
+      res_stamp(a, first, kResStampKV);
+
+      // Local branch and the walk's k = 0 term: Lm = (1 - alpha) L_i + alpha w_0(i) V_i.
+      float Lm[kNB][32];
+      const float* wts = reinterpret_cast<const float*>(smem + L.w);
+      if (fwd) {
+#pragma unroll
+        for (int j0 = 0; j0 < kNB; j0 += 2) {
+          if (j0 < nown) {
+#pragma unroll
+            for (int j = j0; j < j0 + 2; ++j)
+              res_local(a, t, smem + L.k, smem + L.v, blkid[j], qB[j], 1.f - alpha, Lm[j]);
+#pragma unroll
+            for (int j = j0; j < j0 + 2; ++j) {
+              int sl = slot[j], tr, tc;
+              asm volatile("" : "+v"(sl));
+              const bool on = res_slot(p, t, sl, tr, tc);
+              const int cell = on ? res_cell(t, t.r0 + tr, t.c0 + tc) : 0;
+              const float w0 = a.per_token ? wts[slot[j] * p.T] : geo[0];
+              const float f = alpha * w0;
+#pragma unroll
+              for (int c = 0; c < 8; ++c) {
+                float vc[4];
+                load4(reinterpret_cast<const uint16_t*>(smem + L.v + row_off<BF16>(cell, dimof(4 * c, h))), vc);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Lm[j][4 * c + e] += f * vc[e];
+              }
+            }
+          }
+        }
+      }
+
+      // s, then the rows Qt_i = r_i phi(Q_i) of this wave's slots over the V
+      // cells (the local branch is done: the wait closed with a workgroup
+      // barrier), zero for masked slots.  They are the B operand of the M
+      // sweep and, rounded to bf16 like every operand the method derives, the
+      // walk's u_1 in the output.
+      res_stamp(a, first, kResStampLocal);
+      const bool global = p.T >= 2;
+      unsigned char* qt = smem + L.v;
+      if (global || (stats && a.do_m)) {
+        float* s_lds = reinterpret_cast<float*>(smem + L.s);
+        if (stats) {
+          if (p.G > 1) res_wait(a, b, kRcKV);
+          else __syncthreads();
+          res_sum_s(a, smem, b);
+          res_stamp(a, first, kResStampS);
+        } else {
+          __syncthreads();
+          if (tid < kD) s_lds[tid] = get(a.fin_s + (size_t)b * kD + tid);
+          __syncthreads();
+        }
+#pragma unroll
+        for (int j = 0; j < kNB; ++j) {
+          if (j < nown) {
+            v8s x[4];
+            float dot = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+              x[kb] = __builtin_elementwise_max(__builtin_bit_cast(v8s, qB[j][kb]), (v8s)0);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) dot += bf2f((uint16_t)x[kb][e]) * s_lds[16 * kb + 8 * h + e];
+            }
+            dot += __shfl_xor(dot, 32);
+            const float sc = valid[j] ? __builtin_amdgcn_rcpf(dot + a.eps) : 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+              uint32_t o[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                o[e] = pack_bf16x2(bf2f((uint16_t)x[kb][2 * e]) * sc, bf2f((uint16_t)x[kb][2 * e + 1]) * sc);
+              *reinterpret_cast<uint4*>(qt + row_off<BF16>(slot[j], 16 * kb + 8 * h)) =
+                  make_uint4(o[0], o[1], o[2], o[3]);
+            }
+          }
+        }
+        lds_barrier();
+      }
+
+      if (stats && a.do_m) res_sweep_publish<true>(a, smem, b, rk.g);
+      res_stamp(a, first, kResStampM);
+
+      if (stats && a.do_kv) {
+        if (p.G > 1) res_wait(a, b, a.do_m ? kRcM : kRcKV);
+        res_stamp(a, first, kResStampMWait);
+        res_combine(a, smem, b, rk.g, nstat);
+        res_stamp(a, first, kResStampComb);
+        if (p.G > 1) {
+          res_arrive(a, b, rk.g, kRcC);
+          res_wait(a, b, kRcC);
+          res_stamp(a, first, kResStampCWait);
+        } else {
+          wait_all();
+          __syncthreads();
+        }
+      }
+
+      if (fwd) {
+        if (global) {
+          // The statistics as fp32 rows in the K region (with one rank they
+          // are already there): phi(K)^T V, then M; then as bf16 fragments
+          // in the scratch area.
+          if (!(stats && p.G == 1)) {
+            res_stats_to_lds(a, smem, b, p.T >= 3 ? 2 * kD * kD : kD * kD);
+            wait_all();
+            __syncthreads();
+          }
+          const float* rows = reinterpret_cast<const float*>(smem + L.k);
+          res_frags_from_rows(rows, smem + L.scr);
+          if (p.T >= 3) res_frags_from_rows(rows + kD * kD, smem + L.scr + kFragBytes);
+          __syncthreads();
+        }
+        res_stamp(a, first, kResStampFrags);
+        const unsigned char* fkv = smem + L.scr;
+        const unsigned char* fm = smem + L.scr + kFragBytes;
+        uint16_t* Yb = static_cast<uint16_t*>(a.Y) + base * kD;
+#pragma unroll
+        for (int j0 = 0; j0 < kNB; j0 += 2) {
+          if (j0 < nown) {
+            if (global) {
+#pragma unroll
+              for (int j = j0; j < j0 + 2; ++j) {
+                const float* wrow = a.per_token ? wts + slot[j] * p.T : geo;
+                // u_1 = Qt_i from its staged row, in accumulator slot order;
+                // u_k = u_(k-1) M, z = sum_k w_k(i) u_k, then alpha z phi(K)^T V.
+                v8s u1[4];
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+                  u1[kb] = relu_to_slots(*reinterpret_cast<const v8s*>(qt + row_off<BF16>(slot[j], 16 * kb + 8 * h)));
+                float z[32], y[32];
+                const float w1 = wrow[1];
+#pragma unroll
+                for (int v = 0; v < 32; ++v) z[v] = w1 * bf2f((uint16_t)u1[v >> 3][v & 7]);
+                if (p.T >= 3) {
+                  float u[32];
+                  res_apply_bits(fm, u1, u);
+                  const float w2 = wrow[2];
+#pragma unroll
+                  for (int v = 0; v < 32; ++v) z[v] += w2 * u[v];
+                  for (int k = 3; k < p.T; ++k) {
+                    res_apply(fm, u, y);
+                    const float wk = wrow[k];
+#pragma unroll
+                    for (int v = 0; v < 32; ++v) {
+                      u[v] = y[v];
+                      z[v] += wk * y[v];
+                    }
+                  }
+                }
+                res_apply(fkv, z, y);
+#pragma unroll
+                for (int v = 0; v < 32; ++v) Lm[j][v] += alpha * y[v];
+              }
+            }
+#pragma unroll
+            for (int j = j0; j < j0 + 2; ++j) {
+              if (valid[j]) {
+                // The token index recomputed here (not kept from the Q loads).
+                int sl = slot[j], tr, tc;
+                asm volatile("" : "+v"(sl));
+                res_slot(p, t, sl, tr, tc);
+                const size_t tok = (size_t)(t.r0 + tr) * p.W + (t.c0 + tc);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) store4(Yb + tok * kD + dimof(4 * c, h), &Lm[j][4 * c]);
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // The last workgroup to finish clears the launch counters for the next call
+  // (every other workgroup's atomics have completed: each waited for them
+  // before counting itself done).
+  __shared__ int last;
+  if (rk.group >= 0) res_stamp(a, true, kResStampOut);
+  wait_all();
+  __syncthreads();
+  res_stamp(a, true, kResStampEnd);
+  if (tid == 0) last = bump(a.done_cnt) == gridDim.x - 1;
+  __syncthreads();
+  if (last) {
+    for (int i = tid; i < a.BH * kCntWords; i += kResThreads)
+      put(a.slice_cnt + (size_t)(i / kCntWords) * kCntStride + i % kCntWords, 0u);
+    if (a.grouped)
+      for (int i = tid; i < a.BH * 3 * kMaxSubs; i += kResThreads) put(a.sub_cnt + (size_t)i * kCntStride, 0u);
+    if (tid < kXcds) put(a.tickets + tid, 0u);
+    if (a.clear_err && tid == 0) put(a.err, 0u);
+    wait_all();
+    __syncthreads();
+    if (tid == 0) put(a.done_cnt, 0u);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_resident(const ResArgs& a, int grid, hipStream_t s) {
+  static std::atomic<bool> lds_set[kMaxDevices];
+  const hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(&resident_kernel), kResLdsMax, lds_set);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(resident_kernel, dim3(grid), dim3(kResThreads), a.p.L.total, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace lisa

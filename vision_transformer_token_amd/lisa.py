@@ -33,14 +33,41 @@ __all__ = [
     "lisa_backward",
     "lisa_backward_after_forward",
     "lisa_backward_workspace_size",
+    "LISA_ERR_NULL",
+    "LISA_ERR_SHAPE",
+    "LISA_ERR_PARAM",
+    "LISA_ERR_DTYPE",
+    "LISA_ERR_UNSUPPORTED",
+    "LISA_ERR_WORKSPACE",
+    "LISA_ERR_ALIGN",
+    "LISA_ERR_HIP",
     "LISA_ERR_STALLED",
     "LISA_ERR_SCRATCH",
     "lisa_forward_noalloc",
+    "lisa_forward_phases",
+    "lisa_forward_schedule",
+    "LISA_PHASES",
+    "STAGES",
+    "FEATURES",
+    "SCHEDULES",
 ]
+
+LISA_PHASES = 16
+# Stage indices of lisa_forward_phases (LISA_STAGE_* in include/lisa.h).
+STAGES = ["start", "staged", "kv", "local", "s", "m", "mwait", "combine", "cwait", "frags", "out", "end", "kvsweep",
+          "cstaged", "csummed"]
 
 LISA_FP32 = 0
 LISA_BF16 = 1
 LISA_OK = 0
+LISA_ERR_NULL = 1
+LISA_ERR_SHAPE = 2
+LISA_ERR_PARAM = 3
+LISA_ERR_DTYPE = 4
+LISA_ERR_UNSUPPORTED = 5
+LISA_ERR_WORKSPACE = 6
+LISA_ERR_ALIGN = 7
+LISA_ERR_HIP = 8
 LISA_ERR_STALLED = 9
 LISA_ERR_SCRATCH = 10
 
@@ -74,11 +101,14 @@ class Problem(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("eps", ctypes.c_float),
         ("feature", ctypes.c_int32),
+        ("schedule", ctypes.c_int32),
     ]
 
 
 # lisa_feature: phi of the global branch.
 FEATURES = {"relu": 0, "elu": 1}
+# lisa_schedule: which forward kernel runs the pass.
+SCHEDULES = {"auto": 0, "streaming": 1, "resident": 2}
 
 
 class WeightMlp(ctypes.Structure):
@@ -101,6 +131,9 @@ _lib.lisa_forward.argtypes = [_P, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, 
 _lib.lisa_forward.restype = ctypes.c_int
 _lib.lisa_forward_noalloc.argtypes = [_P, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp]
 _lib.lisa_forward_noalloc.restype = ctypes.c_int
+_lib.lisa_forward_phases.argtypes = [_P, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t, _vp,
+                                     ctypes.c_size_t, _vp]
+_lib.lisa_forward_phases.restype = ctypes.c_int
 _lib.lisa_apply.argtypes = _lib.lisa_forward.argtypes
 _lib.lisa_apply.restype = ctypes.c_int
 _lib.lisa_reduce.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
@@ -145,12 +178,24 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
 
 
-def make_problem(q, v, *, grid, T, eps=1e-6, feature="relu"):
+def make_problem(q, v, *, grid, T, eps=1e-6, feature="relu", schedule="auto"):
     """Problem for q [B, heads, n, d_h] and v [B, heads, n, d_v] on an H x W
-    grid; ``feature`` is phi of the global branch, "relu" or "elu" (ELU + 1)."""
+    grid; ``feature`` is phi of the global branch, "relu" or "elu" (ELU + 1);
+    ``schedule`` the forward kernel, "auto", "streaming" or "resident"."""
     H, W = grid
     B, heads, n, d_h = q.shape
-    return Problem(B, heads, H, W, d_h, v.shape[-1], T, _dtype_code(q), eps, FEATURES[feature])
+    return Problem(B, heads, H, W, d_h, v.shape[-1], T, _dtype_code(q), eps, FEATURES[feature],
+                   SCHEDULES[schedule])
+
+
+def lisa_forward_schedule(problem):
+    """The kernel lisa_forward runs for ``problem`` on the current device:
+    "streaming" or "resident"."""
+    out = ctypes.c_int32(-1)
+    st = _lib.lisa_forward_schedule(ctypes.byref(problem), ctypes.byref(out))
+    if st != LISA_OK:
+        raise LisaError(st, "lisa_forward_schedule")
+    return {v: k for k, v in SCHEDULES.items()}[out.value]
 
 
 def lisa_workspace_size(problem):
@@ -186,7 +231,7 @@ def _check_tensors(**ts):
 
 
 def _call_forward(fn, where, q, k, v, *, grid, T, alpha, weights=None, beta=None, eps=1e-6,
-                  out=None, workspace=None, stream=None, feature="relu"):
+                  out=None, workspace=None, stream=None, feature="relu", schedule="auto"):
     _check_tensors(q=q, k=k, v=v, alpha=alpha, weights=weights, out=out, workspace=workspace)
     if weights is not None and weights.dtype != torch.float32:
         raise TypeError("weights must be float32")
@@ -194,7 +239,7 @@ def _call_forward(fn, where, q, k, v, *, grid, T, alpha, weights=None, beta=None
         raise TypeError("alpha must be float32")
     if weights is None and beta is None:
         raise ValueError("give adaptive weights or beta")
-    prob = make_problem(q, v, grid=grid, T=T, eps=eps, feature=feature)
+    prob = make_problem(q, v, grid=grid, T=T, eps=eps, feature=feature, schedule=schedule)
     if out is None:
         out = torch.empty_like(v)
     if workspace is None:
@@ -210,7 +255,7 @@ def _call_forward(fn, where, q, k, v, *, grid, T, alpha, weights=None, beta=None
 
 
 def lisa_forward(q, k, v, *, grid, T, alpha, weights=None, beta=None, eps=1e-6, out=None,
-                 workspace=None, stream=None, feature="relu"):
+                 workspace=None, stream=None, feature="relu", schedule="auto"):
     """Y = LiSA(q, k, v) on the GPU; see include/lisa.h.
 
     q, k: [B, heads, n, 64], v: [B, heads, n, 64], bf16 or fp32, contiguous
@@ -220,11 +265,11 @@ def lisa_forward(q, k, v, *, grid, T, alpha, weights=None, beta=None, eps=1e-6, 
     """
     return _call_forward(_lib.lisa_forward, "lisa_forward", q, k, v, grid=grid, T=T, alpha=alpha,
                          weights=weights, beta=beta, eps=eps, out=out, workspace=workspace,
-                         stream=stream, feature=feature)
+                         stream=stream, feature=feature, schedule=schedule)
 
 
 def lisa_forward_noalloc(q, k, v, *, grid, T, alpha, weights=None, beta=None, eps=1e-6, out=None, stream=None,
-                         feature="relu"):
+                         feature="relu", schedule="auto"):
     """lisa_forward without a workspace (the library's fixed device scratch;
     nothing is allocated by the call itself; ``out`` is allocated here when
     not given); see include/lisa.h."""
@@ -235,7 +280,7 @@ def lisa_forward_noalloc(q, k, v, *, grid, T, alpha, weights=None, beta=None, ep
         raise TypeError("alpha must be float32")
     if weights is None and beta is None:
         raise ValueError("give adaptive weights or beta")
-    prob = make_problem(q, v, grid=grid, T=T, eps=eps, feature=feature)
+    prob = make_problem(q, v, grid=grid, T=T, eps=eps, feature=feature, schedule=schedule)
     if out is None:
         out = torch.empty_like(v)
     st = _lib.lisa_forward_noalloc(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(weights),
@@ -246,12 +291,29 @@ def lisa_forward_noalloc(q, k, v, *, grid, T, alpha, weights=None, beta=None, ep
     return out
 
 
+def lisa_forward_phases(q, k, v, *, grid, T, alpha, stamps, weights=None, beta=None, eps=1e-6, out=None,
+                        workspace=None, stream=None):
+    """lisa_forward that also writes each workgroup's stage timeline into
+    ``stamps`` (an int64 GPU tensor of at least compute units * LISA_PHASES
+    entries); see include/lisa.h."""
+    _check_tensors(stamps=stamps)
+    if stamps.dtype != torch.int64:
+        raise TypeError("stamps must be int64")
+
+    def fn(prob, q_, k_, v_, w_, beta_, a_, y_, ws_, nb_, st_):
+        return _lib.lisa_forward_phases(prob, q_, k_, v_, w_, beta_, a_, y_, ws_, nb_, _ptr(stamps),
+                                        ctypes.c_size_t(stamps.numel()), st_)
+
+    return _call_forward(fn, "lisa_forward_phases", q, k, v, grid=grid, T=T, alpha=alpha, weights=weights,
+                         beta=beta, eps=eps, out=out, workspace=workspace, stream=stream)
+
+
 def lisa_forward_mlp_workspace_size(problem, hidden):
     return int(_lib.lisa_forward_mlp_workspace_size(ctypes.byref(problem), int(hidden)))
 
 
 def lisa_forward_mlp(q, k, v, *, grid, T, alpha, w1, b1, w2, b2, eps=1e-6, out=None, workspace=None,
-                     stream=None):
+                     stream=None, schedule="auto"):
     """Y = LiSA(q, k, v) with the walk weights predicted from concat(q_i, k_i)
     by the two-layer MLP (w1 [heads, hidden, 2 d_h], b1 [heads, hidden],
     w2 [heads, T, hidden], b2 [heads, T], fp32 GPU tensors); see include/lisa.h."""
@@ -260,7 +322,7 @@ def lisa_forward_mlp(q, k, v, *, grid, T, alpha, w1, b1, w2, b2, eps=1e-6, out=N
         if t.dtype != torch.float32:
             raise TypeError(f"{name} must be float32")
     hidden = w1.shape[1]
-    prob = make_problem(q, v, grid=grid, T=T, eps=eps)
+    prob = make_problem(q, v, grid=grid, T=T, eps=eps, schedule=schedule)
     if workspace is None:
         nbytes = lisa_forward_mlp_workspace_size(prob, hidden)
         if nbytes == 0:
@@ -282,7 +344,7 @@ def lisa_attention_workspace_size(problem):
 
 
 def lisa_attention_forward(x, w_qkv, b_qkv, w_o, b_o, *, heads, grid, T, alpha, weights=None, beta=None,
-                           eps=1e-6, out=None, workspace=None, stream=None, feature="relu"):
+                           eps=1e-6, out=None, workspace=None, stream=None, feature="relu", schedule="auto"):
     """The LiSA attention layer: x [B, n, C] (bf16 or fp32, C = 64 heads),
     w_qkv [3C, C] and w_o [C, C] in x's dtype, b_qkv [3C] and b_o [C] fp32;
     see include/lisa.h."""
@@ -293,7 +355,8 @@ def lisa_attention_forward(x, w_qkv, b_qkv, w_o, b_o, *, heads, grid, T, alpha, 
     B, n, C = x.shape
     if C != 64 * heads:
         raise ValueError("x's channels must be 64 * heads")
-    prob = Problem(B, heads, grid[0], grid[1], 64, 64, T, _dtype_code(x), eps, FEATURES[feature])
+    prob = Problem(B, heads, grid[0], grid[1], 64, 64, T, _dtype_code(x), eps, FEATURES[feature],
+                   SCHEDULES[schedule])
     if workspace is None:
         nbytes = lisa_attention_workspace_size(prob)
         if nbytes == 0:
@@ -311,17 +374,18 @@ def lisa_attention_forward(x, w_qkv, b_qkv, w_o, b_o, *, heads, grid, T, alpha, 
 
 
 def lisa_apply(q, k, v, *, grid, T, alpha, workspace, weights=None, beta=None, eps=1e-6, out=None,
-               stream=None, feature="relu"):
+               stream=None, feature="relu", schedule="auto"):
     """Output stage alone, from the statistics a previous lisa_reduce left in ``workspace``."""
     return _call_forward(_lib.lisa_apply, "lisa_apply", q, k, v, grid=grid, T=T, alpha=alpha,
                          weights=weights, beta=beta, eps=eps, out=out, workspace=workspace,
-                         stream=stream, feature=feature)
+                         stream=stream, feature=feature, schedule=schedule)
 
 
-def lisa_reduce(q, k, v, *, grid, eps=1e-6, T=3, workspace=None, outputs=True, stream=None, feature="relu"):
+def lisa_reduce(q, k, v, *, grid, eps=1e-6, T=3, workspace=None, outputs=True, stream=None, feature="relu",
+                schedule="auto"):
     """Statistics stage: returns (s, phi(K)^T V, M) as fp32 tensors, or None if not ``outputs``."""
     _check_tensors(q=q, k=k, v=v, workspace=workspace)
-    prob = make_problem(q, v, grid=grid, T=T, eps=eps, feature=feature)
+    prob = make_problem(q, v, grid=grid, T=T, eps=eps, feature=feature, schedule=schedule)
     if workspace is None:
         workspace = new_workspace(prob, q.device)
     B, heads = q.shape[:2]
