@@ -27,11 +27,20 @@ DEFAULT_WORKLOAD = "pvt_t_stage1"
 ROTATE_BYTES = 600 << 20
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 # The sources the forward kernel is built from (its counters go stale when they change).
-KERNEL_SOURCES = [
-    os.path.join(ROOT, "vision_transformer_token_amd", "csrc", f)
-    for f in ("lisa_flow.hip", "lisa_device.hpp", "lisa_kernels.hpp", "lisa_api.hip")
-]
-BACKWARD_SOURCES = KERNEL_SOURCES + [os.path.join(ROOT, "vision_transformer_token_amd", "csrc", "lisa_backward.hip")]
+def _csrc(*names):
+    return [os.path.join(ROOT, "vision_transformer_token_amd", "csrc", f) for f in names]
+
+
+# The sources each forward kernel is built from (with the host planner that
+# configures its launch): its counters are current while their hash is.
+KERNEL_SOURCES_BY_NAME = {
+    "flow_kernel<bf16>": _csrc("lisa_flow.hip", "lisa_flow_schedule.hpp", "lisa_device.hpp", "lisa_kernels.hpp",
+                               "lisa_api.hip"),
+    "resident_kernel": _csrc("lisa_resident.hip", "lisa_resident.hpp", "lisa_device.hpp", "lisa_kernels.hpp",
+                             "lisa_api.hip"),
+}
+KERNEL_SOURCES = KERNEL_SOURCES_BY_NAME["flow_kernel<bf16>"]
+BACKWARD_SOURCES = KERNEL_SOURCES + _csrc("lisa_backward.hip")
 
 
 def kernel_source_hash(sources=None):
@@ -93,7 +102,7 @@ def load_counters(w, kernel):
     except (OSError, ValueError):
         return None
     entry = c.get("kernels", {}).get(f"{kernel}@{w.name}")
-    if not entry or c.get("source_hash") != kernel_source_hash():
+    if not entry or entry.get("source_hash") != kernel_source_hash(KERNEL_SOURCES_BY_NAME.get(kernel)):
         return None
     return entry.get("hbm_bytes_per_launch")
 
@@ -178,24 +187,55 @@ def summarize_profiles(outdir, workload, commands):
               "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) |", "|---|---|---|---|"]
     entries = {}
     for k in sorted(set(fetch) & set(write)):
-        if k == "copyBuffer":
+        if k not in KERNEL_SOURCES_BY_NAME:  # the copy, torch's workspace fill
             continue
         hbm = fetch[k] * 1024 * f_scale + write[k] * 1024 * w_scale
         entries[f"{k}@{w.name}"] = {"fetch_kib": fetch[k], "write_kib": write[k],
-                                    "hbm_bytes_per_launch": hbm}
+                                    "hbm_bytes_per_launch": hbm,
+                                    "source_hash": kernel_source_hash(KERNEL_SOURCES_BY_NAME[k])}
         lines.append(f"| {k} | {fetch[k]:.0f} | {write[k]:.0f} | {hbm / 1e6:.2f} MB |")
-    lines += ["", f"algorithmic bytes per forward: {w.token_heads * compulsory_bytes_per_token_head(w) / 1e6:.2f} MB",
-              f"kernel source hash: {kernel_source_hash()}"]
+    lines += ["", f"algorithmic bytes per forward: {w.token_heads * compulsory_bytes_per_token_head(w) / 1e6:.2f} MB"]
+    lines += [f"source hash of {k.split('@')[0]}: {e['source_hash']}" for k, e in entries.items()]
+    # Utilisation and instruction mix (two more passes, when present).
+    if os.path.exists(os.path.join(outdir, "pmc_util", "util_counter_collection.csv")):
+        avg_ns = {_short(r["Name"]): float(r["AverageNs"]) for r in stats}
+        util = {c: per_kernel("pmc_util", "util", c) for c in ("MfmaUtil", "VALUBusy", "SQ_INSTS_VALU_MFMA_MOPS_BF16")}
+        inst = {c: per_kernel("pmc_insts", "insts", c)
+                for c in ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_MFMA",
+                          "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE")}
+        lines += ["", "# MFMA and VALU utilisation, instruction mix (rocprofv3 --pmc, two passes)", "",
+                  f"utilisation pass: {commands['util']}", f"instruction pass: {commands['insts']}", "",
+                  "MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES over (GRBM_GUI_ACTIVE x SIMDs); VALUBusy = SQ_ACTIVE_INST_VALU "
+                  "over (GRBM_GUI_ACTIVE x CUs); bf16 MFMA work = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 flops, over "
+                  "the trace's average duration; instructions per wave = SQ_INSTS_* / SQ_WAVES; LDS bank conflicts "
+                  "= SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.", "",
+                  "| kernel | MfmaUtil | VALUBusy | bf16 MFMA TFLOP/s | waves | VALU / wave | SALU / wave | "
+                  "LDS / wave | MFMA / wave | LDS conflict cycles |", "|---|---|---|---|---|---|---|---|---|---|"]
+        for k in sorted(util["MfmaUtil"]):
+            if k not in KERNEL_SOURCES_BY_NAME:
+                continue
+            waves = inst["SQ_WAVES"].get(k, 0.0) or float("nan")
+            tflops = util["SQ_INSTS_VALU_MFMA_MOPS_BF16"].get(k, 0.0) * 512 / (avg_ns.get(k, float("nan")) * 1e-9) / 1e12
+            conflict = inst["SQ_LDS_BANK_CONFLICT"].get(k, 0.0) / max(1.0, inst["SQ_LDS_IDX_ACTIVE"].get(k, 0.0))
+            lines.append(f"| {k} | {util['MfmaUtil'][k]:.1f}% | {util['VALUBusy'].get(k, float('nan')):.1f}% | "
+                         f"{tflops:.1f} | {waves:.0f} | {inst['SQ_INSTS_VALU'].get(k, 0) / waves:.0f} | "
+                         f"{inst['SQ_INSTS_SALU'].get(k, 0) / waves:.0f} | {inst['SQ_INSTS_LDS'].get(k, 0) / waves:.0f} | "
+                         f"{inst['SQ_INSTS_MFMA'].get(k, 0) / waves:.0f} | {100 * conflict:.1f}% |")
+            if f"{k}@{w.name}" in entries:
+                entries[f"{k}@{w.name}"].update({"mfma_util_pct": util["MfmaUtil"][k],
+                                                 "valu_busy_pct": util["VALUBusy"].get(k),
+                                                 "bf16_mfma_tflops": tflops})
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", f"lisa_forward_{w.name}.md"), "w") as f:
+    with open(os.path.join(ROOT, "profiles", f"lisa_forward_{commands.get('name', w.name)}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     try:
         with open(COUNTERS) as f:
             c = json.load(f)
     except (OSError, ValueError):
         c = {}
-    if c.get("source_hash") != kernel_source_hash():
-        c = {"source_hash": kernel_source_hash(), "kernels": {}}
+    c.pop("source_hash", None)
+    c.setdefault("kernels", {})
+    c["kernels"] = {k: e for k, e in c["kernels"].items() if "source_hash" in e}
     c["kernels"].update(entries)
     c["copy_calibration"] = {"fetch_scale": f_scale, "write_scale": w_scale}
     with open(COUNTERS, "w") as f:
@@ -331,8 +371,9 @@ def main():
 
     if args.summarize_profiles:
         fixed = ("python3 bench.py --steps {s} --warmup {w} --no-cpu-baseline --forward-only --workload "
-                 + args.workload)
+                 + args.workload + ("" if args.schedule == "auto" else " --schedule " + args.schedule))
         summarize_profiles(args.summarize_profiles, args.workload, {
+            "name": args.workload + ("" if args.schedule == "auto" else "_" + args.schedule),
             "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace "
                      "-o trace -- " + fixed.format(s=200, w=20),
             "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o fetch -- "
@@ -342,6 +383,11 @@ def main():
             "copy": "rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE --output-format csv -d gpurun_out/pmc_copy_{fetch|write} "
                     "-o c{fetch|write} -- python3 bench.py --calibrate-copy-mib 256",
             "copy_mib": 256,
+            "util": "rocprofv3 --pmc MfmaUtil VALUBusy SQ_INSTS_VALU_MFMA_MOPS_BF16 --output-format csv "
+                    "-d gpurun_out/pmc_util -o util -- " + fixed.format(s=10, w=2),
+            "insts": "rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_INSTS_MFMA "
+                     "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE --output-format csv -d gpurun_out/pmc_insts -o insts -- "
+                     + fixed.format(s=10, w=2),
         })
         return
 

@@ -1,13 +1,17 @@
-"""CPU check of the resident forward kernel's static schedule.
+"""CPU checks of the two forward kernels' static schedules.
 
-tests/schedule_check.cpp includes the schedule header the kernel and the host
-planner use (vision_transformer_token_amd/csrc/lisa_resident.hpp) and checks
-exact coverage of every token, staging of every window cell a tile token
-needs, LDS bounds of every region, DMA run and slot-table row, and the
-combine partition, for the plan the library makes.  Here it is built with
-hipcc for the host only and run on every workload shape, the test suites'
-ragged and edge shapes, and the same shapes planned for devices with other
-compute-unit counts.
+tests/schedule_check.cpp includes the resident kernel's schedule header
+(vision_transformer_token_amd/csrc/lisa_resident.hpp) and checks exact
+coverage of every token, staging of every window cell a tile token needs,
+LDS bounds of every region, DMA run and slot-table row, and the combine
+partition.  tests/flow_schedule_check.cpp does the same for the streaming
+kernel (lisa_flow_schedule.hpp): tiles, token ranges, chunks, combine
+elements, groups and slices, staging bounds, the float quotients of the
+staging DMA, and that the stage order its producer waves walk is the one its
+consumer waves run.  Both use the library's own planners.  They are built
+with hipcc for the host only and run on every workload shape, the test
+suites' ragged and edge shapes, and the same shapes planned for devices with
+other compute-unit counts.
 """
 
 import os
@@ -18,6 +22,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "tests", "schedule_check.cpp")
+FLOW_SRC = os.path.join(ROOT, "tests", "flow_schedule_check.cpp")
 INC = os.path.join(ROOT, "vision_transformer_token_amd", "csrc")
 
 # (B * heads, H, W, T): the workloads and the GPU tests' shapes.
@@ -75,3 +80,37 @@ def test_headline_tiling(checker):
     res = subprocess.run([checker, "56", "56", "3", str(gcap(256, 32, 3136))], capture_output=True, text=True)
     assert res.returncode == 0, res.stdout
     assert "G=8 tiles 2x4 of 28x14" in res.stdout, res.stdout
+
+
+@pytest.fixture(scope="module")
+def flow_checker(tmp_path_factory):
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    exe = str(tmp_path_factory.mktemp("flow") / "flow_schedule_check")
+    res = subprocess.run([hipcc, "-O1", "-std=c++17", "-I", INC, FLOW_SRC, "-o", exe], capture_output=True, text=True)
+    assert res.returncode == 0, res.stdout + res.stderr
+    return exe
+
+
+@pytest.mark.parametrize("cus,xccs", [(256, 8), (304, 8), (80, 1), (32, 1)])
+def test_streaming_schedule_covers_exactly_once(flow_checker, cus, xccs):
+    args, count = [], 0
+    for bh, H, W, T in SHAPES + [(1, 56, 56, 16), (2, 13, 17, 12), (1, 20, 23, 16), (128, 9, 11, 9)]:
+        for es in (2, 4):
+            for per_token in (0, 1):
+                args += [str(v) for v in (H, W, T, bh, es, per_token, cus, xccs, gmax(H * W))]
+                count += 1
+    res = subprocess.run([flow_checker, *args], capture_output=True, text=True)
+    print(res.stdout[-3000:])
+    assert res.returncode == 0, res.stdout[-3000:] + res.stderr
+    assert res.stdout.count("ok ") == count, res.stdout[-3000:]
+
+
+def test_streaming_headline_plan(flow_checker):
+    """PVT-T stage 1 (32 slices of 56 x 56, bf16, per-token weights) on 256
+    compute units: eight ranks per slice, one slice per group."""
+    res = subprocess.run([flow_checker, "56", "56", "3", "32", "2", "1", "256", "8", str(gmax(3136))],
+                         capture_output=True, text=True)
+    assert res.returncode == 0, res.stdout
+    assert "G=8 S=32 Z=1 xcd=0" in res.stdout, res.stdout

@@ -10,6 +10,7 @@
 #include <cstring>
 
 #include "lisa.h"
+#include "lisa_flow_schedule.hpp"
 #include "lisa_kernels.hpp"
 
 namespace {
@@ -88,35 +89,14 @@ lisa_status check_problem(const lisa_problem* p) {
   return LISA_OK;
 }
 
-// Output tile: TR x TC cells made of whole 4 x 8 token blocks (the MFMA
-// local branch works on such blocks), at most kMaxTileTokens tokens, whose
-// staged inputs (TileLayout: K and V cells with a one-cell halo, Q rows,
-// per-token weights) fit one staging buffer.  Among those, the shape that
-// stages the fewest bytes per slice, counting each tile as kTileOverhead
-// bytes more (a stage has fixed costs), ties to the wider tile.
-constexpr long kTileOverhead = 8192;
-
+// The streaming kernel's output tiles (lisa::flow_plan_tiles).
 bool plan_tiles(Plan& pl, bool per_token_weights) {
-  const int es = (int)pl.esize;
-  const int stage = es == 2 ? lisa::Lds<2>::kStage : lisa::Lds<4>::kStage;
-  const int wT = per_token_weights ? pl.T : 0;
-  const int h4 = (pl.H + 3) / 4 * 4, w8 = (pl.W + 7) / 8 * 8;
-  long best = -1;
-  for (int tc = std::min(w8, 64); tc >= 8; tc -= 8)
-    for (int tr = 4; tr <= h4 && tr * tc <= lisa::kMaxTileTokens; tr += 4) {
-      const lisa::TileLayout L = lisa::tile_layout(tr, tc, wT, es);
-      if (L.total > stage) break;
-      const long ntiles = (long)((pl.W + tc - 1) / tc) * ((pl.H + tr - 1) / tr);
-      const long cost = ntiles * (L.total + kTileOverhead);
-      if (best < 0 || cost < best) {
-        best = cost;
-        pl.TR = tr;
-        pl.TC = tc;
-      }
-    }
-  if (best < 0) return false;
-  pl.tiles_x = (pl.W + pl.TC - 1) / pl.TC;
-  pl.ntiles = pl.tiles_x * ((pl.H + pl.TR - 1) / pl.TR);
+  lisa::FlowTiles ft;
+  if (!lisa::flow_plan_tiles(pl.H, pl.W, per_token_weights ? pl.T : 0, (int)pl.esize, ft)) return false;
+  pl.TR = ft.TR;
+  pl.TC = ft.TC;
+  pl.tiles_x = ft.tiles_x;
+  pl.ntiles = ft.ntiles;
   return true;
 }
 
@@ -133,16 +113,7 @@ bool plan_tiles(Plan& pl, bool per_token_weights) {
 #endif
 constexpr int kRoundSlices = LISA_ROUND_SLICES;
 
-int plan_ranks(int grid, int BH, int n) {
-  long per = (long)kRoundSlices * grid / BH;
-  const long tok = (n + 127) / 128;
-  if (per > grid) per = grid;
-  if (per > tok) per = tok;
-  if (per > lisa::kMaxRanks) per = lisa::kMaxRanks;
-  int G = 1;
-  while (2L * G <= per) G *= 2;
-  return G;
-}
+int plan_ranks(int grid, int BH, int n) { return lisa::flow_plan_ranks(grid, BH, n, kRoundSlices); }
 
 // The forward's regions of a workspace, from offset 0: the launch counters
 // first, sized for `counter_slices` slices, at offsets and sizes that do not
@@ -373,22 +344,11 @@ lisa_status run(Plan pl, Mode mode, const void* Q, const void* K, const void* V,
   if (stamps) return LISA_ERR_UNSUPPORTED;  // the stage timeline is the resident kernel's
   if (!plan_tiles(pl, weights != nullptr || mlp != nullptr)) return LISA_ERR_UNSUPPORTED;
   pl.grid = dinfo.cus;
-  pl.G = plan_ranks(pl.grid, pl.BH, pl.n);
-  if (pl.G > pl.gmax) pl.G = pl.gmax;
-  pl.S = pl.grid / pl.G;
-  // Slices per round: all of the group's slices, at most 4.
-  pl.Z = std::min(4, (pl.BH + pl.S - 1) / pl.S);
-  // Where a group's workgroups run.  Pairs (G <= 2) stay on one XCD (the
-  // device hands workgroup w to XCD w % kXcds, so rank tickets are drawn per
-  // XCD): their many small hand-offs then start and finish together.  Larger
-  // groups take tickets from one counter in start order and so spread over
-  // all XCDs: when they were kept on one XCD, an XCD that fell behind in the
-  // HBM-bound KV and M phases held back every group on it (a PVT stage-1
-  // forward, G = 16: 61 us on one XCD, 58 us spread; G = 4 and 8 about even).
-  pl.xcd_groups = (dinfo.xccs == lisa::kXcds && pl.G <= 2 && pl.grid % lisa::kXcds == 0 &&
-                   (pl.grid / lisa::kXcds) % pl.G == 0)
-                      ? 1
-                      : 0;
+  const lisa::FlowGroups fg = lisa::flow_plan_groups(pl.grid, dinfo.xccs, pl.BH, pl.n, pl.gmax, kRoundSlices);
+  pl.G = fg.G;
+  pl.S = fg.S;
+  pl.Z = fg.Z;
+  pl.xcd_groups = fg.xcd_groups;
   a.chunk = pl.chunk;
   a.G = pl.G;
   a.S = pl.S;

@@ -132,10 +132,6 @@ __device__ __forceinline__ float group_sum16(float x) { return dpp_add(group_sum
 // Index of this thread's wave in the workgroup, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
-// q = floor(x / d) for 0 <= x < 2^20, 0 < d < 2^10, via a float reciprocal
-// (inv_d = 1.0f / d): (x + 0.5) / d lies at least 0.5 / d from an integer, far
-// more than the rounding error of the product.
-__device__ __forceinline__ int div_small(int x, float inv_d) { return (int)(((float)x + 0.5f) * inv_d); }
 
 // ---------------------------------------------------------------------------
 // Swizzled LDS rows.  A staged 64-wide row (a token's features, or a grid

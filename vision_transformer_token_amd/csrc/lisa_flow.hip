@@ -29,6 +29,7 @@
 #include <type_traits>
 
 #include "lisa_device.hpp"
+#include "lisa_flow_schedule.hpp"
 #include "lisa_kernels.hpp"
 
 namespace lisa {
@@ -37,88 +38,7 @@ namespace {
 template <class Tr>
 using LdsOf = Lds<(int)sizeof(typename Tr::S)>;
 
-enum Phase { kPKV = 0, kPM = 1, kPC = 2, kPOut = 3, kPEnd = 4 };
 enum Counter { kCntKV = 0, kCntM = 1, kCntC = 2 };
-
-// This workgroup's place in the schedule.
-struct Rank {
-  int group, g;       // group (-1: idle workgroup), rank within the group
-  int tok0, ntok;     // token range of each slice
-  int nch;            // chunks of that range
-  int t0, nt;         // output tiles
-  int e0, E;          // combine elements of the flattened [phi(K)^T V | M]
-};
-
-// Ranks are handed out in the order workgroups start (a ticket per XCD when
-// groups stay within an XCD): a group then only ever waits for workgroups
-// that are already running, so the launch makes progress as long as G
-// workgroups fit on the device at once.  `ticket` comes from take_ticket.
-__device__ __forceinline__ Rank make_rank(const FlowArgs& a, int ticket) {
-  Rank r;
-  if (a.xcd_groups) {
-    r.group = (blockIdx.x % kXcds) * (a.S / kXcds) + ticket / a.G;
-    if (ticket / a.G >= a.S / kXcds) r.group = -1;
-  } else {
-    r.group = ticket / a.G;
-    if (r.group >= a.S) r.group = -1;
-  }
-  r.g = ticket % a.G;
-  r.tok0 = (int)((long long)r.g * a.n / a.G);
-  r.ntok = (int)((long long)(r.g + 1) * a.n / a.G) - r.tok0;
-  r.nch = (r.ntok + a.chunk - 1) / a.chunk;
-  r.t0 = (int)((long long)r.g * a.ntiles / a.G);
-  r.nt = (int)((long long)(r.g + 1) * a.ntiles / a.G) - r.t0;
-  r.E = 2 * kD * kD / a.G;
-  r.e0 = r.g * r.E;
-  return r;
-}
-
-// A stage: round r of the group's slices, phase `ph`, slice z of the round
-// (slice b = group + (r Z + z) S), step j (chunk or tile index in the rank's
-// range).  A round runs each phase for all its slices before the next phase,
-// so a slice's dependency wait overlaps the other slices' stages.
-struct Pos {
-  int r, ph, z, j;
-};
-__device__ __forceinline__ int slice_of(const FlowArgs& a, const Rank& rk, int r, int z) {
-  return rk.group + (r * a.Z + z) * a.S;
-}
-// Slices in round r (0: past the group's last slice).
-__device__ __forceinline__ int round_slices(const FlowArgs& a, const Rank& rk, int r) {
-  const int b0 = slice_of(a, rk, r, 0);
-  if (rk.group < 0 || b0 >= a.BH) return 0;
-  return min(a.Z, (a.BH - b0 + a.S - 1) / a.S);
-}
-__device__ __forceinline__ int phase_len(const FlowArgs& a, const Rank& r, int ph) {
-  switch (ph) {
-    case kPKV: return a.do_kv ? r.nch : 0;
-    case kPM: return a.do_m ? r.nch : 0;
-    case kPC: return a.do_kv ? 1 : 0;
-    case kPOut: return a.do_out ? r.nt : 0;
-  }
-  return 0;
-}
-// The stage after `p` (ph == kPEnd: none); empty phases are skipped.
-__device__ Pos advance(const FlowArgs& a, const Rank& rk, Pos p) {
-  if (p.ph != kPEnd) {
-    if (p.j + 1 < phase_len(a, rk, p.ph)) return Pos{p.r, p.ph, p.z, p.j + 1};
-    if (p.z + 1 < round_slices(a, rk, p.r)) return Pos{p.r, p.ph, p.z + 1, 0};
-  }
-  int r = p.r, ph = p.ph + 1;
-  for (;;) {
-    if (ph >= kPEnd) {
-      ++r;
-      ph = kPKV;
-      if (round_slices(a, rk, r) == 0) return Pos{r, kPEnd, 0, 0};
-    }
-    if (phase_len(a, rk, ph) > 0) return Pos{r, ph, 0, 0};
-    ++ph;
-  }
-}
-__device__ __forceinline__ Pos first_pos(const FlowArgs& a, const Rank& rk) {
-  if (round_slices(a, rk, 0) == 0) return Pos{0, kPEnd, 0, 0};
-  return advance(a, rk, Pos{-1, kPEnd, 0, 0});
-}
 
 // The counter a rank's arrival for phase `counter` of slice b goes to.
 template <int kVar>
@@ -145,20 +65,9 @@ __device__ __forceinline__ void arrive_rank(unsigned* c, int* waves) {
   }
 }
 
-__device__ __forceinline__ void tile_origin(const FlowArgs& a, int t, int& r0, int& c0) {
-  r0 = (t / a.tiles_x) * a.TR;
-  c0 = (t % a.tiles_x) * a.TC;
-}
-
 template <class Tr>
 __device__ __forceinline__ TileLayout layout_of(const FlowArgs& a) {
   return tile_layout(a.TR, a.TC, (a.weights || a.mlp_w1f) ? a.T : 0, (int)sizeof(typename Tr::S));
-}
-
-// Chunk j of the rank's range: first token and length.
-__device__ __forceinline__ void chunk_of(const FlowArgs& a, const Rank& r, int j, int& tok0, int& nv) {
-  tok0 = r.tok0 + j * a.chunk;
-  nv = min(a.chunk, r.tok0 + r.ntok - tok0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1159,7 +1068,7 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
     last = (int)bump(a.tickets + (a.xcd_groups ? blockIdx.x % kXcds : 0));
   }
   __syncthreads();
-  const Rank rk = make_rank(a, last);
+  const Rank rk = make_rank(a, last, blockIdx.x % kXcds);
   // The roles run separate loops over the same stage sequence, with the same
   // barriers: one per stage, plus one at the start of each OUT phase.
   if (producer) {

@@ -50,6 +50,11 @@ constexpr int kMaxSubs = 256 / kSubRanks;
 // plain arrivals and combine).
 constexpr int kVarPlain = 0, kVarGrouped = 1, kVarSolo = 2, kVarElu = 3;
 
+// q = floor(x / d) for 0 <= x < 2^20, 0 < d < 2^10, via a float reciprocal
+// (inv_d = 1.0f / d): (x + 0.5) / d lies at least 0.5 / d from an integer, far
+// more than the rounding error of the product.
+__host__ __device__ __forceinline__ int div_small(int x, float inv_d) { return (int)(((float)x + 0.5f) * inv_d); }
+
 // LDS of one workgroup, per element size ES: two staging buffers of kStage
 // bytes that the DMA of the next stage and the compute of the current one
 // alternate between, then the statistics area (the two 64x64 MFMA fragment
