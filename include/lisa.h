@@ -95,14 +95,16 @@ typedef enum lisa_feature { LISA_FEATURE_RELU = 0, LISA_FEATURE_ELU = 1 } lisa_f
 /* Which forward kernel runs the pass.  Both compute the same quantities in
  * the same precision; they differ in schedule and so in the order of the
  * fp32 sums over tokens.
- *   AUTO      : the library's choice for the problem and device (zero).
+ *   AUTO      : the library's choice for the problem and device (zero): the
+ *               resident kernel wherever it applies, else the streaming one.
  *   STREAMING : workgroups stream tiles through LDS in three passes over K
  *               (statistics, then the rescaled keys, then the output).
  *   RESIDENT  : each workgroup holds its tile of Q, K, V on chip for the
- *               whole pass (bf16 ReLU problems whose tiles fit: T <= 8,
- *               no predictor); LISA_ERR_UNSUPPORTED where it does not apply.
- * lisa_forward, lisa_reduce, lisa_apply and lisa_forward_mlp of one problem
- * (same struct, same device) take the same kernel and so form the same sums. */
+ *               whole pass (bf16 ReLU problems with T <= 8 whose tiles fit
+ *               a workgroup); LISA_ERR_UNSUPPORTED where it does not apply.
+ * lisa_forward, lisa_reduce, lisa_apply, lisa_forward_mlp and the backward's
+ * statistics of one problem (same struct, same device) take the same kernel
+ * and so form the same sums. */
 typedef enum lisa_schedule {
   LISA_SCHEDULE_AUTO = 0,
   LISA_SCHEDULE_STREAMING = 1,

@@ -57,9 +57,10 @@ static void check(int H, int W, int T, int gcap) {
   CHECK(L.tab >= L.w + res_up(slots * T, 64) * 4, "w region");
   CHECK(L.s >= L.tab + slots * 2, "tab region");
   CHECK(L.scr >= L.s + 64 * 4, "s region");
-  CHECK(L.total >= L.scr + kResScratch && L.total >= L.scr + 2 * 64 * 64 * 2, "scr region");
+  CHECK(L.st >= L.scr + kResScratch && L.st >= L.scr + 2 * 64 * 64 * 2, "scr region");
+  CHECK(L.total >= L.st + (p.G == 1 ? 2 * 64 * 64 * 4 : 0), "st region");
   CHECK(L.k % 1024 == 0 && L.v % 1024 == 0 && L.w % 256 == 0 && L.tab % 16 == 0 && L.s % 16 == 0 &&
-            L.scr % 16 == 0,
+            L.scr % 16 == 0 && L.st % 16 == 0,
         "alignment");
   std::vector<int> owner((size_t)H * W, -1);
   for (int g = 0; g < p.G; ++g) {

@@ -232,19 +232,19 @@ enum class Mode { kForward, kReduce, kApply };
 // lisa_apply and the backward's statistics of one problem all cut the slices
 // the same way and form the same fixed-order sums.
 bool resident_fits(const Plan& pl, int cus, bool mlp, lisa::ResPlan& rp) {
-  if (pl.dtype != LISA_BF16 || pl.feature != LISA_FEATURE_RELU || mlp || pl.T > lisa::kResMaxT) return false;
+  (void)mlp;  // the predictor runs inside the resident kernel too
+  if (pl.dtype != LISA_BF16 || pl.feature != LISA_FEATURE_RELU || pl.T > lisa::kResMaxT) return false;
   const int gcap = std::min(std::max(1, cus / pl.BH), plan_ranks(lisa::kMaxRanks, kRoundSlices, pl.n));
   return lisa::res_plan(pl.H, pl.W, pl.T, true, gcap, rp);
 }
 
-// The default between the two kernels where both apply.  Measured on MI355X
-// (256 CUs, bf16, T = 3 or 5): where a slice has one rank the two are even
-// (DeiT-T at 224, 192 slices of 14 x 14: 37.4 against 37.2 us); with several
-// ranks per slice the resident kernel's serial stages still cost more than
-// the streaming kernel's overlapped ones (PVT-T stage 1, 32 slices of
-// 56 x 56 on eight ranks each: 52 against 47 us; one 200 x 320 slice: 61
-// against 51 us).
-bool resident_preferred(const lisa::ResPlan& rp) { return rp.G == 1; }
+// The default between the two kernels where both apply: the resident one.
+// Measured on MI355X (256 CUs, bf16), forward of one call, resident against
+// streaming: PVT-T stage 1 (32 slices of 56 x 56, T = 3) 45.0 / 45.7 us;
+// DeiT-T at 224 (192 slices of 14 x 14, T = 3) 24.5 / 37.0 us; one 200 x 320
+// slice (T = 5) 46.8 / 50.2 us; one 128 x 128 slice 31.9 / 35.4 us; one
+// 256 x 256 slice 43.9 / 49.9 us.
+bool resident_preferred(const lisa::ResPlan&) { return true; }
 
 // Whether the resident kernel runs the problem: where it fits, when asked
 // for, and by default where it is the faster of the two kernels.
@@ -257,9 +257,17 @@ bool resident_plan(const Plan& pl, int cus, bool mlp, lisa::ResPlan& rp) {
 // One launch of the resident kernel, one workgroup per compute unit.
 lisa_status run_resident(const Plan& pl, const lisa::ResPlan& rp, int cus, Mode mode, const void* Q, const void* K,
                          const void* V, const float* weights, float beta, const float* alpha, void* Y, char* ws,
-                         float eps, hipStream_t s, bool clear_err, unsigned long long* stamps = nullptr) {
+                         float eps, hipStream_t s, bool clear_err, unsigned long long* stamps = nullptr,
+                         const lisa_weight_mlp* mlp = nullptr, const void* mlp_frag = nullptr) {
   lisa::ResArgs a{};
   a.stamps = stamps;
+  if (mlp) {
+    a.mlp_w1f = mlp_frag;
+    a.mlp_b1 = mlp->b1;
+    a.mlp_w2 = mlp->w2;
+    a.mlp_b2 = mlp->b2;
+    a.hidden = mlp->hidden;
+  }
   a.Q = Q;
   a.K = K;
   a.V = V;
@@ -280,7 +288,7 @@ lisa_status run_resident(const Plan& pl, const lisa::ResPlan& rp, int cus, Mode 
   a.mode = mode == Mode::kForward ? lisa::kResForward : mode == Mode::kReduce ? lisa::kResReduce : lisa::kResApply;
   a.do_kv = (mode == Mode::kReduce || (mode == Mode::kForward && pl.T >= 2)) ? 1 : 0;
   a.do_m = (mode == Mode::kReduce || (mode == Mode::kForward && pl.T >= 3)) ? 1 : 0;
-  a.per_token = weights != nullptr ? 1 : 0;
+  a.per_token = (weights != nullptr || mlp != nullptr) ? 1 : 0;
   a.grouped = (rp.G >= 64 && pl.BH <= lisa::kMaxSubSlices) ? 1 : 0;
   a.part_s = reinterpret_cast<float*>(ws + pl.part_s);
   a.part_kv = reinterpret_cast<float*>(ws + pl.part_kv);
@@ -337,10 +345,9 @@ lisa_status run(Plan pl, Mode mode, const void* Q, const void* K, const void* V,
   if (!device_info(dinfo)) return LISA_ERR_HIP;
   lisa::ResPlan rp;
   if (resident_plan(pl, dinfo.cus, mlp != nullptr, rp))
-    return run_resident(pl, rp, dinfo.cus, mode, Q, K, V, weights, beta, alpha, Y, ws, eps, s, clear_err, stamps);
-  // The resident kernel asked for and not applicable (the predictor's output
-  // pass after a resident reduce is the streaming kernel's by design).
-  if (pl.schedule == LISA_SCHEDULE_RESIDENT && !mlp) return LISA_ERR_UNSUPPORTED;
+    return run_resident(pl, rp, dinfo.cus, mode, Q, K, V, weights, beta, alpha, Y, ws, eps, s, clear_err, stamps,
+                        mlp, mlp_frag);
+  if (pl.schedule == LISA_SCHEDULE_RESIDENT) return LISA_ERR_UNSUPPORTED;  // asked for, not applicable
   if (stamps) return LISA_ERR_UNSUPPORTED;  // the stage timeline is the resident kernel's
   if (!plan_tiles(pl, weights != nullptr || mlp != nullptr)) return LISA_ERR_UNSUPPORTED;
   pl.grid = dinfo.cus;
@@ -583,20 +590,6 @@ lisa_status lisa_forward_mlp(const lisa_problem* p, const void* Q, const void* K
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (lisa::launch_mlp_prep(pl.dtype, mlp->w1, ws + frag_at, pl.heads, mlp->hidden, s) != hipSuccess)
     return LISA_ERR_HIP;
-  // Where the resident kernel forms this problem's statistics for the other
-  // entry points, it forms them here too (the statistics alone), and the
-  // predictor's output pass reads them from the workspace: the statistics a
-  // backward pass may take over are then those lisa_backward forms.
-  DeviceInfo dinfo;
-  if (!device_info(dinfo)) return LISA_ERR_HIP;
-  lisa::ResPlan rp;
-  const bool resident = pl.T >= 2 && resident_plan(pl, dinfo.cus, false, rp);
-  if (pl.schedule == LISA_SCHEDULE_RESIDENT && !resident) return LISA_ERR_UNSUPPORTED;
-  if (resident) {
-    st = run(pl, Mode::kReduce, Q, K, V, nullptr, 0.f, nullptr, nullptr, ws, p->eps, s);
-    if (st != LISA_OK) return st;
-    return run(pl, Mode::kApply, Q, K, V, nullptr, 0.f, alpha, Y, ws, p->eps, s, mlp, ws + frag_at);
-  }
   return run(pl, Mode::kForward, Q, K, V, nullptr, 0.f, alpha, Y, ws, p->eps, s, mlp, ws + frag_at);
 }
 

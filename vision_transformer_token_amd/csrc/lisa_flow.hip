@@ -315,9 +315,6 @@ __device__ __forceinline__ float sum_s_partials(const FlowArgs& a, int b) {
 // zero) and B = the hidden values; its accumulator element e of lane (n, h)
 // is logit 4 h + e of token n.  A lane's W2 and b1 operands are gathered
 // from their natural layouts together with its W1 operands.
-__host__ __device__ inline size_t mlp_head_floats(int hidden, bool bf16) {
-  return (size_t)hidden * (bf16 ? 64 : 128);
-}
 
 template <class Tr>
 struct MlpRegs {

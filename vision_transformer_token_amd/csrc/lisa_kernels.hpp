@@ -151,6 +151,11 @@ struct FlowArgs {
 };
 
 constexpr int kMaxHidden = 128;
+// Floats of one head's first-layer weights as mlp_prep lays them out for the
+// MFMA (bf16: [hidden/32][8 steps][64 lanes] bf16x8; fp32: [hidden/32][64 steps][64 lanes]).
+__host__ __device__ inline size_t mlp_head_floats(int hidden, bool bf16) {
+  return (size_t)hidden * (bf16 ? 64 : 128);
+}
 
 // The resident forward kernel (lisa_resident.hip): one tile of a slice per
 // rank, staged on chip once (ResPlan).  Modes: the whole forward, the
@@ -189,6 +194,14 @@ struct ResArgs {
   unsigned* tickets;      // [kXcds]
   unsigned* err;
   int clear_err;
+  // The walk-weight predictor (forward only; nullptr: weights or geo):
+  // W1 as laid out by mlp_prep (bf16 fragments), b1 [heads][hidden],
+  // W2 [heads][T][hidden], b2 [heads][T].
+  const void* mlp_w1f;
+  const float* mlp_b1;
+  const float* mlp_w2;
+  const float* mlp_b2;
+  int hidden;
   // Optional stage timeline: workgroup w writes the constant-clock counter
   // (s_memrealtime, 100 MHz) at stage k of its first slice to
   // stamps[w * kResPhases + k] (kResStamp*), and its group and rank to the

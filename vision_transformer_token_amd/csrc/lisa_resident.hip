@@ -19,9 +19,9 @@
 //   after all M partials: its share of the fixed-order sum of the partials
 //     (statistics as fp32 and as MFMA fragments), published;
 //   after all shares: the walk of its tokens on MFMA, Y written once.
-// All four waves (one per SIMD, 512 registers each) do every step; waits on
-// other ranks are polled by one wave while the others sit at the workgroup
-// barrier.
+// All eight waves (two per SIMD, 256 registers each) do every step; waits
+// on other ranks are polled by one wave while the others sit at the
+// workgroup barrier.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -124,8 +124,8 @@ __device__ void res_wait(const ResArgs& a, int b, int c) {
 // SR x SC region, row-major) into swizzled 128-byte rows, 1 KB per wave
 // instruction, waves taking runs in turn; the last run is padded with copies
 // of the last cell.
-__device__ void res_dma_cells(unsigned char* lds, const uint16_t* src, int W, const ResTile& t, int wave) {
-  const int lane = threadIdx.x & 63;
+__device__ void res_dma_cells(unsigned char* lds, const uint16_t* src, int W, const ResTile& t, int wave, int tid) {
+  const int lane = tid & 63;
   const int nrow = t.SR * t.SC;
   const float inv_sc = 1.f / (float)t.SC;
   for (int base = wave * 64; base < nrow * 8; base += 64 * kResWaves) {
@@ -141,8 +141,8 @@ __device__ void res_dma_cells(unsigned char* lds, const uint16_t* src, int W, co
 // DMA of the per-token walk weights of the tile's slots ([slot][T] fp32),
 // 4 bytes per lane; a masked slot takes the tile origin's row.
 __device__ void res_dma_weights(unsigned char* lds, const float* wb, const ResPlan& p, const ResTile& t,
-                                int wave) {
-  const int lane = threadIdx.x & 63;
+                                int wave, int tid) {
+  const int lane = tid & 63;
   const int T = p.T, cnt = p.nblk * 32 * T;
   const float inv_t = 1.f / (float)T;
   for (int e0 = wave * 64; e0 < cnt; e0 += 64 * kResWaves) {
@@ -176,14 +176,14 @@ __device__ __forceinline__ v8s rows_at(const unsigned char* base, int ra, int rb
 // Steps [k0, k1) of 16 slots: acc += phi(K)^T X over the slots, X = the
 // slots' V cells (KV sweep) or their rescaled Q rows (M sweep, by slot), and
 // acc_s += phi(K)^T 1 when kWithS.  Wave output block (mb, nb) of 32 x 32.
-// Steps go in batches of 8, then 4 and 2 (k1 - k0 is even): every operand
+// Steps go in batches of 4, then 2 (k1 - k0 is even): every operand
 // read of a batch (slot-table rows first, then the transposed reads) is
 // issued before its first MFMA, and even and odd steps accumulate into two
 // chains that are added at the end.
 template <bool kIsM, bool kWithS>
 __device__ __forceinline__ void res_sweep(const unsigned char* smem, const ResLayout& L, int k0, int k1, int mb,
-                                          int nb, f32x16& acc, f32x16& acc_s) {
-  const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
+                                          int nb, f32x16& acc, f32x16& acc_s, int tid) {
+  const int lane = tid & 63, i = lane & 15, g = lane >> 4;
   const int colA = 32 * mb + 16 * (g & 1) + 4 * (i & 3);
   const int colB = 32 * nb + 16 * (g & 1) + 4 * (i & 3);
   const uint16_t* tab = reinterpret_cast<const uint16_t*>(smem + L.tab);
@@ -218,11 +218,7 @@ __device__ __forceinline__ void res_sweep(const unsigned char* smem, const ResLa
     }
   };
   int k = k0;
-  for (; k + 8 <= k1; k += 8) batch(std::integral_constant<int, 8>{}, k);
-  if (k + 4 <= k1) {
-    batch(std::integral_constant<int, 4>{}, k);
-    k += 4;
-  }
+  for (; k + 4 <= k1; k += 4) batch(std::integral_constant<int, 4>{}, k);
   if (k + 2 <= k1) batch(std::integral_constant<int, 2>{}, k);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -231,39 +227,78 @@ __device__ __forceinline__ void res_sweep(const unsigned char* smem, const ResLa
   }
 }
 
-// One sweep of the rank's slots by the four waves (wave w: output block w of
-// the 64 x 64 result, every slot) and the publication of its partial:
-// [phi(K)^T V or M] as fp32 rows, and s (KV sweep, waves of the first column
-// block) as 64 fp32.
+// One sweep of the rank's slots and the publication of its partial:
+// [phi(K)^T V or M] as fp32 rows, and s (KV sweep) as 64 fp32.  Waves w and
+// w + 4 compute output block (w >> 1, w & 1) of the 64 x 64 result, over the
+// first ceil(nblk / 2) blocks' slots and over the rest; the second wave
+// leaves its products in the scratch area and the first adds them (first
+// half + second half) and stores the block.  s comes from the waves of the
+// first column block.
 template <bool kIsM>
-__device__ void res_sweep_publish(const ResArgs& a, unsigned char* smem, int b, int g) {
+__device__ void res_sweep_publish(const ResArgs& a, unsigned char* smem, int b, int g, int tid) {
   const ResLayout& L = a.p.L;
-  const int wave = wave_id(), lane = threadIdx.x & 63, m = lane & 31, h = lane >> 5;
-  const int mb = wave >> 1, nb = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, m = lane & 31, h = lane >> 5;
+  const int pw = wave & 3, half = wave >> 2;
+  const int mb = pw >> 1, nb = pw & 1;
   const bool with_s = !kIsM && nb == 0;
+  const int h0 = (a.p.nblk + 1) / 2;
+  const int k0 = half ? 2 * h0 : 0, k1 = half ? 2 * a.p.nblk : 2 * h0;
   f32x16 acc = {}, acc_s = {};
   // The ones product (s) as a variant of its own: no branch among the MFMAs.
   if (with_s)
-    res_sweep<kIsM, true>(smem, L, 0, a.p.nblk * 2, mb, nb, acc, acc_s);
+    res_sweep<kIsM, true>(smem, L, k0, k1, mb, nb, acc, acc_s, tid);
   else
-    res_sweep<kIsM, false>(smem, L, 0, a.p.nblk * 2, mb, nb, acc, acc_s);
-  if (!kIsM) res_stamp(a, b < a.S, kResStampKVSweep);
-  float* part = (kIsM ? a.part_m : a.part_kv) + ((size_t)b * a.p.G + g) * (kD * kD);
+    res_sweep<kIsM, false>(smem, L, k0, k1, mb, nb, acc, acc_s, tid);
+  float* red = reinterpret_cast<float*>(smem + L.scr);  // [4][16][64], then s: [2][2][16]
+  if (half) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) put(part + (32 * mb + 8 * (i >> 2) + 4 * h + (i & 3)) * kD + 32 * nb + m, acc[i]);
-  if (with_s && m == 0) {
-    float* ps = a.part_s + ((size_t)b * a.p.G + g) * kD;
+    for (int i = 0; i < 16; ++i) red[(pw * 16 + i) * 64 + lane] = acc[i];
+    if (with_s && m == 0) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) put(ps + 32 * mb + 8 * (i >> 2) + 4 * h + (i & 3), acc_s[i]);
+      for (int i = 0; i < 16; ++i) red[4 * 16 * 64 + (mb * 2 + h) * 16 + i] = acc_s[i];
+    }
   }
-  res_arrive(a, b, g, kIsM ? kRcM : kRcKV);
+  lds_barrier();
+  if (!kIsM) res_stamp(a, b < a.S, kResStampKVSweep);
+  // One rank per slice (forward): the sum is the statistic itself, left as
+  // fp32 rows in LDS for this rank's output and in the workspace for the
+  // entry points that read it later; no partial, no arrival.
+  const bool direct = a.p.G == 1 && a.mode == kResForward;
+  if (!half) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] += red[(pw * 16 + i) * 64 + lane];
+    float* dst = direct ? (kIsM ? a.fin_m : a.fin_kv) + (size_t)b * (kD * kD)
+                        : (kIsM ? a.part_m : a.part_kv) + ((size_t)b * a.p.G + g) * (kD * kD);
+    float* st = reinterpret_cast<float*>(smem + L.st) + (kIsM ? kD * kD : 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = (32 * mb + 8 * (i >> 2) + 4 * h + (i & 3)) * kD + 32 * nb + m;
+      put(dst + e, acc[i]);
+      if (direct) st[e] = acc[i];
+    }
+    if (with_s && m == 0) {
+      float* ps = direct ? a.fin_s + (size_t)b * kD : a.part_s + ((size_t)b * a.p.G + g) * kD;
+      float* s_lds = reinterpret_cast<float*>(smem + L.s);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int e = 32 * mb + 8 * (i >> 2) + 4 * h + (i & 3);
+        const float v = acc_s[i] + red[4 * 16 * 64 + (mb * 2 + h) * 16 + i];
+        put(ps + e, v);
+        if (direct) s_lds[e] = v;
+      }
+    }
+  }
+  if (direct)
+    lds_barrier();
+  else
+    res_arrive(a, b, g, kIsM ? kRcM : kRcKV);
 }
 
 // s = the fixed-order sum of the slice's G partials, into LDS: wave w sums
 // partials w, w + 4, ... (sixteen loads in flight at a time), then wave 0
 // adds the four sums in wave order.
-__device__ void res_sum_s(const ResArgs& a, unsigned char* smem, int b) {
-  const int wave = wave_id(), lane = threadIdx.x & 63, G = a.p.G;
+__device__ void res_sum_s(const ResArgs& a, unsigned char* smem, int b, int tid) {
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, G = a.p.G;
   float* sw = reinterpret_cast<float*>(smem + a.p.L.scr);  // [waves][64]
   const float* ps = a.part_s + (size_t)b * G * kD + lane;
   const int np = (G - wave + kResWaves - 1) / kResWaves;
@@ -320,12 +355,11 @@ __device__ __forceinline__ void res_combine_store(const ResArgs& a, float* stg, 
 // The G partials' elements (G E <= nstat + G floats) are first staged in the
 // K region (free after the sweeps) as [G][E] floats: each thread issues its
 // loads at once (a single round trip), then writes them to LDS.
-// Then tpe threads share an element (partials q, q + tpe, ... each) and
-// combine by a fixed xor tree, so the order of additions depends on G alone.
+// Then the G partials of each element are added in an order fixed by G.
 // With one rank per slice the totals stay in the staging, in row order,
 // where the output takes them.
-__device__ void res_combine(const ResArgs& a, unsigned char* smem, int b, int g, int nstat) {
-  const int tid = threadIdx.x, G = a.p.G;
+__device__ void res_combine(const ResArgs& a, unsigned char* smem, int b, int g, int nstat, int tid) {
+  const int G = a.p.G;
   int e0, e1;
   res_combine_range(nstat, G, g, e0, e1);
   const int E = e1 - e0, total = G * E;
@@ -344,40 +378,36 @@ __device__ void res_combine(const ResArgs& a, unsigned char* smem, int b, int g,
 #pragma unroll
   for (int i = 0; i < kPer; ++i)
     if (tid + kResThreads * i < total) stg[tid + kResThreads * i] = x[i];
-  __syncthreads();
+  lds_barrier();
   res_stamp(a, b < a.S, kResStampCStaged);
-  int tpe = 1;
-  while (tpe < 64 && 2 * tpe * E <= kResThreads) tpe *= 2;
-  const int per = kResThreads / tpe;
   const bool frags = a.mode == kResReduce;
-  // Four elements at a time, their staged partials read four at a time (up
-  // to sixteen LDS reads in flight); each element's partials are added in
-  // the order q, q + tpe, ...
-  const int q = tid % tpe;
-  for (int base = 0; base < E; base += 4 * per) {
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    int ec[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) ec[k] = min(base + k * per + tid / tpe, E - 1);
-    for (int p0 = q; p0 < G; p0 += 4 * tpe) {
-      float x[4][4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) x[k][u] = p0 + u * tpe < G ? stg[(p0 + u * tpe) * E + ec[k]] : 0.f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[k] += x[k][u];
+  // Consecutive threads take consecutive elements of one partial (no LDS
+  // bank conflicts).  Fewer than kResThreads / 2 elements: ngrp groups of E
+  // threads, group k adding partials k, k + ngrp, ... in turn; then thread e
+  // adds the groups' sums in group order.  More: each thread adds all G
+  // partials of its elements in turn.  Either way the order of additions
+  // depends on G alone.
+  if (2 * E > kResThreads) {
+    for (int e = tid; e < E; e += kResThreads) {
+      float v = 0.f;
+#pragma unroll 4
+      for (int pp = 0; pp < G; ++pp) v += stg[pp * E + e];
+      res_combine_store(a, stg, b, G, e0, e, e, v, frags);
     }
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      for (int o = 1; o < tpe; o <<= 1) v[k] += __shfl_xor(v[k], o);
-    __syncthreads();  // every read of this round is done before totals are written back (one rank)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int e = base + k * per + tid / tpe;
-      if (e < E && q == 0) res_combine_store(a, stg, b, G, e0, e, ec[k], v[k], frags);
+  } else {
+    const int ngrp = kResThreads / E, e = tid % E, pg = tid / E;
+    float* sums = reinterpret_cast<float*>(smem + a.p.L.scr);  // [ngrp][E]
+    if (pg < ngrp) {
+      float v = 0.f;
+#pragma unroll 4
+      for (int pp = pg; pp < G; pp += ngrp) v += stg[pp * E + e];
+      sums[pg * E + e] = v;
+    }
+    lds_barrier();
+    if (tid < E) {
+      float v = 0.f;
+      for (int k = 0; k < ngrp; ++k) v += sums[k * E + tid];
+      res_combine_store(a, stg, b, G, e0, tid, tid, v, frags);
     }
   }
   if (g == 0 && tid < kD) put(a.fin_s + (size_t)b * kD + tid, reinterpret_cast<const float*>(smem + a.p.L.s)[tid]);
@@ -386,8 +416,7 @@ __device__ void res_combine(const ResArgs& a, unsigned char* smem, int b, int g,
 
 // The slice statistics [phi(K)^T V | M] as fp32 rows (nstat floats) from the
 // workspace into the K region: 8-byte coherent loads, all in flight at once.
-__device__ void res_stats_to_lds(const ResArgs& a, unsigned char* smem, int b, int nstat) {
-  const int tid = threadIdx.x;
+__device__ void res_stats_to_lds(const ResArgs& a, unsigned char* smem, int b, int nstat, int tid) {
   uint64_t* dst = reinterpret_cast<uint64_t*>(smem + a.p.L.k);
   constexpr int kPer = 2 * kD * kD / 2 / kResThreads;  // 8-byte pieces per thread
   uint64_t x[kPer];
@@ -405,9 +434,9 @@ __device__ void res_stats_to_lds(const ResArgs& a, unsigned char* smem, int b, i
 // MFMA A-operand fragments (bf16, 8 KB) of a 64 x 64 matrix from its fp32
 // rows in LDS: piece (mb, q, lane) holds X[dimof(8 q + j, lane / 32)][32 mb +
 // lane % 32], j = 0..7, as 16 bytes.
-__device__ void res_frags_from_rows(const float* st, unsigned char* frag) {
+__device__ void res_frags_from_rows(const float* st, unsigned char* frag, int tid) {
   uint4* dst = reinterpret_cast<uint4*>(frag);
-  for (int pc = threadIdx.x; pc < 512; pc += kResThreads) {
+  for (int pc = tid; pc < 512; pc += kResThreads) {
     const int mb = pc >> 8, q = (pc >> 6) & 3, ln = pc & 63;
     const int c = 32 * mb + (ln & 31), h = ln >> 5;
     uint32_t w[4];
@@ -437,9 +466,9 @@ __device__ void res_frags_from_rows(const float* st, unsigned char* frag) {
 // the staged region (only masked tokens see those), reads a clamped staged
 // cell and is masked.
 __device__ void res_local(const ResArgs& a, const ResTile& t, const unsigned char* cK, const unsigned char* cV,
-                          int blk, const bf16x8 (&qB)[4], float scale, float (&L)[32]) {
+                          int blk, const bf16x8 (&qB)[4], float scale, float (&L)[32], int tid) {
   const ResPlan& p = a.p;
-  const int lane = threadIdx.x & 63, n = lane & 31, h = lane >> 5;
+  const int lane = tid & 63, n = lane & 31, h = lane >> 5;
   const int i16 = lane & 15, g = lane >> 4;
   const int br = blk / p.BC, bc = blk % p.BC;
   const int gr0 = t.r0 + 4 * br - 1, gc0 = t.c0 + 8 * bc - 1;  // window origin on the grid
@@ -513,14 +542,82 @@ __device__ void res_local(const ResArgs& a, const ResTile& t, const unsigned cha
   }
 }
 
-// y = x X for X given as A-operand fragments in LDS (frag: (mb, q, lane) ->
-// 16 bytes), x as the bits of its B operands (slot order).
-__device__ __forceinline__ void res_apply_bits(const unsigned char* frag, const v8s (&x)[4], float (&y)[32]) {
-  const int lane = threadIdx.x & 63;
+// The walk-weight predictor for one 32-slot block (forward with the
+// predictor): w = softmax(W2 ReLU(W1 concat(q, k) + b1) + b2) per token [the
+// predictor of note §2.4 Eq. 10], from the slots' raw Q (qB, the B operands
+// of the local branch's logits) and the K row of each token's own cell.  The
+// first layer runs on MFMA 32 hidden units at a time as W1 x^T, W1 in the
+// bf16 fragment order mlp_prep lays out per head; element i of lane (n, h)
+// of its accumulator is hidden unit 32 hb + 8 (i / 4) + i % 4 + 4 h of token
+// n, so lane halves are the two contraction slots of an fp32 MFMA 32x32x2
+// and the second layer is 16 of those (A = W2, rows past T zero), whose
+// element e of lane (n, h) is logit 4 h + e of token n.  The weights go to
+// the slots' entries [slot][T] of the weight region.
+__device__ void res_predict(const ResArgs& a, const unsigned char* cK, int slot, int cell, const bf16x8 (&qB)[4],
+                            int head, float* wts, int tid) {
+  const int lane = tid & 63, m = lane & 31, h = lane >> 5;
+  const int T = a.p.T, hidden = a.hidden, nhb = hidden / 32;
+  const bf16x8* w1 = reinterpret_cast<const bf16x8*>(static_cast<const float*>(a.mlp_w1f) +
+                                                     (size_t)head * mlp_head_floats(hidden, true));
+  bf16x8 xk[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) xk[kb] = *reinterpret_cast<const bf16x8*>(cK + row_off<BF16>(cell, 16 * kb + 8 * h));
+  f32x16 lg = {};
+#pragma unroll 1
+  for (int hb = 0; hb < nhb; ++hb) {
+    bf16x8 fh[8];
+    float w2[16], b1[16];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) fh[st] = w1[((size_t)hb * 8 + st) * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int j = 32 * hb + 8 * (i / 4) + i % 4 + 4 * h;  // hidden unit of slot h, element i
+      w2[i] = m < T ? a.mlp_w2[((size_t)head * T + m) * hidden + j] : 0.f;
+      b1[i] = a.mlp_b1[(size_t)head * hidden + j];
+    }
+    f32x16 c = {};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) c = mma(fh[st], qB[st], c);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) c = mma(fh[4 + st], xk[st], c);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) lg = mma(w2[i], fmaxf(c[i] + b1[i], 0.f), lg);
+  }
+  float v[4], mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int k = 4 * h + e;
+    v[e] = k < T ? lg[e] + a.mlp_b2[head * T + k] : 0.f;
+    if (k < T) mx = fmaxf(mx, v[e]);
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  float sum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[e] = 4 * h + e < T ? __expf(v[e] - mx) : 0.f;
+    sum += v[e];
+  }
+  sum += __shfl_xor(sum, 32);
+  const float inv = 1.f / sum;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (4 * h + e < T) wts[slot * T + 4 * h + e] = v[e] * inv;
+}
+
+// y += x X for X given as A-operand fragments in LDS (frag: (mb, q, lane) ->
+// 16 bytes), x as the bits of its B operands (slot order), y in accumulator
+// layout.
+__device__ __forceinline__ void res_apply_bits(const unsigned char* frag, const v8s (&x)[4], float (&y)[32], int tid) {
+  const int lane = tid & 63;
   // The fragment reads stay next to their products: hoisted out of the
   // per-block and per-term loops, the 16 operands would hold 64 registers.
   asm volatile("" : "+v"(frag));
-  f32x16 c0 = {}, c1 = {};
+  f32x16 c0, c1;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    c0[i] = y[i];
+    c1[i] = y[16 + i];
+  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(frag + ((0 * 4 + q) * 64 + lane) * 16);
@@ -536,11 +633,11 @@ __device__ __forceinline__ void res_apply_bits(const unsigned char* frag, const 
   }
 }
 // The same for x in accumulator layout as fp32 (rounded to bf16 here).
-__device__ __forceinline__ void res_apply(const unsigned char* frag, const float (&x)[32], float (&y)[32]) {
+__device__ __forceinline__ void res_apply(const unsigned char* frag, const float (&x)[32], float (&y)[32], int tid) {
   v8s b[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) b[q] = __builtin_bit_cast(v8s, operand(x, q, BF16{}));
-  res_apply_bits(frag, b, y);
+  res_apply_bits(frag, b, y, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -552,33 +649,36 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
   __shared__ float geo[kMaxT];  // geometric walk weights
   const ResPlan& p = a.p;
   const ResLayout& L = p.L;
-  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63, n = lane & 31, h = lane >> 5;
+  const int tid0 = threadIdx.x;
 
-  if (tid == 0) ticket = (int)bump(a.tickets + (a.xcd_groups ? blockIdx.x % kXcds : 0));
-  if (tid < kMaxT) geo[tid] = a.geo[tid];
+  if (tid0 == 0) ticket = (int)bump(a.tickets + (a.xcd_groups ? blockIdx.x % kXcds : 0));
+  if (tid0 < kMaxT) geo[tid0] = a.geo[tid0];
   __syncthreads();
   const ResRank rk = res_rank(a, ticket);
   res_stamp(a, true, kResStampStart);
-  if (a.stamps && tid == 0)
+  if (a.stamps && tid0 == 0)
     a.stamps[(size_t)blockIdx.x * kResPhases + kResPhases - 1] = ((unsigned long long)(unsigned)rk.group << 32) | (unsigned)rk.g;
   const bool fwd = a.mode != kResReduce;  // local branch and output
   const bool stats = a.mode != kResApply;  // sweeps and combine
 
   if (rk.group >= 0) {
     res_slot_table(reinterpret_cast<uint16_t*>(smem + L.tab), p, res_tile(p, rk.g));
-    // This wave's blocks: wave + 4 j, j < nown.
     constexpr int kNB = kResMaxBlocks / kResWaves;
-    const int nown = min(kNB, (p.nblk - wave + kResWaves - 1) / kResWaves);
     const int nstat = a.do_m ? 2 * kD * kD : kD * kD;
+    // One rank per slice, forward: the sweeps leave the statistics in place.
+    const bool direct = p.G == 1 && a.mode == kResForward;
 
     for (int b = rk.group; b < a.BH; b += a.S) {
       // The tile is the same for every slice, but what depends on it per lane
-      // (window cells, masks, token indices) is cheap to recompute and would
-      // otherwise be held in registers across the whole loop: the rank index
-      // is passed through an empty asm so that nothing derived from it is
-      // hoisted out of the loop.
-      int gi = rk.g;
-      asm volatile("" : "+s"(gi));
+      // (window cells, masks, token indices, operand offsets) is cheap to
+      // recompute and would otherwise be held in registers across the whole
+      // loop: the thread and rank indices are passed through an empty asm so
+      // that nothing derived from them is hoisted out of the loop.
+      int tid = tid0, gi = rk.g;
+      asm volatile("" : "+v"(tid), "+s"(gi));
+      const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, n = lane & 31, h = lane >> 5;
+      // This wave's blocks: wave + 8 j, j < nown.
+      const int nown = min(kNB, (p.nblk - wave + kResWaves - 1) / kResWaves);
       const ResTile t = res_tile(p, gi);
       const bool first = b == rk.group;
       const size_t base = (size_t)b * a.n;
@@ -593,9 +693,9 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
         reinterpret_cast<uint4*>(smem + L.v + L.zrow * kResRowBytes)[tid & 7] = make_uint4(0, 0, 0, 0);
       }
       // Stage: K and V cells, the weights; Q of this wave's blocks into registers.
-      res_dma_cells(smem + L.k, Kb, p.W, t, wave);
-      res_dma_cells(smem + L.v, Vb, p.W, t, wave);
-      if (fwd && a.per_token) res_dma_weights(smem + L.w, a.weights + base * p.T, p, t, wave);
+      res_dma_cells(smem + L.k, Kb, p.W, t, wave, tid);
+      res_dma_cells(smem + L.v, Vb, p.W, t, wave, tid);
+      if (fwd && a.per_token && a.weights) res_dma_weights(smem + L.w, a.weights + base * p.T, p, t, wave, tid);
       // Blocks go in pairs (two independent chains for the scheduler to
       // interleave); when the wave has an odd number of blocks, the last
       // pair's second block repeats the first: computed, never stored.
@@ -622,21 +722,34 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
       res_stamp(a, first, kResStampStaged);
 
       // KV sweep: partials of s and phi(K)^T V.
-      if (stats && a.do_kv) res_sweep_publish<false>(a, smem, b, rk.g);
+      if (stats && a.do_kv) res_sweep_publish<false>(a, smem, b, rk.g, tid);
       res_stamp(a, first, kResStampKV);
+
+      // The predicted walk weights of this wave's slots (each wave reads only
+      // its own slots' weights; LDS accesses of a wave complete in order).
+      float* wts = reinterpret_cast<float*>(smem + L.w);
+      if (fwd && a.mlp_w1f) {
+        const int head = __builtin_amdgcn_readfirstlane(b % a.heads);
+#pragma unroll
+        for (int j = 0; j < kNB; ++j) {
+          if (j < nown) {
+            int sl = slot[j], tr, tc;
+            asm volatile("" : "+v"(sl));
+            const bool on = res_slot(p, t, sl, tr, tc);
+            const int cell = on ? res_cell(t, t.r0 + tr, t.c0 + tc) : 0;
+            res_predict(a, smem + L.k, slot[j], cell, qB[j], head, wts, tid);
+          }
+        }
+      }
 
       // Local branch and the walk's k = 0 term: Lm = (1 - alpha) L_i + alpha w_0(i) V_i.
       float Lm[kNB][32];
-      const float* wts = reinterpret_cast<const float*>(smem + L.w);
       if (fwd) {
 #pragma unroll
-        for (int j0 = 0; j0 < kNB; j0 += 2) {
-          if (j0 < nown) {
-#pragma unroll
-            for (int j = j0; j < j0 + 2; ++j)
-              res_local(a, t, smem + L.k, smem + L.v, blkid[j], qB[j], 1.f - alpha, Lm[j]);
-#pragma unroll
-            for (int j = j0; j < j0 + 2; ++j) {
+        for (int j = 0; j < kNB; ++j) {
+          if (j < nown) {
+            res_local(a, t, smem + L.k, smem + L.v, blkid[j], qB[j], 1.f - alpha, Lm[j], tid);
+            {
               int sl = slot[j], tr, tc;
               asm volatile("" : "+v"(sl));
               const bool on = res_slot(p, t, sl, tr, tc);
@@ -666,9 +779,14 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
       if (global || (stats && a.do_m)) {
         float* s_lds = reinterpret_cast<float*>(smem + L.s);
         if (stats) {
-          if (p.G > 1) res_wait(a, b, kRcKV);
-          else __syncthreads();
-          res_sum_s(a, smem, b);
+          // The wait (or barrier) also orders every wave's local branch,
+          // which reads the V cells, before the Qt rows overwrite them.
+          // (One rank, forward: the KV sweep left s in LDS.)
+          if (p.G > 1)
+            res_wait(a, b, kRcKV);
+          else
+            lds_barrier();
+          if (!direct) res_sum_s(a, smem, b, tid);
           res_stamp(a, first, kResStampS);
         } else {
           __syncthreads();
@@ -702,92 +820,92 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
         lds_barrier();
       }
 
-      if (stats && a.do_m) res_sweep_publish<true>(a, smem, b, rk.g);
+      if (stats && a.do_m) res_sweep_publish<true>(a, smem, b, rk.g, tid);
       res_stamp(a, first, kResStampM);
 
-      if (stats && a.do_kv) {
+      if (stats && a.do_kv && !direct) {
         if (p.G > 1) res_wait(a, b, a.do_m ? kRcM : kRcKV);
         res_stamp(a, first, kResStampMWait);
-        res_combine(a, smem, b, rk.g, nstat);
+        res_combine(a, smem, b, rk.g, nstat, tid);
         res_stamp(a, first, kResStampComb);
         if (p.G > 1) {
           res_arrive(a, b, rk.g, kRcC);
           res_wait(a, b, kRcC);
           res_stamp(a, first, kResStampCWait);
         } else {
-          wait_all();
-          __syncthreads();
+          lds_barrier();  // the totals, in LDS; their global copies complete by the launch's end
         }
       }
 
       if (fwd) {
         if (global) {
-          // The statistics as fp32 rows in the K region (with one rank they
-          // are already there): phi(K)^T V, then M; then as bf16 fragments
-          // in the scratch area.
+          // The statistics as fp32 rows (phi(K)^T V, then M): left by the
+          // sweeps (one rank, forward) or loaded into the K region (with one
+          // rank and the combine they are already there); then as bf16
+          // fragments in the scratch area.
           if (!(stats && p.G == 1)) {
-            res_stats_to_lds(a, smem, b, p.T >= 3 ? 2 * kD * kD : kD * kD);
+            res_stats_to_lds(a, smem, b, p.T >= 3 ? 2 * kD * kD : kD * kD, tid);
             wait_all();
             __syncthreads();
           }
-          const float* rows = reinterpret_cast<const float*>(smem + L.k);
-          res_frags_from_rows(rows, smem + L.scr);
-          if (p.T >= 3) res_frags_from_rows(rows + kD * kD, smem + L.scr + kFragBytes);
-          __syncthreads();
+          const float* rows = reinterpret_cast<const float*>(smem + (direct ? L.st : L.k));
+          res_frags_from_rows(rows, smem + L.scr, tid);
+          if (p.T >= 3) res_frags_from_rows(rows + kD * kD, smem + L.scr + kFragBytes, tid);
+          lds_barrier();
         }
         res_stamp(a, first, kResStampFrags);
         const unsigned char* fkv = smem + L.scr;
         const unsigned char* fm = smem + L.scr + kFragBytes;
         uint16_t* Yb = static_cast<uint16_t*>(a.Y) + base * kD;
+        // One block at a time: u_1 = Qt_i from its staged row, in
+        // accumulator slot order; u_k = u_(k-1) M, z = sum_k w_k(i) u_k; then
+        // Lm += (alpha z) phi(K)^T V, and the block's Y is stored.
 #pragma unroll
-        for (int j0 = 0; j0 < kNB; j0 += 2) {
-          if (j0 < nown) {
+        for (int j = 0; j < kNB; ++j) {
+          if (j < nown) {
             if (global) {
+              const float* wrow = a.per_token ? wts + slot[j] * p.T : geo;
+              v8s u1[4];
 #pragma unroll
-              for (int j = j0; j < j0 + 2; ++j) {
-                const float* wrow = a.per_token ? wts + slot[j] * p.T : geo;
-                // u_1 = Qt_i from its staged row, in accumulator slot order;
-                // u_k = u_(k-1) M, z = sum_k w_k(i) u_k, then alpha z phi(K)^T V.
-                v8s u1[4];
+              for (int kb = 0; kb < 4; ++kb)
+                u1[kb] = relu_to_slots(*reinterpret_cast<const v8s*>(qt + row_off<BF16>(slot[j], 16 * kb + 8 * h)));
+              float z[32];
+              const float w1 = wrow[1];
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
-                  u1[kb] = relu_to_slots(*reinterpret_cast<const v8s*>(qt + row_off<BF16>(slot[j], 16 * kb + 8 * h)));
-                float z[32], y[32];
-                const float w1 = wrow[1];
+              for (int v = 0; v < 32; ++v) z[v] = w1 * bf2f((uint16_t)u1[v >> 3][v & 7]);
+              if (p.T >= 3) {
+                float u[32];
 #pragma unroll
-                for (int v = 0; v < 32; ++v) z[v] = w1 * bf2f((uint16_t)u1[v >> 3][v & 7]);
-                if (p.T >= 3) {
-                  float u[32];
-                  res_apply_bits(fm, u1, u);
-                  const float w2 = wrow[2];
+                for (int v = 0; v < 32; ++v) u[v] = 0.f;
+                res_apply_bits(fm, u1, u, tid);
+                const float w2 = wrow[2];
 #pragma unroll
-                  for (int v = 0; v < 32; ++v) z[v] += w2 * u[v];
-                  for (int k = 3; k < p.T; ++k) {
-                    res_apply(fm, u, y);
-                    const float wk = wrow[k];
+                for (int v = 0; v < 32; ++v) z[v] += w2 * u[v];
+                for (int k = 3; k < p.T; ++k) {
+                  float y[32];
 #pragma unroll
-                    for (int v = 0; v < 32; ++v) {
-                      u[v] = y[v];
-                      z[v] += wk * y[v];
-                    }
+                  for (int v = 0; v < 32; ++v) y[v] = 0.f;
+                  res_apply(fm, u, y, tid);
+                  const float wk = wrow[k];
+#pragma unroll
+                  for (int v = 0; v < 32; ++v) {
+                    u[v] = y[v];
+                    z[v] += wk * y[v];
                   }
                 }
-                res_apply(fkv, z, y);
-#pragma unroll
-                for (int v = 0; v < 32; ++v) Lm[j][v] += alpha * y[v];
               }
+#pragma unroll
+              for (int v = 0; v < 32; ++v) z[v] *= alpha;
+              res_apply(fkv, z, Lm[j], tid);
             }
+            if (valid[j]) {
+              // The token index recomputed here (not kept from the Q loads).
+              int sl = slot[j], tr, tc;
+              asm volatile("" : "+v"(sl));
+              res_slot(p, t, sl, tr, tc);
+              const size_t tok = (size_t)(t.r0 + tr) * p.W + (t.c0 + tc);
 #pragma unroll
-            for (int j = j0; j < j0 + 2; ++j) {
-              if (valid[j]) {
-                // The token index recomputed here (not kept from the Q loads).
-                int sl = slot[j], tr, tc;
-                asm volatile("" : "+v"(sl));
-                res_slot(p, t, sl, tr, tc);
-                const size_t tok = (size_t)(t.r0 + tr) * p.W + (t.c0 + tc);
-#pragma unroll
-                for (int c = 0; c < 8; ++c) store4(Yb + tok * kD + dimof(4 * c, h), &Lm[j][4 * c]);
-              }
+              for (int c = 0; c < 8; ++c) store4(Yb + tok * kD + dimof(4 * c, h), &Lm[j][4 * c]);
             }
           }
         }
@@ -803,18 +921,18 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
   wait_all();
   __syncthreads();
   res_stamp(a, true, kResStampEnd);
-  if (tid == 0) last = bump(a.done_cnt) == gridDim.x - 1;
+  if (tid0 == 0) last = bump(a.done_cnt) == gridDim.x - 1;
   __syncthreads();
   if (last) {
-    for (int i = tid; i < a.BH * kCntWords; i += kResThreads)
+    for (int i = tid0; i < a.BH * kCntWords; i += kResThreads)
       put(a.slice_cnt + (size_t)(i / kCntWords) * kCntStride + i % kCntWords, 0u);
     if (a.grouped)
-      for (int i = tid; i < a.BH * 3 * kMaxSubs; i += kResThreads) put(a.sub_cnt + (size_t)i * kCntStride, 0u);
-    if (tid < kXcds) put(a.tickets + tid, 0u);
-    if (a.clear_err && tid == 0) put(a.err, 0u);
+      for (int i = tid0; i < a.BH * 3 * kMaxSubs; i += kResThreads) put(a.sub_cnt + (size_t)i * kCntStride, 0u);
+    if (tid0 < kXcds) put(a.tickets + tid0, 0u);
+    if (a.clear_err && tid0 == 0) put(a.err, 0u);
     wait_all();
     __syncthreads();
-    if (tid == 0) put(a.done_cnt, 0u);
+    if (tid0 == 0) put(a.done_cnt, 0u);
   }
 }
 

@@ -20,13 +20,16 @@
 
 namespace lisa {
 
-constexpr int kResThreads = 256;            // 4 waves, one per SIMD (512 registers each)
+constexpr int kResThreads = 512;            // 8 waves, two per SIMD (256 registers each)
 constexpr int kResWaves = kResThreads / 64;
-constexpr int kResMaxBlocks = 4 * kResWaves;  // 4 x 8 blocks per tile: at most four per wave
+constexpr int kResMaxBlocks = 2 * kResWaves;  // 4 x 8 blocks per tile: at most two per wave
 constexpr int kResMaxT = 8;                 // walk terms the resident kernel takes
 constexpr int kResLdsMax = 159 * 1024;       // dynamic LDS: a gfx950 workgroup's 160 KB less the static part
 constexpr int kResRowBytes = 128;           // one staged bf16 row of 64 features
-constexpr int kResScratch = 4 * 64 * 4;     // the waves' sums of the s partials (later the fragments)
+// The scratch area: the second half's sweep products (four 32 x 32 fp32
+// blocks and the s column), the waves' sums of the s partials, later the
+// statistics fragments.
+constexpr int kResScratch = 4 * 32 * 32 * 4 + 64 * 4;
 // [G][E] floats staged by a rank's combine: E is nstat / G rounded up or
 // down, so G * E <= nstat + G <= 8192 + 256.  Later the same region holds
 // the statistics' fp32 rows.
@@ -46,7 +49,8 @@ struct ResLayout {
   int w;      // walk weights, [slot][T] fp32 (per-token weights only)
   int tab;    // [slot] uint16: staged cell of the slot's token, or zrow for a masked slot
   int s;      // s = sum_j phi(K_j) of the slice, 64 fp32
-  int scr;    // the waves' s sums, later the statistics fragments (16 KB)
+  int scr;    // the sweeps' second-half products, the waves' s sums, later the statistics fragments
+  int st;     // one rank per slice: the statistics [phi(K)^T V | M] as fp32 rows (32 KB; else unused)
   int total;
 };
 
@@ -127,6 +131,9 @@ __host__ __device__ inline bool res_layout(ResPlan& p) {
   o += 64 * 4;
   p.L.scr = o;
   o += res_max(kResScratch, 2 * 64 * 64 * 2);  // fragments of phi(K)^T V and M
+  // With one rank per slice the sweeps leave the statistics here directly.
+  p.L.st = o;
+  if (p.G == 1) o += 2 * 64 * 64 * 4;
   p.L.total = o;
   return o <= kResLdsMax;
 }
