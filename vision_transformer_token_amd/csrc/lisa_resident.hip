@@ -61,11 +61,23 @@ __device__ __forceinline__ ResRank res_rank(const ResArgs& a, int ticket) {
 // pinned in scalar registers: left to itself the compiler selects between the
 // two fields of the argument block and re-reads the pointer from memory, a
 // full memory round trip, at every use.
+// The result is rebuilt as a global-memory pointer, so that accesses through
+// it stay global (not flat) instructions.
 template <class P>
 __device__ __forceinline__ P* pick(P* p0, P* p1, bool second) {
   uint64_t x0 = reinterpret_cast<uint64_t>(p0), x1 = reinterpret_cast<uint64_t>(p1);
   asm volatile("" : "+s"(x0), "+s"(x1));
-  return reinterpret_cast<P*>(second ? x1 : x0);
+  return (P*)reinterpret_cast<__attribute__((address_space(1))) P*>(second ? x1 : x0);
+}
+
+// An LDS pointer passed through an empty asm (so that nothing derived from
+// it is hoisted), rebuilt as an LDS pointer: accesses through it stay LDS
+// (not flat) instructions.
+__device__ __forceinline__ const unsigned char* lds_launder(const unsigned char* p) {
+  unsigned off = (unsigned)(uintptr_t)(lds_ptr_t)p;
+  asm volatile("" : "+v"(off));
+  return (const unsigned char*)reinterpret_cast<const __attribute__((address_space(3))) unsigned char*>(
+      (uintptr_t)off);
 }
 
 // Stage timeline (ResArgs::stamps): thread 0 of the workgroup, first slice only.
@@ -611,7 +623,7 @@ __device__ __forceinline__ void res_apply_bits(const unsigned char* frag, const 
   const int lane = tid & 63;
   // The fragment reads stay next to their products: hoisted out of the
   // per-block and per-term loops, the 16 operands would hold 64 registers.
-  asm volatile("" : "+v"(frag));
+  frag = lds_launder(frag);
   f32x16 c0, c1;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -869,8 +881,9 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
 #pragma unroll
               for (int kb = 0; kb < 4; ++kb)
                 u1[kb] = relu_to_slots(*reinterpret_cast<const v8s*>(qt + row_off<BF16>(slot[j], 16 * kb + 8 * h)));
+              // alpha rides on the walk weights: z = sum_k (alpha w_k(i)) u_k.
               float z[32];
-              const float w1 = wrow[1];
+              const float w1 = alpha * wrow[1];
 #pragma unroll
               for (int v = 0; v < 32; ++v) z[v] = w1 * bf2f((uint16_t)u1[v >> 3][v & 7]);
               if (p.T >= 3) {
@@ -878,7 +891,7 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
 #pragma unroll
                 for (int v = 0; v < 32; ++v) u[v] = 0.f;
                 res_apply_bits(fm, u1, u, tid);
-                const float w2 = wrow[2];
+                const float w2 = alpha * wrow[2];
 #pragma unroll
                 for (int v = 0; v < 32; ++v) z[v] += w2 * u[v];
                 for (int k = 3; k < p.T; ++k) {
@@ -886,7 +899,7 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
 #pragma unroll
                   for (int v = 0; v < 32; ++v) y[v] = 0.f;
                   res_apply(fm, u, y, tid);
-                  const float wk = wrow[k];
+                  const float wk = alpha * wrow[k];
 #pragma unroll
                   for (int v = 0; v < 32; ++v) {
                     u[v] = y[v];
@@ -894,8 +907,6 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
                   }
                 }
               }
-#pragma unroll
-              for (int v = 0; v < 32; ++v) z[v] *= alpha;
               res_apply(fkv, z, Lm[j], tid);
             }
             if (valid[j]) {
