@@ -242,6 +242,66 @@ def summarize_profiles(outdir, workload, commands):
         json.dump(c, f, indent=1)
 
 
+def write_phases_profile(w, rec, command):
+    """profiles/lisa_forward_phases_<workload>.md from a phases_timing record:
+    each stage's median and 90th-percentile end time over the workgroups, the
+    interval since the previous stage's median end, and, where a stage moves
+    HBM bytes, those bytes over that interval."""
+    G, BH = rec["ranks_per_slice"], w.B * w.heads
+    esize = 2 if w.dtype == "bf16" else 4
+    tok = BH * w.n
+    mat = 64 * 64 * 4
+    inputs = tok * (3 * 64 * esize + (4 * w.T if w.mode == "adaptive" else 0))
+    nstat = 2 if w.T >= 3 else 1
+    direct = G == 1
+    # (stage, what moves to or from HBM in the interval that ends with it, bytes)
+    order = [("start", "", 0),
+             ("staged", "Q, K, V, weights read (algorithmic bytes; the halo cells come on top)", inputs),
+             ("kvsweep", "", 0),
+             ("kv", "partials of s and phi(K)^T V written" if not direct else "s, phi(K)^T V written",
+              BH * (G * (mat + 256) if not direct else mat + 256)),
+             ("local", "", 0),
+             ("s", "s partials read" if not direct else "", BH * G * 256 if not direct else 0),
+             ("m", "partials of M written" if not direct else "M written", BH * G * mat if w.T >= 3 else 0),
+             ("mwait", "", 0),
+             ("cstaged", "every partial read once (by the rank that sums it)", 0 if direct else BH * G * nstat * mat),
+             ("csummed", "", 0),
+             ("combine", "the statistics written", 0 if direct else BH * nstat * mat),
+             ("cwait", "", 0),
+             ("frags", "the statistics read by every rank", 0 if direct else BH * G * nstat * mat),
+             ("out", "", 0),
+             ("end", "Y written (interval from the fragments' end: the output stage)", tok * 64 * esize)]
+    since = {"end": "frags", "cstaged": "mwait"}  # intervals that start earlier than the previous row
+    st = rec["stages"]
+    lines = [f"# Stage timeline of the resident kernel, workload {w.describe()}", "",
+             f"command: {command}", "",
+             f"lisa_forward_phases: every workgroup stamps the device's 100 MHz clock (s_memrealtime) as its "
+             f"wave 0 reaches each stage of its first slice; times are from the first workgroup's start, "
+             f"median and 90th percentile over the {rec['workgroups']} working workgroups, averaged over "
+             f"{rec['calls']} cold calls.  {G} rank(s) per slice.  Wave 0 is the oldest wave and finishes a "
+             f"stage first: a stage's end for the whole workgroup is nearer the next stage's start.  The "
+             f"interval of a stage runs from the previous listed stage's median; the bytes are those the "
+             f"interval moves to or from HBM for the whole launch.", "",
+             "| stage | median end us | p90 end us | interval us | HBM traffic in the interval | MB | GB/s |",
+             "|---|---|---|---|---|---|---|"]
+    prev = None
+    for name, what, nbytes in order:
+        m = st.get(name, {}).get("median_us")
+        if m is None:
+            continue
+        q = st[name]["p90_us"]
+        base = st.get(since.get(name, ""), {}).get("median_us")
+        dt = None if prev is None else m - (base if base is not None else prev)
+        rate = f"{nbytes / (dt * 1e-6) / 1e9:.0f}" if nbytes and dt and dt > 0 else ""
+        lines.append(f"| {name} | {m:.2f} | {q:.2f} | {'' if dt is None else f'{dt:.2f}'} | {what} | "
+                     f"{nbytes / 1e6:.2f} | {rate} |" if nbytes else
+                     f"| {name} | {m:.2f} | {q:.2f} | {'' if dt is None else f'{dt:.2f}'} | {what} | | |")
+        prev = m
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"lisa_forward_phases_{w.name}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def summarize_backward(outdir, workload, command):
     """profiles/ summary of a rocprofv3 kernel trace of bench.py --backward-only."""
     from vision_transformer_token_amd import workloads
@@ -355,6 +415,8 @@ def main():
                     help="time only lisa_forward_mlp (predicted walk weights) and print its line")
     ap.add_argument("--phases", action="store_true",
                     help="print the stage timeline of lisa_forward_phases over --steps cold calls and exit")
+    ap.add_argument("--phases-profile", action="store_true",
+                    help="with --phases: also write profiles/lisa_forward_phases_<workload>.md")
     ap.add_argument("--schedule", default="auto", choices=["auto", "streaming", "resident"],
                     help="forward kernel (lisa_schedule); auto is the library's choice")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -691,8 +753,9 @@ def main():
             med.append(np.nanmedian(rel, axis=0))
             p90.append(np.nanpercentile(rel, 90, axis=0))
             rows = int(active.sum())
+            ranks = int((rank[active] & 0xFFFFFFFF).max()) + 1
         med, p90 = np.nanmean(np.array(med), axis=0), np.nanmean(np.array(p90), axis=0)
-        return {"workgroups": rows, "calls": calls,
+        return {"workgroups": rows, "calls": calls, "ranks_per_slice": ranks,
                 "stages": {name: {"median_us": None if np.isnan(m) else round(float(m), 3),
                                   "p90_us": None if np.isnan(q) else round(float(q), 3)}
                            for name, m, q in zip(lisa.STAGES, med, p90)}}
@@ -700,6 +763,9 @@ def main():
     if args.phases:
         rec = phases_timing(args.steps, args.warmup)
         print(json.dumps({"workload": w.name, "phases": rec}), flush=True)
+        if args.phases_profile:
+            write_phases_profile(w, rec, "python3 bench.py --phases --phases-profile --steps "
+                                 f"{args.steps} --warmup {args.warmup} --workload {w.name}")
         return
 
     if args.backward_only:
