@@ -315,7 +315,7 @@ def summarize_backward(outdir, workload, command):
     total_ns = 0.0
     for r in stats:
         name = _short(r["Name"])
-        if not (name.startswith("bwd_") or name.startswith("flow_kernel")):
+        if not (name.startswith("bwd_") or name in KERNEL_SOURCES_BY_NAME):
             continue
         calls = calls or int(r["Calls"])
         total_ns += float(r["AverageNs"])
@@ -323,7 +323,7 @@ def summarize_backward(outdir, workload, command):
                      f"{float(r['Percentage']):.1f}% |")
     bb = compulsory_bytes_backward(w)
     lines += ["", f"sum of the kernels' averages per call: {total_ns / 1e3:.1f} us "
-                  f"(flow_kernel is the statistics launch the backward starts with)",
+                  f"(the forward kernel, {' or '.join(KERNEL_SOURCES_BY_NAME)}, is the statistics launch the backward starts with)",
               f"algorithmic bytes per call: {w.token_heads * bb / 1e6:.2f} MB ({bb} B per token-head); "
               f"at 8 TB/s: {w.token_heads * bb / 8e12 * 1e6:.1f} us",
               f"kernel source hash (forward and backward sources): {kernel_source_hash(BACKWARD_SOURCES)}"]
@@ -353,7 +353,7 @@ def summarize_layer(outdir, workload, command):
     total_ns = 0.0
     for r in stats:
         name = _short(r["Name"])
-        if not (name.startswith("flow_kernel") or name.startswith("proj_gemm")):
+        if not (name in KERNEL_SOURCES_BY_NAME or name.startswith("proj_gemm")):
             continue
         total_ns += float(r["AverageNs"])
         lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} | "
@@ -380,7 +380,7 @@ def summarize_mlp(outdir, workload, command):
     total_ns = 0.0
     for r in stats:
         name = _short(r["Name"])
-        if not (name.startswith("flow_kernel") or name.startswith("mlp_prep")):
+        if not (name.startswith("flow_kernel") or name == "resident_kernel" or name.startswith("mlp_prep")):
             continue
         total_ns += float(r["AverageNs"])
         lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} | "
