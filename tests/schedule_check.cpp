@@ -55,7 +55,11 @@ static void check(int H, int W, int T, int gcap) {
   CHECK(L.v - L.k >= kResCombineFloats * 4, "k region holds the combine's staging (and the statistics' rows)");
   CHECK(L.w >= L.v + krows * kResRowBytes && L.w >= L.v + slots * kResRowBytes, "v region");
   CHECK(L.tab >= L.w + res_up(slots * T, 64) * 4, "w region");
-  CHECK(L.s >= L.tab + slots * 2, "tab region");
+  CHECK(L.loc >= L.tab + slots * 2, "tab region");
+  CHECK(L.s >= L.loc + res_loc_bytes(p.nblk) && res_loc_mask(p.nblk) >= res_loc_win(p.nblk) + p.nblk * 128 &&
+            res_loc_nbr(p.nblk) >= res_loc_mask(p.nblk) + p.nblk * 8 && res_loc_hot(p.nblk) >= res_loc_nbr(p.nblk) + 256 &&
+            res_loc_hot(p.nblk) % 16 == 0 && L.loc % 16 == 0,
+        "loc region");
   CHECK(L.scr >= L.s + 64 * 4, "s region");
   CHECK(L.st >= L.scr + kResScratch && L.st >= L.scr + 2 * 64 * 64 * 2, "scr region");
   CHECK(L.total >= L.st + (p.G == 1 ? 2 * 64 * 64 * 4 : 0), "st region");

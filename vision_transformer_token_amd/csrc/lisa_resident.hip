@@ -175,6 +175,46 @@ __device__ void res_slot_table(uint16_t* tab, const ResPlan& p, const ResTile& t
   }
 }
 
+// The local branch's tables for tile t (the same for every slice): each
+// block's 6 x 10 window of staged cells (positions 60..63 repeat 59; a cell
+// off the grid, or past the staged region, is clamped to a staged one and
+// masked), each block's grid masks (the logit slots of lane half h whose cell
+// lies on the grid), each lane's neighbour mask (the slots of its token's
+// 3 x 3 neighbourhood) and each lane's one-hot B operands of the four 16-cell
+// steps (1 at its token's own cell): against the V cells' A operands these
+// give the token's own V row.
+__device__ void res_local_tables(unsigned char* smem, const ResPlan& p, const ResTile& t) {
+  unsigned char* loc = smem + p.L.loc;
+  uint16_t* win = reinterpret_cast<uint16_t*>(loc + res_loc_win(p.nblk));
+  uint32_t* msk = reinterpret_cast<uint32_t*>(loc + res_loc_mask(p.nblk));
+  uint32_t* nbr = reinterpret_cast<uint32_t*>(loc + res_loc_nbr(p.nblk));
+  v8s* hot = reinterpret_cast<v8s*>(loc + res_loc_hot(p.nblk));
+  for (int i = threadIdx.x; i < p.nblk * 64; i += kResThreads) {
+    const int blk = i >> 6, c = min(i & 63, 59), br = blk / p.BC, bc = blk % p.BC;
+    win[i] = (uint16_t)res_cell(t, t.r0 + 4 * br - 1 + c / 10, t.c0 + 8 * bc - 1 + c % 10);
+  }
+  for (int i = threadIdx.x; i < p.nblk * 2; i += kResThreads) {
+    const int blk = i >> 1, h = i & 1, br = blk / p.BC, bc = blk % p.BC;
+    const int gr0 = t.r0 + 4 * br - 1, gc0 = t.c0 + 8 * bc - 1;
+    unsigned rowbits = 0, colbits = 0;
+    for (int wr = 0; wr < 6; ++wr) rowbits |= (unsigned)(gr0 + wr >= 0 && gr0 + wr < p.H) << wr;
+    for (int wc = 0; wc < 10; ++wc) colbits |= (unsigned)(gc0 + wc >= 0 && gc0 + wc < p.W) << wc;
+    msk[i] = grid_slots(rowbits, colbits, h);
+  }
+  if (threadIdx.x < 64) {
+    const int n = threadIdx.x & 31, h = threadIdx.x >> 5;
+    nbr[threadIdx.x] = neighbour_slots(n >> 3, n & 7, h);
+  }
+  for (int i = threadIdx.x; i < 4 * 64; i += kResThreads) {
+    const int kb = i >> 6, n = i & 31, h = (i >> 5) & 1;
+    const int own = (n / 8 + 1) * 10 + n % 8 + 1;  // the token's cell in its block's window
+    v8s x = (v8s)0;
+    for (int e = 0; e < 8; ++e)
+      if (16 * kb + 8 * (e >> 2) + 4 * h + (e & 3) == own) x[e] = (short)0x3f80;  // bf16 1.0
+    hot[i] = x;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Sweeps: contractions over the tile's token slots on MFMA.
 // ---------------------------------------------------------------------------
@@ -470,26 +510,27 @@ __device__ void res_frags_from_rows(const float* st, unsigned char* frag, int ti
 // Local branch and output (per 4 x 8 block; one token per lane pair, 32
 // features per lane in accumulator layout).
 // ---------------------------------------------------------------------------
-// Local branch of block blk of tile t on MFMA: logits C[cell][token] =
-// K_win Q_blk^T over the block's 6 x 10 window of cells (60, padded to 64),
-// masked softmax, then L^T = V_win^T P^T with the probabilities as the B
-// operand and V from transposed LDS reads; the denominator is the same
-// product against an all-ones operand.  A window cell off the grid, or past
-// the staged region (only masked tokens see those), reads a clamped staged
-// cell and is masked.
-__device__ void res_local(const ResArgs& a, const ResTile& t, const unsigned char* cK, const unsigned char* cV,
-                          int blk, const bf16x8 (&qB)[4], float scale, float (&L)[32], int tid) {
+// Local branch of block blk on MFMA, and the walk's k = 0 term:
+// Lm = scale L + f V_i.  Logits C[cell][token] = K_win Q_blk^T over the
+// block's 6 x 10 window of cells (60, padded to 64; the cells from the
+// window table), masked softmax (grid and neighbour masks from their tables),
+// then L^T = V_win^T P^T with the probabilities as the B operand and V from
+// transposed LDS reads; the denominator is the same product against an
+// all-ones operand, and V_i the same product against the one-hot operands.
+__device__ void res_local(const ResArgs& a, const unsigned char* smem, int blk, const bf16x8 (&qB)[4], float scale,
+                          float f, float (&Lm)[32], int tid) {
   const ResPlan& p = a.p;
   const int lane = tid & 63, n = lane & 31, h = lane >> 5;
   const int i16 = lane & 15, g = lane >> 4;
-  const int br = blk / p.BC, bc = blk % p.BC;
-  const int gr0 = t.r0 + 4 * br - 1, gc0 = t.c0 + 8 * bc - 1;  // window origin on the grid
-  auto wcell = [&](int c) {
-    c = min(c, 59);
-    return res_cell(t, gr0 + c / 10, gc0 + c % 10);
-  };
+  const unsigned char* cK = smem + p.L.k;
+  const unsigned char* cV = smem + p.L.v;
+  const unsigned char* loc = smem + p.L.loc;
+  const uint16_t* win = reinterpret_cast<const uint16_t*>(loc + res_loc_win(p.nblk)) + blk * 64;
+  const unsigned valid = reinterpret_cast<const uint32_t*>(loc + res_loc_nbr(p.nblk))[lane] &
+                         reinterpret_cast<const uint32_t*>(loc + res_loc_mask(p.nblk))[blk * 2 + h];
+  const bf16x8* hot = reinterpret_cast<const bf16x8*>(loc + res_loc_hot(p.nblk)) + lane;
   f32x16 lg[2] = {};
-  const int sc0 = wcell(n), sc1 = wcell(32 + n);
+  const int sc0 = win[n], sc1 = win[32 + n];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     const bf16x8 A0 = *reinterpret_cast<const bf16x8*>(cK + row_off<BF16>(sc0, 16 * kb + 8 * h));
@@ -497,27 +538,6 @@ __device__ void res_local(const ResArgs& a, const ResTile& t, const unsigned cha
     lg[0] = mma(A0, qB[kb], lg[0]);
     lg[1] = mma(A1, qB[kb], lg[1]);
   }
-  // The window's on-grid rows and columns (wave-uniform), formed without a
-  // branch so that two blocks' local branches stay one stretch of code.
-  unsigned rowbits = 0, colbits = 0;
-#pragma unroll
-  for (int wr = 0; wr < 6; ++wr) rowbits |= (unsigned)(gr0 + wr >= 0 && gr0 + wr < p.H) << wr;
-#pragma unroll
-  for (int wc = 0; wc < 10; ++wc) colbits |= (unsigned)(gc0 + wc >= 0 && gc0 + wc < p.W) << wc;
-  unsigned r0m = 0, r1m = 0, k0m = 0, k1m = 0;
-#pragma unroll
-  for (int wr = 0; wr < 6; ++wr) {
-    const unsigned on = 0u - ((rowbits >> wr) & 1u);
-    r0m |= row_slots(0, wr) & on;
-    r1m |= row_slots(1, wr) & on;
-  }
-#pragma unroll
-  for (int wc = 0; wc < 10; ++wc) {
-    const unsigned on = 0u - ((colbits >> wc) & 1u);
-    k0m |= col_slots(0, wc) & on;
-    k1m |= col_slots(1, wc) & on;
-  }
-  const unsigned valid = neighbour_slots(n >> 3, n & 7, h) & (h ? (r1m & k1m) : (r0m & k0m));
   float pr[32];
   float mx = -1e30f;  // finite: a masked token may have no valid slot
 #pragma unroll
@@ -532,25 +552,27 @@ __device__ void res_local(const ResArgs& a, const ResTile& t, const unsigned cha
 #pragma unroll
   for (int v = 0; v < 32; ++v)
     Bp[v >> 3][v & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(pr[v], a.logit_scale, off));
-  f32x16 la[2] = {}, lden = {};
+  f32x16 la[2] = {}, lv[2] = {}, lden = {};
   const bf16x8 ones = as_bf16((v8s)(short)0x3f80);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     lden = mma(ones, Bp[kb], lden);
-    const int cA = wcell(16 * kb + 4 * (g >> 1) + (i16 >> 2));
-    const int cB = wcell(16 * kb + 8 + 4 * (g >> 1) + (i16 >> 2));
+    const int cA = win[16 * kb + 4 * (g >> 1) + (i16 >> 2)];
+    const int cB = win[16 * kb + 8 + 4 * (g >> 1) + (i16 >> 2)];
+    const bf16x8 hb = hot[kb * 64];
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
       const int d = 32 * db + 16 * (g & 1) + 4 * (i16 & 3);
       const bf16x8 A = as_bf16(join(tr_read(cV + row_off<BF16>(cA, d)), tr_read(cV + row_off<BF16>(cB, d))));
       la[db] = mma(A, Bp[kb], la[db]);
+      lv[db] = mma(A, hb, lv[db]);
     }
   }
   const float inv = scale * __builtin_amdgcn_rcpf(lden[0]);
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    L[v] = la[0][v] * inv;
-    L[16 + v] = la[1][v] * inv;
+    Lm[v] = __builtin_fmaf(f, lv[0][v], la[0][v] * inv);
+    Lm[16 + v] = __builtin_fmaf(f, lv[1][v], la[1][v] * inv);
   }
 }
 
@@ -675,6 +697,7 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
 
   if (rk.group >= 0) {
     res_slot_table(reinterpret_cast<uint16_t*>(smem + L.tab), p, res_tile(p, rk.g));
+    if (fwd) res_local_tables(smem, p, res_tile(p, rk.g));
     constexpr int kNB = kResMaxBlocks / kResWaves;
     const int nstat = a.do_m ? 2 * kD * kD : kD * kD;
     // One rank per slice, forward: the sweeps leave the statistics in place.
@@ -760,22 +783,8 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
 #pragma unroll
         for (int j = 0; j < kNB; ++j) {
           if (j < nown) {
-            res_local(a, t, smem + L.k, smem + L.v, blkid[j], qB[j], 1.f - alpha, Lm[j], tid);
-            {
-              int sl = slot[j], tr, tc;
-              asm volatile("" : "+v"(sl));
-              const bool on = res_slot(p, t, sl, tr, tc);
-              const int cell = on ? res_cell(t, t.r0 + tr, t.c0 + tc) : 0;
-              const float w0 = a.per_token ? wts[slot[j] * p.T] : geo[0];
-              const float f = alpha * w0;
-#pragma unroll
-              for (int c = 0; c < 8; ++c) {
-                float vc[4];
-                load4(reinterpret_cast<const uint16_t*>(smem + L.v + row_off<BF16>(cell, dimof(4 * c, h))), vc);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) Lm[j][4 * c + e] += f * vc[e];
-              }
-            }
+            const float w0 = a.per_token ? wts[slot[j] * p.T] : geo[0];
+            res_local(a, smem, blkid[j], qB[j], 1.f - alpha, alpha * w0, Lm[j], tid);
           }
         }
       }

@@ -48,6 +48,8 @@ struct ResLayout {
   int v;      // V cells; after the local branch, row s = r_s phi(Q_s) of slot s
   int w;      // walk weights, [slot][T] fp32 (per-token weights only)
   int tab;    // [slot] uint16: staged cell of the slot's token, or zrow for a masked slot
+  int loc;    // the local branch's tables: [block][64] uint16 window cells, [block][2] uint32 grid
+              // masks, [64] uint32 neighbour masks, [4][64] bf16x8 one-hot operands (res_loc_*)
   int s;      // s = sum_j phi(K_j) of the slice, 64 fp32
   int scr;    // the sweeps' second-half products, the waves' s sums, later the statistics fragments
   int st;     // one rank per slice: the statistics [phi(K)^T V | M] as fp32 rows (32 KB; else unused)
@@ -107,6 +109,16 @@ __host__ __device__ inline void res_combine_range(int nstat, int G, int g, int& 
   e1 = (int)((long long)(g + 1) * nstat / G);
 }
 
+// The local branch's tables (byte offsets within the loc region, nblk blocks):
+// each block's 64 window cells (uint16), its two grid masks (uint32), each
+// lane's neighbour mask (uint32), each lane's one-hot operands of the four
+// 16-cell steps (bf16x8).
+__host__ __device__ inline int res_loc_win(int) { return 0; }
+__host__ __device__ inline int res_loc_mask(int nblk) { return nblk * 64 * 2; }
+__host__ __device__ inline int res_loc_nbr(int nblk) { return res_up(res_loc_mask(nblk) + nblk * 8, 16); }
+__host__ __device__ inline int res_loc_hot(int nblk) { return res_loc_nbr(nblk) + 64 * 4; }
+__host__ __device__ inline int res_loc_bytes(int nblk) { return res_loc_hot(nblk) + 4 * 64 * 16; }
+
 // The LDS layout for the plan's largest tile; false if it exceeds kResLdsMax.
 __host__ __device__ inline bool res_layout(ResPlan& p) {
   const int cells = p.SR * p.SC;
@@ -127,6 +139,8 @@ __host__ __device__ inline bool res_layout(ResPlan& p) {
   o += res_up(slots * p.wT * 4, 256);  // the weight DMA writes 256-byte runs
   p.L.tab = o;
   o += res_up(slots * 2, 16);
+  p.L.loc = o;
+  o += res_loc_bytes(p.nblk);
   p.L.s = o;
   o += 64 * 4;
   p.L.scr = o;
