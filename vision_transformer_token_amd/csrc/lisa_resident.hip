@@ -80,6 +80,14 @@ __device__ __forceinline__ const unsigned char* lds_launder(const unsigned char*
       (uintptr_t)off);
 }
 
+// Row keys: k = 8 r + swz(r) for the bf16 row r of a staged region (128-byte
+// rows, 16-byte pieces swizzled by row as everywhere in the library), so that
+// element d of row r lies at byte ((k ^ (d / 8)) * 16 + (d % 8) * 2) of the
+// region: one XOR and one shift-add per address.  The slot and window tables
+// hold keys (16 bits: at most 8 K rows of 128 bytes per key unit).
+__device__ __forceinline__ int res_key(int r) { return 8 * r + swz(r); }
+__device__ __forceinline__ int res_at(int key, int d) { return ((key ^ (d >> 3)) << 4) + (d & 7) * 2; }
+
 // Stage timeline (ResArgs::stamps): thread 0 of the workgroup, first slice only.
 __device__ __forceinline__ void res_stamp(const ResArgs& a, bool first, int k) {
   if (a.stamps && first && threadIdx.x == 0)
@@ -167,16 +175,16 @@ __device__ void res_dma_weights(unsigned char* lds, const float* wb, const ResPl
   }
 }
 
-// The staged cell of each slot's token (the zero row for a masked slot).
+// The row key of each slot's token's staged cell (the zero row for a masked slot).
 __device__ void res_slot_table(uint16_t* tab, const ResPlan& p, const ResTile& t) {
   for (int s = threadIdx.x; s < p.nblk * 32; s += kResThreads) {
     int tr, tc;
-    tab[s] = (uint16_t)(res_slot(p, t, s, tr, tc) ? res_cell(t, t.r0 + tr, t.c0 + tc) : p.L.zrow);
+    tab[s] = (uint16_t)res_key(res_slot(p, t, s, tr, tc) ? res_cell(t, t.r0 + tr, t.c0 + tc) : p.L.zrow);
   }
 }
 
-// The local branch's tables for tile t (the same for every slice): each
-// block's 6 x 10 window of staged cells (positions 60..63 repeat 59; a cell
+// The local branch's tables for tile t (the same for every slice): the row
+// keys of each block's 6 x 10 window of staged cells (positions 60..63 repeat 59; a cell
 // off the grid, or past the staged region, is clamped to a staged one and
 // masked), each block's grid masks (the logit slots of lane half h whose cell
 // lies on the grid), each lane's neighbour mask (the slots of its token's
@@ -191,7 +199,7 @@ __device__ void res_local_tables(unsigned char* smem, const ResPlan& p, const Re
   v8s* hot = reinterpret_cast<v8s*>(loc + res_loc_hot(p.nblk));
   for (int i = threadIdx.x; i < p.nblk * 64; i += kResThreads) {
     const int blk = i >> 6, c = min(i & 63, 59), br = blk / p.BC, bc = blk % p.BC;
-    win[i] = (uint16_t)res_cell(t, t.r0 + 4 * br - 1 + c / 10, t.c0 + 8 * bc - 1 + c % 10);
+    win[i] = (uint16_t)res_key(res_cell(t, t.r0 + 4 * br - 1 + c / 10, t.c0 + 8 * bc - 1 + c % 10));
   }
   for (int i = threadIdx.x; i < p.nblk * 2; i += kResThreads) {
     const int blk = i >> 1, h = i & 1, br = blk / p.BC, bc = blk % p.BC;
@@ -219,10 +227,11 @@ __device__ void res_local_tables(unsigned char* smem, const ResPlan& p, const Re
 // Sweeps: contractions over the tile's token slots on MFMA.
 // ---------------------------------------------------------------------------
 // Operand bits of X[row(8h + e)][col0 + m], e = 0..7, for 16 slots whose
-// staged rows lane (i, g) of the wave supplies (ra for the first read, rb for
-// the second); see rows_bits for the lane pattern of ds_read_b64_tr_b16.
-__device__ __forceinline__ v8s rows_at(const unsigned char* base, int ra, int rb, int col) {
-  return join(tr_read(base + row_off<BF16>(ra, col)), tr_read(base + row_off<BF16>(rb, col)));
+// staged rows lane (i, g) of the wave supplies (row keys ka for the first
+// read, kb for the second); see rows_bits for the lane pattern of
+// ds_read_b64_tr_b16.
+__device__ __forceinline__ v8s rows_at(const unsigned char* base, int ka, int kb, int col) {
+  return join(tr_read(base + res_at(ka, col)), tr_read(base + res_at(kb, col)));
 }
 
 // Steps [k0, k1) of 16 slots: acc += phi(K)^T X over the slots, X = the
@@ -257,7 +266,7 @@ __device__ __forceinline__ void res_sweep(const unsigned char* smem, const ResLa
     for (int u = 0; u < U; ++u) {
       const int s1 = 16 * (k + u) + 8 * (g >> 1) + (i >> 2);
       A[u] = __builtin_elementwise_max(rows_at(bK, ra[u], rb[u], colA), (v8s)0);  // ReLU on the bf16 bits
-      B[u] = kIsM ? rows_at(bX, s1, s1 + 4, colB) : rows_at(bX, ra[u], rb[u], colB);
+      B[u] = kIsM ? rows_at(bX, res_key(s1), res_key(s1 + 4), colB) : rows_at(bX, ra[u], rb[u], colB);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -533,8 +542,8 @@ __device__ void res_local(const ResArgs& a, const unsigned char* smem, int blk, 
   const int sc0 = win[n], sc1 = win[32 + n];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-    const bf16x8 A0 = *reinterpret_cast<const bf16x8*>(cK + row_off<BF16>(sc0, 16 * kb + 8 * h));
-    const bf16x8 A1 = *reinterpret_cast<const bf16x8*>(cK + row_off<BF16>(sc1, 16 * kb + 8 * h));
+    const bf16x8 A0 = *reinterpret_cast<const bf16x8*>(cK + res_at(sc0, 16 * kb + 8 * h));
+    const bf16x8 A1 = *reinterpret_cast<const bf16x8*>(cK + res_at(sc1, 16 * kb + 8 * h));
     lg[0] = mma(A0, qB[kb], lg[0]);
     lg[1] = mma(A1, qB[kb], lg[1]);
   }
@@ -563,7 +572,7 @@ __device__ void res_local(const ResArgs& a, const unsigned char* smem, int blk, 
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
       const int d = 32 * db + 16 * (g & 1) + 4 * (i16 & 3);
-      const bf16x8 A = as_bf16(join(tr_read(cV + row_off<BF16>(cA, d)), tr_read(cV + row_off<BF16>(cB, d))));
+      const bf16x8 A = as_bf16(join(tr_read(cV + res_at(cA, d)), tr_read(cV + res_at(cB, d))));
       la[db] = mma(A, Bp[kb], la[db]);
       lv[db] = mma(A, hb, lv[db]);
     }
