@@ -291,8 +291,10 @@ lisa_status run_resident(const Plan& pl, const lisa::ResPlan& rp, int cus, Mode 
   a.per_token = (weights != nullptr || mlp != nullptr) ? 1 : 0;
   a.grouped = (rp.G >= 64 && pl.BH <= lisa::kMaxSubSlices) ? 1 : 0;
   a.part_s = reinterpret_cast<float*>(ws + pl.part_s);
+  // The rank partials as one [BH][G][2][64*64] array over the two partial
+  // regions, which layout_forward places back to back (G <= gmax).
+  if (pl.part_m != pl.part_kv + (size_t)pl.BH * pl.gmax * kD * kD * sizeof(float)) return LISA_ERR_WORKSPACE;
   a.part_kv = reinterpret_cast<float*>(ws + pl.part_kv);
-  a.part_m = reinterpret_cast<float*>(ws + pl.part_m);
   a.fin_s = reinterpret_cast<float*>(ws + pl.fin_s);
   a.fin_kv = reinterpret_cast<float*>(ws + pl.fin_kv);
   a.fin_m = reinterpret_cast<float*>(ws + pl.fin_m);

@@ -181,8 +181,8 @@ struct ResArgs {
   int grouped;            // arrivals counted per group of kSubRanks ranks (sub_cnt)
   ResPlan p;
   float* part_s;          // [BH][G][64]
-  float* part_kv;         // [BH][G][64*64]
-  float* part_m;          // [BH][G][64*64]
+  float* part_kv;         // [BH][G][2][64*64]: phi(K)^T V then M of each rank (the workspace's
+                          // two partial regions, adjacent, as one)
   float* fin_s;           // [BH][64]
   float* fin_kv;          // [BH][64*64]
   float* fin_m;           // [BH][64*64]

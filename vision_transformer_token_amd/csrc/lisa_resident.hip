@@ -329,7 +329,7 @@ __device__ void res_sweep_publish(const ResArgs& a, unsigned char* smem, int b, 
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] += red[(pw * 16 + i) * 64 + lane];
     float* dst = direct ? (kIsM ? a.fin_m : a.fin_kv) + (size_t)b * (kD * kD)
-                        : (kIsM ? a.part_m : a.part_kv) + ((size_t)b * a.p.G + g) * (kD * kD);
+                        : a.part_kv + ((size_t)b * a.p.G + g) * (2 * kD * kD) + (kIsM ? kD * kD : 0);
     float* st = reinterpret_cast<float*>(smem + L.st) + (kIsM ? kD * kD : 0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -434,7 +434,7 @@ __device__ void res_combine(const ResArgs& a, unsigned char* smem, int b, int g,
   for (int i = 0; i < kPer; ++i) {
     const int q = min(tid + kResThreads * i, total - 1);
     const int pp = (int)(((float)q + 0.5f) * inv_e), f = e0 + (q - pp * E);
-    x[i] = get(pick(a.part_kv, a.part_m, f >= kD * kD) + ((size_t)b * G + pp) * (kD * kD) + (f & (kD * kD - 1)));
+    x[i] = get(a.part_kv + ((size_t)b * G + pp) * (2 * kD * kD) + f);
   }
 #pragma unroll
   for (int i = 0; i < kPer; ++i)
@@ -483,8 +483,8 @@ __device__ void res_stats_to_lds(const ResArgs& a, unsigned char* smem, int b, i
   uint64_t x[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int q = tid + kResThreads * i;  // piece q: elements 2 q, 2 q + 1
-    const float* src = pick(a.fin_kv, a.fin_m, 2 * q >= kD * kD) + (size_t)b * (kD * kD) + ((2 * q) & (kD * kD - 1));
+    const int q = tid + kResThreads * i;  // piece q: elements 2 q, 2 q + 1 (phi(K)^T V for i < kPer / 2, then M)
+    const float* src = (i < kPer / 2 ? a.fin_kv : a.fin_m) + (size_t)b * (kD * kD) + ((2 * q) & (kD * kD - 1));
     x[i] = 2 * q < nstat ? get64(src) : 0;
   }
 #pragma unroll
