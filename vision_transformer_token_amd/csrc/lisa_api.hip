@@ -231,27 +231,37 @@ enum class Mode { kForward, kReduce, kApply };
 // (the weight region is always laid out), so lisa_forward, lisa_reduce,
 // lisa_apply and the backward's statistics of one problem all cut the slices
 // the same way and form the same fixed-order sums.
-bool resident_fits(const Plan& pl, int cus, bool mlp, lisa::ResPlan& rp) {
+bool resident_fits(const Plan& pl, int cus, bool mlp, lisa::ResPlan& rp, bool* doubled = nullptr) {
   (void)mlp;  // the predictor runs inside the resident kernel too
   if (pl.dtype != LISA_BF16 || pl.feature != LISA_FEATURE_RELU || pl.T > lisa::kResMaxT) return false;
-  const int gcap = std::min(std::max(1, cus / pl.BH), plan_ranks(lisa::kMaxRanks, kRoundSlices, pl.n));
-  return lisa::res_plan(pl.H, pl.W, pl.T, true, gcap, rp);
+  const int gmax = plan_ranks(lisa::kMaxRanks, kRoundSlices, pl.n);
+  const int gcap = std::min(std::max(1, cus / pl.BH), gmax);
+  if (doubled) *doubled = false;
+  if (lisa::res_plan(pl.H, pl.W, pl.T, true, gcap, rp)) return true;
+  // Slices too large for one tile at the ranks the grid gives each (DeiT-T
+  // 384: 192 slices of 24 x 24 on 256 CUs): twice the ranks, the groups then
+  // taking the slices in two rounds.
+  if (doubled) *doubled = true;
+  return 2 * gcap <= gmax && lisa::res_plan(pl.H, pl.W, pl.T, true, 2 * gcap, rp);
 }
 
 // The default between the two kernels where both apply: the resident one.
 // Measured on MI355X (256 CUs, bf16), forward of one call, resident against
-// streaming: PVT-T stage 1 (32 slices of 56 x 56, T = 3) 45.0 / 45.7 us;
-// DeiT-T at 224 (192 slices of 14 x 14, T = 3) 24.5 / 37.0 us; one 200 x 320
-// slice (T = 5) 46.8 / 50.2 us; one 128 x 128 slice 31.9 / 35.4 us; one
-// 256 x 256 slice 43.9 / 49.9 us.
-bool resident_preferred(const lisa::ResPlan&) { return true; }
+// streaming: PVT-T stage 1 (32 slices of 56 x 56, T = 3) 41.7 / 46.4 us;
+// DeiT-T at 224 (192 slices of 14 x 14, T = 3) 23.4 / 37.1 us; one 200 x 320
+// slice (T = 5) 44.4 / 50.5 us; one 128 x 128 slice 31.0 / 35.0 us; one
+// 256 x 256 slice 43.0 / 50.3 us.  Where the tiles fit only with twice the
+// ranks (two rounds of slices per group), the streaming kernel is the
+// faster: DeiT-T 384 57.8 against 60.7 us.
+bool resident_preferred(const lisa::ResPlan&, bool doubled) { return !doubled; }
 
 // Whether the resident kernel runs the problem: where it fits, when asked
 // for, and by default where it is the faster of the two kernels.
 bool resident_plan(const Plan& pl, int cus, bool mlp, lisa::ResPlan& rp) {
-  if (pl.schedule == LISA_SCHEDULE_STREAMING || !resident_fits(pl, cus, mlp, rp)) return false;
+  bool doubled = false;
+  if (pl.schedule == LISA_SCHEDULE_STREAMING || !resident_fits(pl, cus, mlp, rp, &doubled)) return false;
   if (pl.schedule == LISA_SCHEDULE_RESIDENT) return true;
-  return resident_preferred(rp);
+  return resident_preferred(rp, doubled);
 }
 
 // One launch of the resident kernel, one workgroup per compute unit.
