@@ -52,7 +52,7 @@ static void check(int H, int W, int T, int gcap) {
   const int krows = L.zrow + 1;
   CHECK(L.k == 0 && L.v >= L.k + krows * kResRowBytes, "k region");
   // The combine stages its share of all G partials (nstat floats in all) there.
-  CHECK(L.v - L.k >= kResCombineFloats * 4, "k region holds the combine's staging (and the statistics' rows)");
+  CHECK(L.v - L.k >= kResCombineFloats * 4 && kResCombineFloats % 256 == 0, "k region holds the combine's staging");
   CHECK(L.w >= L.v + krows * kResRowBytes && L.w >= L.v + slots * kResRowBytes, "v region");
   CHECK(L.tab >= L.w + res_up(slots * T, 64) * 4, "w region");
   CHECK(L.loc >= L.tab + slots * 2, "tab region");
@@ -118,8 +118,11 @@ static void check(int H, int W, int T, int gcap) {
       int e0, e1;
       res_combine_range(nstat, p.G, g, e0, e1);
       CHECK(e0 == next && e1 >= e0, "combine range %d", g);
-      CHECK((e1 - e0) * p.G <= kResCombineFloats && (e1 - e0) * p.G * 4 <= L.v - L.k, "combine staging %d",
-            (e1 - e0) * p.G);
+      // The staging DMA writes runs of 256 floats (16 bytes per lane, when E
+      // and e0 are multiples of four) or 64 floats, the last one padded.
+      const int E = e1 - e0, run = (E % 4 == 0 && e0 % 4 == 0) ? 256 : 64;
+      CHECK(res_up(E * p.G, run) <= kResCombineFloats && res_up(E * p.G, run) * 4 <= L.v - L.k, "combine staging %d",
+            E * p.G);
       CHECK(e1 - e0 >= 16, "combine share %d", e1 - e0);  // the float quotient q / E stays exact
       next = e1;
     }

@@ -382,66 +382,66 @@ __device__ void res_sum_s(const ResArgs& a, unsigned char* smem, int b, int tid)
   lds_barrier();
 }
 
-// Store element e = 64 r + c of one statistics matrix as fp32 at fin[e] and
-// as bf16 in its MFMA A-operand fragment slot of frag: fragment (mb, q, lane,
-// j) holds X[dimof(8 q + j, lane / 32)][32 mb + lane % 32].
-__device__ __forceinline__ void res_store_stat(float* fin, uint16_t* frag, int e, float v) {
+// Store element e = 64 r + c of one statistics matrix as bf16 in its MFMA
+// A-operand fragment slot of frag: fragment (mb, q, lane, j) holds
+// X[dimof(8 q + j, lane / 32)][32 mb + lane % 32].
+__device__ __forceinline__ void res_store_frag(uint16_t* frag, int e, float v) {
   const int r = e >> 6, c = e & 63;
-  fin[e] = v;
   const int vs = 16 * (r >> 5) + 4 * ((r >> 3) & 3) + (r & 3);
   const int ln = (c & 31) + 32 * ((r >> 2) & 1);
   const int idx = (((c >> 5) * 4 + vs / 8) * 64 + ln) * 8 + vs % 8;
   __hip_atomic_store(frag + idx, f2bf(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One element's total of the combine: the statistics as fp32 rows
-// (consecutive threads, consecutive elements), which the ranks read back;
-// the bf16 fragment slot too when only the statistics are asked for (another
-// kernel's output pass may read them).  With one rank the staged element is
-// the total: it is kept there, in place, for this rank's output.
-__device__ __forceinline__ void res_combine_store(const ResArgs& a, float* stg, int b, int G, int e0, int e, int ec,
-                                                  float v, bool frags) {
+// One element's total of the combine: the statistics as fp32 rows (which the
+// backward and the entry points reading the statistics take) and in their
+// bf16 fragment slot (which every rank's output loads).
+__device__ __forceinline__ void res_combine_store(const ResArgs& a, int b, int e0, int e, float v) {
   const int f = e0 + e;
   const bool m = f >= kD * kD;
-  float* fin = pick(a.fin_kv, a.fin_m, m) + (size_t)b * (kD * kD);
-  put(fin + (f & (kD * kD - 1)), v);
-  if (frags)
-    res_store_stat(fin, pick(static_cast<uint16_t*>(a.frag_kv), static_cast<uint16_t*>(a.frag_m), m) + (size_t)b * (kD * kD),
-                   f & (kD * kD - 1), v);
-  if (G == 1) stg[ec] = v;
+  put(pick(a.fin_kv, a.fin_m, m) + (size_t)b * (kD * kD) + (f & (kD * kD - 1)), v);
+  res_store_frag(pick(static_cast<uint16_t*>(a.frag_kv), static_cast<uint16_t*>(a.frag_m), m) + (size_t)b * (kD * kD),
+                 f & (kD * kD - 1), v);
 }
 
 // Rank g's share of the slice statistics: elements [e0, e1) of the flattened
 // [phi(K)^T V | M] (nstat = 4096 or 8192 of them) summed over the G partials.
 // The G partials' elements (G E <= nstat + G floats) are first staged in the
-// K region (free after the sweeps) as [G][E] floats: each thread issues its
-// loads at once (a single round trip), then writes them to LDS.
-// Then the G partials of each element are added in an order fixed by G.
-// With one rank per slice the totals stay in the staging, in row order,
-// where the output takes them.
+// K region (free after the sweeps) as [G][E] floats by coherent DMA, all in
+// flight at once (a single round trip): 16 bytes per lane where E and e0 are
+// multiples of four (a lane's four elements then lie in one partial), else
+// 4 bytes.  Then the G partials of each element are added in an order fixed
+// by G.
 __device__ void res_combine(const ResArgs& a, unsigned char* smem, int b, int g, int nstat, int tid) {
   const int G = a.p.G;
   int e0, e1;
   res_combine_range(nstat, G, g, e0, e1);
   const int E = e1 - e0, total = G * E;
   float* stg = reinterpret_cast<float*>(smem + a.p.L.k);
-  // q -> (partial p, element e) with p = floor(q / E): q < 8192 and E >= 16,
+  // q -> (partial p, element e) with p = floor(q / E): q < 8448 and E >= 16,
   // so (q + 1/2) / E in float stays well within 1/(2E) of the exact quotient.
   const float inv_e = 1.f / (float)E;
-  constexpr int kPer = (kResCombineFloats + kResThreads - 1) / kResThreads;  // loads per thread (total <= G E)
-  float x[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int q = min(tid + kResThreads * i, total - 1);
-    const int pp = (int)(((float)q + 0.5f) * inv_e), f = e0 + (q - pp * E);
-    x[i] = get(a.part_kv + ((size_t)b * G + pp) * (2 * kD * kD) + f);
+  const int wave = tid >> 6, lane = tid & 63;
+  const float* part = a.part_kv + (size_t)b * G * (2 * kD * kD) + e0;
+  if ((E & 3) == 0 && (e0 & 3) == 0) {
+    // Runs of 256 floats; the last one is padded with copies of the last
+    // four elements (G E is then a multiple of 256 at most 8448).
+    for (int r = wave; 256 * r < total; r += kResWaves) {
+      const int q = min(256 * r + 4 * lane, total - 4);
+      const int pp = (int)(((float)q + 0.5f) * inv_e);
+      dma16_coherent(part + (size_t)pp * (2 * kD * kD) + (q - pp * E), lds_addr(smem + a.p.L.k + 1024 * r));
+    }
+  } else {
+    // Runs of 64 floats (G E rounds up to at most 8448).
+    for (int r = wave; 64 * r < total; r += kResWaves) {
+      const int q = min(64 * r + lane, total - 1);
+      const int pp = (int)(((float)q + 0.5f) * inv_e);
+      dma4_coherent(part + (size_t)pp * (2 * kD * kD) + (q - pp * E), lds_addr(smem + a.p.L.k + 256 * r));
+    }
   }
-#pragma unroll
-  for (int i = 0; i < kPer; ++i)
-    if (tid + kResThreads * i < total) stg[tid + kResThreads * i] = x[i];
-  lds_barrier();
+  wait_all();
+  __syncthreads();
   res_stamp(a, b < a.S, kResStampCStaged);
-  const bool frags = a.mode == kResReduce;
   // Consecutive threads take consecutive elements of one partial (no LDS
   // bank conflicts).  Fewer than kResThreads / 2 elements: ngrp groups of E
   // threads, group k adding partials k, k + ngrp, ... in turn; then thread e
@@ -453,7 +453,7 @@ __device__ void res_combine(const ResArgs& a, unsigned char* smem, int b, int g,
       float v = 0.f;
 #pragma unroll 4
       for (int pp = 0; pp < G; ++pp) v += stg[pp * E + e];
-      res_combine_store(a, stg, b, G, e0, e, e, v, frags);
+      res_combine_store(a, b, e0, e, v);
     }
   } else {
     const int ngrp = kResThreads / E, e = tid % E, pg = tid / E;
@@ -468,28 +468,23 @@ __device__ void res_combine(const ResArgs& a, unsigned char* smem, int b, int g,
     if (tid < E) {
       float v = 0.f;
       for (int k = 0; k < ngrp; ++k) v += sums[k * E + tid];
-      res_combine_store(a, stg, b, G, e0, tid, tid, v, frags);
+      res_combine_store(a, b, e0, tid, v);
     }
   }
   if (g == 0 && tid < kD) put(a.fin_s + (size_t)b * kD + tid, reinterpret_cast<const float*>(smem + a.p.L.s)[tid]);
   res_stamp(a, b < a.S, kResStampCSummed);
 }
 
-// The slice statistics [phi(K)^T V | M] as fp32 rows (nstat floats) from the
-// workspace into the K region: 8-byte coherent loads, all in flight at once.
-__device__ void res_stats_to_lds(const ResArgs& a, unsigned char* smem, int b, int nstat, int tid) {
-  uint64_t* dst = reinterpret_cast<uint64_t*>(smem + a.p.L.k);
-  constexpr int kPer = 2 * kD * kD / 2 / kResThreads;  // 8-byte pieces per thread
-  uint64_t x[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int q = tid + kResThreads * i;  // piece q: elements 2 q, 2 q + 1 (phi(K)^T V for i < kPer / 2, then M)
-    const float* src = (i < kPer / 2 ? a.fin_kv : a.fin_m) + (size_t)b * (kD * kD) + ((2 * q) & (kD * kD - 1));
-    x[i] = 2 * q < nstat ? get64(src) : 0;
+// The slice statistics' bf16 fragments (phi(K)^T V, then M when nmat = 2),
+// as the combine wrote them, into the scratch area: coherent DMA, 1 KB per
+// wave instruction, all in flight at once; no wait here.
+__device__ void res_frags_dma(const ResArgs& a, unsigned char* frag, int b, int nmat, int tid) {
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int m = 0; m < nmat; ++m) {
+    const unsigned char* src = static_cast<const unsigned char*>(m ? a.frag_m : a.frag_kv) + (size_t)b * kFragBytes;
+    for (int run = wave; run < kFragBytes / 1024; run += kResWaves)
+      dma16_coherent(src + run * 1024 + lane * 16, lds_addr(frag + m * kFragBytes + run * 1024));
   }
-#pragma unroll
-  for (int i = 0; i < kPer; ++i)
-    if (2 * (tid + kResThreads * i) < nstat) dst[tid + kResThreads * i] = x[i];
 }
 
 // MFMA A-operand fragments (bf16, 8 KB) of a 64 x 64 matrix from its fp32
@@ -869,19 +864,19 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
 
       if (fwd) {
         if (global) {
-          // The statistics as fp32 rows (phi(K)^T V, then M): left by the
-          // sweeps (one rank, forward) or loaded into the K region (with one
-          // rank and the combine they are already there); then as bf16
-          // fragments in the scratch area.
-          if (!(stats && p.G == 1)) {
-            res_stats_to_lds(a, smem, b, p.T >= 3 ? 2 * kD * kD : kD * kD, tid);
+          // The statistics (phi(K)^T V, then M) as bf16 fragments in the
+          // scratch area: built from the fp32 rows the sweeps left in LDS
+          // (one rank, forward), else loaded as the combine wrote them.
+          if (direct) {
+            const float* rows = reinterpret_cast<const float*>(smem + L.st);
+            res_frags_from_rows(rows, smem + L.scr, tid);
+            if (p.T >= 3) res_frags_from_rows(rows + kD * kD, smem + L.scr + kFragBytes, tid);
+            lds_barrier();
+          } else {
+            res_frags_dma(a, smem + L.scr, b, p.T >= 3 ? 2 : 1, tid);
             wait_all();
             __syncthreads();
           }
-          const float* rows = reinterpret_cast<const float*>(smem + (direct ? L.st : L.k));
-          res_frags_from_rows(rows, smem + L.scr, tid);
-          if (p.T >= 3) res_frags_from_rows(rows + kD * kD, smem + L.scr + kFragBytes, tid);
-          lds_barrier();
         }
         res_stamp(a, first, kResStampFrags);
         const unsigned char* fkv = smem + L.scr;

@@ -31,8 +31,8 @@ constexpr int kResRowBytes = 128;           // one staged bf16 row of 64 feature
 // statistics fragments.
 constexpr int kResScratch = 4 * 32 * 32 * 4 + 64 * 4;
 // [G][E] floats staged by a rank's combine: E is nstat / G rounded up or
-// down, so G * E <= nstat + G <= 8192 + 256.  Later the same region holds
-// the statistics' fp32 rows.
+// down, so G * E <= nstat + G <= 8192 + 256 (a multiple of 256: the staging
+// DMA's padded last run stays within it too).
 constexpr int kResCombineFloats = 2 * 64 * 64 + 256;
 constexpr int kResKRegionMin = kResCombineFloats * 4;
 
@@ -51,7 +51,7 @@ struct ResLayout {
   int loc;    // the local branch's tables: [block][64] uint16 window cells, [block][2] uint32 grid
               // masks, [64] uint32 neighbour masks, [4][64] bf16x8 one-hot operands (res_loc_*)
   int s;      // s = sum_j phi(K_j) of the slice, 64 fp32
-  int scr;    // the sweeps' second-half products, the waves' s sums, later the statistics fragments
+  int scr;    // the sweeps' second-half products, the waves' s sums, later the statistics' bf16 fragments
   int st;     // one rank per slice: the statistics [phi(K)^T V | M] as fp32 rows (32 KB; else unused)
   int total;
 };
@@ -131,7 +131,7 @@ __host__ __device__ inline bool res_layout(ResPlan& p) {
   int o = 0;
   p.L.k = o;
   // Once the sweeps are done the K region stages the partials a rank
-  // combines (its share of all G partials), then the statistics' rows.
+  // combines (its share of all G partials).
   o += res_max(res_up(krows * kResRowBytes, 1024), kResKRegionMin);
   p.L.v = o;
   o += res_up(vrows * kResRowBytes, 1024);
