@@ -244,7 +244,7 @@ def summarize_profiles(outdir, workload, commands):
 
 def write_phases_profile(w, rec, command):
     """profiles/lisa_forward_phases_<workload>.md from a phases_timing record:
-    each stage's median and 90th-percentile end time over the workgroups, the
+    each stage's median, 90th-percentile and latest end time over the workgroups, the
     interval since the previous stage's median end, and, where a stage moves
     HBM bytes, those bytes over that interval."""
     G, BH = rec["ranks_per_slice"], w.B * w.heads
@@ -266,9 +266,9 @@ def write_phases_profile(w, rec, command):
              ("mwait", "", 0),
              ("cstaged", "every partial read once (by the rank that sums it)", 0 if direct else BH * G * nstat * mat),
              ("csummed", "", 0),
-             ("combine", "the statistics written", 0 if direct else BH * nstat * mat),
+             ("combine", "the statistics written (fp32 rows and bf16 fragments)", 0 if direct else BH * nstat * mat * 3 // 2),
              ("cwait", "", 0),
-             ("frags", "the statistics read by every rank", 0 if direct else BH * G * nstat * mat),
+             ("frags", "the statistics' bf16 fragments read by every rank", 0 if direct else BH * G * nstat * mat // 2),
              ("out", "", 0),
              ("end", "Y written (interval from the fragments' end: the output stage)", tok * 64 * esize)]
     since = {"end": "frags", "cstaged": "mwait"}  # intervals that start earlier than the previous row
@@ -277,25 +277,26 @@ def write_phases_profile(w, rec, command):
              f"command: {command}", "",
              f"lisa_forward_phases: every workgroup stamps the device's 100 MHz clock (s_memrealtime) as its "
              f"wave 0 reaches each stage of its first slice; times are from the first workgroup's start, "
-             f"median and 90th percentile over the {rec['workgroups']} working workgroups, averaged over "
+             f"median, 90th percentile and maximum over the {rec['workgroups']} working workgroups, averaged over "
              f"{rec['calls']} cold calls.  {G} rank(s) per slice.  Wave 0 is the oldest wave and finishes a "
              f"stage first: a stage's end for the whole workgroup is nearer the next stage's start.  The "
              f"interval of a stage runs from the previous listed stage's median; the bytes are those the "
              f"interval moves to or from HBM for the whole launch.", "",
-             "| stage | median end us | p90 end us | interval us | HBM traffic in the interval | MB | GB/s |",
-             "|---|---|---|---|---|---|---|"]
+             "| stage | median end us | p90 end us | max end us | interval us | HBM traffic in the interval | MB | GB/s |",
+             "|---|---|---|---|---|---|---|---|"]
     prev = None
     for name, what, nbytes in order:
         m = st.get(name, {}).get("median_us")
         if m is None:
             continue
-        q = st[name]["p90_us"]
+        q, mx = st[name]["p90_us"], st[name].get("max_us")
+        mxs = "" if mx is None else f"{mx:.2f}"
         base = st.get(since.get(name, ""), {}).get("median_us")
         dt = None if prev is None else m - (base if base is not None else prev)
         rate = f"{nbytes / (dt * 1e-6) / 1e9:.0f}" if nbytes and dt and dt > 0 else ""
-        lines.append(f"| {name} | {m:.2f} | {q:.2f} | {'' if dt is None else f'{dt:.2f}'} | {what} | "
+        lines.append(f"| {name} | {m:.2f} | {q:.2f} | {mxs} | {'' if dt is None else f'{dt:.2f}'} | {what} | "
                      f"{nbytes / 1e6:.2f} | {rate} |" if nbytes else
-                     f"| {name} | {m:.2f} | {q:.2f} | {'' if dt is None else f'{dt:.2f}'} | {what} | | |")
+                     f"| {name} | {m:.2f} | {q:.2f} | {mxs} | {'' if dt is None else f'{dt:.2f}'} | {what} | | |")
         prev = m
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(os.path.join(ROOT, "profiles", f"lisa_forward_phases_{w.name}.md"), "w") as f:
@@ -721,8 +722,8 @@ def main():
 
     def phases_timing(calls, warmup):
         """The stage timeline of lisa_forward_phases over `calls` cold calls
-        (rotating input sets): per stage, the median and 90th percentile over
-        the active workgroups of the time since the first workgroup started,
+        (rotating input sets): per stage, the median, 90th percentile and
+        maximum over the active workgroups of the time since the first workgroup started,
         averaged over the calls, in microseconds."""
         import numpy as np
 
@@ -736,7 +737,7 @@ def main():
 
         for i in range(warmup):
             forward(sets[i % nsets])
-        med, p90, rows = [], [], None
+        med, p90, mx, rows = [], [], [], None
         for i in range(calls):
             stamps.fill_(0)
             torch.cuda.synchronize()
@@ -752,13 +753,17 @@ def main():
             rel[a_st == 0] = np.nan  # stages the problem does not have
             med.append(np.nanmedian(rel, axis=0))
             p90.append(np.nanpercentile(rel, 90, axis=0))
+            mx.append(np.nanmax(rel, axis=0))
             rows = int(active.sum())
             ranks = int((rank[active] & 0xFFFFFFFF).max()) + 1
-        med, p90 = np.nanmean(np.array(med), axis=0), np.nanmean(np.array(p90), axis=0)
+        med, p90, mx = (np.nanmean(np.array(v), axis=0) for v in (med, p90, mx))
+
+        def us(v):
+            return None if np.isnan(v) else round(float(v), 3)
+
         return {"workgroups": rows, "calls": calls, "ranks_per_slice": ranks,
-                "stages": {name: {"median_us": None if np.isnan(m) else round(float(m), 3),
-                                  "p90_us": None if np.isnan(q) else round(float(q), 3)}
-                           for name, m, q in zip(lisa.STAGES, med, p90)}}
+                "stages": {name: {"median_us": us(m), "p90_us": us(q), "max_us": us(z)}
+                           for name, m, q, z in zip(lisa.STAGES, med, p90, mx)}}
 
     if args.phases:
         rec = phases_timing(args.steps, args.warmup)

@@ -47,6 +47,17 @@ def test_problem_struct_matches_header():
     assert ctypes.sizeof(lisa.Problem) == 4 * len(names) == 44
 
 
+def test_stage_list_matches_header():
+    """lisa.STAGES and LISA_PHASES are the header's LISA_STAGE_* enum, in order."""
+    hdr = open(HEADER).read()
+    assert int(re.search(r"#define LISA_PHASES (\d+)", hdr).group(1)) == lisa.LISA_PHASES
+    body = hdr[hdr.index("LISA_STAGE_START = 0"):]
+    body = body[:body.index("};")]
+    names = [n.lower() for n in re.findall(r"LISA_STAGE_(\w+)", body)]
+    assert names == lisa.STAGES
+    assert len(names) < lisa.LISA_PHASES  # the last entry holds the rank
+
+
 def prob(**kw):
     base = dict(batch=2, heads=3, grid_h=5, grid_w=7, d_h=64, d_v=64, T=3, dtype=lisa.LISA_BF16,
                 eps=1e-6)
