@@ -317,6 +317,13 @@ __device__ __forceinline__ void put(float* p, float v) {
 __device__ __forceinline__ void put(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// 16 bytes at agent scope (sc1), for data other workgroups read: one vector
+// store instruction, so a wave's pieces go out as whole lines.
+__device__ __forceinline__ void put16(void* p, uint4 v) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 x = {v.x, v.y, v.z, v.w};
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(x) : "memory");
+}
 __device__ __forceinline__ float get(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -449,11 +449,46 @@ __device__ void res_combine(const ResArgs& a, unsigned char* smem, int b, int g,
   // partials of its elements in turn.  Either way the order of additions
   // depends on G alone.
   if (2 * E > kResThreads) {
+    // A share of whole 16-row blocks (G <= 8) holds whole fragment pieces:
+    // the totals go back into the staging (element e's first partial slot,
+    // read by this thread only) and the pieces are stored 16 bytes at a time.
+    const bool whole = (E & 1023) == 0 && (e0 & 1023) == 0;
     for (int e = tid; e < E; e += kResThreads) {
       float v = 0.f;
 #pragma unroll 4
       for (int pp = 0; pp < G; ++pp) v += stg[pp * E + e];
-      res_combine_store(a, b, e0, e, v);
+      if (whole) {
+        const int f = e0 + e;
+        put(pick(a.fin_kv, a.fin_m, f >= kD * kD) + (size_t)b * (kD * kD) + (f & (kD * kD - 1)), v);
+        stg[e] = v;
+      } else {
+        res_combine_store(a, b, e0, e, v);
+      }
+    }
+    if (whole) {
+      lds_barrier();
+      // Piece (block beta, mb, lane) of the share: rows [16 beta, 16 beta + 16)
+      // of the flattened [phi(K)^T V | M] form fragment step q = beta % 4 of
+      // matrix beta / 4; element j holds row dimof(8 q + j, lane / 32), column
+      // 32 mb + lane % 32.
+      for (int pc = tid; pc < E / 8; pc += kResThreads) {
+        const int beta = e0 / 1024 + pc / 128, mb = (pc >> 6) & 1, ln = pc & 63, q = beta & 3;
+        const int c = 32 * mb + (ln & 31), hh = ln >> 5;
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          float x2[2];
+#pragma unroll
+          for (int t2 = 0; t2 < 2; ++t2) {
+            const int vs = 8 * q + j + t2;
+            const int row = 32 * (vs >> 4) + 8 * ((vs >> 2) & 3) + 4 * hh + (vs & 3);  // in [16 q, 16 q + 16)
+            x2[t2] = stg[4096 * (beta >> 2) + 64 * row + c - e0];
+          }
+          w[j / 2] = pack_bf16x2(x2[0], x2[1]);
+        }
+        unsigned char* frag = static_cast<unsigned char*>(beta >= 4 ? a.frag_m : a.frag_kv) + (size_t)b * kFragBytes;
+        put16(frag + ((mb * 4 + q) * 64 + ln) * 16, make_uint4(w[0], w[1], w[2], w[3]));
+      }
     }
   } else {
     const int ngrp = kResThreads / E, e = tid % E, pg = tid / E;
