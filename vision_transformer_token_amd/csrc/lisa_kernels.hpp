@@ -41,8 +41,11 @@ constexpr int kCntStride = 32;  // words between slices: each slice's counters o
 // With more than kSubRanks ranks per slice, a phase's arrivals are counted per
 // group of kSubRanks ranks, each group's counter on its own 128-byte line
 // (slices < kMaxSubSlices, groups < kMaxSubs); a wait then reads every
-// group's counter at once.
-constexpr int kSubRanks = 16;
+// group's counter at once, one per lane (at most 64).  Arrivals on one
+// counter serialise at the memory: with 256 ranks on one 256 x 256 slice,
+// groups of 4 / 8 / 16 / 32 ranks gave 39.6 / 40.9 / 41.8 / 43.5 us per
+// forward (one 200 x 320 slice: 42.0 / 42.8 / 43.4 / 44.8 us).
+constexpr int kSubRanks = 4;
 constexpr int kMaxSubSlices = 8;
 constexpr int kMaxSubs = 256 / kSubRanks;
 // Kernel variants (without the predictor; FlowArgs::variant): arrivals per

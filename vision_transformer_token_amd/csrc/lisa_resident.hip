@@ -355,29 +355,41 @@ __device__ void res_sweep_publish(const ResArgs& a, unsigned char* smem, int b, 
     res_arrive(a, b, g, kIsM ? kRcM : kRcKV);
 }
 
-// s = the fixed-order sum of the slice's G partials, into LDS: wave w sums
-// partials w, w + 4, ... (sixteen loads in flight at a time), then wave 0
-// adds the four sums in wave order.
+// s = the fixed-order sum of the slice's G partials, into LDS.  The partials
+// ([G][64] floats) are read as 16-byte pieces, every load in flight at once
+// (a single round trip even at G = 256): load i of wave w takes pieces
+// 64 (8 i + w) + lane, i.e. partial 4 (8 i + w) + lane / 16, elements
+// 4 (lane % 16) + 0..3; coherent buffer loads (sc1; a piece past the
+// partials reads as zero).  Each lane adds its loads in i order, then thread
+// e < 64 adds the 32 (wave, lane / 16) sums of its element in a fixed order.
 __device__ void res_sum_s(const ResArgs& a, unsigned char* smem, int b, int tid) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int kLoads = kMaxRanks / 4 / kResWaves;  // loads per lane: 4 partials per wave instruction
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, G = a.p.G;
-  float* sw = reinterpret_cast<float*>(smem + a.p.L.scr);  // [waves][64]
-  const float* ps = a.part_s + (size_t)b * G * kD + lane;
-  const int np = (G - wave + kResWaves - 1) / kResWaves;
-  float t = 0.f;
-  for (int q0 = 0; q0 < np; q0 += 16) {
-    float x[16];
+  float* sw = reinterpret_cast<float*>(smem + a.p.L.scr);  // [waves][64 lanes][4]
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(a.part_s + (size_t)b * G * kD, 0, G * kD * 4, 0x00020000);
+  u32x4 x[kLoads];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) x[q] = get(ps + (size_t)min(wave + kResWaves * (q0 + q), G - 1) * kD);
-#pragma unroll
-    for (int q = 0; q < 16; ++q) t += (q0 + q < np) ? x[q] : 0.f;
+  for (int i = 0; i < kLoads; ++i) {
+    const int piece = 64 * (kResWaves * i + wave) + lane;  // bytes 16 piece .. of the slice's partials
+    x[i] = 16 * piece < G * kD * 4 ? __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * piece, 0, 16) : (u32x4)0u;
   }
-  sw[wave * kD + lane] = t;
+  float t[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) t[c] += __uint_as_float(x[i][c]);
+  *reinterpret_cast<float4*>(sw + 4 * (wave * 64 + lane)) = make_float4(t[0], t[1], t[2], t[3]);
   lds_barrier();
-  if (wave == 0) {
+  if (tid < kD) {
+    const int j = tid >> 2, c = tid & 3;
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < kResWaves; ++w) v += sw[w * kD + lane];
-    reinterpret_cast<float*>(smem + a.p.L.s)[lane] = v;
+    for (int w = 0; w < kResWaves; ++w)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v += sw[4 * (w * 64 + 16 * q + j) + c];
+    reinterpret_cast<float*>(smem + a.p.L.s)[tid] = v;
   }
   lds_barrier();
 }
@@ -494,15 +506,26 @@ __device__ void res_combine(const ResArgs& a, unsigned char* smem, int b, int g,
     const int ngrp = kResThreads / E, e = tid % E, pg = tid / E;
     float* sums = reinterpret_cast<float*>(smem + a.p.L.scr);  // [ngrp][E]
     if (pg < ngrp) {
+      // Eight reads in flight at a time (about 16 partials per group).
       float v = 0.f;
-#pragma unroll 4
-      for (int pp = pg; pp < G; pp += ngrp) v += stg[pp * E + e];
+      for (int p0 = pg; p0 < G; p0 += 8 * ngrp) {
+        float x[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[k] = p0 + k * ngrp < G ? stg[(p0 + k * ngrp) * E + e] : 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v += x[k];
+      }
       sums[pg * E + e] = v;
     }
     lds_barrier();
     if (tid < E) {
+      // ngrp <= kResThreads / 16 = 32 group sums, all read at once.
+      float x[kResThreads / 16];
+#pragma unroll
+      for (int k = 0; k < kResThreads / 16; ++k) x[k] = k < ngrp ? sums[k * E + tid] : 0.f;
       float v = 0.f;
-      for (int k = 0; k < ngrp; ++k) v += sums[k * E + tid];
+#pragma unroll
+      for (int k = 0; k < kResThreads / 16; ++k) v += x[k];
       res_combine_store(a, b, e0, tid, v);
     }
   }
