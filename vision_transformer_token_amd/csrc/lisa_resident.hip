@@ -757,6 +757,16 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
   const bool fwd = a.mode != kResReduce;  // local branch and output
   const bool stats = a.mode != kResApply;  // sweeps and combine
 
+  // The workgroup counts itself done (done_cnt) once it has made its last
+  // counter access, not at its end: after its last slice's C wait when it
+  // takes part in hand-offs, else during its first staging (an idle
+  // workgroup at once).  The atomic's round trip then overlaps a load it
+  // waits for anyway, and the workgroup's end waits for nothing.
+  __shared__ unsigned done_sh;
+  const bool has_slice = rk.group >= 0 && rk.group < a.BH;
+  const bool count_late = has_slice && stats && a.do_kv && p.G > 1;
+  if (!has_slice && tid0 == 0) done_sh = bump(a.done_cnt);
+
   if (rk.group >= 0) {
     res_slot_table(reinterpret_cast<uint16_t*>(smem + L.tab), p, res_tile(p, rk.g));
     if (fwd) res_local_tables(smem, p, res_tile(p, rk.g));
@@ -814,6 +824,7 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
             qB[j][kb] = *reinterpret_cast<const bf16x8*>(Qb + tok * kD + 16 * kb + 8 * h);
         }
       }
+      if (!count_late && first && tid == 0) done_sh = bump(a.done_cnt);
       wait_all();
       __syncthreads();
       res_stamp(a, first, kResStampStaged);
@@ -915,6 +926,9 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
           res_arrive(a, b, rk.g, kRcC);
           res_wait(a, b, kRcC);
           res_stamp(a, first, kResStampCWait);
+          // The last counter access of the workgroup; with an output, the
+          // count goes out with the fragments' DMA below.
+          if (b + a.S >= a.BH && !(fwd && global) && tid == 0) done_sh = bump(a.done_cnt);
         } else {
           lds_barrier();  // the totals, in LDS; their global copies complete by the launch's end
         }
@@ -932,6 +946,7 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
             lds_barrier();
           } else {
             res_frags_dma(a, smem + L.scr, b, p.T >= 3 ? 2 : 1, tid);
+            if (count_late && b + a.S >= a.BH && tid == 0) done_sh = bump(a.done_cnt);
             wait_all();
             __syncthreads();
           }
@@ -995,25 +1010,21 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
     }
   }
 
-  // The last workgroup to finish clears the launch counters for the next call
-  // (every other workgroup's atomics have completed: each waited for them
-  // before counting itself done).
-  __shared__ int last;
+  // The workgroup that counted itself done last clears the launch counters
+  // for the next call: every workgroup counted itself after its last counter
+  // access, and each of its arrivals had been seen by its own waits, so no
+  // other atomic on them is still to come.  The clears need no order among
+  // themselves: the launch's end makes them visible to the next call.
   if (rk.group >= 0) res_stamp(a, true, kResStampOut);
-  wait_all();
   __syncthreads();
   res_stamp(a, true, kResStampEnd);
-  if (tid0 == 0) last = bump(a.done_cnt) == gridDim.x - 1;
-  __syncthreads();
-  if (last) {
+  if (done_sh == gridDim.x - 1) {
     for (int i = tid0; i < a.BH * kCntWords; i += kResThreads)
       put(a.slice_cnt + (size_t)(i / kCntWords) * kCntStride + i % kCntWords, 0u);
     if (a.grouped)
       for (int i = tid0; i < a.BH * 3 * kMaxSubs; i += kResThreads) put(a.sub_cnt + (size_t)i * kCntStride, 0u);
     if (tid0 < kXcds) put(a.tickets + tid0, 0u);
     if (a.clear_err && tid0 == 0) put(a.err, 0u);
-    wait_all();
-    __syncthreads();
     if (tid0 == 0) put(a.done_cnt, 0u);
   }
 }
