@@ -44,10 +44,12 @@
  *     be ordered on one stream; concurrent calls on one workspace race.
  *   - Scheduling: a call launches one workgroup per compute unit, and groups
  *     of its workgroups (up to 256, as many as the problem splits a
- *     (batch, head) slice into) wait for each other.  Ranks are handed out in
- *     the order workgroups start, so a call always completes when it can
- *     eventually run one group at a time; work on other streams only delays
- *     it.  A wait that lasts more than about half a second is abandoned (the
+ *     (batch, head) slice into) wait for each other.  The streaming kernel
+ *     hands out ranks in the order workgroups start; the resident kernel
+ *     gives a group consecutive workgroups (of one XCD where the group fits
+ *     in one), which the device starts in order.  Either way a call
+ *     completes when it can eventually run one group at a time (for the
+ *     resident kernel, on one XCD); work on other streams only delays it.  A wait that lasts more than about half a second is abandoned (the
  *     call then finishes with undefined Y); that only happens if other work keeps a group's
  *     workgroups from starting for that long.  The call cannot report it when
  *     it returns (the work is asynchronous); it raises a flag in the

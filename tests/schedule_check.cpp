@@ -12,7 +12,8 @@
 //     rescaled-Q rows stay inside their LDS regions, the regions do not
 //     overlap, and the layout fits the workgroup's LDS;
 //   - the sweep steps read only slots of the tile; the combine ranges of the
-//     G ranks partition the statistics.
+//     G ranks partition the statistics; the workgroup -> (group, rank) map
+//     takes every rank of every group once.
 // Prints one line per problem ("ok ..." or "FAIL ...") and exits non-zero on
 // any failure.
 #include <cstdio>
@@ -110,6 +111,22 @@ static void check(int H, int W, int T, int gcap) {
   }
   for (int r = 0; r < H; ++r)
     for (int c = 0; c < W; ++c) CHECK(owner[(size_t)r * W + c] >= 0, "token %d,%d uncovered", r, c);
+  // Workgroups -> (group, rank): for the grids of 256 (and 80, 304) compute
+  // units and slice counts around the XCD count, every rank of every group
+  // that has a slice is taken exactly once.
+  for (int grid : {256, 80, 304})
+    for (int BH : {1, 7, 8, 32, 192}) {
+      const int S = grid / p.G;
+      if (S < 1) continue;
+      std::vector<int> seen((size_t)S * p.G, 0);
+      for (int w = 0; w < grid; ++w) {
+        int group, g;
+        res_rank_of(p.G, S, BH, w, grid, group, g);
+        CHECK(group >= -1 && group < S && g >= 0 && g < p.G, "rank of workgroup %d: %d %d", w, group, g);
+        if (group >= 0 && group < S && g >= 0 && g < p.G) ++seen[(size_t)group * p.G + g];
+      }
+      for (int k = 0; k < S * p.G; ++k) CHECK(seen[k] == 1, "grid %d BH %d: group %d rank %d taken %d times", grid, BH, k / p.G, k % p.G, seen[k]);
+    }
   // Combine ranges partition the statistics, for both sizes, and each rank's
   // staging ([G][E] floats) fits the K region and its loads.
   for (int nstat : {4096, 8192}) {

@@ -403,24 +403,51 @@ def test_graph_replay_matches_eager(lisa):
 
 def test_abandoned_wait_is_reported_and_cleared(lisa):
     """lisa_workspace_check: clear after normal calls, set after a call whose
-    dependency wait was abandoned.  The condition is forced from the host: the
-    rank tickets (word 8 of the launch counters at the start of the workspace)
-    start at 1, so the first group of a PVT stage-1 forward (8 ranks per
-    slice, one ticket counter) never gets its rank 0, and its other ranks give
-    up waiting for it after the kernel's own bound; every workgroup still
-    finishes, and the last one resets the counters."""
+    dependency wait was abandoned.  The condition is forced from the host on
+    the streaming kernel, which draws ranks from tickets: the rank tickets
+    (word 8 of the launch counters at the start of the workspace) start at 1,
+    so the first group of a PVT stage-1 forward (one ticket counter) never
+    gets its rank 0, and its other ranks give up waiting for it after the
+    bounded wait's own limit (wait_for, which the resident kernel's waits use
+    too); every workgroup still finishes, and the last one resets the
+    counters."""
     w = workloads.get("pvt_t_stage1")
     d = to_dev(workloads.make_inputs(w))
     prob = lisa.make_problem(d["q"], d["v"], grid=(w.H, w.W), T=w.T, eps=w.eps)
     ws = lisa.new_workspace(prob, d["q"].device)
-    y0 = gpu_y(lisa, d, workspace=ws)
+    y0 = gpu_y(lisa, d, workspace=ws, schedule="streaming")
     assert lisa.lisa_workspace_check(ws) == lisa.LISA_OK
     ws.view(torch.int32)[8] = 1
     t0 = time.time()
-    gpu_y(lisa, d, workspace=ws)
+    gpu_y(lisa, d, workspace=ws, schedule="streaming")
     print(f"[stall] forward with a missing rank: {time.time() - t0:.2f} s", flush=True)
     assert lisa.lisa_workspace_check(ws) == lisa.LISA_ERR_STALLED
     assert lisa.lisa_workspace_check(ws) == lisa.LISA_OK
     assert int(ws.view(torch.int32)[8].item()) == 0
-    y1 = gpu_y(lisa, d, workspace=ws)
+    y1 = gpu_y(lisa, d, workspace=ws, schedule="streaming")
+    assert torch.equal(y0, y1)
+
+
+@pytest.mark.parametrize("name", ["pvt_t_stage1", "long_range_200x320"])
+def test_resident_waits_give_up_once_flagged(lisa, name):
+    """The resident kernel, whose ranks follow the workgroup index (no ticket
+    to withhold): with the stall flag (word 1 of the launch counters) raised
+    before the call, a dependency wait still waiting at its next check of the
+    flag gives up, the call completes, the flag is reported and cleared, and
+    the counters it leaves serve the next call (the same Y as before).  PVT
+    stage 1 waits on one counter per slice; one 200 x 320 slice on counters
+    per group of ranks."""
+    w = workloads.get(name)
+    d = to_dev(workloads.make_inputs(w))
+    prob = lisa.make_problem(d["q"], d["v"], grid=(w.H, w.W), T=w.T, eps=w.eps)
+    ws = lisa.new_workspace(prob, d["q"].device)
+    y0 = gpu_y(lisa, d, workspace=ws, schedule="resident")
+    assert lisa.lisa_workspace_check(ws) == lisa.LISA_OK
+    ws.view(torch.int32)[1] = 1
+    t0 = time.time()
+    gpu_y(lisa, d, workspace=ws, schedule="resident")
+    print(f"[stall] {name} with the flag raised: {time.time() - t0:.3f} s", flush=True)
+    assert lisa.lisa_workspace_check(ws) == lisa.LISA_ERR_STALLED
+    assert lisa.lisa_workspace_check(ws) == lisa.LISA_OK
+    y1 = gpu_y(lisa, d, workspace=ws, schedule="resident")
     assert torch.equal(y0, y1)

@@ -294,7 +294,6 @@ lisa_status run_resident(const Plan& pl, const lisa::ResPlan& rp, int cus, Mode 
   a.logit_scale = (float)(1.4426950408889634 / std::sqrt((double)kD));
   a.p = rp;
   a.S = cus / rp.G;
-  a.xcd_groups = 0;
   a.mode = mode == Mode::kForward ? lisa::kResForward : mode == Mode::kReduce ? lisa::kResReduce : lisa::kResApply;
   a.do_kv = (mode == Mode::kReduce || (mode == Mode::kForward && pl.T >= 2)) ? 1 : 0;
   a.do_m = (mode == Mode::kReduce || (mode == Mode::kForward && pl.T >= 3)) ? 1 : 0;

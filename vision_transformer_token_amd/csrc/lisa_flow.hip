@@ -1110,7 +1110,8 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
 
   // The last workgroup to finish clears the arrival counters for the next
   // launch (every other workgroup's atomics have completed: each waited for
-  // them before counting itself done).
+  // them before counting itself done).  The clears need no order among
+  // themselves: the launch's end makes them visible to the next call.
   wait_all();
   __syncthreads();
   if (tid == 0) last = bump(a.done_cnt) == gridDim.x - 1;
@@ -1122,8 +1123,6 @@ __global__ __launch_bounds__(kThreads) void flow_kernel(FlowArgs a) {
       for (int i = tid; i < a.BH * 3 * kMaxSubs; i += kThreads) put(a.sub_cnt + (size_t)i * kCntStride, 0u);
     if (tid < kXcds) put(a.tickets + tid, 0u);
     if (a.clear_err && tid == 0) put(a.err, 0u);
-    wait_all();
-    __syncthreads();
     if (tid == 0) put(a.done_cnt, 0u);
   }
 }

@@ -177,7 +177,6 @@ struct ResArgs {
   float eps;
   float logit_scale;      // log2(e) / sqrt(d_h)
   int S;                  // groups of G ranks
-  int xcd_groups;         // a group's ranks on one XCD (tickets per XCD)
   int mode;
   int do_kv, do_m;        // statistics formed by this launch
   int per_token;          // weights per token (LDS region [slot][T]) instead of geo
@@ -194,7 +193,7 @@ struct ResArgs {
   unsigned* slice_cnt;    // [BH][kCntStride]
   unsigned* sub_cnt;      // [kMaxSubSlices][3][kMaxSubs][kCntStride]
   unsigned* done_cnt;
-  unsigned* tickets;      // [kXcds]
+  unsigned* tickets;      // [kXcds] the streaming kernel's rank tickets (left at zero here too)
   unsigned* err;
   int clear_err;
   // The walk-weight predictor (forward only; nullptr: weights or geo):

@@ -41,19 +41,10 @@ struct ResRank {
   int group, g;  // group (-1: idle workgroup), rank within the group (= tile of the slice)
 };
 
-// Ranks are handed out in the order workgroups start (a ticket per XCD when
-// groups stay within an XCD), so a group only ever waits for workgroups that
-// are already running.
-__device__ __forceinline__ ResRank res_rank(const ResArgs& a, int ticket) {
+// Ranks follow the workgroup index (res_rank_of).
+__device__ __forceinline__ ResRank res_rank(const ResArgs& a) {
   ResRank r;
-  const int G = a.p.G;
-  if (a.xcd_groups) {
-    const int per = a.S / kXcds;
-    r.group = ticket / G < per ? (int)(blockIdx.x % kXcds) * per + ticket / G : -1;
-  } else {
-    r.group = ticket / G < a.S ? ticket / G : -1;
-  }
-  r.g = ticket % G;
+  res_rank_of(a.p.G, a.S, a.BH, (int)blockIdx.x, (int)gridDim.x, r.group, r.g);
   return r;
 }
 
@@ -741,16 +732,14 @@ __device__ __forceinline__ void res_apply(const unsigned char* frag, const float
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
   extern __shared__ __align__(1024) unsigned char smem[];
-  __shared__ int ticket;
   __shared__ float geo[kMaxT];  // geometric walk weights
   const ResPlan& p = a.p;
   const ResLayout& L = p.L;
   const int tid0 = threadIdx.x;
 
-  if (tid0 == 0) ticket = (int)bump(a.tickets + (a.xcd_groups ? blockIdx.x % kXcds : 0));
   if (tid0 < kMaxT) geo[tid0] = a.geo[tid0];
   __syncthreads();
-  const ResRank rk = res_rank(a, ticket);
+  const ResRank rk = res_rank(a);
   res_stamp(a, true, kResStampStart);
   if (a.stamps && tid0 == 0)
     a.stamps[(size_t)blockIdx.x * kResPhases + kResPhases - 1] = ((unsigned long long)(unsigned)rk.group << 32) | (unsigned)rk.g;
