@@ -130,7 +130,9 @@ size_t layout_forward(Plan& pl, size_t counter_slices) {
     o = up(o + bytes, kAlign);
     return at;
   };
-  pl.done_cnt = take(32 * sizeof(unsigned));
+  // Line 0: finished workgroups, the stall flag (word 1), rank tickets (words
+  // 8..15); lines 1..8: finished workgroups per XCD (the resident kernel).
+  pl.done_cnt = take((1 + lisa::kXcds) * lisa::kCntStride * sizeof(unsigned));
   pl.slice_cnt = take(counter_slices * lisa::kCntStride * sizeof(unsigned));
   pl.sub_cnt = take((size_t)lisa::kMaxSubSlices * 3 * lisa::kMaxSubs * lisa::kCntStride * sizeof(unsigned));
   pl.part_s = take(BH * G * vec);
@@ -312,6 +314,7 @@ lisa_status run_resident(const Plan& pl, const lisa::ResPlan& rp, int cus, Mode 
   a.slice_cnt = reinterpret_cast<unsigned*>(ws + pl.slice_cnt);
   a.sub_cnt = reinterpret_cast<unsigned*>(ws + pl.sub_cnt);
   a.done_cnt = reinterpret_cast<unsigned*>(ws + pl.done_cnt);
+  a.done_xcd = a.done_cnt + lisa::kCntStride;
   a.err = a.done_cnt + 1;
   a.tickets = a.done_cnt + 8;
   a.clear_err = clear_err ? 1 : 0;

@@ -192,7 +192,8 @@ struct ResArgs {
   void* frag_m;
   unsigned* slice_cnt;    // [BH][kCntStride]
   unsigned* sub_cnt;      // [kMaxSubSlices][3][kMaxSubs][kCntStride]
-  unsigned* done_cnt;
+  unsigned* done_cnt;     // XCDs whose workgroups have all finished
+  unsigned* done_xcd;     // [kXcds][kCntStride]: finished workgroups of each XCD (word 0 of each line)
   unsigned* tickets;      // [kXcds] the streaming kernel's rank tickets (left at zero here too)
   unsigned* err;
   int clear_err;

@@ -98,6 +98,17 @@ __device__ void res_arrive(const ResArgs& a, int b, int g, int c) {
   if (threadIdx.x == 0) (void)bump(res_counter(a, b, g, c));
 }
 
+// Thread 0 counts its workgroup finished, in two levels: on its XCD's
+// counter, and, for the XCD's last workgroup, on the device-wide one.  True
+// for the last workgroup of the launch.  (One counter for all 256
+// workgroups serialises their atomics: ~1.5 us before the last one returns.)
+__device__ bool res_count_done(const ResArgs& a) {
+  const int x = (int)(blockIdx.x % kXcds), grid = (int)gridDim.x;
+  const unsigned on_xcd = (unsigned)((grid - x + kXcds - 1) / kXcds);
+  if (bump(a.done_xcd + (size_t)x * kCntStride) != on_xcd - 1) return false;
+  return bump(a.done_cnt) == (unsigned)min(grid, kXcds) - 1;
+}
+
 // Wait until all G ranks of slice b have arrived on counter c: wave 0 polls
 // (lane k reads group k's counter when arrivals are counted per group of
 // kSubRanks ranks), the other waves wait at the barrier.  Bounded like
@@ -754,7 +765,7 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
   __shared__ unsigned done_sh;
   const bool has_slice = rk.group >= 0 && rk.group < a.BH;
   const bool count_late = has_slice && stats && a.do_kv && p.G > 1;
-  if (!has_slice && tid0 == 0) done_sh = bump(a.done_cnt);
+  if (!has_slice && tid0 == 0) done_sh = res_count_done(a);
 
   if (rk.group >= 0) {
     res_slot_table(reinterpret_cast<uint16_t*>(smem + L.tab), p, res_tile(p, rk.g));
@@ -813,7 +824,7 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
             qB[j][kb] = *reinterpret_cast<const bf16x8*>(Qb + tok * kD + 16 * kb + 8 * h);
         }
       }
-      if (!count_late && first && tid == 0) done_sh = bump(a.done_cnt);
+      if (!count_late && first && tid == 0) done_sh = res_count_done(a);
       wait_all();
       __syncthreads();
       res_stamp(a, first, kResStampStaged);
@@ -917,7 +928,7 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
           res_stamp(a, first, kResStampCWait);
           // The last counter access of the workgroup; with an output, the
           // count goes out with the fragments' DMA below.
-          if (b + a.S >= a.BH && !(fwd && global) && tid == 0) done_sh = bump(a.done_cnt);
+          if (b + a.S >= a.BH && !(fwd && global) && tid == 0) done_sh = res_count_done(a);
         } else {
           lds_barrier();  // the totals, in LDS; their global copies complete by the launch's end
         }
@@ -935,7 +946,7 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
             lds_barrier();
           } else {
             res_frags_dma(a, smem + L.scr, b, p.T >= 3 ? 2 : 1, tid);
-            if (count_late && b + a.S >= a.BH && tid == 0) done_sh = bump(a.done_cnt);
+            if (count_late && b + a.S >= a.BH && tid == 0) done_sh = res_count_done(a);
             wait_all();
             __syncthreads();
           }
@@ -1007,12 +1018,13 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
   if (rk.group >= 0) res_stamp(a, true, kResStampOut);
   __syncthreads();
   res_stamp(a, true, kResStampEnd);
-  if (done_sh == gridDim.x - 1) {
+  if (done_sh) {
     for (int i = tid0; i < a.BH * kCntWords; i += kResThreads)
       put(a.slice_cnt + (size_t)(i / kCntWords) * kCntStride + i % kCntWords, 0u);
     if (a.grouped)
       for (int i = tid0; i < a.BH * 3 * kMaxSubs; i += kResThreads) put(a.sub_cnt + (size_t)i * kCntStride, 0u);
     if (tid0 < kXcds) put(a.tickets + tid0, 0u);
+    if (tid0 < kXcds) put(a.done_xcd + (size_t)tid0 * kCntStride, 0u);
     if (a.clear_err && tid0 == 0) put(a.err, 0u);
     if (tid0 == 0) put(a.done_cnt, 0u);
   }
