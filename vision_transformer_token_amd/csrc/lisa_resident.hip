@@ -500,7 +500,9 @@ __device__ void res_combine(const ResArgs& a, unsigned char* smem, int b, int g,
           }
           w[j / 2] = pack_bf16x2(x2[0], x2[1]);
         }
-        unsigned char* frag = static_cast<unsigned char*>(beta >= 4 ? a.frag_m : a.frag_kv) + (size_t)b * kFragBytes;
+        unsigned char* frag =
+            pick(static_cast<unsigned char*>(a.frag_kv), static_cast<unsigned char*>(a.frag_m), beta >= 4) +
+            (size_t)b * kFragBytes;
         put16(frag + ((mb * 4 + q) * 64 + ln) * 16, make_uint4(w[0], w[1], w[2], w[3]));
       }
     }
@@ -681,11 +683,15 @@ __device__ void res_predict(const ResArgs& a, const unsigned char* cK, int slot,
 #pragma unroll
     for (int i = 0; i < 16; ++i) lg = mma(w2[i], fmaxf(c[i] + b1[i], 0.f), lg);
   }
-  float v[4], mx = -INFINITY;
+  float v[4], b2[4], mx = -INFINITY;
+  // b2 read unconditionally (a clamped index): a load under a branch is
+  // waited for inside it, one round trip per load.
+#pragma unroll
+  for (int e = 0; e < 4; ++e) b2[e] = a.mlp_b2[head * T + min(4 * h + e, T - 1)];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int k = 4 * h + e;
-    v[e] = k < T ? lg[e] + a.mlp_b2[head * T + k] : 0.f;
+    v[e] = k < T ? lg[e] + b2[e] : 0.f;
     if (k < T) mx = fmaxf(mx, v[e]);
   }
   mx = fmaxf(mx, __shfl_xor(mx, 32));
