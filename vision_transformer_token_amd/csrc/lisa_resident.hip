@@ -747,6 +747,10 @@ __device__ __forceinline__ void res_apply(const unsigned char* frag, const float
 // ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
+// One instantiation per mode (kResForward, kResReduce, kResApply) and
+// predictor use: each carries only the code its calls run, which keeps the
+// forward's code within the instruction cache a CU pair shares.
+template <int kMode, bool kMlp>
 __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
   extern __shared__ __align__(1024) unsigned char smem[];
   __shared__ float geo[kMaxT];  // geometric walk weights
@@ -760,8 +764,8 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
   res_stamp(a, true, kResStampStart);
   if (a.stamps && tid0 == 0)
     a.stamps[(size_t)blockIdx.x * kResPhases + kResPhases - 1] = ((unsigned long long)(unsigned)rk.group << 32) | (unsigned)rk.g;
-  const bool fwd = a.mode != kResReduce;  // local branch and output
-  const bool stats = a.mode != kResApply;  // sweeps and combine
+  constexpr bool fwd = kMode != kResReduce;  // local branch and output
+  constexpr bool stats = kMode != kResApply;  // sweeps and combine
 
   // The workgroup counts itself done (done_cnt) once it has made its last
   // counter access, not at its end: after its last slice's C wait when it
@@ -779,7 +783,7 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
     constexpr int kNB = kResMaxBlocks / kResWaves;
     const int nstat = a.do_m ? 2 * kD * kD : kD * kD;
     // One rank per slice, forward: the sweeps leave the statistics in place.
-    const bool direct = p.G == 1 && a.mode == kResForward;
+    const bool direct = p.G == 1 && kMode == kResForward;
 
     for (int b = rk.group; b < a.BH; b += a.S) {
       // The tile is the same for every slice, but what depends on it per lane
@@ -842,7 +846,7 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
       // The predicted walk weights of this wave's slots (each wave reads only
       // its own slots' weights; LDS accesses of a wave complete in order).
       float* wts = reinterpret_cast<float*>(smem + L.w);
-      if (fwd && a.mlp_w1f) {
+      if (fwd && kMlp) {
         const int head = __builtin_amdgcn_readfirstlane(b % a.heads);
 #pragma unroll
         for (int j = 0; j < kNB; ++j) {
@@ -1038,12 +1042,21 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
 
 }  // namespace
 
-hipError_t launch_resident(const ResArgs& a, int grid, hipStream_t s) {
+template <int kMode, bool kMlp>
+hipError_t launch_resident_typed(const ResArgs& a, int grid, hipStream_t s) {
   static std::atomic<bool> lds_set[kMaxDevices];
-  const hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(&resident_kernel), kResLdsMax, lds_set);
+  const hipError_t e =
+      ensure_lds_limit(reinterpret_cast<const void*>(&resident_kernel<kMode, kMlp>), kResLdsMax, lds_set);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(resident_kernel, dim3(grid), dim3(kResThreads), a.p.L.total, s, a);
+  hipLaunchKernelGGL((resident_kernel<kMode, kMlp>), dim3(grid), dim3(kResThreads), a.p.L.total, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_resident(const ResArgs& a, int grid, hipStream_t s) {
+  if (a.mode == kResReduce) return launch_resident_typed<kResReduce, false>(a, grid, s);
+  if (a.mode == kResApply) return launch_resident_typed<kResApply, false>(a, grid, s);
+  return a.mlp_w1f ? launch_resident_typed<kResForward, true>(a, grid, s)
+                   : launch_resident_typed<kResForward, false>(a, grid, s);
 }
 
 }  // namespace lisa
