@@ -328,8 +328,16 @@ __device__ void res_sweep_publish(const ResArgs& a, unsigned char* smem, int b, 
   // entry points that read it later; no partial, no arrival.
   const bool direct = a.p.G == 1 && a.mode == kResForward;
   if (!half) {
+    // Every read of the second half's products is in flight before the first
+    // add (left to itself the compiler sinks each read to its store, one LDS
+    // round trip per element).
+    float r[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] += red[(pw * 16 + i) * 64 + lane];
+    for (int i = 0; i < 16; ++i) r[i] = red[(pw * 16 + i) * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(r[i]));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] += r[i];
     float* dst = direct ? (kIsM ? a.fin_m : a.fin_kv) + (size_t)b * (kD * kD)
                         : a.part_kv + ((size_t)b * a.p.G + g) * (2 * kD * kD) + (kIsM ? kD * kD : 0);
     float* st = reinterpret_cast<float*>(smem + L.st) + (kIsM ? kD * kD : 0);
@@ -342,10 +350,15 @@ __device__ void res_sweep_publish(const ResArgs& a, unsigned char* smem, int b, 
     if (with_s && m == 0) {
       float* ps = direct ? a.fin_s + (size_t)b * kD : a.part_s + ((size_t)b * a.p.G + g) * kD;
       float* s_lds = reinterpret_cast<float*>(smem + L.s);
+      float rs[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) rs[i] = red[4 * 16 * 64 + (mb * 2 + h) * 16 + i];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(rs[i]));
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int e = 32 * mb + 8 * (i >> 2) + 4 * h + (i & 3);
-        const float v = acc_s[i] + red[4 * 16 * 64 + (mb * 2 + h) * 16 + i];
+        const float v = acc_s[i] + rs[i];
         put(ps + e, v);
         if (direct) s_lds[e] = v;
       }
@@ -386,11 +399,16 @@ __device__ void res_sum_s(const ResArgs& a, unsigned char* smem, int b, int tid)
   lds_barrier();
   if (tid < kD) {
     const int j = tid >> 2, c = tid & 3;
-    float v = 0.f;
+    float y[4 * kResWaves];
 #pragma unroll
     for (int w = 0; w < kResWaves; ++w)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) v += sw[4 * (w * 64 + 16 * q + j) + c];
+      for (int q = 0; q < 4; ++q) y[4 * w + q] = sw[4 * (w * 64 + 16 * q + j) + c];
+#pragma unroll
+    for (int i = 0; i < 4 * kResWaves; ++i) asm volatile("" : "+v"(y[i]));
+    float v = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4 * kResWaves; ++i) v += y[i];
     reinterpret_cast<float*>(smem + a.p.L.s)[tid] = v;
   }
   lds_barrier();
@@ -468,9 +486,16 @@ __device__ void res_combine(const ResArgs& a, unsigned char* smem, int b, int g,
     // read by this thread only) and the pieces are stored 16 bytes at a time.
     const bool whole = (E & 1023) == 0 && (e0 & 1023) == 0;
     for (int e = tid; e < E; e += kResThreads) {
+      // Eight partials' reads in flight at a time (G <= 16 here), added in
+      // partial order.
       float v = 0.f;
-#pragma unroll 4
-      for (int pp = 0; pp < G; ++pp) v += stg[pp * E + e];
+      for (int p0 = 0; p0 < G; p0 += 8) {
+        float x[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[k] = p0 + k < G ? stg[(p0 + k) * E + e] : 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v += x[k];
+      }
       if (whole) {
         const int f = e0 + e;
         put(pick(a.fin_kv, a.fin_m, f >= kD * kD) + (size_t)b * (kD * kD) + (f & (kD * kD - 1)), v);
@@ -713,7 +738,7 @@ __device__ void res_predict(const ResArgs& a, const unsigned char* cK, int slot,
 // layout.
 __device__ __forceinline__ void res_apply_bits(const unsigned char* frag, const v8s (&x)[4], float (&y)[32], int tid) {
   const int lane = tid & 63;
-  // The fragment reads stay next to their products: hoisted out of the
+  // The fragment reads stay inside each product: hoisted out of the
   // per-block and per-term loops, the 16 operands would hold 64 registers.
   frag = lds_launder(frag);
   f32x16 c0, c1;
@@ -722,13 +747,22 @@ __device__ __forceinline__ void res_apply_bits(const unsigned char* frag, const 
     c0[i] = y[i];
     c1[i] = y[16 + i];
   }
+  // All eight fragment reads in flight before the first product (one LDS
+  // round trip, not one per product).
+  v8s fa[2][4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) fa[mb][q] = *reinterpret_cast<const v8s*>(frag + ((mb * 4 + q) * 64 + lane) * 16);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) asm volatile("" : "+v"(fa[mb][q]));
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(frag + ((0 * 4 + q) * 64 + lane) * 16);
-    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(frag + ((1 * 4 + q) * 64 + lane) * 16);
     const bf16x8 bx = as_bf16(x[q]);
-    c0 = mma(a0, bx, c0);
-    c1 = mma(a1, bx, c1);
+    c0 = mma(as_bf16(fa[0][q]), bx, c0);
+    c1 = mma(as_bf16(fa[1][q]), bx, c1);
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -897,6 +931,15 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
           if (tid < kD) s_lds[tid] = get(a.fin_s + (size_t)b * kD + tid);
           __syncthreads();
         }
+        // This lane's half of s, read once for the wave's blocks, every read
+        // in flight before the first product.
+        float sv[32];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sv[8 * kb + e] = s_lds[16 * kb + 8 * h + e];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) asm volatile("" : "+v"(sv[i]));
 #pragma unroll
         for (int j = 0; j < kNB; ++j) {
           if (j < nown) {
@@ -906,7 +949,7 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
             for (int kb = 0; kb < 4; ++kb) {
               x[kb] = __builtin_elementwise_max(__builtin_bit_cast(v8s, qB[j][kb]), (v8s)0);
 #pragma unroll
-              for (int e = 0; e < 8; ++e) dot += bf2f((uint16_t)x[kb][e]) * s_lds[16 * kb + 8 * h + e];
+              for (int e = 0; e < 8; ++e) dot += bf2f((uint16_t)x[kb][e]) * sv[8 * kb + e];
             }
             dot += __shfl_xor(dot, 32);
             const float sc = valid[j] ? __builtin_amdgcn_rcpf(dot + a.eps) : 0.f;
