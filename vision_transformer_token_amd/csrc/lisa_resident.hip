@@ -490,11 +490,13 @@ __device__ void res_combine(const ResArgs& a, unsigned char* smem, int b, int g,
       // partial order.
       float v = 0.f;
       for (int p0 = 0; p0 < G; p0 += 8) {
-        float x[8];
+        float x[8];  // reads past the last partial repeat it and are not added
 #pragma unroll
-        for (int k = 0; k < 8; ++k) x[k] = p0 + k < G ? stg[(p0 + k) * E + e] : 0.f;
+        for (int k = 0; k < 8; ++k) x[k] = stg[min(p0 + k, G - 1) * E + e];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v += x[k];
+        for (int k = 0; k < 8; ++k) asm volatile("" : "+v"(x[k]));
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v += p0 + k < G ? x[k] : 0.f;
       }
       if (whole) {
         const int f = e0 + e;
@@ -538,23 +540,27 @@ __device__ void res_combine(const ResArgs& a, unsigned char* smem, int b, int g,
       // Eight reads in flight at a time (about 16 partials per group).
       float v = 0.f;
       for (int p0 = pg; p0 < G; p0 += 8 * ngrp) {
-        float x[8];
+        float x[8];  // reads past the last partial repeat it and are not added
 #pragma unroll
-        for (int k = 0; k < 8; ++k) x[k] = p0 + k * ngrp < G ? stg[(p0 + k * ngrp) * E + e] : 0.f;
+        for (int k = 0; k < 8; ++k) x[k] = stg[min(p0 + k * ngrp, G - 1) * E + e];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v += x[k];
+        for (int k = 0; k < 8; ++k) asm volatile("" : "+v"(x[k]));
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v += p0 + k * ngrp < G ? x[k] : 0.f;
       }
       sums[pg * E + e] = v;
     }
     lds_barrier();
     if (tid < E) {
       // ngrp <= kResThreads / 16 = 32 group sums, all read at once.
-      float x[kResThreads / 16];
+      float x[kResThreads / 16];  // reads past the last group repeat it and are not added
 #pragma unroll
-      for (int k = 0; k < kResThreads / 16; ++k) x[k] = k < ngrp ? sums[k * E + tid] : 0.f;
+      for (int k = 0; k < kResThreads / 16; ++k) x[k] = sums[min(k, ngrp - 1) * E + tid];
+#pragma unroll
+      for (int k = 0; k < kResThreads / 16; ++k) asm volatile("" : "+v"(x[k]));
       float v = 0.f;
 #pragma unroll
-      for (int k = 0; k < kResThreads / 16; ++k) v += x[k];
+      for (int k = 0; k < kResThreads / 16; ++k) v += k < ngrp ? x[k] : 0.f;
       res_combine_store(a, b, e0, tid, v);
     }
   }
@@ -582,18 +588,16 @@ __device__ void res_frags_from_rows(const float* st, unsigned char* frag, int ti
   for (int pc = tid; pc < 512; pc += kResThreads) {
     const int mb = pc >> 8, q = (pc >> 6) & 3, ln = pc & 63;
     const int c = 32 * mb + (ln & 31), h = ln >> 5;
-    uint32_t w[4];
+    float x[8];  // all eight reads in flight at once
 #pragma unroll
-    for (int j = 0; j < 8; j += 2) {
-      float x2[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int vs = 8 * q + j + t;
-        x2[t] = st[(32 * (vs >> 4) + 8 * ((vs >> 2) & 3) + 4 * h + (vs & 3)) * kD + c];
-      }
-      w[j / 2] = pack_bf16x2(x2[0], x2[1]);
+    for (int j = 0; j < 8; ++j) {
+      const int vs = 8 * q + j;
+      x[j] = st[(32 * (vs >> 4) + 8 * ((vs >> 2) & 3) + 4 * h + (vs & 3)) * kD + c];
     }
-    dst[pc] = make_uint4(w[0], w[1], w[2], w[3]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(x[j]));
+    dst[pc] = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                         pack_bf16x2(x[6], x[7]));
   }
 }
 
@@ -645,12 +649,22 @@ __device__ void res_local(const ResArgs& a, const unsigned char* smem, int blk, 
     Bp[v >> 3][v & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(pr[v], a.logit_scale, off));
   f32x16 la[2] = {}, lv[2] = {}, lden = {};
   const bf16x8 ones = as_bf16((v8s)(short)0x3f80);
+  // The window cells and one-hot operands of the four steps, read together.
+  int cAB[8];
+  v8s hbs[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    cAB[2 * kb] = win[16 * kb + 4 * (g >> 1) + (i16 >> 2)];
+    cAB[2 * kb + 1] = win[16 * kb + 8 + 4 * (g >> 1) + (i16 >> 2)];
+    hbs[kb] = __builtin_bit_cast(v8s, hot[kb * 64]);
+  }
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) asm volatile("" : "+v"(cAB[2 * kb]), "+v"(cAB[2 * kb + 1]), "+v"(hbs[kb]));
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     lden = mma(ones, Bp[kb], lden);
-    const int cA = win[16 * kb + 4 * (g >> 1) + (i16 >> 2)];
-    const int cB = win[16 * kb + 8 + 4 * (g >> 1) + (i16 >> 2)];
-    const bf16x8 hb = hot[kb * 64];
+    const int cA = cAB[2 * kb], cB = cAB[2 * kb + 1];
+    const bf16x8 hb = as_bf16(hbs[kb]);
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
       const int d = 32 * db + 16 * (g & 1) + 4 * (i16 & 3);
@@ -1016,13 +1030,20 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
           if (j < nown) {
             if (global) {
               const float* wrow = a.per_token ? wts + slot[j] * p.T : geo;
+              // The row and the weights w_1, w_2 read together (one LDS round
+              // trip for the block).
               v8s u1[4];
 #pragma unroll
-              for (int kb = 0; kb < 4; ++kb)
-                u1[kb] = relu_to_slots(*reinterpret_cast<const v8s*>(qt + row_off<BF16>(slot[j], 16 * kb + 8 * h)));
+              for (int kb = 0; kb < 4; ++kb) u1[kb] = *reinterpret_cast<const v8s*>(qt + row_off<BF16>(slot[j], 16 * kb + 8 * h));
+              float w12[2] = {wrow[1], p.T >= 3 ? wrow[2] : 0.f};
+#pragma unroll
+              for (int kb = 0; kb < 4; ++kb) asm volatile("" : "+v"(u1[kb]));
+              asm volatile("" : "+v"(w12[0]), "+v"(w12[1]));
+#pragma unroll
+              for (int kb = 0; kb < 4; ++kb) u1[kb] = relu_to_slots(u1[kb]);
               // alpha rides on the walk weights: z = sum_k (alpha w_k(i)) u_k.
               float z[32];
-              const float w1 = alpha * wrow[1];
+              const float w1 = alpha * w12[0];
 #pragma unroll
               for (int v = 0; v < 32; ++v) z[v] = w1 * bf2f((uint16_t)u1[v >> 3][v & 7]);
               if (p.T >= 3) {
@@ -1030,7 +1051,7 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
 #pragma unroll
                 for (int v = 0; v < 32; ++v) u[v] = 0.f;
                 res_apply_bits(fm, u1, u, tid);
-                const float w2 = alpha * wrow[2];
+                const float w2 = alpha * w12[1];
 #pragma unroll
                 for (int v = 0; v < 32; ++v) z[v] += w2 * u[v];
                 for (int k = 3; k < p.T; ++k) {
