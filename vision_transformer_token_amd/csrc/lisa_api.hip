@@ -247,15 +247,16 @@ bool resident_fits(const Plan& pl, int cus, bool mlp, lisa::ResPlan& rp, bool* d
   return 2 * gcap <= gmax && lisa::res_plan(pl.H, pl.W, pl.T, true, 2 * gcap, rp);
 }
 
-// The default between the two kernels where both apply: the resident one.
-// Measured on MI355X (256 CUs, bf16), forward of one call, resident against
-// streaming: PVT-T stage 1 (32 slices of 56 x 56, T = 3) 41.7 / 46.4 us;
-// DeiT-T at 224 (192 slices of 14 x 14, T = 3) 23.4 / 37.1 us; one 200 x 320
-// slice (T = 5) 44.4 / 50.5 us; one 128 x 128 slice 31.0 / 35.0 us; one
-// 256 x 256 slice 43.0 / 50.3 us.  Where the tiles fit only with twice the
-// ranks (two rounds of slices per group), the streaming kernel is the
-// faster: DeiT-T 384 57.8 against 60.7 us.
-bool resident_preferred(const lisa::ResPlan&, bool doubled) { return !doubled; }
+// The default between the two kernels where both apply: the resident one,
+// also where its tiles fit only with twice the ranks (two rounds of slices
+// per group).  Measured on MI355X (256 CUs, bf16), forward of one call,
+// resident against streaming: PVT-T stage 1 (32 slices of 56 x 56, T = 3)
+// 38.1 / 45.6 us; DeiT-T at 224 (192 slices of 14 x 14, T = 3) 20.3 / 37.1
+// us; DeiT-T at 384 (192 slices of 24 x 24, twice the ranks) 55.4 / 57.8 us;
+// one 200 x 320 slice (T = 5) 36.0 / 46.6 us; one 128 x 128 slice 25.5 /
+// 34.0 us; one 256 x 256 slice 34.0 / 46.8 us; one 64 x 64 slice 24.0 /
+// 27.2 us.
+bool resident_preferred(const lisa::ResPlan&, bool) { return true; }
 
 // Whether the resident kernel runs the problem: where it fits, when asked
 // for, and by default where it is the faster of the two kernels.
