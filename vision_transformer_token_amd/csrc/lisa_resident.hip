@@ -297,8 +297,10 @@ __device__ __forceinline__ void res_sweep(const unsigned char* smem, const ResLa
 // leaves its products in the scratch area and the first adds them (first
 // half + second half) and stores the block.  s comes from the waves of the
 // first column block.
+// arrive = false: the caller counts the arrival later (res_arrive), once it
+// has other work done (the stores have then long completed).
 template <bool kIsM>
-__device__ void res_sweep_publish(const ResArgs& a, unsigned char* smem, int b, int g, int tid) {
+__device__ void res_sweep_publish(const ResArgs& a, unsigned char* smem, int b, int g, int tid, bool arrive = true) {
   const ResLayout& L = a.p.L;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, m = lane & 31, h = lane >> 5;
   const int pw = wave & 3, half = wave >> 2;
@@ -366,7 +368,7 @@ __device__ void res_sweep_publish(const ResArgs& a, unsigned char* smem, int b, 
   }
   if (direct)
     lds_barrier();
-  else
+  else if (arrive)
     res_arrive(a, b, g, kIsM ? kRcM : kRcKV);
 }
 
@@ -888,7 +890,14 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
       res_stamp(a, first, kResStampStaged);
 
       // KV sweep: partials of s and phi(K)^T V.
-      if (stats && a.do_kv) res_sweep_publish<false>(a, smem, b, rk.g, tid);
+      // With a local branch to run and arrivals on one counter per slice,
+      // the KV partial's arrival is counted after it: the publication then
+      // does not wait for its stores to complete before the local branch, and
+      // the arrival costs no wait (PVT-T stage 1 37.1 -> 36.8 us).  With
+      // arrivals counted per group (64 ranks and more, one sequence) the later
+      // arrivals cost more than the wait (200 x 320: 36.3 -> 37.7 us).
+      const bool defer_kv = fwd && p.G > 1 && !a.grouped;
+      if (stats && a.do_kv) res_sweep_publish<false>(a, smem, b, rk.g, tid, !defer_kv);
       res_stamp(a, first, kResStampKV);
 
       // The predicted walk weights of this wave's slots (each wave reads only
@@ -919,6 +928,7 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
           }
         }
       }
+      if (stats && a.do_kv && defer_kv) res_arrive(a, b, rk.g, kRcKV);
 
       // s, then the rows Qt_i = r_i phi(Q_i) of this wave's slots over the V
       // cells (the local branch is done: the wait closed with a workgroup
