@@ -340,14 +340,25 @@ __device__ void res_sweep_publish(const ResArgs& a, unsigned char* smem, int b, 
     for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(r[i]));
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] += r[i];
-    float* dst = direct ? (kIsM ? a.fin_m : a.fin_kv) + (size_t)b * (kD * kD)
-                        : a.part_kv + ((size_t)b * a.p.G + g) * (2 * kD * kD) + (kIsM ? kD * kD : 0);
-    float* st = reinterpret_cast<float*>(smem + L.st) + (kIsM ? kD * kD : 0);
+    if (direct) {
+      float* dst = (kIsM ? a.fin_m : a.fin_kv) + (size_t)b * (kD * kD);
+      float* st = reinterpret_cast<float*>(smem + L.st) + (kIsM ? kD * kD : 0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int e = (32 * mb + 8 * (i >> 2) + 4 * h + (i & 3)) * kD + 32 * nb + m;
-      put(dst + e, acc[i]);
-      if (direct) st[e] = acc[i];
+      for (int i = 0; i < 16; ++i) {
+        const int e = (32 * mb + 8 * (i >> 2) + 4 * h + (i & 3)) * kD + 32 * nb + m;
+        put(dst + e, acc[i]);
+        st[e] = acc[i];
+      }
+    } else {
+      // The partial in accumulator order (res_part_index): this lane's four
+      // consecutive elements of each row quartet are 16 contiguous bytes, and
+      // a wave's stores cover whole 1 KB runs (4 stores per lane, not 16).
+      float* dst = a.part_kv + ((size_t)b * a.p.G + g) * (2 * kD * kD) + (kIsM ? kD * kD : 0) +
+                   (size_t)(mb * 2 + nb) * 1024 + lane * 4;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        put16(dst + t * 256, make_uint4(__float_as_uint(acc[4 * t]), __float_as_uint(acc[4 * t + 1]),
+                                        __float_as_uint(acc[4 * t + 2]), __float_as_uint(acc[4 * t + 3])));
     }
     if (with_s && m == 0) {
       float* ps = direct ? a.fin_s + (size_t)b * kD : a.part_s + ((size_t)b * a.p.G + g) * kD;
@@ -357,12 +368,18 @@ __device__ void res_sweep_publish(const ResArgs& a, unsigned char* smem, int b, 
       for (int i = 0; i < 16; ++i) rs[i] = red[4 * 16 * 64 + (mb * 2 + h) * 16 + i];
 #pragma unroll
       for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(rs[i]));
+      float v[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int e = 32 * mb + 8 * (i >> 2) + 4 * h + (i & 3);
-        const float v = acc_s[i] + rs[i];
-        put(ps + e, v);
-        if (direct) s_lds[e] = v;
+      for (int i = 0; i < 16; ++i) v[i] = acc_s[i] + rs[i];
+      // Elements 32 mb + 8 t + 4 h + (0..3): four consecutive floats per t.
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int e = 32 * mb + 8 * t + 4 * h;
+        put16(ps + e, make_uint4(__float_as_uint(v[4 * t]), __float_as_uint(v[4 * t + 1]),
+                                 __float_as_uint(v[4 * t + 2]), __float_as_uint(v[4 * t + 3])));
+        if (direct)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) s_lds[e + u] = v[4 * t + u];
       }
     }
   }
@@ -427,15 +444,25 @@ __device__ __forceinline__ void res_store_frag(uint16_t* frag, int e, float v) {
   __hip_atomic_store(frag + idx, f2bf(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The rank partials of phi(K)^T V and M hold each 64 x 64 matrix in the
+// sweeps' accumulator order: element (r, c), r = 32 mb + 8 t + 4 h + u,
+// c = 32 nb + m, at ((2 mb + nb) 4 + t) 256 + (32 h + m) 4 + u.  The row-major
+// index of partial element p:
+__device__ __forceinline__ int res_part_row_major(int p) {
+  const int blk = p >> 10, t = (p >> 8) & 3, ln = (p >> 2) & 63, u = p & 3;
+  return (32 * (blk >> 1) + 8 * t + 4 * (ln >> 5) + u) * kD + 32 * (blk & 1) + (ln & 31);
+}
+
 // One element's total of the combine: the statistics as fp32 rows (which the
 // backward and the entry points reading the statistics take) and in their
 // bf16 fragment slot (which every rank's output loads).
 __device__ __forceinline__ void res_combine_store(const ResArgs& a, int b, int e0, int e, float v) {
   const int f = e0 + e;
   const bool m = f >= kD * kD;
-  put(pick(a.fin_kv, a.fin_m, m) + (size_t)b * (kD * kD) + (f & (kD * kD - 1)), v);
+  const int x = res_part_row_major(f & (kD * kD - 1));
+  put(pick(a.fin_kv, a.fin_m, m) + (size_t)b * (kD * kD) + x, v);
   res_store_frag(pick(static_cast<uint16_t*>(a.frag_kv), static_cast<uint16_t*>(a.frag_m), m) + (size_t)b * (kD * kD),
-                 f & (kD * kD - 1), v);
+                 x, v);
 }
 
 // Rank g's share of the slice statistics: elements [e0, e1) of the flattened
@@ -483,9 +510,11 @@ __device__ void res_combine(const ResArgs& a, unsigned char* smem, int b, int g,
   // partials of its elements in turn.  Either way the order of additions
   // depends on G alone.
   if (2 * E > kResThreads) {
-    // A share of whole 16-row blocks (G <= 8) holds whole fragment pieces:
+    // A share of whole 32 x 32 blocks (G <= 8; the partials are in
+    // accumulator order) holds whole fragment pieces and whole row segments:
     // the totals go back into the staging (element e's first partial slot,
-    // read by this thread only) and the pieces are stored 16 bytes at a time.
+    // read by this thread only), then the pieces and the fp32 rows are
+    // stored 16 bytes at a time.
     const bool whole = (E & 1023) == 0 && (e0 & 1023) == 0;
     for (int e = tid; e < E; e += kResThreads) {
       // Eight partials' reads in flight at a time (G <= 16 here), added in
@@ -501,8 +530,6 @@ __device__ void res_combine(const ResArgs& a, unsigned char* smem, int b, int g,
         for (int k = 0; k < 8; ++k) v += p0 + k < G ? x[k] : 0.f;
       }
       if (whole) {
-        const int f = e0 + e;
-        put(pick(a.fin_kv, a.fin_m, f >= kD * kD) + (size_t)b * (kD * kD) + (f & (kD * kD - 1)), v);
         stg[e] = v;
       } else {
         res_combine_store(a, b, e0, e, v);
@@ -510,29 +537,36 @@ __device__ void res_combine(const ResArgs& a, unsigned char* smem, int b, int g,
     }
     if (whole) {
       lds_barrier();
-      // Piece (block beta, mb, lane) of the share: rows [16 beta, 16 beta + 16)
-      // of the flattened [phi(K)^T V | M] form fragment step q = beta % 4 of
-      // matrix beta / 4; element j holds row dimof(8 q + j, lane / 32), column
-      // 32 mb + lane % 32.
-      for (int pc = tid; pc < E / 8; pc += kResThreads) {
-        const int beta = e0 / 1024 + pc / 128, mb = (pc >> 6) & 1, ln = pc & 63, q = beta & 3;
-        const int c = 32 * mb + (ln & 31), hh = ln >> 5;
-        uint32_t w[4];
-#pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          float x2[2];
-#pragma unroll
-          for (int t2 = 0; t2 < 2; ++t2) {
-            const int vs = 8 * q + j + t2;
-            const int row = 32 * (vs >> 4) + 8 * ((vs >> 2) & 3) + 4 * hh + (vs & 3);  // in [16 q, 16 q + 16)
-            x2[t2] = stg[4096 * (beta >> 2) + 64 * row + c - e0];
-          }
-          w[j / 2] = pack_bf16x2(x2[0], x2[1]);
-        }
+      // Block lb of the share is the 32 x 32 block (mb, nb) = (blk / 2,
+      // blk % 2), blk = beta % 4, of matrix beta / 4 (beta = e0 / 1024 + lb):
+      // its totals sit at stg[1024 lb + 256 t + 4 lane + u] (row 32 mb + 8 t
+      // + 4 (lane / 32) + u, column 32 nb + lane % 32).
+      const int nbk = E / 1024;
+      // Fragment pieces: the block holds steps q = 2 mb, 2 mb + 1 of fragment
+      // half nb; piece (nb, q, lane) element j is row dimof(8 q + j, lane /
+      // 32), i.e. t = 2 (q % 2) + j / 4, u = j % 4: two float4 of the staging.
+      for (int pc = tid; pc < nbk * 128; pc += kResThreads) {
+        const int lb = pc >> 7, beta = e0 / 1024 + lb, blk = beta & 3, qq = (pc >> 6) & 1, ln = pc & 63;
+        const int q = 2 * (blk >> 1) + qq;
+        const float4 lo = *reinterpret_cast<const float4*>(stg + 1024 * lb + 256 * (2 * qq) + 4 * ln);
+        const float4 hi = *reinterpret_cast<const float4*>(stg + 1024 * lb + 256 * (2 * qq + 1) + 4 * ln);
         unsigned char* frag =
             pick(static_cast<unsigned char*>(a.frag_kv), static_cast<unsigned char*>(a.frag_m), beta >= 4) +
             (size_t)b * kFragBytes;
-        put16(frag + ((mb * 4 + q) * 64 + ln) * 16, make_uint4(w[0], w[1], w[2], w[3]));
+        put16(frag + (((blk & 1) * 4 + q) * 64 + ln) * 16,
+              make_uint4(pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w), pack_bf16x2(hi.x, hi.y),
+                         pack_bf16x2(hi.z, hi.w)));
+      }
+      // fp32 rows: row segment (rr, four columns from 4 cq) of the block.
+      for (int sg = tid; sg < nbk * 256; sg += kResThreads) {
+        const int lb = sg >> 8, beta = e0 / 1024 + lb, blk = beta & 3, rr = (sg >> 3) & 31, cq = sg & 7;
+        const int t = rr >> 3, hh = (rr >> 2) & 1, u = rr & 3;
+        float x[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[k] = stg[1024 * lb + 256 * t + 4 * (32 * hh + 4 * cq + k) + u];
+        float* fin = pick(a.fin_kv, a.fin_m, beta >= 4) + (size_t)b * (kD * kD);
+        put16(fin + (32 * (blk >> 1) + rr) * kD + 32 * (blk & 1) + 4 * cq,
+              make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])));
       }
     }
   } else {
