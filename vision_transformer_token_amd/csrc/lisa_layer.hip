@@ -148,12 +148,15 @@ __global__ __launch_bounds__(256) void proj_gemm(ProjArgs a) {
           o0[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
           o1[e] = pack_bf16x2(v[8 + 2 * e], v[8 + 2 * e + 1]);
         }
-        reinterpret_cast<u32x4*>(dst)[0] = o0;
-        reinterpret_cast<u32x4*>(dst)[1] = o1;
+        // Streaming stores (nontemporal): the outputs are not read again by
+        // this kernel (QKV 20.0 -> ~17 us at PVT-T stage 1).
+        __builtin_nontemporal_store(o0, reinterpret_cast<u32x4*>(dst));
+        __builtin_nontemporal_store(o1, reinterpret_cast<u32x4*>(dst) + 1);
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          reinterpret_cast<float4*>(dst)[j] = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
+          __builtin_nontemporal_store(f32x4{v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]},
+                                      reinterpret_cast<f32x4*>(dst) + j);
       }
     }
   }
