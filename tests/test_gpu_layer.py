@@ -83,6 +83,11 @@ CASES = [
     ("one-token", 3, 1, 1, 1, 3, "fp32", "adaptive"),
     ("ragged-bf16", 2, 3, 13, 21, 3, "bf16", "adaptive"),
     ("t1-bf16", 1, 2, 7, 6, 1, "bf16", "adaptive"),
+    # One head (64 channels), bf16: the streaming QKV projection, on a ragged
+    # last row tile and on more 64-row tiles than its grid (each workgroup
+    # walks several).
+    ("one-head-bf16", 3, 1, 9, 11, 3, "bf16", "adaptive"),
+    ("one-head-long-bf16", 2, 1, 150, 171, 3, "bf16", "geometric"),
 ]
 
 
