@@ -64,16 +64,19 @@ template <class S>
 struct Piece;
 template <>
 struct Piece<uint16_t> {
-  uint4 w[2];
+  u32x4 w[2];
   __device__ __forceinline__ void load(const uint16_t* row, int f0) {
-    w[0] = *reinterpret_cast<const uint4*>(row + f0);
-    w[1] = *reinterpret_cast<const uint4*>(row + f0 + 8);
+    w[0] = *reinterpret_cast<const u32x4*>(row + f0);
+    w[1] = *reinterpret_cast<const u32x4*>(row + f0 + 8);
   }
   __device__ __forceinline__ float operator[](int e) const {  // e: a compile-time constant after unrolling
-    const uint4& v = w[e >> 3];
-    const uint32_t x = (e & 6) == 0 ? v.x : (e & 6) == 2 ? v.y : (e & 6) == 4 ? v.z : v.w;
+    const uint32_t x = w[e >> 3][(e & 7) >> 1];
     return __uint_as_float((e & 1) ? (x & 0xffff0000u) : (x << 16));
   }
+  // The loaded value is needed here: pieces loaded before and pinned
+  // together are waited for together (otherwise the compiler may reuse one
+  // register tuple and wait for each load before issuing the next).
+  __device__ __forceinline__ void pin() { asm volatile("" : "+v"(w[0]), "+v"(w[1])); }
 };
 template <>
 struct Piece<float> {
@@ -86,7 +89,28 @@ struct Piece<float> {
     const float4& v = w[e >> 2];
     return (e & 3) == 0 ? v.x : (e & 3) == 1 ? v.y : (e & 3) == 2 ? v.z : v.w;
   }
+  __device__ __forceinline__ void pin() {}
 };
+
+// This lane's part of a . b over its 16 features.  bf16 rows: v_dot2 on the
+// packed pairs (the products of two bf16 values are exact in fp32; fp32
+// sums, pair by pair); fp32 rows: fused multiply-adds in feature order.
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dotp(const Piece<uint16_t>& a, const Piece<uint16_t>& b) {
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t x = a.w[j >> 2][j & 3], y = b.w[j >> 2][j & 3];
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, x), __builtin_bit_cast(bf16x2v, y), acc, false);
+  }
+  return acc;
+}
+__device__ __forceinline__ float dotp(const Piece<float>& a, const Piece<float>& b) {
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < kF; ++e) acc += a[e] * b[e];
+  return acc;
+}
 
 // Sum over the lane quad of a token (every lane of the quad gets it).
 __device__ __forceinline__ float quad_sum(float x) { return dpp_add(dpp_add(x, 0xB1), 0x4E); }
@@ -396,8 +420,14 @@ __global__ __launch_bounds__(kTT) void bwd_token_a(BwdArgs a) {
   float q[kF], dy[kF];
   float m = 0.f, Z = 1.f, dyL = 0.f, dyv = 0.f;
   if (on) {
-    load16(Qb + (size_t)i * kD, f0, q);
-    load16(dYb + (size_t)i * kD, f0, dy);
+    Piece<S> qp, dyp;  // raw Q_i and dY_i as loaded, for the window's dot products
+    qp.load(Qb + (size_t)i * kD, f0);
+    dyp.load(dYb + (size_t)i * kD, f0);
+#pragma unroll
+    for (int e = 0; e < kF; ++e) {
+      q[e] = qp[e];
+      dy[e] = dyp[e];
+    }
     // Local branch at token i: window logits, their max and sum, dY . L_i.
     const int row = i / a.W, col = i % a.W;
     // The window's rows three at a time (one grid row of it), loaded without
@@ -414,11 +444,10 @@ __global__ __launch_bounds__(kTT) void bwd_token_a(BwdArgs a) {
 #pragma unroll
       for (int u = 0; u < 3; ++u) y[u].load(Kb + (size_t)(cw[g0 + u] >= 0 ? cw[g0 + u] : i) * kD, f0);
 #pragma unroll
-      for (int u = 0; u < 3; ++u) {
-        float acc = 0.f;
+      for (int u = 0; u < 3; ++u) y[u].pin();
 #pragma unroll
-        for (int e = 0; e < kF; ++e) acc += q[e] * y[u][e];
-        const float d = quad_sum(acc);
+      for (int u = 0; u < 3; ++u) {
+        const float d = quad_sum(dotp(qp, y[u]));
         z[g0 + u] = cw[g0 + u] >= 0 ? d * kRs : -INFINITY;
         m = fmaxf(m, z[g0 + u]);
       }
@@ -430,11 +459,10 @@ __global__ __launch_bounds__(kTT) void bwd_token_a(BwdArgs a) {
 #pragma unroll
       for (int u = 0; u < 3; ++u) y[u].load(Vb + (size_t)(cw[g0 + u] >= 0 ? cw[g0 + u] : i) * kD, f0);
 #pragma unroll
-      for (int u = 0; u < 3; ++u) {
-        float acc = 0.f;
+      for (int u = 0; u < 3; ++u) y[u].pin();
 #pragma unroll
-        for (int e = 0; e < kF; ++e) acc += dy[e] * y[u][e];
-        const float d = quad_sum(acc);
+      for (int u = 0; u < 3; ++u) {
+        const float d = quad_sum(dotp(dyp, y[u]));
         if (cw[g0 + u] >= 0) {
           const float e = __expf(z[g0 + u] - m);
           Z += e;
@@ -443,7 +471,9 @@ __global__ __launch_bounds__(kTT) void bwd_token_a(BwdArgs a) {
       }
     }
     dyL /= Z;
-    dyv = dot64(Vb + (size_t)i * kD, f0, dy);
+    Piece<S> vi;
+    vi.load(Vb + (size_t)i * kD, f0);
+    dyv = quad_sum(dotp(dyp, vi));
   } else {
 #pragma unroll
     for (int e = 0; e < kF; ++e) q[e] = dy[e] = 0.f;
@@ -842,8 +872,12 @@ __global__ __launch_bounds__(kTT) void bwd_token_q(BwdArgs a) {
   acc_to_quad<S>(acc, wrows, tw, f0, dqt);
   if (!on) return;  // no barrier follows
   const float4 tp = a.tok[base + i];  // m_i, Z_i, c_i, dz_i
+  Piece<S> qp, dyp;  // raw Q_i and dY_i as loaded, for the window's dot products
+  qp.load(Qb + (size_t)i * kD, f0);
+  dyp.load(dYb + (size_t)i * kD, f0);
   float q[kF];
-  load16(Qb + (size_t)i * kD, f0, q);
+#pragma unroll
+  for (int e = 0; e < kF; ++e) q[e] = qp[e];
   float den = 0.f;
 #pragma unroll
   for (int e = 0; e < kF; ++e) den += fmaxf(q[e], 0.f) * s_sh[f0 + e];
@@ -856,13 +890,13 @@ __global__ __launch_bounds__(kTT) void bwd_token_q(BwdArgs a) {
   for (int j = 0; j < 9; ++j) {
     const int c = window_cell(a, row, col, j);
     if (c < 0) continue;
-    float kc[kF];
-    load16(Kb + (size_t)c * kD, f0, kc);
-    float zq = 0.f;
-#pragma unroll
-    for (int e = 0; e < kF; ++e) zq += kc[e] * q[e];
-    const float p = __expf(quad_sum(zq) * kRs - tp.x) / tp.y;
-    const float g = p * ((1.f - alpha) * dot64(Vb + (size_t)c * kD, f0, x) - tp.z) * kRs;
+    Piece<S> kc, vc;
+    kc.load(Kb + (size_t)c * kD, f0);
+    vc.load(Vb + (size_t)c * kD, f0);
+    kc.pin();
+    vc.pin();
+    const float p = __expf(quad_sum(dotp(kc, qp)) * kRs - tp.x) / tp.y;
+    const float g = p * ((1.f - alpha) * quad_sum(dotp(vc, dyp)) - tp.z) * kRs;
 #pragma unroll
     for (int e = 0; e < kF; ++e) dqt[e] += g * kc[e];
   }
