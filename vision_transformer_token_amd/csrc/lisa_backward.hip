@@ -193,12 +193,11 @@ __device__ __forceinline__ void put_row(unsigned char* rows, int tk, int f0, con
   }
 }
 
-// Whole workgroup: stage the 64 x 64 fp32 matrix src for Y = X src^T
-// (kTr) or Y = X src (!kTr).
+// Stage elements e .. e + 3 (one row) of a 64 x 64 fp32 matrix, v4, for
+// Y = X M^T (kTr) or Y = X M (!kTr).
 template <class S, bool kTr>
-__device__ __forceinline__ void stage_mat(unsigned char* dst, const float* src) {
-  for (int e = threadIdx.x * 4; e < kD * kD; e += blockDim.x * 4) {
-    const float4 v4 = *reinterpret_cast<const float4*>(src + e);
+__device__ __forceinline__ void stage_quad(unsigned char* dst, float4 v4, int e) {
+  {
     const float v[4] = {v4.x, v4.y, v4.z, v4.w};
     const int r = e / kD, c = e % kD;
 #pragma unroll
@@ -213,6 +212,13 @@ __device__ __forceinline__ void stage_mat(unsigned char* dst, const float* src) 
       }
     }
   }
+}
+// Whole workgroup: stage the 64 x 64 fp32 matrix src for Y = X src^T
+// (kTr) or Y = X src (!kTr).
+template <class S, bool kTr>
+__device__ __forceinline__ void stage_mat(unsigned char* dst, const float* src) {
+  for (int e = threadIdx.x * 4; e < kD * kD; e += blockDim.x * 4)
+    stage_quad<S, kTr>(dst, *reinterpret_cast<const float4*>(src + e), e);
 }
 
 __device__ __forceinline__ f32x4 mfma16_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -410,6 +416,9 @@ __global__ __launch_bounds__(kTT) void bwd_token_a(BwdArgs a) {
   const S* Vb = static_cast<const S*>(a.V) + base * kD;
   const S* dYb = static_cast<const S*>(a.dY) + base * kD;
   if (t < kD) s_sh[t] = a.fin_s[(size_t)b * kD + t];
+  // bf16: this thread's float4 of P_1, loaded before the window gather.
+  float4 pnext = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (!kF32 && a.T >= 2) pnext = *reinterpret_cast<const float4*>(a.pk + (size_t)b * (a.T - 1) * kD * kD + 4 * t);
   float wk[kMaxTBwd];
 #pragma unroll
   for (int k = 0; k < kMaxTBwd; ++k) wk[k] = (on && k < a.T) ? wgt(a, base + i, k) : 0.f;
@@ -571,11 +580,14 @@ __global__ __launch_bounds__(kTT) void bwd_token_a(BwdArgs a) {
       for (int e = 0; e < 4; ++e) dyd[ct][e] = bf2f(dyT[(16 * ct + li) * kTS + 16 * wv + 4 * lk + e]);
     const uint16_t* Ph = reinterpret_cast<const uint16_t*>(Pst);
     const uint16_t* Pl = Ph + kD * kRB;
+    static_assert(kTT * 4 == kD * kD, "one float4 of each P_k per thread");
 #pragma unroll
     for (int k = 1; k < kMaxTBwd; ++k) {
       if (k > T1) break;
       __syncthreads();
-      stage_mat<S, false>(Pst, a.pk + ((size_t)b * T1 + (k - 1)) * kD * kD);
+      stage_quad<S, false>(Pst, pnext, 4 * t);
+      // The next term's matrix, in flight over this term's products.
+      if (k < T1) pnext = *reinterpret_cast<const float4*>(a.pk + ((size_t)b * T1 + k) * kD * kD + 4 * t);
       {
         // alpha w_k r phi(Q), split: feature t / 16, tokens 16 (t % 16) .. + 15.
         const int fa = t / 16, t0 = 16 * (t % 16);
@@ -834,6 +846,10 @@ __global__ __launch_bounds__(kTT) void bwd_token_q(BwdArgs a) {
   const S* dYb = static_cast<const S*>(a.dY) + base * kD;
   stage_mat<S, false>(dMs, a.dmkv + (size_t)b * 2 * kD * kD);
   if (t < kD) s_sh[t] = a.fin_s[(size_t)b * kD + t];
+  // This thread's float4 of P_1 (one float4 of each P_k per thread).
+  static_assert(kTT * 4 == kD * kD, "one float4 of each P_k per thread");
+  float4 pnext = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (a.T >= 2) pnext = *reinterpret_cast<const float4*>(a.pk + (size_t)b * (a.T - 1) * kD * kD + 4 * t);
   float x[kF];
   if (on) load16(Kb + (size_t)i * kD, f0, x);
   else
@@ -857,7 +873,9 @@ __global__ __launch_bounds__(kTT) void bwd_token_q(BwdArgs a) {
   const int ib = blk * kBT + (t / 64) * 16 + 4 * ((t % 64) / 16);
   for (int k = 1; k <= T1; ++k) {
     __syncthreads();
-    stage_mat<S, true>(Ps, a.pk + ((size_t)b * T1 + (k - 1)) * kD * kD);
+    stage_quad<S, true>(Ps, pnext, 4 * t);
+    // The next term's matrix, in flight over this term's products.
+    if (k < T1) pnext = *reinterpret_cast<const float4*>(a.pk + ((size_t)b * T1 + k) * kD * kD + 4 * t);
     __syncthreads();
     f32x4 y[4] = {};
     wave_mm<S>(wrows, Ps, y);
