@@ -40,7 +40,10 @@ KERNEL_SOURCES_BY_NAME = {
                              "lisa_api.hip"),
 }
 KERNEL_SOURCES = KERNEL_SOURCES_BY_NAME["flow_kernel<bf16>"]
-BACKWARD_SOURCES = KERNEL_SOURCES + _csrc("lisa_backward.hip")
+# The backward starts with the resident kernel's statistics launch; the layer
+# runs the projections around the resident kernel.
+BACKWARD_SOURCES = KERNEL_SOURCES_BY_NAME["resident_kernel"] + _csrc("lisa_backward.hip")
+LAYER_SOURCES = KERNEL_SOURCES_BY_NAME["resident_kernel"] + _csrc("lisa_layer.hip")
 
 
 def kernel_source_hash(sources=None):
@@ -128,6 +131,8 @@ def _short(name):
         return "mlp_prep<bf16>" if "BF16" in name else "mlp_prep<fp32>"
     if "copyBuffer" in name:
         return "copyBuffer"
+    if "proj_stream_qkv" in name:
+        return "proj_stream_qkv<bf16>"
     m = re.search(r"proj_gemm<(unsigned short|float), (true|false)>", name)
     if m:
         return f"proj_gemm<{'bf16' if m.group(1) == 'unsigned short' else 'fp32'}, " \
@@ -327,7 +332,7 @@ def summarize_backward(outdir, workload, command):
                   f"(the forward kernel, {' or '.join(KERNEL_SOURCES_BY_NAME)}, is the statistics launch the backward starts with)",
               f"algorithmic bytes per call: {w.token_heads * bb / 1e6:.2f} MB ({bb} B per token-head); "
               f"at 8 TB/s: {w.token_heads * bb / 8e12 * 1e6:.1f} us",
-              f"kernel source hash (forward and backward sources): {kernel_source_hash(BACKWARD_SOURCES)}"]
+              f"kernel source hash (statistics launch and backward sources): {kernel_source_hash(BACKWARD_SOURCES)}"]
     with open(os.path.join(ROOT, "profiles", f"lisa_backward_{w.name}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -354,7 +359,7 @@ def summarize_layer(outdir, workload, command):
     total_ns = 0.0
     for r in stats:
         name = _short(r["Name"])
-        if not (name in KERNEL_SOURCES_BY_NAME or name.startswith("proj_gemm")):
+        if not (name in KERNEL_SOURCES_BY_NAME or name.startswith("proj_")):
             continue
         total_ns += float(r["AverageNs"])
         lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} | "
@@ -364,7 +369,7 @@ def summarize_layer(outdir, workload, command):
     lines += ["", f"sum of the kernels' averages per call: {total_ns / 1e3:.1f} us",
               f"algorithmic bytes per call: {tok * bb / 1e6:.2f} MB ({bb} B per token: X read, Y written, "
               f"weights); at 8 TB/s: {tok * bb / 8e12 * 1e6:.1f} us",
-              f"kernel source hash: {kernel_source_hash()}"]
+              f"kernel source hash (operator and projection sources): {kernel_source_hash(LAYER_SOURCES)}"]
     with open(os.path.join(ROOT, "profiles", f"lisa_attention_forward_{w.name}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -391,7 +396,7 @@ def summarize_mlp(outdir, workload, command):
                   f"(mlp_prep lays W1 out for the kernel's lanes)",
               f"algorithmic bytes per call: {w.token_heads * bb / 1e6:.2f} MB ({bb} B per token-head: "
               f"no weight tensor); at 8 TB/s: {w.token_heads * bb / 8e12 * 1e6:.1f} us",
-              f"kernel source hash: {kernel_source_hash()}"]
+              f"kernel source hash (operator sources): {kernel_source_hash(KERNEL_SOURCES_BY_NAME['resident_kernel'])}"]
     with open(os.path.join(ROOT, "profiles", f"lisa_forward_mlp_{w.name}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
