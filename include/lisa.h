@@ -296,6 +296,9 @@ lisa_status lisa_forward_mlp(const lisa_problem* p, const void* Q, const void* K
  * Q, K, V and O live in the workspace (lisa_attention_workspace_size bytes,
  * 256-byte aligned, zero-filled before its first use), in the problem's
  * dtype: with bf16 inputs each is rounded once, as between separate layers.
+ * With one head in bf16 (where lisa_forward takes the resident kernel) the
+ * output projection is applied in the operator's output stage instead: O is
+ * rounded to bf16 as the product's operand, the same values as stored.
  * The projections run on MFMA with fp32 sums.  Errors as for lisa_forward;
  * X, Y and the weights need 16-byte alignment, the biases 4. */
 size_t lisa_attention_workspace_size(const lisa_problem* p);

@@ -85,9 +85,13 @@ CASES = [
     ("t1-bf16", 1, 2, 7, 6, 1, "bf16", "adaptive"),
     # One head (64 channels), bf16: the streaming QKV projection, on a ragged
     # last row tile and on more 64-row tiles than its grid (each workgroup
-    # walks several).
+    # walks several), and the output projection folded into the operator's
+    # output stage: one rank per slice, many ranks per slice (grouped
+    # arrivals), no global branch (T = 1), more walk terms (T = 5).
     ("one-head-bf16", 3, 1, 9, 11, 3, "bf16", "adaptive"),
     ("one-head-long-bf16", 2, 1, 150, 171, 3, "bf16", "geometric"),
+    ("one-head-t1-bf16", 2, 1, 7, 6, 1, "bf16", "adaptive"),
+    ("one-head-t5-bf16", 4, 1, 20, 23, 5, "bf16", "adaptive"),
 ]
 
 

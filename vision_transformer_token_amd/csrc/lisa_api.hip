@@ -271,9 +271,14 @@ bool resident_plan(const Plan& pl, int cus, bool mlp, lisa::ResPlan& rp) {
 lisa_status run_resident(const Plan& pl, const lisa::ResPlan& rp, int cus, Mode mode, const void* Q, const void* K,
                          const void* V, const float* weights, float beta, const float* alpha, void* Y, char* ws,
                          float eps, hipStream_t s, bool clear_err, unsigned long long* stamps = nullptr,
-                         const lisa_weight_mlp* mlp = nullptr, const void* mlp_frag = nullptr) {
+                         const lisa_weight_mlp* mlp = nullptr, const void* mlp_frag = nullptr,
+                         const void* wo = nullptr, const float* bo = nullptr) {
   lisa::ResArgs a{};
   a.stamps = stamps;
+  if (mode == Mode::kForward) {
+    a.wo = wo;
+    a.bo = bo;
+  }
   if (mlp) {
     a.mlp_w1f = mlp_frag;
     a.mlp_b1 = mlp->b1;
@@ -327,7 +332,8 @@ lisa_status run_resident(const Plan& pl, const lisa::ResPlan& rp, int cus, Mode 
 lisa_status run(Plan pl, Mode mode, const void* Q, const void* K, const void* V,
                 const float* weights, float beta, const float* alpha, void* Y, char* ws, float eps,
                 hipStream_t s, const lisa_weight_mlp* mlp = nullptr, const void* mlp_frag = nullptr,
-                bool clear_err = false, unsigned long long* stamps = nullptr) {
+                bool clear_err = false, unsigned long long* stamps = nullptr, const void* wo = nullptr,
+                const float* bo = nullptr) {
   lisa::FlowArgs a{};
   a.clear_err = clear_err ? 1 : 0;
   if (mlp) {
@@ -361,7 +367,8 @@ lisa_status run(Plan pl, Mode mode, const void* Q, const void* K, const void* V,
   lisa::ResPlan rp;
   if (resident_plan(pl, dinfo.cus, mlp != nullptr, rp))
     return run_resident(pl, rp, dinfo.cus, mode, Q, K, V, weights, beta, alpha, Y, ws, eps, s, clear_err, stamps,
-                        mlp, mlp_frag);
+                        mlp, mlp_frag, wo, bo);
+  if (wo) return LISA_ERR_UNSUPPORTED;  // the folded projection is the resident kernel's
   if (pl.schedule == LISA_SCHEDULE_RESIDENT) return LISA_ERR_UNSUPPORTED;  // asked for, not applicable
   if (stamps) return LISA_ERR_UNSUPPORTED;  // the stage timeline is the resident kernel's
   if (!plan_tiles(pl, weights != nullptr || mlp != nullptr)) return LISA_ERR_UNSUPPORTED;
@@ -650,7 +657,20 @@ lisa_status lisa_attention_forward(const lisa_problem* p, const void* X, const v
   pa.bias = b_qkv;
   pa.out = q;
   pa.N = 3 * pa.K;
+  // One head on the resident kernel: the output projection is folded into
+  // the operator's output stage (O never goes to HBM).
+  bool fold = false;
+  if (pl.heads == 1) {
+    DeviceInfo dinfo;
+    lisa::ResPlan rp;
+    if (!device_info(dinfo)) return LISA_ERR_HIP;
+    fold = resident_plan(pl, dinfo.cus, false, rp);
+  }
+  pa.cache_out = fold ? 1 : 0;
   if (lisa::launch_proj(pl.dtype, false, pa, s) != hipSuccess) return LISA_ERR_HIP;
+  if (fold)
+    return run(pl, Mode::kForward, q, q + step, q + 2 * step, weights, beta, alpha, Y, ws, p->eps, s, nullptr,
+               nullptr, false, nullptr, w_o, b_o);
   st = run(pl, Mode::kForward, q, q + step, q + 2 * step, weights, beta, alpha, o, ws, p->eps, s);
   if (st != LISA_OK) return st;
   // Y = concat_h(O_h) Wo^T + bo.
@@ -659,6 +679,7 @@ lisa_status lisa_attention_forward(const lisa_problem* p, const void* X, const v
   pa.bias = b_o;
   pa.out = Y;
   pa.N = pa.K;
+  pa.cache_out = 0;
   if (lisa::launch_proj(pl.dtype, true, pa, s) != hipSuccess) return LISA_ERR_HIP;
   return LISA_OK;
 }

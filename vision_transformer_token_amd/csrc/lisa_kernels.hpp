@@ -205,6 +205,11 @@ struct ResArgs {
   const float* mlp_w2;
   const float* mlp_b2;
   int hidden;
+  // A one-head layer's output projection folded into the output (forward
+  // only; nullptr: Y = O): Y = O Wo^T + bo, O rounded to bf16 as the product's
+  // operand.  Wo [64][64] bf16 as torch lays it out ([out][in]), bo [64].
+  const void* wo;
+  const float* bo;
   // Optional stage timeline: workgroup w writes the constant-clock counter
   // (s_memrealtime, 100 MHz) at stage k of its first slice to
   // stamps[w * kResPhases + k] (kResStamp*), and its group and rank to the
@@ -252,6 +257,7 @@ struct ProjArgs {
   int M, N, K;            // M = B n; N = 3C (QKV) or C; K = C
   int n, heads;
   size_t head_elems;      // B * heads * n * 64
+  int cache_out;          // QKV: plain stores (the outputs are read next), else nontemporal ones
 };
 hipError_t launch_proj(int dtype, bool out_proj, const ProjArgs& a, hipStream_t s);
 

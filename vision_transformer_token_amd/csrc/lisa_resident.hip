@@ -637,6 +637,31 @@ __device__ void res_frags_from_rows(const float* st, unsigned char* frag, int ti
   }
 }
 
+// The folded output projection's operands, per slice: this thread's piece
+// of the A-operand fragments of X = Wo^T (piece (mb, q, lane) holds
+// X[dimof(8 q + j, lane / 32)][32 mb + lane % 32], j = 0..7, as above: two
+// runs of four consecutive elements of row 32 mb + lane % 32 of Wo) and, for
+// threads 0..15, four of the bias.  Loaded into registers, then stored into
+// the K region (free in the output stage), fragments then bias.
+struct ResProj {
+  uint2 w[2];
+  float4 b;
+};
+__device__ __forceinline__ ResProj res_proj_load(const ResArgs& a, int tid) {
+  ResProj x;
+  const int mb = tid >> 8, q = (tid >> 6) & 3, lane = tid & 63;
+  const uint16_t* row = static_cast<const uint16_t*>(a.wo) + (32 * mb + (lane & 31)) * kD;
+  x.w[0] = *reinterpret_cast<const uint2*>(row + dimof(8 * q, lane >> 5));
+  x.w[1] = *reinterpret_cast<const uint2*>(row + dimof(8 * q + 4, lane >> 5));
+  x.b = tid < 16 ? reinterpret_cast<const float4*>(a.bo)[tid] : make_float4(0.f, 0.f, 0.f, 0.f);
+  return x;
+}
+__device__ __forceinline__ void res_proj_store(unsigned char* dst, const ResProj& x, int tid) {
+  static_assert(kResThreads == 512, "one fragment piece per thread");
+  reinterpret_cast<uint4*>(dst)[tid] = make_uint4(x.w[0].x, x.w[0].y, x.w[1].x, x.w[1].y);
+  if (tid < 16) reinterpret_cast<float4*>(dst + kFragBytes)[tid] = x.b;
+}
+
 // ---------------------------------------------------------------------------
 // Local branch and output (per 4 x 8 block; one token per lane pair, 32
 // features per lane in accumulator layout).
@@ -834,7 +859,7 @@ __device__ __forceinline__ void res_apply(const unsigned char* frag, const float
 // One instantiation per mode (kResForward, kResReduce, kResApply) and
 // predictor use: each carries only the code its calls run, which keeps the
 // forward's code within the instruction cache a CU pair shares.
-template <int kMode, bool kMlp>
+template <int kMode, bool kMlp, bool kProj>
 __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
   extern __shared__ __align__(1024) unsigned char smem[];
   __shared__ float geo[kMaxT];  // geometric walk weights
@@ -1046,6 +1071,10 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
       }
 
       if (fwd) {
+        // The folded projection's operands: loads issued here, stored into
+        // the K region with the statistics' fragments below.
+        ResProj proj{};
+        if constexpr (kProj) proj = res_proj_load(a, tid);
         if (global) {
           // The statistics (phi(K)^T V, then M) as bf16 fragments in the
           // scratch area: built from the fp32 rows the sweeps left in LDS
@@ -1054,13 +1083,18 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
             const float* rows = reinterpret_cast<const float*>(smem + L.st);
             res_frags_from_rows(rows, smem + L.scr, tid);
             if (p.T >= 3) res_frags_from_rows(rows + kD * kD, smem + L.scr + kFragBytes, tid);
+            if constexpr (kProj) res_proj_store(smem + L.k, proj, tid);
             lds_barrier();
           } else {
             res_frags_dma(a, smem + L.scr, b, p.T >= 3 ? 2 : 1, tid);
             if (count_late && b + a.S >= a.BH && tid == 0) done_sh = res_count_done(a);
             wait_all();
+            if constexpr (kProj) res_proj_store(smem + L.k, proj, tid);
             __syncthreads();
           }
+        } else if constexpr (kProj) {
+          res_proj_store(smem + L.k, proj, tid);
+          __syncthreads();
         }
         res_stamp(a, first, kResStampFrags);
         const unsigned char* fkv = smem + L.scr;
@@ -1113,6 +1147,23 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
               }
               res_apply(fkv, z, Lm[j], tid);
             }
+            if constexpr (kProj) {
+              // Y = O Wo^T + bo: the bias into the accumulators, then the
+              // product with O (rounded to bf16 as its operand).
+              const float* bias = reinterpret_cast<const float*>(smem + L.k + kFragBytes);
+              float yo[32];
+#pragma unroll
+              for (int c = 0; c < 8; ++c) {
+                const float4 bq = *reinterpret_cast<const float4*>(bias + dimof(4 * c, h));
+                yo[4 * c] = bq.x;
+                yo[4 * c + 1] = bq.y;
+                yo[4 * c + 2] = bq.z;
+                yo[4 * c + 3] = bq.w;
+              }
+              res_apply(smem + L.k, Lm[j], yo, tid);
+#pragma unroll
+              for (int v = 0; v < 32; ++v) Lm[j][v] = yo[v];
+            }
             if (valid[j]) {
               // The token index recomputed here (not kept from the Q loads).
               int sl = slot[j], tr, tc;
@@ -1150,19 +1201,20 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
 
 }  // namespace
 
-template <int kMode, bool kMlp>
+template <int kMode, bool kMlp, bool kProj = false>
 hipError_t launch_resident_typed(const ResArgs& a, int grid, hipStream_t s) {
   static std::atomic<bool> lds_set[kMaxDevices];
   const hipError_t e =
-      ensure_lds_limit(reinterpret_cast<const void*>(&resident_kernel<kMode, kMlp>), kResLdsMax, lds_set);
+      ensure_lds_limit(reinterpret_cast<const void*>(&resident_kernel<kMode, kMlp, kProj>), kResLdsMax, lds_set);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((resident_kernel<kMode, kMlp>), dim3(grid), dim3(kResThreads), a.p.L.total, s, a);
+  hipLaunchKernelGGL((resident_kernel<kMode, kMlp, kProj>), dim3(grid), dim3(kResThreads), a.p.L.total, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_resident(const ResArgs& a, int grid, hipStream_t s) {
   if (a.mode == kResReduce) return launch_resident_typed<kResReduce, false>(a, grid, s);
   if (a.mode == kResApply) return launch_resident_typed<kResApply, false>(a, grid, s);
+  if (a.wo) return a.mlp_w1f ? hipErrorInvalidValue : launch_resident_typed<kResForward, false, true>(a, grid, s);
   return a.mlp_w1f ? launch_resident_typed<kResForward, true>(a, grid, s)
                    : launch_resident_typed<kResForward, false>(a, grid, s);
 }
