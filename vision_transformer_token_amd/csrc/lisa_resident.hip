@@ -1164,7 +1164,30 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
 #pragma unroll
               for (int v = 0; v < 32; ++v) Lm[j][v] = yo[v];
             }
-            if (valid[j]) {
+            if (global) {
+              // Y through the block's own slot rows of the Qt region (its u_1
+              // was read from them at the block's start; no other wave reads
+              // them): written as bf16 rows, then read back so that each
+              // store instruction writes one block row, 8 tokens x 128
+              // contiguous bytes, as whole lines, nontemporally (Y is not
+              // read again here; dirty lines would be written back at the
+              // kernel's end, on the next kernel's time).
+#pragma unroll
+              for (int c = 0; c < 8; ++c)
+                *reinterpret_cast<uint2*>(qt + row_off<BF16>(slot[j], dimof(4 * c, h))) =
+                    make_uint2(pack_bf16x2(Lm[j][4 * c], Lm[j][4 * c + 1]), pack_bf16x2(Lm[j][4 * c + 2], Lm[j][4 * c + 3]));
+              asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's rows are written
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int sl = blkid[j] * 32 + 8 * r + (lane >> 3), pc = lane & 7;
+                int tr, tc;
+                const bool on = res_slot(p, t, sl, tr, tc);
+                const u32x4 v = *reinterpret_cast<const u32x4*>(qt + row_off<BF16>(sl, 8 * pc));
+                if (on)
+                  __builtin_nontemporal_store(
+                      v, reinterpret_cast<u32x4*>(Yb + ((size_t)(t.r0 + tr) * p.W + (t.c0 + tc)) * kD + 8 * pc));
+              }
+            } else if (valid[j]) {
               // The token index recomputed here (not kept from the Q loads).
               int sl = slot[j], tr, tc;
               asm volatile("" : "+v"(sl));
