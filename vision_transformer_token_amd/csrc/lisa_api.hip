@@ -666,7 +666,6 @@ lisa_status lisa_attention_forward(const lisa_problem* p, const void* X, const v
     if (!device_info(dinfo)) return LISA_ERR_HIP;
     fold = resident_plan(pl, dinfo.cus, false, rp);
   }
-  pa.cache_out = fold ? 1 : 0;
   if (lisa::launch_proj(pl.dtype, false, pa, s) != hipSuccess) return LISA_ERR_HIP;
   if (fold)
     return run(pl, Mode::kForward, q, q + step, q + 2 * step, weights, beta, alpha, Y, ws, p->eps, s, nullptr,
@@ -679,7 +678,6 @@ lisa_status lisa_attention_forward(const lisa_problem* p, const void* X, const v
   pa.bias = b_o;
   pa.out = Y;
   pa.N = pa.K;
-  pa.cache_out = 0;
   if (lisa::launch_proj(pl.dtype, true, pa, s) != hipSuccess) return LISA_ERR_HIP;
   return LISA_OK;
 }

@@ -257,7 +257,6 @@ struct ProjArgs {
   int M, N, K;            // M = B n; N = 3C (QKV) or C; K = C
   int n, heads;
   size_t head_elems;      // B * heads * n * 64
-  int cache_out;          // QKV: plain stores (the outputs are read next), else nontemporal ones
 };
 hipError_t launch_proj(int dtype, bool out_proj, const ProjArgs& a, hipStream_t s);
 

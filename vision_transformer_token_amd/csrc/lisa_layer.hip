@@ -292,23 +292,15 @@ __global__ __launch_bounds__(256) void proj_stream_qkv(ProjArgs a) {
     for (int j = 0; j < 2; ++j) {
       const int m = rt * 64 + 16 * w + 8 * j + ln / 8;
       if (m >= a.M) continue;
-      u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + out_index<false>(a, m, c0 + 8 * (ln % 8)));
-      if (a.cache_out)
-        *dst = o[j];
-      else
-        __builtin_nontemporal_store(o[j], dst);
+      __builtin_nontemporal_store(
+          o[j], reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + out_index<false>(a, m, c0 + 8 * (ln % 8))));
     }
   }
 }
 
 template <class S>
 hipError_t launch_proj_typed(bool out_proj, const ProjArgs& a, hipStream_t s) {
-  // Nontemporal stores, unless the operator that reads Q, K, V next folds
-  // the output projection (the layer's one kernel after this one): then
-  // plain stores leave them in the cache for its staging (PVT-T stage 1,
-  // that pair 55.9 -> 54.4 us; with the output projection as a kernel of its
-  // own, plain stores cost 3 us).  The streaming kernel pays for the QKV
-  // projection (PVT-T stage 1, 64
+  // The streaming kernel pays for the QKV projection (PVT-T stage 1, 64
   // channels: 17.7 -> 15.5 us with 1024 workgroups; 256 / 512 / 768 / 1536 /
   // 2048 of them: 23.9 / 17.5 / 15.8 / 17.2 / 20.1 us); the output projection
   // takes about as long either way (8.0 -> 8.0 us at 768 workgroups, 8.8 at
