@@ -293,6 +293,31 @@ __device__ __forceinline__ void acc_to_quad(const f32x4 (&acc)[4], unsigned char
   }
 }
 
+// The wave's 16 token rows of an output (x: this lane's 16 features of its
+// token, stored if `on`; tok0: the wave's first token).  bf16: through the
+// wave's LDS rows, so that each store instruction writes eight whole
+// 128-byte rows, nontemporally (the outputs are not read again here; dirty
+// lines would be written back at the kernel's end, on the next kernel's
+// time).  fp32: each lane its own 64 bytes.
+template <class S>
+__device__ __forceinline__ void store_rows(S* out, int tok0, int n, unsigned char* X, int tw, int f0,
+                                           const float (&x)[kF], bool on) {
+  if constexpr (RowsOf<S>::kF32) {
+    if (on) store16(out + (size_t)(tok0 + tw) * kD, f0, x);
+  } else {
+    quad_lds_sync();
+    if (on) put_row<S>(X, tw, f0, x);
+    quad_lds_sync();
+    const int lane = threadIdx.x % 64;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 8 * h + lane / 8, pc = lane % 8;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(X + r * RowsOf<S>::kRowBytes + 16 * pc);
+      if (tok0 + r < n) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out + (size_t)(tok0 + r) * kD + 8 * pc));
+    }
+  }
+}
+
 // Sum over the wave (butterfly of fixed shape: the same order every run).
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
@@ -888,7 +913,7 @@ __global__ __launch_bounds__(kTT) void bwd_token_q(BwdArgs a) {
   }
   float dqt[kF];
   acc_to_quad<S>(acc, wrows, tw, f0, dqt);
-  if (!on) return;  // no barrier follows
+  if (on) {
   const float4 tp = a.tok[base + i];  // m_i, Z_i, c_i, dz_i
   Piece<S> qp, dyp;  // raw Q_i and dY_i as loaded, for the window's dot products
   qp.load(Qb + (size_t)i * kD, f0);
@@ -918,7 +943,8 @@ __global__ __launch_bounds__(kTT) void bwd_token_q(BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < kF; ++e) dqt[e] += g * kc[e];
   }
-  store16(static_cast<S*>(a.dQ) + (base + i) * kD, f0, dqt);
+  }
+  store_rows<S>(static_cast<S*>(a.dQ) + base * kD, blk * kBT + (t / 64) * 16, a.n, wrows, tw, f0, dqt, on);
 }
 
 // dK_j = (dM Qt_j + dKV V_j + ds) [K_j > 0] + sum_i dz_ij q_i / 8 and
@@ -997,7 +1023,7 @@ __global__ __launch_bounds__(kTT) void bwd_token_kv(BwdArgs a) {
   float dk[kF], dv[kF];
   acc_to_quad<S>(acck, wrows, tw, f0, dk);
   acc_to_quad<S>(accv, wrows, tw, f0, dv);
-  if (!on) return;  // no barrier follows
+  if (on) {
 #pragma unroll
   for (int e = 0; e < kF; ++e) dk[e] = kr[e] > 0.f ? dk[e] + ds_sh[f0 + e] : 0.f;
   {
@@ -1032,8 +1058,9 @@ __global__ __launch_bounds__(kTT) void bwd_token_kv(BwdArgs a) {
       dv[e] += pv * yc[e];
     }
   }
-  store16(static_cast<S*>(a.dK) + (base + i) * kD, f0, dk);
-  store16(static_cast<S*>(a.dV) + (base + i) * kD, f0, dv);
+  }
+  store_rows<S>(static_cast<S*>(a.dK) + base * kD, blk * kBT + (t / 64) * 16, a.n, wrows, tw, f0, dk, on);
+  store_rows<S>(static_cast<S*>(a.dV) + base * kD, blk * kBT + (t / 64) * 16, a.n, wrows, tw, f0, dv, on);
 }
 
 template <class S>
