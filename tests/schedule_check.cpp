@@ -14,12 +14,18 @@
 //   - the sweep steps read only slots of the tile; the combine ranges of the
 //     G ranks partition the statistics; the workgroup -> (group, rank) map
 //     takes every rank of every group once.
+// It also checks the layer projections' schedules (lisa_layer.hpp) for a set
+// of row and output counts: the blocked kernel's workgroups take every
+// (row block, column block) once; the streaming kernel's units take every
+// (row tile, column block) once, and the units a workgroup walks share its
+// column block.
 // Prints one line per problem ("ok ..." or "FAIL ...") and exits non-zero on
 // any failure.
 #include <cstdio>
 #include <cstdlib>
 #include <vector>
 
+#include "lisa_layer.hpp"
 #include "lisa_resident.hpp"
 
 using namespace lisa;
@@ -150,7 +156,39 @@ static void check(int H, int W, int T, int gcap) {
                 p.ty, p.tx, p.TR, p.TC, p.nblk, p.SR, p.SC, L.total);
 }
 
+static void check_proj(int M, int N) {
+  const int before = fails;
+  const int nct = N / 64;
+  const int nrb = (M + 64 * kProjTiles - 1) / (64 * kProjTiles), nrt = (M + 63) / 64;
+  std::vector<int> seen((size_t)nrb * nct, 0);
+  const int grid = proj_grid(M, N);
+  for (int w = 0; w < grid; ++w) {
+    int rb, cb;
+    proj_block(M, N, w, rb, cb);
+    CHECK(rb >= -1 && rb < nrb && cb >= 0 && cb < nct, "proj block of %d: %d %d", w, rb, cb);
+    if (rb >= 0 && rb < nrb && cb >= 0 && cb < nct) ++seen[(size_t)rb * nct + cb];
+  }
+  for (size_t k = 0; k < seen.size(); ++k) CHECK(seen[k] == 1, "M %d N %d: block %zu taken %d times", M, N, k, seen[k]);
+  const int U = proj_units(M, N), G = proj_stream_grid(M, N);
+  CHECK(U % (8 * nct) == 0 && G >= 1 && G <= U && (G % (8 * nct) == 0 || G == U), "stream grid %d of %d units", G, U);
+  std::vector<int> tiles((size_t)nrt * nct, 0);
+  for (int g = 0; g < G; ++g) {
+    int rt0, cb0;
+    proj_unit(N, g, rt0, cb0);
+    for (int u = g; u < U; u += G) {
+      int rt, cb;
+      proj_unit(N, u, rt, cb);
+      CHECK(cb == cb0 && cb >= 0 && cb < nct && rt >= 0, "unit %d of workgroup %d: tile %d block %d", u, g, rt, cb);
+      if (rt < nrt && cb >= 0 && cb < nct) ++tiles[(size_t)rt * nct + cb];
+    }
+  }
+  for (size_t k = 0; k < tiles.size(); ++k) CHECK(tiles[k] == 1, "M %d N %d: unit %zu taken %d times", M, N, k, tiles[k]);
+  if (fails == before) std::printf("proj %d %d covered: %d workgroups, %d units on %d\n", M, N, grid, U, G);
+}
+
 int main(int argc, char** argv) {
+  for (int M : {1, 63, 64, 65, 297, 1000, 37632, 51300, 100352})
+    for (int N : {64, 192, 384, 576}) check_proj(M, N);
   for (int i = 1; i + 3 < argc; i += 4) check(std::atoi(argv[i]), std::atoi(argv[i + 1]), std::atoi(argv[i + 2]),
                                                 std::atoi(argv[i + 3]));
   if (fails) std::printf("%d failures\n", fails);

@@ -74,6 +74,17 @@ def test_resident_schedule_covers_exactly_once(checker, cus):
     assert res.stdout.count("ok ") + res.stdout.count("none ") == len(SHAPES)
 
 
+def test_projection_schedules_cover_exactly_once(checker):
+    """The layer's projections (lisa_layer.hpp): for row counts from 1 to
+    PVT-T stage 1's 100,352 and 64 to 576 outputs, the blocked kernel's
+    workgroups and the streaming kernel's units each take every output block
+    once, and a streaming workgroup's units share its column block."""
+    res = subprocess.run([checker], capture_output=True, text=True)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert res.stdout.count(" covered: ") == 36, res.stdout
+    assert "proj 100352 192 covered: 1176 workgroups, 4704 units on 1008" in res.stdout, res.stdout
+
+
 def test_headline_tiling(checker):
     """PVT-T stage 1 (32 slices of 56 x 56) on 256 compute units: eight ranks
     per slice on 28 x 14 tiles, everything on chip."""

@@ -32,6 +32,7 @@
 
 #include "lisa_device.hpp"
 #include "lisa_kernels.hpp"
+#include "lisa_layer.hpp"
 
 namespace lisa {
 namespace {
@@ -56,35 +57,13 @@ __device__ __forceinline__ size_t out_index(const ProjArgs& a, int m, int c) {
 }
 
 constexpr int kRowPad = 68;  // floats per LDS row: four lane groups 272 floats apart, on distinct banks
-constexpr int kProjTiles = 4;  // 64-row tiles per workgroup: each weight operand read serves four
-
-constexpr int kXcds = 8;
-// Row block and column block of workgroup w (row block -1: idle).  With
-// several column blocks, XCD x takes row blocks x, x + 8, ..., each with all
-// its column blocks in a row; the grid is padded to whole rounds of 8.
-__host__ __device__ inline void proj_block(const ProjArgs& a, int w, int& rb, int& cb) {
-  const int nct = a.N / 64, nrb = (a.M + 64 * kProjTiles - 1) / (64 * kProjTiles);
-  if (nct == 1) {
-    rb = w;
-    cb = 0;
-  } else {
-    const int x = w % kXcds, k = w / kXcds;
-    rb = x + kXcds * (k / nct);
-    cb = k % nct;
-  }
-  if (rb >= nrb) rb = -1;
-}
-__host__ inline unsigned proj_grid(const ProjArgs& a) {
-  const int nct = a.N / 64, nrb = (a.M + 64 * kProjTiles - 1) / (64 * kProjTiles);
-  return nct == 1 ? (unsigned)nrb : (unsigned)((nrb + kXcds - 1) / kXcds * kXcds * nct);
-}
 
 template <class S, bool kOut>
 __global__ __launch_bounds__(256) void proj_gemm(ProjArgs a) {
   __shared__ __align__(16) float rows[4][16 * kRowPad];
   const int t = threadIdx.x, w = t / 64, ln = t % 64, li = ln % 16, lk = ln / 16;
   int rb, cb;
-  proj_block(a, (int)blockIdx.x, rb, cb);
+  proj_block(a.M, a.N, (int)blockIdx.x, rb, cb);
   if (rb < 0) return;  // no barrier in this kernel
   const int c0 = cb * 64;
   const int mb = rb * (64 * kProjTiles) + 16 * w;  // wave's rows in tile r: mb + 64 r + 0..15
@@ -204,36 +183,25 @@ __global__ __launch_bounds__(256) void proj_gemm(ProjArgs a) {
 
 // The QKV projection in bf16 with K = 64 (one head's channels in, as in a
 // one-head stage): the whole contraction of a row is one 16-byte operand per
-// lane and MFMA step, so a workgroup can stream.  A fixed grid of workgroups walks the 64 x 64
-// output blocks (unit u = block of XCD u % 8, as proj_block maps them); the
-// grid is a multiple of 8 times the column blocks, so a workgroup keeps one
-// column block, loads its weights and bias once, and each wave loads the
-// next block's 16 input rows before it works on the current one.
-constexpr int kStreamGrid = 1024;  // workgroups: four per CU of a 256-CU device, rounded down below
-
-__host__ inline int proj_units(const ProjArgs& a) {
-  const int nct = a.N / 64, nrt = (a.M + 63) / 64;
-  return (nrt + kXcds - 1) / kXcds * kXcds * nct;
-}
-__host__ inline unsigned proj_stream_grid(const ProjArgs& a) {
-  const int step = kXcds * (a.N / 64);
-  int g = kStreamGrid / step * step;
-  if (g < step) g = step;
-  const int u = proj_units(a);
-  return (unsigned)(g < u ? g : u);
-}
-
+// lane and MFMA step, so a workgroup can stream.  A fixed grid of workgroups
+// walks the 64 x 64 output blocks (proj_unit); a workgroup keeps one column
+// block, loads its weights and bias once, and each wave loads the next
+// block's 16 input rows before it works on the current one.
 __global__ __launch_bounds__(256) void proj_stream_qkv(ProjArgs a) {
   __shared__ __align__(16) float rows[4][16 * kRowPad];
   const int t = threadIdx.x, w = t / 64, ln = t % 64, li = ln % 16, lk = ln / 16;
-  const int nct = a.N / 64, nrt = (a.M + 63) / 64;
-  const int U = (nrt + kXcds - 1) / kXcds * kXcds * nct;
+  const int nrt = (a.M + 63) / 64, U = proj_units(a.M, a.N);
   const uint16_t* A = static_cast<const uint16_t*>(a.A);
   const uint16_t* Wt = static_cast<const uint16_t*>(a.Wt);
-  // Unit u: row tile x + 8 (k / nct), column block k % nct (k = u / 8).
   const int u0 = (int)blockIdx.x;
-  const int cb = (u0 / kXcds) % nct, c0 = cb * 64;
-  auto tile_of = [&](int u) { return u % kXcds + kXcds * ((u / kXcds) / nct); };
+  int rt0, cb;
+  proj_unit(a.N, u0, rt0, cb);  // every unit of this workgroup has column block cb
+  const int c0 = cb * 64;
+  auto tile_of = [&](int u) {
+    int rt, cbu;
+    proj_unit(a.N, u, rt, cbu);
+    return rt;
+  };
   bf16x8 bv[2][4];
 #pragma unroll
   for (int h = 0; h < 2; ++h)
@@ -306,10 +274,10 @@ hipError_t launch_proj_typed(bool out_proj, const ProjArgs& a, hipStream_t s) {
   // takes about as long either way (8.0 -> 8.0 us at 768 workgroups, 8.8 at
   // 1024) and keeps the blocked kernel.
   if (sizeof(S) == 2 && a.K == 64 && !out_proj) {
-    hipLaunchKernelGGL(proj_stream_qkv, dim3(proj_stream_grid(a)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(proj_stream_qkv, dim3(proj_stream_grid(a.M, a.N)), dim3(256), 0, s, a);
     return hipGetLastError();
   }
-  const dim3 grid(proj_grid(a));
+  const dim3 grid(proj_grid(a.M, a.N));
   if (out_proj)
     hipLaunchKernelGGL((proj_gemm<S, true>), grid, dim3(256), 0, s, a);
   else
