@@ -43,7 +43,7 @@ KERNEL_SOURCES = KERNEL_SOURCES_BY_NAME["flow_kernel<bf16>"]
 # The backward starts with the resident kernel's statistics launch; the layer
 # runs the projections around the resident kernel.
 BACKWARD_SOURCES = KERNEL_SOURCES_BY_NAME["resident_kernel"] + _csrc("lisa_backward.hip")
-LAYER_SOURCES = KERNEL_SOURCES_BY_NAME["resident_kernel"] + _csrc("lisa_layer.hip")
+LAYER_SOURCES = KERNEL_SOURCES_BY_NAME["resident_kernel"] + _csrc("lisa_layer.hip", "lisa_layer.hpp")
 
 
 def kernel_source_hash(sources=None):
