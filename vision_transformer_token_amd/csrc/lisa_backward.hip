@@ -689,14 +689,20 @@ __global__ __launch_bounds__(kTT) void bwd_token_a(BwdArgs a) {
         if (k <= T1) dw[k] = alpha * dyy[k];
     }
   }
-  // dalpha's share: sum_i dY_i . (G_i - L_i), fixed-order tree.
-  if (qd == 0) red[tk] = on ? dyG - dyL : 0.f;
-  __syncthreads();
-  for (int o = kBT / 2; o > 0; o >>= 1) {
-    if (t < o) red[t] += red[t + o];
+  // dalpha's share: sum_i dY_i . (G_i - L_i), in a fixed order: each wave's
+  // 16 tokens by a butterfly (the quad's lanes hold the same value: every
+  // fourth lane takes part), then the 16 waves' sums in order.
+  {
+    float v = on && qd == 0 ? dyG - dyL : 0.f;
+    v = wave_sum(v);
+    if ((t & 63) == 0) red[t >> 6] = v;
     __syncthreads();
+    if (t == 0) {
+      float u = 0.f;
+      for (int w2 = 0; w2 < kTT / 64; ++w2) u += red[w2];
+      a.da_part[(size_t)b * a.nblk + blk] = u;
+    }
   }
-  if (t == 0) a.da_part[(size_t)b * a.nblk + blk] = red[0];
 }
 
 // dP_k (the token workgroups' partials, summed in order); then, from the
