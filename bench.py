@@ -370,6 +370,41 @@ def summarize_layer(outdir, workload, command):
               f"algorithmic bytes per call: {tok * bb / 1e6:.2f} MB ({bb} B per token: X read, Y written, "
               f"weights); at 8 TB/s: {tok * bb / 8e12 * 1e6:.1f} us",
               f"kernel source hash (operator and projection sources): {kernel_source_hash(LAYER_SOURCES)}"]
+    # Counter passes over the same run, when present: utilisation, then HBM
+    # bytes scaled by the copy calibration stored with the forward's counters.
+    util_csv = os.path.join(outdir, "pmc_layer_util", "util_counter_collection.csv")
+    if os.path.exists(util_csv):
+        def per_kernel(path, counter):
+            acc = {}
+            for r in _csv_rows(path):
+                if r["Counter_Name"] == counter:
+                    acc.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+            return {k: sum(v) / len(v) for k, v in acc.items()}
+        avg_ns = {_short(r["Name"]): float(r["AverageNs"]) for r in stats}
+        mfma = per_kernel(util_csv, "MfmaUtil")
+        valu = per_kernel(util_csv, "VALUBusy")
+        mops = per_kernel(util_csv, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        fetch = per_kernel(os.path.join(outdir, "pmc_layer_fetch", "fetch_counter_collection.csv"), "FETCH_SIZE")
+        write = per_kernel(os.path.join(outdir, "pmc_layer_write", "write_counter_collection.csv"), "WRITE_SIZE")
+        with open(COUNTERS) as f:
+            cal = json.load(f)["copy_calibration"]
+        run = "python3 bench.py --layer-only --steps 10 --warmup 2 --no-cpu-baseline --workload " + w.name
+        lines += ["", "# Utilisation and HBM traffic per launch (rocprofv3 --pmc, one pass each)", "",
+                  f"utilisation pass: rocprofv3 --pmc MfmaUtil VALUBusy SQ_INSTS_VALU_MFMA_MOPS_BF16 --output-format csv "
+                  f"-d gpurun_out/pmc_layer_util -o util -- {run}",
+                  f"traffic passes: rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv "
+                  f"-d gpurun_out/pmc_layer_fetch -o fetch (pmc_layer_write -o write) -- {run}",
+                  f"FETCH_SIZE scaled by {cal['fetch_scale']:.3f} and WRITE_SIZE by {cal['write_scale']:.3f} "
+                  "(the plain-copy calibration in profiles/counters.json).", "",
+                  "| kernel | MfmaUtil | VALUBusy | bf16 MFMA TFLOP/s | HBM bytes (scaled) | GB/s |", "|---|---|---|---|---|---|"]
+        for k in sorted(mfma):
+            if not (k in KERNEL_SOURCES_BY_NAME or k.startswith("proj_")):
+                continue
+            ns = avg_ns.get(k, float("nan"))
+            hbm = fetch.get(k, float("nan")) * 1024 * cal["fetch_scale"] + write.get(k, float("nan")) * 1024 * cal["write_scale"]
+            tflops = mops.get(k, 0.0) * 512 / (ns * 1e-9) / 1e12
+            lines.append(f"| {k} | {mfma[k]:.1f}% | {valu.get(k, float('nan')):.1f}% | {tflops:.1f} | "
+                         f"{hbm / 1e6:.2f} MB | {hbm / ns:.0f} |")
     with open(os.path.join(ROOT, "profiles", f"lisa_attention_forward_{w.name}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
