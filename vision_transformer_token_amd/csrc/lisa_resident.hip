@@ -1177,13 +1177,17 @@ __global__ __launch_bounds__(kResThreads) void resident_kernel(ResArgs a) {
                 *reinterpret_cast<uint2*>(qt + row_off<BF16>(slot[j], dimof(4 * c, h))) =
                     make_uint2(pack_bf16x2(Lm[j][4 * c], Lm[j][4 * c + 1]), pack_bf16x2(Lm[j][4 * c + 2], Lm[j][4 * c + 3]));
               asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's rows are written
+              // The block's first token row and column (one division per
+              // block, on the wave-uniform block index); block row r, token
+              // column lane / 8.
+              int tr0, tc0;
+              res_slot(p, t, __builtin_amdgcn_readfirstlane(blkid[j]) * 32, tr0, tc0);
+              const int pc = lane & 7, tc = tc0 + (lane >> 3);
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
-                const int sl = blkid[j] * 32 + 8 * r + (lane >> 3), pc = lane & 7;
-                int tr, tc;
-                const bool on = res_slot(p, t, sl, tr, tc);
+                const int sl = blkid[j] * 32 + 8 * r + (lane >> 3), tr = tr0 + r;
                 const u32x4 v = *reinterpret_cast<const u32x4*>(qt + row_off<BF16>(sl, 8 * pc));
-                if (on)
+                if (tr < t.th && tc < t.tw)
                   __builtin_nontemporal_store(
                       v, reinterpret_cast<u32x4*>(Yb + ((size_t)(t.r0 + tr) * p.W + (t.c0 + tc)) * kD + 8 * pc));
               }
