@@ -18,7 +18,9 @@
 //     over its tokens -> partial of M, published;
 //   after all M partials: its share of the fixed-order sum of the partials
 //     (statistics as fp32 and as MFMA fragments), published;
-//   after all shares: the walk of its tokens on MFMA, Y written once.
+//   after all shares: the walk of its tokens on MFMA, Y written once (whole
+//     rows per store instruction, nontemporally; for a one-head layer, after
+//     the output projection applied to each block).
 // All eight waves (two per SIMD, 256 registers each) do every step; waits
 // on other ranks are polled by one wave while the others sit at the
 // workgroup barrier.
