@@ -92,6 +92,9 @@ CASES = [
     ("one-head-long-bf16", 2, 1, 150, 171, 3, "bf16", "geometric"),
     ("one-head-t1-bf16", 2, 1, 7, 6, 1, "bf16", "adaptive"),
     ("one-head-t5-bf16", 4, 1, 20, 23, 5, "bf16", "adaptive"),
+    # One head where the resident kernel does not apply (T > 8): the
+    # streaming operator and the output projection as a kernel of its own.
+    ("one-head-t9-bf16", 2, 1, 12, 13, 9, "bf16", "geometric"),
 ]
 
 
